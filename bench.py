@@ -1,0 +1,211 @@
+"""Decode-step benchmark on one MI355X: tokens/s and achieved HBM GB/s.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one qd_decode_step call: embedding, every layer (fused RMSNorm + QKV
+GEMV, q/k norm + RoPE + KV append, split-K attention + merge, o_proj + residual,
+RMSNorm + gate/up + SwiGLU, down + residual), final norm, lm_head and greedy
+argmax, for one batch of synthetic input already resident in HBM. Each step
+re-runs the same positions (the step is idempotent at a position), so every
+timed step attends over exactly `past` cached tokens.
+
+Prints ONE JSON line. `roofline` covers the dominant kernel kind: its
+algorithmic bytes per launch divided by its average launch duration, measured
+with HIP events recorded on the library's stream around each launch of every
+kind, in a second pass of the same K steps right after the clean timed region.
+`cpu_baseline` is the fp64 oracle timed on the host over a bounded sample of
+whole decode steps of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "decode tokens/s + achieved HBM GB/s (% of peak), Qwen2-0.5B-shape, batch 1/16"
+
+
+def _bytes_per_launch(shape, B, ctx):
+    """Algorithmic bytes per launch of each kernel kind: weights read once, KV read
+    once, activations counted at their float32 size."""
+    from decode_step_amd import qd as Q
+    wb = 2 if shape.w_dtype == "bf16" else 4
+    kvb = 2 if shape.kv_dtype == "bf16" else 4
+    D, F, V = shape.hidden, shape.ffn, shape.vocab
+    qd_, kvd = shape.q_dim, shape.kv_dim
+    qkvr = qd_ + 2 * kvd
+    kv_tokens = int(np.sum(ctx + 1))
+    act = 4
+    out = {
+        Q.QD_K_QKV: qkvr * D * wb + (qkvr * wb if shape.qkv_bias else 0) + D * wb + B * (D + qkvr) * act,
+        Q.QD_K_ATTN: kv_tokens * 2 * kvd * kvb + B * qd_ * act,
+        Q.QD_K_O: D * qd_ * wb + B * (qd_ + 2 * D) * act,
+        Q.QD_K_GATEUP: 2 * F * D * wb + D * wb + B * (D + F) * act,
+        Q.QD_K_DOWN: D * F * wb + B * (F + 2 * D) * act,
+        Q.QD_K_LMHEAD: V * D * wb + D * wb + B * (D + V) * act,
+    }
+    return out
+
+
+def step_bytes(shape, B, ctx):
+    """Algorithmic bytes of one whole step (every weight once, every cached K/V once,
+    the new K/V written, the embedding rows and the logits)."""
+    wb = 2 if shape.w_dtype == "bf16" else 4
+    kvb = 2 if shape.kv_dtype == "bf16" else 4
+    c = shape.param_counts()
+    # every parameter once, except that an untied embedding table is only gathered
+    # (B rows, counted below); a tied table is read whole as the lm_head
+    weights = (c["total"] - (0 if shape.tied else shape.vocab * shape.hidden)) * wb
+    kv_read = int(np.sum(ctx)) * shape.n_layers * 2 * shape.kv_dim * kvb
+    kv_write = B * shape.n_layers * 2 * shape.kv_dim * kvb
+    emb_rows = B * shape.hidden * wb
+    logits = B * shape.vocab * 4
+    return weights + kv_read + kv_write + emb_rows + logits
+
+
+def cpu_baseline(wl, case_host, ctx, tokens, budget_s=12.0):
+    """Whole oracle decode steps on the host until about budget_s seconds have
+    run (at least two steps), after one untimed step that widens the weights."""
+    from oracle.qwen2 import OracleWeights, decode_step
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    shape = wl.shape
+    host_w, kh, vh, table = case_host
+    ow = OracleWeights(shape, host_w, cache_layers=True)
+    decode_step(shape, ow, kh, vh, table, ctx, tokens=tokens)
+    n, t0 = 0, time.perf_counter()
+    while True:
+        decode_step(shape, ow, kh, vh, table, ctx, tokens=tokens)
+        n += 1
+        el = time.perf_counter() - t0
+        if (el >= budget_s and n >= 2) or el > 4 * budget_s:
+            break
+    B = len(ctx)
+    return {"value": round(B * n / el, 4), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} whole decode steps of {wl.name} (batch {B}) in {el:.1f} s, fp64 numpy, "
+                      f"after one untimed step that widens the weights"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="qwen2-0.5b-bf16-b1-past512")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the multi-GPU layout is described in DESIGN.md and not run.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from decode_step_amd import qd as Q
+    from decode_step_amd.runner import DecodeRunner
+    from workloads import shapes as S, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    wl = S.WORKLOADS[args.workload]
+    shape = wl.shape
+    dev = "cuda"
+    ctx = synth.make_ctx(wl.batch, wl.past, wl.ctx_range, wl.seed)
+    B = wl.batch
+    w = synth.make_weights(shape, seed=wl.seed, device=dev)
+    kv = synth.make_kv(shape, ctx, extra=2, seed=wl.seed, device=dev, random_order=wl.paged_random)
+    runner = DecodeRunner(shape, w, kv.k, kv.v, kv.block_table, max_batch=B, max_ctx=int(ctx.max()) + 2,
+                          device=dev)
+    tokens = synth.make_tokens(B, shape.vocab, seed=wl.seed, name="tok0")
+    tok_d = torch.from_numpy(tokens).to(dev)
+    pos_d = torch.from_numpy(ctx).to(dev)
+    logits = torch.empty(B, shape.vocab, device=dev)
+    nxt = torch.empty(B, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        runner.step(ctx, pos_d, tokens=tok_d, logits=logits, next_tokens=nxt, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = 1e3 * elapsed / args.steps
+    tok_s = B * args.steps / elapsed
+    sb = step_bytes(shape, B, ctx)
+    print(f"[bench] {wl.name}: {ms_per_step:.4f} ms/step, {tok_s:.1f} tokens/s, "
+          f"{sb / 1e6:.2f} MB/step -> {sb / elapsed * args.steps / 1e9:.1f} GB/s end to end",
+          file=sys.stderr, flush=True)
+
+    # profiled pass: events around every launch of every kind
+    kinds = {Q.QD_K_EMBED: "embed", Q.QD_K_QKV: "qkv_gemv", Q.QD_K_QKV_POST: "qkv_post",
+             Q.QD_K_ATTN: "attention", Q.QD_K_MERGE: "attn_merge", Q.QD_K_O: "o_proj_gemv",
+             Q.QD_K_GATEUP: "gate_up_gemv", Q.QD_K_DOWN: "down_gemv", Q.QD_K_LMHEAD: "lm_head_gemv",
+             Q.QD_K_ARGMAX: "argmax", Q.QD_K_OTHER: "other"}
+    mask = 0
+    for k in kinds:
+        mask |= 1 << k
+    steps_prof = min(args.steps, max(1, 8000 // (shape.n_layers * 8 + 8)))
+    Q.qd_profile_enable(mask)
+    for _ in range(steps_prof):
+        step()
+    torch.cuda.synchronize()
+    per_kind = {}
+    for k, name in kinds.items():
+        n, ms = Q.qd_profile_read(k)
+        if n:
+            per_kind[k] = (n, ms)
+    Q.qd_profile_enable(0)
+    bpl = _bytes_per_launch(shape, B, ctx)
+    total_ms = sum(ms for _, ms in per_kind.values())
+    for k, (n, ms) in sorted(per_kind.items(), key=lambda kv_: -kv_[1][1]):
+        avg_us = 1e3 * ms / n
+        gbs = (bpl[k] / (avg_us * 1e-6) / 1e9) if k in bpl else float("nan")
+        print(f"[bench]   {kinds[k]:>14}: {n // steps_prof:3d}/step avg {avg_us:8.2f} us "
+              f"({100 * ms / total_ms:5.1f}% of kernel time) {gbs:8.1f} GB/s", file=sys.stderr)
+    dom = max((k for k in per_kind if k in bpl), key=lambda k: per_kind[k][1])
+    n_dom, ms_dom = per_kind[dom]
+    avg_s = ms_dom / n_dom * 1e-3
+    achieved = bpl[dom] / avg_s / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": kinds[dom], "bytes_per_launch": int(bpl[dom]),
+                "avg_launch_us": round(avg_s * 1e6, 3)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        case_host = (synth.weights_to_host(w), [synth.to_host_bits(t).copy() for t in kv.k],
+                     [synth.to_host_bits(t).copy() for t in kv.v], kv.block_table)
+        cpu = cpu_baseline(wl, case_host, ctx, tokens)
+
+    rec = {"metric": METRIC, "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic",
+           "config": {"workload": wl.name, "batch": B, "past": int(ctx.max()) if wl.past else None,
+                      "ctx_range": list(wl.ctx_range) if wl.ctx_range else None},
+           "hbm_gbs_end_to_end": round(sb * args.steps / elapsed / 1e9, 1),
+           "hbm_frac_end_to_end": round(sb * args.steps / elapsed / 1e9 / HBM_PEAK_GBS, 4),
+           "bytes_per_step": int(sb),
+           "roofline": roofline, "cpu_baseline": cpu}
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,374 @@
+// C ABI of libqd (declared in include/qd.h): argument checks on the host, the
+// workspace plan, and the in-order launch sequence of one decode step on the
+// caller's stream. Nothing here allocates, synchronises or reads device memory.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/qd.h"
+#include "qd_launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+qd_status fail(qd_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+constexpr int kMaxBatch = 16;
+constexpr int kMaxChunk = 256;        // tokens per attention split (LDS score buffer)
+constexpr int kLogitsGridCap = 2048;  // workgroups of the lm_head GEMV = argmax partials per row
+constexpr int kGemvGridCap = 4096;
+constexpr size_t kGemvLds = 60 * 1024;   // dynamic LDS of the GEMV, below the 64 KB launch limit
+
+qd_status check_config(const qd_config* c) {
+    if (!c) return fail(QD_EINVAL, "cfg is NULL");
+    if (c->n_layers < 1 || c->hidden < 8 || c->n_q_heads < 1 || c->n_kv_heads < 1 || c->ffn < 8 ||
+        c->vocab < 1)
+        return fail(QD_ESHAPE, "config sizes must be positive (layers %d hidden %d heads %d/%d ffn %d vocab %d)",
+                    c->n_layers, c->hidden, c->n_q_heads, c->n_kv_heads, c->ffn, c->vocab);
+    if (c->hidden % 8 || c->ffn % 8)
+        return fail(QD_ESHAPE, "hidden (%d) and ffn (%d) must be multiples of 8", c->hidden, c->ffn);
+    if (c->hidden > 16384) return fail(QD_ESHAPE, "hidden %d > 16384", c->hidden);
+    if (c->head_dim != 64 && c->head_dim != 128)
+        return fail(QD_ESHAPE, "head_dim %d not in {64, 128}", c->head_dim);
+    if (c->n_q_heads % c->n_kv_heads)
+        return fail(QD_ESHAPE, "n_q_heads %d not a multiple of n_kv_heads %d", c->n_q_heads, c->n_kv_heads);
+    if (c->n_q_heads / c->n_kv_heads > 8)
+        return fail(QD_ESHAPE, "group %d > 8", c->n_q_heads / c->n_kv_heads);
+    if (c->page_size != 16) return fail(QD_ESHAPE, "page_size %d != 16", c->page_size);
+    if ((c->w_dtype != QD_F32 && c->w_dtype != QD_BF16) || (c->kv_dtype != QD_F32 && c->kv_dtype != QD_BF16))
+        return fail(QD_EINVAL, "dtype out of range (w %d kv %d)", c->w_dtype, c->kv_dtype);
+    if (!(c->rms_eps > 0.f) || !(c->rope_theta > 0.f))
+        return fail(QD_ESHAPE, "rms_eps and rope_theta must be > 0");
+    return QD_OK;
+}
+
+struct DecodePlan {
+    int B, D, Hq, Hkv, hd, G, F, V, qkvr;
+    int chunk, S;
+    size_t off_x, off_qkv, off_q, off_part, off_ctx, off_h, off_logits, off_pv, off_pi, total;
+};
+
+// Attention split: about 512 workgroups over (sequence, kv head, split), each
+// split a whole number of pages and at most kMaxChunk tokens.
+void plan_split(const qd_config* c, int B, int max_tokens, int* chunk, int* S) {
+    const int page = c->page_size;
+    const int pages = (max_tokens + page - 1) / page;
+    int want = (512 + B * c->n_kv_heads - 1) / (B * c->n_kv_heads);
+    if (want < 1) want = 1;
+    int pages_per = (pages + want - 1) / want;
+    if (pages_per < 1) pages_per = 1;
+    if (pages_per * page > kMaxChunk) pages_per = kMaxChunk / page;
+    *chunk = pages_per * page;
+    *S = (max_tokens + *chunk - 1) / *chunk;
+    if (*S < 1) *S = 1;
+}
+
+DecodePlan plan_decode(const qd_config* c, int B, int S, int chunk) {
+    DecodePlan p{};
+    p.B = B; p.D = c->hidden; p.Hq = c->n_q_heads; p.Hkv = c->n_kv_heads; p.hd = c->head_dim;
+    p.G = p.Hq / p.Hkv; p.F = c->ffn; p.V = c->vocab;
+    p.qkvr = (p.Hq + 2 * p.Hkv) * p.hd;
+    p.chunk = chunk; p.S = S;
+    size_t o = 0;
+    auto take = [&](size_t bytes) { size_t at = o; o = round_up(o + bytes, 256); return at; };
+    p.off_x = take(sizeof(float) * B * p.D);
+    p.off_qkv = take(sizeof(float) * B * p.qkvr);
+    p.off_q = take(sizeof(float) * B * p.Hq * p.hd);
+    p.off_part = take(sizeof(float) * (size_t)B * p.Hkv * S * p.G * (p.hd + 2));
+    p.off_ctx = take(sizeof(float) * B * p.Hq * p.hd);
+    p.off_h = take(sizeof(float) * (size_t)B * p.F);
+    p.off_logits = take(sizeof(float) * (size_t)B * p.V);
+    p.off_pv = take(sizeof(float) * B * kLogitsGridCap);
+    p.off_pi = take(sizeof(int) * B * kLogitsGridCap);
+    p.total = o;
+    return p;
+}
+
+int gemv_kt(int B, int K) {
+    int kt = (int)(kGemvLds / (sizeof(float) * (size_t)B));
+    kt = kt / 64 * 64;
+    return kt >= K ? K : kt;
+}
+
+// Optional event timing of selected kernel kinds (qd_profile_*): when a kind is
+// enabled, a HIP event is recorded on the caller's stream just before and just
+// after each of its launches; the pairs are read back only by qd_profile_read.
+constexpr int kProfSlots = 8192;
+struct ProfState {
+    bool ready = false;
+    uint32_t mask = 0;
+    int next = 0;
+    hipEvent_t ev[2 * kProfSlots];
+    int kind[kProfSlots];
+};
+ProfState g_prof;
+
+inline int prof_begin(int kind, hipStream_t s) {
+    if (!(g_prof.mask & (1u << kind)) || g_prof.next >= kProfSlots) return -1;
+    const int slot = g_prof.next++;
+    g_prof.kind[slot] = kind;
+    (void)hipEventRecord(g_prof.ev[2 * slot], s);
+    return slot;
+}
+inline void prof_end(int slot, hipStream_t s) {
+    if (slot >= 0) (void)hipEventRecord(g_prof.ev[2 * slot + 1], s);
+}
+
+#define QD_LAUNCH_K(kind, expr, name)                                                   \
+    do {                                                                               \
+        const int slot_ = prof_begin((kind), s);                                       \
+        hipError_t e_ = (expr);                                                        \
+        prof_end(slot_, s);                                                            \
+        if (e_ != hipSuccess) return fail(QD_EHIP, "%s launch failed: %s", name, hipGetErrorString(e_)); \
+    } while (0)
+#define QD_LAUNCH(expr, name) QD_LAUNCH_K(QD_K_OTHER, expr, name)
+
+qd_status check_layer(const qd_config* c, const qd_layer* L, int l) {
+    const void* need[] = {L->attn_norm, L->wq, L->wk, L->wv, L->wo, L->mlp_norm, L->w_gate, L->w_up, L->w_down};
+    const char* names[] = {"attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_up", "w_down"};
+    for (int i = 0; i < 9; ++i) {
+        if (!need[i]) return fail(QD_EINVAL, "layer %d: %s is NULL", l, names[i]);
+        if (!aligned16(need[i])) return fail(QD_EALIGN, "layer %d: %s not 16-byte aligned", l, names[i]);
+    }
+    if (c->qk_norm && (!L->q_norm || !L->k_norm))
+        return fail(QD_EINVAL, "layer %d: qk_norm set but q_norm/k_norm NULL", l);
+    const void* opt[] = {L->bq, L->bk, L->bv, L->q_norm, L->k_norm};
+    for (const void* p : opt)
+        if (p && !aligned4(p)) return fail(QD_EALIGN, "layer %d: bias/gain not 4-byte aligned", l);
+    return QD_OK;
+}
+
+qd_status check_kv_positions(const qd_config* c, const qd_kv* kv, int B, const int32_t* pos_host,
+                             int* max_tokens) {
+    if (!kv || !kv->k_pages_host || !kv->v_pages_host || !kv->block_table || !kv->block_table_host)
+        return fail(QD_EINVAL, "kv pointers NULL");
+    if (kv->max_blocks < 1 || kv->num_pages < 1)
+        return fail(QD_ESHAPE, "kv max_blocks %d / num_pages %d", kv->max_blocks, kv->num_pages);
+    if (!pos_host) return fail(QD_EINVAL, "pos_host is NULL");
+    const long cap = (long)kv->max_blocks * c->page_size;
+    int mt = 0;
+    for (int b = 0; b < B; ++b) {
+        const int p = pos_host[b];
+        if (p < 0) return fail(QD_EPOSITION, "pos[%d] = %d < 0", b, p);
+        if (p >= cap) return fail(QD_ECAPACITY, "pos[%d] = %d >= block table capacity %ld", b, p, cap);
+        for (int j = 0; j <= p / c->page_size; ++j) {
+            const int pg = kv->block_table_host[(long)b * kv->max_blocks + j];
+            if (pg < 0 || pg >= kv->num_pages)
+                return fail(QD_ECAPACITY, "block_table[%d][%d] = %d outside [0, %d)", b, j, pg, kv->num_pages);
+        }
+        if (p + 1 > mt) mt = p + 1;
+    }
+    *max_tokens = mt;
+    return QD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qd_last_error(void) { return g_err.c_str(); }
+
+int32_t qd_abi_version(void) { return QD_ABI_VERSION; }
+
+size_t qd_workspace_bytes(const qd_config* cfg, int32_t batch, int32_t max_ctx, int32_t prefill_tokens) {
+    if (check_config(cfg) != QD_OK) return 0;
+    if (prefill_tokens > 0) return 0;   // prefill plan added with the MFMA path
+    if (batch < 1 || batch > kMaxBatch || max_ctx < 1) return 0;
+    int chunk, S;
+    plan_split(cfg, batch, max_ctx, &chunk, &S);
+    // the worst case over any positions below max_ctx is the smallest chunk (one page)
+    const int S_worst = (max_ctx + cfg->page_size - 1) / cfg->page_size;
+    return plan_decode(cfg, batch, S_worst > S ? S_worst : S, cfg->page_size).total;
+}
+
+qd_status qd_decode_step(const qd_config* cfg, const qd_weights* w, const qd_kv* kv, int32_t batch,
+                         const int32_t* tokens, const float* x_in, const int32_t* pos,
+                         const int32_t* pos_host, float* logits, int32_t* next_tokens, float* x_out,
+                         float* layer_out, void* workspace, size_t workspace_bytes, void* stream) {
+    g_err.clear();
+    qd_status st = check_config(cfg);
+    if (st != QD_OK) return st;
+    const qd_config& c = *cfg;
+    if (batch < 1 || batch > kMaxBatch) return fail(QD_ESHAPE, "batch %d not in [1, %d]", batch, kMaxBatch);
+    if (!w || !w->layers_host) return fail(QD_EINVAL, "weights or layers_host is NULL");
+    if (!tokens && !x_in) return fail(QD_EINVAL, "tokens and x_in are both NULL");
+    if (tokens && !w->embed) return fail(QD_EINVAL, "tokens given but embed is NULL");
+    if (tokens && !aligned4(tokens)) return fail(QD_EALIGN, "tokens not 4-byte aligned");
+    if (x_in && !aligned4(x_in)) return fail(QD_EALIGN, "x_in not 4-byte aligned");
+    if (!pos) return fail(QD_EINVAL, "pos is NULL");
+    const bool want_head = logits || next_tokens;
+    if (want_head && (!w->final_norm || !w->lm_head))
+        return fail(QD_EINVAL, "logits/next_tokens requested but final_norm or lm_head is NULL");
+    if (want_head && !aligned16(w->lm_head)) return fail(QD_EALIGN, "lm_head not 16-byte aligned");
+    for (int l = 0; l < c.n_layers; ++l)
+        if ((st = check_layer(cfg, &w->layers_host[l], l)) != QD_OK) return st;
+    int max_tokens = 0;
+    if ((st = check_kv_positions(cfg, kv, batch, pos_host, &max_tokens)) != QD_OK) return st;
+    for (int l = 0; l < c.n_layers; ++l) {
+        if (!kv->k_pages_host[l] || !kv->v_pages_host[l])
+            return fail(QD_EINVAL, "kv pages of layer %d NULL", l);
+        if (!aligned16(kv->k_pages_host[l]) || !aligned16(kv->v_pages_host[l]))
+            return fail(QD_EALIGN, "kv pages of layer %d not 16-byte aligned", l);
+    }
+    int chunk, S;
+    plan_split(cfg, batch, max_tokens, &chunk, &S);
+    const DecodePlan P = plan_decode(cfg, batch, S, chunk);
+    if (!workspace) return fail(QD_EWORKSPACE, "workspace is NULL");
+    if (((uintptr_t)workspace & 255u) != 0) return fail(QD_EALIGN, "workspace not 256-byte aligned");
+    if (workspace_bytes < P.total)
+        return fail(QD_EWORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, P.total);
+
+    hipStream_t s = (hipStream_t)stream;
+    char* ws = (char*)workspace;
+    float* x = (float*)(ws + P.off_x);
+    float* qkv = (float*)(ws + P.off_qkv);
+    float* q = (float*)(ws + P.off_q);
+    float* part = (float*)(ws + P.off_part);
+    float* ctx = (float*)(ws + P.off_ctx);
+    float* h = (float*)(ws + P.off_h);
+    float* lg = logits ? logits : (float*)(ws + P.off_logits);
+    float* pv = (float*)(ws + P.off_pv);
+    int* pi = (int*)(ws + P.off_pi);
+    const int wbf = c.w_dtype == QD_BF16, kvbf = c.kv_dtype == QD_BF16;
+    const int B = batch, D = P.D;
+    const int cap = kv->max_blocks * c.page_size;
+
+    if (tokens) QD_LAUNCH_K(QD_K_EMBED, qd::launch_embed(tokens, w->embed, x, B, D, c.vocab, wbf, s), "embed");
+    else QD_LAUNCH(qd::launch_copy(x_in, x, (long)B * D, s), "copy x_in");
+
+    for (int l = 0; l < c.n_layers; ++l) {
+        const qd_layer& L = w->layers_host[l];
+        // RMSNorm -> q|k|v GEMV + bias
+        qd::GemvArgs g{};
+        g.w[0] = L.wq; g.w[1] = L.wk; g.w[2] = L.wv;
+        g.bias[0] = L.bq; g.bias[1] = L.bk; g.bias[2] = L.bv;
+        g.seg_end[0] = P.Hq * P.hd; g.seg_end[1] = (P.Hq + P.Hkv) * P.hd; g.seg_end[2] = P.qkvr;
+        g.nseg = 3; g.N = P.qkvr; g.K = D; g.B = B; g.x = x; g.gain = L.attn_norm; g.eps = c.rms_eps;
+        g.y = qkv; g.kt = gemv_kt(B, D);
+        QD_LAUNCH_K(QD_K_QKV, qd::launch_gemv(g, wbf, qd::EPI_STORE, kGemvGridCap, nullptr, s), "qkv gemv");
+        // [q/k norm] + RoPE + KV append
+        qd::QkvPostArgs qp{};
+        qp.qkv = qkv; qp.q_out = q; qp.k_cache = kv->k_pages_host[l]; qp.v_cache = kv->v_pages_host[l];
+        qp.block_table = kv->block_table; qp.max_blocks = kv->max_blocks; qp.num_pages = kv->num_pages;
+        qp.pos = pos; qp.capacity = cap;
+        qp.q_norm = L.q_norm; qp.k_norm = L.k_norm; qp.qk_norm = c.qk_norm; qp.eps = c.rms_eps;
+        qp.theta = c.rope_theta; qp.Hq = P.Hq; qp.Hkv = P.Hkv; qp.hd = P.hd; qp.page = c.page_size; qp.B = B;
+        QD_LAUNCH_K(QD_K_QKV_POST, qd::launch_qkv_post(qp, wbf, kvbf, s), "qkv post");
+        // split-K attention + merge
+        qd::AttnArgs at{};
+        at.q = q; at.k_cache = kv->k_pages_host[l]; at.v_cache = kv->v_pages_host[l];
+        at.block_table = kv->block_table; at.max_blocks = kv->max_blocks; at.num_pages = kv->num_pages;
+        at.pos = pos; at.capacity = cap;
+        at.part = part; at.ctx = ctx; at.Hq = P.Hq; at.Hkv = P.Hkv; at.hd = P.hd; at.page = c.page_size;
+        at.chunk = P.chunk; at.S = P.S; at.B = B; at.scale = 1.0f / sqrtf((float)P.hd);
+        QD_LAUNCH_K(QD_K_ATTN, qd::launch_attn_decode(at, kvbf, s), "attention");
+        QD_LAUNCH_K(QD_K_MERGE, qd::launch_attn_merge(at, s), "attention merge");
+        // o_proj + residual
+        qd::GemvArgs go{};
+        go.w[0] = L.wo; go.seg_end[0] = go.seg_end[1] = go.seg_end[2] = D; go.nseg = 1;
+        go.N = D; go.K = P.Hq * P.hd; go.B = B; go.x = ctx; go.gain = nullptr; go.y = x;
+        go.kt = gemv_kt(B, go.K);
+        QD_LAUNCH_K(QD_K_O, qd::launch_gemv(go, wbf, qd::EPI_RESID, kGemvGridCap, nullptr, s), "o_proj gemv");
+        // RMSNorm -> gate|up GEMV -> SwiGLU
+        qd::GemvArgs gu{};
+        gu.w[0] = L.w_gate; gu.w[1] = L.w_up; gu.seg_end[0] = gu.seg_end[1] = gu.seg_end[2] = P.F;
+        gu.nseg = 1; gu.N = P.F; gu.K = D; gu.B = B; gu.x = x; gu.gain = L.mlp_norm; gu.eps = c.rms_eps;
+        gu.y = h; gu.kt = gemv_kt(B, D);
+        QD_LAUNCH_K(QD_K_GATEUP, qd::launch_gemv(gu, wbf, qd::EPI_SWIGLU, kGemvGridCap, nullptr, s), "gate/up gemv");
+        // down + residual
+        qd::GemvArgs gd{};
+        gd.w[0] = L.w_down; gd.seg_end[0] = gd.seg_end[1] = gd.seg_end[2] = D; gd.nseg = 1;
+        gd.N = D; gd.K = P.F; gd.B = B; gd.x = h; gd.gain = nullptr; gd.y = x; gd.kt = gemv_kt(B, P.F);
+        QD_LAUNCH_K(QD_K_DOWN, qd::launch_gemv(gd, wbf, qd::EPI_RESID, kGemvGridCap, nullptr, s), "down gemv");
+        if (layer_out) QD_LAUNCH(qd::launch_copy(x, layer_out + (size_t)l * B * D, (long)B * D, s), "layer_out copy");
+    }
+    if (x_out) QD_LAUNCH(qd::launch_copy(x, x_out, (long)B * D, s), "x_out copy");
+    if (want_head) {
+        qd::GemvArgs gl{};
+        gl.w[0] = w->lm_head; gl.seg_end[0] = gl.seg_end[1] = gl.seg_end[2] = c.vocab; gl.nseg = 1;
+        gl.N = c.vocab; gl.K = D; gl.B = B; gl.x = x; gl.gain = w->final_norm; gl.eps = c.rms_eps;
+        gl.y = lg; gl.part_val = pv; gl.part_idx = pi; gl.kt = gemv_kt(B, D);
+        int grid = 0;
+        QD_LAUNCH_K(QD_K_LMHEAD, qd::launch_gemv(gl, wbf, qd::EPI_LOGITS, kLogitsGridCap, &grid, s), "lm_head gemv");
+        if (next_tokens) QD_LAUNCH_K(QD_K_ARGMAX, qd::launch_argmax(pv, pi, grid, next_tokens, B, s), "argmax");
+    }
+    return QD_OK;
+}
+
+int32_t qd_profile_enable(uint32_t kind_mask) {
+    if (!g_prof.ready) {
+        for (int i = 0; i < 2 * kProfSlots; ++i)
+            if (hipEventCreate(&g_prof.ev[i]) != hipSuccess) return fail(QD_EHIP, "hipEventCreate failed");
+        g_prof.ready = true;
+    }
+    g_prof.mask = kind_mask;
+    g_prof.next = 0;
+    return QD_OK;
+}
+
+int32_t qd_profile_read(int32_t kind, int32_t* launches, double* total_ms) {
+    if (!launches || !total_ms) return fail(QD_EINVAL, "launches/total_ms NULL");
+    *launches = 0;
+    *total_ms = 0.0;
+    for (int slot = 0; slot < g_prof.next; ++slot) {
+        if (g_prof.kind[slot] != kind) continue;
+        if (hipEventSynchronize(g_prof.ev[2 * slot + 1]) != hipSuccess)
+            return fail(QD_EHIP, "hipEventSynchronize failed");
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, g_prof.ev[2 * slot], g_prof.ev[2 * slot + 1]) != hipSuccess)
+            return fail(QD_EHIP, "hipEventElapsedTime failed");
+        *launches += 1;
+        *total_ms += ms;
+    }
+    return QD_OK;
+}
+
+void qd_profile_reset(void) { g_prof.next = 0; }
+
+qd_status qd_kv_append(const qd_config* cfg, const qd_kv* kv, int32_t layer_index, int32_t batch,
+                       const int32_t* pos, const int32_t* pos_host, const float* k, const float* v,
+                       void* stream) {
+    g_err.clear();
+    qd_status st = check_config(cfg);
+    if (st != QD_OK) return st;
+    if (batch < 1) return fail(QD_ESHAPE, "batch %d < 1", batch);
+    if (layer_index < 0 || layer_index >= cfg->n_layers)
+        return fail(QD_ESHAPE, "layer_index %d outside [0, %d)", layer_index, cfg->n_layers);
+    if (!k || !v || !pos) return fail(QD_EINVAL, "k, v or pos is NULL");
+    int mt = 0;
+    if ((st = check_kv_positions(cfg, kv, batch, pos_host, &mt)) != QD_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    void* kc = kv->k_pages_host[layer_index];
+    void* vc = kv->v_pages_host[layer_index];
+    if (!kc || !vc) return fail(QD_EINVAL, "kv pages of layer %d NULL", layer_index);
+    QD_LAUNCH(qd::launch_kv_append(k, v, kc, vc, kv->block_table, kv->max_blocks, kv->num_pages, pos,
+                                   kv->max_blocks * cfg->page_size, cfg->n_kv_heads, cfg->head_dim,
+                                   cfg->page_size, batch, cfg->kv_dtype == QD_BF16, s),
+              "kv append");
+    return QD_OK;
+}
+
+qd_status qd_prefill_block(const qd_config* cfg, const qd_layer* layer, int32_t layer_index, const qd_kv* kv,
+                           int32_t n_tokens, int32_t start_pos, const void* x_in, int32_t x_dtype,
+                           float* x_out, void* workspace, size_t workspace_bytes, void* stream) {
+    g_err.clear();
+    (void)cfg; (void)layer; (void)layer_index; (void)kv; (void)n_tokens; (void)start_pos; (void)x_in;
+    (void)x_dtype; (void)x_out; (void)workspace; (void)workspace_bytes; (void)stream;
+    return fail(QD_EUNSUPPORTED, "qd_prefill_block: MFMA prefill path not built yet");
+}
+
+}  // extern "C"

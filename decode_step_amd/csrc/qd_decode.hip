@@ -1,0 +1,564 @@
+// Decode-step kernels for gfx950 (CDNA4, 64-lane wavefronts).
+//
+// Decode at batch 1..16 is HBM-bound: every weight is read once per step and
+// used for B fused multiply-adds. The GEMV streams row-major [out][in] weights
+// with 16-byte loads, LPR lanes sharing one row so each wave load covers
+// 64/LPR rows x LPR*16 contiguous bytes. The activation (with its RMSNorm
+// applied) sits in LDS; each lane's partial dot products are combined with
+// cross-lane shuffles, and the bias / residual / SwiGLU / argmax epilogue runs
+// on the lane holding the total (Tang page, section 2.3: epilogues on the
+// reducing thread; gate|up as one sibling reduction reading the normed input
+// once).
+#include "qd_device.h"
+#include "qd_launch.h"
+
+namespace qd {
+
+constexpr int kGemvThreads = 256;
+constexpr int kGemvUR = 2;     // row groups in flight per lane
+constexpr int kGemvJB = 4;     // 16-byte chunks loaded per lane before use
+
+template <int LPR>
+constexpr int rows_per_tile() { return 4 * (kWave / LPR) * kGemvUR; }
+
+int gemv_rows_per_tile(int K) { return K <= 2048 ? rows_per_tile<16>() : rows_per_tile<64>(); }
+
+template <typename WT, int LPR, int BM, int EPI>
+__global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
+    constexpr int CE = VecN<WT>::n;
+    constexpr int RPW = kWave / LPR;
+    constexpr int UR = kGemvUR;
+    constexpr int RPT = 4 * RPW * UR;
+    constexpr int NW = (EPI == EPI_SWIGLU) ? 2 : 1;
+    extern __shared__ float xs[];          // [B][kt] staged activation
+    __shared__ float rscale[16];
+    __shared__ float red_v[4][16];
+    __shared__ int red_i[4][16];
+
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+    const int li = lane % LPR, slot = lane / LPR;
+    const int B = a.B, K = a.K, N = a.N, kt_max = a.kt;
+
+    if (a.gain) {   // RMSNorm scale of each batch row over the whole K
+        for (int b = wave; b < B; b += 4) {
+            float s = 0.f;
+            for (int k = lane; k < K; k += kWave) { float v = a.x[(long)b * K + k]; s += v * v; }
+            s = group_sum<kWave>(s);
+            if (lane == 0) rscale[b] = 1.0f / sqrtf(s / (float)K + a.eps);
+        }
+        __syncthreads();
+    }
+    auto stage = [&](int k0, int kt) {
+        for (int idx = tid; idx < B * kt; idx += kGemvThreads) {
+            int b = idx / kt, k = idx - b * kt;
+            float v = a.x[(long)b * K + k0 + k];
+            if (a.gain) v = v * rscale[b] * load_scalar<WT>(a.gain, k0 + k);
+            xs[b * kt + k] = v;
+        }
+    };
+    const bool one_pass = kt_max >= K;
+    if (one_pass) { stage(0, K); __syncthreads(); }
+
+    float best_v[BM];
+    int best_i[BM];
+#pragma unroll
+    for (int b = 0; b < BM; ++b) { best_v[b] = -INFINITY; best_i[b] = 0x7fffffff; }
+
+    const int ntiles = (N + RPT - 1) / RPT;
+    for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        float acc[UR][NW][BM];
+        const WT* wp[UR][NW];
+        int rows[UR];
+#pragma unroll
+        for (int u = 0; u < UR; ++u) {
+            rows[u] = tile * RPT + (wave * UR + u) * RPW + slot;
+            const int r = rows[u];
+#pragma unroll
+            for (int n = 0; n < NW; ++n) {
+                wp[u][n] = nullptr;
+#pragma unroll
+                for (int b = 0; b < BM; ++b) acc[u][n][b] = 0.f;
+            }
+            if (r < N) {
+                if (EPI == EPI_SWIGLU) {
+                    wp[u][0] = (const WT*)a.w[0] + (long)r * K;
+                    wp[u][NW - 1] = (const WT*)a.w[1] + (long)r * K;
+                } else {
+                    const bool s0 = r < a.seg_end[0], s1 = r < a.seg_end[1];
+                    const void* wsel = s0 ? a.w[0] : (s1 ? a.w[1] : a.w[2]);
+                    const int base = s0 ? 0 : (s1 ? a.seg_end[0] : a.seg_end[1]);
+                    wp[u][0] = (const WT*)wsel + (long)(r - base) * K;
+                }
+            }
+        }
+        for (int k0 = 0; k0 < K; k0 += kt_max) {
+            const int kt = min(kt_max, K - k0);
+            if (!one_pass) { __syncthreads(); stage(k0, kt); __syncthreads(); }
+            const int nck = kt / CE;
+            for (int c0 = 0; c0 < nck; c0 += LPR * kGemvJB) {
+                uint4 wv[UR][NW][kGemvJB];
+#pragma unroll
+                for (int u = 0; u < UR; ++u)
+#pragma unroll
+                    for (int n = 0; n < NW; ++n)
+#pragma unroll
+                        for (int j = 0; j < kGemvJB; ++j) {
+                            const int c = c0 + li + j * LPR;
+                            if (wp[u][n] && c < nck)
+                                wv[u][n][j] = *(const uint4*)(wp[u][n] + k0 + c * CE);
+                            else
+                                wv[u][n][j] = make_uint4(0, 0, 0, 0);
+                        }
+#pragma unroll
+                for (int j = 0; j < kGemvJB; ++j) {
+                    const int c = c0 + li + j * LPR;
+                    if (c >= nck) break;
+                    float wf[UR][NW][CE];
+#pragma unroll
+                    for (int u = 0; u < UR; ++u)
+#pragma unroll
+                        for (int n = 0; n < NW; ++n) widen16(wv[u][n][j], wf[u][n]);
+#pragma unroll
+                    for (int b = 0; b < BM; ++b) {
+                        if (b >= B) break;
+                        float xv[CE];
+                        const float4* xp = (const float4*)(xs + b * kt + c * CE);
+#pragma unroll
+                        for (int q = 0; q < CE / 4; ++q) {
+                            float4 t = xp[q];
+                            xv[4 * q] = t.x; xv[4 * q + 1] = t.y; xv[4 * q + 2] = t.z; xv[4 * q + 3] = t.w;
+                        }
+#pragma unroll
+                        for (int u = 0; u < UR; ++u)
+#pragma unroll
+                            for (int n = 0; n < NW; ++n)
+#pragma unroll
+                                for (int e = 0; e < CE; ++e)
+                                    acc[u][n][b] = fmaf(wf[u][n][e], xv[e], acc[u][n][b]);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < UR; ++u)
+#pragma unroll
+            for (int n = 0; n < NW; ++n)
+#pragma unroll
+                for (int b = 0; b < BM; ++b) acc[u][n][b] = group_sum<LPR>(acc[u][n][b]);
+
+        if (li == 0) {
+#pragma unroll
+            for (int u = 0; u < UR; ++u) {
+                const int r = rows[u];
+                if (r >= N) continue;
+                float bias = 0.f;
+                if (EPI == EPI_STORE) {
+                    const bool s0 = r < a.seg_end[0], s1 = r < a.seg_end[1];
+                    const void* bsel = s0 ? a.bias[0] : (s1 ? a.bias[1] : a.bias[2]);
+                    const int base = s0 ? 0 : (s1 ? a.seg_end[0] : a.seg_end[1]);
+                    if (bsel) bias = load_scalar<WT>(bsel, r - base);
+                }
+#pragma unroll
+                for (int b = 0; b < BM; ++b) {
+                    if (b >= B) break;
+                    float* yp = a.y + (long)b * N + r;
+                    if (EPI == EPI_STORE) *yp = acc[u][0][b] + bias;
+                    else if (EPI == EPI_RESID) *yp = *yp + acc[u][0][b];
+                    else if (EPI == EPI_SWIGLU) *yp = silu(acc[u][0][b]) * acc[u][NW - 1][b];
+                    else {
+                        *yp = acc[u][0][b];
+                        if (better(acc[u][0][b], r, best_v[b], best_i[b])) {
+                            best_v[b] = acc[u][0][b];
+                            best_i[b] = r;
+                        }
+                    }
+                }
+            }
+        }
+    }
+    if (EPI == EPI_LOGITS) {
+#pragma unroll
+        for (int b = 0; b < BM; ++b) {
+            if (b >= B) break;
+            float v = best_v[b];
+            int i = best_i[b];
+            wave_argmax(v, i);
+            if (lane == 0) { red_v[wave][b] = v; red_i[wave][b] = i; }
+        }
+        __syncthreads();
+        if (tid < B) {
+            float v = red_v[0][tid];
+            int i = red_i[0][tid];
+            for (int w = 1; w < 4; ++w)
+                if (better(red_v[w][tid], red_i[w][tid], v, i)) { v = red_v[w][tid]; i = red_i[w][tid]; }
+            a.part_val[tid * gridDim.x + blockIdx.x] = v;
+            a.part_idx[tid * gridDim.x + blockIdx.x] = i;
+        }
+    }
+}
+
+template <typename WT, int LPR, int BM>
+static hipError_t gemv_dispatch_epi(const GemvArgs& a, int epi, int grid, size_t shm, hipStream_t s) {
+    switch (epi) {
+        case EPI_STORE: hipLaunchKernelGGL((gemv_kernel<WT, LPR, BM, EPI_STORE>), dim3(grid), dim3(kGemvThreads), shm, s, a); break;
+        case EPI_RESID: hipLaunchKernelGGL((gemv_kernel<WT, LPR, BM, EPI_RESID>), dim3(grid), dim3(kGemvThreads), shm, s, a); break;
+        case EPI_SWIGLU: hipLaunchKernelGGL((gemv_kernel<WT, LPR, BM, EPI_SWIGLU>), dim3(grid), dim3(kGemvThreads), shm, s, a); break;
+        default: hipLaunchKernelGGL((gemv_kernel<WT, LPR, BM, EPI_LOGITS>), dim3(grid), dim3(kGemvThreads), shm, s, a); break;
+    }
+    return hipGetLastError();
+}
+
+template <typename WT, int LPR>
+static hipError_t gemv_dispatch_bm(const GemvArgs& a, int epi, int grid, size_t shm, hipStream_t s) {
+    if (a.B <= 1) return gemv_dispatch_epi<WT, LPR, 1>(a, epi, grid, shm, s);
+    if (a.B <= 4) return gemv_dispatch_epi<WT, LPR, 4>(a, epi, grid, shm, s);
+    return gemv_dispatch_epi<WT, LPR, 16>(a, epi, grid, shm, s);
+}
+
+hipError_t launch_gemv(const GemvArgs& a, int w_is_bf16, int epi, int grid_cap, int* grid_out,
+                       hipStream_t s) {
+    const int rpt = gemv_rows_per_tile(a.K);
+    const int tiles = (a.N + rpt - 1) / rpt;
+    const int grid = tiles < grid_cap ? tiles : grid_cap;
+    if (grid_out) *grid_out = grid;
+    const size_t shm = (size_t)a.B * (size_t)(a.kt < a.K ? a.kt : a.K) * sizeof(float);
+    if (a.K <= 2048)
+        return w_is_bf16 ? gemv_dispatch_bm<uint16_t, 16>(a, epi, grid, shm, s)
+                         : gemv_dispatch_bm<float, 16>(a, epi, grid, shm, s);
+    return w_is_bf16 ? gemv_dispatch_bm<uint16_t, 64>(a, epi, grid, shm, s)
+                     : gemv_dispatch_bm<float, 64>(a, epi, grid, shm, s);
+}
+
+// ---------------------------------------------------------------------------
+// q/k per-head RMSNorm (optional), RoPE and the KV append: one wavefront per
+// (head, sequence). Lane i rotates the half-split pair (i, i + hd/2) by
+// pos * theta^(-2i/hd); the angle and its sine/cosine are taken in double and
+// rounded to float. k is stored rotated (nanoinfer page, phase 4: rotate once,
+// on insert); v is stored as projected.
+template <typename WT, typename KVT>
+__global__ __launch_bounds__(64) void qkv_post_kernel(QkvPostArgs a) {
+    const int h = blockIdx.x, b = blockIdx.y, i = threadIdx.x;
+    const int hd = a.hd, half = hd >> 1;
+    const int p = a.pos[b];
+    if (p < 0 || p >= a.capacity) return;
+    const int qkvr = (a.Hq + 2 * a.Hkv) * hd;
+    const bool is_q = h < a.Hq;
+    const float* src = a.qkv + (long)b * qkvr + (is_q ? h * hd : a.Hq * hd + (h - a.Hq) * hd);
+    const bool act = i < half;
+    float lo = act ? src[i] : 0.f, hi = act ? src[i + half] : 0.f;
+    if (a.qk_norm) {
+        const void* g = is_q ? a.q_norm : a.k_norm;
+        float ss = group_sum<kWave>(lo * lo + hi * hi);
+        float r = 1.0f / sqrtf(ss / (float)hd + a.eps);
+        if (act) {
+            lo = lo * r * load_scalar<WT>(g, i);
+            hi = hi * r * load_scalar<WT>(g, i + half);
+        }
+    }
+    if (!act) return;
+    double inv = pow((double)a.theta, -2.0 * (double)i / (double)hd);
+    double sd, cd;
+    sincos((double)p * inv, &sd, &cd);
+    const float c = (float)cd, sn = (float)sd;
+    const float lo2 = lo * c - hi * sn, hi2 = hi * c + lo * sn;
+    if (is_q) {
+        float* q = a.q_out + ((long)b * a.Hq + h) * hd;
+        q[i] = lo2;
+        q[i + half] = hi2;
+    } else {
+        const int g = h - a.Hq;
+        const int page_id = a.block_table[(long)b * a.max_blocks + p / a.page];
+        if (page_id < 0 || page_id >= a.num_pages) return;
+        const long off = (((long)page_id * a.Hkv + g) * a.page + (p % a.page)) * hd;
+        KVT* kc = (KVT*)a.k_cache + off;
+        KVT* vc = (KVT*)a.v_cache + off;
+        const float* vs = a.qkv + (long)b * qkvr + (a.Hq + a.Hkv) * hd + g * hd;
+        kc[i] = from_f32<KVT>(lo2);
+        kc[i + half] = from_f32<KVT>(hi2);
+        vc[i] = from_f32<KVT>(vs[i]);
+        vc[i + half] = from_f32<KVT>(vs[i + half]);
+    }
+}
+
+hipError_t launch_qkv_post(const QkvPostArgs& a, int w_is_bf16, int kv_is_bf16, hipStream_t s) {
+    dim3 grid(a.Hq + a.Hkv, a.B);
+    if (w_is_bf16) {
+        if (kv_is_bf16) hipLaunchKernelGGL((qkv_post_kernel<uint16_t, uint16_t>), grid, dim3(64), 0, s, a);
+        else hipLaunchKernelGGL((qkv_post_kernel<uint16_t, float>), grid, dim3(64), 0, s, a);
+    } else {
+        if (kv_is_bf16) hipLaunchKernelGGL((qkv_post_kernel<float, uint16_t>), grid, dim3(64), 0, s, a);
+        else hipLaunchKernelGGL((qkv_post_kernel<float, float>), grid, dim3(64), 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Split-K decode attention over the paged cache. One workgroup per
+// (split, kv head, sequence) reads each cached K and V row of its chunk once
+// for all `group` query heads that share the KV head (GQA: query head h reads
+// KV head h / group). Within the chunk: scores, chunk max m, l = sum exp(s-m),
+// o = sum exp(s-m) v; the partial (o, m, l) is combined across chunks by the
+// merge kernel (Tang page, section 2.2: online softmax as a monoid; Table 1:
+// split-K). A token attends to itself: the chunk range ends at pos (inclusive).
+constexpr int kAttnThreads = 256;
+constexpr int kMaxGroup = 8;
+constexpr int kMaxChunk = 256;
+
+template <typename KVT, int HD>
+__global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnArgs a) {
+    constexpr int CE = VecN<KVT>::n;
+    constexpr int LPT = HD / CE;          // lanes per token
+    constexpr int TPW = kWave / LPT;      // tokens per wave per pass
+    constexpr int TPB = 4 * TPW;
+    __shared__ float sc[kMaxGroup][kMaxChunk];
+    __shared__ float red[4][kMaxGroup][HD];
+    __shared__ float ml[kMaxGroup][2];
+
+    const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int G = a.Hq / a.Hkv;
+    const int p = a.pos[b];
+    if (p < 0 || p >= a.capacity) return;
+    if (a.chunk > kMaxChunk) return;
+    const int T = p + 1;
+    const int t_begin = s * a.chunk;
+    if (t_begin >= T) return;
+    const int t_end = min(T, t_begin + a.chunk);
+    const int n = t_end - t_begin;
+
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+    const int li = lane % LPT, slot = lane / LPT;
+
+    float qv[kMaxGroup][CE];
+#pragma unroll
+    for (int hl = 0; hl < kMaxGroup; ++hl)
+#pragma unroll
+        for (int e = 0; e < CE; ++e)
+            qv[hl][e] = (hl < G) ? a.q[((long)b * a.Hq + g * G + hl) * HD + li * CE + e] : 0.f;
+
+    const int* bt = a.block_table + (long)b * a.max_blocks;
+    // a page id outside the pool reads as zeros instead of faulting
+    auto load_row = [&](const void* base, int t, float (&f)[CE]) {
+        const int page_id = bt[t / a.page];
+        if (page_id < 0 || page_id >= a.num_pages) {
+#pragma unroll
+            for (int e = 0; e < CE; ++e) f[e] = 0.f;
+            return;
+        }
+        widen16(*(const uint4*)((const KVT*)base +
+                                (((long)page_id * a.Hkv + g) * a.page + (t % a.page)) * HD + li * CE), f);
+    };
+
+    // scores
+    for (int t0 = t_begin; t0 < t_end; t0 += TPB) {
+        const int t = t0 + wave * TPW + slot;
+        float kf[CE];
+        if (t < t_end) load_row(a.k_cache, t, kf);
+        else {
+#pragma unroll
+            for (int e = 0; e < CE; ++e) kf[e] = 0.f;
+        }
+#pragma unroll
+        for (int hl = 0; hl < kMaxGroup; ++hl) {
+            if (hl >= G) break;
+            float d = 0.f;
+#pragma unroll
+            for (int e = 0; e < CE; ++e) d = fmaf(qv[hl][e], kf[e], d);
+            d = group_sum<LPT>(d);
+            if (li == 0 && t < t_end) sc[hl][t - t_begin] = d * a.scale;
+        }
+    }
+    __syncthreads();
+    // chunk max and exp-sum per head
+    for (int hl = wave; hl < G; hl += 4) {
+        float m = -INFINITY;
+        for (int j = lane; j < n; j += kWave) m = fmaxf(m, sc[hl][j]);
+        m = wave_max(m);
+        float l = 0.f;
+        for (int j = lane; j < n; j += kWave) {
+            float e = expf(sc[hl][j] - m);
+            sc[hl][j] = e;
+            l += e;
+        }
+        l = group_sum<kWave>(l);
+        if (lane == 0) { ml[hl][0] = m; ml[hl][1] = l; }
+    }
+    __syncthreads();
+    // o = sum_t p_t v_t
+    float oacc[kMaxGroup][CE];
+#pragma unroll
+    for (int hl = 0; hl < kMaxGroup; ++hl)
+#pragma unroll
+        for (int e = 0; e < CE; ++e) oacc[hl][e] = 0.f;
+    for (int t0 = t_begin; t0 < t_end; t0 += TPB) {
+        const int t = t0 + wave * TPW + slot;
+        if (t < t_end) {
+            float vf[CE];
+            load_row(a.v_cache, t, vf);
+#pragma unroll
+            for (int hl = 0; hl < kMaxGroup; ++hl) {
+                if (hl >= G) break;
+                const float pr = sc[hl][t - t_begin];
+#pragma unroll
+                for (int e = 0; e < CE; ++e) oacc[hl][e] = fmaf(pr, vf[e], oacc[hl][e]);
+            }
+        }
+    }
+    // combine token slots within the wave (lanes li, li+LPT, ...), then across waves
+#pragma unroll
+    for (int hl = 0; hl < kMaxGroup; ++hl) {
+        if (hl >= G) break;
+#pragma unroll
+        for (int e = 0; e < CE; ++e) {
+            float v = oacc[hl][e];
+#pragma unroll
+            for (int off = 32; off >= LPT; off >>= 1) v += __shfl_xor(v, off, kWave);
+            if (slot == 0) red[wave][hl][li * CE + e] = v;
+        }
+    }
+    __syncthreads();
+    float* out = a.part + ((((long)b * a.Hkv + g) * a.S + s) * G) * (HD + 2);
+    for (int idx = tid; idx < G * HD; idx += kAttnThreads) {
+        const int hl = idx / HD, d = idx - hl * HD;
+        out[hl * (HD + 2) + d] = red[0][hl][d] + red[1][hl][d] + red[2][hl][d] + red[3][hl][d];
+    }
+    if (tid < G) {
+        out[tid * (HD + 2) + HD] = ml[tid][0];
+        out[tid * (HD + 2) + HD + 1] = ml[tid][1];
+    }
+}
+
+// Merge of the chunk partials of one (query head, sequence):
+// M = max m_s, ctx = sum_s o_s e^(m_s - M) / sum_s l_s e^(m_s - M).
+__global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a) {
+    const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+    const int HD = a.hd, G = a.Hq / a.Hkv, g = h / G, hl = h - g * G;
+    if (d >= HD) return;
+    const int p = a.pos[b];
+    if (p < 0 || p >= a.capacity) return;
+    const int ns = min(a.S, (p + 1 + a.chunk - 1) / a.chunk);
+    const float* base = a.part + (((long)b * a.Hkv + g) * a.S) * G * (HD + 2) + hl * (HD + 2);
+    const long stride = (long)G * (HD + 2);
+    float M = -INFINITY;
+    for (int s = 0; s < ns; ++s) M = fmaxf(M, base[s * stride + HD]);
+    float L = 0.f, O = 0.f;
+    for (int s = 0; s < ns; ++s) {
+        const float w = expf(base[s * stride + HD] - M);
+        L = fmaf(base[s * stride + HD + 1], w, L);
+        O = fmaf(base[s * stride + d], w, O);
+    }
+    a.ctx[((long)b * a.Hq + h) * HD + d] = O / L;
+}
+
+hipError_t launch_attn_decode(const AttnArgs& a, int kv_is_bf16, hipStream_t s) {
+    dim3 grid(a.S, a.Hkv, a.B);
+    if (a.hd == 64) {
+        if (kv_is_bf16) hipLaunchKernelGGL((attn_decode_kernel<uint16_t, 64>), grid, dim3(kAttnThreads), 0, s, a);
+        else hipLaunchKernelGGL((attn_decode_kernel<float, 64>), grid, dim3(kAttnThreads), 0, s, a);
+    } else {
+        if (kv_is_bf16) hipLaunchKernelGGL((attn_decode_kernel<uint16_t, 128>), grid, dim3(kAttnThreads), 0, s, a);
+        else hipLaunchKernelGGL((attn_decode_kernel<float, 128>), grid, dim3(kAttnThreads), 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_merge(const AttnArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL(attn_merge_kernel, dim3(a.Hq, a.B), dim3(128), 0, s, a);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Embedding gather (exact widen of the row; tied embeddings, nanoinfer page,
+// model notes). An id outside [0, V) yields a zero row instead of a fault.
+template <typename WT>
+__global__ __launch_bounds__(256) void embed_kernel(const int* tokens, const void* embed, float* x,
+                                                    int D, int V) {
+    const int b = blockIdx.x;
+    const int tok = tokens[b];
+    const bool ok = tok >= 0 && tok < V;
+    const void* row = (const char*)embed + (ok ? (long)tok * D * (long)sizeof(WT) : 0L);
+    for (int d = threadIdx.x; d < D; d += blockDim.x)
+        x[(long)b * D + d] = ok ? load_scalar<WT>(row, d) : 0.f;
+}
+
+hipError_t launch_embed(const int* tokens, const void* embed, float* x, int B, int D, int V,
+                        int w_is_bf16, hipStream_t s) {
+    if (w_is_bf16) hipLaunchKernelGGL((embed_kernel<uint16_t>), dim3(B), dim3(256), 0, s, tokens, embed, x, D, V);
+    else hipLaunchKernelGGL((embed_kernel<float>), dim3(B), dim3(256), 0, s, tokens, embed, x, D, V);
+    return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void copy_kernel(const float* src, float* dst, long n) {
+    for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x)
+        dst[i] = src[i];
+}
+
+hipError_t launch_copy(const float* src, float* dst, long n, hipStream_t s) {
+    long blocks = (n + 255) / 256;
+    if (blocks > 1024) blocks = 1024;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks), dim3(256), 0, s, src, dst, n);
+    return hipGetLastError();
+}
+
+// Final greedy argmax over the per-workgroup (value, row) partials of the
+// lm_head; the argmax pair is a monoid (Tang page, section 2.2), lowest row wins ties.
+__global__ __launch_bounds__(256) void argmax_kernel(const float* pv, const int* pi, int nparts, int* out) {
+    __shared__ float sv[4];
+    __shared__ int si[4];
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    float v = -INFINITY;
+    int i = 0x7fffffff;
+    for (int j = tid; j < nparts; j += 256) {
+        const float ov = pv[(long)b * nparts + j];
+        const int oi = pi[(long)b * nparts + j];
+        if (better(ov, oi, v, i)) { v = ov; i = oi; }
+    }
+    wave_argmax(v, i);
+    if (lane == 0) { sv[wave] = v; si[wave] = i; }
+    __syncthreads();
+    if (tid == 0) {
+        for (int w = 1; w < 4; ++w)
+            if (better(sv[w], si[w], sv[0], si[0])) { sv[0] = sv[w]; si[0] = si[w]; }
+        out[b] = si[0];
+    }
+}
+
+hipError_t launch_argmax(const float* part_val, const int* part_idx, int nparts, int* out, int B,
+                         hipStream_t s) {
+    hipLaunchKernelGGL(argmax_kernel, dim3(B), dim3(256), 0, s, part_val, part_idx, nparts, out);
+    return hipGetLastError();
+}
+
+// Store already-rotated k, v ([B][Hkv][hd] float) at positions pos[b].
+template <typename KVT>
+__global__ __launch_bounds__(128) void kv_append_kernel(const float* k, const float* v, void* kc, void* vc,
+                                                        const int* bt, int max_blocks, int num_pages,
+                                                        const int* pos, int capacity, int Hkv, int hd,
+                                                        int page) {
+    const int g = blockIdx.x, b = blockIdx.y;
+    const int p = pos[b];
+    if (p < 0 || p >= capacity) return;
+    const int page_id = bt[(long)b * max_blocks + p / page];
+    if (page_id < 0 || page_id >= num_pages) return;
+    const long off = (((long)page_id * Hkv + g) * page + (p % page)) * hd;
+    for (int d = threadIdx.x; d < hd; d += blockDim.x) {
+        ((KVT*)kc)[off + d] = from_f32<KVT>(k[((long)b * Hkv + g) * hd + d]);
+        ((KVT*)vc)[off + d] = from_f32<KVT>(v[((long)b * Hkv + g) * hd + d]);
+    }
+}
+
+hipError_t launch_kv_append(const float* k, const float* v, void* k_cache, void* v_cache,
+                            const int* block_table, int max_blocks, int num_pages, const int* pos,
+                            int capacity, int Hkv, int hd, int page, int B, int kv_is_bf16,
+                            hipStream_t s) {
+    dim3 grid(Hkv, B);
+    if (kv_is_bf16)
+        hipLaunchKernelGGL((kv_append_kernel<uint16_t>), grid, dim3(128), 0, s, k, v, k_cache, v_cache,
+                           block_table, max_blocks, num_pages, pos, capacity, Hkv, hd, page);
+    else
+        hipLaunchKernelGGL((kv_append_kernel<float>), grid, dim3(128), 0, s, k, v, k_cache, v_cache,
+                           block_table, max_blocks, num_pages, pos, capacity, Hkv, hd, page);
+    return hipGetLastError();
+}
+
+}  // namespace qd

@@ -1,0 +1,76 @@
+// Host-side launchers of the libqd kernels. Each returns hipSuccess or the
+// launch error; shapes are checked by the C-ABI layer before these run.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qd {
+
+enum Epi { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3 };
+
+// y[b][row] (op)= sum_k W[row][k] * xn[b][k], where xn = x, or the RMSNorm of x
+// with `gain` when gain != nullptr. Rows come from up to three row-major
+// segments stacked in order (q/k/v; unused seg_end entries = N); SWIGLU reads row r of w[0] (gate) and of
+// w[1] (up) and stores silu(gate) * up.
+struct GemvArgs {
+    const void* w[3];
+    const void* bias[3];
+    int seg_end[3];
+    int nseg;
+    int N, K, B;
+    const float* x;
+    const void* gain;
+    float eps;
+    float* y;
+    float* part_val;   // EPI_LOGITS: per-(b, workgroup) best value
+    int* part_idx;     //             and its row
+    int kt;            // K elements staged in LDS per pass
+};
+hipError_t launch_gemv(const GemvArgs& a, int w_is_bf16, int epi, int grid_cap, int* grid_out,
+                       hipStream_t s);
+int gemv_rows_per_tile(int K);
+
+struct QkvPostArgs {
+    const float* qkv;       // [B][Hq*hd + 2*Hkv*hd]
+    float* q_out;           // [B][Hq][hd]
+    void* k_cache;
+    void* v_cache;          // page pools [pages][Hkv][page][hd]
+    const int* block_table;
+    int max_blocks, num_pages;
+    const int* pos;
+    int capacity;           // max_blocks * page
+    const void* q_norm;
+    const void* k_norm;
+    int qk_norm;
+    float eps, theta;
+    int Hq, Hkv, hd, page, B;
+};
+hipError_t launch_qkv_post(const QkvPostArgs& a, int w_is_bf16, int kv_is_bf16, hipStream_t s);
+
+struct AttnArgs {
+    const float* q;         // [B][Hq][hd], rotated
+    const void* k_cache;
+    const void* v_cache;
+    const int* block_table;
+    int max_blocks, num_pages;
+    const int* pos;
+    int capacity;
+    float* part;            // [B][Hkv][S][G][hd+2]: o[hd], m, l
+    float* ctx;             // merge output [B][Hq*hd]
+    int Hq, Hkv, hd, page, chunk, S, B;
+    float scale;
+};
+hipError_t launch_attn_decode(const AttnArgs& a, int kv_is_bf16, hipStream_t s);
+hipError_t launch_attn_merge(const AttnArgs& a, hipStream_t s);
+
+hipError_t launch_embed(const int* tokens, const void* embed, float* x, int B, int D, int V,
+                        int w_is_bf16, hipStream_t s);
+hipError_t launch_copy(const float* src, float* dst, long n, hipStream_t s);
+hipError_t launch_argmax(const float* part_val, const int* part_idx, int nparts, int* out, int B,
+                         hipStream_t s);
+hipError_t launch_kv_append(const float* k, const float* v, void* k_cache, void* v_cache,
+                            const int* block_table, int max_blocks, int num_pages, const int* pos,
+                            int capacity, int Hkv, int hd, int page, int B, int kv_is_bf16,
+                            hipStream_t s);
+
+}  // namespace qd

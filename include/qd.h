@@ -1,0 +1,176 @@
+/*
+ * qd.h -- C ABI of the MI355X (gfx950) decode-step library libqd.so.
+ *
+ * One decode forward step of a Qwen2-style grouped-query-attention transformer,
+ * plus the one-block causal prefill and the KV append, as hand-written HIP
+ * kernels enqueued on the caller's stream.
+ *
+ * What is computed (per the pages; each entry point names its passages):
+ *   x = embed[token]                                   (nanoinfer, model notes: tied embeddings)
+ *   per layer (nanoinfer, phase 3: the pre-norm block):
+ *     n = x * (1/sqrt(sum(x^2)/D + eps)) * g_attn       (nanocompile, phase 1: sum then divide)
+ *     q, k, v = W n + b                                 (nanoinfer, model notes: q/k/v biases only)
+ *     [per-head RMSNorm of q and k]                     (8B-class shape only)
+ *     RoPE half-split at position pos[b]                (nanoinfer, phase 3; phase 4: rotate on insert)
+ *     K/V of the new token -> cache slot, then attend   (nanoserve day 49: write before the read)
+ *     o_h = softmax(q_h K_g^T / sqrt(hd)) V_g, g = h / group   (nanoinfer, phase 3: repeat, j <= i)
+ *     x += W_o o ;  n2 = rmsnorm(x) ;  x += W_d (silu(W_g n2) * (W_u n2))
+ *   logits = W_lm rmsnorm(x; g_final) ; next = argmax (lowest index on a tie)
+ * Attention runs as split-K online softmax with a merge (Tang, section 2.2 and
+ * Table 1: online softmax and split reductions are monoids), which changes only
+ * the rounding, not the result.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless the name ends in _host.
+ *   - Matrices are row-major [out][in]; weight dtype from qd_config.w_dtype
+ *     (QD_BF16: raw bf16, QD_F32: float). Biases and gains use the same dtype.
+ *   - The caller owns and allocates everything (weights, KV pages, block table,
+ *     workspace, outputs). The library never allocates device memory, never
+ *     synchronises the stream and never reads device memory back to the host.
+ *   - All work is enqueued in order on `stream` (a hipStream_t passed as void*;
+ *     NULL is the default stream). The call returns once it is enqueued.
+ *   - Arguments are checked on the host BEFORE anything is enqueued; a non-OK
+ *     status means nothing was enqueued (except QD_EHIP, which reports a failed
+ *     launch part-way). qd_last_error() gives a message (thread-local).
+ *   - Faults inside a kernel surface as HIP errors at the caller's next sync.
+ *   - Calls on different streams are independent iff they use different
+ *     workspaces and touch different KV slots.
+ */
+#ifndef QD_H
+#define QD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QD_ABI_VERSION 1
+
+typedef enum {
+    QD_OK = 0,
+    QD_EINVAL = -1,        /* a required pointer is NULL, or an enum is out of range      */
+    QD_ESHAPE = -2,        /* sizes inconsistent or outside the supported set             */
+    QD_EALIGN = -3,        /* a pointer is not 16-byte aligned (128-bit loads)            */
+    QD_ECAPACITY = -4,     /* a position lies beyond the block table or the page pool     */
+    QD_EPOSITION = -5,     /* a position is negative                                       */
+    QD_EWORKSPACE = -6,    /* workspace NULL or smaller than qd_workspace_bytes()         */
+    QD_EUNSUPPORTED = -7,  /* a dtype / option combination that is not implemented        */
+    QD_EHIP = -8           /* a HIP launch failed (message names the kernel)              */
+} qd_status;
+
+typedef enum { QD_F32 = 0, QD_BF16 = 1 } qd_dtype;
+
+/* Model configuration. hidden, ffn and head_dim must be multiples of 8;
+ * n_q_heads must be a multiple of n_kv_heads; head_dim in {64, 128};
+ * page_size in {16}; n_q_heads / n_kv_heads <= 8. */
+typedef struct {
+    int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab, page_size;
+    float rms_eps, rope_theta;
+    int32_t qk_norm;   /* 1: per-head RMSNorm of q and k (gain [head_dim]) before RoPE */
+    int32_t w_dtype;   /* qd_dtype of matrices, biases, gains and the embedding         */
+    int32_t kv_dtype;  /* qd_dtype of the KV cache                                      */
+} qd_config;
+
+/* One decoder layer. Shapes: wq [Hq*hd][D], wk/wv [Hkv*hd][D], wo [D][Hq*hd],
+ * w_gate/w_up [F][D], w_down [D][F]; attn_norm/mlp_norm [D]; bq [Hq*hd],
+ * bk/bv [Hkv*hd] (NULL: no bias); q_norm/k_norm [hd] (used iff qk_norm). */
+typedef struct {
+    const void *attn_norm, *wq, *wk, *wv, *bq, *bk, *bv, *q_norm, *k_norm;
+    const void *wo, *mlp_norm, *w_gate, *w_up, *w_down;
+} qd_layer;
+
+/* Whole-model weights. embed [V][D]; final_norm [D]; lm_head [V][D] or equal to
+ * embed (tied). `layers_host` is a HOST array of n_layers qd_layer structs. */
+typedef struct {
+    const void *embed, *final_norm, *lm_head;
+    const qd_layer *layers_host;
+} qd_weights;
+
+/* Paged KV cache. For each layer l, k_pages_host[l] / v_pages_host[l] are device
+ * pointers to a page pool [num_pages][n_kv_heads][page_size][head_dim] in
+ * kv_dtype. block_table is device int32 [batch][max_blocks]: position p of
+ * sequence b lives in page block_table[b][p / page_size], slot p % page_size
+ * (nanoserve day 49, BlockTable.slot). block_table_host is the same table on the
+ * host; every entry a call touches is checked against [0, num_pages). All layers
+ * share the one table. */
+typedef struct {
+    void *const *k_pages_host;
+    void *const *v_pages_host;
+    const int32_t *block_table;
+    const int32_t *block_table_host;
+    int32_t max_blocks, num_pages;
+} qd_kv;
+
+/* Workspace bytes a call needs: for a decode step over `batch` sequences whose
+ * positions are all < max_ctx (prefill_tokens = 0), or a prefill of
+ * prefill_tokens tokens (batch = 1). Returns 0 if the config is invalid. */
+size_t qd_workspace_bytes(const qd_config *cfg, int32_t batch, int32_t max_ctx,
+                          int32_t prefill_tokens);
+
+/* One decode step for `batch` sequences, one new token each: embedding,
+ * every layer, final norm, lm_head and greedy argmax.
+ *   tokens      [B] int32 token ids, or NULL when x_in is given
+ *   x_in        [B][D] float input of layer 0 (block-only use), or NULL
+ *   pos         [B] int32 device: tokens already cached = position of the new token
+ *   pos_host    [B] int32 host copy of pos, used for checks and work partitioning
+ *   logits      [B][V] float out, or NULL
+ *   next_tokens [B] int32 out (greedy argmax of the logits), or NULL
+ *   x_out       [B][D] float out: the last layer's output (before the final norm), or NULL
+ *   layer_out   [n_layers][B][D] float out: residual stream after each layer, or NULL
+ * The new token's K/V are written into every layer's cache at pos[b] before it
+ * attends over positions 0..pos[b]; re-running at the same pos is idempotent.
+ * lm_head / final_norm may be NULL only when logits and next_tokens are NULL. */
+qd_status qd_decode_step(const qd_config *cfg, const qd_weights *w, const qd_kv *kv,
+                         int32_t batch, const int32_t *tokens, const float *x_in,
+                         const int32_t *pos, const int32_t *pos_host,
+                         float *logits, int32_t *next_tokens, float *x_out, float *layer_out,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/* One decoder block over n_tokens consecutive tokens of sequence 0 of the block
+ * table, at positions start_pos .. start_pos + n_tokens - 1, causal (row i
+ * attends to positions 0..start_pos+i). bf16 weights only: the projections are
+ * MFMA bf16 matrix products with float accumulation, their activation operands
+ * rounded to bf16. x_in [N][D] in x_dtype (QD_BF16 or QD_F32); x_out [N][D] float.
+ * K/V of all N tokens are written into layer `layer`'s cache. */
+qd_status qd_prefill_block(const qd_config *cfg, const qd_layer *layer, int32_t layer_index,
+                           const qd_kv *kv, int32_t n_tokens, int32_t start_pos,
+                           const void *x_in, int32_t x_dtype, float *x_out,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/* Store already-rotated k and v ([B][Hkv][hd] float) of `batch` sequences at
+ * positions pos[b] of layer `layer_index`, in the cache dtype (bf16: round half
+ * to even; nanoinfer, phase 1). nanoinfer, phase 4: keys are rotated once, on
+ * insert; this call only stores. */
+qd_status qd_kv_append(const qd_config *cfg, const qd_kv *kv, int32_t layer_index,
+                       int32_t batch, const int32_t *pos, const int32_t *pos_host,
+                       const float *k, const float *v, void *stream);
+
+/* Kernel kinds for the optional event timing below. */
+typedef enum {
+    QD_K_EMBED = 0, QD_K_QKV = 1, QD_K_QKV_POST = 2, QD_K_ATTN = 3, QD_K_MERGE = 4,
+    QD_K_O = 5, QD_K_GATEUP = 6, QD_K_DOWN = 7, QD_K_LMHEAD = 8, QD_K_ARGMAX = 9,
+    QD_K_PREFILL_GEMM = 10, QD_K_PREFILL_ATTN = 11, QD_K_OTHER = 12
+} qd_kernel_kind;
+
+/* Measurement hook, off by default: while bit k of kind_mask is set, every launch
+ * of kernel kind k records a HIP event on the call's stream just before and just
+ * after it (process-wide, up to 8192 launches until the next enable or reset).
+ * qd_profile_read waits for those events and returns the number of timed launches
+ * of `kind` and their summed durations in milliseconds. Not thread-safe; meant
+ * for benchmarks. The first enable creates the events (no device allocation). */
+int32_t qd_profile_enable(uint32_t kind_mask);
+int32_t qd_profile_read(int32_t kind, int32_t *launches, double *total_ms);
+void qd_profile_reset(void);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char *qd_last_error(void);
+
+/* QD_ABI_VERSION of the loaded library. */
+int32_t qd_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QD_H */

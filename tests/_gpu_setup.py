@@ -1,0 +1,61 @@
+"""Shared set-up for the GPU parity tests: seeded inputs drawn once on the
+device, the libqd runner over them, and host copies for the oracle."""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+from workloads import synth
+
+
+def rel_err(got, ref) -> float:
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    return float(np.max(np.abs(got - ref)) / max(np.max(np.abs(ref)), 1e-300))
+
+
+@dataclass
+class Case:
+    shape: object
+    w: dict
+    kv: object
+    runner: object
+    host_w: dict
+    k_host: list
+    v_host: list
+    ctx: np.ndarray
+
+
+def make_case(shape, ctx, seed=0, extra=4, random_order=False, max_batch=None, device="cuda",
+              gain_mode="one_plus", prefill_tokens=0) -> Case:
+    from decode_step_amd.runner import DecodeRunner
+    ctx = np.asarray(ctx, dtype=np.int32)
+    w = synth.make_weights(shape, seed=seed, device=device, gain_mode=gain_mode)
+    kv = synth.make_kv(shape, ctx, extra=extra, seed=seed, device=device, random_order=random_order)
+    B = len(ctx) if max_batch is None else max_batch
+    runner = DecodeRunner(shape, w, kv.k, kv.v, kv.block_table, max_batch=B,
+                          max_ctx=int(ctx.max()) + extra + 1, device=device,
+                          prefill_tokens=prefill_tokens)
+    host_w = synth.weights_to_host(w)
+    kh = [synth.to_host_bits(t).copy() for t in kv.k]
+    vh = [synth.to_host_bits(t).copy() for t in kv.v]
+    return Case(shape, w, kv, runner, host_w, kh, vh, ctx)
+
+
+def dev_i32(a, device="cuda") -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
+
+
+def guarded(n: int, device="cuda", pad: int = 1024, fill=float("nan")):
+    """A float buffer of n elements between two canary regions; returns (full, view)."""
+    full = torch.full((n + 2 * pad,), fill, dtype=torch.float32, device=device)
+    full[:pad] = 12345.0
+    full[pad + n:] = 12345.0
+    return full, full[pad:pad + n]
+
+
+def canaries_intact(full: torch.Tensor, n: int, pad: int = 1024) -> bool:
+    f = full.cpu()
+    return bool(torch.all(f[:pad] == 12345.0)) and bool(torch.all(f[pad + n:] == 12345.0))

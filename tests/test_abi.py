@@ -1,0 +1,189 @@
+"""C-ABI checks that need no GPU: the library loads and exports every symbol the
+header declares, the ctypes structs match the C layout, and every host-checkable
+argument error returns its own status before anything is enqueued (the fake
+device addresses below are never dereferenced: checks fail first).
+"""
+import ctypes
+import os
+import re
+import subprocess
+from ctypes import POINTER, c_int32, c_void_p
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qd.h")
+
+Q = pytest.importorskip("decode_step_amd.qd")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(Q.LIB_PATH):
+        from decode_step_amd import build as B
+        B.build()
+    return Q.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qd_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ["qd_decode_step", "qd_prefill_block", "qd_kv_append", "qd_workspace_bytes",
+              "qd_last_error", "qd_abi_version"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", Q.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT\s+(qd_\w+)", out))
+    for n in declared_functions():
+        assert n in exported, n
+        assert hasattr(lib, n)
+    assert lib.qd_abi_version() == 1
+
+
+def test_struct_layout_matches_the_header(tmp_path):
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "qd.h"\n'
+                   'int main(void){printf("%zu %zu %zu %zu %zu %zu\\n", sizeof(qd_config),'
+                   ' sizeof(qd_layer), sizeof(qd_weights), sizeof(qd_kv),'
+                   ' offsetof(qd_kv, max_blocks), offsetof(qd_config, rms_eps)); return 0;}\n')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)], check=True)
+    got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True).stdout.split()]
+    want = [ctypes.sizeof(Q.qd_config), ctypes.sizeof(Q.qd_layer), ctypes.sizeof(Q.qd_weights),
+            ctypes.sizeof(Q.qd_kv), Q.qd_kv.max_blocks.offset, Q.qd_config.rms_eps.offset]
+    assert got == want
+
+
+# ---------------------------------------------------------------- host-side errors
+
+FAKE = 0x7f0000000000   # 16-byte aligned, never dereferenced
+
+
+def _cfg(**over):
+    d = dict(n_layers=1, hidden=64, n_q_heads=4, n_kv_heads=2, head_dim=64, ffn=96, vocab=100,
+             page_size=16, rms_eps=1e-6, rope_theta=1e6, qk_norm=0, w_dtype=Q.QD_BF16,
+             kv_dtype=Q.QD_BF16)
+    d.update(over)
+    return Q.qd_config(**d)
+
+
+class Fixture:
+    def __init__(self, cfg, pos=(5,), table=None, num_pages=4, max_blocks=2):
+        self.cfg = cfg
+        L = cfg.n_layers
+        self.layers = (Q.qd_layer * L)()
+        for l in range(L):
+            for i, n in enumerate(Q.LAYER_FIELDS):
+                if n not in ("bq", "bk", "bv", "q_norm", "k_norm"):
+                    setattr(self.layers[l], n, FAKE + 4096 * i)
+        self.w = Q.qd_weights(FAKE, FAKE, FAKE, ctypes.cast(self.layers, POINTER(Q.qd_layer)))
+        self.kp = (c_void_p * L)(*([FAKE] * L))
+        self.vp = (c_void_p * L)(*([FAKE] * L))
+        B = len(pos)
+        t = np.zeros((B, max_blocks), np.int32) if table is None else np.asarray(table, np.int32)
+        self.table = np.ascontiguousarray(t)
+        self.kv = Q.qd_kv(ctypes.cast(self.kp, POINTER(c_void_p)), ctypes.cast(self.vp, POINTER(c_void_p)),
+                          FAKE, self.table.ctypes.data_as(POINTER(c_int32)), max_blocks, num_pages)
+        self.pos = np.ascontiguousarray(pos, np.int32)
+
+    def decode(self, batch=None, tokens=FAKE, x_in=None, ws=FAKE, ws_bytes=1 << 40, logits=FAKE,
+               pos_host=True):
+        B = len(self.pos) if batch is None else batch
+        ph = self.pos.ctypes.data_as(POINTER(c_int32)) if pos_host else None
+        return Q.qd_decode_step(self.cfg, self.w, self.kv, B, tokens, x_in, FAKE, ph, logits, None,
+                                None, None, ws, ws_bytes, None)
+
+
+def _expect(status, what):
+    assert status == what, (Q.STATUS_NAMES.get(status), Q.qd_last_error())
+    assert Q.qd_last_error() != ""
+
+
+def test_null_config(lib):
+    f = Fixture(_cfg())
+    st = lib.qd_decode_step(None, ctypes.byref(f.w), ctypes.byref(f.kv), 1, FAKE, None, FAKE,
+                            f.pos.ctypes.data_as(POINTER(c_int32)), FAKE, None, None, None, FAKE,
+                            1 << 40, None)
+    _expect(st, Q.QD_EINVAL)
+
+
+@pytest.mark.parametrize("over", [dict(head_dim=96), dict(hidden=60), dict(n_q_heads=5),
+                                  dict(n_q_heads=18, n_kv_heads=2), dict(page_size=32),
+                                  dict(n_layers=0)])
+def test_bad_shapes(lib, over):
+    _expect(Fixture(_cfg(**over)).decode(), Q.QD_ESHAPE)
+
+
+def test_bad_dtype(lib):
+    _expect(Fixture(_cfg(w_dtype=7)).decode(), Q.QD_EINVAL)
+
+
+def test_batch_out_of_range(lib):
+    _expect(Fixture(_cfg()).decode(batch=0), Q.QD_ESHAPE)
+    _expect(Fixture(_cfg(), pos=[1] * 17, max_blocks=1).decode(), Q.QD_ESHAPE)
+
+
+def test_negative_position(lib):
+    _expect(Fixture(_cfg(), pos=(-1,)).decode(), Q.QD_EPOSITION)
+
+
+def test_position_beyond_table(lib):
+    _expect(Fixture(_cfg(), pos=(32,), max_blocks=2).decode(), Q.QD_ECAPACITY)
+
+
+def test_block_table_entry_out_of_pool(lib):
+    _expect(Fixture(_cfg(), pos=(20,), table=[[0, 9]], num_pages=4).decode(), Q.QD_ECAPACITY)
+    _expect(Fixture(_cfg(), pos=(3,), table=[[-1, 0]], num_pages=4).decode(), Q.QD_ECAPACITY)
+
+
+def test_workspace_checks(lib):
+    f = Fixture(_cfg())
+    _expect(f.decode(ws=None), Q.QD_EWORKSPACE)
+    _expect(f.decode(ws_bytes=1024), Q.QD_EWORKSPACE)
+    _expect(f.decode(ws=FAKE + 16), Q.QD_EALIGN)
+
+
+def test_misaligned_weight(lib):
+    f = Fixture(_cfg())
+    f.layers[0].wq = FAKE + 2
+    _expect(f.decode(), Q.QD_EALIGN)
+
+
+def test_missing_inputs(lib):
+    f = Fixture(_cfg())
+    _expect(f.decode(tokens=None, x_in=None), Q.QD_EINVAL)
+    _expect(f.decode(pos_host=False), Q.QD_EINVAL)
+    f.layers[0].w_up = None
+    _expect(f.decode(), Q.QD_EINVAL)
+
+
+def test_qk_norm_needs_gains(lib):
+    _expect(Fixture(_cfg(qk_norm=1)).decode(), Q.QD_EINVAL)
+
+
+def test_workspace_bytes(lib):
+    cfg = _cfg()
+    a = Q.qd_workspace_bytes(cfg, 1, 512)
+    b = Q.qd_workspace_bytes(cfg, 16, 4097)
+    assert 0 < a < b
+    assert Q.qd_workspace_bytes(_cfg(head_dim=96), 1, 512) == 0
+    assert Q.qd_workspace_bytes(cfg, 0, 512) == 0
+
+
+def test_kv_append_checks(lib):
+    f = Fixture(_cfg())
+    ph = f.pos.ctypes.data_as(POINTER(c_int32))
+    _expect(Q.qd_kv_append(f.cfg, f.kv, 3, 1, FAKE, ph, FAKE, FAKE, None), Q.QD_ESHAPE)
+    _expect(Q.qd_kv_append(f.cfg, f.kv, 0, 1, FAKE, ph, None, FAKE, None), Q.QD_EINVAL)
+    f2 = Fixture(_cfg(), pos=(40,))
+    _expect(Q.qd_kv_append(f2.cfg, f2.kv, 0, 1, FAKE, f2.pos.ctypes.data_as(POINTER(c_int32)),
+                           FAKE, FAKE, None), Q.QD_ECAPACITY)

@@ -1,0 +1,239 @@
+"""GPU parity of the decode step (qd_decode_step through the C ABI) against the
+fp64 CPU oracle, on the same seeded inputs.
+
+Tolerances (max |gpu - ref| / max |ref| per tensor): 1e-4 for the fp32 block,
+2e-3 for bf16 weights/KV; greedy token ids identical. Shapes: a small ragged
+model (several GEMV tiles plus a ragged tail, positions on and around page
+boundaries, position 0), the fp32 Qwen2 block at past 16, the full 24-layer
+0.5B step at past 512 with a 32-step greedy run, batch 16 with per-sequence
+context in [128, 4096] over a random paged block table, and the 8B-class shape
+with per-head q/k RMSNorm at past 4096.
+"""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+from oracle.qwen2 import OracleWeights, decode_step
+from workloads import shapes as S
+from workloads import synth
+from tests._gpu_setup import make_case, dev_i32, rel_err, guarded, canaries_intact
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+SMALL = S.ModelShape(n_layers=2, hidden=136, n_q_heads=4, n_kv_heads=2, head_dim=64, ffn=264,
+                     vocab=1000)
+
+
+def _run_step(case, pos, tokens=None, x_in=None, want_layers=True):
+    sh = case.shape
+    B = len(pos)
+    logits = torch.full((B, sh.vocab), float("nan"), device="cuda")
+    nxt = torch.full((B,), -1, dtype=torch.int32, device="cuda")
+    layer_out = torch.full((sh.n_layers, B, sh.hidden), float("nan"), device="cuda") if want_layers else None
+    x_out = torch.full((B, sh.hidden), float("nan"), device="cuda")
+    tok_d = dev_i32(tokens) if tokens is not None else None
+    case.runner.step(np.asarray(pos, np.int32), dev_i32(pos), tokens=tok_d, x_in=x_in,
+                     logits=logits if x_in is None else None, next_tokens=nxt if x_in is None else None,
+                     x_out=x_out, layer_out=layer_out)
+    torch.cuda.synchronize()
+    return logits, nxt, x_out, layer_out
+
+
+def _oracle(case, pos, tokens=None, x_in=None, with_logits=True, cache_layers=True):
+    ow = OracleWeights(case.shape, case.host_w, cache_layers=cache_layers)
+    return decode_step(case.shape, ow, case.k_host, case.v_host, case.kv.block_table,
+                       np.asarray(pos), tokens=tokens, x_in=x_in, with_logits=with_logits)
+
+
+def _cache_matches(case, f32_tol=1e-5):
+    """Every stored K/V equals the oracle's: within one bf16 unit in the last place
+    (the float32 value the GPU rounds may sit on the other side of a rounding
+    boundary from the oracle's), or within f32_tol relative for a float32 cache."""
+    for l in range(case.shape.n_layers):
+        for dev, host in ((case.kv.k[l], case.k_host[l]), (case.kv.v[l], case.v_host[l])):
+            g = synth.to_host_bits(dev)
+            if g.dtype == np.uint16:
+                d = np.abs(g.view(np.int16).astype(np.int32) - host.view(np.int16).astype(np.int32))
+                if d.max() > 1:
+                    return False
+            elif rel_err(g, host) > f32_tol:
+                return False
+    return True
+
+
+# ---------------------------------------------------------------- small ragged model
+
+@pytest.mark.parametrize("w_dtype,kv_dtype,tol", [("bf16", "bf16", 2e-3), ("f32", "f32", 1e-4),
+                                                  ("bf16", "f32", 2e-3)])
+def test_small_ragged_batch(w_dtype, kv_dtype, tol):
+    shape = replace(SMALL, w_dtype=w_dtype, kv_dtype=kv_dtype)
+    ctx = np.array([0, 15, 16, 17, 100, 255, 33], np.int32)
+    case = make_case(shape, ctx, seed=11, random_order=True)
+    tok = synth.make_tokens(len(ctx), shape.vocab, seed=11)
+    logits, nxt, x_out, layer_out = _run_step(case, ctx, tokens=tok)
+    ref = _oracle(case, ctx, tokens=tok)
+    assert rel_err(logits.cpu().numpy(), ref.logits) <= tol
+    assert rel_err(layer_out.cpu().numpy(), ref.layer_out) <= tol
+    assert rel_err(x_out.cpu().numpy(), ref.x_out) <= tol
+    assert list(nxt.cpu().numpy()) == list(ref.next_tokens)
+    assert _cache_matches(case)
+
+
+def test_small_qk_norm_no_bias_untied():
+    shape = replace(SMALL, qkv_bias=False, qk_norm=True, tied=False, n_q_heads=8, n_kv_heads=2,
+                    head_dim=128)
+    ctx = np.array([3, 64, 130], np.int32)
+    case = make_case(shape, ctx, seed=12, random_order=True)
+    tok = synth.make_tokens(len(ctx), shape.vocab, seed=12)
+    logits, nxt, _, layer_out = _run_step(case, ctx, tokens=tok)
+    ref = _oracle(case, ctx, tokens=tok)
+    assert rel_err(logits.cpu().numpy(), ref.logits) <= 2e-3
+    assert rel_err(layer_out.cpu().numpy(), ref.layer_out) <= 2e-3
+    assert list(nxt.cpu().numpy()) == list(ref.next_tokens)
+
+
+def test_position_zero_returns_v():
+    """One cached token (the new one): attention output is the stored v exactly, so the
+    block output equals the oracle's to fp32 rounding of the GEMVs."""
+    shape = replace(SMALL, n_layers=1, w_dtype="f32", kv_dtype="f32")
+    case = make_case(shape, np.array([0]), seed=3)
+    x = synth.make_x(1, shape.hidden, seed=3, device="cuda")
+    _, _, x_out, _ = _run_step(case, [0], x_in=x)
+    ref = _oracle(case, [0], x_in=synth.to_host_bits(x), with_logits=False)
+    assert rel_err(x_out.cpu().numpy(), ref.x_out) <= 1e-5
+
+
+def test_outputs_guarded_and_deterministic():
+    shape = SMALL
+    ctx = np.array([40, 7], np.int32)
+    case = make_case(shape, ctx, seed=5, random_order=True)
+    tok = dev_i32(synth.make_tokens(2, shape.vocab, seed=5))
+    n = 2 * shape.vocab
+    outs = []
+    for _ in range(2):
+        full, view = guarded(n)
+        nxt = torch.full((2,), -1, dtype=torch.int32, device="cuda")
+        case.runner.step(ctx, dev_i32(ctx), tokens=tok, logits=view.view(2, shape.vocab), next_tokens=nxt)
+        torch.cuda.synchronize()
+        assert canaries_intact(full, n)
+        assert not torch.isnan(view).any()
+        outs.append((view.cpu().clone(), nxt.cpu().clone()))
+    # same position twice: idempotent and bitwise deterministic (no float atomics)
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+def test_kv_append_matches_oracle_rounding():
+    from oracle.numerics import store_kv
+    shape = replace(SMALL, n_layers=1)
+    ctx = np.array([5, 31, 200], np.int32)
+    case = make_case(shape, ctx, seed=9, random_order=True)
+    k = torch.randn(3, shape.n_kv_heads, shape.head_dim, device="cuda")
+    v = torch.randn(3, shape.n_kv_heads, shape.head_dim, device="cuda")
+    case.runner.kv_append(0, ctx, dev_i32(ctx), k, v)
+    torch.cuda.synchronize()
+    kg = synth.to_host_bits(case.kv.k[0])
+    vg = synth.to_host_bits(case.kv.v[0])
+    kh, vh = k.cpu().numpy(), v.cpu().numpy()
+    bt = case.kv.block_table
+    for b, p in enumerate(ctx):
+        pg, sl = bt[b, p // 16], p % 16
+        assert np.array_equal(kg[pg, :, sl, :], store_kv(kh[b], "bf16"))
+        assert np.array_equal(vg[pg, :, sl, :], store_kv(vh[b], "bf16"))
+
+
+# ---------------------------------------------------------------- full-size workloads
+
+@pytest.mark.timeout(300)
+def test_qwen2_block_f32_past16():
+    wl = S.QWEN2_BLOCK_F32_PAST16
+    ctx = np.array([wl.past], np.int32)
+    case = make_case(wl.shape, ctx, seed=wl.seed)
+    x = synth.make_x(1, wl.shape.hidden, seed=wl.seed, device="cuda")
+    _, _, x_out, layer_out = _run_step(case, ctx, x_in=x)
+    ref = _oracle(case, ctx, x_in=synth.to_host_bits(x), with_logits=False)
+    assert rel_err(x_out.cpu().numpy(), ref.x_out) <= 1e-4
+    assert _cache_matches(case)
+
+
+@pytest.mark.timeout(600)
+def test_qwen2_0p5b_b1_past512_and_32_greedy_steps():
+    wl = S.QWEN2_0P5B_B1_PAST512
+    sh = wl.shape
+    ctx = np.array([wl.past], np.int32)
+    case = make_case(sh, ctx, seed=wl.seed, extra=wl.greedy_steps + 1)
+    tok0 = synth.make_tokens(1, sh.vocab, seed=wl.seed, name="tok0")
+    # step 1: full comparison of logits and every layer's output
+    logits, nxt, _, layer_out = _run_step(case, ctx, tokens=tok0)
+    ow = OracleWeights(sh, case.host_w, cache_layers=True)
+    ref = decode_step(sh, ow, case.k_host, case.v_host, case.kv.block_table, ctx, tokens=tok0)
+    assert rel_err(logits.cpu().numpy(), ref.logits) <= 2e-3
+    for l in range(sh.n_layers):
+        assert rel_err(layer_out[l].cpu().numpy(), ref.layer_out[l]) <= 2e-3, l
+    gpu_tokens, ref_tokens = [int(nxt.cpu()[0])], [int(ref.next_tokens[0])]
+    # steps 2..32: each side feeds back its own argmax
+    pos = ctx.copy()
+    tok_d = nxt.clone()
+    lg = torch.empty(1, sh.vocab, device="cuda")
+    worst = 0.0
+    for step in range(1, wl.greedy_steps):
+        pos = pos + 1
+        nxt_d = torch.empty(1, dtype=torch.int32, device="cuda")
+        case.runner.step(pos, dev_i32(pos), tokens=tok_d, logits=lg, next_tokens=nxt_d)
+        r = decode_step(sh, ow, case.k_host, case.v_host, case.kv.block_table, pos,
+                        tokens=np.array(ref_tokens[-1:], np.int32))
+        torch.cuda.synchronize()
+        worst = max(worst, rel_err(lg.cpu().numpy(), r.logits))
+        gpu_tokens.append(int(nxt_d.cpu()[0]))
+        ref_tokens.append(int(r.next_tokens[0]))
+        tok_d = nxt_d
+    print(f"32-step greedy: worst logits rel err {worst:.3e}; tokens {gpu_tokens}")
+    assert gpu_tokens == ref_tokens
+    assert worst <= 2e-3
+
+
+@pytest.mark.timeout(600)
+def test_qwen2_0p5b_b16_paged_random_ctx():
+    wl = S.QWEN2_0P5B_B16_PAGED
+    sh = wl.shape
+    ctx = synth.make_ctx(wl.batch, None, wl.ctx_range, wl.seed)
+    case = make_case(sh, ctx, seed=wl.seed, extra=wl.greedy_steps + 1, random_order=True)
+    tok = synth.make_tokens(wl.batch, sh.vocab, seed=wl.seed)
+    logits, nxt, _, layer_out = _run_step(case, ctx, tokens=tok)
+    ow = OracleWeights(sh, case.host_w, cache_layers=True)
+    ref = decode_step(sh, ow, case.k_host, case.v_host, case.kv.block_table, ctx, tokens=tok)
+    assert rel_err(logits.cpu().numpy(), ref.logits) <= 2e-3
+    assert rel_err(layer_out.cpu().numpy(), ref.layer_out) <= 2e-3
+    assert list(nxt.cpu().numpy()) == list(ref.next_tokens)
+    # a few greedy steps for all 16 sequences
+    pos, tok_d, ref_tok = ctx.copy(), nxt.clone(), ref.next_tokens.copy()
+    for _ in range(wl.greedy_steps - 1):
+        pos = pos + 1
+        nd = torch.empty(wl.batch, dtype=torch.int32, device="cuda")
+        case.runner.step(pos, dev_i32(pos), tokens=tok_d, next_tokens=nd)
+        r = decode_step(sh, ow, case.k_host, case.v_host, case.kv.block_table, pos, tokens=ref_tok)
+        torch.cuda.synchronize()
+        assert list(nd.cpu().numpy()) == list(r.next_tokens)
+        tok_d, ref_tok = nd, r.next_tokens
+
+
+@pytest.mark.timeout(900)
+def test_qwen_8b_qknorm_b1_past4096():
+    wl = S.QWEN_8B_B1_PAST4096
+    sh = wl.shape
+    ctx = np.array([wl.past], np.int32)
+    case = make_case(sh, ctx, seed=wl.seed, extra=2)
+    tok = synth.make_tokens(1, sh.vocab, seed=wl.seed, name="tok0")
+    logits, nxt, _, layer_out = _run_step(case, ctx, tokens=tok)
+    ref = _oracle(case, ctx, tokens=tok, cache_layers=False)
+    assert rel_err(logits.cpu().numpy(), ref.logits) <= 2e-3
+    assert rel_err(layer_out.cpu().numpy(), ref.layer_out) <= 2e-3
+    assert int(nxt.cpu()[0]) == int(ref.next_tokens[0])
