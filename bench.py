@@ -2,7 +2,8 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
-A step is one qd_decode_step call: embedding, every layer (fused RMSNorm + QKV
+A step is one qd_decode_step call (timed as a HIP-graph replay of that call,
+captured once; the eager-launch rate is reported beside it): embedding, every layer (fused RMSNorm + QKV
 GEMV, q/k norm + RoPE + KV append, split-K attention + merge, o_proj + residual,
 RMSNorm + gate/up + SwiGLU, down + residual), final norm, lm_head and greedy
 argmax, for one batch of synthetic input already resident in HBM. Each step
@@ -105,6 +106,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="qwen2-0.5b-bf16-b1-past512")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replay")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -133,23 +135,44 @@ def main():
     pos_d = torch.from_numpy(ctx).to(dev)
     logits = torch.empty(B, shape.vocab, device=dev)
     nxt = torch.empty(B, dtype=torch.int32, device=dev)
-    stream = torch.cuda.current_stream()
-
     def step():
-        runner.step(ctx, pos_d, tokens=tok_d, logits=logits, next_tokens=nxt, stream=stream)
+        runner.step(ctx, pos_d, tokens=tok_d, logits=logits, next_tokens=nxt,
+                    stream=torch.cuda.current_stream())
 
+    def timed(fn, k):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(k):
+            fn()
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    sb = step_bytes(shape, B, ctx)
+    # eager launches (one qd_decode_step call per step)
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    el_eager = timed(step, args.steps)
+    print(f"[bench] {wl.name} eager: {1e3 * el_eager / args.steps:.4f} ms/step, "
+          f"{B * args.steps / el_eager:.1f} tokens/s", file=sys.stderr, flush=True)
+    # the same call captured once in a HIP graph and replayed (NEXT-2: one launch per step)
+    graph = None
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(args.warmup):
+            graph.replay()
+        elapsed = timed(graph.replay, args.steps)
+    else:
+        elapsed = el_eager
     ms_per_step = 1e3 * elapsed / args.steps
     tok_s = B * args.steps / elapsed
-    sb = step_bytes(shape, B, ctx)
-    print(f"[bench] {wl.name}: {ms_per_step:.4f} ms/step, {tok_s:.1f} tokens/s, "
+    print(f"[bench] {wl.name} {'graph' if graph else 'eager'}: {ms_per_step:.4f} ms/step, {tok_s:.1f} tokens/s, "
           f"{sb / 1e6:.2f} MB/step -> {sb / elapsed * args.steps / 1e9:.1f} GB/s end to end",
           file=sys.stderr, flush=True)
 
@@ -200,6 +223,8 @@ def main():
            "data": "synthetic",
            "config": {"workload": wl.name, "batch": B, "past": int(ctx.max()) if wl.past else None,
                       "ctx_range": list(wl.ctx_range) if wl.ctx_range else None},
+           "launch": "hip_graph" if graph else "eager",
+           "eager_tokens_per_s": round(B * args.steps / el_eager, 2),
            "hbm_gbs_end_to_end": round(sb * args.steps / elapsed / 1e9, 1),
            "hbm_frac_end_to_end": round(sb * args.steps / elapsed / 1e9 / HBM_PEAK_GBS, 4),
            "bytes_per_step": int(sb),

@@ -59,21 +59,16 @@ qd_status check_config(const qd_config* c) {
 struct DecodePlan {
     int B, D, Hq, Hkv, hd, G, F, V, qkvr;
     int chunk, S;
-    size_t off_x, off_qkv, off_q, off_part, off_ctx, off_h, off_logits, off_pv, off_pi, total;
+    size_t off_x, off_qkv, off_part, off_cnt, off_ctx, off_h, off_logits, off_pv, off_pi, total;
 };
 
-// Attention split: about 512 workgroups over (sequence, kv head, split), each
-// split a whole number of pages and at most kMaxChunk tokens.
-void plan_split(const qd_config* c, int B, int max_tokens, int* chunk, int* S) {
-    const int page = c->page_size;
-    const int pages = (max_tokens + page - 1) / page;
-    int want = (512 + B * c->n_kv_heads - 1) / (B * c->n_kv_heads);
-    if (want < 1) want = 1;
-    int pages_per = (pages + want - 1) / want;
-    if (pages_per < 1) pages_per = 1;
-    if (pages_per * page > kMaxChunk) pages_per = kMaxChunk / page;
-    *chunk = pages_per * page;
-    *S = (max_tokens + *chunk - 1) / *chunk;
+// Attention split: the largest chunk one workgroup holds in registers (a whole
+// number of pages), S = ceil(tokens / chunk) splits per (sequence, kv head).
+void plan_split(const qd_config* c, int max_tokens, int* chunk, int* S) {
+    int ch = qd::attn_max_chunk(c->head_dim, c->kv_dtype == QD_BF16);
+    ch = ch / c->page_size * c->page_size;
+    *chunk = ch;
+    *S = (max_tokens + ch - 1) / ch;
     if (*S < 1) *S = 1;
 }
 
@@ -87,8 +82,8 @@ DecodePlan plan_decode(const qd_config* c, int B, int S, int chunk) {
     auto take = [&](size_t bytes) { size_t at = o; o = round_up(o + bytes, 256); return at; };
     p.off_x = take(sizeof(float) * B * p.D);
     p.off_qkv = take(sizeof(float) * B * p.qkvr);
-    p.off_q = take(sizeof(float) * B * p.Hq * p.hd);
     p.off_part = take(sizeof(float) * (size_t)B * p.Hkv * S * p.G * (p.hd + 2));
+    p.off_cnt = take(sizeof(unsigned) * B * p.Hkv);
     p.off_ctx = take(sizeof(float) * B * p.Hq * p.hd);
     p.off_h = take(sizeof(float) * (size_t)B * p.F);
     p.off_logits = take(sizeof(float) * (size_t)B * p.V);
@@ -189,10 +184,8 @@ size_t qd_workspace_bytes(const qd_config* cfg, int32_t batch, int32_t max_ctx, 
     if (prefill_tokens > 0) return 0;   // prefill plan added with the MFMA path
     if (batch < 1 || batch > kMaxBatch || max_ctx < 1) return 0;
     int chunk, S;
-    plan_split(cfg, batch, max_ctx, &chunk, &S);
-    // the worst case over any positions below max_ctx is the smallest chunk (one page)
-    const int S_worst = (max_ctx + cfg->page_size - 1) / cfg->page_size;
-    return plan_decode(cfg, batch, S_worst > S ? S_worst : S, cfg->page_size).total;
+    plan_split(cfg, max_ctx, &chunk, &S);
+    return plan_decode(cfg, batch, S, chunk).total;
 }
 
 qd_status qd_decode_step(const qd_config* cfg, const qd_weights* w, const qd_kv* kv, int32_t batch,
@@ -225,7 +218,7 @@ qd_status qd_decode_step(const qd_config* cfg, const qd_weights* w, const qd_kv*
             return fail(QD_EALIGN, "kv pages of layer %d not 16-byte aligned", l);
     }
     int chunk, S;
-    plan_split(cfg, batch, max_tokens, &chunk, &S);
+    plan_split(cfg, max_tokens, &chunk, &S);
     const DecodePlan P = plan_decode(cfg, batch, S, chunk);
     if (!workspace) return fail(QD_EWORKSPACE, "workspace is NULL");
     if (((uintptr_t)workspace & 255u) != 0) return fail(QD_EALIGN, "workspace not 256-byte aligned");
@@ -236,8 +229,8 @@ qd_status qd_decode_step(const qd_config* cfg, const qd_weights* w, const qd_kv*
     char* ws = (char*)workspace;
     float* x = (float*)(ws + P.off_x);
     float* qkv = (float*)(ws + P.off_qkv);
-    float* q = (float*)(ws + P.off_q);
     float* part = (float*)(ws + P.off_part);
+    unsigned* cnt = (unsigned*)(ws + P.off_cnt);
     float* ctx = (float*)(ws + P.off_ctx);
     float* h = (float*)(ws + P.off_h);
     float* lg = logits ? logits : (float*)(ws + P.off_logits);
@@ -246,54 +239,50 @@ qd_status qd_decode_step(const qd_config* cfg, const qd_weights* w, const qd_kv*
     const int wbf = c.w_dtype == QD_BF16, kvbf = c.kv_dtype == QD_BF16;
     const int B = batch, D = P.D;
     const int cap = kv->max_blocks * c.page_size;
+    auto gemv = [&](const qd::GemvArgs& g, int epi, int grid_cap, int* grid_out) {
+        return B == 1 ? qd::launch_gemv1(g, wbf, epi, grid_cap, grid_out, s)
+                      : qd::launch_gemv(g, wbf, epi, grid_cap, grid_out, s);
+    };
 
     if (tokens) QD_LAUNCH_K(QD_K_EMBED, qd::launch_embed(tokens, w->embed, x, B, D, c.vocab, wbf, s), "embed");
     else QD_LAUNCH(qd::launch_copy(x_in, x, (long)B * D, s), "copy x_in");
 
     for (int l = 0; l < c.n_layers; ++l) {
         const qd_layer& L = w->layers_host[l];
-        // RMSNorm -> q|k|v GEMV + bias
+        // RMSNorm -> q|k|v GEMV + bias (also zeroes this layer's attention merge counters)
         qd::GemvArgs g{};
         g.w[0] = L.wq; g.w[1] = L.wk; g.w[2] = L.wv;
         g.bias[0] = L.bq; g.bias[1] = L.bk; g.bias[2] = L.bv;
         g.seg_end[0] = P.Hq * P.hd; g.seg_end[1] = (P.Hq + P.Hkv) * P.hd; g.seg_end[2] = P.qkvr;
         g.nseg = 3; g.N = P.qkvr; g.K = D; g.B = B; g.x = x; g.gain = L.attn_norm; g.eps = c.rms_eps;
-        g.y = qkv; g.kt = gemv_kt(B, D);
-        QD_LAUNCH_K(QD_K_QKV, qd::launch_gemv(g, wbf, qd::EPI_STORE, kGemvGridCap, nullptr, s), "qkv gemv");
-        // [q/k norm] + RoPE + KV append
-        qd::QkvPostArgs qp{};
-        qp.qkv = qkv; qp.q_out = q; qp.k_cache = kv->k_pages_host[l]; qp.v_cache = kv->v_pages_host[l];
-        qp.block_table = kv->block_table; qp.max_blocks = kv->max_blocks; qp.num_pages = kv->num_pages;
-        qp.pos = pos; qp.capacity = cap;
-        qp.q_norm = L.q_norm; qp.k_norm = L.k_norm; qp.qk_norm = c.qk_norm; qp.eps = c.rms_eps;
-        qp.theta = c.rope_theta; qp.Hq = P.Hq; qp.Hkv = P.Hkv; qp.hd = P.hd; qp.page = c.page_size; qp.B = B;
-        QD_LAUNCH_K(QD_K_QKV_POST, qd::launch_qkv_post(qp, wbf, kvbf, s), "qkv post");
-        // split-K attention + merge
+        g.y = qkv; g.kt = gemv_kt(B, D); g.zero_ptr = cnt; g.zero_n = B * P.Hkv;
+        QD_LAUNCH_K(QD_K_QKV, gemv(g, qd::EPI_STORE, kGemvGridCap, nullptr), "qkv gemv");
+        // [q/k norm] + RoPE + KV append + split-K attention + merge
         qd::AttnArgs at{};
-        at.q = q; at.k_cache = kv->k_pages_host[l]; at.v_cache = kv->v_pages_host[l];
+        at.qkv = qkv; at.k_cache = kv->k_pages_host[l]; at.v_cache = kv->v_pages_host[l];
         at.block_table = kv->block_table; at.max_blocks = kv->max_blocks; at.num_pages = kv->num_pages;
-        at.pos = pos; at.capacity = cap;
-        at.part = part; at.ctx = ctx; at.Hq = P.Hq; at.Hkv = P.Hkv; at.hd = P.hd; at.page = c.page_size;
-        at.chunk = P.chunk; at.S = P.S; at.B = B; at.scale = 1.0f / sqrtf((float)P.hd);
-        QD_LAUNCH_K(QD_K_ATTN, qd::launch_attn_decode(at, kvbf, s), "attention");
-        QD_LAUNCH_K(QD_K_MERGE, qd::launch_attn_merge(at, s), "attention merge");
+        at.pos = pos; at.capacity = cap; at.q_norm = L.q_norm; at.k_norm = L.k_norm; at.qk_norm = c.qk_norm;
+        at.eps = c.rms_eps; at.theta = c.rope_theta; at.part = part; at.counters = cnt; at.ctx = ctx;
+        at.Hq = P.Hq; at.Hkv = P.Hkv; at.hd = P.hd; at.page = c.page_size; at.chunk = P.chunk; at.S = P.S;
+        at.B = B; at.scale = 1.0f / sqrtf((float)P.hd);
+        QD_LAUNCH_K(QD_K_ATTN, qd::launch_attention(at, wbf, kvbf, s), "attention");
         // o_proj + residual
         qd::GemvArgs go{};
         go.w[0] = L.wo; go.seg_end[0] = go.seg_end[1] = go.seg_end[2] = D; go.nseg = 1;
         go.N = D; go.K = P.Hq * P.hd; go.B = B; go.x = ctx; go.gain = nullptr; go.y = x;
         go.kt = gemv_kt(B, go.K);
-        QD_LAUNCH_K(QD_K_O, qd::launch_gemv(go, wbf, qd::EPI_RESID, kGemvGridCap, nullptr, s), "o_proj gemv");
+        QD_LAUNCH_K(QD_K_O, gemv(go, qd::EPI_RESID, kGemvGridCap, nullptr), "o_proj gemv");
         // RMSNorm -> gate|up GEMV -> SwiGLU
         qd::GemvArgs gu{};
         gu.w[0] = L.w_gate; gu.w[1] = L.w_up; gu.seg_end[0] = gu.seg_end[1] = gu.seg_end[2] = P.F;
         gu.nseg = 1; gu.N = P.F; gu.K = D; gu.B = B; gu.x = x; gu.gain = L.mlp_norm; gu.eps = c.rms_eps;
         gu.y = h; gu.kt = gemv_kt(B, D);
-        QD_LAUNCH_K(QD_K_GATEUP, qd::launch_gemv(gu, wbf, qd::EPI_SWIGLU, kGemvGridCap, nullptr, s), "gate/up gemv");
+        QD_LAUNCH_K(QD_K_GATEUP, gemv(gu, qd::EPI_SWIGLU, kGemvGridCap, nullptr), "gate/up gemv");
         // down + residual
         qd::GemvArgs gd{};
         gd.w[0] = L.w_down; gd.seg_end[0] = gd.seg_end[1] = gd.seg_end[2] = D; gd.nseg = 1;
         gd.N = D; gd.K = P.F; gd.B = B; gd.x = h; gd.gain = nullptr; gd.y = x; gd.kt = gemv_kt(B, P.F);
-        QD_LAUNCH_K(QD_K_DOWN, qd::launch_gemv(gd, wbf, qd::EPI_RESID, kGemvGridCap, nullptr, s), "down gemv");
+        QD_LAUNCH_K(QD_K_DOWN, gemv(gd, qd::EPI_RESID, kGemvGridCap, nullptr), "down gemv");
         if (layer_out) QD_LAUNCH(qd::launch_copy(x, layer_out + (size_t)l * B * D, (long)B * D, s), "layer_out copy");
     }
     if (x_out) QD_LAUNCH(qd::launch_copy(x, x_out, (long)B * D, s), "x_out copy");
@@ -303,7 +292,7 @@ qd_status qd_decode_step(const qd_config* cfg, const qd_weights* w, const qd_kv*
         gl.N = c.vocab; gl.K = D; gl.B = B; gl.x = x; gl.gain = w->final_norm; gl.eps = c.rms_eps;
         gl.y = lg; gl.part_val = pv; gl.part_idx = pi; gl.kt = gemv_kt(B, D);
         int grid = 0;
-        QD_LAUNCH_K(QD_K_LMHEAD, qd::launch_gemv(gl, wbf, qd::EPI_LOGITS, kLogitsGridCap, &grid, s), "lm_head gemv");
+        QD_LAUNCH_K(QD_K_LMHEAD, gemv(gl, qd::EPI_LOGITS, kLogitsGridCap, &grid), "lm_head gemv");
         if (next_tokens) QD_LAUNCH_K(QD_K_ARGMAX, qd::launch_argmax(pv, pi, grid, next_tokens, B, s), "argmax");
     }
     return QD_OK;

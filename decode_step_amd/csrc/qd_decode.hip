@@ -38,6 +38,8 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
     const int li = lane % LPR, slot = lane / LPR;
     const int B = a.B, K = a.K, N = a.N, kt_max = a.kt;
+    if (a.zero_ptr && blockIdx.x == 0)
+        for (int i = tid; i < a.zero_n; i += kGemvThreads) a.zero_ptr[i] = 0u;
 
     if (a.gain) {   // RMSNorm scale of each batch row over the whole K
         for (int b = wave; b < B; b += 4) {
@@ -227,243 +229,6 @@ hipError_t launch_gemv(const GemvArgs& a, int w_is_bf16, int epi, int grid_cap, 
                          : gemv_dispatch_bm<float, 16>(a, epi, grid, shm, s);
     return w_is_bf16 ? gemv_dispatch_bm<uint16_t, 64>(a, epi, grid, shm, s)
                      : gemv_dispatch_bm<float, 64>(a, epi, grid, shm, s);
-}
-
-// ---------------------------------------------------------------------------
-// q/k per-head RMSNorm (optional), RoPE and the KV append: one wavefront per
-// (head, sequence). Lane i rotates the half-split pair (i, i + hd/2) by
-// pos * theta^(-2i/hd); the angle and its sine/cosine are taken in double and
-// rounded to float. k is stored rotated (nanoinfer page, phase 4: rotate once,
-// on insert); v is stored as projected.
-template <typename WT, typename KVT>
-__global__ __launch_bounds__(64) void qkv_post_kernel(QkvPostArgs a) {
-    const int h = blockIdx.x, b = blockIdx.y, i = threadIdx.x;
-    const int hd = a.hd, half = hd >> 1;
-    const int p = a.pos[b];
-    if (p < 0 || p >= a.capacity) return;
-    const int qkvr = (a.Hq + 2 * a.Hkv) * hd;
-    const bool is_q = h < a.Hq;
-    const float* src = a.qkv + (long)b * qkvr + (is_q ? h * hd : a.Hq * hd + (h - a.Hq) * hd);
-    const bool act = i < half;
-    float lo = act ? src[i] : 0.f, hi = act ? src[i + half] : 0.f;
-    if (a.qk_norm) {
-        const void* g = is_q ? a.q_norm : a.k_norm;
-        float ss = group_sum<kWave>(lo * lo + hi * hi);
-        float r = 1.0f / sqrtf(ss / (float)hd + a.eps);
-        if (act) {
-            lo = lo * r * load_scalar<WT>(g, i);
-            hi = hi * r * load_scalar<WT>(g, i + half);
-        }
-    }
-    if (!act) return;
-    double inv = pow((double)a.theta, -2.0 * (double)i / (double)hd);
-    double sd, cd;
-    sincos((double)p * inv, &sd, &cd);
-    const float c = (float)cd, sn = (float)sd;
-    const float lo2 = lo * c - hi * sn, hi2 = hi * c + lo * sn;
-    if (is_q) {
-        float* q = a.q_out + ((long)b * a.Hq + h) * hd;
-        q[i] = lo2;
-        q[i + half] = hi2;
-    } else {
-        const int g = h - a.Hq;
-        const int page_id = a.block_table[(long)b * a.max_blocks + p / a.page];
-        if (page_id < 0 || page_id >= a.num_pages) return;
-        const long off = (((long)page_id * a.Hkv + g) * a.page + (p % a.page)) * hd;
-        KVT* kc = (KVT*)a.k_cache + off;
-        KVT* vc = (KVT*)a.v_cache + off;
-        const float* vs = a.qkv + (long)b * qkvr + (a.Hq + a.Hkv) * hd + g * hd;
-        kc[i] = from_f32<KVT>(lo2);
-        kc[i + half] = from_f32<KVT>(hi2);
-        vc[i] = from_f32<KVT>(vs[i]);
-        vc[i + half] = from_f32<KVT>(vs[i + half]);
-    }
-}
-
-hipError_t launch_qkv_post(const QkvPostArgs& a, int w_is_bf16, int kv_is_bf16, hipStream_t s) {
-    dim3 grid(a.Hq + a.Hkv, a.B);
-    if (w_is_bf16) {
-        if (kv_is_bf16) hipLaunchKernelGGL((qkv_post_kernel<uint16_t, uint16_t>), grid, dim3(64), 0, s, a);
-        else hipLaunchKernelGGL((qkv_post_kernel<uint16_t, float>), grid, dim3(64), 0, s, a);
-    } else {
-        if (kv_is_bf16) hipLaunchKernelGGL((qkv_post_kernel<float, uint16_t>), grid, dim3(64), 0, s, a);
-        else hipLaunchKernelGGL((qkv_post_kernel<float, float>), grid, dim3(64), 0, s, a);
-    }
-    return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
-// Split-K decode attention over the paged cache. One workgroup per
-// (split, kv head, sequence) reads each cached K and V row of its chunk once
-// for all `group` query heads that share the KV head (GQA: query head h reads
-// KV head h / group). Within the chunk: scores, chunk max m, l = sum exp(s-m),
-// o = sum exp(s-m) v; the partial (o, m, l) is combined across chunks by the
-// merge kernel (Tang page, section 2.2: online softmax as a monoid; Table 1:
-// split-K). A token attends to itself: the chunk range ends at pos (inclusive).
-constexpr int kAttnThreads = 256;
-constexpr int kMaxGroup = 8;
-constexpr int kMaxChunk = 256;
-
-template <typename KVT, int HD>
-__global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnArgs a) {
-    constexpr int CE = VecN<KVT>::n;
-    constexpr int LPT = HD / CE;          // lanes per token
-    constexpr int TPW = kWave / LPT;      // tokens per wave per pass
-    constexpr int TPB = 4 * TPW;
-    __shared__ float sc[kMaxGroup][kMaxChunk];
-    __shared__ float red[4][kMaxGroup][HD];
-    __shared__ float ml[kMaxGroup][2];
-
-    const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-    const int G = a.Hq / a.Hkv;
-    const int p = a.pos[b];
-    if (p < 0 || p >= a.capacity) return;
-    if (a.chunk > kMaxChunk) return;
-    const int T = p + 1;
-    const int t_begin = s * a.chunk;
-    if (t_begin >= T) return;
-    const int t_end = min(T, t_begin + a.chunk);
-    const int n = t_end - t_begin;
-
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
-    const int li = lane % LPT, slot = lane / LPT;
-
-    float qv[kMaxGroup][CE];
-#pragma unroll
-    for (int hl = 0; hl < kMaxGroup; ++hl)
-#pragma unroll
-        for (int e = 0; e < CE; ++e)
-            qv[hl][e] = (hl < G) ? a.q[((long)b * a.Hq + g * G + hl) * HD + li * CE + e] : 0.f;
-
-    const int* bt = a.block_table + (long)b * a.max_blocks;
-    // a page id outside the pool reads as zeros instead of faulting
-    auto load_row = [&](const void* base, int t, float (&f)[CE]) {
-        const int page_id = bt[t / a.page];
-        if (page_id < 0 || page_id >= a.num_pages) {
-#pragma unroll
-            for (int e = 0; e < CE; ++e) f[e] = 0.f;
-            return;
-        }
-        widen16(*(const uint4*)((const KVT*)base +
-                                (((long)page_id * a.Hkv + g) * a.page + (t % a.page)) * HD + li * CE), f);
-    };
-
-    // scores
-    for (int t0 = t_begin; t0 < t_end; t0 += TPB) {
-        const int t = t0 + wave * TPW + slot;
-        float kf[CE];
-        if (t < t_end) load_row(a.k_cache, t, kf);
-        else {
-#pragma unroll
-            for (int e = 0; e < CE; ++e) kf[e] = 0.f;
-        }
-#pragma unroll
-        for (int hl = 0; hl < kMaxGroup; ++hl) {
-            if (hl >= G) break;
-            float d = 0.f;
-#pragma unroll
-            for (int e = 0; e < CE; ++e) d = fmaf(qv[hl][e], kf[e], d);
-            d = group_sum<LPT>(d);
-            if (li == 0 && t < t_end) sc[hl][t - t_begin] = d * a.scale;
-        }
-    }
-    __syncthreads();
-    // chunk max and exp-sum per head
-    for (int hl = wave; hl < G; hl += 4) {
-        float m = -INFINITY;
-        for (int j = lane; j < n; j += kWave) m = fmaxf(m, sc[hl][j]);
-        m = wave_max(m);
-        float l = 0.f;
-        for (int j = lane; j < n; j += kWave) {
-            float e = expf(sc[hl][j] - m);
-            sc[hl][j] = e;
-            l += e;
-        }
-        l = group_sum<kWave>(l);
-        if (lane == 0) { ml[hl][0] = m; ml[hl][1] = l; }
-    }
-    __syncthreads();
-    // o = sum_t p_t v_t
-    float oacc[kMaxGroup][CE];
-#pragma unroll
-    for (int hl = 0; hl < kMaxGroup; ++hl)
-#pragma unroll
-        for (int e = 0; e < CE; ++e) oacc[hl][e] = 0.f;
-    for (int t0 = t_begin; t0 < t_end; t0 += TPB) {
-        const int t = t0 + wave * TPW + slot;
-        if (t < t_end) {
-            float vf[CE];
-            load_row(a.v_cache, t, vf);
-#pragma unroll
-            for (int hl = 0; hl < kMaxGroup; ++hl) {
-                if (hl >= G) break;
-                const float pr = sc[hl][t - t_begin];
-#pragma unroll
-                for (int e = 0; e < CE; ++e) oacc[hl][e] = fmaf(pr, vf[e], oacc[hl][e]);
-            }
-        }
-    }
-    // combine token slots within the wave (lanes li, li+LPT, ...), then across waves
-#pragma unroll
-    for (int hl = 0; hl < kMaxGroup; ++hl) {
-        if (hl >= G) break;
-#pragma unroll
-        for (int e = 0; e < CE; ++e) {
-            float v = oacc[hl][e];
-#pragma unroll
-            for (int off = 32; off >= LPT; off >>= 1) v += __shfl_xor(v, off, kWave);
-            if (slot == 0) red[wave][hl][li * CE + e] = v;
-        }
-    }
-    __syncthreads();
-    float* out = a.part + ((((long)b * a.Hkv + g) * a.S + s) * G) * (HD + 2);
-    for (int idx = tid; idx < G * HD; idx += kAttnThreads) {
-        const int hl = idx / HD, d = idx - hl * HD;
-        out[hl * (HD + 2) + d] = red[0][hl][d] + red[1][hl][d] + red[2][hl][d] + red[3][hl][d];
-    }
-    if (tid < G) {
-        out[tid * (HD + 2) + HD] = ml[tid][0];
-        out[tid * (HD + 2) + HD + 1] = ml[tid][1];
-    }
-}
-
-// Merge of the chunk partials of one (query head, sequence):
-// M = max m_s, ctx = sum_s o_s e^(m_s - M) / sum_s l_s e^(m_s - M).
-__global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a) {
-    const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
-    const int HD = a.hd, G = a.Hq / a.Hkv, g = h / G, hl = h - g * G;
-    if (d >= HD) return;
-    const int p = a.pos[b];
-    if (p < 0 || p >= a.capacity) return;
-    const int ns = min(a.S, (p + 1 + a.chunk - 1) / a.chunk);
-    const float* base = a.part + (((long)b * a.Hkv + g) * a.S) * G * (HD + 2) + hl * (HD + 2);
-    const long stride = (long)G * (HD + 2);
-    float M = -INFINITY;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, base[s * stride + HD]);
-    float L = 0.f, O = 0.f;
-    for (int s = 0; s < ns; ++s) {
-        const float w = expf(base[s * stride + HD] - M);
-        L = fmaf(base[s * stride + HD + 1], w, L);
-        O = fmaf(base[s * stride + d], w, O);
-    }
-    a.ctx[((long)b * a.Hq + h) * HD + d] = O / L;
-}
-
-hipError_t launch_attn_decode(const AttnArgs& a, int kv_is_bf16, hipStream_t s) {
-    dim3 grid(a.S, a.Hkv, a.B);
-    if (a.hd == 64) {
-        if (kv_is_bf16) hipLaunchKernelGGL((attn_decode_kernel<uint16_t, 64>), grid, dim3(kAttnThreads), 0, s, a);
-        else hipLaunchKernelGGL((attn_decode_kernel<float, 64>), grid, dim3(kAttnThreads), 0, s, a);
-    } else {
-        if (kv_is_bf16) hipLaunchKernelGGL((attn_decode_kernel<uint16_t, 128>), grid, dim3(kAttnThreads), 0, s, a);
-        else hipLaunchKernelGGL((attn_decode_kernel<float, 128>), grid, dim3(kAttnThreads), 0, s, a);
-    }
-    return hipGetLastError();
-}
-
-hipError_t launch_attn_merge(const AttnArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL(attn_merge_kernel, dim3(a.Hq, a.B), dim3(128), 0, s, a);
-    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------

@@ -36,6 +36,20 @@ __device__ __forceinline__ void widen16(const uint4 v, float (&f)[4]) {
     f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
 }
 
+// Round floats to the storage type and pack them into one 16-byte vector.
+template <typename T> __device__ __forceinline__ uint4 pack16(const float (&f)[VecN<T>::n]);
+template <> __device__ __forceinline__ uint4 pack16<uint16_t>(const float (&f)[8]) {
+    uint4 v;
+    v.x = (uint32_t)f32_to_bf16(f[0]) | ((uint32_t)f32_to_bf16(f[1]) << 16);
+    v.y = (uint32_t)f32_to_bf16(f[2]) | ((uint32_t)f32_to_bf16(f[3]) << 16);
+    v.z = (uint32_t)f32_to_bf16(f[4]) | ((uint32_t)f32_to_bf16(f[5]) << 16);
+    v.w = (uint32_t)f32_to_bf16(f[6]) | ((uint32_t)f32_to_bf16(f[7]) << 16);
+    return v;
+}
+template <> __device__ __forceinline__ uint4 pack16<float>(const float (&f)[4]) {
+    return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3]));
+}
+
 template <typename T> __device__ __forceinline__ float load_scalar(const void* p, int i);
 template <> __device__ __forceinline__ float load_scalar<uint16_t>(const void* p, int i) {
     return bf16_to_f32(((const uint16_t*)p)[i]);

@@ -25,14 +25,20 @@ struct GemvArgs {
     float* part_val;   // EPI_LOGITS: per-(b, workgroup) best value
     int* part_idx;     //             and its row
     int kt;            // K elements staged in LDS per pass
+    unsigned* zero_ptr;  // optional: workgroup 0 stores zeros here (counters of a later kernel)
+    int zero_n;
 };
 hipError_t launch_gemv(const GemvArgs& a, int w_is_bf16, int epi, int grid_cap, int* grid_out,
                        hipStream_t s);
+// batch-1 fast path (qd_gemv.hip); part_val/part_idx hold one entry per workgroup
+hipError_t launch_gemv1(const GemvArgs& a, int w_is_bf16, int epi, int grid_cap, int* grid_out,
+                        hipStream_t s);
 int gemv_rows_per_tile(int K);
 
-struct QkvPostArgs {
-    const float* qkv;       // [B][Hq*hd + 2*Hkv*hd]
-    float* q_out;           // [B][Hq][hd]
+// Decode attention with the q/k norm, RoPE, the new token's KV append and the
+// split merge fused in (one launch per layer); see qd_attention.hip.
+struct AttnArgs {
+    const float* qkv;       // [B][Hq*hd + 2*Hkv*hd] projections (bias added)
     void* k_cache;
     void* v_cache;          // page pools [pages][Hkv][page][hd]
     const int* block_table;
@@ -43,25 +49,14 @@ struct QkvPostArgs {
     const void* k_norm;
     int qk_norm;
     float eps, theta;
-    int Hq, Hkv, hd, page, B;
-};
-hipError_t launch_qkv_post(const QkvPostArgs& a, int w_is_bf16, int kv_is_bf16, hipStream_t s);
-
-struct AttnArgs {
-    const float* q;         // [B][Hq][hd], rotated
-    const void* k_cache;
-    const void* v_cache;
-    const int* block_table;
-    int max_blocks, num_pages;
-    const int* pos;
-    int capacity;
     float* part;            // [B][Hkv][S][G][hd+2]: o[hd], m, l
-    float* ctx;             // merge output [B][Hq*hd]
+    unsigned* counters;     // [B][Hkv], zero when the kernel starts
+    float* ctx;             // [B][Hq*hd]
     int Hq, Hkv, hd, page, chunk, S, B;
     float scale;
 };
-hipError_t launch_attn_decode(const AttnArgs& a, int kv_is_bf16, hipStream_t s);
-hipError_t launch_attn_merge(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attention(const AttnArgs& a, int w_is_bf16, int kv_is_bf16, hipStream_t s);
+int attn_max_chunk(int hd, int kv_is_bf16);
 
 hipError_t launch_embed(const int* tokens, const void* embed, float* x, int B, int D, int V,
                         int w_is_bf16, hipStream_t s);

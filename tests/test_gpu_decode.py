@@ -131,6 +131,44 @@ def test_outputs_guarded_and_deterministic():
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
 
 
+def test_graph_replay_matches_eager():
+    """One decode step captured in a HIP graph and replayed several times, with eager
+    work and synchronisations in between: every replay equals the eager result bitwise."""
+    shape = SMALL
+    ctx = np.array([70, 3, 129], np.int32)
+    case = make_case(shape, ctx, seed=21, random_order=True)
+    tok = dev_i32(synth.make_tokens(3, shape.vocab, seed=21))
+    pos = dev_i32(ctx)
+    logits = torch.empty(3, shape.vocab, device="cuda")
+    nxt = torch.empty(3, dtype=torch.int32, device="cuda")
+
+    def step():
+        case.runner.step(ctx, pos, tokens=tok, logits=logits, next_tokens=nxt,
+                         stream=torch.cuda.current_stream())
+
+    step()
+    torch.cuda.synchronize()
+    ref_logits, ref_next = logits.clone(), nxt.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for i in range(4):
+        logits.fill_(float("nan"))
+        nxt.fill_(-1)
+        junk = torch.randn(1000, device="cuda").sum()   # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(logits, ref_logits), i
+        assert torch.equal(nxt, ref_next), i
+    del junk
+
+
 def test_kv_append_matches_oracle_rounding():
     from oracle.numerics import store_kv
     shape = replace(SMALL, n_layers=1)
