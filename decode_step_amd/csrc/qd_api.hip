@@ -59,17 +59,23 @@ qd_status check_config(const qd_config* c) {
 struct DecodePlan {
     int B, D, Hq, Hkv, hd, G, F, V, qkvr;
     int chunk, S;
-    size_t off_x, off_qkv, off_part, off_cnt, off_ctx, off_h, off_logits, off_pv, off_pi, total;
+    size_t off_x, off_qkv, off_part, off_rope, off_ctx, off_h, off_logits, off_pv, off_pi, total;
 };
 
-// Attention split: the largest chunk one workgroup holds in registers (a whole
-// number of pages), S = ceil(tokens / chunk) splits per (sequence, kv head).
-void plan_split(const qd_config* c, int max_tokens, int* chunk, int* S) {
+// Attention work split: S = ceil(tokens / chunk) splits per (sequence, kv head),
+// chunk = the most one workgroup holds in registers (a whole number of pages);
+// the query heads of a KV head go to separate workgroups (hpw = 1) unless that
+// makes more than 1024 workgroups. Returns false when the context needs more
+// splits than one merge combines.
+bool plan_split(const qd_config* c, int B, int max_tokens, int* chunk, int* S, int* hpw) {
     int ch = qd::attn_max_chunk(c->head_dim, c->kv_dtype == QD_BF16);
     ch = ch / c->page_size * c->page_size;
     *chunk = ch;
     *S = (max_tokens + ch - 1) / ch;
     if (*S < 1) *S = 1;
+    const long wgs = (long)(*S) * B * c->n_q_heads;
+    *hpw = wgs <= 1024 ? 1 : c->n_q_heads / c->n_kv_heads;
+    return *S <= qd::attn_max_splits();
 }
 
 DecodePlan plan_decode(const qd_config* c, int B, int S, int chunk) {
@@ -82,8 +88,8 @@ DecodePlan plan_decode(const qd_config* c, int B, int S, int chunk) {
     auto take = [&](size_t bytes) { size_t at = o; o = round_up(o + bytes, 256); return at; };
     p.off_x = take(sizeof(float) * B * p.D);
     p.off_qkv = take(sizeof(float) * B * p.qkvr);
-    p.off_part = take(sizeof(float) * (size_t)B * p.Hkv * S * p.G * (p.hd + 2));
-    p.off_cnt = take(sizeof(unsigned) * B * p.Hkv);
+    p.off_part = take(sizeof(float) * (size_t)B * p.Hq * S * (p.hd + 2));
+    p.off_rope = take(sizeof(float) * 2 * B * (p.hd / 2));
     p.off_ctx = take(sizeof(float) * B * p.Hq * p.hd);
     p.off_h = take(sizeof(float) * (size_t)B * p.F);
     p.off_logits = take(sizeof(float) * (size_t)B * p.V);
@@ -183,8 +189,8 @@ size_t qd_workspace_bytes(const qd_config* cfg, int32_t batch, int32_t max_ctx, 
     if (check_config(cfg) != QD_OK) return 0;
     if (prefill_tokens > 0) return 0;   // prefill plan added with the MFMA path
     if (batch < 1 || batch > kMaxBatch || max_ctx < 1) return 0;
-    int chunk, S;
-    plan_split(cfg, max_ctx, &chunk, &S);
+    int chunk, S, hpw;
+    if (!plan_split(cfg, batch, max_ctx, &chunk, &S, &hpw)) return 0;
     return plan_decode(cfg, batch, S, chunk).total;
 }
 
@@ -217,8 +223,10 @@ qd_status qd_decode_step(const qd_config* cfg, const qd_weights* w, const qd_kv*
         if (!aligned16(kv->k_pages_host[l]) || !aligned16(kv->v_pages_host[l]))
             return fail(QD_EALIGN, "kv pages of layer %d not 16-byte aligned", l);
     }
-    int chunk, S;
-    plan_split(cfg, max_tokens, &chunk, &S);
+    int chunk, S, hpw;
+    if (!plan_split(cfg, batch, max_tokens, &chunk, &S, &hpw))
+        return fail(QD_ECAPACITY, "context of %d tokens needs %d attention splits > %d", max_tokens, S,
+                    qd::attn_max_splits());
     const DecodePlan P = plan_decode(cfg, batch, S, chunk);
     if (!workspace) return fail(QD_EWORKSPACE, "workspace is NULL");
     if (((uintptr_t)workspace & 255u) != 0) return fail(QD_EALIGN, "workspace not 256-byte aligned");
@@ -230,7 +238,7 @@ qd_status qd_decode_step(const qd_config* cfg, const qd_weights* w, const qd_kv*
     float* x = (float*)(ws + P.off_x);
     float* qkv = (float*)(ws + P.off_qkv);
     float* part = (float*)(ws + P.off_part);
-    unsigned* cnt = (unsigned*)(ws + P.off_cnt);
+    float2* rope = (float2*)(ws + P.off_rope);
     float* ctx = (float*)(ws + P.off_ctx);
     float* h = (float*)(ws + P.off_h);
     float* lg = logits ? logits : (float*)(ws + P.off_logits);
@@ -244,27 +252,29 @@ qd_status qd_decode_step(const qd_config* cfg, const qd_weights* w, const qd_kv*
                       : qd::launch_gemv(g, wbf, epi, grid_cap, grid_out, s);
     };
 
-    if (tokens) QD_LAUNCH_K(QD_K_EMBED, qd::launch_embed(tokens, w->embed, x, B, D, c.vocab, wbf, s), "embed");
-    else QD_LAUNCH(qd::launch_copy(x_in, x, (long)B * D, s), "copy x_in");
+    qd::StepInputArgs si{};
+    si.tokens = tokens; si.embed = w->embed; si.x_in = x_in; si.x = x; si.pos = pos; si.rope = rope;
+    si.B = B; si.D = D; si.V = c.vocab; si.hd = P.hd; si.theta = c.rope_theta;
+    QD_LAUNCH_K(QD_K_EMBED, qd::launch_step_input(si, wbf, s), "step input");
 
     for (int l = 0; l < c.n_layers; ++l) {
         const qd_layer& L = w->layers_host[l];
-        // RMSNorm -> q|k|v GEMV + bias (also zeroes this layer's attention merge counters)
+        // RMSNorm -> q|k|v GEMV + bias
         qd::GemvArgs g{};
         g.w[0] = L.wq; g.w[1] = L.wk; g.w[2] = L.wv;
         g.bias[0] = L.bq; g.bias[1] = L.bk; g.bias[2] = L.bv;
         g.seg_end[0] = P.Hq * P.hd; g.seg_end[1] = (P.Hq + P.Hkv) * P.hd; g.seg_end[2] = P.qkvr;
         g.nseg = 3; g.N = P.qkvr; g.K = D; g.B = B; g.x = x; g.gain = L.attn_norm; g.eps = c.rms_eps;
-        g.y = qkv; g.kt = gemv_kt(B, D); g.zero_ptr = cnt; g.zero_n = B * P.Hkv;
+        g.y = qkv; g.kt = gemv_kt(B, D);
         QD_LAUNCH_K(QD_K_QKV, gemv(g, qd::EPI_STORE, kGemvGridCap, nullptr), "qkv gemv");
         // [q/k norm] + RoPE + KV append + split-K attention + merge
         qd::AttnArgs at{};
         at.qkv = qkv; at.k_cache = kv->k_pages_host[l]; at.v_cache = kv->v_pages_host[l];
         at.block_table = kv->block_table; at.max_blocks = kv->max_blocks; at.num_pages = kv->num_pages;
         at.pos = pos; at.capacity = cap; at.q_norm = L.q_norm; at.k_norm = L.k_norm; at.qk_norm = c.qk_norm;
-        at.eps = c.rms_eps; at.theta = c.rope_theta; at.part = part; at.counters = cnt; at.ctx = ctx;
+        at.eps = c.rms_eps; at.theta = c.rope_theta; at.part = part; at.rope = rope; at.ctx = ctx;
         at.Hq = P.Hq; at.Hkv = P.Hkv; at.hd = P.hd; at.page = c.page_size; at.chunk = P.chunk; at.S = P.S;
-        at.B = B; at.scale = 1.0f / sqrtf((float)P.hd);
+        at.B = B; at.hpw = hpw; at.scale = 1.0f / sqrtf((float)P.hd);
         QD_LAUNCH_K(QD_K_ATTN, qd::launch_attention(at, wbf, kvbf, s), "attention");
         // o_proj + residual
         qd::GemvArgs go{};

@@ -1,199 +1,210 @@
 // Decode attention for gfx950: per-head q/k RMSNorm, RoPE, the KV append of the
-// new token and split-K online-softmax attention over the paged cache, in one
-// kernel per layer.
+// new token and split-K softmax attention over the paged cache.
 //
-// One workgroup per (split, kv head g, sequence b) reads each cached K and V
-// row of its split once for all `group` query heads sharing KV head g (query
-// head h reads KV head h / group: repeat, not tile -- nanoinfer page, phase 3).
-// A split keeps (o, m, l) = (sum exp(s - m) v, max s, sum exp(s - m)); the
-// last split to finish merges them with weights exp(m_s - M), M = max m_s
-// (Tang page, section 2.2: online softmax is a monoid; Table 1: split-K).
+// Work item = (split s of the context, group of `hpw` query heads of KV head g,
+// sequence b), one workgroup of NWV waves each. LPT lanes hold one token's
+// 16-byte row chunks, so a wave covers 64/LPT tokens per pass and every lane
+// issues the loads of all its passes up front (page ids come from LDS, so no
+// load waits on another). Query head h reads KV head h / group (repeat, not
+// tile -- nanoinfer page, phase 3); splitting the query heads of one KV head
+// over several workgroups spreads the score and value arithmetic over more
+// CUs (each re-reads the same K/V rows, mostly from cache).
+//
+// Within a split the softmax is the plain two-pass one (scores to LDS, max,
+// exp, sum). A context that fits one split writes the attention output
+// directly; otherwise each split publishes (o, m, l) = (sum exp(s - m) v, max s,
+// sum exp(s - m)) and a merge kernel combines them with weights exp(m_s - M),
+// M = max m_s (Tang page, section 2.2: online softmax is a monoid; Table 1:
+// split-K).
 //
 // The new token (position p) is not read from the cache: its k is projected,
 // normed (8B-class shape), rotated, rounded to the cache type, written to its
-// slot, and that stored value is what the scores use (nanoserve day 49: the
-// step writes this token's K/V into its row before it attends; nanoinfer page,
-// phase 4: keys are rotated once, on insert). The query rows are normed and
-// rotated here too.
-//
-// RoPE (nanoinfer page, phase 3: half-split pairs i and i + hd/2): the angle
-// p * theta^(-2i/hd) is formed and reduced modulo 2*pi in double, then its
-// sine and cosine are taken in float. A lane holds CE consecutive elements of a
-// head, so the partner of element i sits in lane li ^ (LPT/2) and arrives by one
-// cross-lane shuffle.
+// slot by one workgroup, and that stored value is what the scores use
+// (nanoserve day 49: the step writes this token's K/V into its row before it
+// attends; nanoinfer page, phase 4: keys are rotated once, on insert). Wave 0
+// norms and rotates the query heads and the new k with the step's cos/sin table
+// (built once per step by the input kernel; RoPE pairs i and i + hd/2, nanoinfer
+// page, phase 3): a lane holds CE consecutive elements of a head and loads their
+// rotation partners.
 #include "qd_device.h"
 #include "qd_launch.h"
 
 namespace qd {
 
-constexpr int kAttnThreads = 256;
 constexpr int kMaxGroup = 8;
-constexpr int kMaxChunk = 256;
-constexpr int kAttnIters = 8;   // token passes whose K/V rows a lane holds in registers
+constexpr int kAttnWaves = 8;    // waves per workgroup
+constexpr int kAttnPasses = 9;   // token passes whose K/V rows a lane holds in registers
+constexpr int kMaxSplits = 64;
 
 template <int HD, typename KVT>
-constexpr int attn_tokens_per_pass() { return 4 * (kWave / (HD / VecN<KVT>::n)); }
+constexpr int attn_chunk() { return kAttnPasses * kAttnWaves * (kWave / (HD / VecN<KVT>::n)); }
 
 int attn_max_chunk(int hd, int kv_is_bf16) {
-    int tpb;
-    if (hd == 64) tpb = kv_is_bf16 ? attn_tokens_per_pass<64, uint16_t>() : attn_tokens_per_pass<64, float>();
-    else tpb = kv_is_bf16 ? attn_tokens_per_pass<128, uint16_t>() : attn_tokens_per_pass<128, float>();
-    int c = tpb * kAttnIters;
-    return c < kMaxChunk ? c : kMaxChunk;
+    if (hd == 64) return kv_is_bf16 ? attn_chunk<64, uint16_t>() : attn_chunk<64, float>();
+    return kv_is_bf16 ? attn_chunk<128, uint16_t>() : attn_chunk<128, float>();
 }
+int attn_max_splits() { return kMaxSplits; }
 
 __device__ __forceinline__ void load_f32xN(const float* p, float* f, int n) {
 #pragma unroll
     for (int q = 0; q < n / 4; ++q) {
-        float4 t = ((const float4*)p)[q];
+        const float4 t = ((const float4*)p)[q];
         f[4 * q] = t.x; f[4 * q + 1] = t.y; f[4 * q + 2] = t.z; f[4 * q + 3] = t.w;
     }
 }
 
-// Half-split rotation of the CE elements this lane holds (lower half when li < LPT/2).
-template <int CE, int LPT>
-__device__ __forceinline__ void rope_lane(float (&u)[CE], const float (&c)[CE], const float (&sn)[CE], bool lower) {
+// Half-split rotation of the CE elements a lane holds (`lower`: its elements are
+// in the first half of the head); `pr` holds the partner elements i +- hd/2.
+template <int CE>
+__device__ __forceinline__ void rope_lane(float (&u)[CE], const float (&pr)[CE], const float (&c)[CE],
+                                          const float (&sn)[CE], bool lower) {
 #pragma unroll
-    for (int e = 0; e < CE; ++e) {
-        const float partner = __shfl_xor(u[e], LPT / 2, kWave);
-        u[e] = lower ? u[e] * c[e] - partner * sn[e] : u[e] * c[e] + partner * sn[e];
-    }
+    for (int e = 0; e < CE; ++e) u[e] = lower ? u[e] * c[e] - pr[e] * sn[e] : u[e] * c[e] + pr[e] * sn[e];
 }
 
 template <typename WT, typename KVT, int HD>
-__global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kAttnWaves * kWave) void attn_kernel(AttnArgs a) {
     constexpr int CE = VecN<KVT>::n;
     constexpr int LPT = HD / CE;
     constexpr int TPW = kWave / LPT;
-    constexpr int TPB = 4 * TPW;
-    constexpr int NI = kAttnIters;
-    __shared__ float sc[kMaxGroup][kMaxChunk];
-    __shared__ float red[4][kMaxGroup][HD];
-    __shared__ float ml[kMaxGroup][2];
-    __shared__ int is_last;
+    constexpr int NWV = kAttnWaves;
+    constexpr int TPB = NWV * TPW;
+    constexpr int NP = kAttnPasses;
+    constexpr int MAXT = NP * TPB;
+    constexpr int NT = NWV * kWave;
+    __shared__ float sc[kMaxGroup][MAXT];
+    __shared__ float red[NWV][kMaxGroup][HD];
+    __shared__ float mls[kMaxGroup][2];
+    __shared__ float qs[kMaxGroup][HD];
+    __shared__ uint4 knew[LPT];   // the new token's K and V rows in stored (cache-type) form
+    __shared__ uint4 vnew[LPT];
+    __shared__ int spage[MAXT / 16 + 2];
 
-    const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int G = a.Hq / a.Hkv;
+    const int hgroups = (G + a.hpw - 1) / a.hpw;
+    const int s = blockIdx.x, g = blockIdx.y / hgroups, hg = blockIdx.y % hgroups, b = blockIdx.z;
+    const int h0 = hg * a.hpw, nh = min(a.hpw, G - h0);   // query heads g*G + h0 .. + nh - 1
     const int p = a.pos[b];
-    if (p < 0 || p >= a.capacity || a.chunk > NI * TPB || a.chunk > kMaxChunk || G > kMaxGroup) return;
+    if (p < 0 || p >= a.capacity || a.chunk > MAXT || a.hpw > kMaxGroup || a.page < 16 || nh <= 0) return;
     const int T = p + 1;
     const int ns = min(a.S, (T + a.chunk - 1) / a.chunk);
     const int t_begin = s * a.chunk;
     if (t_begin >= T) return;
     const int t_end = min(T, t_begin + a.chunk);
     const int n = t_end - t_begin;
+    const bool has_new = p >= t_begin && p < t_end;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
     const int li = lane % LPT, slot = lane / LPT;
-    const bool lower = li < LPT / 2;
     const int* bt = a.block_table + (long)b * a.max_blocks;
 
-    // cached K/V rows of this split (position p excluded: it is the new token)
-    uint4 kraw[NI], vraw[NI];
+    // page ids of this split's pages (an entry outside the pool reads as page 0
+    // and is masked), then every K/V row load issued back to back
+    const int pg0 = t_begin / a.page;
+    const int npg = (t_end - 1) / a.page - pg0 + 1;
+    if (tid < npg) {
+        const int pg = bt[pg0 + tid];
+        spage[tid] = (pg >= 0 && pg < a.num_pages) ? pg : -1;
+    }
+    __syncthreads();
+    uint4 kraw[NP], vraw[NP];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
+    for (int i = 0; i < NP; ++i) {
         const int t = t_begin + i * TPB + wave * TPW + slot;
-        kraw[i] = make_uint4(0, 0, 0, 0);
-        vraw[i] = make_uint4(0, 0, 0, 0);
-        if (t < t_end && t != p) {
-            const int page_id = bt[t / a.page];
-            if (page_id >= 0 && page_id < a.num_pages) {
-                const long off = (((long)page_id * a.Hkv + g) * a.page + (t % a.page)) * HD + li * CE;
-                kraw[i] = *(const uint4*)((const KVT*)a.k_cache + off);
-                vraw[i] = *(const uint4*)((const KVT*)a.v_cache + off);
+        const int tt = t < t_end ? t : t_begin;
+        const int pg = spage[tt / a.page - pg0];
+        const bool ok = t < t_end && t != p && pg >= 0;
+        const long off = (((long)max(pg, 0) * a.Hkv + g) * a.page + (tt % a.page)) * HD + li * CE;
+        const uint4 kv = *(const uint4*)((const KVT*)a.k_cache + off);
+        const uint4 vv = *(const uint4*)((const KVT*)a.v_cache + off);
+        kraw[i] = ok ? kv : make_uint4(0, 0, 0, 0);
+        vraw[i] = ok ? vv : make_uint4(0, 0, 0, 0);
+    }
+    // wave 0: norm and rotation of this workgroup's query heads and of the new k
+    // (one head-chunk of CE elements per lane, LPT lanes per head; index nh is k)
+    if (wave == 0) {
+        const int qkvr = (a.Hq + 2 * a.Hkv) * HD;
+        const float* src = a.qkv + (long)b * qkvr;
+        const int items = (nh + (has_new ? 1 : 0)) * LPT;
+        for (int base = 0; base < items; base += kWave) {
+            const int idx = base + lane;
+            const bool act = idx < items;
+            const int hl = act ? idx / LPT : 0, l2 = idx % LPT, lp2 = l2 ^ (LPT / 2);
+            const float* hsrc = hl < nh ? src + (g * G + h0 + hl) * HD : src + a.Hq * HD + g * HD;
+            float u[CE], up[CE], cs[CE], sn[CE];
+            load_f32xN(hsrc + l2 * CE, u, CE);
+            load_f32xN(hsrc + lp2 * CE, up, CE);
+            const float2* tab = a.rope + (long)b * (HD / 2) + (l2 % (LPT / 2)) * CE;
+#pragma unroll
+            for (int e = 0; e < CE; ++e) { const float2 t = tab[e]; cs[e] = t.x; sn[e] = t.y; }
+            if (a.qk_norm) {   // per-head RMSNorm: the sum of squares over the head's LPT lanes
+                float ss = 0.f;
+#pragma unroll
+                for (int e = 0; e < CE; ++e) ss += u[e] * u[e];
+                ss = group_sum<LPT>(ss);
+                const float r = 1.0f / sqrtf(ss / (float)HD + a.eps);
+                const void* gain = hl < nh ? a.q_norm : a.k_norm;
+#pragma unroll
+                for (int e = 0; e < CE; ++e) {
+                    u[e] = u[e] * r * load_scalar<WT>(gain, l2 * CE + e);
+                    up[e] = up[e] * r * load_scalar<WT>(gain, lp2 * CE + e);
+                }
+            }
+            rope_lane<CE>(u, up, cs, sn, l2 < LPT / 2);
+            if (!act) continue;
+            if (hl < nh) {
+#pragma unroll
+                for (int e = 0; e < CE; ++e) qs[hl][l2 * CE + e] = u[e];
+            } else {
+                float vn[CE];
+                load_f32xN(src + (a.Hq + a.Hkv) * HD + g * HD + l2 * CE, vn, CE);
+                const uint4 kst = pack16<KVT>(u), vst = pack16<KVT>(vn);
+                knew[l2] = kst;
+                vnew[l2] = vst;
+                if (hg == 0) {   // one workgroup per (sequence, kv head) stores the new row
+                    const int page_id = bt[p / a.page];
+                    if (page_id >= 0 && page_id < a.num_pages) {
+                        const long off = (((long)page_id * a.Hkv + g) * a.page + (p % a.page)) * HD + l2 * CE;
+                        *(uint4*)((KVT*)a.k_cache + off) = kst;
+                        *(uint4*)((KVT*)a.v_cache + off) = vst;
+                    }
+                }
             }
         }
     }
-    // projected q of the group's heads and the new k, v of head g
-    const int qkvr = (a.Hq + 2 * a.Hkv) * HD;
-    const float* src = a.qkv + (long)b * qkvr;
-    float q[kMaxGroup][CE];
+    __syncthreads();
+    // the new token's row, in stored form, replaces the (unread) cache row
+    if (has_new) {
 #pragma unroll
-    for (int hl = 0; hl < kMaxGroup; ++hl) {
-        if (hl < G) load_f32xN(src + (g * G + hl) * HD + li * CE, q[hl], CE);
-        else {
-#pragma unroll
-            for (int e = 0; e < CE; ++e) q[hl][e] = 0.f;
+        for (int i = 0; i < NP; ++i) {
+            const int t = t_begin + i * TPB + wave * TPW + slot;
+            if (t == p) { kraw[i] = knew[li]; vraw[i] = vnew[li]; }
         }
     }
-    float kn[CE], vn[CE];
-    load_f32xN(src + a.Hq * HD + g * HD + li * CE, kn, CE);
-    load_f32xN(src + (a.Hq + a.Hkv) * HD + g * HD + li * CE, vn, CE);
-
-    // rotation angles of this lane's elements: i = (li mod LPT/2) * CE + e
-    float cs[CE], sn[CE];
+    // scores s = q . k / sqrt(hd): heads in a rolled loop (q from LDS), the
+    // token passes unrolled so the K rows stay in registers
+    for (int hl = 0; hl < nh; ++hl) {
+        float qv[CE];
 #pragma unroll
-    for (int e = 0; e < CE; ++e) {
-        const int i = (li % (LPT / 2)) * CE + e;
-        const double inv = pow((double)a.theta, -2.0 * (double)i / (double)HD);
-        double ang = (double)p * inv;
-        const double two_pi = 6.283185307179586476925286766559;
-        ang -= two_pi * rint(ang / two_pi);
-        sincosf((float)ang, &sn[e], &cs[e]);
-    }
-    if (a.qk_norm) {
+        for (int e = 0; e < CE; ++e) qv[e] = qs[hl][li * CE + e];
 #pragma unroll
-        for (int hl = 0; hl < kMaxGroup; ++hl) {
-            if (hl >= G) break;
-            float ss = 0.f;
-#pragma unroll
-            for (int e = 0; e < CE; ++e) ss += q[hl][e] * q[hl][e];
-            ss = group_sum<LPT>(ss);
-            const float r = 1.0f / sqrtf(ss / (float)HD + a.eps);
-#pragma unroll
-            for (int e = 0; e < CE; ++e) q[hl][e] = q[hl][e] * r * load_scalar<WT>(a.q_norm, li * CE + e);
-        }
-        float ss = 0.f;
-#pragma unroll
-        for (int e = 0; e < CE; ++e) ss += kn[e] * kn[e];
-        ss = group_sum<LPT>(ss);
-        const float r = 1.0f / sqrtf(ss / (float)HD + a.eps);
-#pragma unroll
-        for (int e = 0; e < CE; ++e) kn[e] = kn[e] * r * load_scalar<WT>(a.k_norm, li * CE + e);
-    }
-#pragma unroll
-    for (int hl = 0; hl < kMaxGroup; ++hl)
-        if (hl < G) rope_lane<CE, LPT>(q[hl], cs, sn, lower);
-    rope_lane<CE, LPT>(kn, cs, sn, lower);
-    // stored form of the new K/V (rounded to the cache type) and the append
-    const uint4 kst = pack16<KVT>(kn), vst = pack16<KVT>(vn);
-    float kq[CE], vq[CE];
-    widen16(kst, kq);
-    widen16(vst, vq);
-    if (p >= t_begin && p < t_end && wave == 0 && slot == 0) {
-        const int page_id = bt[p / a.page];
-        if (page_id >= 0 && page_id < a.num_pages) {
-            const long off = (((long)page_id * a.Hkv + g) * a.page + (p % a.page)) * HD + li * CE;
-            *(uint4*)((KVT*)a.k_cache + off) = kst;
-            *(uint4*)((KVT*)a.v_cache + off) = vst;
-        }
-    }
-
-    // scores s = q . k / sqrt(hd)
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-        if (i * TPB >= n) break;
-        const int t = t_begin + i * TPB + wave * TPW + slot;
-        float kf[CE];
-        widen16(kraw[i], kf);
-        if (t == p) {
-#pragma unroll
-            for (int e = 0; e < CE; ++e) kf[e] = kq[e];
-        }
-#pragma unroll
-        for (int hl = 0; hl < kMaxGroup; ++hl) {
-            if (hl >= G) break;
+        for (int i = 0; i < NP; ++i) {
+            if (i * TPB >= n) break;
+            const int t = t_begin + i * TPB + wave * TPW + slot;
+            float kf[CE];
+            widen16(kraw[i], kf);
             float d = 0.f;
 #pragma unroll
-            for (int e = 0; e < CE; ++e) d = fmaf(q[hl][e], kf[e], d);
+            for (int e = 0; e < CE; ++e) d = fmaf(qv[e], kf[e], d);
             d = group_sum<LPT>(d);
             if (li == 0 && t < t_end) sc[hl][t - t_begin] = d * a.scale;
         }
     }
     __syncthreads();
-    for (int hl = wave; hl < G; hl += 4) {
+    // per head: m = max s, p = exp(s - m), l = sum p
+    for (int hl = wave; hl < nh; hl += NWV) {
         float m = -INFINITY;
         for (int j = lane; j < n; j += kWave) m = fmaxf(m, sc[hl][j]);
-        m = wave_max(m);
+        m = group_max<kWave>(m);
         float l = 0.f;
         for (int j = lane; j < n; j += kWave) {
             const float e = expf(sc[hl][j] - m);
@@ -201,89 +212,103 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
             l += e;
         }
         l = group_sum<kWave>(l);
-        if (lane == 0) { ml[hl][0] = m; ml[hl][1] = l; }
+        if (lane == 0) { mls[hl][0] = m; mls[hl][1] = l; }
     }
     __syncthreads();
-    // o = sum_t exp(s_t - m) v_t
-    float o[kMaxGroup][CE];
+    // o = sum_t p_t v_t, one head at a time
+    for (int hl = 0; hl < nh; ++hl) {
+        float o[CE];
 #pragma unroll
-    for (int hl = 0; hl < kMaxGroup; ++hl)
+        for (int e = 0; e < CE; ++e) o[e] = 0.f;
 #pragma unroll
-        for (int e = 0; e < CE; ++e) o[hl][e] = 0.f;
+        for (int i = 0; i < NP; ++i) {
+            if (i * TPB >= n) break;
+            const int t = t_begin + i * TPB + wave * TPW + slot;
+            const float pr = t < t_end ? sc[hl][t - t_begin] : 0.f;
+            float vf[CE];
+            widen16(vraw[i], vf);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-        if (i * TPB >= n) break;
-        const int t = t_begin + i * TPB + wave * TPW + slot;
-        if (t >= t_end) continue;
-        float vf[CE];
-        widen16(vraw[i], vf);
-        if (t == p) {
-#pragma unroll
-            for (int e = 0; e < CE; ++e) vf[e] = vq[e];
+            for (int e = 0; e < CE; ++e) o[e] = fmaf(pr, vf[e], o[e]);
         }
-#pragma unroll
-        for (int hl = 0; hl < kMaxGroup; ++hl) {
-            if (hl >= G) break;
-            const float pr = sc[hl][t - t_begin];
-#pragma unroll
-            for (int e = 0; e < CE; ++e) o[hl][e] = fmaf(pr, vf[e], o[hl][e]);
-        }
-    }
-#pragma unroll
-    for (int hl = 0; hl < kMaxGroup; ++hl) {
-        if (hl >= G) break;
 #pragma unroll
         for (int e = 0; e < CE; ++e) {
-            float v = o[hl][e];
-#pragma unroll
-            for (int off = kWave / 2; off >= LPT; off >>= 1) v += __shfl_xor(v, off, kWave);
+            const float v = strided_sum<LPT>(o[e]);
             if (slot == 0) red[wave][hl][li * CE + e] = v;
         }
     }
     __syncthreads();
-    float* ctx = a.ctx + ((long)b * a.Hq + g * G) * HD;
+    const int hq0 = g * G + h0;   // first query head of this workgroup
     if (ns == 1) {
-        for (int idx = tid; idx < G * HD; idx += kAttnThreads) {
+        float* ctx = a.ctx + ((long)b * a.Hq + hq0) * HD;
+        for (int idx = tid; idx < nh * HD; idx += NT) {
             const int hl = idx / HD, d = idx - hl * HD;
-            ctx[idx] = (red[0][hl][d] + red[1][hl][d] + red[2][hl][d] + red[3][hl][d]) / ml[hl][1];
+            float v = 0.f;
+#pragma unroll
+            for (int w = 0; w < NWV; ++w) v += red[w][hl][d];
+            ctx[idx] = v / mls[hl][1];
         }
         return;
     }
-    // several splits: publish the partial; the last split to arrive merges
-    float* part = a.part + (((long)b * a.Hkv + g) * a.S) * G * (HD + 2);
-    const long sstride = (long)G * (HD + 2);
-    for (int idx = tid; idx < G * HD; idx += kAttnThreads) {
+    // several splits: publish (o, m, l) for the merge kernel; layout [B][Hq][S][hd + 2]
+    for (int idx = tid; idx < nh * HD; idx += NT) {
         const int hl = idx / HD, d = idx - hl * HD;
-        part[s * sstride + hl * (HD + 2) + d] = red[0][hl][d] + red[1][hl][d] + red[2][hl][d] + red[3][hl][d];
+        float v = 0.f;
+#pragma unroll
+        for (int w = 0; w < NWV; ++w) v += red[w][hl][d];
+        a.part[(((long)b * a.Hq + hq0 + hl) * a.S + s) * (HD + 2) + d] = v;
     }
-    if (tid < G) {
-        part[s * sstride + tid * (HD + 2) + HD] = ml[tid][0];
-        part[s * sstride + tid * (HD + 2) + HD + 1] = ml[tid][1];
-    }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) is_last = atomicAdd(a.counters + (long)b * a.Hkv + g, 1u) == (unsigned)(ns - 1);
-    __syncthreads();
-    if (!is_last) return;
-    __threadfence();
-    for (int idx = tid; idx < G * HD; idx += kAttnThreads) {
-        const int hl = idx / HD, d = idx - hl * HD;
-        const float* ps = part + hl * (HD + 2);
-        float M = -INFINITY;
-        for (int j = 0; j < ns; ++j) M = fmaxf(M, ps[j * sstride + HD]);
-        float L = 0.f, O = 0.f;
-        for (int j = 0; j < ns; ++j) {
-            const float w = expf(ps[j * sstride + HD] - M);
-            L = fmaf(ps[j * sstride + HD + 1], w, L);
-            O = fmaf(ps[j * sstride + d], w, O);
-        }
-        ctx[idx] = O / L;
+    if (tid < nh) {
+        float* pm = a.part + (((long)b * a.Hq + hq0 + tid) * a.S + s) * (HD + 2) + HD;
+        pm[0] = mls[tid][0];
+        pm[1] = mls[tid][1];
     }
 }
 
+// Merge of the split partials of one (query head, sequence): M = max_s m_s,
+// ctx = sum_s o_s e^(m_s - M) / sum_s l_s e^(m_s - M).
+__global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a) {
+    __shared__ float wgt[kMaxSplits];
+    __shared__ float lsum;
+    const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+    const int p = a.pos[b];
+    if (p < 0 || p >= a.capacity) return;
+    const int ns = min(min(a.S, kMaxSplits), (p + 1 + a.chunk - 1) / a.chunk);
+    if (ns <= 1) return;   // one split: the attention kernel wrote the output itself
+    const float* base = a.part + ((long)b * a.Hq + h) * a.S * (a.hd + 2);
+    if (d < kWave) {   // wave 0: weights of the splits
+        float m = -INFINITY;
+        for (int j = d; j < ns; j += kWave) m = fmaxf(m, base[j * (a.hd + 2) + a.hd]);
+        m = group_max<kWave>(m);
+        float l = 0.f;
+        for (int j = d; j < ns; j += kWave) {
+            const float w = expf(base[j * (a.hd + 2) + a.hd] - m);
+            wgt[j] = w;
+            l = fmaf(base[j * (a.hd + 2) + a.hd + 1], w, l);
+        }
+        l = group_sum<kWave>(l);
+        if (d == 0) lsum = l;
+    }
+    __syncthreads();
+    if (d >= a.hd) return;
+    float o = 0.f;
+    int j = 0;
+    for (; j + 4 <= ns; j += 4) {
+        const float o0 = base[(j + 0) * (a.hd + 2) + d], o1 = base[(j + 1) * (a.hd + 2) + d];
+        const float o2 = base[(j + 2) * (a.hd + 2) + d], o3 = base[(j + 3) * (a.hd + 2) + d];
+        o = fmaf(o0, wgt[j], o);
+        o = fmaf(o1, wgt[j + 1], o);
+        o = fmaf(o2, wgt[j + 2], o);
+        o = fmaf(o3, wgt[j + 3], o);
+    }
+    for (; j < ns; ++j) o = fmaf(base[j * (a.hd + 2) + d], wgt[j], o);
+    a.ctx[((long)b * a.Hq + h) * a.hd + d] = o / lsum;
+}
+
 hipError_t launch_attention(const AttnArgs& a, int w_is_bf16, int kv_is_bf16, hipStream_t s) {
-    dim3 grid(a.S, a.Hkv, a.B);
-    dim3 block(kAttnThreads);
+    const int G = a.Hq / a.Hkv;
+    const int hgroups = (G + a.hpw - 1) / a.hpw;
+    dim3 grid(a.S, a.Hkv * hgroups, a.B);
+    dim3 block(kAttnWaves * kWave);
 #define QD_ATTN(WT, KVT, HD) hipLaunchKernelGGL((attn_kernel<WT, KVT, HD>), grid, block, 0, s, a)
     if (a.hd == 64) {
         if (w_is_bf16) { if (kv_is_bf16) QD_ATTN(uint16_t, uint16_t, 64); else QD_ATTN(uint16_t, float, 64); }
@@ -293,6 +318,46 @@ hipError_t launch_attention(const AttnArgs& a, int w_is_bf16, int kv_is_bf16, hi
         else { if (kv_is_bf16) QD_ATTN(float, uint16_t, 128); else QD_ATTN(float, float, 128); }
     }
 #undef QD_ATTN
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.S == 1) return e;
+    hipLaunchKernelGGL(attn_merge_kernel, dim3(a.Hq, a.B), dim3(128), 0, s, a);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Step input: x = embedding row (exact widen; tied table, nanoinfer page, model
+// notes) or the given x_in row, and the step's RoPE table: for position p and
+// pair i, the angle p * theta^(-2i/hd) is formed and reduced modulo 2*pi in
+// double, then its cosine and sine are taken in float. An id outside [0, V)
+// yields a zero row instead of a fault.
+template <typename WT>
+__global__ __launch_bounds__(256) void step_input_kernel(StepInputArgs a) {
+    const int b = blockIdx.x, tid = threadIdx.x;
+    float* x = a.x + (long)b * a.D;
+    if (a.tokens) {
+        const int tok = a.tokens[b];
+        const bool ok = tok >= 0 && tok < a.V;
+        const void* row = (const char*)a.embed + (ok ? (long)tok * a.D * (long)sizeof(WT) : 0L);
+        for (int d = tid; d < a.D; d += blockDim.x) x[d] = ok ? load_scalar<WT>(row, d) : 0.f;
+    } else {
+        for (int d = tid; d < a.D; d += blockDim.x) x[d] = a.x_in[(long)b * a.D + d];
+    }
+    const int half = a.hd / 2;
+    if (tid < half) {
+        const int p = a.pos[b];
+        const double inv = pow((double)a.theta, -2.0 * (double)tid / (double)a.hd);
+        double ang = (double)p * inv;
+        const double two_pi = 6.283185307179586476925286766559;
+        ang -= two_pi * rint(ang / two_pi);
+        float sv, cv;
+        sincosf((float)ang, &sv, &cv);
+        a.rope[(long)b * half + tid] = make_float2(cv, sv);
+    }
+}
+
+hipError_t launch_step_input(const StepInputArgs& a, int w_is_bf16, hipStream_t s) {
+    if (w_is_bf16) hipLaunchKernelGGL((step_input_kernel<uint16_t>), dim3(a.B), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((step_input_kernel<float>), dim3(a.B), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

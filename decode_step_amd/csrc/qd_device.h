@@ -62,18 +62,76 @@ template <typename T> __device__ __forceinline__ T from_f32(float f);
 template <> __device__ __forceinline__ uint16_t from_f32<uint16_t>(float f) { return f32_to_bf16(f); }
 template <> __device__ __forceinline__ float from_f32<float>(float f) { return f; }
 
-// Sum over groups of W consecutive lanes (W a power of two <= 64); every lane
-// of the group ends with the group's total.
+// Cross-lane reductions on 64-lane wavefronts. Within a 16-lane row they use
+// DPP operand modifiers (quad_perm, row_half_mirror, row_mirror, row_ror), which
+// fold into the VALU op; across rows they use gfx950's permlane16/permlane32
+// swaps. Every lane of a group ends with the same bits (each step adds a pair
+// in both lanes, and a + b == b + a exactly).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;   // lane i <-> 7 - i within 8
+constexpr int kDppMirror = 0x140;       // lane i <-> 15 - i within 16
+constexpr int kDppRor8 = 0x128;         // lane i <- (i + 8) mod 16, i.e. i ^ 8
+
+// the other half of a permlane swap pair: (lane's own value, partner's value) summed
+__device__ __forceinline__ float swap16_sum(float v) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
+    return __int_as_float(r[0]) + __int_as_float(r[1]);
+}
+__device__ __forceinline__ float swap32_sum(float v) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+    return __int_as_float(r[0]) + __int_as_float(r[1]);
+}
+__device__ __forceinline__ float swap16_max(float v) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
+    return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+}
+__device__ __forceinline__ float swap32_max(float v) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+    return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+}
+
+// Sum over aligned groups of W lanes (W a power of two <= 64); every lane of a
+// group ends with the group's total.
 template <int W>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-    for (int off = W / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+    if (W >= 2) v += dpp_f<kDppQuadXor1>(v);
+    if (W >= 4) v += dpp_f<kDppQuadXor2>(v);
+    if (W >= 8) v += dpp_f<kDppHalfMirror>(v);
+    if (W >= 16) v += dpp_f<kDppMirror>(v);
+    if (W >= 32) v = swap16_sum(v);
+    if (W >= 64) v = swap32_sum(v);
     return v;
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+template <int W>
+__device__ __forceinline__ float group_max(float v) {
+    if (W >= 2) v = fmaxf(v, dpp_f<kDppQuadXor1>(v));
+    if (W >= 4) v = fmaxf(v, dpp_f<kDppQuadXor2>(v));
+    if (W >= 8) v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+    if (W >= 16) v = fmaxf(v, dpp_f<kDppMirror>(v));
+    if (W >= 32) v = swap16_max(v);
+    if (W >= 64) v = swap32_max(v);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) { return group_max<kWave>(v); }
+
+// Sum over the lanes that share lane % FROM (FROM in {8, 16, 32}): adds lanes
+// i ^ FROM, i ^ 2*FROM, ... up to i ^ 32.
+template <int FROM>
+__device__ __forceinline__ float strided_sum(float v) {
+    if (FROM <= 8) v += dpp_f<kDppRor8>(v);
+    if (FROM <= 16) v = swap16_sum(v);
+    v = swap32_sum(v);
     return v;
 }
 
@@ -82,11 +140,34 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
     return v > bv || (v == bv && i < bi);
 }
 
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(float& v, int& i) {
+    const float ov = dpp_f<CTRL>(v);
+    const int oi = dpp_i<CTRL>(i);
+    if (better(ov, oi, v, i)) { v = ov; i = oi; }
+}
+
+// Whole-wave argmax: every lane ends with the best (value, index) of the wave.
 __device__ __forceinline__ void wave_argmax(float& v, int& i) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        float ov = __shfl_xor(v, off, kWave);
-        int oi = __shfl_xor(i, off, kWave);
+    argmax_step<kDppQuadXor1>(v, i);
+    argmax_step<kDppQuadXor2>(v, i);
+    argmax_step<kDppHalfMirror>(v, i);
+    argmax_step<kDppMirror>(v, i);
+    const int lane = __lane_id();
+    {
+        auto rv = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
+        auto ri = __builtin_amdgcn_permlane16_swap(i, i, false, false);
+        const bool odd_row = (lane >> 4) & 1;
+        const float ov = __int_as_float(odd_row ? rv[0] : rv[1]);
+        const int oi = odd_row ? ri[0] : ri[1];
+        if (better(ov, oi, v, i)) { v = ov; i = oi; }
+    }
+    {
+        auto rv = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+        auto ri = __builtin_amdgcn_permlane32_swap(i, i, false, false);
+        const bool upper = lane >= 32;
+        const float ov = __int_as_float(upper ? rv[0] : rv[1]);
+        const int oi = upper ? ri[0] : ri[1];
         if (better(ov, oi, v, i)) { v = ov; i = oi; }
     }
 }

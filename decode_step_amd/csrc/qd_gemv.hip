@@ -211,14 +211,23 @@ static hipError_t gemv1_dispatch(const GemvArgs& a, int cfg, int* grid_out, int 
     }
 }
 
-// Shape heuristic: few rows -> split K over the waves of a workgroup so that
-// about 200+ workgroups share the matrix; many rows -> whole rows per wave.
+// Shape heuristic: the largest row tile that still gives at least 256
+// workgroups (one per CU), so a matrix is spread over the whole chip; the
+// lm_head (grid-strided over many tiles) keeps the largest tile.
 static int gemv1_pick(int N, int K, int epi) {
     const bool small_k = K <= 2048;
     if (epi == EPI_LOGITS) return small_k ? G_SMALLK_UR2 : G_BIGK_UR2;
-    if (small_k) return N <= 2048 ? G_SMALLK_FEWROWS : G_SMALLK;
-    if (N <= 4096 && K > 8192) return G_BIGK_FEWROWS;
-    return epi == EPI_SWIGLU ? G_BIGK : G_BIGK_UR2;
+    const int cfgs_small[3] = {G_SMALLK_UR2, G_SMALLK, G_SMALLK_FEWROWS};
+    const int rpt_small[3] = {32, 16, 4};
+    const int cfgs_big[3] = {G_BIGK_UR2, G_BIGK, G_BIGK_FEWROWS};
+    const int rpt_big[3] = {8, 4, 2};
+    const int* cfgs = small_k ? cfgs_small : cfgs_big;
+    const int* rpt = small_k ? rpt_small : rpt_big;
+    for (int i = 0; i < 3; ++i) {
+        if (epi == EPI_SWIGLU && cfgs[i] == G_SMALLK_UR2) continue;
+        if ((N + rpt[i] - 1) / rpt[i] >= 256) return cfgs[i];
+    }
+    return cfgs[2];
 }
 
 hipError_t launch_gemv1(const GemvArgs& a, int w_is_bf16, int epi, int grid_cap, int* grid_out, hipStream_t s) {

@@ -49,14 +49,31 @@ struct AttnArgs {
     const void* k_norm;
     int qk_norm;
     float eps, theta;
-    float* part;            // [B][Hkv][S][G][hd+2]: o[hd], m, l
-    unsigned* counters;     // [B][Hkv], zero when the kernel starts
+    float* part;            // [B][Hq][S][hd+2]: o[hd], m, l of each split
+    const float2* rope;     // [B][hd/2] (cos, sin) of the step's positions
     float* ctx;             // [B][Hq*hd]
     int Hq, Hkv, hd, page, chunk, S, B;
+    int hpw;                // query heads per workgroup
     float scale;
 };
+// attention kernel, plus the split merge kernel when S > 1
 hipError_t launch_attention(const AttnArgs& a, int w_is_bf16, int kv_is_bf16, hipStream_t s);
 int attn_max_chunk(int hd, int kv_is_bf16);
+int attn_max_splits();
+
+// x = embedding rows of `tokens` (or a copy of x_in), plus the RoPE table of the
+// step's positions (qd_attention.hip).
+struct StepInputArgs {
+    const int* tokens;
+    const void* embed;
+    const float* x_in;
+    float* x;
+    const int* pos;
+    float2* rope;           // [B][hd/2]
+    int B, D, V, hd;
+    float theta;
+};
+hipError_t launch_step_input(const StepInputArgs& a, int w_is_bf16, hipStream_t s);
 
 hipError_t launch_embed(const int* tokens, const void* embed, float* x, int B, int D, int V,
                         int w_is_bf16, hipStream_t s);
