@@ -99,6 +99,83 @@ def cpu_baseline(wl, case_host, ctx, tokens, budget_s=12.0):
                       f"after one untimed step that widens the weights"}
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def prefill_flops(shape, n, start=0):
+    """2*M*N*K over the four projection GEMMs, and the causal attention's
+    2 * Hq * hd * (sum over rows of keys attended) * 2 (scores and P.V)."""
+    D, F, qd, kvd = shape.hidden, shape.ffn, shape.q_dim, shape.kv_dim
+    gemm = 2 * n * ((qd + 2 * kvd) * D + D * qd + 2 * F * D + D * F)
+    keys = sum(start + i + 1 for i in range(n))
+    attn = 2 * shape.n_q_heads * shape.head_dim * keys * 2
+    return gemm, attn
+
+
+def bench_prefill(wl, args):
+    import torch
+    from decode_step_amd import qd as Q
+    from decode_step_amd.runner import DecodeRunner
+    from workloads import synth
+    sh, n = wl.shape, wl.prefill_tokens
+    w = synth.make_weights(sh, seed=wl.seed, device="cuda", with_embed=False)
+    kv = synth.make_kv(sh, np.array([0]), extra=n, seed=wl.seed, device="cuda")
+    runner = DecodeRunner(sh, w, kv.k, kv.v, kv.block_table, max_batch=1, max_ctx=n, device="cuda",
+                          prefill_tokens=n)
+    x = synth.make_x(n, sh.hidden, seed=wl.seed, dtype="bf16", device="cuda")
+    x_out = torch.empty(n, sh.hidden, device="cuda")
+
+    def step():
+        runner.prefill(0, n, 0, x, x_out, stream=torch.cuda.current_stream())
+
+    for _ in range(args.warmup):
+        step()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    gemm_f, attn_f = prefill_flops(sh, n)
+    ms = 1e3 * el / args.steps
+    # profiled pass: GEMM launches and attention
+    Q.qd_profile_enable((1 << Q.QD_K_PREFILL_GEMM) | (1 << Q.QD_K_PREFILL_ATTN))
+    np_ = min(args.steps, 200)
+    for _ in range(np_):
+        step()
+    torch.cuda.synchronize()
+    ng, ms_g = Q.qd_profile_read(Q.QD_K_PREFILL_GEMM)
+    na, ms_a = Q.qd_profile_read(Q.QD_K_PREFILL_ATTN)
+    Q.qd_profile_enable(0)
+    gemm_s = ms_g * 1e-3 / np_          # all four GEMM launches of one block
+    gemm_tfs = gemm_f / gemm_s / 1e12
+    print(f"[bench] {wl.name}: {ms:.4f} ms/block, GEMMs {1e6 * gemm_s:.1f} us = {gemm_tfs:.1f} TFLOP/s "
+          f"({100 * gemm_tfs / MFMA_BF16_PEAK_TFLOPS:.1f}% of bf16 MFMA peak), attention "
+          f"{1e3 * ms_a / np_:.1f} us", file=sys.stderr, flush=True)
+    rec = {"metric": "prefill tokens/s + bf16 MFMA utilisation, 8B-shape block, 512 tokens",
+           "value": round(n * args.steps / el, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": wl.name, "tokens": n, "start": 0}, "launch": "hip_graph",
+           "block_tflops": round((gemm_f + attn_f) / el * args.steps / 1e12, 1),
+           "roofline": {"bound": "mfma", "achieved": round(gemm_tfs, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(gemm_tfs / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                        "kernel": "mfma_gemm (4 launches per block)", "flops_per_block": int(gemm_f),
+                        "avg_block_gemm_us": round(1e6 * gemm_s, 2)},
+           "attention_us": round(1e3 * ms_a / np_, 2), "cpu_baseline": None}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -122,6 +199,8 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     wl = S.WORKLOADS[args.workload]
+    if wl.kind == "prefill":
+        return bench_prefill(wl, args)
     shape = wl.shape
     dev = "cuda"
     ctx = synth.make_ctx(wl.batch, wl.past, wl.ctx_range, wl.seed)

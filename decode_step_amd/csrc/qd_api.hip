@@ -68,6 +68,7 @@ struct DecodePlan {
 // makes more than 1024 workgroups. Returns false when the context needs more
 // splits than one merge combines.
 bool plan_split(const qd_config* c, int B, int max_tokens, int* chunk, int* S, int* hpw) {
+    // B = sequences (decode) or query rows (prefill); max_tokens = longest context
     int ch = qd::attn_max_chunk(c->head_dim, c->kv_dtype == QD_BF16);
     ch = ch / c->page_size * c->page_size;
     *chunk = ch;
@@ -95,6 +96,27 @@ DecodePlan plan_decode(const qd_config* c, int B, int S, int chunk) {
     p.off_logits = take(sizeof(float) * (size_t)B * p.V);
     p.off_pv = take(sizeof(float) * B * kLogitsGridCap);
     p.off_pi = take(sizeof(int) * B * kLogitsGridCap);
+    p.total = o;
+    return p;
+}
+
+struct PrefillPlan {
+    size_t off_nrm, off_qkv, off_q, off_part, off_ctx, off_ctxb, off_h, total;
+};
+
+PrefillPlan plan_prefill(const qd_config* c, int N, int S) {
+    PrefillPlan p{};
+    const int qkvr = (c->n_q_heads + 2 * c->n_kv_heads) * c->head_dim;
+    const size_t qdim = (size_t)c->n_q_heads * c->head_dim;
+    size_t o = 0;
+    auto take = [&](size_t bytes) { size_t at = o; o = round_up(o + bytes, 256); return at; };
+    p.off_nrm = take(2 * (size_t)N * c->hidden);            // bf16 normed rows (reused by the MLP norm)
+    p.off_qkv = take(4 * (size_t)N * qkvr);
+    p.off_q = take(4 * (size_t)N * qdim);
+    p.off_part = take(4 * (size_t)N * qdim / c->head_dim * S * (c->head_dim + 2));
+    p.off_ctx = take(4 * (size_t)N * qdim);
+    p.off_ctxb = take(2 * (size_t)N * qdim);
+    p.off_h = take(2 * (size_t)N * c->ffn);
     p.total = o;
     return p;
 }
@@ -187,7 +209,12 @@ int32_t qd_abi_version(void) { return QD_ABI_VERSION; }
 
 size_t qd_workspace_bytes(const qd_config* cfg, int32_t batch, int32_t max_ctx, int32_t prefill_tokens) {
     if (check_config(cfg) != QD_OK) return 0;
-    if (prefill_tokens > 0) return 0;   // prefill plan added with the MFMA path
+    if (prefill_tokens > 0) {
+        if (max_ctx < prefill_tokens) return 0;
+        int chunk, S, hpw;
+        if (!plan_split(cfg, prefill_tokens, max_ctx, &chunk, &S, &hpw)) return 0;
+        return plan_prefill(cfg, prefill_tokens, S).total;
+    }
     if (batch < 1 || batch > kMaxBatch || max_ctx < 1) return 0;
     int chunk, S, hpw;
     if (!plan_split(cfg, batch, max_ctx, &chunk, &S, &hpw)) return 0;
@@ -275,6 +302,7 @@ qd_status qd_decode_step(const qd_config* cfg, const qd_weights* w, const qd_kv*
         at.eps = c.rms_eps; at.theta = c.rope_theta; at.part = part; at.rope = rope; at.ctx = ctx;
         at.Hq = P.Hq; at.Hkv = P.Hkv; at.hd = P.hd; at.page = c.page_size; at.chunk = P.chunk; at.S = P.S;
         at.B = B; at.hpw = hpw; at.scale = 1.0f / sqrtf((float)P.hd);
+        at.prefill_start = -1; at.q_rot = nullptr;
         QD_LAUNCH_K(QD_K_ATTN, qd::launch_attention(at, wbf, kvbf, s), "attention");
         // o_proj + residual
         qd::GemvArgs go{};
@@ -365,9 +393,97 @@ qd_status qd_prefill_block(const qd_config* cfg, const qd_layer* layer, int32_t 
                            int32_t n_tokens, int32_t start_pos, const void* x_in, int32_t x_dtype,
                            float* x_out, void* workspace, size_t workspace_bytes, void* stream) {
     g_err.clear();
-    (void)cfg; (void)layer; (void)layer_index; (void)kv; (void)n_tokens; (void)start_pos; (void)x_in;
-    (void)x_dtype; (void)x_out; (void)workspace; (void)workspace_bytes; (void)stream;
-    return fail(QD_EUNSUPPORTED, "qd_prefill_block: MFMA prefill path not built yet");
+    qd_status st = check_config(cfg);
+    if (st != QD_OK) return st;
+    const qd_config& c = *cfg;
+    if (c.w_dtype != QD_BF16) return fail(QD_EUNSUPPORTED, "prefill needs bf16 weights (MFMA bf16 GEMMs)");
+    if (!layer) return fail(QD_EINVAL, "layer is NULL");
+    if ((st = check_layer(cfg, layer, layer_index)) != QD_OK) return st;
+    if (layer_index < 0 || layer_index >= c.n_layers)
+        return fail(QD_ESHAPE, "layer_index %d outside [0, %d)", layer_index, c.n_layers);
+    if (n_tokens < 1) return fail(QD_ESHAPE, "n_tokens %d < 1", n_tokens);
+    if (start_pos < 0) return fail(QD_EPOSITION, "start_pos %d < 0", start_pos);
+    if (!x_in || !x_out) return fail(QD_EINVAL, "x_in or x_out is NULL");
+    if (x_dtype != QD_BF16 && x_dtype != QD_F32) return fail(QD_EINVAL, "x_dtype %d", x_dtype);
+    if (!aligned4(x_in) || !aligned4(x_out)) return fail(QD_EALIGN, "x_in / x_out not 4-byte aligned");
+    // every position start .. start + n - 1 must have a page in row 0 of the block table
+    const int32_t last = start_pos + n_tokens - 1;
+    int max_tokens = 0;
+    if ((st = check_kv_positions(cfg, kv, 1, &last, &max_tokens)) != QD_OK) return st;
+    void* kc = kv->k_pages_host[layer_index];
+    void* vc = kv->v_pages_host[layer_index];
+    if (!kc || !vc) return fail(QD_EINVAL, "kv pages of layer %d NULL", layer_index);
+    if (!aligned16(kc) || !aligned16(vc)) return fail(QD_EALIGN, "kv pages of layer %d not 16-byte aligned", layer_index);
+    int chunk, S, hpw;
+    if (!plan_split(cfg, n_tokens, max_tokens, &chunk, &S, &hpw))
+        return fail(QD_ECAPACITY, "context of %d tokens needs %d attention splits > %d", max_tokens, S,
+                    qd::attn_max_splits());
+    const PrefillPlan P = plan_prefill(cfg, n_tokens, S);
+    if (!workspace) return fail(QD_EWORKSPACE, "workspace is NULL");
+    if (((uintptr_t)workspace & 255u) != 0) return fail(QD_EALIGN, "workspace not 256-byte aligned");
+    if (workspace_bytes < P.total)
+        return fail(QD_EWORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, P.total);
+
+    hipStream_t s = (hipStream_t)stream;
+    char* ws = (char*)workspace;
+    uint16_t* nrm = (uint16_t*)(ws + P.off_nrm);
+    float* qkv = (float*)(ws + P.off_qkv);
+    float* qrot = (float*)(ws + P.off_q);
+    float* part = (float*)(ws + P.off_part);
+    float* ctx = (float*)(ws + P.off_ctx);
+    uint16_t* ctxb = (uint16_t*)(ws + P.off_ctxb);
+    uint16_t* h = (uint16_t*)(ws + P.off_h);
+    const qd_layer& L = *layer;
+    const int N = n_tokens, D = c.hidden, Hq = c.n_q_heads, Hkv = c.n_kv_heads, hd = c.head_dim;
+    const int qkvr = (Hq + 2 * Hkv) * hd;
+    const int kvbf = c.kv_dtype == QD_BF16;
+
+    // RMSNorm -> bf16 operand; the input rows become the float32 residual in x_out
+    qd::PrefillNormArgs nr{};
+    if (x_dtype == QD_BF16) nr.x_bf16 = x_in; else nr.x_f32 = (const float*)x_in;
+    nr.x_res = x_out; nr.gain = L.attn_norm; nr.out = nrm; nr.rows = N; nr.D = D; nr.eps = c.rms_eps;
+    QD_LAUNCH(qd::launch_prefill_norm(nr, 1, s), "prefill norm");
+    // q|k|v = norm(x) W^T (+ bias)
+    qd::GemmArgs g{};
+    g.A = nrm; g.w[0] = L.wq; g.w[1] = L.wk; g.w[2] = L.wv; g.bias[0] = L.bq; g.bias[1] = L.bk; g.bias[2] = L.bv;
+    g.seg_end[0] = Hq * hd; g.seg_end[1] = (Hq + Hkv) * hd; g.seg_end[2] = qkvr;
+    g.M = N; g.N = qkvr; g.K = D; g.C = qkv; g.ldc = qkvr;
+    QD_LAUNCH_K(QD_K_PREFILL_GEMM, qd::launch_mfma_gemm(g, qd::GEMM_STORE, s), "qkv gemm");
+    // [q/k norm] + RoPE; K/V of every row into the cache
+    qd::PrefillRopeArgs rp{};
+    rp.qkv = qkv; rp.q_out = qrot; rp.k_cache = kc; rp.v_cache = vc; rp.block_table = kv->block_table;
+    rp.num_pages = kv->num_pages; rp.capacity = kv->max_blocks * c.page_size; rp.start = start_pos; rp.rows = N;
+    rp.q_norm = L.q_norm; rp.k_norm = L.k_norm; rp.qk_norm = c.qk_norm; rp.eps = c.rms_eps; rp.theta = c.rope_theta;
+    rp.Hq = Hq; rp.Hkv = Hkv; rp.hd = hd; rp.page = c.page_size;
+    QD_LAUNCH(qd::launch_prefill_rope_append(rp, 1, kvbf, s), "prefill rope/append");
+    // causal attention: row i attends over positions 0 .. start + i
+    qd::AttnArgs at{};
+    at.k_cache = kc; at.v_cache = vc; at.block_table = kv->block_table; at.max_blocks = kv->max_blocks;
+    at.num_pages = kv->num_pages; at.pos = nullptr; at.capacity = kv->max_blocks * c.page_size;
+    at.part = part; at.ctx = ctx; at.Hq = Hq; at.Hkv = Hkv; at.hd = hd; at.page = c.page_size;
+    at.chunk = chunk; at.S = S; at.B = N; at.hpw = hpw; at.scale = 1.0f / sqrtf((float)hd);
+    at.prefill_start = start_pos; at.q_rot = qrot;
+    QD_LAUNCH_K(QD_K_PREFILL_ATTN, qd::launch_attention(at, 1, kvbf, s), "prefill attention");
+    QD_LAUNCH(qd::launch_to_bf16(ctx, ctxb, (long)N * Hq * hd, s), "context to bf16");
+    // x += ctx W_o^T
+    qd::GemmArgs go{};
+    go.A = ctxb; go.w[0] = L.wo; go.seg_end[0] = go.seg_end[1] = go.seg_end[2] = D;
+    go.M = N; go.N = D; go.K = Hq * hd; go.C = x_out; go.ldc = D;
+    QD_LAUNCH_K(QD_K_PREFILL_GEMM, qd::launch_mfma_gemm(go, qd::GEMM_RESID, s), "o_proj gemm");
+    // RMSNorm -> bf16; h = silu(n W_g^T) * (n W_u^T) in bf16
+    qd::PrefillNormArgs n2{};
+    n2.x_f32 = x_out; n2.gain = L.mlp_norm; n2.out = nrm; n2.rows = N; n2.D = D; n2.eps = c.rms_eps;
+    QD_LAUNCH(qd::launch_prefill_norm(n2, 1, s), "prefill mlp norm");
+    qd::GemmArgs gu{};
+    gu.A = nrm; gu.w[0] = L.w_gate; gu.w[1] = L.w_up; gu.seg_end[0] = gu.seg_end[1] = gu.seg_end[2] = c.ffn;
+    gu.M = N; gu.N = c.ffn; gu.K = D; gu.C = h; gu.ldc = c.ffn;
+    QD_LAUNCH_K(QD_K_PREFILL_GEMM, qd::launch_mfma_gemm(gu, qd::GEMM_SWIGLU, s), "gate/up gemm");
+    // x += h W_d^T
+    qd::GemmArgs gd{};
+    gd.A = h; gd.w[0] = L.w_down; gd.seg_end[0] = gd.seg_end[1] = gd.seg_end[2] = D;
+    gd.M = N; gd.N = D; gd.K = c.ffn; gd.C = x_out; gd.ldc = D;
+    QD_LAUNCH_K(QD_K_PREFILL_GEMM, qd::launch_mfma_gemm(gd, qd::GEMM_RESID, s), "down gemm");
+    return QD_OK;
 }
 
 }  // extern "C"

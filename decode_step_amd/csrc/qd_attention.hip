@@ -84,7 +84,8 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_kernel(AttnArgs a) {
     const int hgroups = (G + a.hpw - 1) / a.hpw;
     const int s = blockIdx.x, g = blockIdx.y / hgroups, hg = blockIdx.y % hgroups, b = blockIdx.z;
     const int h0 = hg * a.hpw, nh = min(a.hpw, G - h0);   // query heads g*G + h0 .. + nh - 1
-    const int p = a.pos[b];
+    const bool prefill = a.prefill_start >= 0;
+    const int p = prefill ? a.prefill_start + b : a.pos[b];
     if (p < 0 || p >= a.capacity || a.chunk > MAXT || a.hpw > kMaxGroup || a.page < 16 || nh <= 0) return;
     const int T = p + 1;
     const int ns = min(a.S, (T + a.chunk - 1) / a.chunk);
@@ -92,10 +93,10 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_kernel(AttnArgs a) {
     if (t_begin >= T) return;
     const int t_end = min(T, t_begin + a.chunk);
     const int n = t_end - t_begin;
-    const bool has_new = p >= t_begin && p < t_end;
+    const bool has_new = !prefill && p >= t_begin && p < t_end;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
     const int li = lane % LPT, slot = lane / LPT;
-    const int* bt = a.block_table + (long)b * a.max_blocks;
+    const int* bt = a.block_table + (prefill ? 0L : (long)b * a.max_blocks);
 
     // page ids of this split's pages (an entry outside the pool reads as page 0
     // and is masked), then every K/V row load issued back to back
@@ -112,7 +113,7 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_kernel(AttnArgs a) {
         const int t = t_begin + i * TPB + wave * TPW + slot;
         const int tt = t < t_end ? t : t_begin;
         const int pg = spage[tt / a.page - pg0];
-        const bool ok = t < t_end && t != p && pg >= 0;
+        const bool ok = t < t_end && (t != p || prefill) && pg >= 0;
         const long off = (((long)max(pg, 0) * a.Hkv + g) * a.page + (tt % a.page)) * HD + li * CE;
         const uint4 kv = *(const uint4*)((const KVT*)a.k_cache + off);
         const uint4 vv = *(const uint4*)((const KVT*)a.v_cache + off);
@@ -121,7 +122,12 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_kernel(AttnArgs a) {
     }
     // wave 0: norm and rotation of this workgroup's query heads and of the new k
     // (one head-chunk of CE elements per lane, LPT lanes per head; index nh is k)
-    if (wave == 0) {
+    if (prefill) {   // q already normed and rotated
+        for (int idx = tid; idx < nh * HD; idx += NT) {
+            const int hl = idx / HD, d = idx - hl * HD;
+            qs[hl][d] = a.q_rot[((long)b * a.Hq + g * G + h0 + hl) * HD + d];
+        }
+    } else if (wave == 0) {
         const int qkvr = (a.Hq + 2 * a.Hkv) * HD;
         const float* src = a.qkv + (long)b * qkvr;
         const int items = (nh + (has_new ? 1 : 0)) * LPT;
@@ -270,7 +276,7 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a) {
     __shared__ float wgt[kMaxSplits];
     __shared__ float lsum;
     const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
-    const int p = a.pos[b];
+    const int p = a.prefill_start >= 0 ? a.prefill_start + b : a.pos[b];
     if (p < 0 || p >= a.capacity) return;
     const int ns = min(min(a.S, kMaxSplits), (p + 1 + a.chunk - 1) / a.chunk);
     if (ns <= 1) return;   // one split: the attention kernel wrote the output itself

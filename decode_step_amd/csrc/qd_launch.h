@@ -55,6 +55,11 @@ struct AttnArgs {
     int Hq, Hkv, hd, page, chunk, S, B;
     int hpw;                // query heads per workgroup
     float scale;
+    // prefill mode (prefill_start >= 0): work item z is row z of one sequence at
+    // position prefill_start + z, its q already normed and rotated in q_rot
+    // [rows][Hq][hd], its K/V already in the cache (block table row 0)
+    int prefill_start;
+    const float* q_rot;
 };
 // attention kernel, plus the split merge kernel when S > 1
 hipError_t launch_attention(const AttnArgs& a, int w_is_bf16, int kv_is_bf16, hipStream_t s);
@@ -84,5 +89,45 @@ hipError_t launch_kv_append(const float* k, const float* v, void* k_cache, void*
                             const int* block_table, int max_blocks, int num_pages, const int* pos,
                             int capacity, int Hkv, int hd, int page, int B, int kv_is_bf16,
                             hipStream_t s);
+
+// Prefill block (qd_prefill.hip).
+enum GemmEpi { GEMM_STORE = 0, GEMM_RESID = 1, GEMM_SWIGLU = 2 };
+struct GemmArgs {
+    const void* A;          // bf16 [M][K]
+    const void* w[3];       // bf16 row-major [rows][K] segments (SWIGLU: w[0] gate, w[1] up)
+    const void* bias[3];    // GEMM_STORE: optional per-segment bias (bf16)
+    int seg_end[3];         // cumulative rows of the segments (unused entries = N)
+    int M, N, K;            // N = output columns (SWIGLU: h columns)
+    void* C;                // float [M][ldc] (STORE, RESID) or bf16 [M][ldc] (SWIGLU)
+    int ldc;
+};
+hipError_t launch_mfma_gemm(const GemmArgs& a, int epi, hipStream_t s);
+
+struct PrefillNormArgs {
+    const void* x_bf16;     // input rows, bf16 ... or
+    const float* x_f32;     // ... float (exactly one is set)
+    float* x_res;           // optional: input widened into the float32 residual
+    const void* gain;
+    uint16_t* out;          // bf16 [rows][D]
+    int rows, D;
+    float eps;
+};
+hipError_t launch_prefill_norm(const PrefillNormArgs& a, int w_is_bf16, hipStream_t s);
+
+struct PrefillRopeArgs {
+    const float* qkv;       // [rows][Hq*hd + 2*Hkv*hd]
+    float* q_out;           // [rows][Hq][hd]
+    void* k_cache;
+    void* v_cache;
+    const int* block_table; // the sequence's row of the block table
+    int num_pages, capacity, start, rows;
+    const void* q_norm;
+    const void* k_norm;
+    int qk_norm;
+    float eps, theta;
+    int Hq, Hkv, hd, page;
+};
+hipError_t launch_prefill_rope_append(const PrefillRopeArgs& a, int w_is_bf16, int kv_is_bf16, hipStream_t s);
+hipError_t launch_to_bf16(const float* x, void* y, long n, hipStream_t s);
 
 }  // namespace qd

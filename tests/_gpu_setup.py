@@ -59,3 +59,34 @@ def guarded(n: int, device="cuda", pad: int = 1024, fill=float("nan")):
 def canaries_intact(full: torch.Tensor, n: int, pad: int = 1024) -> bool:
     f = full.cpu()
     return bool(torch.all(f[:pad] == 12345.0)) and bool(torch.all(f[pad + n:] == 12345.0))
+
+
+def kv_mismatch(dev_pool, host_pool, abs_frac=1e-4) -> str:
+    """Stored K/V agree when every element is within one bf16 step of its own
+    value (the float32 value the GPU rounds may sit across a rounding boundary
+    from the oracle's) plus abs_frac of the pool's largest magnitude (a value
+    that cancels to near zero carries the projection's absolute rounding
+    error, which can be many of its own tiny bf16 steps). Float32 pools use a
+    1e-5 relative bound instead of the bf16 step. Returns "" when they agree,
+    else a description of the worst element and the count over tolerance."""
+    g = synth.to_host_bits(dev_pool)
+    if g.dtype == np.uint16:
+        gw = (g.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        hw = (np.asarray(host_pool).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        step = np.ldexp(1.0, np.frexp(np.abs(hw))[1] - 8)
+    else:
+        gw = g.astype(np.float64)
+        hw = np.asarray(host_pool, dtype=np.float64)
+        step = 1e-5 * np.abs(hw)
+    tol = step + abs_frac * np.max(np.abs(hw))
+    over = np.abs(gw - hw) / tol
+    if np.all(over <= 1.0):
+        return ""
+    i = int(np.argmax(over))
+    idx = np.unravel_index(i, gw.shape)
+    return (f"{int(np.sum(over > 1.0))} of {over.size} elements over tolerance; worst at {idx}: "
+            f"gpu {gw.flat[i]:.6g} oracle {hw.flat[i]:.6g} tol {tol.flat[i]:.3g}")
+
+
+def kv_matches(dev_pool, host_pool, abs_frac=1e-4) -> bool:
+    return kv_mismatch(dev_pool, host_pool, abs_frac) == ""

@@ -187,3 +187,26 @@ def test_kv_append_checks(lib):
     f2 = Fixture(_cfg(), pos=(40,))
     _expect(Q.qd_kv_append(f2.cfg, f2.kv, 0, 1, FAKE, f2.pos.ctypes.data_as(POINTER(c_int32)),
                            FAKE, FAKE, None), Q.QD_ECAPACITY)
+
+
+def _prefill(f, n=10, start=0, x=FAKE, x_dtype=None, ws_bytes=1 << 40, layer_index=0):
+    return Q.qd_prefill_block(f.cfg, f.layers[0], layer_index, f.kv, n, start, x,
+                              Q.QD_BF16 if x_dtype is None else x_dtype, FAKE, FAKE, ws_bytes, None)
+
+
+def test_prefill_checks(lib):
+    f = Fixture(_cfg(), pos=(5,), max_blocks=2, num_pages=4)
+    _expect(_prefill(Fixture(_cfg(w_dtype=Q.QD_F32))), Q.QD_EUNSUPPORTED)
+    _expect(_prefill(f, n=0), Q.QD_ESHAPE)
+    _expect(_prefill(f, start=-1), Q.QD_EPOSITION)
+    _expect(_prefill(f, n=30, start=5), Q.QD_ECAPACITY)      # position 34 >= 2 pages * 16
+    _expect(_prefill(f, x=None), Q.QD_EINVAL)
+    _expect(_prefill(f, x_dtype=9), Q.QD_EINVAL)
+    _expect(_prefill(f, ws_bytes=64), Q.QD_EWORKSPACE)
+    _expect(_prefill(f, layer_index=3), Q.QD_ESHAPE)
+
+
+def test_prefill_workspace_bytes(lib):
+    cfg = _cfg()
+    assert Q.qd_workspace_bytes(cfg, 1, 512, 512) > Q.qd_workspace_bytes(cfg, 1, 512, 16) > 0
+    assert Q.qd_workspace_bytes(cfg, 1, 10, 512) == 0     # max_ctx below the prefill length

@@ -18,7 +18,7 @@ import torch
 from oracle.qwen2 import OracleWeights, decode_step
 from workloads import shapes as S
 from workloads import synth
-from tests._gpu_setup import make_case, dev_i32, rel_err, guarded, canaries_intact
+from tests._gpu_setup import make_case, dev_i32, rel_err, guarded, canaries_intact, kv_matches
 
 pytestmark = pytest.mark.gpu
 
@@ -54,20 +54,9 @@ def _oracle(case, pos, tokens=None, x_in=None, with_logits=True, cache_layers=Tr
                        np.asarray(pos), tokens=tokens, x_in=x_in, with_logits=with_logits)
 
 
-def _cache_matches(case, f32_tol=1e-5):
-    """Every stored K/V equals the oracle's: within one bf16 unit in the last place
-    (the float32 value the GPU rounds may sit on the other side of a rounding
-    boundary from the oracle's), or within f32_tol relative for a float32 cache."""
-    for l in range(case.shape.n_layers):
-        for dev, host in ((case.kv.k[l], case.k_host[l]), (case.kv.v[l], case.v_host[l])):
-            g = synth.to_host_bits(dev)
-            if g.dtype == np.uint16:
-                d = np.abs(g.view(np.int16).astype(np.int32) - host.view(np.int16).astype(np.int32))
-                if d.max() > 1:
-                    return False
-            elif rel_err(g, host) > f32_tol:
-                return False
-    return True
+def _cache_matches(case):
+    return all(kv_matches(dev, host) for l in range(case.shape.n_layers)
+               for dev, host in ((case.kv.k[l], case.k_host[l]), (case.kv.v[l], case.v_host[l])))
 
 
 # ---------------------------------------------------------------- small ragged model

@@ -1,0 +1,127 @@
+"""GPU parity of the one-block causal prefill (qd_prefill_block through the C ABI)
+against the oracle's prefill_block on the same seeded inputs.
+
+The projections are bf16 MFMA GEMMs with float32 accumulation; the oracle rounds
+the same operands to bf16 (normed input, attention context, SwiGLU output).
+Tolerance on the block output, max |gpu - ref| / max |ref|: 2e-3 on the small
+shapes, 4e-3 on the 8B-class block. The float32 values the device rounds to bf16
+differ from the oracle's float64 ones, so some rounded operands land one bf16 step
+(2^-8 relative) away, and each such step feeds the next rounding point: a plain
+float32 emulation of the 8B block at 512 tokens has 1.9% of the attention context,
+3.7% of the MLP input and 28% of the SwiGLU output one step off, and its output
+differs from the oracle by 1.8e-3. Taking every rounded operand as one step off,
+independently, gives a down-projection error of 2^-8/sqrt(3) * ||w_j * H_i||
+(about 5e-3 absolute at ffn 12288, std 0.02 weights), about 2.5e-3 of max |ref|
+at the six-sigma tail of 2M outputs; 4e-3 covers it with the o-projection's share.
+Every K/V the block stores is within one bf16 step of the oracle's plus 5e-4 of
+the pool's largest magnitude: one normed-input element one bf16 step off moves a
+K/V element of that token by up to 2^-8 * |x| * |w| (after the head norm's
+1/rms), about 1.4e-3 absolute, 3.5e-4 of max |K|, at five-sigma inputs and
+weights; near-zero elements show it as many of their own steps.
+Shapes: small ragged blocks (token counts and widths that are not multiples of
+the 128 x 128 GEMM tile), a chunked prefill over a non-empty cache, prefill
+followed by a decode step, and the 8B-class block at 512 tokens.
+"""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+from oracle.qwen2 import OracleWeights, prefill_block, decode_step
+from workloads import shapes as S
+from workloads import synth
+from tests._gpu_setup import make_case, dev_i32, rel_err, kv_mismatch
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+SMALL = S.ModelShape(n_layers=1, hidden=200, n_q_heads=4, n_kv_heads=2, head_dim=64, ffn=328,
+                     vocab=300)
+
+
+def _check_kv(dev_pool, host_pool):
+    msg = kv_mismatch(dev_pool, host_pool, abs_frac=5e-4)
+    assert not msg, msg
+
+
+def _prefill(case, n, start, x_in):
+    x_out = torch.full((n, case.shape.hidden), float("nan"), device="cuda")
+    case.runner.prefill(0, n, start, x_in, x_out)
+    torch.cuda.synchronize()
+    return x_out
+
+
+@pytest.mark.parametrize("shape,n", [(SMALL, 37), (SMALL, 130),
+                                     (replace(SMALL, qkv_bias=False, qk_norm=True, n_q_heads=8,
+                                              n_kv_heads=2, head_dim=128, hidden=256), 71)])
+def test_small_prefill_block(shape, n):
+    case = make_case(shape, np.array([0]), seed=13, extra=n + 1, prefill_tokens=n)
+    x = synth.make_x(n, shape.hidden, seed=13, dtype="bf16", device="cuda")
+    out = _prefill(case, n, 0, x)
+    ow = OracleWeights(shape, case.host_w)
+    ref = prefill_block(shape, ow.layer(0), case.k_host[0], case.v_host[0], case.kv.block_table[0], 0,
+                        synth.to_host_bits(x))
+    assert rel_err(out.cpu().numpy(), ref) <= 2e-3
+    _check_kv(case.kv.k[0], case.k_host[0])
+    _check_kv(case.kv.v[0], case.v_host[0])
+
+
+def test_chunked_prefill_over_a_cache_then_decode():
+    shape = replace(SMALL, vocab=300)
+    n1, n2 = 20, 29
+    case = make_case(shape, np.array([0]), seed=17, extra=n1 + n2 + 2, prefill_tokens=n1 + n2)
+    x = synth.make_x(n1 + n2, shape.hidden, seed=17, dtype="bf16", device="cuda")
+    ow = OracleWeights(shape, case.host_w)
+    out1 = _prefill(case, n1, 0, x[:n1].contiguous())
+    out2 = _prefill(case, n2, n1, x[n1:].contiguous())
+    ref1 = prefill_block(shape, ow.layer(0), case.k_host[0], case.v_host[0], case.kv.block_table[0], 0,
+                         synth.to_host_bits(x[:n1]))
+    ref2 = prefill_block(shape, ow.layer(0), case.k_host[0], case.v_host[0], case.kv.block_table[0], n1,
+                         synth.to_host_bits(x[n1:]))
+    assert rel_err(out1.cpu().numpy(), ref1) <= 2e-3
+    assert rel_err(out2.cpu().numpy(), ref2) <= 2e-3
+    # handoff: a decode step at position n1 + n2 over the prefilled cache
+    pos = np.array([n1 + n2], np.int32)
+    tok = synth.make_tokens(1, shape.vocab, seed=17)
+    logits = torch.empty(1, shape.vocab, device="cuda")
+    nxt = torch.empty(1, dtype=torch.int32, device="cuda")
+    case.runner.step(pos, dev_i32(pos), tokens=dev_i32(tok), logits=logits, next_tokens=nxt)
+    torch.cuda.synchronize()
+    r = decode_step(shape, ow, case.k_host, case.v_host, case.kv.block_table, pos, tokens=tok)
+    assert rel_err(logits.cpu().numpy(), r.logits) <= 2e-3
+    assert int(nxt.cpu()[0]) == int(r.next_tokens[0])
+
+
+@pytest.mark.timeout(600)
+def test_qwen_8b_block_prefill512():
+    wl = S.QWEN_8B_BLOCK_PREFILL512
+    sh = wl.shape
+    n = wl.prefill_tokens
+    w = synth.make_weights(sh, seed=wl.seed, device="cuda", with_embed=False)
+    kv = synth.make_kv(sh, np.array([0]), extra=n, seed=wl.seed, device="cuda")
+    from decode_step_amd.runner import DecodeRunner
+    runner = DecodeRunner(sh, w, kv.k, kv.v, kv.block_table, max_batch=1, max_ctx=n, device="cuda",
+                          prefill_tokens=n)
+    x = synth.make_x(n, sh.hidden, seed=wl.seed, dtype="bf16", device="cuda")
+    x_out = torch.full((n, sh.hidden), float("nan"), device="cuda")
+    runner.prefill(0, n, 0, x, x_out)
+    torch.cuda.synchronize()
+    host_w = synth.weights_to_host(w)
+    # host copies of the pools after the GPU block: the oracle overwrites exactly the
+    # slots the block writes (positions 0..511) before it reads any of them
+    k_pool = synth.to_host_bits(kv.k[0]).copy()
+    v_pool = synth.to_host_bits(kv.v[0]).copy()
+    ow = OracleWeights(sh, host_w, cache_layers=False)
+    ref = prefill_block(sh, ow.layer(0), k_pool, v_pool, kv.block_table[0], 0, synth.to_host_bits(x))
+    err = rel_err(x_out.cpu().numpy(), ref)
+    print(f"8B block prefill 512: max rel err {err:.3e}")
+    assert err <= 4e-3
+    _check_kv(kv.k[0], k_pool)
+    _check_kv(kv.v[0], v_pool)
