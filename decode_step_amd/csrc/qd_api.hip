@@ -275,8 +275,13 @@ qd_status qd_decode_step(const qd_config* cfg, const qd_weights* w, const qd_kv*
     const int B = batch, D = P.D;
     const int cap = kv->max_blocks * c.page_size;
     auto gemv = [&](const qd::GemvArgs& g, int epi, int grid_cap, int* grid_out) {
-        return B == 1 ? qd::launch_gemv1(g, wbf, epi, grid_cap, grid_out, s)
-                      : qd::launch_gemv(g, wbf, epi, grid_cap, grid_out, s);
+        if (B == 1) return qd::launch_gemv1(g, wbf, epi, grid_cap, grid_out, s);
+        if (wbf) {
+            qd::GemvArgs m = g;
+            m.kt = qd::gemm16_chunk(g.K);
+            return qd::launch_gemm16(m, epi, grid_cap, grid_out, s);
+        }
+        return qd::launch_gemv(g, wbf, epi, grid_cap, grid_out, s);
     };
 
     qd::StepInputArgs si{};

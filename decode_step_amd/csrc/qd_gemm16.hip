@@ -1,0 +1,528 @@
+// Batched decode projections (2..16 sequences) on the gfx950 matrix cores.
+//
+// A decode projection at batch B streams a row-major [N][K] bf16 weight matrix
+// once and does B multiply-adds per weight. At B = 16 that is 16 FMAs per two
+// bytes: at 8 TB/s the vector ALUs would have to run near their fp32 peak, so
+// the product goes to v_mfma_f32_16x16x32_bf16 instead, with the weights as
+// the A operand (16 output rows) and the B token vectors as the 16 columns of
+// the B operand (columns past B are zeros).
+//
+// The matrix cores take bf16 operands, but a decode step keeps its activations
+// in float32. Each activation (RMSNorm gain applied) is split into two bf16
+// values, hi = bf16(v) and lo = bf16(v - hi); W v = W hi + W lo up to
+// 2^-17 |v| per term, so the product keeps float32-level accuracy at the cost
+// of a second MFMA, and the matrix cores stay far from busy (the kernel is HBM
+// bound). RMSNorm is folded in as in the batch-1 GEMV (Tang page, section 2.3):
+// the staged operand is x * g, and r = 1/sqrt(sum(x^2)/K + eps) (nanocompile
+// page, phase 1) scales each finished output.
+//
+// Workgroup: 4 waves; WR = 4/WK waves along rows, WK waves split each K chunk
+// and meet in LDS in a fixed order (deterministic). A wave owns R blocks of 16
+// rows (two per block for gate|up). The activation chunk sits in LDS in the
+// MFMA B-fragment layout, [k/8][token] of 16-byte groups, hi and lo apart, so
+// a fragment read is one conflict-free 16-byte LDS read per lane. Weight
+// fragments are loaded U k-steps ahead of their use.
+#include "qd_device.h"
+#include "qd_launch.h"
+
+namespace qd {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 g16_bf16x8;
+typedef __attribute__((ext_vector_type(4))) float g16_f32x4;
+
+constexpr int kG16Chunk = 1024;   // K elements staged per chunk: 64 KB of LDS for 16 tokens
+constexpr int kG16U = 4;          // k-steps (of 32) per pipeline stage
+
+__device__ __forceinline__ g16_bf16x8 g16_frag(uint4 v) { return __builtin_bit_cast(g16_bf16x8, v); }
+
+// Loads are issued unconditionally from an address that is always valid (the
+// caller clamps it) and masked afterwards: a load under a per-lane branch makes
+// the compiler wait for every outstanding load before the branch joins, which
+// would empty the prefetch pipeline.
+__device__ __forceinline__ uint4 masked(uint4 v, bool ok) {
+    return ok ? v : make_uint4(0, 0, 0, 0);
+}
+__device__ __forceinline__ float4 masked(float4 v, bool ok) {
+    return ok ? v : make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+// v -> (hi, lo) with hi = bf16(v) and lo = bf16(v - hi), both round-to-nearest-even
+// through v_cvt_pk_bf16_f32; a pair's first element sits in the low half-word.
+__device__ __forceinline__ void split_hi_lo(const float (&v)[8], uint4& hi, uint4& lo) {
+    typedef __attribute__((ext_vector_type(2))) float f2;
+    typedef __attribute__((ext_vector_type(2))) __bf16 b2;
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t hu = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{v[2 * i], v[2 * i + 1]}, b2));
+        const float h0 = __uint_as_float(hu << 16), h1 = __uint_as_float(hu & 0xffff0000u);
+        h[i] = hu;
+        l[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{v[2 * i] - h0, v[2 * i + 1] - h1}, b2));
+    }
+    hi = make_uint4(h[0], h[1], h[2], h[3]);
+    lo = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
+// (value, index) argmax over the lanes that share lane % 16
+__device__ __forceinline__ void argmax_across_rows(float& v, int& i) {
+    const int lane = __lane_id();
+    {
+        auto rv = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
+        auto ri = __builtin_amdgcn_permlane16_swap(i, i, false, false);
+        const bool odd_row = (lane >> 4) & 1;
+        const float ov = __int_as_float(odd_row ? rv[0] : rv[1]);
+        const int oi = odd_row ? ri[0] : ri[1];
+        if (better(ov, oi, v, i)) { v = ov; i = oi; }
+    }
+    {
+        auto rv = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+        auto ri = __builtin_amdgcn_permlane32_swap(i, i, false, false);
+        const bool upper = lane >= 32;
+        const float ov = __int_as_float(upper ? rv[0] : rv[1]);
+        const int oi = upper ? ri[0] : ri[1];
+        if (better(ov, oi, v, i)) { v = ov; i = oi; }
+    }
+}
+
+template <int EPI, int R, int WK>
+__global__ __launch_bounds__(256) void gemm16_kernel(GemvArgs a) {
+    constexpr int NW = (EPI == EPI_SWIGLU) ? 2 : 1;
+    constexpr int WR = 4 / WK;
+    constexpr int TR = WR * R * 16;          // output rows per tile
+    constexpr int U = kG16U;
+    extern __shared__ uint4 xs[];            // hi: [chunk/8][16], then lo: [chunk/8][16]
+    __shared__ float ssum[4][16];
+    __shared__ g16_f32x4 red[WK > 1 ? WK - 1 : 1][WR][R][NW][kWave];
+    __shared__ float bv_s[4][16];
+    __shared__ int bi_s[4][16];
+
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+    const int wr = wave % WR, wk = wave / WR;
+    const int col = lane & 15, kq = lane >> 4;
+    const int B = a.B, K = a.K, N = a.N;
+    const int kc_max = a.kt;                 // multiple of 32
+    const int nchunk = (K + kc_max - 1) / kc_max;
+    const int ntiles = (N + TR - 1) / TR;
+    uint4* xhi = xs;
+    uint4* xlo = xs + (kc_max / 8) * 16;
+
+    if (a.zero_ptr && blockIdx.x == 0)
+        for (int i = tid; i < a.zero_n; i += 256) a.zero_ptr[i] = 0u;
+
+    // Stage x[:, k0 .. k0 + kcp) (times the gain) as hi/lo bf16 fragments; items past
+    // K or B are zeros. Thread tid always handles token tid % 16, so its running
+    // sum of squares belongs to one token.
+    float ss = 0.f;
+    auto stage = [&](int k0, int kcp, bool acc_ss) {
+        for (int i = tid; i < (kcp / 8) * 16; i += 256) {
+            const int t = i & 15, j = i >> 4, k = k0 + j * 8;
+            float v[8];
+            if (t < B && k < K) {
+                const float4 p0 = *(const float4*)(a.x + (long)t * K + k);
+                const float4 p1 = *(const float4*)(a.x + (long)t * K + k + 4);
+                v[0] = p0.x; v[1] = p0.y; v[2] = p0.z; v[3] = p0.w;
+                v[4] = p1.x; v[5] = p1.y; v[6] = p1.z; v[7] = p1.w;
+                if (a.gain) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        if (acc_ss) ss += v[e] * v[e];
+                        v[e] *= load_scalar<uint16_t>(a.gain, k + e);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = 0.f;
+            }
+            split_hi_lo(v, xhi[j * 16 + t], xlo[j * 16 + t]);
+        }
+    };
+
+    const bool one_chunk = nchunk == 1;
+    if (one_chunk) {
+        stage(0, (K + 31) & ~31, true);
+        __syncthreads();
+    }
+    float rs = 1.0f;          // RMSNorm scale of token `col`
+    bool have_rs = false;
+    float best_v = -INFINITY;
+    int best_i = 0x7fffffff;
+
+    for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        // weight row pointers of this lane's A fragments (row = block base + col)
+        const uint16_t* wrow[R][NW];      // rows past N read row 0 (masked)
+        bool rok[R];
+#pragma unroll
+        for (int rb = 0; rb < R; ++rb) {
+            const int r = tile * TR + (wr * R + rb) * 16 + col;
+            rok[rb] = r < N;
+#pragma unroll
+            for (int n = 0; n < NW; ++n) {
+                const uint16_t* p = (const uint16_t*)a.w[n];
+                if (r < N) {
+                    if (EPI == EPI_SWIGLU) {
+                        p = (const uint16_t*)a.w[n] + (long)r * K;
+                    } else {
+                        const bool s0 = r < a.seg_end[0], s1 = r < a.seg_end[1];
+                        const void* w = s0 ? a.w[0] : (s1 ? a.w[1] : a.w[2]);
+                        const int base = s0 ? 0 : (s1 ? a.seg_end[0] : a.seg_end[1]);
+                        p = (const uint16_t*)w + (long)(r - base) * K;
+                    }
+                }
+                wrow[rb][n] = p;
+            }
+        }
+        g16_f32x4 acc[R][NW];
+#pragma unroll
+        for (int rb = 0; rb < R; ++rb)
+#pragma unroll
+            for (int n = 0; n < NW; ++n) acc[rb][n] = g16_f32x4{0.f, 0.f, 0.f, 0.f};
+
+        for (int ch = 0; ch < nchunk; ++ch) {
+            const int k0 = ch * kc_max;
+            const int kc = min(kc_max, K - k0);
+            const int kcp = (kc + 31) & ~31;
+            if (!one_chunk) {
+                __syncthreads();                       // previous chunk's readers are done
+                stage(k0, kcp, !have_rs);
+                __syncthreads();
+            }
+            const int nsteps = kcp / 32;
+            const int s0 = wk * nsteps / WK, s1 = (wk + 1) * nsteps / WK;
+            uint4 wa[U][R][NW], wb[U][R][NW];
+            auto load = [&](uint4 (&w)[U][R][NW], int sb) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int s = sb + u;
+                    const int k = k0 + s * 32 + kq * 8;
+                    const bool kok = s < s1 && k < K;
+                    const int kc = kok ? k : 0;
+#pragma unroll
+                    for (int rb = 0; rb < R; ++rb)
+#pragma unroll
+                        for (int n = 0; n < NW; ++n)
+                            w[u][rb][n] = masked(*(const uint4*)(wrow[rb][n] + kc), kok && rok[rb]);
+                }
+            };
+            auto mma = [&](const uint4 (&w)[U][R][NW], int sb) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int s = sb + u;
+                    if (s >= s1) break;
+                    const g16_bf16x8 bh = g16_frag(xhi[(s * 4 + kq) * 16 + col]);
+                    const g16_bf16x8 bl = g16_frag(xlo[(s * 4 + kq) * 16 + col]);
+#pragma unroll
+                    for (int rb = 0; rb < R; ++rb)
+#pragma unroll
+                        for (int n = 0; n < NW; ++n) {
+                            const g16_bf16x8 af = g16_frag(w[u][rb][n]);
+                            acc[rb][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bh, acc[rb][n], 0, 0, 0);
+                            acc[rb][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bl, acc[rb][n], 0, 0, 0);
+                        }
+                }
+            };
+            int s = s0;
+            if (s < s1) load(wa, s);
+            while (s < s1) {
+                load(wb, s + U);
+                mma(wa, s);
+                s += U;
+                if (s >= s1) break;
+                load(wa, s + U);
+                mma(wb, s);
+                s += U;
+            }
+        }
+
+        if (!have_rs) {            // every thread reaches this on the first tile
+            if (a.gain) {
+                const float t = strided_sum<16>(ss);
+                if (lane < 16) ssum[wave][lane] = t;
+                __syncthreads();
+                rs = 1.0f / sqrtf((ssum[0][col] + ssum[1][col] + ssum[2][col] + ssum[3][col]) / (float)K + a.eps);
+            }
+            have_rs = true;
+        }
+
+        if (WK > 1) {
+            if (wk > 0)
+#pragma unroll
+                for (int rb = 0; rb < R; ++rb)
+#pragma unroll
+                    for (int n = 0; n < NW; ++n) red[wk - 1][wr][rb][n][lane] = acc[rb][n];
+            __syncthreads();
+            if (wk == 0)
+#pragma unroll
+                for (int q = 0; q < WK - 1; ++q)
+#pragma unroll
+                    for (int rb = 0; rb < R; ++rb)
+#pragma unroll
+                        for (int n = 0; n < NW; ++n) acc[rb][n] += red[q][wr][rb][n][lane];
+            __syncthreads();
+        }
+
+        if (wk == 0 && col < B) {
+            float* yrow = a.y + (long)col * N;
+#pragma unroll
+            for (int rb = 0; rb < R; ++rb) {
+                const int rbase = tile * TR + (wr * R + rb) * 16 + kq * 4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = rbase + e;
+                    if (r >= N) break;
+                    const float v0 = acc[rb][0][e] * rs;
+                    if (EPI == EPI_STORE) {
+                        const bool s0 = r < a.seg_end[0], s1 = r < a.seg_end[1];
+                        const void* bsel = s0 ? a.bias[0] : (s1 ? a.bias[1] : a.bias[2]);
+                        const int base = s0 ? 0 : (s1 ? a.seg_end[0] : a.seg_end[1]);
+                        yrow[r] = bsel ? v0 + load_scalar<uint16_t>(bsel, r - base) : v0;
+                    } else if (EPI == EPI_RESID) {
+                        yrow[r] = yrow[r] + v0;
+                    } else if (EPI == EPI_SWIGLU) {
+                        yrow[r] = silu(v0) * (acc[rb][NW - 1][e] * rs);
+                    } else {
+                        yrow[r] = v0;
+                        if (better(v0, r, best_v, best_i)) { best_v = v0; best_i = r; }
+                    }
+                }
+            }
+        }
+    }
+
+    if (EPI == EPI_LOGITS) {
+        argmax_across_rows(best_v, best_i);
+        if (lane < 16) { bv_s[wave][lane] = best_v; bi_s[wave][lane] = best_i; }
+        __syncthreads();
+        if (tid < B) {
+            float v = bv_s[0][tid];
+            int i = bi_s[0][tid];
+            for (int w = 1; w < WR; ++w)            // waves 0 .. WR-1 hold the wk == 0 results
+                if (better(bv_s[w][tid], bi_s[w][tid], v, i)) { v = bv_s[w][tid]; i = bi_s[w][tid]; }
+            a.part_val[(long)tid * gridDim.x + blockIdx.x] = v;
+            a.part_idx[(long)tid * gridDim.x + blockIdx.x] = i;
+        }
+    }
+}
+
+// One 16-row block per wave-row, activations straight from memory: with a
+// single row block per workgroup a staged copy of the activation would be read
+// once, so each lane loads its own B fragment (8 float32 of one token) from
+// L2 in the same pipeline as the weights and splits it into hi/lo in
+// registers. No LDS staging, no barrier before the first MFMA. The gain, when
+// present, must be 16-byte aligned.
+template <int EPI, int WK>
+__global__ __launch_bounds__(64 * WK) void gemm16_direct_kernel(GemvArgs a) {
+    constexpr bool GAIN = EPI != EPI_RESID;       // every normed projection; residual ones have none
+    constexpr int NW = (EPI == EPI_SWIGLU) ? 2 : 1;
+    constexpr int TR = 16;
+    constexpr int U = kG16U;
+    __shared__ float ssum[WK][16];
+    __shared__ g16_f32x4 red[WK - 1][NW][kWave];
+
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+    const int wk = wave;
+    const int col = lane & 15, kq = lane >> 4;
+    const int B = a.B, K = a.K, N = a.N;
+    const int tile = blockIdx.x;
+    const bool tok = col < B;
+    const float* xrow = a.x + (long)(tok ? col : 0) * K;
+    const uint16_t* gain = (const uint16_t*)a.gain;
+
+    if (a.zero_ptr && blockIdx.x == 0)
+        for (int i = tid; i < a.zero_n; i += 64 * WK) a.zero_ptr[i] = 0u;
+
+    const uint16_t* wrow[NW];         // a row past N reads row 0 (masked)
+    const int r_own = tile * TR + col;
+    const bool rok = r_own < N;
+    {
+        const int r = r_own;
+#pragma unroll
+        for (int n = 0; n < NW; ++n) {
+            const uint16_t* p = (const uint16_t*)a.w[n];
+            if (r < N) {
+                if (EPI == EPI_SWIGLU) {
+                    p = (const uint16_t*)a.w[n] + (long)r * K;
+                } else {
+                    const bool s0 = r < a.seg_end[0], s1 = r < a.seg_end[1];
+                    const void* w = s0 ? a.w[0] : (s1 ? a.w[1] : a.w[2]);
+                    const int base = s0 ? 0 : (s1 ? a.seg_end[0] : a.seg_end[1]);
+                    p = (const uint16_t*)w + (long)(r - base) * K;
+                }
+            }
+            wrow[n] = p;
+        }
+    }
+    g16_f32x4 acc[NW];
+#pragma unroll
+    for (int n = 0; n < NW; ++n) acc[n] = g16_f32x4{0.f, 0.f, 0.f, 0.f};
+    float ss = 0.f;
+
+    const int nsteps = (K + 31) / 32;
+    const int s0 = wk * nsteps / WK, s1 = (wk + 1) * nsteps / WK;
+    struct Stage {
+        uint4 w[U][NW];
+        float4 x0[U], x1[U];
+        uint4 g[U];
+    };
+    Stage sa, sb;
+    auto load = [&](Stage& st, int sbase) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int s = sbase + u;
+            const int k = s * 32 + kq * 8;
+            const bool ok = s < s1 && k < K;
+            const int kc = ok ? k : 0;
+#pragma unroll
+            for (int n = 0; n < NW; ++n) st.w[u][n] = masked(*(const uint4*)(wrow[n] + kc), ok && rok);
+            st.x0[u] = masked(*(const float4*)(xrow + kc), ok && tok);
+            st.x1[u] = masked(*(const float4*)(xrow + kc + 4), ok && tok);
+            if (GAIN) st.g[u] = masked(*(const uint4*)(gain + kc), ok);
+        }
+    };
+    auto mma = [&](const Stage& st, int sbase) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (sbase + u >= s1) break;
+            float v[8] = {st.x0[u].x, st.x0[u].y, st.x0[u].z, st.x0[u].w,
+                          st.x1[u].x, st.x1[u].y, st.x1[u].z, st.x1[u].w};
+            if (GAIN) {
+                float gf[8];
+                widen16(st.g[u], gf);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    ss += v[e] * v[e];
+                    v[e] *= gf[e];
+                }
+            }
+            uint4 hu, lu;
+            split_hi_lo(v, hu, lu);
+            const g16_bf16x8 bh = g16_frag(hu);
+            const g16_bf16x8 bl = g16_frag(lu);
+#pragma unroll
+            for (int n = 0; n < NW; ++n) {
+                const g16_bf16x8 af = g16_frag(st.w[u][n]);
+                acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bh, acc[n], 0, 0, 0);
+                acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bl, acc[n], 0, 0, 0);
+            }
+        }
+    };
+    int s = s0;
+    if (s < s1) load(sa, s);
+    while (s < s1) {
+        load(sb, s + U);
+        mma(sa, s);
+        s += U;
+        if (s >= s1) break;
+        load(sa, s + U);
+        mma(sb, s);
+        s += U;
+    }
+
+    // sum of squares of token `col` over this wave's K range, then over the WK waves
+    // of this wave-row (fixed order); partial products likewise
+    if (GAIN) {
+        const float t = strided_sum<16>(ss);
+        if (lane < 16) ssum[wave][lane] = t;
+    }
+    if (wk > 0)
+#pragma unroll
+        for (int n = 0; n < NW; ++n) red[wk - 1][n][lane] = acc[n];
+    __syncthreads();
+    float rs = 1.0f;
+    if (wk == 0) {
+#pragma unroll
+        for (int q = 0; q < WK - 1; ++q)
+#pragma unroll
+            for (int n = 0; n < NW; ++n) acc[n] += red[q][n][lane];
+        if (GAIN) {
+            float t = 0.f;
+#pragma unroll
+            for (int q = 0; q < WK; ++q) t += ssum[q][col];
+            rs = 1.0f / sqrtf(t / (float)K + a.eps);
+        }
+    }
+
+    float best_v = -INFINITY;
+    int best_i = 0x7fffffff;
+    if (wk == 0 && tok) {
+        float* yrow = a.y + (long)col * N;
+        const int rbase = tile * TR + kq * 4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = rbase + e;
+            if (r >= N) break;
+            const float v0 = acc[0][e] * rs;
+            if (EPI == EPI_STORE) {
+                const bool q0 = r < a.seg_end[0], q1 = r < a.seg_end[1];
+                const void* bsel = q0 ? a.bias[0] : (q1 ? a.bias[1] : a.bias[2]);
+                const int base = q0 ? 0 : (q1 ? a.seg_end[0] : a.seg_end[1]);
+                yrow[r] = bsel ? v0 + load_scalar<uint16_t>(bsel, r - base) : v0;
+            } else if (EPI == EPI_RESID) {
+                yrow[r] = yrow[r] + v0;
+            } else if (EPI == EPI_SWIGLU) {
+                yrow[r] = silu(v0) * (acc[NW - 1][e] * rs);
+            } else {
+                yrow[r] = v0;
+                if (better(v0, r, best_v, best_i)) { best_v = v0; best_i = r; }
+            }
+        }
+    }
+    if (EPI == EPI_LOGITS) {           // wave 0 holds the block's 16 rows for every token
+        argmax_across_rows(best_v, best_i);
+        if (wk == 0 && lane < B) {
+            a.part_val[(long)lane * gridDim.x + blockIdx.x] = best_v;
+            a.part_idx[(long)lane * gridDim.x + blockIdx.x] = best_i;
+        }
+    }
+}
+
+// K split into the fewest chunks of at most kG16Chunk, evened out (multiples of 32)
+int gemm16_chunk(int K) {
+    const int kp = (K + 31) & ~31;
+    const int n = (kp + kG16Chunk - 1) / kG16Chunk;
+    return ((kp + n - 1) / n + 31) & ~31;
+}
+
+// Many-row matrices (the lm_head) take wide tiles and a capped, grid-strided
+// grid with the activation staged once per workgroup; the rest take one 16-row
+// block per workgroup with the four waves splitting K and the activation read
+// directly, which spreads even the smallest decode matrix (896 rows) over 56
+// workgroups.
+hipError_t launch_gemm16(const GemvArgs& a, int epi, int grid_cap, int* grid_out, hipStream_t s) {
+    if (a.B < 1 || a.B > 16 || a.K % 8 || a.kt != gemm16_chunk(a.K)) return hipErrorInvalidValue;
+    const bool wide = a.N >= 16 * 2048;
+    const bool gain_ok = epi == EPI_RESID ? a.gain == nullptr
+                                          : (a.gain != nullptr && ((uintptr_t)a.gain & 15u) == 0);
+    if (!wide && gain_ok) {
+        const int grid = (a.N + 15) / 16;
+        if (grid > grid_cap) return hipErrorInvalidValue;
+        if (grid_out) *grid_out = grid;
+        const bool deep = a.K >= 2048;       // long K: eight waves split it
+#define QD_G16D(E)                                                                                       \
+    if (deep) hipLaunchKernelGGL((gemm16_direct_kernel<E, 8>), dim3(grid), dim3(512), 0, s, a);          \
+    else hipLaunchKernelGGL((gemm16_direct_kernel<E, 4>), dim3(grid), dim3(256), 0, s, a);
+        switch (epi) {
+            case EPI_STORE: QD_G16D(EPI_STORE) break;
+            case EPI_RESID: QD_G16D(EPI_RESID) break;
+            case EPI_SWIGLU: QD_G16D(EPI_SWIGLU) break;
+            default: QD_G16D(EPI_LOGITS) break;
+        }
+#undef QD_G16D
+        return hipGetLastError();
+    }
+    const size_t shm = (size_t)a.kt * 64;    // hi + lo, 16 tokens, 2 bytes each
+    auto go = [&](auto kern, int tr) {
+        const int tiles = (a.N + tr - 1) / tr;
+        const int grid = tiles < grid_cap ? tiles : grid_cap;
+        if (grid_out) *grid_out = grid;
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(256), shm, s, a);
+        return hipGetLastError();
+    };
+    switch (epi) {
+        case EPI_STORE: return wide ? go(gemm16_kernel<EPI_STORE, 2, 1>, 128) : go(gemm16_kernel<EPI_STORE, 1, 4>, 16);
+        case EPI_RESID: return wide ? go(gemm16_kernel<EPI_RESID, 2, 1>, 128) : go(gemm16_kernel<EPI_RESID, 1, 4>, 16);
+        case EPI_SWIGLU: return go(gemm16_kernel<EPI_SWIGLU, 1, 4>, 16);
+        default: return wide ? go(gemm16_kernel<EPI_LOGITS, 2, 1>, 128) : go(gemm16_kernel<EPI_LOGITS, 1, 4>, 16);
+    }
+}
+
+}  // namespace qd

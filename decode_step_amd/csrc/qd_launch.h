@@ -34,6 +34,10 @@ hipError_t launch_gemv(const GemvArgs& a, int w_is_bf16, int epi, int grid_cap, 
 hipError_t launch_gemv1(const GemvArgs& a, int w_is_bf16, int epi, int grid_cap, int* grid_out,
                         hipStream_t s);
 int gemv_rows_per_tile(int K);
+// batch 2..16 with bf16 weights on the matrix cores (qd_gemm16.hip); a.kt must be
+// gemm16_chunk(a.K); part_val/part_idx hold [B][grid] entries
+hipError_t launch_gemm16(const GemvArgs& a, int epi, int grid_cap, int* grid_out, hipStream_t s);
+int gemm16_chunk(int K);
 
 // Decode attention with the q/k norm, RoPE, the new token's KV append and the
 // split merge fused in (one launch per layer); see qd_attention.hip.

@@ -77,6 +77,26 @@ def test_small_ragged_batch(w_dtype, kv_dtype, tol):
     assert _cache_matches(case)
 
 
+@pytest.mark.parametrize("batch", [2, 5, 16])
+def test_batched_projections_chunked_k_wide_vocab(batch):
+    """Batched decode (B > 1, bf16 weights) runs its projections on the matrix cores.
+    hidden 1032 and ffn 2056 are not multiples of 32 and exceed one staged K chunk
+    (2 and 3 chunks); vocab 40003 takes the wide (128-row) lm_head tiling with a
+    ragged last tile; B = 5 leaves MFMA columns empty."""
+    shape = replace(SMALL, n_layers=2, hidden=1032, ffn=2056, vocab=40003, n_q_heads=6,
+                    n_kv_heads=2, head_dim=64)
+    ctx = np.array([(37 * b + 5) % 300 for b in range(batch)], np.int32)
+    case = make_case(shape, ctx, seed=31 + batch, random_order=True)
+    tok = synth.make_tokens(batch, shape.vocab, seed=31 + batch)
+    logits, nxt, x_out, layer_out = _run_step(case, ctx, tokens=tok)
+    ref = _oracle(case, ctx, tokens=tok)
+    assert rel_err(logits.cpu().numpy(), ref.logits) <= 2e-3
+    assert rel_err(layer_out.cpu().numpy(), ref.layer_out) <= 2e-3
+    assert rel_err(x_out.cpu().numpy(), ref.x_out) <= 2e-3
+    assert list(nxt.cpu().numpy()) == list(ref.next_tokens)
+    assert _cache_matches(case)
+
+
 def test_small_qk_norm_no_bias_untied():
     shape = replace(SMALL, qkv_bias=False, qk_norm=True, tied=False, n_q_heads=8, n_kv_heads=2,
                     head_dim=128)
