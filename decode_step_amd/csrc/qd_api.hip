@@ -28,9 +28,12 @@ bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 constexpr int kMaxBatch = 16;
-constexpr int kMaxChunk = 256;        // tokens per attention split (LDS score buffer)
 constexpr int kLogitsGridCap = 2048;  // workgroups of the lm_head GEMV = argmax partials per row
 constexpr int kGemvGridCap = 4096;
+#ifndef QD_GEMV1_GRID_CAP
+#define QD_GEMV1_GRID_CAP 512
+#endif
+constexpr int kGemv1GridCap = QD_GEMV1_GRID_CAP;   // batch-1 projections grid-stride beyond this
 constexpr size_t kGemvLds = 60 * 1024;   // dynamic LDS of the GEMV, below the 64 KB launch limit
 
 qd_status check_config(const qd_config* c) {
@@ -62,20 +65,42 @@ struct DecodePlan {
     size_t off_x, off_qkv, off_part, off_rope, off_ctx, off_h, off_logits, off_pv, off_pi, total;
 };
 
-// Attention work split: S = ceil(tokens / chunk) splits per (sequence, kv head),
-// chunk = the most one workgroup holds in registers (a whole number of pages);
-// the query heads of a KV head go to separate workgroups (hpw = 1) unless that
-// makes more than 1024 workgroups. Returns false when the context needs more
-// splits than one merge combines.
+// Attention work split. Grouped: one workgroup holds all query heads of a KV
+// head (each K/V row is read once) and a split of `chunk` tokens, the chunk
+// sized so the (sequence, KV head, split) items come to about kAttnTargetWgs
+// workgroups, at least kAttnMinChunk tokens and at most what one workgroup
+// holds in registers. When that leaves fewer than kAttnMinWgs workgroups (one
+// short sequence), the query heads go to separate workgroups instead (hpw = 1)
+// with the largest chunk, which spreads the score and value arithmetic over
+// more CUs. Returns false when the context needs more splits than one merge
+// combines.
+constexpr int kAttnTargetWgs = 512;
+constexpr int kAttnMinWgs = 128;
+constexpr int kAttnMinChunk = 64;
 bool plan_split(const qd_config* c, int B, int max_tokens, int* chunk, int* S, int* hpw) {
     // B = sequences (decode) or query rows (prefill); max_tokens = longest context
-    int ch = qd::attn_max_chunk(c->head_dim, c->kv_dtype == QD_BF16);
-    ch = ch / c->page_size * c->page_size;
-    *chunk = ch;
-    *S = (max_tokens + ch - 1) / ch;
-    if (*S < 1) *S = 1;
-    const long wgs = (long)(*S) * B * c->n_q_heads;
-    *hpw = wgs <= 1024 ? 1 : c->n_q_heads / c->n_kv_heads;
+    const int pg = c->page_size;
+    const int ch_max = qd::attn_max_chunk(c->head_dim, c->kv_dtype == QD_BF16, 1) / pg * pg;
+    const int ch_wide = qd::attn_max_chunk(c->head_dim, c->kv_dtype == QD_BF16, 0) / pg * pg;
+    const long work = (long)B * c->n_kv_heads;
+    const int tokens = max_tokens < 1 ? 1 : max_tokens;
+    long ch = (tokens * work + kAttnTargetWgs - 1) / kAttnTargetWgs;
+    ch = (ch + pg - 1) / pg * pg;
+    if (ch < kAttnMinChunk) ch = kAttnMinChunk;
+    const long need = (tokens + qd::attn_max_splits() - 1) / qd::attn_max_splits();   // merge capacity
+    if (ch < need) ch = (need + pg - 1) / pg * pg;
+    if (ch > ch_max) ch = ch_max;
+    *chunk = (int)ch;
+    *S = (tokens + *chunk - 1) / *chunk;
+    *hpw = c->n_q_heads / c->n_kv_heads;
+    if ((long)(*S) * work < kAttnMinWgs && *hpw > 1) {
+        *chunk = ch_wide;
+        *S = (tokens + ch_wide - 1) / ch_wide;
+        *hpw = 1;
+    } else if (*S > qd::attn_max_splits()) {   // beyond the grouped chunk: the wide one
+        *chunk = ch_wide;
+        *S = (tokens + ch_wide - 1) / ch_wide;
+    }
     return *S <= qd::attn_max_splits();
 }
 
@@ -275,7 +300,8 @@ qd_status qd_decode_step(const qd_config* cfg, const qd_weights* w, const qd_kv*
     const int B = batch, D = P.D;
     const int cap = kv->max_blocks * c.page_size;
     auto gemv = [&](const qd::GemvArgs& g, int epi, int grid_cap, int* grid_out) {
-        if (B == 1) return qd::launch_gemv1(g, wbf, epi, grid_cap, grid_out, s);
+        if (B == 1) return qd::launch_gemv1(g, wbf, epi, epi == qd::EPI_LOGITS ? grid_cap : kGemv1GridCap,
+                                            grid_out, s);
         if (wbf) {
             qd::GemvArgs m = g;
             m.kt = qd::gemm16_chunk(g.K);

@@ -33,15 +33,23 @@ namespace qd {
 
 constexpr int kMaxGroup = 8;
 constexpr int kAttnWaves = 8;    // waves per workgroup
-constexpr int kAttnPasses = 9;   // token passes whose K/V rows a lane holds in registers
+// Token passes whose K/V rows a lane holds in registers: many for one query
+// head per workgroup (a short context in one split), few for grouped heads,
+// where fewer registers let two workgroups share a CU.
+constexpr int kAttnPassesWide = 9;
+constexpr int kAttnPassesGrouped = 4;
 constexpr int kMaxSplits = 64;
 
-template <int HD, typename KVT>
-constexpr int attn_chunk() { return kAttnPasses * kAttnWaves * (kWave / (HD / VecN<KVT>::n)); }
+template <int HD, typename KVT, int NP>
+constexpr int attn_chunk() { return NP * kAttnWaves * (kWave / (HD / VecN<KVT>::n)); }
 
-int attn_max_chunk(int hd, int kv_is_bf16) {
-    if (hd == 64) return kv_is_bf16 ? attn_chunk<64, uint16_t>() : attn_chunk<64, float>();
-    return kv_is_bf16 ? attn_chunk<128, uint16_t>() : attn_chunk<128, float>();
+int attn_max_chunk(int hd, int kv_is_bf16, int grouped) {
+    if (grouped) {
+        if (hd == 64) return kv_is_bf16 ? attn_chunk<64, uint16_t, kAttnPassesGrouped>() : attn_chunk<64, float, kAttnPassesGrouped>();
+        return kv_is_bf16 ? attn_chunk<128, uint16_t, kAttnPassesGrouped>() : attn_chunk<128, float, kAttnPassesGrouped>();
+    }
+    if (hd == 64) return kv_is_bf16 ? attn_chunk<64, uint16_t, kAttnPassesWide>() : attn_chunk<64, float, kAttnPassesWide>();
+    return kv_is_bf16 ? attn_chunk<128, uint16_t, kAttnPassesWide>() : attn_chunk<128, float, kAttnPassesWide>();
 }
 int attn_max_splits() { return kMaxSplits; }
 
@@ -62,14 +70,13 @@ __device__ __forceinline__ void rope_lane(float (&u)[CE], const float (&pr)[CE],
     for (int e = 0; e < CE; ++e) u[e] = lower ? u[e] * c[e] - pr[e] * sn[e] : u[e] * c[e] + pr[e] * sn[e];
 }
 
-template <typename WT, typename KVT, int HD>
+template <typename WT, typename KVT, int HD, int NP>
 __global__ __launch_bounds__(kAttnWaves * kWave) void attn_kernel(AttnArgs a) {
     constexpr int CE = VecN<KVT>::n;
     constexpr int LPT = HD / CE;
     constexpr int TPW = kWave / LPT;
     constexpr int NWV = kAttnWaves;
     constexpr int TPB = NWV * TPW;
-    constexpr int NP = kAttnPasses;
     constexpr int MAXT = NP * TPB;
     constexpr int NT = NWV * kWave;
     __shared__ float sc[kMaxGroup][MAXT];
@@ -110,6 +117,10 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_kernel(AttnArgs a) {
     uint4 kraw[NP], vraw[NP];
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
+        if (i * TPB >= n) {   // past this split's tokens (uniform over the workgroup)
+            kraw[i] = vraw[i] = make_uint4(0, 0, 0, 0);
+            continue;
+        }
         const int t = t_begin + i * TPB + wave * TPW + slot;
         const int tt = t < t_end ? t : t_begin;
         const int pg = spage[tt / a.page - pg0];
@@ -226,15 +237,29 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_kernel(AttnArgs a) {
         float o[CE];
 #pragma unroll
         for (int e = 0; e < CE; ++e) o[e] = 0.f;
+        // the lane's probabilities, read up front (masked, no branch) when the pass
+        // count is small; the wide variant reads them pass by pass to save registers
+        constexpr bool PRE = NP <= kAttnPassesGrouped;
+        float pr[PRE ? NP : 1];
+        if (PRE) {
+#pragma unroll
+            for (int i = 0; i < NP; ++i) {
+                const int j = i * TPB + wave * TPW + slot;
+                const float v = sc[hl][j < n ? j : 0];
+                pr[PRE ? i : 0] = j < n ? v : 0.f;
+            }
+        }
 #pragma unroll
         for (int i = 0; i < NP; ++i) {
             if (i * TPB >= n) break;
-            const int t = t_begin + i * TPB + wave * TPW + slot;
-            const float pr = t < t_end ? sc[hl][t - t_begin] : 0.f;
+            if (!PRE) {
+                const int j = i * TPB + wave * TPW + slot;
+                pr[0] = j < n ? sc[hl][j] : 0.f;
+            }
             float vf[CE];
             widen16(vraw[i], vf);
 #pragma unroll
-            for (int e = 0; e < CE; ++e) o[e] = fmaf(pr, vf[e], o[e]);
+            for (int e = 0; e < CE; ++e) o[e] = fmaf(pr[PRE ? i : 0], vf[e], o[e]);
         }
 #pragma unroll
         for (int e = 0; e < CE; ++e) {
@@ -271,43 +296,53 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_kernel(AttnArgs a) {
 }
 
 // Merge of the split partials of one (query head, sequence): M = max_s m_s,
-// ctx = sum_s o_s e^(m_s - M) / sum_s l_s e^(m_s - M).
-__global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a) {
+// ctx = sum_s o_s e^(m_s - M) / sum_s l_s e^(m_s - M). The 256 threads form
+// 256/hd groups that take every (256/hd)-th split, each with 16 partial loads
+// in flight; the groups' sums meet in LDS in a fixed order.
+constexpr int kMergeThreads = 256;
+__global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
     __shared__ float wgt[kMaxSplits];
     __shared__ float lsum;
-    const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+    __shared__ float osum[kMergeThreads];
+    const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
     const int p = a.prefill_start >= 0 ? a.prefill_start + b : a.pos[b];
     if (p < 0 || p >= a.capacity) return;
     const int ns = min(min(a.S, kMaxSplits), (p + 1 + a.chunk - 1) / a.chunk);
     if (ns <= 1) return;   // one split: the attention kernel wrote the output itself
-    const float* base = a.part + ((long)b * a.Hq + h) * a.S * (a.hd + 2);
-    if (d < kWave) {   // wave 0: weights of the splits
-        float m = -INFINITY;
-        for (int j = d; j < ns; j += kWave) m = fmaxf(m, base[j * (a.hd + 2) + a.hd]);
-        m = group_max<kWave>(m);
-        float l = 0.f;
-        for (int j = d; j < ns; j += kWave) {
-            const float w = expf(base[j * (a.hd + 2) + a.hd] - m);
-            wgt[j] = w;
-            l = fmaf(base[j * (a.hd + 2) + a.hd + 1], w, l);
-        }
-        l = group_sum<kWave>(l);
-        if (d == 0) lsum = l;
+    const int hd = a.hd, stride = hd + 2;
+    const float* base = a.part + ((long)b * a.Hq + h) * a.S * stride;
+    if (tid < kWave) {   // wave 0: weights of the splits
+        const float mj = tid < ns ? base[tid * stride + hd] : -INFINITY;
+        const float lj = tid < ns ? base[tid * stride + hd + 1] : 0.f;
+        const float m = group_max<kWave>(mj);
+        const float w = tid < ns ? expf(mj - m) : 0.f;
+        if (tid < ns) wgt[tid] = w;
+        const float l = group_sum<kWave>(lj * w);
+        if (tid == 0) lsum = l;
     }
     __syncthreads();
-    if (d >= a.hd) return;
+    const int ng = kMergeThreads / hd, grp = tid / hd, d = tid - grp * hd;
     float o = 0.f;
-    int j = 0;
-    for (; j + 4 <= ns; j += 4) {
-        const float o0 = base[(j + 0) * (a.hd + 2) + d], o1 = base[(j + 1) * (a.hd + 2) + d];
-        const float o2 = base[(j + 2) * (a.hd + 2) + d], o3 = base[(j + 3) * (a.hd + 2) + d];
-        o = fmaf(o0, wgt[j], o);
-        o = fmaf(o1, wgt[j + 1], o);
-        o = fmaf(o2, wgt[j + 2], o);
-        o = fmaf(o3, wgt[j + 3], o);
+    for (int j0 = grp; j0 < ns; j0 += 16 * ng) {
+        float v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int j = j0 + u * ng;
+            v[u] = base[(j < ns ? j : 0) * stride + d];
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int j = j0 + u * ng;
+            if (j < ns) o = fmaf(v[u], wgt[j], o);
+        }
     }
-    for (; j < ns; ++j) o = fmaf(base[j * (a.hd + 2) + d], wgt[j], o);
-    a.ctx[((long)b * a.Hq + h) * a.hd + d] = o / lsum;
+    osum[tid] = o;
+    __syncthreads();
+    if (tid < hd) {
+        float t = osum[tid];
+        for (int q = 1; q < ng; ++q) t += osum[q * hd + tid];
+        a.ctx[((long)b * a.Hq + h) * hd + tid] = t / lsum;
+    }
 }
 
 hipError_t launch_attention(const AttnArgs& a, int w_is_bf16, int kv_is_bf16, hipStream_t s) {
@@ -315,7 +350,13 @@ hipError_t launch_attention(const AttnArgs& a, int w_is_bf16, int kv_is_bf16, hi
     const int hgroups = (G + a.hpw - 1) / a.hpw;
     dim3 grid(a.S, a.Hkv * hgroups, a.B);
     dim3 block(kAttnWaves * kWave);
-#define QD_ATTN(WT, KVT, HD) hipLaunchKernelGGL((attn_kernel<WT, KVT, HD>), grid, block, 0, s, a)
+#define QD_ATTN(WT, KVT, HD)                                                                          \
+    do {                                                                                              \
+        if (a.chunk <= attn_chunk<HD, KVT, kAttnPassesGrouped>())                                     \
+            hipLaunchKernelGGL((attn_kernel<WT, KVT, HD, kAttnPassesGrouped>), grid, block, 0, s, a); \
+        else                                                                                          \
+            hipLaunchKernelGGL((attn_kernel<WT, KVT, HD, kAttnPassesWide>), grid, block, 0, s, a);    \
+    } while (0)
     if (a.hd == 64) {
         if (w_is_bf16) { if (kv_is_bf16) QD_ATTN(uint16_t, uint16_t, 64); else QD_ATTN(uint16_t, float, 64); }
         else { if (kv_is_bf16) QD_ATTN(float, uint16_t, 64); else QD_ATTN(float, float, 64); }
@@ -326,7 +367,7 @@ hipError_t launch_attention(const AttnArgs& a, int w_is_bf16, int kv_is_bf16, hi
 #undef QD_ATTN
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.S == 1) return e;
-    hipLaunchKernelGGL(attn_merge_kernel, dim3(a.Hq, a.B), dim3(128), 0, s, a);
+    hipLaunchKernelGGL(attn_merge_kernel, dim3(a.Hq, a.B), dim3(kMergeThreads), 0, s, a);
     return hipGetLastError();
 }
 

@@ -67,7 +67,7 @@ struct AttnArgs {
 };
 // attention kernel, plus the split merge kernel when S > 1
 hipError_t launch_attention(const AttnArgs& a, int w_is_bf16, int kv_is_bf16, hipStream_t s);
-int attn_max_chunk(int hd, int kv_is_bf16);
+int attn_max_chunk(int hd, int kv_is_bf16, int grouped);
 int attn_max_splits();
 
 // x = embedding rows of `tokens` (or a copy of x_in), plus the RoPE table of the
