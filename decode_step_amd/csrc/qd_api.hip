@@ -488,6 +488,13 @@ qd_status qd_prefill_block(const qd_config* cfg, const qd_layer* layer, int32_t 
     rp.Hq = Hq; rp.Hkv = Hkv; rp.hd = hd; rp.page = c.page_size;
     QD_LAUNCH(qd::launch_prefill_rope_append(rp, 1, kvbf, s), "prefill rope/append");
     // causal attention: row i attends over positions 0 .. start + i
+    if (kvbf) {   // matrix cores; the context comes out in bf16, the o_proj operand
+        qd::PrefillAttnArgs pa{};
+        pa.q = qrot; pa.k_cache = kc; pa.v_cache = vc; pa.block_table = kv->block_table;
+        pa.num_pages = kv->num_pages; pa.rows = N; pa.start = start_pos; pa.Hq = Hq; pa.Hkv = Hkv; pa.hd = hd;
+        pa.page = c.page_size; pa.scale = 1.0f / sqrtf((float)hd); pa.out = ctxb;
+        QD_LAUNCH_K(QD_K_PREFILL_ATTN, qd::launch_prefill_attn_mfma(pa, s), "prefill attention");
+    } else {
     qd::AttnArgs at{};
     at.k_cache = kc; at.v_cache = vc; at.block_table = kv->block_table; at.max_blocks = kv->max_blocks;
     at.num_pages = kv->num_pages; at.pos = nullptr; at.capacity = kv->max_blocks * c.page_size;
@@ -496,6 +503,7 @@ qd_status qd_prefill_block(const qd_config* cfg, const qd_layer* layer, int32_t 
     at.prefill_start = start_pos; at.q_rot = qrot;
     QD_LAUNCH_K(QD_K_PREFILL_ATTN, qd::launch_attention(at, 1, kvbf, s), "prefill attention");
     QD_LAUNCH(qd::launch_to_bf16(ctx, ctxb, (long)N * Hq * hd, s), "context to bf16");
+    }
     // x += ctx W_o^T
     qd::GemmArgs go{};
     go.A = ctxb; go.w[0] = L.wo; go.seg_end[0] = go.seg_end[1] = go.seg_end[2] = D;

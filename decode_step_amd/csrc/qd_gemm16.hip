@@ -46,44 +46,6 @@ __device__ __forceinline__ float4 masked(float4 v, bool ok) {
     return ok ? v : make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
-// v -> (hi, lo) with hi = bf16(v) and lo = bf16(v - hi), both round-to-nearest-even
-// through v_cvt_pk_bf16_f32; a pair's first element sits in the low half-word.
-__device__ __forceinline__ void split_hi_lo(const float (&v)[8], uint4& hi, uint4& lo) {
-    typedef __attribute__((ext_vector_type(2))) float f2;
-    typedef __attribute__((ext_vector_type(2))) __bf16 b2;
-    uint32_t h[4], l[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t hu = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{v[2 * i], v[2 * i + 1]}, b2));
-        const float h0 = __uint_as_float(hu << 16), h1 = __uint_as_float(hu & 0xffff0000u);
-        h[i] = hu;
-        l[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{v[2 * i] - h0, v[2 * i + 1] - h1}, b2));
-    }
-    hi = make_uint4(h[0], h[1], h[2], h[3]);
-    lo = make_uint4(l[0], l[1], l[2], l[3]);
-}
-
-// (value, index) argmax over the lanes that share lane % 16
-__device__ __forceinline__ void argmax_across_rows(float& v, int& i) {
-    const int lane = __lane_id();
-    {
-        auto rv = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
-        auto ri = __builtin_amdgcn_permlane16_swap(i, i, false, false);
-        const bool odd_row = (lane >> 4) & 1;
-        const float ov = __int_as_float(odd_row ? rv[0] : rv[1]);
-        const int oi = odd_row ? ri[0] : ri[1];
-        if (better(ov, oi, v, i)) { v = ov; i = oi; }
-    }
-    {
-        auto rv = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
-        auto ri = __builtin_amdgcn_permlane32_swap(i, i, false, false);
-        const bool upper = lane >= 32;
-        const float ov = __int_as_float(upper ? rv[0] : rv[1]);
-        const int oi = upper ? ri[0] : ri[1];
-        if (better(ov, oi, v, i)) { v = ov; i = oi; }
-    }
-}
-
 template <int EPI, int R, int WK>
 __global__ __launch_bounds__(256) void gemm16_kernel(GemvArgs a) {
     constexpr int NW = (EPI == EPI_SWIGLU) ? 2 : 1;

@@ -70,6 +70,21 @@ hipError_t launch_attention(const AttnArgs& a, int w_is_bf16, int kv_is_bf16, hi
 int attn_max_chunk(int hd, int kv_is_bf16, int grouped);
 int attn_max_splits();
 
+// Causal prefill attention on the matrix cores (qd_prefill_attn.hip): bf16 K/V
+// cache, q rotated in float32 [rows][Hq][hd], context out in bf16 [rows][Hq*hd].
+struct PrefillAttnArgs {
+    const float* q;
+    const void* k_cache;
+    const void* v_cache;      // page pools [pages][Hkv][page][hd], bf16
+    const int* block_table;   // the sequence's row
+    int num_pages;
+    int rows, start;          // query row i sits at position start + i
+    int Hq, Hkv, hd, page;
+    float scale;
+    uint16_t* out;
+};
+hipError_t launch_prefill_attn_mfma(const PrefillAttnArgs& a, hipStream_t s);
+
 // x = embedding rows of `tokens` (or a copy of x_in), plus the RoPE table of the
 // step's positions (qd_attention.hip).
 struct StepInputArgs {
