@@ -473,13 +473,15 @@ qd_status qd_prefill_block(const qd_config* cfg, const qd_layer* layer, int32_t 
     qd::PrefillNormArgs nr{};
     if (x_dtype == QD_BF16) nr.x_bf16 = x_in; else nr.x_f32 = (const float*)x_in;
     nr.x_res = x_out; nr.gain = L.attn_norm; nr.out = nrm; nr.rows = N; nr.D = D; nr.eps = c.rms_eps;
-    QD_LAUNCH(qd::launch_prefill_norm(nr, 1, s), "prefill norm");
-    // q|k|v = norm(x) W^T (+ bias)
+    // q|k|v = norm(x) W^T (+ bias); a K-split product accumulates into a cleared buffer
     qd::GemmArgs g{};
     g.A = nrm; g.w[0] = L.wq; g.w[1] = L.wk; g.w[2] = L.wv; g.bias[0] = L.bq; g.bias[1] = L.bk; g.bias[2] = L.bv;
     g.seg_end[0] = Hq * hd; g.seg_end[1] = (Hq + Hkv) * hd; g.seg_end[2] = qkvr;
     g.M = N; g.N = qkvr; g.K = D; g.C = qkv; g.ldc = qkvr;
-    QD_LAUNCH_K(QD_K_PREFILL_GEMM, qd::launch_mfma_gemm(g, qd::GEMM_STORE, s), "qkv gemm");
+    const int qkv_splits = qd::mfma_gemm_splits(g, qd::GEMM_STORE);
+    if (qkv_splits > 1) { nr.zero = qkv; nr.zero_n = (long)N * qkvr; }
+    QD_LAUNCH(qd::launch_prefill_norm(nr, 1, s), "prefill norm");
+    QD_LAUNCH_K(QD_K_PREFILL_GEMM, qd::launch_mfma_gemm(g, qd::GEMM_STORE, qkv_splits, s), "qkv gemm");
     // [q/k norm] + RoPE; K/V of every row into the cache
     qd::PrefillRopeArgs rp{};
     rp.qkv = qkv; rp.q_out = qrot; rp.k_cache = kc; rp.v_cache = vc; rp.block_table = kv->block_table;
@@ -508,7 +510,7 @@ qd_status qd_prefill_block(const qd_config* cfg, const qd_layer* layer, int32_t 
     qd::GemmArgs go{};
     go.A = ctxb; go.w[0] = L.wo; go.seg_end[0] = go.seg_end[1] = go.seg_end[2] = D;
     go.M = N; go.N = D; go.K = Hq * hd; go.C = x_out; go.ldc = D;
-    QD_LAUNCH_K(QD_K_PREFILL_GEMM, qd::launch_mfma_gemm(go, qd::GEMM_RESID, s), "o_proj gemm");
+    QD_LAUNCH_K(QD_K_PREFILL_GEMM, qd::launch_mfma_gemm(go, qd::GEMM_RESID, 0, s), "o_proj gemm");
     // RMSNorm -> bf16; h = silu(n W_g^T) * (n W_u^T) in bf16
     qd::PrefillNormArgs n2{};
     n2.x_f32 = x_out; n2.gain = L.mlp_norm; n2.out = nrm; n2.rows = N; n2.D = D; n2.eps = c.rms_eps;
@@ -516,12 +518,12 @@ qd_status qd_prefill_block(const qd_config* cfg, const qd_layer* layer, int32_t 
     qd::GemmArgs gu{};
     gu.A = nrm; gu.w[0] = L.w_gate; gu.w[1] = L.w_up; gu.seg_end[0] = gu.seg_end[1] = gu.seg_end[2] = c.ffn;
     gu.M = N; gu.N = c.ffn; gu.K = D; gu.C = h; gu.ldc = c.ffn;
-    QD_LAUNCH_K(QD_K_PREFILL_GEMM, qd::launch_mfma_gemm(gu, qd::GEMM_SWIGLU, s), "gate/up gemm");
+    QD_LAUNCH_K(QD_K_PREFILL_GEMM, qd::launch_mfma_gemm(gu, qd::GEMM_SWIGLU, 1, s), "gate/up gemm");
     // x += h W_d^T
     qd::GemmArgs gd{};
     gd.A = h; gd.w[0] = L.w_down; gd.seg_end[0] = gd.seg_end[1] = gd.seg_end[2] = D;
     gd.M = N; gd.N = D; gd.K = c.ffn; gd.C = x_out; gd.ldc = D;
-    QD_LAUNCH_K(QD_K_PREFILL_GEMM, qd::launch_mfma_gemm(gd, qd::GEMM_RESID, s), "down gemm");
+    QD_LAUNCH_K(QD_K_PREFILL_GEMM, qd::launch_mfma_gemm(gd, qd::GEMM_RESID, 0, s), "down gemm");
     return QD_OK;
 }
 

@@ -120,7 +120,11 @@ struct GemmArgs {
     void* C;                // float [M][ldc] (STORE, RESID) or bf16 [M][ldc] (SWIGLU)
     int ldc;
 };
-hipError_t launch_mfma_gemm(const GemmArgs& a, int epi, hipStream_t s);
+// splits > 1 (not for SwiGLU): K is cut into that many ranges whose partial products
+// are added into C with float atomics (RESID: onto the residual; STORE: C zeroed
+// beforehand, bias added by the first range); splits = 0 picks a value
+hipError_t launch_mfma_gemm(const GemmArgs& a, int epi, int splits, hipStream_t s);
+int mfma_gemm_splits(const GemmArgs& a, int epi);
 
 struct PrefillNormArgs {
     const void* x_bf16;     // input rows, bf16 ... or
@@ -130,6 +134,8 @@ struct PrefillNormArgs {
     uint16_t* out;          // bf16 [rows][D]
     int rows, D;
     float eps;
+    float* zero;            // optional: zero_n floats cleared (the next split-K GEMM's output)
+    long zero_n;
 };
 hipError_t launch_prefill_norm(const PrefillNormArgs& a, int w_is_bf16, hipStream_t s);
 

@@ -5,14 +5,20 @@
 // SwiGLU output). The residual stream stays float32.
 //
 // GEMM: C[M][N] (op)= A[M][K] . W[N][K]^T with both operands K-contiguous, as
-// the weights are stored row-major [out][in]. One workgroup of 4 waves owns a
-// 128 x 128 tile (2 x 2 waves of 64 x 64, each 2 x 2 MFMA tiles of 32 x 32),
-// walks K in steps of 32 with the A and W tiles staged in LDS (double
-// buffered, padded rows against bank conflicts), and the next K step's global
-// loads are issued before the current step's MFMAs. Epilogues (Tang page,
-// section 2.3): store float32 (q|k|v), add into the float32 residual (o_proj,
-// down), or silu(gate) * up rounded to bf16 with gate and up tiles of the same
-// columns held by the same lane (sibling reductions merged).
+// the weights are stored row-major [out][in]. A workgroup of 4 waves owns a
+// 128 x BN tile (BN = 128 or 256; 2 x 2 waves of 64 x BN/2, each a grid of
+// 32 x 32 MFMA tiles) and walks K in steps of 64. Tiles are staged in LDS
+// (double buffered, rows padded against bank conflicts) from two register
+// stages, so a tile's global loads are issued two K steps before its MFMAs:
+// at M = 512 the loads come mostly from L2 and the other cache levels, and two
+// steps of MFMAs cover that latency. The wider tile keeps the LDS traffic per
+// MFMA below the LDS bandwidth (a 64 x 128 wave tile reads 6 operand fragments
+// per 8 MFMAs). Workgroups are numbered so that the M tiles sharing one weight
+// tile are dispatched together onto one XCD (dispatch goes round-robin over
+// the 8 XCDs) and read it from that XCD's L2. Epilogues (Tang page, section
+// 2.3): store float32 (q|k|v, plus bias), add into the float32 residual
+// (o_proj, down), or silu(gate) * up rounded to bf16 with the gate and up
+// tiles of the same columns held by the same lane (sibling reductions merged).
 #include "qd_device.h"
 #include "qd_launch.h"
 
@@ -21,12 +27,13 @@ namespace qd {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 
-constexpr int kGemmBM = 128, kGemmBN = 128, kGemmBK = 32;
-constexpr int kGemmLdsRow = kGemmBK + 8;   // bf16 elements per padded LDS row (80 bytes)
+constexpr int kGemmBM = 128, kGemmBK = 64;
+constexpr int kGemmLdsRow = kGemmBK + 8;   // bf16 elements per padded LDS row (144 bytes)
+constexpr int kXcds = 8;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
-// W row pointer of output column n (stacked segments, as in the decode GEMV)
+// W row of output column n (stacked segments, as in the decode GEMV)
 __device__ __forceinline__ const uint16_t* gemm_wrow(const GemmArgs& a, int n) {
     const bool s0 = n < a.seg_end[0], s1 = n < a.seg_end[1];
     const void* w = s0 ? a.w[0] : (s1 ? a.w[1] : a.w[2]);
@@ -34,99 +41,138 @@ __device__ __forceinline__ const uint16_t* gemm_wrow(const GemmArgs& a, int n) {
     return (const uint16_t*)w + (long)(n - base) * a.K;
 }
 
-template <int EPI>
-__global__ __launch_bounds__(256) void mfma_gemm_kernel(GemmArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][kGemmBM * kGemmLdsRow];
-    __shared__ __attribute__((aligned(16))) uint16_t Ws[2][kGemmBN * kGemmLdsRow];
+template <int EPI, int BN>
+__global__ __launch_bounds__(256) void mfma_gemm_kernel(GemmArgs a, int ntn, int ntm) {
+    constexpr int BM = kGemmBM, BK = kGemmBK, LR = kGemmLdsRow;
+    constexpr int TJ = BN / 64;                 // 32-column MFMA tiles per wave
+    constexpr int AL = BM * BK / 8 / 256;       // 16-byte A chunks per thread per K step
+    constexpr int WL = BN * BK / 8 / 256;       // 16-byte W chunks per thread per K step
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LR];
+    __shared__ __attribute__((aligned(16))) uint16_t Ws[2][BN * LR];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int M = a.M, K = a.K;
-    // output tile: rows m0.., columns: for SwiGLU the tile holds 64 h-columns as
-    // 64 gate rows followed by 64 up rows of W; otherwise 128 columns of C
-    const int m0 = blockIdx.y * kGemmBM;
-    const int tileN = blockIdx.x;
 
-    // each thread loads 2 chunks (16 bytes = 8 bf16) of the A tile and 2 of the W tile per K step
-    int a_row[2], a_kc[2], w_row[2], w_kc[2];
-    const uint16_t* a_ptr[2];
-    const uint16_t* w_ptr[2];
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        const int idx = tid + r * 256;           // 0..511: row = idx / 4, chunk = idx % 4
-        a_row[r] = idx >> 2; a_kc[r] = idx & 3;
-        w_row[r] = idx >> 2; w_kc[r] = idx & 3;
-        const int m = m0 + a_row[r];
-        a_ptr[r] = (m < M) ? (const uint16_t*)a.A + (long)m * K : nullptr;
-        int n;
-        bool valid;
-        if (EPI == GEMM_SWIGLU) {
-            const int hcol = tileN * 64 + (w_row[r] & 63);
-            valid = hcol < a.N;
-            w_ptr[r] = valid ? (const uint16_t*)a.w[w_row[r] >> 6] + (long)hcol * K : nullptr;
+    // tile of this workgroup: the ntm M tiles of an N tile are consecutive on one XCD
+    int tileN, tileM;
+    {
+        const int id = blockIdx.x;
+        if (ntn % kXcds == 0) {
+            const int xcd = id % kXcds, slot = id / kXcds;
+            tileM = slot % ntm;
+            tileN = (slot / ntm) * kXcds + xcd;
         } else {
-            n = tileN * kGemmBN + w_row[r];
-            valid = n < a.N;
-            w_ptr[r] = valid ? gemm_wrow(a, n) : nullptr;
+            tileN = id % ntn;
+            tileM = id / ntn;
         }
     }
-    auto load_tile = [&](int k0, uint4 (&ra)[2], uint4 (&rw)[2]) {
+    const int m0 = tileM * BM;
+
+    // chunk q of this thread: row idx / 8, 16-byte column idx % 8 of the tile's K step;
+    // rows outside the matrix read row 0 and are zeroed
+    const uint16_t* a_src[AL];
+    bool a_ok[AL];
+    const uint16_t* w_src[WL];
+    bool w_ok[WL];
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            const int ka = k0 + a_kc[r] * 8, kw = k0 + w_kc[r] * 8;
-            ra[r] = (a_ptr[r] && ka < K) ? *(const uint4*)(a_ptr[r] + ka) : make_uint4(0, 0, 0, 0);
-            rw[r] = (w_ptr[r] && kw < K) ? *(const uint4*)(w_ptr[r] + kw) : make_uint4(0, 0, 0, 0);
+    for (int q = 0; q < AL; ++q) {
+        const int m = m0 + (tid + 256 * q) / 8;
+        a_ok[q] = m < M;
+        a_src[q] = (const uint16_t*)a.A + (long)(a_ok[q] ? m : 0) * K;
+    }
+#pragma unroll
+    for (int q = 0; q < WL; ++q) {
+        const int r = (tid + 256 * q) / 8;
+        if (EPI == GEMM_SWIGLU) {
+            const int hcol = tileN * (BN / 2) + (r % (BN / 2));
+            w_ok[q] = hcol < a.N;
+            w_src[q] = (const uint16_t*)a.w[r / (BN / 2)] + (long)(w_ok[q] ? hcol : 0) * K;
+        } else {
+            const int n = tileN * BN + r;
+            w_ok[q] = n < a.N;
+            w_src[q] = w_ok[q] ? gemm_wrow(a, n) : (const uint16_t*)a.w[0];
+        }
+    }
+    const int kc = (tid & 7) * 8;
+    struct Stage {
+        uint4 a[AL];
+        uint4 w[WL];
+    };
+    auto load = [&](Stage& st, int kt) {
+        const int k = kt * BK + kc;
+        const bool kok = k < K;
+        const int kk = kok ? k : 0;
+#pragma unroll
+        for (int q = 0; q < AL; ++q) {
+            const uint4 v = *(const uint4*)(a_src[q] + kk);
+            st.a[q] = (kok && a_ok[q]) ? v : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int q = 0; q < WL; ++q) {
+            const uint4 v = *(const uint4*)(w_src[q] + kk);
+            st.w[q] = (kok && w_ok[q]) ? v : make_uint4(0, 0, 0, 0);
         }
     };
-    auto store_tile = [&](int buf, const uint4 (&ra)[2], const uint4 (&rw)[2]) {
+    auto store = [&](int buf, const Stage& st) {
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            *(uint4*)&As[buf][a_row[r] * kGemmLdsRow + a_kc[r] * 8] = ra[r];
-            *(uint4*)&Ws[buf][w_row[r] * kGemmLdsRow + w_kc[r] * 8] = rw[r];
-        }
+        for (int q = 0; q < AL; ++q) *(uint4*)&As[buf][((tid + 256 * q) / 8) * LR + kc] = st.a[q];
+#pragma unroll
+        for (int q = 0; q < WL; ++q) *(uint4*)&Ws[buf][((tid + 256 * q) / 8) * LR + kc] = st.w[q];
     };
 
-    f32x16_t acc[2][2];
+    f32x16_t acc[2][TJ];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < TJ; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-    uint4 ra[2], rw[2];
-    load_tile(0, ra, rw);
-    store_tile(0, ra, rw);
-    __syncthreads();
-    const int nk = (K + kGemmBK - 1) / kGemmBK;
-    // lane's operand rows within the wave tile and k offset within a 16-wide step
+    // lane's operand row within a 32-row MFMA tile and k offset within a 16-wide step
     const int lrow = lane & 31, lk = (lane >> 5) * 8;
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nk) load_tile((kt + 1) * kGemmBK, ra, rw);
+    auto wtile_row = [&](int j) {
+        if (EPI == GEMM_SWIGLU)   // j < TJ/2: gate rows, else up rows, of h-columns wn*BN/4 ..
+            return (j < TJ / 2 ? 0 : BN / 2) + wn * (BN / 4) + (j % (TJ / 2)) * 32 + lrow;
+        return wn * (BN / 2) + j * 32 + lrow;
+    };
+    auto compute = [&](int buf) {
 #pragma unroll
-        for (int ks = 0; ks < kGemmBK; ks += 16) {
-            bf16x8_t av[2], bv[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-                av[i] = as_bf16x8(*(const uint4*)&As[buf][(wm * 64 + i * 32 + lrow) * kGemmLdsRow + ks + lk]);
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                // SwiGLU: wave column-half wn holds h-columns wn*32..; j = 0 gate rows, j = 1 up rows
-                const int wrow = (EPI == GEMM_SWIGLU) ? (j * 64 + wn * 32 + lrow) : (wn * 64 + j * 32 + lrow);
-                bv[j] = as_bf16x8(*(const uint4*)&Ws[buf][wrow * kGemmLdsRow + ks + lk]);
-            }
+        for (int ks = 0; ks < BK; ks += 16) {
+            bf16x8_t av[2], bv[TJ];
 #pragma unroll
             for (int i = 0; i < 2; ++i)
+                av[i] = as_bf16x8(*(const uint4*)&As[buf][(wm * 64 + i * 32 + lrow) * LR + ks + lk]);
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < TJ; ++j) bv[j] = as_bf16x8(*(const uint4*)&Ws[buf][wtile_row(j) * LR + ks + lk]);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < TJ; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
         }
-        if (kt + 1 < nk) {
-            store_tile(buf ^ 1, ra, rw);
-            __syncthreads();
-        }
+    };
+
+    // pipeline: LDS[kt & 1] holds step kt; register stages hold steps kt + 1 and kt + 2
+    const int nk = (K + BK - 1) / BK;
+    Stage s0, s1;
+    load(s0, 0);
+    if (nk > 1) load(s1, 1);
+    store(0, s0);
+    if (nk > 2) load(s0, 2);
+    __syncthreads();
+    for (int kt = 0; kt < nk; kt += 2) {
+        compute(0);                       // step kt (even)
+        if (kt + 1 < nk) store(1, s1);
+        if (kt + 3 < nk) load(s1, kt + 3);
+        __syncthreads();
+        if (kt + 1 >= nk) break;
+        compute(1);                       // step kt + 1
+        if (kt + 2 < nk) store(0, s0);
+        if (kt + 4 < nk) load(s0, kt + 4);
+        __syncthreads();
     }
-    // epilogue: lane holds column (lane % 32) of each 32 x 32 tile and rows
+
+    // epilogue: lane holds column lrow of each 32 x 32 tile and rows
     // (e / 4) * 8 + (lane / 32) * 4 + (e % 4)
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -135,21 +181,24 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(GemmArgs a) {
             const int m = m0 + wm * 64 + i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
             if (m >= M) continue;
             if (EPI == GEMM_SWIGLU) {
-                const int hcol = tileN * 64 + wn * 32 + lrow;
-                if (hcol < a.N) {
-                    const float g = acc[i][0][e], u = acc[i][1][e];
-                    ((uint16_t*)a.C)[(long)m * a.ldc + hcol] = f32_to_bf16(silu(g) * u);
+#pragma unroll
+                for (int j = 0; j < TJ / 2; ++j) {
+                    const int hcol = tileN * (BN / 2) + wn * (BN / 4) + j * 32 + lrow;
+                    if (hcol < a.N) {
+                        const float g = acc[i][j][e], u = acc[i][j + TJ / 2][e];
+                        ((uint16_t*)a.C)[(long)m * a.ldc + hcol] = f32_to_bf16(silu(g) * u);
+                    }
                 }
             } else {
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const int n = tileN * kGemmBN + wn * 64 + j * 32 + lrow;
+                for (int j = 0; j < TJ; ++j) {
+                    const int n = tileN * BN + wn * (BN / 2) + j * 32 + lrow;
                     if (n >= a.N) continue;
                     float* cp = (float*)a.C + (long)m * a.ldc + n;
                     if (EPI == GEMM_STORE) {
-                        const bool s0 = n < a.seg_end[0], s1 = n < a.seg_end[1];
-                        const void* bsel = s0 ? a.bias[0] : (s1 ? a.bias[1] : a.bias[2]);
-                        const int base = s0 ? 0 : (s1 ? a.seg_end[0] : a.seg_end[1]);
+                        const bool s0b = n < a.seg_end[0], s1b = n < a.seg_end[1];
+                        const void* bsel = s0b ? a.bias[0] : (s1b ? a.bias[1] : a.bias[2]);
+                        const int base = s0b ? 0 : (s1b ? a.seg_end[0] : a.seg_end[1]);
                         *cp = bsel ? acc[i][j][e] + bf16_to_f32(((const uint16_t*)bsel)[n - base]) : acc[i][j][e];
                     } else {
                         *cp = *cp + acc[i][j][e];
@@ -160,14 +209,250 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(GemmArgs a) {
     }
 }
 
-hipError_t launch_mfma_gemm(const GemmArgs& a, int epi, hipStream_t s) {
-    const int cols = epi == GEMM_SWIGLU ? 64 : kGemmBN;
-    dim3 grid((a.N + cols - 1) / cols, (a.M + kGemmBM - 1) / kGemmBM);
-    switch (epi) {
-        case GEMM_STORE: hipLaunchKernelGGL((mfma_gemm_kernel<GEMM_STORE>), grid, dim3(256), 0, s, a); break;
-        case GEMM_RESID: hipLaunchKernelGGL((mfma_gemm_kernel<GEMM_RESID>), grid, dim3(256), 0, s, a); break;
-        default: hipLaunchKernelGGL((mfma_gemm_kernel<GEMM_SWIGLU>), grid, dim3(256), 0, s, a); break;
+// ---------------------------------------------------------------------------
+// The same GEMM with the tiles fed by LDS DMA (global_load_lds_dwordx4): each
+// lane's 16 bytes go from memory straight into LDS at the wave's base + 16 x
+// lane, no register staging. At M = 512 the tiles come from L2 and the caches
+// behind it with a latency of a microsecond or two, so what bounds a CU is the
+// bytes it has in flight: K steps of 32 go through a ring of NS LDS stages
+// (the LDS holds about 144 KB of them) and each step's loads are issued
+// NS - 1 steps ahead. The DMA writes rows of 32 bf16 (64 bytes) back to back,
+// so the rows are swizzled instead of padded: 16-byte chunk c of row r sits at
+// position c ^ ((r / 4) % 4), which keeps 16 consecutive rows on distinct
+// banks for the fragment reads; lane L of a load instruction (16 rows) reads
+// chunk (L % 4) ^ ((L / 16) % 4) of row L / 4. Completion is counted with
+// s_waitcnt vmcnt before one barrier per step, which also frees the stage read
+// in the previous step. Rows outside the matrix read row 0 (their outputs are
+// dropped); K must be a multiple of 32 (the DMA cannot zero a tail).
+typedef __attribute__((address_space(3))) void qd_lds_void;
+
+// One wave-wide LDS DMA of 16 bytes per lane: lane i's global source lands at
+// lds + 16 i. Issued as inline asm so the compiler does not see an LDS write it
+// would have to order against later LDS reads: left to itself it cannot tell
+// which ring stage a pending DMA targets and waits for all of them. Completion
+// is the caller's business (s_waitcnt vmcnt); the compiler's own vmcnt waits
+// stay correct, as extra outstanding loads only make a wait stricter.
+__device__ __forceinline__ void lds_dma16(const uint16_t* src, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds_addr) : "memory", "m0");
+}
+
+// s_waitcnt immediates (vmcnt in bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8])
+constexpr int wait_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x70 | 0xF00; }
+constexpr int kWaitLgkm0 = 0xF | (0x3 << 14) | 0x70;
+constexpr int kDmaBK = 32;
+constexpr int kDmaLds = 147456;    // bytes of LDS the ring may take
+
+template <int BM, int BN>
+constexpr int dma_stages() { return kDmaLds / ((BM + BN) * kDmaBK * 2); }
+
+// BM x BN tile, 2 x 2 waves of BM/2 x BN/2 (TI x TJ MFMA tiles of 32 x 32)
+template <int EPI, int BM, int BN>
+__global__ __launch_bounds__(256) void mfma_gemm_dma_kernel(GemmArgs a, int ntn, int ntm, int splits) {
+    constexpr int BK = kDmaBK, RB = BK * 2;       // row bytes
+    constexpr int TI = BM / 64, TJ = BN / 64;
+    constexpr int QA = BM / 64, QW = BN / 64;    // load instructions (16 rows each) per wave per step
+    constexpr int NQ = QA + QW;
+    constexpr int NS = dma_stages<BM, BN>();
+    constexpr int SA = BM * RB, SB = (BM + BN) * RB;            // A part, whole stage
+    static_assert(NS >= 3 && (NS - 2) * NQ <= 63, "ring depth");
+    __shared__ __attribute__((aligned(16))) uint8_t ring[NS * SB];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int M = a.M, K = a.K;
+
+    // tile and K range of this workgroup; the M tiles of an N tile (and K range) are
+    // consecutive on one XCD
+    int tileN, tileM, split;
+    {
+        const int id = blockIdx.x;
+        if (ntn % kXcds == 0) {
+            const int xcd = id % kXcds, slot = id / kXcds;
+            tileM = slot % ntm;
+            split = (slot / ntm) % splits;
+            tileN = (slot / ntm / splits) * kXcds + xcd;
+        } else {
+            tileN = id % ntn;
+            tileM = (id / ntn) % ntm;
+            split = id / ntn / ntm;
+        }
     }
+    const int m0 = tileM * BM;
+
+    // source of lane's chunk in load instruction q: row 16 (wave Q + q) + lane / 4,
+    // chunk (lane % 4) ^ ((lane / 16) % 4)
+    const int lchunk = ((lane & 3) ^ ((lane >> 4) & 3)) * 8;
+    const uint16_t* asrc[QA];
+    const uint16_t* wsrc[QW];
+#pragma unroll
+    for (int q = 0; q < QA; ++q) {
+        const int m = m0 + 16 * (wave * QA + q) + (lane >> 2);
+        asrc[q] = (const uint16_t*)a.A + (long)(m < M ? m : 0) * K + lchunk;
+    }
+#pragma unroll
+    for (int q = 0; q < QW; ++q) {
+        const int r = 16 * (wave * QW + q) + (lane >> 2);
+        const uint16_t* p;
+        if (EPI == GEMM_SWIGLU) {
+            const int hcol = tileN * (BN / 2) + (r % (BN / 2));
+            p = (const uint16_t*)a.w[r / (BN / 2)] + (long)(hcol < a.N ? hcol : 0) * K;
+        } else {
+            const int n = tileN * BN + r;
+            p = n < a.N ? gemm_wrow(a, n) : (const uint16_t*)a.w[0];
+        }
+        wsrc[q] = p + lchunk;
+    }
+    const uint32_t ring_lds = (uint32_t)(uintptr_t)(qd_lds_void*)ring;
+    const int nk_all = K / BK;
+    const int kt_begin = split * nk_all / splits;
+    const int nk = (split + 1) * nk_all / splits - kt_begin;   // K steps of this range
+    auto issue = [&](int stage, int kt) {
+        const int k0 = (kt_begin + kt) * BK;
+        const uint32_t base = ring_lds + stage * SB;
+#pragma unroll
+        for (int q = 0; q < QA; ++q)
+            lds_dma16(asrc[q] + k0, __builtin_amdgcn_readfirstlane(base + 16 * (wave * QA + q) * RB));
+#pragma unroll
+        for (int q = 0; q < QW; ++q)
+            lds_dma16(wsrc[q] + k0, __builtin_amdgcn_readfirstlane(base + SA + 16 * (wave * QW + q) * RB));
+    };
+
+    f32x16_t acc[TI][TJ];
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    const int lrow = lane & 31, lhalf = lane >> 5;
+    auto wtile_row = [&](int j) {
+        if (EPI == GEMM_SWIGLU)
+            return (j < TJ / 2 ? 0 : BN / 2) + wn * (BN / 4) + (j % (TJ / 2)) * 32 + lrow;
+        return wn * (BN / 2) + j * 32 + lrow;
+    };
+    auto frag = [&](const uint8_t* base, int row, int ks) {
+        const int c = 2 * ks + lhalf;
+        return as_bf16x8(*(const uint4*)(base + row * RB + ((c ^ ((row >> 2) & 3)) << 4)));
+    };
+    auto compute = [&](const uint8_t* st) {
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            bf16x8_t av[TI], bv[TJ];
+#pragma unroll
+            for (int i = 0; i < TI; ++i) av[i] = frag(st, wm * (BM / 2) + i * 32 + lrow, ks);
+#pragma unroll
+            for (int j = 0; j < TJ; ++j) bv[j] = frag(st + SA, wtile_row(j), ks);
+#pragma unroll
+            for (int i = 0; i < TI; ++i)
+#pragma unroll
+                for (int j = 0; j < TJ; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+        }
+    };
+    // Every step issues exactly NQ loads per lane (past the end it reloads the last
+    // step into the free stage, unused), so one constant wait count serves all steps.
+    if (nk > 0) {
+#pragma unroll
+        for (int t = 0; t < NS - 1; ++t) issue(t, t < nk ? t : nk - 1);
+        for (int t = 0; t < nk; ++t) {
+            __builtin_amdgcn_s_waitcnt(wait_vm((NS - 2) * NQ));   // step t landed (this lane's part)
+            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);               // this lane's reads of step t-1 done
+            __builtin_amdgcn_s_barrier();                         // ... and every lane's
+            const int tn = t + NS - 1;
+            issue((t + NS - 1) % NS, tn < nk ? tn : nk - 1);      // into the stage of step t-1
+            compute(ring + (t % NS) * SB);
+        }
+        __builtin_amdgcn_s_waitcnt(wait_vm(0));   // no DMA into LDS outlives the loop
+    }
+
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int m = m0 + wm * (BM / 2) + i * 32 + (e >> 2) * 8 + lhalf * 4 + (e & 3);
+            if (m >= M) continue;
+            if (EPI == GEMM_SWIGLU) {
+#pragma unroll
+                for (int j = 0; j < TJ / 2; ++j) {
+                    const int hcol = tileN * (BN / 2) + wn * (BN / 4) + j * 32 + lrow;
+                    if (hcol < a.N) {
+                        const float g = acc[i][j][e], u = acc[i][j + TJ / 2][e];
+                        ((uint16_t*)a.C)[(long)m * a.ldc + hcol] = f32_to_bf16(silu(g) * u);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < TJ; ++j) {
+                    const int n = tileN * BN + wn * (BN / 2) + j * 32 + lrow;
+                    if (n >= a.N) continue;
+                    float* cp = (float*)a.C + (long)m * a.ldc + n;
+                    float v = acc[i][j][e];
+                    if (EPI == GEMM_STORE && split == 0) {
+                        const bool s0b = n < a.seg_end[0], s1b = n < a.seg_end[1];
+                        const void* bsel = s0b ? a.bias[0] : (s1b ? a.bias[1] : a.bias[2]);
+                        const int base = s0b ? 0 : (s1b ? a.seg_end[0] : a.seg_end[1]);
+                        if (bsel) v += bf16_to_f32(((const uint16_t*)bsel)[n - base]);
+                    }
+                    if (splits > 1) unsafeAtomicAdd(cp, v);
+                    else if (EPI == GEMM_STORE) *cp = v;
+                    else *cp = *cp + v;
+                }
+            }
+        }
+    }
+}
+
+constexpr int kGemmTargetWgs = 256;
+
+// K a multiple of 32: LDS DMA kernel. Tile choice (measured at M = 512 on 256
+// CUs): SwiGLU takes 256 x 256 tiles (two 128 x 128 operand blocks per wave
+// halve the LDS and memory bytes per MFMA) and cannot split K (its epilogue is
+// not linear). q|k|v takes 128 x 128 tiles (192 workgroups). The residual
+// products take 128 x 128 tiles and at most two K ranges whose partial
+// products meet in the float32 residual through float atomics: the atomics
+// (about 2.4e11 per second) cost more than the arithmetic they spread past two
+// ranges, and 256 x 256 tiles would need eight. Other K: the register-staged
+// kernel with 128 x 128 tiles.
+struct GemmPlan { int bm, bn, splits; };
+static GemmPlan gemm_plan(const GemmArgs& a, int epi) {
+    if (a.K % kDmaBK != 0) return {kGemmBM, 128, 1};
+    if (epi == GEMM_SWIGLU) return {a.M <= 128 ? 128 : 256, 256, 1};
+    if (epi == GEMM_STORE) return {128, 128, 1};
+    const int nk = a.K / kDmaBK;
+    const int tiles = ((a.M + 127) / 128) * ((a.N + 127) / 128);
+    int s = 1;
+    while (s < 2 && (long)tiles * (s + 1) <= kGemmTargetWgs && nk / (s + 1) >= 8) ++s;
+    return {128, 128, s};
+}
+int mfma_gemm_splits(const GemmArgs& a, int epi) { return gemm_plan(a, epi).splits; }
+
+hipError_t launch_mfma_gemm(const GemmArgs& a, int epi, int splits, hipStream_t s) {
+    if (a.M < 1 || a.N < 1 || a.K < 8 || a.K % 8) return hipErrorInvalidValue;
+    const GemmPlan pl = gemm_plan(a, epi);
+    if (splits <= 0) splits = pl.splits;
+    if (splits != pl.splits) return hipErrorInvalidValue;
+    if (a.K % kDmaBK != 0) {
+        const int ntm = (a.M + kGemmBM - 1) / kGemmBM;
+        const int cols = epi == GEMM_SWIGLU ? 64 : 128, ntn = (a.N + cols - 1) / cols;
+        switch (epi) {
+            case GEMM_STORE: hipLaunchKernelGGL((mfma_gemm_kernel<GEMM_STORE, 128>), dim3(ntn * ntm), dim3(256), 0, s, a, ntn, ntm); break;
+            case GEMM_RESID: hipLaunchKernelGGL((mfma_gemm_kernel<GEMM_RESID, 128>), dim3(ntn * ntm), dim3(256), 0, s, a, ntn, ntm); break;
+            default: hipLaunchKernelGGL((mfma_gemm_kernel<GEMM_SWIGLU, 128>), dim3(ntn * ntm), dim3(256), 0, s, a, ntn, ntm); break;
+        }
+        return hipGetLastError();
+    }
+    const int ntm = (a.M + pl.bm - 1) / pl.bm;
+    const int cols = epi == GEMM_SWIGLU ? pl.bn / 2 : pl.bn, ntn = (a.N + cols - 1) / cols;
+    const dim3 grid(ntn * ntm * splits);
+#define QD_GEMM_DMA(E)                                                                                                  \
+    if (pl.bm == 256) hipLaunchKernelGGL((mfma_gemm_dma_kernel<E, 256, 256>), grid, dim3(256), 0, s, a, ntn, ntm, splits); \
+    else if (pl.bn == 256) hipLaunchKernelGGL((mfma_gemm_dma_kernel<E, 128, 256>), grid, dim3(256), 0, s, a, ntn, ntm, splits); \
+    else hipLaunchKernelGGL((mfma_gemm_dma_kernel<E, 128, 128>), grid, dim3(256), 0, s, a, ntn, ntm, splits);
+    switch (epi) {
+        case GEMM_STORE: QD_GEMM_DMA(GEMM_STORE) break;
+        case GEMM_RESID: QD_GEMM_DMA(GEMM_RESID) break;
+        default: QD_GEMM_DMA(GEMM_SWIGLU) break;
+    }
+#undef QD_GEMM_DMA
     return hipGetLastError();
 }
 
@@ -181,6 +466,11 @@ __global__ __launch_bounds__(256) void prefill_norm_kernel(PrefillNormArgs a) {
     __shared__ float wsum[4];
     const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int D = a.D;
+    if (a.zero) {   // this row's share of the buffer to clear
+        const long per = (a.zero_n + gridDim.x - 1) / gridDim.x;
+        const long z0 = (long)row * per, z1 = min(a.zero_n, z0 + per);
+        for (long i = z0 + tid; i < z1; i += 256) a.zero[i] = 0.f;
+    }
     float ss = 0.f;
     for (int d = tid; d < D; d += 256) {
         const float v = a.x_bf16 ? bf16_to_f32(((const uint16_t*)a.x_bf16)[(long)row * D + d])
