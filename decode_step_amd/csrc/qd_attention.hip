@@ -39,6 +39,11 @@ constexpr int kAttnWaves = 8;    // waves per workgroup
 constexpr int kAttnPassesWide = 9;
 constexpr int kAttnPassesGrouped = 4;
 constexpr int kMaxSplits = 64;
+constexpr int kAttnPage = 16;     // tokens per KV page (the only page size the library takes)
+constexpr float kLog2e = 1.4426950408889634f;
+
+// 2^x from the hardware exp2 (v_exp_f32); e^x = 2^(x log2 e)
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <int HD, typename KVT, int NP>
 constexpr int attn_chunk() { return NP * kAttnWaves * (kWave / (HD / VecN<KVT>::n)); }
@@ -71,7 +76,7 @@ __device__ __forceinline__ void rope_lane(float (&u)[CE], const float (&pr)[CE],
 }
 
 template <typename WT, typename KVT, int HD, int NP>
-__global__ __launch_bounds__(kAttnWaves * kWave) void attn_kernel(AttnArgs a) {
+__device__ __forceinline__ void attn_body(const AttnArgs& a) {
     constexpr int CE = VecN<KVT>::n;
     constexpr int LPT = HD / CE;
     constexpr int TPW = kWave / LPT;
@@ -79,13 +84,13 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_kernel(AttnArgs a) {
     constexpr int TPB = NWV * TPW;
     constexpr int MAXT = NP * TPB;
     constexpr int NT = NWV * kWave;
-    __shared__ float sc[kMaxGroup][MAXT];
-    __shared__ float red[NWV][kMaxGroup][HD];
-    __shared__ float mls[kMaxGroup][2];
+    constexpr int PG = kAttnPage;
+    __shared__ float red[NWV][kMaxGroup][HD];   // each wave's o per head
+    __shared__ float2 wml[NWV][kMaxGroup];      // each wave's (m, l) per head
     __shared__ float qs[kMaxGroup][HD];
     __shared__ uint4 knew[LPT];   // the new token's K and V rows in stored (cache-type) form
     __shared__ uint4 vnew[LPT];
-    __shared__ int spage[MAXT / 16 + 2];
+    __shared__ int spage[MAXT / PG + 2];
 
     const int G = a.Hq / a.Hkv;
     const int hgroups = (G + a.hpw - 1) / a.hpw;
@@ -93,7 +98,7 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_kernel(AttnArgs a) {
     const int h0 = hg * a.hpw, nh = min(a.hpw, G - h0);   // query heads g*G + h0 .. + nh - 1
     const bool prefill = a.prefill_start >= 0;
     const int p = prefill ? a.prefill_start + b : a.pos[b];
-    if (p < 0 || p >= a.capacity || a.chunk > MAXT || a.hpw > kMaxGroup || a.page < 16 || nh <= 0) return;
+    if (p < 0 || p >= a.capacity || a.chunk > MAXT || a.hpw > kMaxGroup || nh <= 0) return;
     const int T = p + 1;
     const int ns = min(a.S, (T + a.chunk - 1) / a.chunk);
     const int t_begin = s * a.chunk;
@@ -105,10 +110,35 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_kernel(AttnArgs a) {
     const int li = lane % LPT, slot = lane / LPT;
     const int* bt = a.block_table + (prefill ? 0L : (long)b * a.max_blocks);
 
-    // page ids of this split's pages (an entry outside the pool reads as page 0
-    // and is masked), then every K/V row load issued back to back
-    const int pg0 = t_begin / a.page;
-    const int npg = (t_end - 1) / a.page - pg0 + 1;
+    // 1. loads of the q/k rotation (one head-chunk of CE elements per thread, LPT
+    //    threads per head; item nh is the new k), issued first so their latency
+    //    overlaps the page-table and K/V loads below
+    const int qkvr = (a.Hq + 2 * a.Hkv) * HD;
+    const int items = prefill ? 0 : (nh + (has_new ? 1 : 0)) * LPT;
+    const bool pro = tid < items;                       // whole LPT-lane groups
+    const int phl = tid / LPT, pl2 = tid % LPT, plp2 = pl2 ^ (LPT / 2);
+    float u[CE], up[CE], cs[CE], sn[CE], vn[CE];
+    if (pro) {
+        const float* src = a.qkv + (long)b * qkvr;
+        const float* hsrc = phl < nh ? src + (g * G + h0 + phl) * HD : src + a.Hq * HD + g * HD;
+        load_f32xN(hsrc + pl2 * CE, u, CE);
+        load_f32xN(hsrc + plp2 * CE, up, CE);
+        const float2* tab = a.rope + (long)b * (HD / 2) + (pl2 % (LPT / 2)) * CE;
+#pragma unroll
+        for (int e = 0; e < CE; ++e) { const float2 t = tab[e]; cs[e] = t.x; sn[e] = t.y; }
+        if (phl == nh) load_f32xN(src + (a.Hq + a.Hkv) * HD + g * HD + pl2 * CE, vn, CE);
+    }
+    if (prefill) {   // q already normed and rotated
+        for (int idx = tid; idx < nh * HD; idx += NT) {
+            const int hl = idx / HD, d = idx - hl * HD;
+            qs[hl][d] = a.q_rot[((long)b * a.Hq + g * G + h0 + hl) * HD + d];
+        }
+    }
+
+    // 2. page ids of this split's pages (an entry outside the pool reads as page 0
+    //    and is masked), then every K/V row load issued back to back
+    const int pg0 = t_begin / PG;
+    const int npg = (t_end - 1) / PG - pg0 + 1;
     if (tid < npg) {
         const int pg = bt[pg0 + tid];
         spage[tid] = (pg >= 0 && pg < a.num_pages) ? pg : -1;
@@ -123,67 +153,45 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_kernel(AttnArgs a) {
         }
         const int t = t_begin + i * TPB + wave * TPW + slot;
         const int tt = t < t_end ? t : t_begin;
-        const int pg = spage[tt / a.page - pg0];
+        const int pg = spage[tt / PG - pg0];
         const bool ok = t < t_end && (t != p || prefill) && pg >= 0;
-        const long off = (((long)max(pg, 0) * a.Hkv + g) * a.page + (tt % a.page)) * HD + li * CE;
+        const long off = (((long)max(pg, 0) * a.Hkv + g) * PG + (tt % PG)) * HD + li * CE;
         const uint4 kv = *(const uint4*)((const KVT*)a.k_cache + off);
         const uint4 vv = *(const uint4*)((const KVT*)a.v_cache + off);
         kraw[i] = ok ? kv : make_uint4(0, 0, 0, 0);
         vraw[i] = ok ? vv : make_uint4(0, 0, 0, 0);
     }
-    // wave 0: norm and rotation of this workgroup's query heads and of the new k
-    // (one head-chunk of CE elements per lane, LPT lanes per head; index nh is k)
-    if (prefill) {   // q already normed and rotated
-        for (int idx = tid; idx < nh * HD; idx += NT) {
-            const int hl = idx / HD, d = idx - hl * HD;
-            qs[hl][d] = a.q_rot[((long)b * a.Hq + g * G + h0 + hl) * HD + d];
-        }
-    } else if (wave == 0) {
-        const int qkvr = (a.Hq + 2 * a.Hkv) * HD;
-        const float* src = a.qkv + (long)b * qkvr;
-        const int items = (nh + (has_new ? 1 : 0)) * LPT;
-        for (int base = 0; base < items; base += kWave) {
-            const int idx = base + lane;
-            const bool act = idx < items;
-            const int hl = act ? idx / LPT : 0, l2 = idx % LPT, lp2 = l2 ^ (LPT / 2);
-            const float* hsrc = hl < nh ? src + (g * G + h0 + hl) * HD : src + a.Hq * HD + g * HD;
-            float u[CE], up[CE], cs[CE], sn[CE];
-            load_f32xN(hsrc + l2 * CE, u, CE);
-            load_f32xN(hsrc + lp2 * CE, up, CE);
-            const float2* tab = a.rope + (long)b * (HD / 2) + (l2 % (LPT / 2)) * CE;
+
+    // 3. [per-head q/k RMSNorm] and RoPE of the loaded rows; the new k and v go to
+    //    LDS in stored form and (one workgroup per sequence and KV head) to the cache
+    if (pro) {
+        if (a.qk_norm) {   // per-head RMSNorm: the sum of squares over the head's LPT lanes
+            float ss = 0.f;
 #pragma unroll
-            for (int e = 0; e < CE; ++e) { const float2 t = tab[e]; cs[e] = t.x; sn[e] = t.y; }
-            if (a.qk_norm) {   // per-head RMSNorm: the sum of squares over the head's LPT lanes
-                float ss = 0.f;
+            for (int e = 0; e < CE; ++e) ss += u[e] * u[e];
+            ss = group_sum<LPT>(ss);
+            const float r = 1.0f / sqrtf(ss / (float)HD + a.eps);
+            const void* gain = phl < nh ? a.q_norm : a.k_norm;
 #pragma unroll
-                for (int e = 0; e < CE; ++e) ss += u[e] * u[e];
-                ss = group_sum<LPT>(ss);
-                const float r = 1.0f / sqrtf(ss / (float)HD + a.eps);
-                const void* gain = hl < nh ? a.q_norm : a.k_norm;
-#pragma unroll
-                for (int e = 0; e < CE; ++e) {
-                    u[e] = u[e] * r * load_scalar<WT>(gain, l2 * CE + e);
-                    up[e] = up[e] * r * load_scalar<WT>(gain, lp2 * CE + e);
-                }
+            for (int e = 0; e < CE; ++e) {
+                u[e] = u[e] * r * load_scalar<WT>(gain, pl2 * CE + e);
+                up[e] = up[e] * r * load_scalar<WT>(gain, plp2 * CE + e);
             }
-            rope_lane<CE>(u, up, cs, sn, l2 < LPT / 2);
-            if (!act) continue;
-            if (hl < nh) {
+        }
+        rope_lane<CE>(u, up, cs, sn, pl2 < LPT / 2);
+        if (phl < nh) {
 #pragma unroll
-                for (int e = 0; e < CE; ++e) qs[hl][l2 * CE + e] = u[e];
-            } else {
-                float vn[CE];
-                load_f32xN(src + (a.Hq + a.Hkv) * HD + g * HD + l2 * CE, vn, CE);
-                const uint4 kst = pack16<KVT>(u), vst = pack16<KVT>(vn);
-                knew[l2] = kst;
-                vnew[l2] = vst;
-                if (hg == 0) {   // one workgroup per (sequence, kv head) stores the new row
-                    const int page_id = bt[p / a.page];
-                    if (page_id >= 0 && page_id < a.num_pages) {
-                        const long off = (((long)page_id * a.Hkv + g) * a.page + (p % a.page)) * HD + l2 * CE;
-                        *(uint4*)((KVT*)a.k_cache + off) = kst;
-                        *(uint4*)((KVT*)a.v_cache + off) = vst;
-                    }
+            for (int e = 0; e < CE; ++e) qs[phl][pl2 * CE + e] = u[e];
+        } else {
+            const uint4 kst = pack16<KVT>(u), vst = pack16<KVT>(vn);
+            knew[pl2] = kst;
+            vnew[pl2] = vst;
+            if (hg == 0) {
+                const int page_id = bt[p / PG];
+                if (page_id >= 0 && page_id < a.num_pages) {
+                    const long off = (((long)page_id * a.Hkv + g) * PG + (p % PG)) * HD + pl2 * CE;
+                    *(uint4*)((KVT*)a.k_cache + off) = kst;
+                    *(uint4*)((KVT*)a.v_cache + off) = vst;
                 }
             }
         }
@@ -197,106 +205,181 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_kernel(AttnArgs a) {
             if (t == p) { kraw[i] = knew[li]; vraw[i] = vnew[li]; }
         }
     }
-    // scores s = q . k / sqrt(hd): heads in a rolled loop (q from LDS), the
-    // token passes unrolled so the K rows stay in registers
+
+    // scores in base-2 units, s * log2(e), so that e^(s - m) = 2^(s' - m') comes from
+    // the hardware exp2 (v_exp_f32, about 1 ulp); the partials for the merge keep
+    // m in the same units
+    const float scale2 = a.scale * kLog2e;
+    const int hq0 = g * G + h0;   // first query head of this workgroup
+
+    if constexpr (NP <= kAttnPassesGrouped) {
+        // Grouped heads: scores to LDS, one wave per head takes the split's max, exp
+        // and sum (each exponential once), then o = sum p v per head.
+        __shared__ float sc[kMaxGroup][MAXT];
+        __shared__ float mls[kMaxGroup][2];
+        for (int hl = 0; hl < nh; ++hl) {
+            float qv[CE];
+#pragma unroll
+            for (int e = 0; e < CE; ++e) qv[e] = qs[hl][li * CE + e];
+#pragma unroll
+            for (int i = 0; i < NP; ++i) {
+                if (i * TPB >= n) continue;
+                const int j = i * TPB + wave * TPW + slot;
+                float kf[CE];
+                widen16(kraw[i], kf);
+                float d = 0.f;
+#pragma unroll
+                for (int e = 0; e < CE; ++e) d = fmaf(qv[e], kf[e], d);
+                d = group_sum<LPT>(d);
+                if (li == 0 && j < n) sc[hl][j] = d * scale2;
+            }
+        }
+        __syncthreads();
+        for (int hl = wave; hl < nh; hl += NWV) {
+            float m = -INFINITY;
+            for (int j = lane; j < n; j += kWave) m = fmaxf(m, sc[hl][j]);
+            m = group_max<kWave>(m);
+            float l = 0.f;
+            for (int j = lane; j < n; j += kWave) {
+                const float e = exp2_hw(sc[hl][j] - m);
+                sc[hl][j] = e;
+                l += e;
+            }
+            l = group_sum<kWave>(l);
+            if (lane == 0) { mls[hl][0] = m; mls[hl][1] = l; }
+        }
+        __syncthreads();
+        for (int hl = 0; hl < nh; ++hl) {
+            float pr[NP], o[CE];
+#pragma unroll
+            for (int i = 0; i < NP; ++i) {   // the lane's probabilities up front (masked)
+                const int j = i * TPB + wave * TPW + slot;
+                const float v = sc[hl][j < n ? j : 0];
+                pr[i] = j < n ? v : 0.f;
+            }
+#pragma unroll
+            for (int e = 0; e < CE; ++e) o[e] = 0.f;
+#pragma unroll
+            for (int i = 0; i < NP; ++i) {
+                if (i * TPB >= n) continue;
+                float vf[CE];
+                widen16(vraw[i], vf);
+#pragma unroll
+                for (int e = 0; e < CE; ++e) o[e] = fmaf(pr[i], vf[e], o[e]);
+            }
+#pragma unroll
+            for (int e = 0; e < CE; ++e) {
+                const float v = strided_sum<LPT>(o[e]);
+                if (slot == 0) red[wave][hl][li * CE + e] = v;
+            }
+        }
+        __syncthreads();
+        for (int idx = tid; idx < nh * HD; idx += NT) {
+            const int hl = idx / HD, d = idx - hl * HD;
+            float v = 0.f;
+#pragma unroll
+            for (int w = 0; w < NWV; ++w) v += red[w][hl][d];
+            if (ns == 1) {
+                a.ctx[((long)b * a.Hq + hq0) * HD + idx] = v / mls[hl][1];
+            } else {   // publish (o, m, l) for the merge kernel; layout [B][Hq][S][hd + 2]
+                float* pp = a.part + (((long)b * a.Hq + hq0 + hl) * a.S + s) * (HD + 2);
+                pp[d] = v;
+                if (d == 0) { pp[HD] = mls[hl][0]; pp[HD + 1] = mls[hl][1]; }
+            }
+        }
+        return;
+    }
+
+    // 4. (one head per workgroup, many passes) per head, each wave over its own
+    //    tokens: scores s = q.k/sqrt(hd) kept in
+    //    registers, m = max s, p = exp(s - m), l = sum p, o = sum p v (the online
+    //    softmax of Tang page, section 2.2, with the waves as its blocks)
     for (int hl = 0; hl < nh; ++hl) {
         float qv[CE];
 #pragma unroll
         for (int e = 0; e < CE; ++e) qv[e] = qs[hl][li * CE + e];
+        float sv[NP];
+        float mw = -INFINITY;
 #pragma unroll
         for (int i = 0; i < NP; ++i) {
-            if (i * TPB >= n) break;
-            const int t = t_begin + i * TPB + wave * TPW + slot;
+            sv[i] = -INFINITY;
+            if (i * TPB >= n) continue;   // uniform; the loop itself is fully unrolled
             float kf[CE];
             widen16(kraw[i], kf);
             float d = 0.f;
 #pragma unroll
             for (int e = 0; e < CE; ++e) d = fmaf(qv[e], kf[e], d);
             d = group_sum<LPT>(d);
-            if (li == 0 && t < t_end) sc[hl][t - t_begin] = d * a.scale;
+            const int j = i * TPB + wave * TPW + slot;
+            sv[i] = j < n ? d * scale2 : -INFINITY;
+            mw = fmaxf(mw, sv[i]);
         }
-    }
-    __syncthreads();
-    // per head: m = max s, p = exp(s - m), l = sum p
-    for (int hl = wave; hl < nh; hl += NWV) {
-        float m = -INFINITY;
-        for (int j = lane; j < n; j += kWave) m = fmaxf(m, sc[hl][j]);
-        m = group_max<kWave>(m);
-        float l = 0.f;
-        for (int j = lane; j < n; j += kWave) {
-            const float e = expf(sc[hl][j] - m);
-            sc[hl][j] = e;
-            l += e;
-        }
-        l = group_sum<kWave>(l);
-        if (lane == 0) { mls[hl][0] = m; mls[hl][1] = l; }
-    }
-    __syncthreads();
-    // o = sum_t p_t v_t, one head at a time
-    for (int hl = 0; hl < nh; ++hl) {
-        float o[CE];
+        mw = wave_max(mw);
+        float lw = 0.f, o[CE];
 #pragma unroll
         for (int e = 0; e < CE; ++e) o[e] = 0.f;
-        // the lane's probabilities, read up front (masked, no branch) when the pass
-        // count is small; the wide variant reads them pass by pass to save registers
-        constexpr bool PRE = NP <= kAttnPassesGrouped;
-        float pr[PRE ? NP : 1];
-        if (PRE) {
 #pragma unroll
-            for (int i = 0; i < NP; ++i) {
-                const int j = i * TPB + wave * TPW + slot;
-                const float v = sc[hl][j < n ? j : 0];
-                pr[PRE ? i : 0] = j < n ? v : 0.f;
+        for (int i = 0; i < NP; ++i) {   // fixed trip count (no early exit): the K/V
+            if (i * TPB < n) {           // rows stay in registers, fully unrolled
+                const float pr = sv[i] == -INFINITY ? 0.f : exp2_hw(sv[i] - mw);
+                lw += pr;
+                float vf[CE];
+                widen16(vraw[i], vf);
+#pragma unroll
+                for (int e = 0; e < CE; ++e) o[e] = fmaf(pr, vf[e], o[e]);
             }
         }
-#pragma unroll
-        for (int i = 0; i < NP; ++i) {
-            if (i * TPB >= n) break;
-            if (!PRE) {
-                const int j = i * TPB + wave * TPW + slot;
-                pr[0] = j < n ? sc[hl][j] : 0.f;
-            }
-            float vf[CE];
-            widen16(vraw[i], vf);
-#pragma unroll
-            for (int e = 0; e < CE; ++e) o[e] = fmaf(pr[PRE ? i : 0], vf[e], o[e]);
-        }
+        lw = strided_sum<LPT>(lw);
 #pragma unroll
         for (int e = 0; e < CE; ++e) {
             const float v = strided_sum<LPT>(o[e]);
             if (slot == 0) red[wave][hl][li * CE + e] = v;
         }
+        if (lane == 0) wml[wave][hl] = make_float2(mw, lw);
     }
     __syncthreads();
-    const int hq0 = g * G + h0;   // first query head of this workgroup
-    if (ns == 1) {
-        float* ctx = a.ctx + ((long)b * a.Hq + hq0) * HD;
-        for (int idx = tid; idx < nh * HD; idx += NT) {
-            const int hl = idx / HD, d = idx - hl * HD;
-            float v = 0.f;
-#pragma unroll
-            for (int w = 0; w < NWV; ++w) v += red[w][hl][d];
-            ctx[idx] = v / mls[hl][1];
-        }
-        return;
-    }
-    // several splits: publish (o, m, l) for the merge kernel; layout [B][Hq][S][hd + 2]
+
+    // 5. the waves' (m, l, o) combined: M = max m_w, weights e^(m_w - M) (a wave
+    //    without a valid token has m_w = -inf and weight 0)
     for (int idx = tid; idx < nh * HD; idx += NT) {
         const int hl = idx / HD, d = idx - hl * HD;
-        float v = 0.f;
+        float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < NWV; ++w) v += red[w][hl][d];
-        a.part[(((long)b * a.Hq + hq0 + hl) * a.S + s) * (HD + 2) + d] = v;
-    }
-    if (tid < nh) {
-        float* pm = a.part + (((long)b * a.Hq + hq0 + tid) * a.S + s) * (HD + 2) + HD;
-        pm[0] = mls[tid][0];
-        pm[1] = mls[tid][1];
+        for (int w = 0; w < NWV; ++w) M = fmaxf(M, wml[w][hl].x);
+        float L = 0.f, O = 0.f;
+#pragma unroll
+        for (int w = 0; w < NWV; ++w) {
+            const float e = wml[w][hl].x == -INFINITY ? 0.f : exp2_hw(wml[w][hl].x - M);
+            L = fmaf(wml[w][hl].y, e, L);
+            O = fmaf(red[w][hl][d], e, O);
+        }
+        if (ns == 1) {
+            a.ctx[((long)b * a.Hq + hq0) * HD + idx] = O / L;
+        } else {   // several splits: publish (o, m, l) for the merge kernel; layout [B][Hq][S][hd + 2]
+            float* pp = a.part + (((long)b * a.Hq + hq0 + hl) * a.S + s) * (HD + 2);
+            pp[d] = O;
+            if (d == 0) { pp[HD] = M; pp[HD + 1] = L; }
+        }
     }
 }
 
+// Two launch shapes of the same body: the grouped one (few passes) keeps its
+// registers low enough for two workgroups per CU; the wide one (9 passes of K/V
+// rows in registers) may use up to 256 VGPRs, one workgroup per CU, rather than
+// spill.
+template <typename WT, typename KVT, int HD, int NP>
+__global__ __launch_bounds__(kAttnWaves * kWave) void attn_kernel(AttnArgs a) {
+    attn_body<WT, KVT, HD, NP>(a);
+}
+template <typename WT, typename KVT, int HD, int NP>
+__global__ __launch_bounds__(kAttnWaves * kWave) __attribute__((amdgpu_waves_per_eu(1, 2)))
+void attn_wide_kernel(AttnArgs a) {
+    attn_body<WT, KVT, HD, NP>(a);
+}
+
 // Merge of the split partials of one (query head, sequence): M = max_s m_s,
-// ctx = sum_s o_s e^(m_s - M) / sum_s l_s e^(m_s - M). The 256 threads form
+// ctx = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M) (the attention kernel keeps
+// m in base-2 units, so this is the e^(m_s - M) weighting). The 256 threads form
 // 256/hd groups that take every (256/hd)-th split, each with 16 partial loads
 // in flight; the groups' sums meet in LDS in a fixed order.
 constexpr int kMergeThreads = 256;
@@ -315,7 +398,7 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
         const float mj = tid < ns ? base[tid * stride + hd] : -INFINITY;
         const float lj = tid < ns ? base[tid * stride + hd + 1] : 0.f;
         const float m = group_max<kWave>(mj);
-        const float w = tid < ns ? expf(mj - m) : 0.f;
+        const float w = tid < ns ? exp2_hw(mj - m) : 0.f;   // m in base-2 units
         if (tid < ns) wgt[tid] = w;
         const float l = group_sum<kWave>(lj * w);
         if (tid == 0) lsum = l;
@@ -346,6 +429,7 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
 }
 
 hipError_t launch_attention(const AttnArgs& a, int w_is_bf16, int kv_is_bf16, hipStream_t s) {
+    if (a.page != kAttnPage) return hipErrorInvalidValue;
     const int G = a.Hq / a.Hkv;
     const int hgroups = (G + a.hpw - 1) / a.hpw;
     dim3 grid(a.S, a.Hkv * hgroups, a.B);
@@ -355,7 +439,7 @@ hipError_t launch_attention(const AttnArgs& a, int w_is_bf16, int kv_is_bf16, hi
         if (a.chunk <= attn_chunk<HD, KVT, kAttnPassesGrouped>())                                     \
             hipLaunchKernelGGL((attn_kernel<WT, KVT, HD, kAttnPassesGrouped>), grid, block, 0, s, a); \
         else                                                                                          \
-            hipLaunchKernelGGL((attn_kernel<WT, KVT, HD, kAttnPassesWide>), grid, block, 0, s, a);    \
+            hipLaunchKernelGGL((attn_wide_kernel<WT, KVT, HD, kAttnPassesWide>), grid, block, 0, s, a); \
     } while (0)
     if (a.hd == 64) {
         if (w_is_bf16) { if (kv_is_bf16) QD_ATTN(uint16_t, uint16_t, 64); else QD_ATTN(uint16_t, float, 64); }

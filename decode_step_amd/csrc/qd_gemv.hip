@@ -21,6 +21,8 @@
 
 namespace qd {
 
+constexpr int kCus = 256;
+
 template <typename WT, int LPR, int WK, int UR, int CPL, int EPI>
 __global__ __launch_bounds__(256) void gemv1_kernel(GemvArgs a) {
     constexpr int CE = VecN<WT>::n;
@@ -187,9 +189,17 @@ __global__ __launch_bounds__(256) void gemv1_kernel(GemvArgs a) {
     }
 }
 
-// (LPR, WK, UR, CPL) shapes compiled; every one handles any K and N.
+// (LPR, WK, UR, CPL) shapes compiled; every one handles any K and N. RPT rows per
+// workgroup tile = (4 / WK) * (64 / LPR) * UR; one pass over K covers
+// CPL * LPR * WK * 8 columns (more take further passes, each a memory round trip).
+struct Gemv1Shape { int lpr, wk, ur, cpl; };
 enum Gemv1Cfg { G_SMALLK_FEWROWS = 0, G_SMALLK = 1, G_SMALLK_UR2 = 2, G_BIGK_FEWROWS = 3, G_BIGK = 4,
-                G_BIGK_UR2 = 5 };
+                G_BIGK_UR2 = 5, G_SMALLK_8 = 6, G_LONGK_4 = 7, G_NCFG = 8 };
+constexpr Gemv1Shape kGemv1Shapes[G_NCFG] = {
+    {16, 4, 1, 2}, {16, 1, 1, 8}, {16, 1, 2, 8}, {32, 4, 1, 6}, {64, 1, 1, 8}, {64, 1, 2, 8}, {16, 2, 1, 4},
+    {16, 4, 1, 10}};
+constexpr int gemv1_rpt(int c) { return (4 / kGemv1Shapes[c].wk) * (64 / kGemv1Shapes[c].lpr) * kGemv1Shapes[c].ur; }
+constexpr int gemv1_kpass(int c) { return kGemv1Shapes[c].cpl * kGemv1Shapes[c].lpr * kGemv1Shapes[c].wk * 8; }
 
 template <typename WT, int EPI>
 static hipError_t gemv1_dispatch(const GemvArgs& a, int cfg, int* grid_out, int grid_cap, hipStream_t s) {
@@ -201,33 +211,45 @@ static hipError_t gemv1_dispatch(const GemvArgs& a, int cfg, int* grid_out, int 
         hipLaunchKernelGGL(kern, dim3(grid), dim3(256), shm, s, a);
         return hipGetLastError();
     };
+#define QD_G1C(C) \
+    case C: return go(gemv1_kernel<WT, kGemv1Shapes[C].lpr, kGemv1Shapes[C].wk, kGemv1Shapes[C].ur, kGemv1Shapes[C].cpl, EPI>, gemv1_rpt(C));
     switch (cfg) {
-        case G_SMALLK_FEWROWS: return go(gemv1_kernel<WT, 16, 4, 1, 2, EPI>, 1 * 4 * 1);
-        case G_SMALLK: return go(gemv1_kernel<WT, 16, 1, 1, 8, EPI>, 4 * 4 * 1);
-        case G_SMALLK_UR2: return go(gemv1_kernel<WT, 16, 1, 2, 8, EPI>, 4 * 4 * 2);
-        case G_BIGK_FEWROWS: return go(gemv1_kernel<WT, 32, 4, 1, 6, EPI>, 1 * 2 * 1);
-        case G_BIGK: return go(gemv1_kernel<WT, 64, 1, 1, 8, EPI>, 4 * 1 * 1);
-        default: return go(gemv1_kernel<WT, 64, 1, 2, 8, EPI>, 4 * 1 * 2);
+        QD_G1C(G_SMALLK_FEWROWS) QD_G1C(G_SMALLK) QD_G1C(G_SMALLK_UR2) QD_G1C(G_BIGK_FEWROWS) QD_G1C(G_BIGK)
+        QD_G1C(G_SMALLK_8) QD_G1C(G_LONGK_4)
+        default: return go(gemv1_kernel<WT, 64, 1, 2, 8, EPI>, gemv1_rpt(G_BIGK_UR2));
     }
+#undef QD_G1C
 }
 
-// Shape heuristic: the largest row tile that still gives at least 256
-// workgroups (one per CU), so a matrix is spread over the whole chip; the
-// lm_head (grid-strided over many tiles) keeps the largest tile.
+// Shape choice. A batch-1 projection is about one memory round trip plus the
+// transfer, so a second partial round of workgroups on the 256 CUs nearly
+// doubles it: among the shapes that cover K in one pass, take the smallest
+// row tile whose tiles fit one round (spreading the matrix over as many CUs as
+// possible); a matrix too tall for that takes the largest such tile and a
+// capped, grid-strided grid; a K no shape covers in one pass keeps the old
+// rule (largest tile with at least 256 workgroups). The lm_head keeps its
+// grid-strided wide tile.
 static int gemv1_pick(int N, int K, int epi) {
     const bool small_k = K <= 2048;
     if (epi == EPI_LOGITS) return small_k ? G_SMALLK_UR2 : G_BIGK_UR2;
-    const int cfgs_small[3] = {G_SMALLK_UR2, G_SMALLK, G_SMALLK_FEWROWS};
-    const int rpt_small[3] = {32, 16, 4};
-    const int cfgs_big[3] = {G_BIGK_UR2, G_BIGK, G_BIGK_FEWROWS};
-    const int rpt_big[3] = {8, 4, 2};
-    const int* cfgs = small_k ? cfgs_small : cfgs_big;
-    const int* rpt = small_k ? rpt_small : rpt_big;
-    for (int i = 0; i < 3; ++i) {
-        if (epi == EPI_SWIGLU && cfgs[i] == G_SMALLK_UR2) continue;
-        if ((N + rpt[i] - 1) / rpt[i] >= 256) return cfgs[i];
+    int best = -1, widest = -1;
+    for (int c = 0; c < G_NCFG; ++c) {
+        if (gemv1_kpass(c) < K) continue;
+        const int tiles = (N + gemv1_rpt(c) - 1) / gemv1_rpt(c);
+        // ties on the row tile go to the shape with the least idle lanes (smallest pass)
+        if (tiles <= kCus && (best < 0 || gemv1_rpt(c) < gemv1_rpt(best) ||
+                              (gemv1_rpt(c) == gemv1_rpt(best) && gemv1_kpass(c) < gemv1_kpass(best))))
+            best = c;
+        if (widest < 0 || gemv1_rpt(c) > gemv1_rpt(widest) ||
+            (gemv1_rpt(c) == gemv1_rpt(widest) && gemv1_kpass(c) < gemv1_kpass(widest)))
+            widest = c;
     }
-    return cfgs[2];
+    if (best >= 0) return best;
+    if (widest >= 0) return widest;
+    const int cfgs_big[3] = {G_BIGK_UR2, G_BIGK, G_BIGK_FEWROWS};
+    for (int i = 0; i < 3; ++i)
+        if ((N + gemv1_rpt(cfgs_big[i]) - 1) / gemv1_rpt(cfgs_big[i]) >= kCus) return cfgs_big[i];
+    return G_BIGK_FEWROWS;
 }
 
 hipError_t launch_gemv1(const GemvArgs& a, int w_is_bf16, int epi, int grid_cap, int* grid_out, hipStream_t s) {
