@@ -172,6 +172,60 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
     }
 }
 
+// A kernel-argument pointer pinned to scalar registers, as a global-memory
+// (address space 1) byte pointer. Choosing among several such pointers with a
+// per-lane condition could otherwise be compiled as a per-lane load from the
+// argument block (a memory round trip the weight loads behind it would wait
+// for); pinned values are chosen with plain selects, and the explicit address
+// space keeps the loads through them global loads rather than flat ones.
+typedef __attribute__((address_space(1))) const char gbyte;
+__device__ __forceinline__ gbyte* sgpr_gptr(const void* p) {
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (gbyte*)(((uint64_t)hi << 32) | lo);
+}
+typedef unsigned int qd_u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 gld16(gbyte* p) {
+    const qd_u32x4 v = *(const __attribute__((address_space(1))) qd_u32x4*)p;
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+template <typename T> __device__ __forceinline__ float gld_scalar(gbyte* p, long i) {
+    if constexpr (sizeof(T) == 2) return bf16_to_f32(*(const __attribute__((address_space(1))) uint16_t*)(p + 2 * i));
+    else return *(const __attribute__((address_space(1))) float*)(p + 4 * i);
+}
+
+// LDS address (offset within the workgroup's LDS) of a __shared__ object.
+typedef __attribute__((address_space(3))) void qd_lds_void;
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const qd_lds_void*)p;
+}
+
+// One wave-wide LDS DMA of 16 bytes per lane: lane i's global source lands at
+// lds + 16 i. Issued as inline asm so the compiler does not see an LDS write it
+// would have to order against later LDS reads (left to itself it waits for every
+// outstanding load before the next LDS access). Completion is the caller's
+// business (s_waitcnt vmcnt); the compiler's own vmcnt waits stay correct, as
+// extra outstanding loads only make a wait stricter.
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "memory", "m0");
+}
+
+// s_waitcnt immediates (vmcnt in bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8])
+constexpr int wait_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x70 | 0xF00; }
+constexpr int kWaitLgkm0 = 0xF | (0x3 << 14) | 0x70;
+
+// Workgroup barrier for LDS traffic: this wave's LDS accesses complete, then
+// s_barrier; compiler-only fences keep LDS accesses on their side. Unlike
+// __syncthreads it does not wait for outstanding global loads, so prefetched
+// weights stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // v -> (hi, lo) with hi = bf16(v) and lo = bf16(v - hi), both round-to-nearest-even
 // through v_cvt_pk_bf16_f32; a pair's first element sits in the low half-word.
 __device__ __forceinline__ void split_hi_lo(const float (&v)[8], uint4& hi, uint4& lo) {

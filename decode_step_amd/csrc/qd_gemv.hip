@@ -1,27 +1,37 @@
 // Single-row (batch 1) GEMV for gfx950, tuned for latency.
 //
 // A decode-step projection is an HBM stream of a row-major [N][K] weight
-// matrix against one activation vector; at 0.5B shapes a whole matrix is only
-// one or two memory latencies' worth of data, so each lane issues every weight
-// load it will need before it touches the activation, and the activation is
-// staged into LDS in a single pass.
+// matrix against one activation vector. Each lane issues every weight load of
+// its tile before anything else; the activation (and the RMSNorm gain) go to
+// LDS by DMA behind them, so a workgroup waits for memory once per tile.
 //
 // RMSNorm is folded into the product (Tang page, section 2.3, epilogues on the
 // reducing thread): W (x * r * g) = r * (W (x * g)) with r = 1/sqrt(sum(x^2)/K + eps)
 // (nanocompile page, phase 1: the mean square is a sum then a divide; eps
-// inside the root), so the staging pass stores x * g and accumulates sum(x^2)
-// at the same time, and r scales the finished dot product.
+// inside the root); one pass over the staged x forms x * g and sum(x^2), and r
+// scales the finished dot product.
 //
 // Layout of one workgroup (256 threads = 4 waves): LPR lanes share a row and
 // read 16-byte chunks lane-interleaved (each wave load covers 64/LPR rows of
 // LPR*16 contiguous bytes); WK waves split K and meet in LDS; UR row groups
 // per lane; CPL chunks per lane per row per pass.
+//
+// No load sits under a per-lane condition: a lane whose chunk lies past its K
+// range (or whose row lies past N) loads a valid chunk of a valid row and
+// multiplies it by a block of zeros kept in LDS behind x. (A masked load would
+// be turned into a branch, and the compiler then waits for every outstanding
+// load where the branches join.)
 #include "qd_device.h"
 #include "qd_launch.h"
 
 namespace qd {
 
 constexpr int kCus = 256;
+
+// floats of x staged in LDS: K rounded up to whole 1 KB DMA blocks
+__host__ __device__ constexpr int gemv1_xpad(int K) { return (K + 255) & ~255; }
+// bytes of gain staged in LDS (whole 1 KB blocks)
+__host__ __device__ constexpr int gemv1_gpad(int K, int wbytes) { return (K * wbytes + 1023) & ~1023; }
 
 template <typename WT, int LPR, int WK, int UR, int CPL, int EPI>
 __global__ __launch_bounds__(256) void gemv1_kernel(GemvArgs a) {
@@ -30,7 +40,7 @@ __global__ __launch_bounds__(256) void gemv1_kernel(GemvArgs a) {
     constexpr int WR = 4 / WK;
     constexpr int RPT = WR * RPW * UR;
     constexpr int NW = (EPI == EPI_SWIGLU) ? 2 : 1;
-    extern __shared__ float xs[];
+    extern __shared__ __align__(16) float xs[];   // x (then x * g) [xpad] | zeros [8] | gain [gpad bytes]
     __shared__ float wsum[4];
     __shared__ float red[WK][RPT][NW];
     __shared__ float red_v[4];
@@ -41,58 +51,99 @@ __global__ __launch_bounds__(256) void gemv1_kernel(GemvArgs a) {
     const int li = lane % LPR, slot = lane / LPR;
     const int K = a.K, N = a.N, KC = K / CE;
     const int kcw = (KC + WK - 1) / WK;
-    const int kc0 = wk * kcw, kc1 = min(KC, kc0 + kcw);
+    const int kc0 = min(KC, wk * kcw), kc1 = min(KC, kc0 + kcw);
     const int ntiles = (N + RPT - 1) / RPT;
+    const int xpad = gemv1_xpad(K);
+    const int cz = xpad / CE;                 // chunk index of the zero block
+    float* gs = xs + xpad + 8;
 
-    auto wptr = [&](int r, int n) -> const WT* {
-        if (EPI == EPI_SWIGLU) return (const WT*)a.w[n] + (long)r * K;
+    gbyte* wseg[3] = {sgpr_gptr(a.w[0]), sgpr_gptr(a.w[1]), sgpr_gptr(a.w[2])};
+    gbyte* bseg[3] = {sgpr_gptr(a.bias[0]), sgpr_gptr(a.bias[1]), sgpr_gptr(a.bias[2])};
+    auto wptr = [&](int r, int n) -> gbyte* {   // r < N
+        if (EPI == EPI_SWIGLU) return wseg[n] + (long)r * K * (long)sizeof(WT);
         const bool s0 = r < a.seg_end[0], s1 = r < a.seg_end[1];
-        const void* w = s0 ? a.w[0] : (s1 ? a.w[1] : a.w[2]);
+        gbyte* w = s0 ? wseg[0] : (s1 ? wseg[1] : wseg[2]);
         const int base = s0 ? 0 : (s1 ? a.seg_end[0] : a.seg_end[1]);
-        return (const WT*)w + (long)(r - base) * K;
+        return w + (long)(r - base) * K * (long)sizeof(WT);
     };
     uint4 wv[UR][NW][CPL];
-    auto issue = [&](int tile, int cbase) {
+    float pre[UR] = {};   // RESID: the residual row; STORE: the bias, times psc (0 without one)
+    float psc[UR] = {};
+    auto issue = [&](int tile, int cbase, bool first) {
 #pragma unroll
         for (int u = 0; u < UR; ++u) {
             const int r = tile * RPT + (wr * UR + u) * RPW + slot;
+            const int rr = r < N ? r : N - 1;
 #pragma unroll
             for (int n = 0; n < NW; ++n) {
-                const WT* wp = r < N ? wptr(r, n) : nullptr;
+                gbyte* wp = wptr(rr, n);
 #pragma unroll
                 for (int j = 0; j < CPL; ++j) {
                     const int c = cbase + li + j * LPR;
-                    wv[u][n][j] = (wp && c < kc1) ? *(const uint4*)(wp + c * CE) : make_uint4(0, 0, 0, 0);
+                    wv[u][n][j] = gld16(wp + (long)(c < kc1 ? c : 0) * 16);
                 }
+            }
+            if (first && EPI == EPI_RESID) { pre[u] = a.y[rr]; psc[u] = 1.f; }
+            if (first && EPI == EPI_STORE) {
+                const bool s0 = rr < a.seg_end[0], s1 = rr < a.seg_end[1];
+                gbyte* bsel = s0 ? bseg[0] : (s1 ? bseg[1] : bseg[2]);
+                const int base = s0 ? 0 : (s1 ? a.seg_end[0] : a.seg_end[1]);
+                // without a bias: load a valid weight and scale it by 0 (the scale is
+                // applied in the epilogue, so nothing waits for this load before then)
+                pre[u] = gld_scalar<WT>(bsel ? bsel : wseg[0], bsel ? rr - base : 0);
+                psc[u] = bsel ? 1.f : 0.f;
             }
         }
     };
     int tile = blockIdx.x;
-    if (tile < ntiles) issue(tile, kc0);
+    issue(tile < ntiles ? tile : ntiles - 1, kc0, true);   // unconditional: no join for the loads to wait at
 
+    // x and the gain into LDS by DMA, behind the weights (source indices clamped to
+    // the vectors; what lands past K is never read)
+    {
+        const uint32_t xl = lds_addr(xs);
+        for (int j = wave; j < xpad / 256; j += 4) {
+            const int f = min(j * 256 + lane * 4, K - 4);
+            lds_dma16(a.x + f, __builtin_amdgcn_readfirstlane(xl + j * 1024));
+        }
+        if (a.gain) {
+            constexpr int GE = 16 / (int)sizeof(WT);      // gain elements per lane
+            const uint32_t gl = lds_addr(gs);
+            for (int j = wave; j < gemv1_gpad(K, sizeof(WT)) / 1024; j += 4) {
+                const int e = min(j * 64 * GE + lane * GE, K - GE);
+                lds_dma16((const WT*)a.gain + e, __builtin_amdgcn_readfirstlane(gl + j * 1024));
+            }
+        }
+    }
     // counters a later kernel of the step starts from zero
     if (a.zero_ptr && blockIdx.x == 0)
         for (int i = tid; i < a.zero_n; i += 256) a.zero_ptr[i] = 0u;
+    __builtin_amdgcn_s_waitcnt(wait_vm(0));   // this wave's weights and DMA landed
+    lds_barrier();                            // ... and every wave's DMA
 
-    // stage x * g (or x) and sum(x^2)
+    // x * g and sum(x^2) in place; the zero block behind x
     float ss = 0.f;
-    for (int k4 = tid; k4 < K / 4; k4 += 256) {
-        float4 v = ((const float4*)a.x)[k4];
-        if (a.gain) {
-            ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-            const int k = 4 * k4;
-            v.x *= load_scalar<WT>(a.gain, k);
-            v.y *= load_scalar<WT>(a.gain, k + 1);
-            v.z *= load_scalar<WT>(a.gain, k + 2);
-            v.w *= load_scalar<WT>(a.gain, k + 3);
-        }
-        ((float4*)xs)[k4] = v;
-    }
     if (a.gain) {
+        for (int k4 = tid; k4 < K / 4; k4 += 256) {
+            float4 v = ((const float4*)xs)[k4];
+            float g[4];
+            if (sizeof(WT) == 2) {
+                const uint2 gb = ((const uint2*)gs)[k4];
+                g[0] = __uint_as_float(gb.x << 16); g[1] = __uint_as_float(gb.x & 0xffff0000u);
+                g[2] = __uint_as_float(gb.y << 16); g[3] = __uint_as_float(gb.y & 0xffff0000u);
+            } else {
+                const float4 gf = ((const float4*)gs)[k4];
+                g[0] = gf.x; g[1] = gf.y; g[2] = gf.z; g[3] = gf.w;
+            }
+            ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+            v.x *= g[0]; v.y *= g[1]; v.z *= g[2]; v.w *= g[3];
+            ((float4*)xs)[k4] = v;
+        }
         ss = group_sum<kWave>(ss);
         if (lane == 0) wsum[wave] = ss;
     }
-    __syncthreads();
+    if (tid < 8) xs[xpad + tid] = 0.f;
+    lds_barrier();
     const float rscale = a.gain ? 1.0f / sqrtf((wsum[0] + wsum[1] + wsum[2] + wsum[3]) / (float)K + a.eps) : 1.0f;
 
     float best_v = -INFINITY;
@@ -104,15 +155,15 @@ __global__ __launch_bounds__(256) void gemv1_kernel(GemvArgs a) {
 #pragma unroll
             for (int n = 0; n < NW; ++n) acc[u][n] = 0.f;
         for (int cbase = kc0; cbase < kc1; cbase += CPL * LPR) {
-            if (cbase != kc0) issue(tile, cbase);
+            if (cbase != kc0) issue(tile, cbase, false);
 #pragma unroll
             for (int j = 0; j < CPL; ++j) {
                 const int c = cbase + li + j * LPR;
-                if (c >= kc1) break;
+                const float* xp = xs + (c < kc1 ? c : cz) * CE;
                 float xv[CE];
 #pragma unroll
                 for (int q = 0; q < CE / 4; ++q) {
-                    const float4 t = ((const float4*)(xs + c * CE))[q];
+                    const float4 t = ((const float4*)xp)[q];
                     xv[4 * q] = t.x; xv[4 * q + 1] = t.y; xv[4 * q + 2] = t.z; xv[4 * q + 3] = t.w;
                 }
 #pragma unroll
@@ -126,8 +177,12 @@ __global__ __launch_bounds__(256) void gemv1_kernel(GemvArgs a) {
                     }
             }
         }
+        float cur[UR], csc[UR];
+#pragma unroll
+        for (int u = 0; u < UR; ++u) { cur[u] = pre[u]; csc[u] = psc[u]; }
+        const int this_tile = tile;
         const int next = tile + gridDim.x;
-        if (next < ntiles) issue(next, kc0);
+        if (next < ntiles) issue(next, kc0, true);
 #pragma unroll
         for (int u = 0; u < UR; ++u)
 #pragma unroll
@@ -139,40 +194,29 @@ __global__ __launch_bounds__(256) void gemv1_kernel(GemvArgs a) {
 #pragma unroll
                     for (int n = 0; n < NW; ++n) red[wk][(wr * UR + u) * RPW + slot][n] = acc[u][n];
             }
-            __syncthreads();
-            if (wk == 0 && li == 0) {
+            lds_barrier();
 #pragma unroll
-                for (int u = 0; u < UR; ++u)
+            for (int u = 0; u < UR; ++u)
 #pragma unroll
-                    for (int n = 0; n < NW; ++n) {
-                        float v = 0.f;
+                for (int n = 0; n < NW; ++n) {
+                    float v = 0.f;
 #pragma unroll
-                        for (int q = 0; q < WK; ++q) v += red[q][(wr * UR + u) * RPW + slot][n];
-                        acc[u][n] = v;
-                    }
-            }
-            __syncthreads();
-        }
-        if (wk == 0 && li == 0) {
-#pragma unroll
-            for (int u = 0; u < UR; ++u) {
-                const int r = tile * RPT + (wr * UR + u) * RPW + slot;
-                if (r >= N) continue;
-                float* yp = a.y + r;
-                const float v0 = acc[u][0] * rscale;
-                if (EPI == EPI_STORE) {
-                    const bool s0 = r < a.seg_end[0], s1 = r < a.seg_end[1];
-                    const void* bsel = s0 ? a.bias[0] : (s1 ? a.bias[1] : a.bias[2]);
-                    const int base = s0 ? 0 : (s1 ? a.seg_end[0] : a.seg_end[1]);
-                    *yp = bsel ? v0 + load_scalar<WT>(bsel, r - base) : v0;
-                } else if (EPI == EPI_RESID) {
-                    *yp = *yp + v0;
-                } else if (EPI == EPI_SWIGLU) {
-                    *yp = silu(v0) * (acc[u][NW - 1] * rscale);
-                } else {
-                    *yp = v0;
-                    if (better(v0, r, best_v, best_i)) { best_v = v0; best_i = r; }
+                    for (int q = 0; q < WK; ++q) v += red[q][(wr * UR + u) * RPW + slot][n];
+                    acc[u][n] = v;
                 }
+            lds_barrier();   // red is rewritten by the next tile
+        }
+#pragma unroll
+        for (int u = 0; u < UR; ++u) {
+            const int r = this_tile * RPT + (wr * UR + u) * RPW + slot;
+            const float v0 = acc[u][0] * rscale;
+            float out;
+            if (EPI == EPI_STORE || EPI == EPI_RESID) out = fmaf(cur[u], csc[u], v0);
+            else if (EPI == EPI_SWIGLU) out = silu(v0) * (acc[u][NW - 1] * rscale);
+            else out = v0;
+            if (wk == 0 && li == 0 && r < N) {
+                a.y[r] = out;
+                if (EPI == EPI_LOGITS && better(v0, r, best_v, best_i)) { best_v = v0; best_i = r; }
             }
         }
     }
@@ -203,8 +247,10 @@ constexpr int gemv1_kpass(int c) { return kGemv1Shapes[c].cpl * kGemv1Shapes[c].
 
 template <typename WT, int EPI>
 static hipError_t gemv1_dispatch(const GemvArgs& a, int cfg, int* grid_out, int grid_cap, hipStream_t s) {
-    const size_t shm = (size_t)a.K * sizeof(float);
+    const size_t shm = (size_t)(gemv1_xpad(a.K) + 8) * sizeof(float) + (a.gain ? gemv1_gpad(a.K, sizeof(WT)) : 0);
     auto go = [&](auto kern, int rpt) {
+        if (shm > 65536 && hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm) != hipSuccess)
+            return hipErrorInvalidValue;
         const int tiles = (a.N + rpt - 1) / rpt;
         const int grid = tiles < grid_cap ? tiles : grid_cap;
         if (grid_out) *grid_out = grid;

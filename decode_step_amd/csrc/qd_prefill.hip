@@ -224,21 +224,6 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(GemmArgs a, int ntn, int
 // s_waitcnt vmcnt before one barrier per step, which also frees the stage read
 // in the previous step. Rows outside the matrix read row 0 (their outputs are
 // dropped); K must be a multiple of 32 (the DMA cannot zero a tail).
-typedef __attribute__((address_space(3))) void qd_lds_void;
-
-// One wave-wide LDS DMA of 16 bytes per lane: lane i's global source lands at
-// lds + 16 i. Issued as inline asm so the compiler does not see an LDS write it
-// would have to order against later LDS reads: left to itself it cannot tell
-// which ring stage a pending DMA targets and waits for all of them. Completion
-// is the caller's business (s_waitcnt vmcnt); the compiler's own vmcnt waits
-// stay correct, as extra outstanding loads only make a wait stricter.
-__device__ __forceinline__ void lds_dma16(const uint16_t* src, uint32_t lds_addr) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds_addr) : "memory", "m0");
-}
-
-// s_waitcnt immediates (vmcnt in bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8])
-constexpr int wait_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x70 | 0xF00; }
-constexpr int kWaitLgkm0 = 0xF | (0x3 << 14) | 0x70;
 constexpr int kDmaBK = 32;
 constexpr int kDmaLds = 147456;    // bytes of LDS the ring may take
 
