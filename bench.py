@@ -176,6 +176,26 @@ def bench_prefill(wl, args):
     print(json.dumps(rec), flush=True)
 
 
+COPY_PROBE_BYTES = 1 << 30
+
+
+def copy_probe(reps=5):
+    """A plain copy of COPY_PROBE_BYTES between two device buffers, reps times:
+    each launch reads and writes exactly that many bytes, so the hardware
+    counters it reads give the scale from counter units to bytes."""
+    import torch
+    src = torch.empty(COPY_PROBE_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    print(json.dumps({"copy_probe_bytes": COPY_PROBE_BYTES, "reps": reps,
+                      "gbs_read_plus_write": round(2 * COPY_PROBE_BYTES * reps / el / 1e9, 1)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -184,6 +204,9 @@ def main():
     ap.add_argument("--workload", default="qwen2-0.5b-bf16-b1-past512")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replay")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run only a plain device-to-device copy of 1 GiB (5 times): the reference kernel "
+                         "that scales the FETCH_SIZE / WRITE_SIZE counters to bytes")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -198,6 +221,8 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.copy_probe:
+        return copy_probe()
     wl = S.WORKLOADS[args.workload]
     if wl.kind == "prefill":
         return bench_prefill(wl, args)

@@ -77,8 +77,42 @@ struct DecodePlan {
 constexpr int kAttnTargetWgs = 512;
 constexpr int kAttnMinWgs = 128;
 constexpr int kAttnMinChunk = 64;
-bool plan_split(const qd_config* c, int B, int max_tokens, int* chunk, int* S, int* hpw) {
-    // B = sequences (decode) or query rows (prefill); max_tokens = longest context
+#ifndef QD_B1_CHUNK
+#define QD_B1_CHUNK 144     // tokens per split at batch 1 (o_proj merges the splits)
+#endif
+#ifndef QD_B1_HPW
+#define QD_B1_HPW 1         // query heads per workgroup at batch 1 (0: the whole group)
+#endif
+
+// Batch-1 decode whose o_proj GEMV merges the attention splits itself (no merge
+// launch): splits of at least QD_B1_CHUNK tokens, at most gemv1_merge_max_splits()
+// of them, each small enough for the grouped attention kernel. Needs the context
+// vector (Hq * hd) within 1024 and Hq within 32.
+static bool plan_b1_merge(const qd_config* c, int max_tokens, int* chunk, int* S, int* hpw) {
+    const int pg = c->page_size, G = c->n_q_heads / c->n_kv_heads;
+    const int qdim = c->n_q_heads * c->head_dim;
+    if (qdim > 1024 || c->n_q_heads > 32 || c->head_dim % 4) return false;
+    const int ch_max = qd::attn_max_chunk(c->head_dim, c->kv_dtype == QD_BF16, 1) / pg * pg;
+    const int T = max_tokens < 1 ? 1 : max_tokens;
+    const int smax = qd::gemv1_merge_max_splits();
+    int ch = (T + smax - 1) / smax;
+    if (ch < QD_B1_CHUNK) ch = QD_B1_CHUNK;
+    ch = (ch + pg - 1) / pg * pg;
+    if (ch > ch_max) return false;
+    *chunk = ch;
+    *S = (T + ch - 1) / ch;
+    *hpw = (QD_B1_HPW > 0 && QD_B1_HPW < G) ? QD_B1_HPW : G;
+    return true;
+}
+
+bool plan_split(const qd_config* c, int B, int max_tokens, int* chunk, int* S, int* hpw, bool* merge_in_o = nullptr) {
+    // B = sequences (decode) or query rows (prefill); max_tokens = longest context.
+    // merge_in_o != nullptr: a decode step, whose batch-1 form may merge in o_proj
+    if (merge_in_o) *merge_in_o = false;
+    if (merge_in_o && B == 1 && plan_b1_merge(c, max_tokens, chunk, S, hpw)) {
+        *merge_in_o = true;
+        return true;
+    }
     const int pg = c->page_size;
     const int ch_max = qd::attn_max_chunk(c->head_dim, c->kv_dtype == QD_BF16, 1) / pg * pg;
     const int ch_wide = qd::attn_max_chunk(c->head_dim, c->kv_dtype == QD_BF16, 0) / pg * pg;
@@ -242,7 +276,8 @@ size_t qd_workspace_bytes(const qd_config* cfg, int32_t batch, int32_t max_ctx, 
     }
     if (batch < 1 || batch > kMaxBatch || max_ctx < 1) return 0;
     int chunk, S, hpw;
-    if (!plan_split(cfg, batch, max_ctx, &chunk, &S, &hpw)) return 0;
+    bool merge_in_o = false;
+    if (!plan_split(cfg, batch, max_ctx, &chunk, &S, &hpw, &merge_in_o)) return 0;
     return plan_decode(cfg, batch, S, chunk).total;
 }
 
@@ -276,7 +311,8 @@ qd_status qd_decode_step(const qd_config* cfg, const qd_weights* w, const qd_kv*
             return fail(QD_EALIGN, "kv pages of layer %d not 16-byte aligned", l);
     }
     int chunk, S, hpw;
-    if (!plan_split(cfg, batch, max_tokens, &chunk, &S, &hpw))
+    bool merge_in_o = false;
+    if (!plan_split(cfg, batch, max_tokens, &chunk, &S, &hpw, &merge_in_o))
         return fail(QD_ECAPACITY, "context of %d tokens needs %d attention splits > %d", max_tokens, S,
                     qd::attn_max_splits());
     const DecodePlan P = plan_decode(cfg, batch, S, chunk);
@@ -290,6 +326,7 @@ qd_status qd_decode_step(const qd_config* cfg, const qd_weights* w, const qd_kv*
     float* x = (float*)(ws + P.off_x);
     float* qkv = (float*)(ws + P.off_qkv);
     float* part = (float*)(ws + P.off_part);
+    float2* part_ml = (float2*)(part + (size_t)batch * P.Hq * S * P.hd);
     float2* rope = (float2*)(ws + P.off_rope);
     float* ctx = (float*)(ws + P.off_ctx);
     float* h = (float*)(ws + P.off_h);
@@ -330,7 +367,8 @@ qd_status qd_decode_step(const qd_config* cfg, const qd_weights* w, const qd_kv*
         at.qkv = qkv; at.k_cache = kv->k_pages_host[l]; at.v_cache = kv->v_pages_host[l];
         at.block_table = kv->block_table; at.max_blocks = kv->max_blocks; at.num_pages = kv->num_pages;
         at.pos = pos; at.capacity = cap; at.q_norm = L.q_norm; at.k_norm = L.k_norm; at.qk_norm = c.qk_norm;
-        at.eps = c.rms_eps; at.theta = c.rope_theta; at.part = part; at.rope = rope; at.ctx = ctx;
+        at.eps = c.rms_eps; at.theta = c.rope_theta; at.part = part; at.part_ml = part_ml;
+        at.part_always = merge_in_o ? 1 : 0; at.rope = rope; at.ctx = ctx;
         at.Hq = P.Hq; at.Hkv = P.Hkv; at.hd = P.hd; at.page = c.page_size; at.chunk = P.chunk; at.S = P.S;
         at.B = B; at.hpw = hpw; at.scale = 1.0f / sqrtf((float)P.hd);
         at.prefill_start = -1; at.q_rot = nullptr;
@@ -340,6 +378,10 @@ qd_status qd_decode_step(const qd_config* cfg, const qd_weights* w, const qd_kv*
         go.w[0] = L.wo; go.seg_end[0] = go.seg_end[1] = go.seg_end[2] = D; go.nseg = 1;
         go.N = D; go.K = P.Hq * P.hd; go.B = B; go.x = ctx; go.gain = nullptr; go.y = x;
         go.kt = gemv_kt(B, go.K);
+        if (merge_in_o) {   // the context is merged from the attention's splits here
+            go.part = part; go.part_ml = part_ml; go.part_pos = pos;
+            go.part_S = S; go.part_chunk = chunk; go.part_hd = P.hd;
+        }
         QD_LAUNCH_K(QD_K_O, gemv(go, qd::EPI_RESID, kGemvGridCap, nullptr), "o_proj gemv");
         // RMSNorm -> gate|up GEMV -> SwiGLU
         qd::GemvArgs gu{};
@@ -500,7 +542,8 @@ qd_status qd_prefill_block(const qd_config* cfg, const qd_layer* layer, int32_t 
     qd::AttnArgs at{};
     at.k_cache = kc; at.v_cache = vc; at.block_table = kv->block_table; at.max_blocks = kv->max_blocks;
     at.num_pages = kv->num_pages; at.pos = nullptr; at.capacity = kv->max_blocks * c.page_size;
-    at.part = part; at.ctx = ctx; at.Hq = Hq; at.Hkv = Hkv; at.hd = hd; at.page = c.page_size;
+    at.part = part; at.part_ml = (float2*)(part + (size_t)N * Hq * S * hd);
+    at.ctx = ctx; at.Hq = Hq; at.Hkv = Hkv; at.hd = hd; at.page = c.page_size;
     at.chunk = chunk; at.S = S; at.B = N; at.hpw = hpw; at.scale = 1.0f / sqrtf((float)hd);
     at.prefill_start = start_pos; at.q_rot = qrot;
     QD_LAUNCH_K(QD_K_PREFILL_ATTN, qd::launch_attention(at, 1, kvbf, s), "prefill attention");

@@ -279,12 +279,12 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
             float v = 0.f;
 #pragma unroll
             for (int w = 0; w < NWV; ++w) v += red[w][hl][d];
-            if (ns == 1) {
+            if (ns == 1 && !a.part_always) {
                 a.ctx[((long)b * a.Hq + hq0) * HD + idx] = v / mls[hl][1];
-            } else {   // publish (o, m, l) for the merge kernel; layout [B][Hq][S][hd + 2]
-                float* pp = a.part + (((long)b * a.Hq + hq0 + hl) * a.S + s) * (HD + 2);
-                pp[d] = v;
-                if (d == 0) { pp[HD] = mls[hl][0]; pp[HD + 1] = mls[hl][1]; }
+            } else {   // publish (o, m, l) for the merge
+                const long pi = ((long)b * a.Hq + hq0 + hl) * a.S + s;
+                a.part[pi * HD + d] = v;
+                if (d == 0) a.part_ml[pi] = make_float2(mls[hl][0], mls[hl][1]);
             }
         }
         return;
@@ -353,12 +353,12 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
             L = fmaf(wml[w][hl].y, e, L);
             O = fmaf(red[w][hl][d], e, O);
         }
-        if (ns == 1) {
+        if (ns == 1 && !a.part_always) {
             a.ctx[((long)b * a.Hq + hq0) * HD + idx] = O / L;
-        } else {   // several splits: publish (o, m, l) for the merge kernel; layout [B][Hq][S][hd + 2]
-            float* pp = a.part + (((long)b * a.Hq + hq0 + hl) * a.S + s) * (HD + 2);
-            pp[d] = O;
-            if (d == 0) { pp[HD] = M; pp[HD + 1] = L; }
+        } else {   // publish (o, m, l) for the merge
+            const long pi = ((long)b * a.Hq + hq0 + hl) * a.S + s;
+            a.part[pi * HD + d] = O;
+            if (d == 0) a.part_ml[pi] = make_float2(M, L);
         }
     }
 }
@@ -392,11 +392,13 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
     if (p < 0 || p >= a.capacity) return;
     const int ns = min(min(a.S, kMaxSplits), (p + 1 + a.chunk - 1) / a.chunk);
     if (ns <= 1) return;   // one split: the attention kernel wrote the output itself
-    const int hd = a.hd, stride = hd + 2;
-    const float* base = a.part + ((long)b * a.Hq + h) * a.S * stride;
+    const int hd = a.hd;
+    const float* base = a.part + ((long)b * a.Hq + h) * a.S * hd;
+    const float2* mlb = a.part_ml + ((long)b * a.Hq + h) * a.S;
     if (tid < kWave) {   // wave 0: weights of the splits
-        const float mj = tid < ns ? base[tid * stride + hd] : -INFINITY;
-        const float lj = tid < ns ? base[tid * stride + hd + 1] : 0.f;
+        const float2 ml = mlb[tid < ns ? tid : 0];
+        const float mj = tid < ns ? ml.x : -INFINITY;
+        const float lj = tid < ns ? ml.y : 0.f;
         const float m = group_max<kWave>(mj);
         const float w = tid < ns ? exp2_hw(mj - m) : 0.f;   // m in base-2 units
         if (tid < ns) wgt[tid] = w;
@@ -411,7 +413,7 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
             const int j = j0 + u * ng;
-            v[u] = base[(j < ns ? j : 0) * stride + d];
+            v[u] = base[(j < ns ? j : 0) * hd + d];
         }
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
@@ -450,7 +452,7 @@ hipError_t launch_attention(const AttnArgs& a, int w_is_bf16, int kv_is_bf16, hi
     }
 #undef QD_ATTN
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || a.S == 1) return e;
+    if (e != hipSuccess || a.S == 1 || a.part_always) return e;   // part_always: the consumer merges
     hipLaunchKernelGGL(attn_merge_kernel, dim3(a.Hq, a.B), dim3(kMergeThreads), 0, s, a);
     return hipGetLastError();
 }

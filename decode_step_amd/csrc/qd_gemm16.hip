@@ -437,6 +437,159 @@ __global__ __launch_bounds__(64 * WK) void gemm16_direct_kernel(GemvArgs a) {
     }
 }
 
+// Single-shot form for matrices whose K range fits the workgroup's registers:
+// every wave issues all of its k-steps' loads (weights, activation, gain) at
+// once, then runs its MFMAs. The grid is (16-row blocks, K splits); K is cut into
+// `splits` ranges of 32-wide steps and each range over the 4 waves, at most SPW
+// steps per wave. A residual product with several K ranges adds its partial
+// sums into y with float atomics (each range's sum is complete and fixed; only
+// the order of the final few additions varies from run to run); every other
+// epilogue takes one range (splits = 1), so its output is formed once.
+template <int EPI, int SPW>
+__global__ __launch_bounds__(256) void gemm16_split_kernel(GemvArgs a, int splits) {
+    constexpr bool GAIN = EPI != EPI_RESID;
+    constexpr int NW = (EPI == EPI_SWIGLU) ? 2 : 1;
+    constexpr int WK = 4;
+    __shared__ float ssum[WK][16];
+    __shared__ g16_f32x4 red[WK - 1][NW][kWave];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+    const int col = lane & 15, kq = lane >> 4;
+    const int B = a.B, K = a.K, N = a.N;
+    const int tile = blockIdx.x, ks = blockIdx.y;
+    const bool tok = col < B;
+    const float* xrow = a.x + (long)(tok ? col : 0) * K;
+    const uint16_t* gain = (const uint16_t*)a.gain;
+    const int nsteps = (K + 31) / 32;
+    const int a0 = ks * nsteps / splits, a1 = (ks + 1) * nsteps / splits;
+    const int s0 = a0 + wave * (a1 - a0) / WK, s1 = a0 + (wave + 1) * (a1 - a0) / WK;
+
+    const uint16_t* wrow[NW];        // a row past N reads row 0 (masked)
+    const int r_own = tile * 16 + col;
+    const bool rok = r_own < N;
+#pragma unroll
+    for (int n = 0; n < NW; ++n) {
+        const uint16_t* p = (const uint16_t*)a.w[n];
+        if (rok) {
+            if (EPI == EPI_SWIGLU) {
+                p = (const uint16_t*)a.w[n] + (long)r_own * K;
+            } else {
+                const bool q0 = r_own < a.seg_end[0], q1 = r_own < a.seg_end[1];
+                const void* w = q0 ? a.w[0] : (q1 ? a.w[1] : a.w[2]);
+                const int base = q0 ? 0 : (q1 ? a.seg_end[0] : a.seg_end[1]);
+                p = (const uint16_t*)w + (long)(r_own - base) * K;
+            }
+        }
+        wrow[n] = p;
+    }
+    uint4 wv[SPW][NW];
+    float4 x0[SPW], x1[SPW];
+    uint4 gv[SPW];
+#pragma unroll
+    for (int u = 0; u < SPW; ++u) {
+        const int st = s0 + u;
+        const int k = st * 32 + kq * 8;
+        const bool ok = st < s1 && k < K;
+        const int kc = ok ? k : 0;
+#pragma unroll
+        for (int n = 0; n < NW; ++n) wv[u][n] = masked(*(const uint4*)(wrow[n] + kc), ok && rok);
+        x0[u] = masked(*(const float4*)(xrow + kc), ok && tok);
+        x1[u] = masked(*(const float4*)(xrow + kc + 4), ok && tok);
+        if (GAIN) gv[u] = masked(*(const uint4*)(gain + kc), ok);
+    }
+    const int rbase = tile * 16 + kq * 4;
+    float yv[4] = {0.f, 0.f, 0.f, 0.f};       // single-range residual: y read with the loads
+    if (EPI == EPI_RESID && splits == 1) {
+        const float* yrow = a.y + (long)(tok ? col : 0) * N;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = rbase + e;
+            const float t = yrow[r < N ? r : 0];
+            yv[e] = (tok && r < N) ? t : 0.f;
+        }
+    }
+    g16_f32x4 acc[NW];
+#pragma unroll
+    for (int n = 0; n < NW; ++n) acc[n] = g16_f32x4{0.f, 0.f, 0.f, 0.f};
+    float ss = 0.f;
+#pragma unroll
+    for (int u = 0; u < SPW; ++u) {
+        float v[8] = {x0[u].x, x0[u].y, x0[u].z, x0[u].w, x1[u].x, x1[u].y, x1[u].z, x1[u].w};
+        if (GAIN) {
+            float gf[8];
+            widen16(gv[u], gf);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                ss += v[e] * v[e];
+                v[e] *= gf[e];
+            }
+        }
+        uint4 hu, lu;
+        split_hi_lo(v, hu, lu);
+        const g16_bf16x8 bh = g16_frag(hu);
+        const g16_bf16x8 bl = g16_frag(lu);
+#pragma unroll
+        for (int n = 0; n < NW; ++n) {
+            const g16_bf16x8 af = g16_frag(wv[u][n]);
+            acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bh, acc[n], 0, 0, 0);
+            acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bl, acc[n], 0, 0, 0);
+        }
+    }
+    // the four waves' partial products and sums of squares meet in wave 0, in a fixed order
+    if (GAIN) {
+        const float t = strided_sum<16>(ss);
+        if (lane < 16) ssum[wave][lane] = t;
+    }
+    if (wave > 0)
+#pragma unroll
+        for (int n = 0; n < NW; ++n) red[wave - 1][n][lane] = acc[n];
+    __syncthreads();
+    if (wave != 0 || !tok) return;
+#pragma unroll
+    for (int q = 0; q < WK - 1; ++q)
+#pragma unroll
+        for (int n = 0; n < NW; ++n) acc[n] += red[q][n][lane];
+    float rs = 1.0f;
+    if (GAIN) {
+        float t = 0.f;
+#pragma unroll
+        for (int q = 0; q < WK; ++q) t += ssum[q][col];
+        rs = 1.0f / sqrtf(t / (float)K + a.eps);
+    }
+    float* yrow = a.y + (long)col * N;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int r = rbase + e;
+        if (r >= N) break;
+        const float v0 = acc[0][e] * rs;
+        if (EPI == EPI_STORE) {
+            const bool q0 = r < a.seg_end[0], q1 = r < a.seg_end[1];
+            const void* bsel = q0 ? a.bias[0] : (q1 ? a.bias[1] : a.bias[2]);
+            const int base = q0 ? 0 : (q1 ? a.seg_end[0] : a.seg_end[1]);
+            yrow[r] = bsel ? v0 + load_scalar<uint16_t>(bsel, r - base) : v0;
+        } else if (EPI == EPI_RESID) {
+            if (splits == 1) yrow[r] = yv[e] + v0;
+            else unsafeAtomicAdd(yrow + r, v0);
+        } else {
+            yrow[r] = silu(v0) * (acc[NW - 1][e] * rs);
+        }
+    }
+}
+
+// Shape of the single-shot form for a matrix, or spw = 0 when it does not apply:
+// a residual product takes k-steps per wave by K (4 from 2048 up, else 2) and as
+// many K ranges as that needs; a normed product must fit one range of at most 8
+// steps per wave (K <= 1024).
+struct G16Split { int spw, splits; };
+static G16Split gemm16_split_shape(int K, int epi) {
+    const int nsteps = (K + 31) / 32;
+    if (epi == EPI_RESID) {
+        const int spw = K >= 2048 ? 4 : 2;
+        return {spw, (nsteps + 4 * spw - 1) / (4 * spw)};
+    }
+    if ((epi == EPI_STORE || epi == EPI_SWIGLU) && nsteps <= 32) return {8, 1};
+    return {0, 0};
+}
+
 // K split into the fewest chunks of at most kG16Chunk, evened out (multiples of 32)
 int gemm16_chunk(int K) {
     const int kp = (K + 31) & ~31;
@@ -456,6 +609,22 @@ hipError_t launch_gemm16(const GemvArgs& a, int epi, int grid_cap, int* grid_out
                                           : (a.gain != nullptr && ((uintptr_t)a.gain & 15u) == 0);
     if (!wide && gain_ok) {
         const int grid = (a.N + 15) / 16;
+        const G16Split sp = gemm16_split_shape(a.K, epi);
+        if (sp.spw) {
+            if (grid > grid_cap) return hipErrorInvalidValue;
+            if (grid_out) *grid_out = grid;
+            const dim3 g2(grid, sp.splits);
+#define QD_G16S(E, S) hipLaunchKernelGGL((gemm16_split_kernel<E, S>), g2, dim3(256), 0, s, a, sp.splits)
+            if (epi == EPI_RESID) {
+                if (sp.spw == 4) QD_G16S(EPI_RESID, 4); else QD_G16S(EPI_RESID, 2);
+            } else if (epi == EPI_STORE) {
+                QD_G16S(EPI_STORE, 8);
+            } else {
+                QD_G16S(EPI_SWIGLU, 8);
+            }
+#undef QD_G16S
+            return hipGetLastError();
+        }
         if (grid > grid_cap) return hipErrorInvalidValue;
         if (grid_out) *grid_out = grid;
         const bool deep = a.K >= 2048;       // long K: eight waves split it

@@ -27,13 +27,20 @@
 namespace qd {
 
 constexpr int kCus = 256;
+#ifndef QD_B1_OCFG
+#define QD_B1_OCFG 0        // GEMV shape of the residual product that merges attention splits
+#endif
 
 // floats of x staged in LDS: K rounded up to whole 1 KB DMA blocks
 __host__ __device__ constexpr int gemv1_xpad(int K) { return (K + 255) & ~255; }
 // bytes of gain staged in LDS (whole 1 KB blocks)
 __host__ __device__ constexpr int gemv1_gpad(int K, int wbytes) { return (K * wbytes + 1023) & ~1023; }
 
-template <typename WT, int LPR, int WK, int UR, int CPL, int EPI>
+// Splits of the decode attention that the residual product can merge itself
+// (MS > 0: x is formed from the attention's partials, at most MS of them).
+constexpr int kG1MergeHeads = 32;
+
+template <typename WT, int LPR, int WK, int UR, int CPL, int EPI, int MS = 0>
 __global__ __launch_bounds__(256) void gemv1_kernel(GemvArgs a) {
     constexpr int CE = VecN<WT>::n;
     constexpr int RPW = kWave / LPR;
@@ -98,9 +105,31 @@ __global__ __launch_bounds__(256) void gemv1_kernel(GemvArgs a) {
     int tile = blockIdx.x;
     issue(tile < ntiles ? tile : ntiles - 1, kc0, true);   // unconditional: no join for the loads to wait at
 
-    // x and the gain into LDS by DMA, behind the weights (source indices clamped to
-    // the vectors; what lands past K is never read)
-    {
+    // MS > 0: this thread's four context elements from every split, and (threads
+    // below Hq) head tid's split maxima and sums, loaded behind the weights from
+    // clamped (always valid) indices; splits past the valid count are masked below
+    float4 ov[MS > 0 ? MS : 1];
+    float2 mlv[MS > 0 ? MS : 1];
+    int ns = 0;
+    if constexpr (MS > 0) {
+        const int hd = a.part_hd, S = a.part_S;
+        const int e0 = 4 * tid < K ? 4 * tid : 0;
+        const int hh = e0 / hd, d = e0 - hh * hd;
+        const int hm = tid < K / hd ? tid : 0;
+#pragma unroll
+        for (int sp = 0; sp < MS; ++sp) {
+            const int sc = sp < S ? sp : S - 1;
+            ov[sp] = *(const float4*)(a.part + ((long)hh * S + sc) * hd + d);
+        }
+        if (wave == 0) {   // wave-uniform: the (m, l) pairs are wave 0's (Hq <= 32)
+#pragma unroll
+            for (int sp = 0; sp < MS; ++sp) mlv[sp] = a.part_ml[(long)hm * S + (sp < S ? sp : S - 1)];
+        }
+        const int p = a.part_pos[0];
+        ns = p >= 0 ? min(S, (p + 1 + a.part_chunk - 1) / a.part_chunk) : 0;
+    } else {
+        // x and the gain into LDS by DMA, behind the weights (source indices clamped
+        // to the vectors; what lands past K is never read)
         const uint32_t xl = lds_addr(xs);
         for (int j = wave; j < xpad / 256; j += 4) {
             const int f = min(j * 256 + lane * 4, K - 4);
@@ -120,6 +149,40 @@ __global__ __launch_bounds__(256) void gemv1_kernel(GemvArgs a) {
         for (int i = tid; i < a.zero_n; i += 256) a.zero_ptr[i] = 0u;
     __builtin_amdgcn_s_waitcnt(wait_vm(0));   // this wave's weights and DMA landed
     lds_barrier();                            // ... and every wave's DMA
+
+    if constexpr (MS > 0) {
+        // merge of the splits (Tang page, section 2.2: the online-softmax monoid):
+        // with M = max m_s over the valid splits (base-2 units), head h's context is
+        // sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M)
+        __shared__ float wgt[kG1MergeHeads][MS];
+        const int hd = a.part_hd;
+        if (tid < K / hd) {
+            float M = -INFINITY;
+#pragma unroll
+            for (int sp = 0; sp < MS; ++sp) M = sp < ns ? fmaxf(M, mlv[sp].x) : M;
+            float w[MS], L = 0.f;
+#pragma unroll
+            for (int sp = 0; sp < MS; ++sp) {
+                w[sp] = sp < ns ? __builtin_amdgcn_exp2f(mlv[sp].x - M) : 0.f;
+                L = fmaf(mlv[sp].y, w[sp], L);
+            }
+            const float rl = ns > 0 ? 1.0f / L : 0.f;
+#pragma unroll
+            for (int sp = 0; sp < MS; ++sp) wgt[tid][sp] = w[sp] * rl;
+        }
+        lds_barrier();
+        if (4 * tid < K) {
+            const int hh = 4 * tid / hd;
+            float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int sp = 0; sp < MS; ++sp) {
+                const float wv_ = wgt[hh][sp];
+                o.x = fmaf(ov[sp].x, wv_, o.x); o.y = fmaf(ov[sp].y, wv_, o.y);
+                o.z = fmaf(ov[sp].z, wv_, o.z); o.w = fmaf(ov[sp].w, wv_, o.w);
+            }
+            ((float4*)xs)[tid] = o;
+        }
+    }
 
     // x * g and sum(x^2) in place; the zero block behind x
     float ss = 0.f;
@@ -245,7 +308,7 @@ constexpr Gemv1Shape kGemv1Shapes[G_NCFG] = {
 constexpr int gemv1_rpt(int c) { return (4 / kGemv1Shapes[c].wk) * (64 / kGemv1Shapes[c].lpr) * kGemv1Shapes[c].ur; }
 constexpr int gemv1_kpass(int c) { return kGemv1Shapes[c].cpl * kGemv1Shapes[c].lpr * kGemv1Shapes[c].wk * 8; }
 
-template <typename WT, int EPI>
+template <typename WT, int EPI, int MS = 0>
 static hipError_t gemv1_dispatch(const GemvArgs& a, int cfg, int* grid_out, int grid_cap, hipStream_t s) {
     const size_t shm = (size_t)(gemv1_xpad(a.K) + 8) * sizeof(float) + (a.gain ? gemv1_gpad(a.K, sizeof(WT)) : 0);
     auto go = [&](auto kern, int rpt) {
@@ -258,11 +321,18 @@ static hipError_t gemv1_dispatch(const GemvArgs& a, int cfg, int* grid_out, int 
         return hipGetLastError();
     };
 #define QD_G1C(C) \
-    case C: return go(gemv1_kernel<WT, kGemv1Shapes[C].lpr, kGemv1Shapes[C].wk, kGemv1Shapes[C].ur, kGemv1Shapes[C].cpl, EPI>, gemv1_rpt(C));
-    switch (cfg) {
-        QD_G1C(G_SMALLK_FEWROWS) QD_G1C(G_SMALLK) QD_G1C(G_SMALLK_UR2) QD_G1C(G_BIGK_FEWROWS) QD_G1C(G_BIGK)
-        QD_G1C(G_SMALLK_8) QD_G1C(G_LONGK_4)
-        default: return go(gemv1_kernel<WT, 64, 1, 2, 8, EPI>, gemv1_rpt(G_BIGK_UR2));
+    case C: return go(gemv1_kernel<WT, kGemv1Shapes[C].lpr, kGemv1Shapes[C].wk, kGemv1Shapes[C].ur, kGemv1Shapes[C].cpl, EPI, MS>, gemv1_rpt(C));
+    if constexpr (MS > 0) {
+        switch (cfg) {
+            QD_G1C(G_SMALLK_FEWROWS) QD_G1C(G_SMALLK)
+            default: return hipErrorInvalidValue;
+        }
+    } else {
+        switch (cfg) {
+            QD_G1C(G_SMALLK_FEWROWS) QD_G1C(G_SMALLK) QD_G1C(G_SMALLK_UR2) QD_G1C(G_BIGK_FEWROWS) QD_G1C(G_BIGK)
+            QD_G1C(G_SMALLK_8) QD_G1C(G_LONGK_4)
+            default: return go(gemv1_kernel<WT, 64, 1, 2, 8, EPI>, gemv1_rpt(G_BIGK_UR2));
+        }
     }
 #undef QD_G1C
 }
@@ -298,8 +368,24 @@ static int gemv1_pick(int N, int K, int epi) {
     return G_BIGK_FEWROWS;
 }
 
+int gemv1_merge_max_splits() { return 16; }
+
 hipError_t launch_gemv1(const GemvArgs& a, int w_is_bf16, int epi, int grid_cap, int* grid_out, hipStream_t s) {
     const int cfg = gemv1_pick(a.N, a.K, epi);
+    if (a.part) {   // residual product over the merged attention context
+        if (epi != EPI_RESID || a.gain || a.part_hd % 4 || a.K % a.part_hd || a.K > 1024 ||
+            a.K / a.part_hd > kG1MergeHeads || a.part_S < 1 || a.part_S > 16 || a.part_chunk < 1)
+            return hipErrorInvalidValue;
+        // one shape (it covers K <= 1024 in one pass); MS = the smallest of 2, 4, 8, 16 >= S
+        const int mc = QD_B1_OCFG;
+#define QD_G1M(WT)                                                                                      \
+        if (a.part_S <= 2) return gemv1_dispatch<WT, EPI_RESID, 2>(a, mc, grid_out, grid_cap, s);      \
+        if (a.part_S <= 4) return gemv1_dispatch<WT, EPI_RESID, 4>(a, mc, grid_out, grid_cap, s);      \
+        if (a.part_S <= 8) return gemv1_dispatch<WT, EPI_RESID, 8>(a, mc, grid_out, grid_cap, s);      \
+        return gemv1_dispatch<WT, EPI_RESID, 16>(a, mc, grid_out, grid_cap, s);
+        if (w_is_bf16) { QD_G1M(uint16_t) } else { QD_G1M(float) }
+#undef QD_G1M
+    }
 #define QD_G1(WT)                                                                                 \
     switch (epi) {                                                                                \
         case EPI_STORE: return gemv1_dispatch<WT, EPI_STORE>(a, cfg, grid_out, grid_cap, s);      \

@@ -27,6 +27,13 @@ struct GemvArgs {
     int kt;            // K elements staged in LDS per pass
     unsigned* zero_ptr;  // optional: workgroup 0 stores zeros here (counters of a later kernel)
     int zero_n;
+    // optional, batch-1 residual product only: x is the decode attention's context,
+    // merged here from its split partials (AttnArgs::part / part_ml, [Hq][S]) with
+    // ns = ceil((pos[0] + 1) / part_chunk) valid splits; then K = Hq * part_hd
+    const float* part;
+    const float2* part_ml;
+    const int* part_pos;
+    int part_S, part_chunk, part_hd;
 };
 hipError_t launch_gemv(const GemvArgs& a, int w_is_bf16, int epi, int grid_cap, int* grid_out,
                        hipStream_t s);
@@ -34,6 +41,8 @@ hipError_t launch_gemv(const GemvArgs& a, int w_is_bf16, int epi, int grid_cap, 
 hipError_t launch_gemv1(const GemvArgs& a, int w_is_bf16, int epi, int grid_cap, int* grid_out,
                         hipStream_t s);
 int gemv_rows_per_tile(int K);
+// most attention splits launch_gemv1 merges itself (GemvArgs::part)
+int gemv1_merge_max_splits();
 // batch 2..16 with bf16 weights on the matrix cores (qd_gemm16.hip); a.kt must be
 // gemm16_chunk(a.K); part_val/part_idx hold [B][grid] entries
 hipError_t launch_gemm16(const GemvArgs& a, int epi, int grid_cap, int* grid_out, hipStream_t s);
@@ -53,7 +62,10 @@ struct AttnArgs {
     const void* k_norm;
     int qk_norm;
     float eps, theta;
-    float* part;            // [B][Hq][S][hd+2]: o[hd], m, l of each split
+    float* part;            // [B][Hq][S][hd]: o of each split (sum of e^(s - m) v)
+    float2* part_ml;        // [B][Hq][S]: (m, l) of each split, m in base-2 units
+    int part_always;        // publish (o, m, l) even when the context fits one split
+                            // (batch 1: the o_proj GEMV merges the splits itself)
     const float2* rope;     // [B][hd/2] (cos, sin) of the step's positions
     float* ctx;             // [B][Hq*hd]
     int Hq, Hkv, hd, page, chunk, S, B;

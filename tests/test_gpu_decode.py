@@ -121,35 +121,49 @@ def test_position_zero_returns_v():
     assert rel_err(x_out.cpu().numpy(), ref.x_out) <= 1e-5
 
 
-def test_outputs_guarded_and_deterministic():
+@pytest.mark.parametrize("ctx_list", [[40], [40, 7]])
+def test_outputs_guarded_and_deterministic(ctx_list):
+    """Same position twice: idempotent. Batch 1 is bitwise deterministic (no float
+    atomics on its path); batches of 2..16 add the K ranges of the residual
+    projections with float atomics, so only the order of those few additions may
+    vary: the two runs agree to float32 rounding (1e-5 of the largest logit, the
+    last-bit differences of the residual grown over the layers)."""
     shape = SMALL
-    ctx = np.array([40, 7], np.int32)
+    ctx = np.array(ctx_list, np.int32)
+    B = len(ctx)
     case = make_case(shape, ctx, seed=5, random_order=True)
-    tok = dev_i32(synth.make_tokens(2, shape.vocab, seed=5))
-    n = 2 * shape.vocab
+    tok = dev_i32(synth.make_tokens(B, shape.vocab, seed=5))
+    n = B * shape.vocab
     outs = []
     for _ in range(2):
         full, view = guarded(n)
-        nxt = torch.full((2,), -1, dtype=torch.int32, device="cuda")
-        case.runner.step(ctx, dev_i32(ctx), tokens=tok, logits=view.view(2, shape.vocab), next_tokens=nxt)
+        nxt = torch.full((B,), -1, dtype=torch.int32, device="cuda")
+        case.runner.step(ctx, dev_i32(ctx), tokens=tok, logits=view.view(B, shape.vocab), next_tokens=nxt)
         torch.cuda.synchronize()
         assert canaries_intact(full, n)
         assert not torch.isnan(view).any()
         outs.append((view.cpu().clone(), nxt.cpu().clone()))
-    # same position twice: idempotent and bitwise deterministic (no float atomics)
-    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    assert torch.equal(outs[0][1], outs[1][1])
+    if B == 1:
+        assert torch.equal(outs[0][0], outs[1][0])
+    else:
+        assert rel_err(outs[0][0].numpy(), outs[1][0].numpy().astype(np.float64)) <= 1e-5
 
 
-def test_graph_replay_matches_eager():
+@pytest.mark.parametrize("ctx_list", [[70], [70, 3, 129]])
+def test_graph_replay_matches_eager(ctx_list):
     """One decode step captured in a HIP graph and replayed several times, with eager
-    work and synchronisations in between: every replay equals the eager result bitwise."""
+    work and synchronisations in between: every replay equals the eager result
+    (bitwise at batch 1; to float32 rounding where float atomics add the residual
+    projections' K ranges), with the same tokens."""
     shape = SMALL
-    ctx = np.array([70, 3, 129], np.int32)
+    ctx = np.array(ctx_list, np.int32)
+    B = len(ctx)
     case = make_case(shape, ctx, seed=21, random_order=True)
-    tok = dev_i32(synth.make_tokens(3, shape.vocab, seed=21))
+    tok = dev_i32(synth.make_tokens(B, shape.vocab, seed=21))
     pos = dev_i32(ctx)
-    logits = torch.empty(3, shape.vocab, device="cuda")
-    nxt = torch.empty(3, dtype=torch.int32, device="cuda")
+    logits = torch.empty(B, shape.vocab, device="cuda")
+    nxt = torch.empty(B, dtype=torch.int32, device="cuda")
 
     def step():
         case.runner.step(ctx, pos, tokens=tok, logits=logits, next_tokens=nxt,
@@ -173,7 +187,11 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        assert torch.equal(logits, ref_logits), i
+        if B == 1:
+            assert torch.equal(logits, ref_logits), i
+        else:
+            assert not torch.isnan(logits).any(), i
+            assert rel_err(logits.cpu().numpy(), ref_logits.cpu().numpy().astype(np.float64)) <= 1e-5, i
         assert torch.equal(nxt, ref_next), i
     del junk
 
