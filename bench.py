@@ -13,7 +13,11 @@ timed step attends over exactly `past` cached tokens.
 Prints ONE JSON line. `roofline` covers the dominant kernel kind: its
 algorithmic bytes per launch divided by its average launch duration, measured
 with HIP events recorded on the library's stream around each launch of every
-kind, in a second pass of the same K steps right after the clean timed region.
+kind, in a second pass of the same steps right after the clean timed region
+(net of an event pair's own cost, plus the launch's equal share of the
+replayed step's dispatch time). `traffic` is the measured HBM bytes per launch
+of that kernel from the hardware-counter summaries under profiles/, when they
+were taken from the current sources.
 `cpu_baseline` is the fp64 oracle timed on the host over a bounded sample of
 whole decode steps of the same workload.
 """
@@ -71,6 +75,39 @@ def step_bytes(shape, B, ctx):
     emb_rows = B * shape.hidden * wb
     logits = B * shape.vocab * 4
     return weights + kv_read + kv_write + emb_rows + logits
+
+
+def csrc_digest():
+    """sha256 over the HIP sources of libqd (file names and contents, sorted): the
+    hardware-counter figures under profiles/ hold only for the sources they were
+    taken from."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "decode_step_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_from_profiles(workload, kernel):
+    """HBM bytes per launch of `kernel` from the FETCH_SIZE / WRITE_SIZE counter
+    summaries in profiles/ (lines 'traffic: {json}'), or None when none was taken
+    for these exact sources."""
+    import glob
+    digest = csrc_digest()
+    for f in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        with open(f) as fh:
+            for line in fh:
+                if not line.startswith("traffic: "):
+                    continue
+                rec = json.loads(line[len("traffic: "):])
+                if rec.get("workload") == workload and rec.get("kernel") == kernel:
+                    if rec.get("csrc_sha256") == digest:
+                        return int(rec["bytes_per_launch"]), os.path.relpath(f, ROOT)
+                    return None, f"{os.path.relpath(f, ROOT)} (taken from other sources)"
+    return None, "no counter run for these sources"
 
 
 def cpu_baseline(wl, case_host, ctx, tokens, budget_s=12.0):
@@ -312,22 +349,36 @@ def main():
     torch.cuda.synchronize()
     pair_us = float(np.mean([1e3 * a_.elapsed_time(b_) for a_, b_ in cal]))
     bpl = _bytes_per_launch(shape, B, ctx)
+    # Each launch's net duration is its event interval less the cost of an event pair.
+    # In the replayed graph the kernels run back to back, and the step time also holds
+    # the dispatch of every launch; that remainder, shared equally over the launches,
+    # is added to each net duration to give the launch's slot in the replayed step
+    # (the slots sum to the step time; rocprofv3's kernel durations of a graph replay
+    # tile the step the same way).
+    net_us = {k: 1e3 * ms / n - pair_us for k, (n, ms) in per_kind.items()}
+    launches_per_step = sum(n for n, _ in per_kind.values()) / steps_prof
+    net_step_us = sum(net_us[k] * n / steps_prof for k, (n, _) in per_kind.items())
+    share_us = max(0.0, (ms_per_step * 1e3 - net_step_us) / launches_per_step)
     total_ms = sum(ms for _, ms in per_kind.values())
-    print(f"[bench] event pair with nothing between: {pair_us:.2f} us (subtracted below)", file=sys.stderr)
-    for k, (n, ms) in sorted(per_kind.items(), key=lambda kv_: -kv_[1][1]):
-        avg_us = 1e3 * ms / n - pair_us
-        gbs = (bpl[k] / (avg_us * 1e-6) / 1e9) if k in bpl else float("nan")
-        print(f"[bench]   {kinds[k]:>14}: {n // steps_prof:3d}/step avg {avg_us:8.2f} us "
-              f"({100 * ms / total_ms:5.1f}% of kernel time) {gbs:8.1f} GB/s", file=sys.stderr)
-    dom = max((k for k in per_kind if k in bpl), key=lambda k: per_kind[k][1])
-    n_dom, ms_dom = per_kind[dom]
-    avg_s = (ms_dom / n_dom * 1e3 - pair_us) * 1e-6
+    print(f"[bench] event pair with nothing between: {pair_us:.2f} us (subtracted); dispatch share "
+          f"{share_us:.2f} us per launch ({launches_per_step:.0f} launches, net kernel time "
+          f"{net_step_us:.1f} of {1e3 * ms_per_step:.1f} us per step)", file=sys.stderr)
+    for k, (n, ms) in sorted(per_kind.items(), key=lambda kv_: -net_us[kv_[0]] * kv_[1][0]):
+        slot = net_us[k] + share_us
+        gbs = (bpl[k] / (slot * 1e-6) / 1e9) if k in bpl else float("nan")
+        print(f"[bench]   {kinds[k]:>14}: {n // steps_prof:3d}/step net {net_us[k]:8.2f} us, slot {slot:8.2f} us "
+              f"{gbs:8.1f} GB/s", file=sys.stderr)
+    dom = max((k for k in per_kind if k in bpl), key=lambda k: net_us[k] * per_kind[k][0])
+    n_dom = per_kind[dom][0]
+    avg_s = (net_us[dom] + share_us) * 1e-6
     achieved = bpl[dom] / avg_s / 1e9
+    traffic, traffic_src = traffic_from_profiles(wl.name, kinds[dom])
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": kinds[dom], "bytes_per_launch": int(bpl[dom]),
-                "avg_launch_us": round(avg_s * 1e6, 3), "event_pair_us": round(pair_us, 3),
-                "avg_launch_us_raw": round(ms_dom / n_dom * 1e3, 3)}
+                "avg_launch_us": round(avg_s * 1e6, 3), "net_launch_us": round(net_us[dom], 3),
+                "dispatch_share_us": round(share_us, 3), "event_pair_us": round(pair_us, 3),
+                "traffic_source": traffic_src}
 
     cpu = None
     if not args.no_cpu_baseline:

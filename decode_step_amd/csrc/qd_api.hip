@@ -74,7 +74,10 @@ struct DecodePlan {
 // with the largest chunk, which spreads the score and value arithmetic over
 // more CUs. Returns false when the context needs more splits than one merge
 // combines.
-constexpr int kAttnTargetWgs = 512;
+#ifndef QD_ATTN_TARGET
+#define QD_ATTN_TARGET 1024
+#endif
+constexpr int kAttnTargetWgs = QD_ATTN_TARGET;
 constexpr int kAttnMinWgs = 128;
 constexpr int kAttnMinChunk = 64;
 #ifndef QD_B1_CHUNK

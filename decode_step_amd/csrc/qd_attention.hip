@@ -41,6 +41,13 @@ constexpr int kAttnPassesGrouped = 4;
 constexpr int kMaxSplits = 64;
 constexpr int kAttnPage = 16;     // tokens per KV page (the only page size the library takes)
 constexpr float kLog2e = 1.4426950408889634f;
+// the matrix-core grouped kernel (attn_mfma_kernel)
+constexpr int kAmKeys = 32;      // keys per block
+constexpr int kAmWaves = 4;
+constexpr int kAmBlocksPerWave = 2;
+constexpr int kAmChunk = kAmWaves * kAmBlocksPerWave * kAmKeys;   // keys per split at most
+constexpr int kAmHeads = 16;     // query heads per workgroup at most (the MFMA's columns)
+
 
 // 2^x from the hardware exp2 (v_exp_f32); e^x = 2^(x log2 e)
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -49,6 +56,7 @@ template <int HD, typename KVT, int NP>
 constexpr int attn_chunk() { return NP * kAttnWaves * (kWave / (HD / VecN<KVT>::n)); }
 
 int attn_max_chunk(int hd, int kv_is_bf16, int grouped) {
+    if (grouped && kv_is_bf16) return kAmChunk;   // the matrix-core kernel (decode steps)
     if (grouped) {
         if (hd == 64) return kv_is_bf16 ? attn_chunk<64, uint16_t, kAttnPassesGrouped>() : attn_chunk<64, float, kAttnPassesGrouped>();
         return kv_is_bf16 ? attn_chunk<128, uint16_t, kAttnPassesGrouped>() : attn_chunk<128, float, kAttnPassesGrouped>();
@@ -377,11 +385,296 @@ void attn_wide_kernel(AttnArgs a) {
     attn_body<WT, KVT, HD, NP>(a);
 }
 
+// ---------------------------------------------------------------------------
+// Grouped decode attention on the matrix cores (bf16 KV cache, decode steps):
+// one workgroup takes every query head of one KV head (G <= 16) over one split
+// of the context, so each K/V row is read once, and the dot products run on
+// v_mfma_f32_16x16x32_bf16 instead of lane reductions.
+//
+// Scores, transposed: S^T[key][head] = K Q^T with K straight from the paged
+// cache as the A operand (a lane's 16-byte fragment is 8 consecutive dims of
+// one key row) and q as the B operand (head = column; columns past G are
+// zero). A lane then holds one head's scores for 4 keys of each 16-key half of
+// a 32-key block, and those 8 scores are directly its B fragment of P^T for the
+// product O^T[dim][head] = V^T P^T: the contraction runs over keys in the order
+// (4 keys of half 0, 4 of half 1) per lane, and the V^T fragment (A operand)
+// is read from LDS in that same key order. V is written into LDS transposed,
+// [dim][key], per wave. q and P are float32, each split into bf16 hi + lo and
+// multiplied twice (K and V are exact in bf16), keeping float32 accuracy.
+//
+// Each wave keeps an online softmax (m, l) per head over its blocks (Tang page,
+// section 2.2); the waves' states meet in LDS and the split publishes
+// (o, m, l) for the merge, or writes the context when it is the only split.
+// The new token's q/k norm, RoPE and KV append are as in attn_body.
+typedef __attribute__((ext_vector_type(8))) __bf16 am_bf16x8;
+typedef __attribute__((ext_vector_type(4))) float am_f32x4;
+__device__ __forceinline__ am_bf16x8 am_frag(uint4 v) { return __builtin_bit_cast(am_bf16x8, v); }
+
+
+template <typename WT, int HD>
+__global__ __launch_bounds__(kAmWaves * kWave) void attn_mfma_kernel(AttnArgs a) {
+    constexpr int NWV = kAmWaves, NBW = kAmBlocksPerWave;
+    constexpr int NT = NWV * kWave;
+    constexpr int KS = HD / 32;          // 32-dim slices of the score contraction
+    constexpr int DT = HD / 16;          // 16-dim tiles of the output
+    constexpr int VL = HD / 16;          // 16-byte V loads per lane per block (half a key row)
+    constexpr int VTS = kAmKeys + 8;     // u16 per transposed V row (padded)
+    constexpr int RS = HD + 4;           // floats per row of the wave-combine tile (padded)
+    constexpr int LPT = HD / 8;          // lanes per head row in the rotation (8 elements each)
+    constexpr int PG = kAttnPage;
+    constexpr int VT_BYTES = NWV * HD * VTS * 2;
+    static_assert(NWV * kAmHeads * RS * 4 <= VT_BYTES, "combine tile must fit the V tiles");
+    __shared__ __align__(16) char smem[VT_BYTES];       // V^T tiles, then the combine tile
+    __shared__ __align__(16) float qs[kAmHeads][HD];
+    __shared__ uint4 knew[LPT];
+    __shared__ uint4 vnew[LPT];
+    __shared__ int spage[kAmChunk / PG + 2];
+    __shared__ float2 wml[NWV][kAmHeads];
+
+    const int G = a.Hq / a.Hkv;
+    const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int p = a.pos[b];
+    if (p < 0 || p >= a.capacity || a.chunk > kAmChunk || G > kAmHeads) return;
+    const int T = p + 1;
+    const int ns = min(a.S, (T + a.chunk - 1) / a.chunk);
+    const int t_begin = s * a.chunk;
+    if (t_begin >= T) return;
+    const int t_end = min(T, t_begin + a.chunk);
+    const int n = t_end - t_begin;
+    const bool has_new = p >= t_begin && p < t_end;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+    const int c16 = lane & 15, q4 = lane >> 4;
+    const int* bt = a.block_table + (long)b * a.max_blocks;
+
+    // 1. loads of the q/k rotation: the G query heads of KV head g and, in the split
+    //    that holds position p, the new k (row G) and v
+    const int qkvr = (a.Hq + 2 * a.Hkv) * HD;
+    const int items = (G + (has_new ? 1 : 0)) * LPT;
+    const bool pro = tid < items;
+    const int phl = tid / LPT, pl2 = tid % LPT, plp2 = pl2 ^ (LPT / 2);
+    float u[8], up[8], cs[8], sn[8], vn[8];
+    if (pro) {
+        const float* src = a.qkv + (long)b * qkvr;
+        const float* hsrc = phl < G ? src + (g * G + phl) * HD : src + a.Hq * HD + g * HD;
+        load_f32xN(hsrc + pl2 * 8, u, 8);
+        load_f32xN(hsrc + plp2 * 8, up, 8);
+        const float2* tab = a.rope + (long)b * (HD / 2) + (pl2 % (LPT / 2)) * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { const float2 t = tab[e]; cs[e] = t.x; sn[e] = t.y; }
+        if (phl == G) load_f32xN(src + (a.Hq + a.Hkv) * HD + g * HD + pl2 * 8, vn, 8);
+    }
+
+    // 2. page ids of the split (an entry outside the pool reads as page 0, masked)
+    const int pg0 = t_begin / PG;
+    const int npg = (t_end - 1) / PG - pg0 + 1;
+    if (tid < npg) {
+        const int pg = bt[pg0 + tid];
+        spage[tid] = (pg >= 0 && pg < a.num_pages) ? pg : -1;
+    }
+    __syncthreads();
+
+    // 3. every K/V load of this wave's blocks (block wave + NWV j of the split): K as
+    //    A fragments (key half*16 + c16, dims 32 kk + 8 q4), V rows (key lane % 32,
+    //    dims (lane / 32) * HD/2 + 8 jj); a key past the split, at p or without a page
+    //    reads a valid row and is zeroed
+    uint4 kf[NBW][2][KS], vf[NBW][VL];
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) {
+        const int kb = wave + NWV * j;
+        const int kbase = t_begin + kb * kAmKeys;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int t = kbase + half * 16 + c16;
+            const int tt = t < t_end ? t : t_begin;
+            const int pg = spage[tt / PG - pg0];
+            const bool ok = t < t_end && t != p && pg >= 0;
+            const long off = (((long)max(pg, 0) * a.Hkv + g) * PG + (tt % PG)) * HD + 8 * q4;
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) {
+                const uint4 v = *(const uint4*)((const uint16_t*)a.k_cache + off + 32 * kk);
+                kf[j][half][kk] = ok ? v : make_uint4(0, 0, 0, 0);
+            }
+        }
+        {
+            const int t = kbase + (lane & 31);
+            const int tt = t < t_end ? t : t_begin;
+            const int pg = spage[tt / PG - pg0];
+            const bool ok = t < t_end && t != p && pg >= 0;
+            const long off = (((long)max(pg, 0) * a.Hkv + g) * PG + (tt % PG)) * HD + (lane >> 5) * (HD / 2);
+#pragma unroll
+            for (int jj = 0; jj < VL; ++jj) {
+                const uint4 v = *(const uint4*)((const uint16_t*)a.v_cache + off + 8 * jj);
+                vf[j][jj] = ok ? v : make_uint4(0, 0, 0, 0);
+            }
+        }
+    }
+
+    // 4. [per-head q/k RMSNorm] and RoPE; the new k and v rounded to bf16 go to LDS
+    //    and to the cache (this is the only workgroup of (sequence, KV head) whose
+    //    split holds p)
+    if (pro) {
+        if (a.qk_norm) {
+            float ss = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss += u[e] * u[e];
+            ss = group_sum<LPT>(ss);
+            const float r = 1.0f / sqrtf(ss / (float)HD + a.eps);
+            const void* gain = phl < G ? a.q_norm : a.k_norm;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                u[e] = u[e] * r * load_scalar<WT>(gain, pl2 * 8 + e);
+                up[e] = up[e] * r * load_scalar<WT>(gain, plp2 * 8 + e);
+            }
+        }
+        rope_lane<8>(u, up, cs, sn, pl2 < LPT / 2);
+        if (phl < G) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qs[phl][pl2 * 8 + e] = u[e];
+        } else {
+            const uint4 kst = pack16<uint16_t>(u), vst = pack16<uint16_t>(vn);
+            knew[pl2] = kst;
+            vnew[pl2] = vst;
+            const int page_id = bt[p / PG];
+            if (page_id >= 0 && page_id < a.num_pages) {
+                const long off = (((long)page_id * a.Hkv + g) * PG + (p % PG)) * HD + pl2 * 8;
+                *(uint4*)((uint16_t*)a.k_cache + off) = kst;
+                *(uint4*)((uint16_t*)a.v_cache + off) = vst;
+            }
+        }
+    }
+    __syncthreads();
+    if (has_new) {   // the new token's rows, in stored form, replace the (unread) cache rows
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) {
+            const int kbase = t_begin + (wave + NWV * j) * kAmKeys;
+#pragma unroll
+            for (int half = 0; half < 2; ++half)
+                if (kbase + half * 16 + c16 == p)
+#pragma unroll
+                    for (int kk = 0; kk < KS; ++kk) kf[j][half][kk] = knew[4 * kk + q4];
+            if (kbase + (lane & 31) == p)
+#pragma unroll
+                for (int jj = 0; jj < VL; ++jj) vf[j][jj] = vnew[(lane >> 5) * (HD / 16) + jj];
+        }
+    }
+
+    // 5. q^T as B fragments: head c16 (zero past G), dims 32 kk + 8 q4, bf16 hi + lo
+    uint4 qh[KS], ql[KS];
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = c16 < G ? qs[c16][32 * kk + 8 * q4 + e] : 0.f;
+        split_hi_lo(v, qh[kk], ql[kk]);
+    }
+
+    // 6. the wave's blocks: scores in base-2 units (s * log2 e, so that e^(s - m) is the
+    //    hardware exp2 of s' - m'), online softmax for head c16, O^T += V^T P^T
+    const float scale2 = a.scale * kLog2e;
+    float m = -INFINITY, l = 0.f;        // l: this lane's share (its keys of each block)
+    am_f32x4 o[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt] = am_f32x4{0.f, 0.f, 0.f, 0.f};
+    uint16_t* vtw = (uint16_t*)smem + wave * HD * VTS;
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) {
+        const int kb = wave + NWV * j;
+        if (kb * kAmKeys >= n) break;    // uniform over the wave
+        const int kbase = t_begin + kb * kAmKeys;
+        // V^T of the block into the wave's tile: vtw[dim][key]
+#pragma unroll
+        for (int jj = 0; jj < VL; ++jj) {
+            const uint32_t w4[4] = {vf[j][jj].x, vf[j][jj].y, vf[j][jj].z, vf[j][jj].w};
+            const int d0 = (lane >> 5) * (HD / 2) + 8 * jj;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                vtw[(d0 + 2 * e) * VTS + (lane & 31)] = (uint16_t)(w4[e] & 0xffffu);
+                vtw[(d0 + 2 * e + 1) * VTS + (lane & 31)] = (uint16_t)(w4[e] >> 16);
+            }
+        }
+        float sv[8];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            am_f32x4 sacc = am_f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) {
+                sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am_frag(kf[j][half][kk]), am_frag(qh[kk]), sacc, 0, 0, 0);
+                sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am_frag(kf[j][half][kk]), am_frag(ql[kk]), sacc, 0, 0, 0);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const bool valid = kbase + half * 16 + 4 * q4 + e < t_end;
+                sv[half * 4 + e] = valid ? sacc[e] * scale2 : -INFINITY;
+                mx = fmaxf(mx, sv[half * 4 + e]);
+            }
+        }
+        mx = swap32_max(swap16_max(mx));       // over the block's 32 keys
+        const float mn = fmaxf(m, mx);         // finite: key kbase is valid
+        const float alpha = exp2_hw(m - mn);   // 0 while m = -inf
+        float pv[8];
+        float ps = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            pv[i] = sv[i] == -INFINITY ? 0.f : exp2_hw(sv[i] - mn);
+            ps += pv[i];
+        }
+        l = fmaf(l, alpha, ps);
+        m = mn;
+        uint4 ph, pl;
+        split_hi_lo(pv, ph, pl);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            o[dt] *= alpha;
+            const uint16_t* row = vtw + (dt * 16 + c16) * VTS;
+            const uint2 v0 = *(const uint2*)(row + 4 * q4);
+            const uint2 v1 = *(const uint2*)(row + 16 + 4 * q4);
+            const uint4 vfr = make_uint4(v0.x, v0.y, v1.x, v1.y);
+            o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am_frag(vfr), am_frag(ph), o[dt], 0, 0, 0);
+            o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am_frag(vfr), am_frag(pl), o[dt], 0, 0, 0);
+        }
+    }
+
+    // 7. l over the lanes of head c16; the waves' (m, l, o) meet in LDS: M = max m_w,
+    //    weights 2^(m_w - M) (a wave without a block has m_w = -inf and weight 0)
+    l = strided_sum<16>(l);
+    __syncthreads();                       // every wave is done with its V tile
+    float* red = (float*)smem;             // [NWV][16][RS]: o^T of each wave, as [head][dim]
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+        *(float4*)(red + (wave * kAmHeads + c16) * RS + dt * 16 + 4 * q4) =
+            make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+    if (lane < kAmHeads) wml[wave][lane] = make_float2(m, l);
+    __syncthreads();
+    const int hq0 = g * G;
+    for (int idx = tid; idx < G * HD; idx += NT) {
+        const int hl = idx / HD, d = idx - hl * HD;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NWV; ++w) M = fmaxf(M, wml[w][hl].x);
+        float L = 0.f, O = 0.f;
+#pragma unroll
+        for (int w = 0; w < NWV; ++w) {
+            const float e = wml[w][hl].x == -INFINITY ? 0.f : exp2_hw(wml[w][hl].x - M);
+            L = fmaf(wml[w][hl].y, e, L);
+            O = fmaf(red[(w * kAmHeads + hl) * RS + d], e, O);
+        }
+        if (ns == 1 && !a.part_always) {
+            a.ctx[((long)b * a.Hq + hq0) * HD + idx] = O / L;
+        } else {   // publish (o, m, l) for the merge
+            const long pi = ((long)b * a.Hq + hq0 + hl) * a.S + s;
+            a.part[pi * HD + d] = O;
+            if (d == 0) a.part_ml[pi] = make_float2(M, L);
+        }
+    }
+}
+
 // Merge of the split partials of one (query head, sequence): M = max_s m_s,
 // ctx = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M) (the attention kernel keeps
 // m in base-2 units, so this is the e^(m_s - M) weighting). The 256 threads form
-// 256/hd groups that take every (256/hd)-th split, each with 16 partial loads
-// in flight; the groups' sums meet in LDS in a fixed order.
+// 256/hd groups that take every (256/hd)-th split: the first 32 of each group
+// are loaded together with the (m, l) pairs, any further ones 16 at a time; the
+// groups' sums meet in LDS in a fixed order.
 constexpr int kMergeThreads = 256;
 __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
     __shared__ float wgt[kMaxSplits];
@@ -395,6 +688,16 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
     const int hd = a.hd;
     const float* base = a.part + ((long)b * a.Hq + h) * a.S * hd;
     const float2* mlb = a.part_ml + ((long)b * a.Hq + h) * a.S;
+    const int ng = kMergeThreads / hd, grp = tid / hd, d = tid - grp * hd;
+    // the first 32 partials of this thread's group are loaded before anything waits,
+    // so they share one memory round trip with the (m, l) loads below
+    constexpr int kFirst = 32;
+    float v0[kFirst];
+#pragma unroll
+    for (int u = 0; u < kFirst; ++u) {
+        const int j = grp + u * ng;
+        v0[u] = base[(j < ns ? j : 0) * hd + d];
+    }
     if (tid < kWave) {   // wave 0: weights of the splits
         const float2 ml = mlb[tid < ns ? tid : 0];
         const float mj = tid < ns ? ml.x : -INFINITY;
@@ -406,9 +709,13 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
         if (tid == 0) lsum = l;
     }
     __syncthreads();
-    const int ng = kMergeThreads / hd, grp = tid / hd, d = tid - grp * hd;
     float o = 0.f;
-    for (int j0 = grp; j0 < ns; j0 += 16 * ng) {
+#pragma unroll
+    for (int u = 0; u < kFirst; ++u) {
+        const int j = grp + u * ng;
+        if (j < ns) o = fmaf(v0[u], wgt[j], o);
+    }
+    for (int j0 = grp + kFirst * ng; j0 < ns; j0 += 16 * ng) {
         float v[16];
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
@@ -434,6 +741,21 @@ hipError_t launch_attention(const AttnArgs& a, int w_is_bf16, int kv_is_bf16, hi
     if (a.page != kAttnPage) return hipErrorInvalidValue;
     const int G = a.Hq / a.Hkv;
     const int hgroups = (G + a.hpw - 1) / a.hpw;
+    const bool mfma = kv_is_bf16 && a.prefill_start < 0 && a.hpw == G && G <= kAmHeads &&
+                      (G + 1) * (a.hd / 8) <= kAmWaves * kWave && a.chunk <= kAmChunk &&
+                      (a.hd == 64 || a.hd == 128);
+    if (mfma) {
+        const dim3 grid(a.S, a.Hkv, a.B), block(kAmWaves * kWave);
+#define QD_AM(WT)                                                                             \
+        if (a.hd == 64) hipLaunchKernelGGL((attn_mfma_kernel<WT, 64>), grid, block, 0, s, a); \
+        else hipLaunchKernelGGL((attn_mfma_kernel<WT, 128>), grid, block, 0, s, a);
+        if (w_is_bf16) { QD_AM(uint16_t) } else { QD_AM(float) }
+#undef QD_AM
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess || a.S == 1 || a.part_always) return e;
+        hipLaunchKernelGGL(attn_merge_kernel, dim3(a.Hq, a.B), dim3(kMergeThreads), 0, s, a);
+        return hipGetLastError();
+    }
     dim3 grid(a.S, a.Hkv * hgroups, a.B);
     dim3 block(kAttnWaves * kWave);
 #define QD_ATTN(WT, KVT, HD)                                                                          \
