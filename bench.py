@@ -39,11 +39,20 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "decode tokens/s + achieved HBM GB/s (% of peak), Qwen2-0.5B-shape, batch 1/16"
 
 
+def _dtype_bytes(shape):
+    """(bytes per matrix element, extra bytes per matrix row, bytes per gain or bias
+    element): int8 matrices carry a float32 scale per row and bf16 gains/biases."""
+    if shape.w_dtype == "i8":
+        return 1, 4, 2
+    wb = 2 if shape.w_dtype == "bf16" else 4
+    return wb, 0, wb
+
+
 def _bytes_per_launch(shape, B, ctx):
     """Algorithmic bytes per launch of each kernel kind: weights read once, KV read
     once, activations counted at their float32 size."""
     from decode_step_amd import qd as Q
-    wb = 2 if shape.w_dtype == "bf16" else 4
+    wb, rb, gb = _dtype_bytes(shape)
     kvb = 2 if shape.kv_dtype == "bf16" else 4
     D, F, V = shape.hidden, shape.ffn, shape.vocab
     qd_, kvd = shape.q_dim, shape.kv_dim
@@ -51,12 +60,12 @@ def _bytes_per_launch(shape, B, ctx):
     kv_tokens = int(np.sum(ctx + 1))
     act = 4
     out = {
-        Q.QD_K_QKV: qkvr * D * wb + (qkvr * wb if shape.qkv_bias else 0) + D * wb + B * (D + qkvr) * act,
+        Q.QD_K_QKV: qkvr * (D * wb + rb) + (qkvr * gb if shape.qkv_bias else 0) + D * gb + B * (D + qkvr) * act,
         Q.QD_K_ATTN: kv_tokens * 2 * kvd * kvb + B * qd_ * act,
-        Q.QD_K_O: D * qd_ * wb + B * (qd_ + 2 * D) * act,
-        Q.QD_K_GATEUP: 2 * F * D * wb + D * wb + B * (D + F) * act,
-        Q.QD_K_DOWN: D * F * wb + B * (F + 2 * D) * act,
-        Q.QD_K_LMHEAD: V * D * wb + D * wb + B * (D + V) * act,
+        Q.QD_K_O: D * (qd_ * wb + rb) + B * (qd_ + 2 * D) * act,
+        Q.QD_K_GATEUP: 2 * F * (D * wb + rb) + D * gb + B * (D + F) * act,
+        Q.QD_K_DOWN: D * (F * wb + rb) + B * (F + 2 * D) * act,
+        Q.QD_K_LMHEAD: V * (D * wb + rb) + D * gb + B * (D + V) * act,
     }
     return out
 
@@ -64,15 +73,20 @@ def _bytes_per_launch(shape, B, ctx):
 def step_bytes(shape, B, ctx):
     """Algorithmic bytes of one whole step (every weight once, every cached K/V once,
     the new K/V written, the embedding rows and the logits)."""
-    wb = 2 if shape.w_dtype == "bf16" else 4
+    wb, rb, gb = _dtype_bytes(shape)
     kvb = 2 if shape.kv_dtype == "bf16" else 4
     c = shape.param_counts()
-    # every parameter once, except that an untied embedding table is only gathered
-    # (B rows, counted below); a tied table is read whole as the lm_head
-    weights = (c["total"] - (0 if shape.tied else shape.vocab * shape.hidden)) * wb
+    D, F, V, L = shape.hidden, shape.ffn, shape.vocab, shape.n_layers
+    # matrices (and their rows), then norm gains and biases; every parameter once,
+    # except that an untied embedding table is only gathered (B rows, counted below);
+    # a tied table is read whole as the lm_head
+    bias = L * (shape.q_dim + 2 * shape.kv_dim) if shape.qkv_bias else 0
+    mat = c["total"] - c["norms"] - bias - (0 if shape.tied else V * D)
+    rows = L * (shape.q_dim + 2 * shape.kv_dim + D + 2 * F + D) + V
+    weights = mat * wb + rows * rb + (c["norms"] + bias) * gb
     kv_read = int(np.sum(ctx)) * shape.n_layers * 2 * shape.kv_dim * kvb
     kv_write = B * shape.n_layers * 2 * shape.kv_dim * kvb
-    emb_rows = B * shape.hidden * wb
+    emb_rows = B * (D * wb + rb)
     logits = B * shape.vocab * 4
     return weights + kv_read + kv_write + emb_rows + logits
 
@@ -268,6 +282,13 @@ def main():
     ctx = synth.make_ctx(wl.batch, wl.past, wl.ctx_range, wl.seed)
     B = wl.batch
     w = synth.make_weights(shape, seed=wl.seed, device=dev)
+    host_w = None
+    if shape.w_dtype == "i8":   # the bf16 draw through the library's int8 quantizer
+        from decode_step_amd.runner import quantize_weights_int8
+        if not args.no_cpu_baseline:
+            host_w = synth.weights_to_host(w)
+        w = quantize_weights_int8(w)
+        torch.cuda.synchronize()
     kv = synth.make_kv(shape, ctx, extra=2, seed=wl.seed, device=dev, random_order=wl.paged_random)
     runner = DecodeRunner(shape, w, kv.k, kv.v, kv.block_table, max_batch=B, max_ctx=int(ctx.max()) + 2,
                           device=dev)
@@ -382,13 +403,19 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        case_host = (synth.weights_to_host(w), [synth.to_host_bits(t).copy() for t in kv.k],
+        if shape.w_dtype == "i8":   # the oracle runs the same codes dequantized
+            from oracle.quant import quantized_model
+            hw = quantized_model(host_w)[0]
+        else:
+            hw = synth.weights_to_host(w)
+        case_host = (hw, [synth.to_host_bits(t).copy() for t in kv.k],
                      [synth.to_host_bits(t).copy() for t in kv.v], kv.block_table)
         cpu = cpu_baseline(wl, case_host, ctx, tokens)
 
     rec = {"metric": METRIC, "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
-           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "int8w" if shape.w_dtype == "i8" else ("f32" if shape.w_dtype == "f32" else "bf16"),
            "data": "synthetic",
            "config": {"workload": wl.name, "batch": B, "past": int(ctx.max()) if wl.past else None,
                       "ctx_range": list(wl.ctx_range) if wl.ctx_range else None},

@@ -52,8 +52,11 @@ qd_status check_config(const qd_config* c) {
     if (c->n_q_heads / c->n_kv_heads > 8)
         return fail(QD_ESHAPE, "group %d > 8", c->n_q_heads / c->n_kv_heads);
     if (c->page_size != 16) return fail(QD_ESHAPE, "page_size %d != 16", c->page_size);
-    if ((c->w_dtype != QD_F32 && c->w_dtype != QD_BF16) || (c->kv_dtype != QD_F32 && c->kv_dtype != QD_BF16))
+    if ((c->w_dtype != QD_F32 && c->w_dtype != QD_BF16 && c->w_dtype != QD_I8) ||
+        (c->kv_dtype != QD_F32 && c->kv_dtype != QD_BF16))
         return fail(QD_EINVAL, "dtype out of range (w %d kv %d)", c->w_dtype, c->kv_dtype);
+    if (c->w_dtype == QD_I8 && (c->hidden % 16 || c->ffn % 16))
+        return fail(QD_ESHAPE, "int8 weights need hidden (%d) and ffn (%d) multiples of 16", c->hidden, c->ffn);
     if (!(c->rms_eps > 0.f) || !(c->rope_theta > 0.f))
         return fail(QD_ESHAPE, "rms_eps and rope_theta must be > 0");
     return QD_OK;
@@ -231,6 +234,11 @@ qd_status check_layer(const qd_config* c, const qd_layer* L, int l) {
     }
     if (c->qk_norm && (!L->q_norm || !L->k_norm))
         return fail(QD_EINVAL, "layer %d: qk_norm set but q_norm/k_norm NULL", l);
+    if (c->w_dtype == QD_I8) {
+        const float* sc[] = {L->s_q, L->s_k, L->s_v, L->s_o, L->s_gate, L->s_up, L->s_down};
+        for (const float* p : sc)
+            if (!p || ((uintptr_t)p & 3u)) return fail(QD_EINVAL, "layer %d: int8 row scales NULL or misaligned", l);
+    }
     const void* opt[] = {L->bq, L->bk, L->bv, L->q_norm, L->k_norm};
     for (const void* p : opt)
         if (p && !aligned4(p)) return fail(QD_EALIGN, "layer %d: bias/gain not 4-byte aligned", l);
@@ -305,6 +313,11 @@ qd_status qd_decode_step(const qd_config* cfg, const qd_weights* w, const qd_kv*
     if (want_head && !aligned16(w->lm_head)) return fail(QD_EALIGN, "lm_head not 16-byte aligned");
     for (int l = 0; l < c.n_layers; ++l)
         if ((st = check_layer(cfg, &w->layers_host[l], l)) != QD_OK) return st;
+    if (c.w_dtype == QD_I8) {
+        if (batch != 1) return fail(QD_EUNSUPPORTED, "int8 weights: batch-1 decode steps only (batch %d)", batch);
+        if (tokens && !w->s_embed) return fail(QD_EINVAL, "int8 weights: s_embed is NULL");
+        if (want_head && !w->s_lm_head) return fail(QD_EINVAL, "int8 weights: s_lm_head is NULL");
+    }
     int max_tokens = 0;
     if ((st = check_kv_positions(cfg, kv, batch, pos_host, &max_tokens)) != QD_OK) return st;
     for (int l = 0; l < c.n_layers; ++l) {
@@ -336,11 +349,12 @@ qd_status qd_decode_step(const qd_config* cfg, const qd_weights* w, const qd_kv*
     float* lg = logits ? logits : (float*)(ws + P.off_logits);
     float* pv = (float*)(ws + P.off_pv);
     int* pi = (int*)(ws + P.off_pi);
-    const int wbf = c.w_dtype == QD_BF16, kvbf = c.kv_dtype == QD_BF16;
+    // wbf: bf16 gains and biases (bf16 or int8 matrices); wty: the GEMV's weight type
+    const int wbf = c.w_dtype != QD_F32, kvbf = c.kv_dtype == QD_BF16, wty = c.w_dtype;
     const int B = batch, D = P.D;
     const int cap = kv->max_blocks * c.page_size;
     auto gemv = [&](const qd::GemvArgs& g, int epi, int grid_cap, int* grid_out) {
-        if (B == 1) return qd::launch_gemv1(g, wbf, epi, epi == qd::EPI_LOGITS ? grid_cap : kGemv1GridCap,
+        if (B == 1) return qd::launch_gemv1(g, wty, epi, epi == qd::EPI_LOGITS ? grid_cap : kGemv1GridCap,
                                             grid_out, s);
         if (wbf) {
             qd::GemvArgs m = g;
@@ -351,9 +365,10 @@ qd_status qd_decode_step(const qd_config* cfg, const qd_weights* w, const qd_kv*
     };
 
     qd::StepInputArgs si{};
-    si.tokens = tokens; si.embed = w->embed; si.x_in = x_in; si.x = x; si.pos = pos; si.rope = rope;
+    si.tokens = tokens; si.embed = w->embed; si.embed_scale = w->s_embed; si.x_in = x_in; si.x = x;
+    si.pos = pos; si.rope = rope;
     si.B = B; si.D = D; si.V = c.vocab; si.hd = P.hd; si.theta = c.rope_theta;
-    QD_LAUNCH_K(QD_K_EMBED, qd::launch_step_input(si, wbf, s), "step input");
+    QD_LAUNCH_K(QD_K_EMBED, qd::launch_step_input(si, wty, s), "step input");
 
     for (int l = 0; l < c.n_layers; ++l) {
         const qd_layer& L = w->layers_host[l];
@@ -362,6 +377,7 @@ qd_status qd_decode_step(const qd_config* cfg, const qd_weights* w, const qd_kv*
         g.w[0] = L.wq; g.w[1] = L.wk; g.w[2] = L.wv;
         g.bias[0] = L.bq; g.bias[1] = L.bk; g.bias[2] = L.bv;
         g.seg_end[0] = P.Hq * P.hd; g.seg_end[1] = (P.Hq + P.Hkv) * P.hd; g.seg_end[2] = P.qkvr;
+        g.wscale[0] = L.s_q; g.wscale[1] = L.s_k; g.wscale[2] = L.s_v;
         g.nseg = 3; g.N = P.qkvr; g.K = D; g.B = B; g.x = x; g.gain = L.attn_norm; g.eps = c.rms_eps;
         g.y = qkv; g.kt = gemv_kt(B, D);
         QD_LAUNCH_K(QD_K_QKV, gemv(g, qd::EPI_STORE, kGemvGridCap, nullptr), "qkv gemv");
@@ -378,7 +394,7 @@ qd_status qd_decode_step(const qd_config* cfg, const qd_weights* w, const qd_kv*
         QD_LAUNCH_K(QD_K_ATTN, qd::launch_attention(at, wbf, kvbf, s), "attention");
         // o_proj + residual
         qd::GemvArgs go{};
-        go.w[0] = L.wo; go.seg_end[0] = go.seg_end[1] = go.seg_end[2] = D; go.nseg = 1;
+        go.w[0] = L.wo; go.wscale[0] = L.s_o; go.seg_end[0] = go.seg_end[1] = go.seg_end[2] = D; go.nseg = 1;
         go.N = D; go.K = P.Hq * P.hd; go.B = B; go.x = ctx; go.gain = nullptr; go.y = x;
         go.kt = gemv_kt(B, go.K);
         if (merge_in_o) {   // the context is merged from the attention's splits here
@@ -388,13 +404,14 @@ qd_status qd_decode_step(const qd_config* cfg, const qd_weights* w, const qd_kv*
         QD_LAUNCH_K(QD_K_O, gemv(go, qd::EPI_RESID, kGemvGridCap, nullptr), "o_proj gemv");
         // RMSNorm -> gate|up GEMV -> SwiGLU
         qd::GemvArgs gu{};
-        gu.w[0] = L.w_gate; gu.w[1] = L.w_up; gu.seg_end[0] = gu.seg_end[1] = gu.seg_end[2] = P.F;
+        gu.w[0] = L.w_gate; gu.w[1] = L.w_up; gu.wscale[0] = L.s_gate; gu.wscale[1] = L.s_up;
+        gu.seg_end[0] = gu.seg_end[1] = gu.seg_end[2] = P.F;
         gu.nseg = 1; gu.N = P.F; gu.K = D; gu.B = B; gu.x = x; gu.gain = L.mlp_norm; gu.eps = c.rms_eps;
         gu.y = h; gu.kt = gemv_kt(B, D);
         QD_LAUNCH_K(QD_K_GATEUP, gemv(gu, qd::EPI_SWIGLU, kGemvGridCap, nullptr), "gate/up gemv");
         // down + residual
         qd::GemvArgs gd{};
-        gd.w[0] = L.w_down; gd.seg_end[0] = gd.seg_end[1] = gd.seg_end[2] = D; gd.nseg = 1;
+        gd.w[0] = L.w_down; gd.wscale[0] = L.s_down; gd.seg_end[0] = gd.seg_end[1] = gd.seg_end[2] = D; gd.nseg = 1;
         gd.N = D; gd.K = P.F; gd.B = B; gd.x = h; gd.gain = nullptr; gd.y = x; gd.kt = gemv_kt(B, P.F);
         QD_LAUNCH_K(QD_K_DOWN, gemv(gd, qd::EPI_RESID, kGemvGridCap, nullptr), "down gemv");
         if (layer_out) QD_LAUNCH(qd::launch_copy(x, layer_out + (size_t)l * B * D, (long)B * D, s), "layer_out copy");
@@ -402,13 +419,26 @@ qd_status qd_decode_step(const qd_config* cfg, const qd_weights* w, const qd_kv*
     if (x_out) QD_LAUNCH(qd::launch_copy(x, x_out, (long)B * D, s), "x_out copy");
     if (want_head) {
         qd::GemvArgs gl{};
-        gl.w[0] = w->lm_head; gl.seg_end[0] = gl.seg_end[1] = gl.seg_end[2] = c.vocab; gl.nseg = 1;
+        gl.w[0] = w->lm_head; gl.wscale[0] = w->s_lm_head; gl.seg_end[0] = gl.seg_end[1] = gl.seg_end[2] = c.vocab;
+        gl.nseg = 1;
         gl.N = c.vocab; gl.K = D; gl.B = B; gl.x = x; gl.gain = w->final_norm; gl.eps = c.rms_eps;
         gl.y = lg; gl.part_val = pv; gl.part_idx = pi; gl.kt = gemv_kt(B, D);
         int grid = 0;
         QD_LAUNCH_K(QD_K_LMHEAD, gemv(gl, qd::EPI_LOGITS, kLogitsGridCap, &grid), "lm_head gemv");
         if (next_tokens) QD_LAUNCH_K(QD_K_ARGMAX, qd::launch_argmax(pv, pi, grid, next_tokens, B, s), "argmax");
     }
+    return QD_OK;
+}
+
+qd_status qd_quantize_rows_int8(const void* w, int32_t w_dtype, int64_t rows, int32_t cols, int8_t* q,
+                                float* scale, void* stream) {
+    if (!w || !q || !scale) return fail(QD_EINVAL, "w, q or scale is NULL");
+    if (w_dtype != QD_F32 && w_dtype != QD_BF16) return fail(QD_EINVAL, "w_dtype %d not F32 or BF16", w_dtype);
+    if (rows < 1 || rows > 0x7fffffffLL || cols < 16 || cols % 16)
+        return fail(QD_ESHAPE, "rows %lld / cols %d (cols a positive multiple of 16)", (long long)rows, cols);
+    if (!aligned16(w) || !aligned16(q) || !aligned16(scale)) return fail(QD_EALIGN, "w, q or scale not 16-byte aligned");
+    hipStream_t s = (hipStream_t)stream;
+    QD_LAUNCH(qd::launch_quantize_rows(w, w_dtype == QD_BF16, (long)rows, cols, q, scale, s), "quantize");
     return QD_OK;
 }
 

@@ -793,7 +793,12 @@ __global__ __launch_bounds__(256) void step_input_kernel(StepInputArgs a) {
         const int tok = a.tokens[b];
         const bool ok = tok >= 0 && tok < a.V;
         const void* row = (const char*)a.embed + (ok ? (long)tok * a.D * (long)sizeof(WT) : 0L);
-        for (int d = tid; d < a.D; d += blockDim.x) x[d] = ok ? load_scalar<WT>(row, d) : 0.f;
+        if constexpr (sizeof(WT) == 1) {   // int8 row times its scale (nanoinfer, phase 6)
+            const float sc = ok ? a.embed_scale[tok] : 0.f;
+            for (int d = tid; d < a.D; d += blockDim.x) x[d] = (float)((const int8_t*)row)[d] * sc;
+        } else {
+            for (int d = tid; d < a.D; d += blockDim.x) x[d] = ok ? load_scalar<WT>(row, d) : 0.f;
+        }
     } else {
         for (int d = tid; d < a.D; d += blockDim.x) x[d] = a.x_in[(long)b * a.D + d];
     }
@@ -810,8 +815,9 @@ __global__ __launch_bounds__(256) void step_input_kernel(StepInputArgs a) {
     }
 }
 
-hipError_t launch_step_input(const StepInputArgs& a, int w_is_bf16, hipStream_t s) {
-    if (w_is_bf16) hipLaunchKernelGGL((step_input_kernel<uint16_t>), dim3(a.B), dim3(256), 0, s, a);
+hipError_t launch_step_input(const StepInputArgs& a, int w_type, hipStream_t s) {
+    if (w_type == 2) hipLaunchKernelGGL((step_input_kernel<int8_t>), dim3(a.B), dim3(256), 0, s, a);
+    else if (w_type == 1) hipLaunchKernelGGL((step_input_kernel<uint16_t>), dim3(a.B), dim3(256), 0, s, a);
     else hipLaunchKernelGGL((step_input_kernel<float>), dim3(a.B), dim3(256), 0, s, a);
     return hipGetLastError();
 }

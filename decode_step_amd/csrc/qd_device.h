@@ -23,6 +23,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 template <typename T> struct VecN;
 template <> struct VecN<uint16_t> { static constexpr int n = 8; };
 template <> struct VecN<float> { static constexpr int n = 4; };
+template <> struct VecN<int8_t> { static constexpr int n = 16; };
+
+// Type of the norm gains and biases that go with a weight type: int8 matrices
+// keep their gains and biases in bf16.
+template <typename WT> struct GainT { using type = WT; };
+template <> struct GainT<int8_t> { using type = uint16_t; };
 
 // Widen one 16-byte vector of T into floats.
 __device__ __forceinline__ void widen16(const uint4 v, float (&f)[8]) {
@@ -30,6 +36,13 @@ __device__ __forceinline__ void widen16(const uint4 v, float (&f)[8]) {
     f[2] = __uint_as_float(v.y << 16); f[3] = __uint_as_float(v.y & 0xffff0000u);
     f[4] = __uint_as_float(v.z << 16); f[5] = __uint_as_float(v.z & 0xffff0000u);
     f[6] = __uint_as_float(v.w << 16); f[7] = __uint_as_float(v.w & 0xffff0000u);
+}
+__device__ __forceinline__ void widen16(const uint4 v, float (&f)[16]) {   // int8, sign-extended
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) f[4 * i + b] = (float)(int8_t)(w[i] >> (8 * b));
 }
 __device__ __forceinline__ void widen16(const uint4 v, float (&f)[4]) {
     f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);

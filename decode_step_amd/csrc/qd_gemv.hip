@@ -35,6 +35,8 @@ constexpr int kCus = 256;
 __host__ __device__ constexpr int gemv1_xpad(int K) { return (K + 255) & ~255; }
 // bytes of gain staged in LDS (whole 1 KB blocks)
 __host__ __device__ constexpr int gemv1_gpad(int K, int wbytes) { return (K * wbytes + 1023) & ~1023; }
+// floats of zeros staged behind x (one chunk of the widest weight type, int8's 16)
+constexpr int kG1Zeros = 16;
 
 // Splits of the decode attention that the residual product can merge itself
 // (MS > 0: x is formed from the attention's partials, at most MS of them).
@@ -43,11 +45,13 @@ constexpr int kG1MergeHeads = 32;
 template <typename WT, int LPR, int WK, int UR, int CPL, int EPI, int MS = 0>
 __global__ __launch_bounds__(256) void gemv1_kernel(GemvArgs a) {
     constexpr int CE = VecN<WT>::n;
+    using GT = typename GainT<WT>::type;      // gains and biases
+    constexpr bool I8 = sizeof(WT) == 1;      // int8 rows carry a float scale each
     constexpr int RPW = kWave / LPR;
     constexpr int WR = 4 / WK;
     constexpr int RPT = WR * RPW * UR;
     constexpr int NW = (EPI == EPI_SWIGLU) ? 2 : 1;
-    extern __shared__ __align__(16) float xs[];   // x (then x * g) [xpad] | zeros [8] | gain [gpad bytes]
+    extern __shared__ __align__(16) float xs[];   // x (then x * g) [xpad] | zeros [16] | gain [gpad bytes]
     __shared__ float wsum[4];
     __shared__ float red[WK][RPT][NW];
     __shared__ float red_v[4];
@@ -62,10 +66,11 @@ __global__ __launch_bounds__(256) void gemv1_kernel(GemvArgs a) {
     const int ntiles = (N + RPT - 1) / RPT;
     const int xpad = gemv1_xpad(K);
     const int cz = xpad / CE;                 // chunk index of the zero block
-    float* gs = xs + xpad + 8;
+    float* gs = xs + xpad + kG1Zeros;
 
     gbyte* wseg[3] = {sgpr_gptr(a.w[0]), sgpr_gptr(a.w[1]), sgpr_gptr(a.w[2])};
     gbyte* bseg[3] = {sgpr_gptr(a.bias[0]), sgpr_gptr(a.bias[1]), sgpr_gptr(a.bias[2])};
+    gbyte* sseg[3] = {sgpr_gptr(a.wscale[0]), sgpr_gptr(a.wscale[1]), sgpr_gptr(a.wscale[2])};
     auto wptr = [&](int r, int n) -> gbyte* {   // r < N
         if (EPI == EPI_SWIGLU) return wseg[n] + (long)r * K * (long)sizeof(WT);
         const bool s0 = r < a.seg_end[0], s1 = r < a.seg_end[1];
@@ -76,6 +81,11 @@ __global__ __launch_bounds__(256) void gemv1_kernel(GemvArgs a) {
     uint4 wv[UR][NW][CPL];
     float pre[UR] = {};   // RESID: the residual row; STORE: the bias, times psc (0 without one)
     float psc[UR] = {};
+    float srow[UR][NW];   // int8: the rows' scales (1 otherwise)
+#pragma unroll
+    for (int u = 0; u < UR; ++u)
+#pragma unroll
+        for (int n = 0; n < NW; ++n) srow[u][n] = 1.f;
     auto issue = [&](int tile, int cbase, bool first) {
 #pragma unroll
         for (int u = 0; u < UR; ++u) {
@@ -97,8 +107,20 @@ __global__ __launch_bounds__(256) void gemv1_kernel(GemvArgs a) {
                 const int base = s0 ? 0 : (s1 ? a.seg_end[0] : a.seg_end[1]);
                 // without a bias: load a valid weight and scale it by 0 (the scale is
                 // applied in the epilogue, so nothing waits for this load before then)
-                pre[u] = gld_scalar<WT>(bsel ? bsel : wseg[0], bsel ? rr - base : 0);
+                pre[u] = gld_scalar<GT>(bsel ? bsel : wseg[0], bsel ? rr - base : 0);
                 psc[u] = bsel ? 1.f : 0.f;
+            }
+            if (first && I8) {
+#pragma unroll
+                for (int n = 0; n < NW; ++n) {
+                    if (EPI == EPI_SWIGLU) {
+                        srow[u][n] = gld_scalar<float>(sseg[n], rr);
+                    } else {
+                        const bool s0 = rr < a.seg_end[0], s1 = rr < a.seg_end[1];
+                        gbyte* ssel = s0 ? sseg[0] : (s1 ? sseg[1] : sseg[2]);
+                        srow[u][n] = gld_scalar<float>(ssel, rr - (s0 ? 0 : (s1 ? a.seg_end[0] : a.seg_end[1])));
+                    }
+                }
             }
         }
     };
@@ -136,11 +158,11 @@ __global__ __launch_bounds__(256) void gemv1_kernel(GemvArgs a) {
             lds_dma16(a.x + f, __builtin_amdgcn_readfirstlane(xl + j * 1024));
         }
         if (a.gain) {
-            constexpr int GE = 16 / (int)sizeof(WT);      // gain elements per lane
+            constexpr int GE = 16 / (int)sizeof(GT);      // gain elements per lane
             const uint32_t gl = lds_addr(gs);
-            for (int j = wave; j < gemv1_gpad(K, sizeof(WT)) / 1024; j += 4) {
+            for (int j = wave; j < gemv1_gpad(K, sizeof(GT)) / 1024; j += 4) {
                 const int e = min(j * 64 * GE + lane * GE, K - GE);
-                lds_dma16((const WT*)a.gain + e, __builtin_amdgcn_readfirstlane(gl + j * 1024));
+                lds_dma16((const GT*)a.gain + e, __builtin_amdgcn_readfirstlane(gl + j * 1024));
             }
         }
     }
@@ -190,7 +212,7 @@ __global__ __launch_bounds__(256) void gemv1_kernel(GemvArgs a) {
         for (int k4 = tid; k4 < K / 4; k4 += 256) {
             float4 v = ((const float4*)xs)[k4];
             float g[4];
-            if (sizeof(WT) == 2) {
+            if (sizeof(GT) == 2) {
                 const uint2 gb = ((const uint2*)gs)[k4];
                 g[0] = __uint_as_float(gb.x << 16); g[1] = __uint_as_float(gb.x & 0xffff0000u);
                 g[2] = __uint_as_float(gb.y << 16); g[3] = __uint_as_float(gb.y & 0xffff0000u);
@@ -205,7 +227,7 @@ __global__ __launch_bounds__(256) void gemv1_kernel(GemvArgs a) {
         ss = group_sum<kWave>(ss);
         if (lane == 0) wsum[wave] = ss;
     }
-    if (tid < 8) xs[xpad + tid] = 0.f;
+    if (tid < kG1Zeros) xs[xpad + tid] = 0.f;
     lds_barrier();
     const float rscale = a.gain ? 1.0f / sqrtf((wsum[0] + wsum[1] + wsum[2] + wsum[3]) / (float)K + a.eps) : 1.0f;
 
@@ -240,9 +262,13 @@ __global__ __launch_bounds__(256) void gemv1_kernel(GemvArgs a) {
                     }
             }
         }
-        float cur[UR], csc[UR];
+        float cur[UR], csc[UR], cs_[UR][NW];
 #pragma unroll
-        for (int u = 0; u < UR; ++u) { cur[u] = pre[u]; csc[u] = psc[u]; }
+        for (int u = 0; u < UR; ++u) {
+            cur[u] = pre[u]; csc[u] = psc[u];
+#pragma unroll
+            for (int n = 0; n < NW; ++n) cs_[u][n] = srow[u][n];
+        }
         const int this_tile = tile;
         const int next = tile + gridDim.x;
         if (next < ntiles) issue(next, kc0, true);
@@ -272,10 +298,11 @@ __global__ __launch_bounds__(256) void gemv1_kernel(GemvArgs a) {
 #pragma unroll
         for (int u = 0; u < UR; ++u) {
             const int r = this_tile * RPT + (wr * UR + u) * RPW + slot;
-            const float v0 = acc[u][0] * rscale;
+            const float v0 = I8 ? acc[u][0] * cs_[u][0] * rscale : acc[u][0] * rscale;
             float out;
             if (EPI == EPI_STORE || EPI == EPI_RESID) out = fmaf(cur[u], csc[u], v0);
-            else if (EPI == EPI_SWIGLU) out = silu(v0) * (acc[u][NW - 1] * rscale);
+            else if (EPI == EPI_SWIGLU)
+                out = silu(v0) * (I8 ? acc[u][NW - 1] * cs_[u][NW - 1] * rscale : acc[u][NW - 1] * rscale);
             else out = v0;
             if (wk == 0 && li == 0 && r < N) {
                 a.y[r] = out;
@@ -298,19 +325,27 @@ __global__ __launch_bounds__(256) void gemv1_kernel(GemvArgs a) {
 
 // (LPR, WK, UR, CPL) shapes compiled; every one handles any K and N. RPT rows per
 // workgroup tile = (4 / WK) * (64 / LPR) * UR; one pass over K covers
-// CPL * LPR * WK * 8 columns (more take further passes, each a memory round trip).
+// CPL * LPR * WK 16-byte chunks (8 bf16 or 16 int8 columns each; more take
+// further passes, each a memory round trip). The first G_NCFG serve float and
+// bf16 rows; int8 rows, whose chunks hold twice the columns, take their own
+// shapes sized to the 0.5B rows (56 chunks at K = 896, 304 at K = 4864) so that
+// few lanes idle.
 struct Gemv1Shape { int lpr, wk, ur, cpl; };
 enum Gemv1Cfg { G_SMALLK_FEWROWS = 0, G_SMALLK = 1, G_SMALLK_UR2 = 2, G_BIGK_FEWROWS = 3, G_BIGK = 4,
-                G_BIGK_UR2 = 5, G_SMALLK_8 = 6, G_LONGK_4 = 7, G_NCFG = 8 };
-constexpr Gemv1Shape kGemv1Shapes[G_NCFG] = {
+                G_BIGK_UR2 = 5, G_SMALLK_8 = 6, G_LONGK_4 = 7, G_NCFG = 8,
+                G_I8_WIDE = 8, G_I8_NARROW = 9, G_I8_LONGK = 10, G_I8_MID = 11, G_I8_MID2 = 12, G_NALL = 13 };
+constexpr Gemv1Shape kGemv1Shapes[G_NALL] = {
     {16, 4, 1, 2}, {16, 1, 1, 8}, {16, 1, 2, 8}, {32, 4, 1, 6}, {64, 1, 1, 8}, {64, 1, 2, 8}, {16, 2, 1, 4},
-    {16, 4, 1, 10}};
+    {16, 4, 1, 10},
+    {8, 1, 2, 7}, {8, 4, 1, 2}, {16, 4, 1, 5}, {8, 1, 1, 7}, {16, 1, 2, 4}};
 constexpr int gemv1_rpt(int c) { return (4 / kGemv1Shapes[c].wk) * (64 / kGemv1Shapes[c].lpr) * kGemv1Shapes[c].ur; }
-constexpr int gemv1_kpass(int c) { return kGemv1Shapes[c].cpl * kGemv1Shapes[c].lpr * kGemv1Shapes[c].wk * 8; }
+// columns one pass covers, for CE weight elements per 16-byte chunk
+constexpr int gemv1_kpass(int c, int ce = 8) { return kGemv1Shapes[c].cpl * kGemv1Shapes[c].lpr * kGemv1Shapes[c].wk * ce; }
 
 template <typename WT, int EPI, int MS = 0>
 static hipError_t gemv1_dispatch(const GemvArgs& a, int cfg, int* grid_out, int grid_cap, hipStream_t s) {
-    const size_t shm = (size_t)(gemv1_xpad(a.K) + 8) * sizeof(float) + (a.gain ? gemv1_gpad(a.K, sizeof(WT)) : 0);
+    using GT = typename GainT<WT>::type;
+    const size_t shm = (size_t)(gemv1_xpad(a.K) + kG1Zeros) * sizeof(float) + (a.gain ? gemv1_gpad(a.K, sizeof(GT)) : 0);
     auto go = [&](auto kern, int rpt) {
         if (shm > 65536 && hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm) != hipSuccess)
             return hipErrorInvalidValue;
@@ -322,7 +357,19 @@ static hipError_t gemv1_dispatch(const GemvArgs& a, int cfg, int* grid_out, int 
     };
 #define QD_G1C(C) \
     case C: return go(gemv1_kernel<WT, kGemv1Shapes[C].lpr, kGemv1Shapes[C].wk, kGemv1Shapes[C].ur, kGemv1Shapes[C].cpl, EPI, MS>, gemv1_rpt(C));
-    if constexpr (MS > 0) {
+    if constexpr (sizeof(WT) == 1) {
+        if constexpr (MS > 0) {
+            switch (cfg) {
+                QD_G1C(G_I8_NARROW)
+                default: return hipErrorInvalidValue;
+            }
+        } else {
+            switch (cfg) {
+                QD_G1C(G_I8_WIDE) QD_G1C(G_I8_NARROW) QD_G1C(G_I8_LONGK) QD_G1C(G_I8_MID) QD_G1C(G_I8_MID2)
+                default: return hipErrorInvalidValue;
+            }
+        }
+    } else if constexpr (MS > 0) {
         switch (cfg) {
             QD_G1C(G_SMALLK_FEWROWS) QD_G1C(G_SMALLK)
             default: return hipErrorInvalidValue;
@@ -345,23 +392,24 @@ static hipError_t gemv1_dispatch(const GemvArgs& a, int cfg, int* grid_out, int 
 // capped, grid-strided grid; a K no shape covers in one pass keeps the old
 // rule (largest tile with at least 256 workgroups). The lm_head keeps its
 // grid-strided wide tile.
-static int gemv1_pick(int N, int K, int epi) {
-    const bool small_k = K <= 2048;
-    if (epi == EPI_LOGITS) return small_k ? G_SMALLK_UR2 : G_BIGK_UR2;
+static int gemv1_pick(int N, int K, int epi, int ce) {
+    const bool small_k = K <= 2048, i8 = ce == 16;
+    if (epi == EPI_LOGITS) return i8 ? (K <= gemv1_kpass(G_I8_WIDE, ce) ? G_I8_WIDE : G_I8_LONGK)
+                                     : (small_k ? G_SMALLK_UR2 : G_BIGK_UR2);
     int best = -1, widest = -1;
-    for (int c = 0; c < G_NCFG; ++c) {
-        if (gemv1_kpass(c) < K) continue;
+    for (int c = i8 ? G_NCFG : 0; c < (i8 ? G_NALL : G_NCFG); ++c) {
+        if (gemv1_kpass(c, ce) < K) continue;
         const int tiles = (N + gemv1_rpt(c) - 1) / gemv1_rpt(c);
         // ties on the row tile go to the shape with the least idle lanes (smallest pass)
         if (tiles <= kCus && (best < 0 || gemv1_rpt(c) < gemv1_rpt(best) ||
-                              (gemv1_rpt(c) == gemv1_rpt(best) && gemv1_kpass(c) < gemv1_kpass(best))))
+                              (gemv1_rpt(c) == gemv1_rpt(best) && gemv1_kpass(c, ce) < gemv1_kpass(best, ce))))
             best = c;
         if (widest < 0 || gemv1_rpt(c) > gemv1_rpt(widest) ||
-            (gemv1_rpt(c) == gemv1_rpt(widest) && gemv1_kpass(c) < gemv1_kpass(widest)))
+            (gemv1_rpt(c) == gemv1_rpt(widest) && gemv1_kpass(c, ce) < gemv1_kpass(widest, ce)))
             widest = c;
     }
     if (best >= 0) return best;
-    if (widest >= 0) return widest;
+    if (widest >= 0 || i8) return i8 && widest < 0 ? G_I8_LONGK : widest;
     const int cfgs_big[3] = {G_BIGK_UR2, G_BIGK, G_BIGK_FEWROWS};
     for (int i = 0; i < 3; ++i)
         if ((N + gemv1_rpt(cfgs_big[i]) - 1) / gemv1_rpt(cfgs_big[i]) >= kCus) return cfgs_big[i];
@@ -370,20 +418,23 @@ static int gemv1_pick(int N, int K, int epi) {
 
 int gemv1_merge_max_splits() { return 16; }
 
-hipError_t launch_gemv1(const GemvArgs& a, int w_is_bf16, int epi, int grid_cap, int* grid_out, hipStream_t s) {
-    const int cfg = gemv1_pick(a.N, a.K, epi);
+hipError_t launch_gemv1(const GemvArgs& a, int w_type, int epi, int grid_cap, int* grid_out, hipStream_t s) {
+    // w_type: 0 float, 1 bf16, 2 int8 (with a.wscale); the picker counts bf16-sized
+    // chunks for float and bf16, 16-element ones for int8
+    if (w_type == 2 && (a.K % 16 || !a.wscale[0])) return hipErrorInvalidValue;
+    const int cfg = gemv1_pick(a.N, a.K, epi, w_type == 2 ? 16 : 8);
     if (a.part) {   // residual product over the merged attention context
         if (epi != EPI_RESID || a.gain || a.part_hd % 4 || a.K % a.part_hd || a.K > 1024 ||
             a.K / a.part_hd > kG1MergeHeads || a.part_S < 1 || a.part_S > 16 || a.part_chunk < 1)
             return hipErrorInvalidValue;
         // one shape (it covers K <= 1024 in one pass); MS = the smallest of 2, 4, 8, 16 >= S
-        const int mc = QD_B1_OCFG;
+        const int mc = w_type == 2 ? (int)G_I8_NARROW : QD_B1_OCFG;
 #define QD_G1M(WT)                                                                                      \
         if (a.part_S <= 2) return gemv1_dispatch<WT, EPI_RESID, 2>(a, mc, grid_out, grid_cap, s);      \
         if (a.part_S <= 4) return gemv1_dispatch<WT, EPI_RESID, 4>(a, mc, grid_out, grid_cap, s);      \
         if (a.part_S <= 8) return gemv1_dispatch<WT, EPI_RESID, 8>(a, mc, grid_out, grid_cap, s);      \
         return gemv1_dispatch<WT, EPI_RESID, 16>(a, mc, grid_out, grid_cap, s);
-        if (w_is_bf16) { QD_G1M(uint16_t) } else { QD_G1M(float) }
+        if (w_type == 2) { QD_G1M(int8_t) } else if (w_type == 1) { QD_G1M(uint16_t) } else { QD_G1M(float) }
 #undef QD_G1M
     }
 #define QD_G1(WT)                                                                                 \
@@ -393,7 +444,7 @@ hipError_t launch_gemv1(const GemvArgs& a, int w_is_bf16, int epi, int grid_cap,
         case EPI_SWIGLU: return gemv1_dispatch<WT, EPI_SWIGLU>(a, cfg, grid_out, grid_cap, s);    \
         default: return gemv1_dispatch<WT, EPI_LOGITS>(a, cfg, grid_out, grid_cap, s);            \
     }
-    if (w_is_bf16) { QD_G1(uint16_t) } else { QD_G1(float) }
+    if (w_type == 2) { QD_G1(int8_t) } else if (w_type == 1) { QD_G1(uint16_t) } else { QD_G1(float) }
 #undef QD_G1
 }
 

@@ -34,11 +34,15 @@ struct GemvArgs {
     const float2* part_ml;
     const int* part_pos;
     int part_S, part_chunk, part_hd;
+    // int8 weights: float scale of each row, per segment (SWIGLU: [0] gate, [1] up);
+    // the product of row r is scaled by it
+    const float* wscale[3];
 };
 hipError_t launch_gemv(const GemvArgs& a, int w_is_bf16, int epi, int grid_cap, int* grid_out,
                        hipStream_t s);
-// batch-1 fast path (qd_gemv.hip); part_val/part_idx hold one entry per workgroup
-hipError_t launch_gemv1(const GemvArgs& a, int w_is_bf16, int epi, int grid_cap, int* grid_out,
+// batch-1 fast path (qd_gemv.hip); part_val/part_idx hold one entry per workgroup;
+// w_type 0 float, 1 bf16, 2 int8 rows with a.wscale (K a multiple of 16)
+hipError_t launch_gemv1(const GemvArgs& a, int w_type, int epi, int grid_cap, int* grid_out,
                         hipStream_t s);
 int gemv_rows_per_tile(int K);
 // most attention splits launch_gemv1 merges itself (GemvArgs::part)
@@ -102,6 +106,7 @@ hipError_t launch_prefill_attn_mfma(const PrefillAttnArgs& a, hipStream_t s);
 struct StepInputArgs {
     const int* tokens;
     const void* embed;
+    const float* embed_scale;   // int8 embedding: row scales
     const float* x_in;
     float* x;
     const int* pos;
@@ -109,7 +114,7 @@ struct StepInputArgs {
     int B, D, V, hd;
     float theta;
 };
-hipError_t launch_step_input(const StepInputArgs& a, int w_is_bf16, hipStream_t s);
+hipError_t launch_step_input(const StepInputArgs& a, int w_type, hipStream_t s);   // 0 f32, 1 bf16, 2 int8
 
 hipError_t launch_embed(const int* tokens, const void* embed, float* x, int B, int D, int V,
                         int w_is_bf16, hipStream_t s);
@@ -166,5 +171,9 @@ struct PrefillRopeArgs {
 };
 hipError_t launch_prefill_rope_append(const PrefillRopeArgs& a, int w_is_bf16, int kv_is_bf16, hipStream_t s);
 hipError_t launch_to_bf16(const float* x, void* y, long n, hipStream_t s);
+
+// Per-row symmetric int8 quantization of a [rows][cols] matrix (qd_quant.hip).
+hipError_t launch_quantize_rows(const void* w, int w_is_bf16, long rows, int cols, int8_t* q, float* scale,
+                                hipStream_t s);
 
 }  // namespace qd

@@ -15,12 +15,16 @@ LIB_PATH = os.path.join(HERE, "libqd.so")
 
 QD_OK, QD_EINVAL, QD_ESHAPE, QD_EALIGN, QD_ECAPACITY = 0, -1, -2, -3, -4
 QD_EPOSITION, QD_EWORKSPACE, QD_EUNSUPPORTED, QD_EHIP = -5, -6, -7, -8
-QD_F32, QD_BF16 = 0, 1
+QD_F32, QD_BF16, QD_I8 = 0, 1, 2
 STATUS_NAMES = {0: "QD_OK", -1: "QD_EINVAL", -2: "QD_ESHAPE", -3: "QD_EALIGN", -4: "QD_ECAPACITY",
                 -5: "QD_EPOSITION", -6: "QD_EWORKSPACE", -7: "QD_EUNSUPPORTED", -8: "QD_EHIP"}
 
 LAYER_FIELDS = ["attn_norm", "wq", "wk", "wv", "bq", "bk", "bv", "q_norm", "k_norm",
-                "wo", "mlp_norm", "w_gate", "w_up", "w_down"]
+                "wo", "mlp_norm", "w_gate", "w_up", "w_down",
+                "s_q", "s_k", "s_v", "s_o", "s_gate", "s_up", "s_down"]
+# int8 models: the row-scale field of each quantized matrix
+SCALE_OF = {"wq": "s_q", "wk": "s_k", "wv": "s_v", "wo": "s_o", "w_gate": "s_gate", "w_up": "s_up",
+            "w_down": "s_down", "embed": "s_embed", "lm_head": "s_lm_head"}
 
 
 class qd_config(Structure):
@@ -37,7 +41,7 @@ class qd_layer(Structure):
 
 class qd_weights(Structure):
     _fields_ = [("embed", c_void_p), ("final_norm", c_void_p), ("lm_head", c_void_p),
-                ("layers_host", POINTER(qd_layer))]
+                ("layers_host", POINTER(qd_layer)), ("s_embed", c_void_p), ("s_lm_head", c_void_p)]
 
 
 class qd_kv(Structure):
@@ -46,7 +50,7 @@ class qd_kv(Structure):
                 ("max_blocks", c_int32), ("num_pages", c_int32)]
 
 
-EXPORTS = ["qd_workspace_bytes", "qd_decode_step", "qd_prefill_block", "qd_kv_append",
+EXPORTS = ["qd_workspace_bytes", "qd_decode_step", "qd_prefill_block", "qd_kv_append", "qd_quantize_rows_int8",
            "qd_last_error", "qd_abi_version", "qd_profile_enable", "qd_profile_read",
            "qd_profile_reset"]
 
@@ -77,6 +81,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qd_kv_append.argtypes = [POINTER(qd_config), POINTER(qd_kv), c_int32, c_int32, P,
                                  POINTER(c_int32), P, P, P]
     lib.qd_kv_append.restype = c_int32
+    lib.qd_quantize_rows_int8.argtypes = [P, c_int32, ctypes.c_int64, c_int32, P, P, P]
+    lib.qd_quantize_rows_int8.restype = c_int32
     lib.qd_last_error.argtypes = []
     lib.qd_last_error.restype = c_char_p
     lib.qd_abi_version.argtypes = []
@@ -127,6 +133,11 @@ def qd_prefill_block(cfg, layer, layer_index, kv, n_tokens, start_pos, x_in, x_d
 def qd_kv_append(cfg, kv, layer_index, batch, pos, pos_host, k, v, stream) -> int:
     return int(lib().qd_kv_append(ctypes.byref(cfg), ctypes.byref(kv), layer_index, batch, pos,
                                   pos_host, k, v, stream))
+
+
+def qd_quantize_rows_int8(w, w_dtype, rows, cols, q, scale, stream) -> int:
+    """Raw call; pointers are integers (device addresses)."""
+    return int(lib().qd_quantize_rows_int8(w, w_dtype, rows, cols, q, scale, stream))
 
 
 def qd_last_error() -> str:

@@ -17,7 +17,7 @@ from . import qd as Q
 
 
 def _dtype_code(d: str) -> int:
-    return {"f32": Q.QD_F32, "bf16": Q.QD_BF16}[d]
+    return {"f32": Q.QD_F32, "bf16": Q.QD_BF16, "i8": Q.QD_I8}[d]
 
 
 def make_config(shape) -> Q.qd_config:
@@ -45,6 +45,36 @@ def _stream_handle(stream: Optional[torch.cuda.Stream]):
     return s.cuda_stream or None
 
 
+def quantize_int8(w: torch.Tensor, stream=None):
+    """One matrix through qd_quantize_rows_int8: (int8 codes [rows][cols], float32
+    scales [rows]) on w's device."""
+    if w.dim() != 2 or not w.is_contiguous():
+        raise ValueError("quantize_int8 takes a contiguous 2-D matrix")
+    code = Q.QD_BF16 if w.dtype == torch.bfloat16 else Q.QD_F32
+    q = torch.empty(w.shape, dtype=torch.int8, device=w.device)
+    sc = torch.empty(w.shape[0], dtype=torch.float32, device=w.device)
+    Q.check(Q.qd_quantize_rows_int8(w.data_ptr(), code, w.shape[0], w.shape[1], q.data_ptr(), sc.data_ptr(),
+                                    _stream_handle(stream)))
+    return q, sc
+
+
+def quantize_weights_int8(weights: dict, stream=None) -> dict:
+    """The model's weights with every projection matrix and the embedding (and an
+    untied lm_head) replaced by int8 codes plus row scales (keys of qd.SCALE_OF);
+    norm gains and biases are kept as they are."""
+    out = {k: v for k, v in weights.items() if k != "layers"}
+    for k in ("embed", "lm_head"):
+        if weights.get(k) is not None:
+            out[k], out[Q.SCALE_OF[k]] = quantize_int8(weights[k], stream)
+    out["layers"] = []
+    for L in weights["layers"]:
+        M = dict(L)
+        for k in ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down"):
+            M[k], M[Q.SCALE_OF[k]] = quantize_int8(L[k], stream)
+        out["layers"].append(M)
+    return out
+
+
 class DecodeRunner:
     """Holds the C views of one model's weights, KV pools and block table."""
 
@@ -58,9 +88,12 @@ class DecodeRunner:
         self.layers = (Q.qd_layer * L)(*[make_layer(x) for x in weights["layers"]])
         lm = weights.get("lm_head")
         emb = weights.get("embed")
+        s_emb = weights.get("s_embed")
+        s_lm = weights.get("s_lm_head")
         self.weights = Q.qd_weights(embed=_ptr(emb), final_norm=_ptr(weights.get("final_norm")),
                                     lm_head=_ptr(lm if lm is not None else emb),
-                                    layers_host=ctypes.cast(self.layers, POINTER(Q.qd_layer)))
+                                    layers_host=ctypes.cast(self.layers, POINTER(Q.qd_layer)),
+                                    s_embed=_ptr(s_emb), s_lm_head=_ptr(s_lm if s_lm is not None else s_emb))
         self.k_pools, self.v_pools = k_pools, v_pools
         self._kp = (c_void_p * L)(*[p.data_ptr() for p in k_pools])
         self._vp = (c_void_p * L)(*[p.data_ptr() for p in v_pools])

@@ -23,7 +23,8 @@
  * Conventions for every entry point:
  *   - Pointers are DEVICE pointers unless the name ends in _host.
  *   - Matrices are row-major [out][in]; weight dtype from qd_config.w_dtype
- *     (QD_BF16: raw bf16, QD_F32: float). Biases and gains use the same dtype.
+ *     (QD_BF16: raw bf16, QD_F32: float; biases and gains use the same dtype;
+ *     QD_I8: int8 matrices with one float scale per row, see below).
  *   - The caller owns and allocates everything (weights, KV pages, block table,
  *     workspace, outputs). The library never allocates device memory, never
  *     synchronises the stream and never reads device memory back to the host.
@@ -46,7 +47,7 @@
 extern "C" {
 #endif
 
-#define QD_ABI_VERSION 1
+#define QD_ABI_VERSION 2
 
 typedef enum {
     QD_OK = 0,
@@ -60,7 +61,7 @@ typedef enum {
     QD_EHIP = -8           /* a HIP launch failed (message names the kernel)              */
 } qd_status;
 
-typedef enum { QD_F32 = 0, QD_BF16 = 1 } qd_dtype;
+typedef enum { QD_F32 = 0, QD_BF16 = 1, QD_I8 = 2 } qd_dtype;
 
 /* Model configuration. hidden, ffn and head_dim must be multiples of 8;
  * n_q_heads must be a multiple of n_kv_heads; head_dim in {64, 128};
@@ -69,23 +70,31 @@ typedef struct {
     int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab, page_size;
     float rms_eps, rope_theta;
     int32_t qk_norm;   /* 1: per-head RMSNorm of q and k (gain [head_dim]) before RoPE */
-    int32_t w_dtype;   /* qd_dtype of matrices, biases, gains and the embedding         */
+    int32_t w_dtype;   /* qd_dtype of matrices, biases, gains and the embedding; QD_I8:
+                        * int8 matrices and embedding (per-row scales), bf16 biases
+                        * and gains (nanoinfer, phase 6: norms and biases are never
+                        * quantized); batch-1 decode steps only                     */
     int32_t kv_dtype;  /* qd_dtype of the KV cache                                      */
 } qd_config;
 
 /* One decoder layer. Shapes: wq [Hq*hd][D], wk/wv [Hkv*hd][D], wo [D][Hq*hd],
  * w_gate/w_up [F][D], w_down [D][F]; attn_norm/mlp_norm [D]; bq [Hq*hd],
- * bk/bv [Hkv*hd] (NULL: no bias); q_norm/k_norm [hd] (used iff qk_norm). */
+ * bk/bv [Hkv*hd] (NULL: no bias); q_norm/k_norm [hd] (used iff qk_norm).
+ * s_* (QD_I8 only, else ignored): float [rows] scale of each matrix row, so that
+ * row r of the matrix is q[r][:] * s[r] (qd_quantize_rows_int8 makes them). */
 typedef struct {
     const void *attn_norm, *wq, *wk, *wv, *bq, *bk, *bv, *q_norm, *k_norm;
     const void *wo, *mlp_norm, *w_gate, *w_up, *w_down;
+    const float *s_q, *s_k, *s_v, *s_o, *s_gate, *s_up, *s_down;
 } qd_layer;
 
 /* Whole-model weights. embed [V][D]; final_norm [D]; lm_head [V][D] or equal to
- * embed (tied). `layers_host` is a HOST array of n_layers qd_layer structs. */
+ * embed (tied). `layers_host` is a HOST array of n_layers qd_layer structs.
+ * s_embed / s_lm_head: float [V] row scales (QD_I8 only; equal when tied). */
 typedef struct {
     const void *embed, *final_norm, *lm_head;
     const qd_layer *layers_host;
+    const float *s_embed, *s_lm_head;
 } qd_weights;
 
 /* Paged KV cache. For each layer l, k_pages_host[l] / v_pages_host[l] are device
@@ -146,6 +155,18 @@ qd_status qd_prefill_block(const qd_config *cfg, const qd_layer *layer, int32_t 
 qd_status qd_kv_append(const qd_config *cfg, const qd_kv *kv, int32_t layer_index,
                        int32_t batch, const int32_t *pos, const int32_t *pos_host,
                        const float *k, const float *v, void *stream);
+
+/* Per-output-channel symmetric int8 weight quantization (nanoinfer, phase 6):
+ * for each row r of the row-major [rows][cols] matrix w (w_dtype QD_F32 or
+ * QD_BF16, widened exactly to float), scale[r] = max_k |w[r][k]| / 127 and
+ * q[r][k] = round(w[r][k] / scale[r]), both quotients in float32 with IEEE
+ * rounding, the integer rounding half away from zero (the range is [-127, 127],
+ * so a weight and its negation give opposite codes); a row of zeros gets scale 0
+ * and codes 0. q: int8 [rows][cols] out; scale: float [rows] out. cols must be a
+ * multiple of 16 and every pointer 16-byte aligned. An offline weight
+ * conversion: one workgroup per row, enqueued on `stream`. */
+qd_status qd_quantize_rows_int8(const void *w, int32_t w_dtype, int64_t rows, int32_t cols,
+                                int8_t *q, float *scale, void *stream);
 
 /* Kernel kinds for the optional event timing below. */
 typedef enum {

@@ -29,12 +29,12 @@ def lib():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(qd_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(qd_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ["qd_decode_step", "qd_prefill_block", "qd_kv_append", "qd_workspace_bytes",
+    for n in ["qd_decode_step", "qd_prefill_block", "qd_kv_append", "qd_workspace_bytes", "qd_quantize_rows_int8",
               "qd_last_error", "qd_abi_version"]:
         assert n in names
 
@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol(lib):
     for n in declared_functions():
         assert n in exported, n
         assert hasattr(lib, n)
-    assert lib.qd_abi_version() == 1
+    assert lib.qd_abi_version() == 2
 
 
 def test_struct_layout_matches_the_header(tmp_path):
@@ -210,3 +210,28 @@ def test_prefill_workspace_bytes(lib):
     cfg = _cfg()
     assert Q.qd_workspace_bytes(cfg, 1, 512, 512) > Q.qd_workspace_bytes(cfg, 1, 512, 16) > 0
     assert Q.qd_workspace_bytes(cfg, 1, 10, 512) == 0     # max_ctx below the prefill length
+
+
+def test_int8_checks(lib):
+    _expect(Fixture(_cfg(w_dtype=Q.QD_I8, hidden=72)).decode(), Q.QD_ESHAPE)      # hidden % 16
+    _expect(Fixture(_cfg(w_dtype=Q.QD_I8, ffn=104)).decode(), Q.QD_ESHAPE)        # ffn % 16
+    f = Fixture(_cfg(w_dtype=Q.QD_I8))
+    _expect(f.decode(), Q.QD_EINVAL)                       # tokens given, s_embed NULL
+    f.w.s_embed = FAKE
+    _expect(f.decode(), Q.QD_EINVAL)                       # logits wanted, s_lm_head NULL
+    f.w.s_lm_head = FAKE
+    f.layers[0].s_up = FAKE + 2
+    _expect(f.decode(), Q.QD_EINVAL)                       # misaligned row scales
+    f.layers[0].s_up = None
+    _expect(f.decode(), Q.QD_EINVAL)                       # missing row scales
+    f2 = Fixture(_cfg(w_dtype=Q.QD_I8), pos=(3, 4))
+    _expect(f2.decode(), Q.QD_EUNSUPPORTED)                # batch-1 steps only
+    _expect(_prefill(Fixture(_cfg(w_dtype=Q.QD_I8))), Q.QD_EUNSUPPORTED)
+
+
+def test_quantize_checks(lib):
+    _expect(Q.qd_quantize_rows_int8(None, Q.QD_BF16, 4, 32, FAKE, FAKE, None), Q.QD_EINVAL)
+    _expect(Q.qd_quantize_rows_int8(FAKE, Q.QD_I8, 4, 32, FAKE, FAKE, None), Q.QD_EINVAL)
+    _expect(Q.qd_quantize_rows_int8(FAKE, Q.QD_BF16, 4, 20, FAKE, FAKE, None), Q.QD_ESHAPE)
+    _expect(Q.qd_quantize_rows_int8(FAKE, Q.QD_BF16, 0, 32, FAKE, FAKE, None), Q.QD_ESHAPE)
+    _expect(Q.qd_quantize_rows_int8(FAKE + 8, Q.QD_F32, 4, 32, FAKE, FAKE, None), Q.QD_EALIGN)

@@ -28,7 +28,8 @@ class ModelShape:
     qkv_bias: bool = True
     qk_norm: bool = False
     tied: bool = True
-    w_dtype: str = "bf16"      # "bf16" | "f32": matrices, embedding, norms, biases
+    w_dtype: str = "bf16"      # "bf16" | "f32": matrices, embedding, norms, biases;
+                               # "i8": int8 matrices and embedding with row scales, bf16 norms/biases
     kv_dtype: str = "bf16"     # "bf16" | "f32": the KV cache storage type
     page_size: int = 16
 
@@ -101,6 +102,11 @@ QWEN2_0P5B_B16_PAGED = Workload(
     shape=QWEN2_0P5B, kind="decode", batch=16, ctx_range=(128, 4096), paged_random=True,
     greedy_steps=4)
 
+# The 0.5B step with per-row int8 weights (quantized from the bf16 draw), batch 1, past 512.
+QWEN2_0P5B_INT8_B1_PAST512 = Workload(
+    name="qwen2-0.5b-int8-b1-past512",
+    shape=replace(QWEN2_0P5B, w_dtype="i8"), kind="decode", batch=1, past=512, greedy_steps=8)
+
 # 8B-class shape with per-head q/k RMSNorm, batch 1, 4096 cached tokens.
 QWEN_8B_B1_PAST4096 = Workload(
     name="qwen-8b-qknorm-bf16-b1-past4096",
@@ -114,7 +120,7 @@ QWEN_8B_BLOCK_PREFILL512 = Workload(
 
 WORKLOADS = {w.name: w for w in (QWEN2_BLOCK_F32_PAST16, QWEN2_0P5B_B1_PAST512,
                                  QWEN2_0P5B_B16_PAGED, QWEN_8B_B1_PAST4096,
-                                 QWEN_8B_BLOCK_PREFILL512)}
+                                 QWEN_8B_BLOCK_PREFILL512, QWEN2_0P5B_INT8_B1_PAST512)}
 
 
 def tiny_shape(**over) -> ModelShape:

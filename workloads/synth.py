@@ -65,8 +65,9 @@ def uniform_int(n: int, lo: int, hi: int, seed: int, name: str) -> np.ndarray:
 
 def make_weights(shape: ModelShape, seed: int = 0, device="cpu", gain_mode: str = "one_plus",
                  with_embed: bool = True, w_std: float = W_STD) -> dict:
-    """All weights of the model as torch tensors on `device`, row-major [out][in]."""
-    wd = shape.w_dtype
+    """All weights of the model as torch tensors on `device`, row-major [out][in].
+    An int8 shape ("i8") is drawn in bf16, the form its codes are quantized from."""
+    wd = "bf16" if shape.w_dtype == "i8" else shape.w_dtype
     gmean = 1.0 if gain_mode == "one_plus" else 0.0
     D, F = shape.hidden, shape.ffn
     out = {"layers": []}
