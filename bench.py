@@ -247,6 +247,53 @@ def copy_probe(reps=5):
                       "gbs_read_plus_write": round(2 * COPY_PROBE_BYTES * reps / el / 1e9, 1)}), flush=True)
 
 
+def bench_sample(wl, args):
+    """qd_sample over B rows of seeded logits, timed over K back-to-back launches."""
+    import torch
+    from decode_step_amd.runner import sample
+    from workloads import synth
+    B, V, X = wl.batch, wl.shape.vocab, wl.extra
+    logits = synth.normal((B, V), X["logit_std"], 0.0, "f32", wl.seed, "sample_logits", "cuda")
+    u = torch.from_numpy(synth.uniform_int(B, 0, (1 << 24) - 1, wl.seed, "sample_u").astype(np.float32)
+                         / float(1 << 24)).cuda()
+    tok = torch.empty(B, dtype=torch.int32, device="cuda")
+    run = lambda: sample(logits, X["temperature"], X["top_k"], X["top_p"], u, tok)
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    us = 1e3 * e0.elapsed_time(e1) / args.steps
+    nbytes = B * V * 4                     # every logit read once
+    gbs = nbytes / (us * 1e-6) / 1e9
+    print(f"[bench] {wl.name}: {us:.2f} us per call ({B} rows), {gbs:.1f} GB/s of logits", file=sys.stderr)
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle.sampler import sample as oracle_sample
+        lh, uh = logits.cpu().numpy(), u.cpu().numpy()
+        t0, n = time.perf_counter(), 0
+        while time.perf_counter() - t0 < 10.0 or n < 1:
+            oracle_sample(lh, X["temperature"], X["top_k"], X["top_p"], uh)
+            n += 1
+        el = time.perf_counter() - t0
+        cpu = {"value": round(B * n / el, 2), "unit": "sampled tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"{n} calls of the numpy oracle sampler over the same {B} x {V} logits in {el:.1f} s"}
+    rec = {"metric": "sampled tokens/s, temperature/top-k/top-p sampler, 0.5B vocabulary",
+           "value": round(B / (us * 1e-6), 1), "unit": "sampled tokens/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(us / 1e3, 5), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+           "config": {"workload": wl.name, "batch": B, "vocab": V, **X}, "launch": "eager",
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "sample_kernel",
+                        "bytes_per_launch": nbytes, "avg_launch_us": round(us, 3)},
+           "cpu_baseline": cpu}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -277,6 +324,8 @@ def main():
     wl = S.WORKLOADS[args.workload]
     if wl.kind == "prefill":
         return bench_prefill(wl, args)
+    if wl.kind == "sample":
+        return bench_sample(wl, args)
     shape = wl.shape
     dev = "cuda"
     ctx = synth.make_ctx(wl.batch, wl.past, wl.ctx_range, wl.seed)

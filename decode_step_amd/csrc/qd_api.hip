@@ -8,6 +8,7 @@
 
 #include "../../include/qd.h"
 #include "qd_launch.h"
+#include <cmath>
 
 namespace {
 
@@ -439,6 +440,28 @@ qd_status qd_quantize_rows_int8(const void* w, int32_t w_dtype, int64_t rows, in
     if (!aligned16(w) || !aligned16(q) || !aligned16(scale)) return fail(QD_EALIGN, "w, q or scale not 16-byte aligned");
     hipStream_t s = (hipStream_t)stream;
     QD_LAUNCH(qd::launch_quantize_rows(w, w_dtype == QD_BF16, (long)rows, cols, q, scale, s), "quantize");
+    return QD_OK;
+}
+
+qd_status qd_sample(const float* logits, int32_t batch, int32_t vocab, float temperature, int32_t top_k,
+                    float top_p, const float* uniforms, int32_t* tokens, void* stream) {
+    if (!logits || !tokens) return fail(QD_EINVAL, "logits or tokens is NULL");
+    if (batch < 1 || vocab < 1) return fail(QD_ESHAPE, "batch %d / vocab %d must be positive", batch, vocab);
+    if (!(temperature >= 0.f) || !std::isfinite(temperature))
+        return fail(QD_EINVAL, "temperature %g must be finite and >= 0", (double)temperature);
+    if (!(top_p > 0.f && top_p <= 1.f)) return fail(QD_EINVAL, "top_p %g not in (0, 1]", (double)top_p);
+    if (temperature > 0.f) {
+        if (!uniforms) return fail(QD_EINVAL, "uniforms is NULL");
+        if (top_k < 1 || top_k > qd::kSampleMaxK)
+            return fail(QD_EUNSUPPORTED, "top_k %d: sampling takes 1 <= top_k <= %d", top_k, qd::kSampleMaxK);
+    }
+    if (!aligned4(logits) || !aligned4(tokens) || (uniforms && !aligned4(uniforms)))
+        return fail(QD_EALIGN, "logits, uniforms or tokens not 4-byte aligned");
+    qd::SampleArgs a{};
+    a.logits = logits; a.B = batch; a.V = vocab; a.temperature = temperature; a.top_k = top_k;
+    a.top_p = top_p; a.one_minus_p = (float)(1.0 - (double)top_p); a.uniforms = uniforms; a.tokens = tokens;
+    hipStream_t s = (hipStream_t)stream;
+    QD_LAUNCH_K(QD_K_ARGMAX, qd::launch_sample(a, s), "sample");
     return QD_OK;
 }
 

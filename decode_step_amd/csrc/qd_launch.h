@@ -172,6 +172,20 @@ struct PrefillRopeArgs {
 hipError_t launch_prefill_rope_append(const PrefillRopeArgs& a, int w_is_bf16, int kv_is_bf16, hipStream_t s);
 hipError_t launch_to_bf16(const float* x, void* y, long n, hipStream_t s);
 
+// Temperature / top-k / top-p sampling of one token per row of logits (qd_sample.hip).
+constexpr int kSampleMaxK = 1024;
+struct SampleArgs {
+    const float* logits;    // [B][V]
+    int B, V;
+    float temperature;      // 0: argmax
+    int top_k;              // 1 .. kSampleMaxK when temperature > 0
+    float top_p;            // (0, 1]; 1 keeps every top-k candidate
+    float one_minus_p;      // the top-p threshold, float32(1 - p) formed in double
+    const float* uniforms;  // [B] in [0, 1)
+    int* tokens;            // [B] out
+};
+hipError_t launch_sample(const SampleArgs& a, hipStream_t s);
+
 // Per-row symmetric int8 quantization of a [rows][cols] matrix (qd_quant.hip).
 hipError_t launch_quantize_rows(const void* w, int w_is_bf16, long rows, int cols, int8_t* q, float* scale,
                                 hipStream_t s);

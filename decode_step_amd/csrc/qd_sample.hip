@@ -1,0 +1,310 @@
+// Next-token sampling from a row of logits on the GPU (nanoinfer page, phase 5:
+// temperature -> top-k -> top-p -> softmax -> inverse-CDF draw, in that order;
+// temperature 0 is the argmax). One workgroup of 1024 threads per row; no
+// device memory beyond the logits, the uniforms and the tokens.
+//
+// Per row, with T > 0 and 1 <= k <= 1024:
+// 1. top-k: the k-th largest logit is found exactly by a three-digit radix
+//    select over order-preserving 32-bit keys (11, 11 and 10 bits), with the
+//    histograms in LDS. The first digit reads the row; when the logits in its
+//    boundary bin and above fit the candidate space (the usual case: the top
+//    bins of a vocabulary's logits are sparse), they are compacted into LDS and
+//    the other two digits run there, else each digit reads the row again. Every
+//    logit >= the k-th largest is a candidate, so ties at the boundary are all
+//    kept (the transformers warper removes only scores below the k-th).
+//    Dividing by T > 0 keeps the order, so the threshold is taken on the logits
+//    themselves.
+// 2. The candidates (at most kSampleCand; more, from ties, give token -1) are
+//    compacted into LDS with z = logit / T (float32, IEEE division), and sorted
+//    ascending by (z, token id): a stable ascending sort, the order the page
+//    settles on (a tied pair keeps its index order).
+// 3. top-p as the page's reference defines it: with probabilities
+//    e_j / S (e_j = exp(z_j - max z), S their sum), the cumulative sum over the
+//    ascending order is taken in float32, one term at a time, and every token
+//    whose cumulative sum is <= 1 - p is removed; the largest always stays.
+// 4. The kept tokens, back in token-id order, get probabilities e_j / S_kept;
+//    their running sum, again one term at a time, is searched for the first
+//    token whose cumulative value exceeds u * total (an inverse-CDF draw that
+//    does not need the probabilities to sum to exactly one).
+#include "qd_device.h"
+#include "qd_launch.h"
+
+namespace qd {
+
+constexpr int kSampleThreads = 1024;
+constexpr int kSampleCand = 2048;    // candidates a row may hold (k plus ties at the boundary)
+
+// larger float -> larger key, for every non-NaN value
+__device__ __forceinline__ uint32_t order_key(float f) {
+    const uint32_t b = __float_as_uint(f);
+    return b ^ ((b & 0x80000000u) ? 0xffffffffu : 0x80000000u);
+}
+
+// Radix-select step: in hist[0..nb), scanned from the top bin down, the bin where
+// the running count reaches `need`; returns the bin and the count of the bins
+// above it. Run by wave 0 (every lane returns the same).
+__device__ __forceinline__ void top_bin(const int* hist, int nb, int need, int lane, int& bin, int& above) {
+    const int per = nb / kWave;                // bins per lane, lane 0 holding the highest
+    const int hi = nb - per * lane;            // this lane's bins: [hi - per, hi)
+    int mine = 0;
+    for (int j = hi - 1; j >= hi - per; --j) mine += hist[j];
+    // exclusive prefix over lanes 0..lane-1 (the bins above this lane's)
+    int incl = mine;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int t = __shfl_up(incl, d);
+        if (lane >= d) incl += t;
+    }
+    const int excl = incl - mine;
+    const bool here = excl < need && incl >= need;
+    int b = -1, a = 0;
+    if (here) {
+        int run = excl;
+        for (int j = hi - 1; j >= hi - per; --j) {
+            if (run + hist[j] >= need) { b = j; a = run; break; }
+            run += hist[j];
+        }
+    }
+    // broadcast from the lane that found it (exactly one lane, as 1 <= need <= total)
+    const unsigned long long m = __ballot(here);
+    const int src = m ? __ffsll((long long)m) - 1 : 0;
+    bin = __shfl(b, src);
+    above = __shfl(a, src);
+}
+
+__global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleArgs a) {
+    __shared__ int hist[2048];
+    __shared__ unsigned long long ck[kSampleCand];   // (order key of z) << 32 | token
+    __shared__ float ce[kSampleCand];                // e_j in ascending order
+    __shared__ int s_bin, s_above, s_cnt, s_j0;
+    __shared__ float s_red[kSampleThreads / kWave];
+    const int row = blockIdx.x, tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+    const int V = a.V;
+    const float* lg = a.logits + (long)row * V;
+
+    if (a.temperature == 0.f) {   // greedy: the lowest index among the maxima
+        float bv = -INFINITY;
+        int bi = 0x7fffffff;
+        for (int i = tid; i < V; i += kSampleThreads) {
+            const float v = lg[i];
+            if (better(v, i, bv, bi)) { bv = v; bi = i; }
+        }
+        wave_argmax(bv, bi);
+        __shared__ float wv[kSampleThreads / kWave];
+        __shared__ int wi[kSampleThreads / kWave];
+        if (lane == 0) { wv[wave] = bv; wi[wave] = bi; }
+        __syncthreads();
+        if (tid == 0) {
+            for (int w = 1; w < kSampleThreads / kWave; ++w)
+                if (better(wv[w], wi[w], wv[0], wi[0])) { wv[0] = wv[w]; wi[0] = wi[w]; }
+            a.tokens[row] = wi[0];
+        }
+        return;
+    }
+
+    // Every element of the row through fn(index, value): float4 loads, four in flight
+    // per thread, when the row is 16-byte aligned (scalar loads otherwise).
+    const bool vec = (V % 4 == 0) && (((uintptr_t)lg & 15u) == 0);
+    auto scan = [&](auto&& fn) {
+        if (vec) {
+            const int V4 = V / 4;
+            const float4* l4 = (const float4*)lg;
+            int i4 = tid;
+            for (; i4 + 3 * kSampleThreads < V4; i4 += 4 * kSampleThreads) {
+                float4 q[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) q[u] = l4[i4 + u * kSampleThreads];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int i = 4 * (i4 + u * kSampleThreads);
+                    fn(i, q[u].x); fn(i + 1, q[u].y); fn(i + 2, q[u].z); fn(i + 3, q[u].w);
+                }
+            }
+            for (; i4 < V4; i4 += kSampleThreads) {
+                const float4 q = l4[i4];
+                fn(4 * i4, q.x); fn(4 * i4 + 1, q.y); fn(4 * i4 + 2, q.z); fn(4 * i4 + 3, q.w);
+            }
+        } else {
+            for (int i = tid; i < V; i += kSampleThreads) fn(i, lg[i]);
+        }
+    };
+    // one radix-select digit: histogram of the keys whose bits above this digit equal
+    // `prefix`, then the bin where the count from the top reaches `need`
+    auto digit = [&](int sh, int width, uint32_t& prefix, int& need, auto&& for_each_key) {
+        const int nb = 1 << width, hs = sh + width;
+        for (int j = tid; j < 2048; j += kSampleThreads) hist[j] = 0;
+        __syncthreads();
+        for_each_key([&](uint32_t key) {
+            if (hs >= 32 || (key >> hs) == prefix) atomicAdd(&hist[(key >> sh) & (nb - 1)], 1);
+        });
+        __syncthreads();
+        if (wave == 0) {
+            int bin, above;
+            top_bin(hist, nb, need, lane, bin, above);
+            if (lane == 0) { s_bin = bin; s_above = above; }
+        }
+        __syncthreads();
+        prefix = (prefix << width) | (uint32_t)s_bin;
+        need -= s_above;
+        __syncthreads();
+    };
+    auto global_keys = [&](auto&& f) { scan([&](int, float v) { f(order_key(v)); }); };
+
+    // 1. the k-th largest key, 11 + 11 + 10 bits. After the first digit, when the
+    //    boundary bin and everything above it fit the candidate space, those logits
+    //    are compacted into LDS once and the last two digits run there; otherwise
+    //    they read the row again.
+    const int k = a.top_k < V ? a.top_k : V;
+    uint32_t prefix = 0;
+    int need = k;
+    digit(21, 11, prefix, need, global_keys);
+    const int n0 = (k - need) + hist[prefix];      // logits in the boundary bin or above
+    const bool in_lds = n0 <= kSampleCand;
+    if (tid == 0) s_cnt = 0;
+    for (int j = tid; j < kSampleCand; j += kSampleThreads) ck[j] = ~0ull;
+    __syncthreads();
+    if (in_lds) {
+        const uint32_t b0 = prefix;
+        scan([&](int i, float v) {
+            const uint32_t key = order_key(v);
+            if ((key >> 21) >= b0) {
+                const int slot = atomicAdd(&s_cnt, 1);
+                ck[slot] = ((unsigned long long)key << 32) | (uint32_t)i;
+            }
+        });
+        __syncthreads();
+        auto lds_keys = [&](auto&& f) {
+            for (int j = tid; j < n0; j += kSampleThreads) f((uint32_t)(ck[j] >> 32));
+        };
+        digit(10, 11, prefix, need, lds_keys);
+        digit(0, 10, prefix, need, lds_keys);
+        const uint32_t thresh = prefix;
+        // 2. the candidates, in place: keys at or above the threshold become (key of
+        //    z = logit / T, token); the rest sort to the end
+        if (tid == 0) s_cnt = 0;
+        __syncthreads();
+        for (int j = tid; j < n0; j += kSampleThreads) {
+            const unsigned long long e = ck[j];
+            const uint32_t key = (uint32_t)(e >> 32), i = (uint32_t)(e & 0xffffffffu);
+            if (key >= thresh) {
+                atomicAdd(&s_cnt, 1);
+                const float z = __fdiv_rn(lg[i], a.temperature);
+                ck[j] = ((unsigned long long)order_key(z) << 32) | i;
+            } else {
+                ck[j] = ~0ull;
+            }
+        }
+        __syncthreads();
+    } else {
+        digit(10, 11, prefix, need, global_keys);
+        digit(0, 10, prefix, need, global_keys);
+        const uint32_t thresh = prefix;
+        // 2. candidates: every logit whose key reaches the threshold, with z = logit / T
+        scan([&](int i, float v) {
+            if (order_key(v) >= thresh) {
+                const int slot = atomicAdd(&s_cnt, 1);
+                if (slot < kSampleCand) {
+                    const float z = __fdiv_rn(v, a.temperature);
+                    ck[slot] = ((unsigned long long)order_key(z) << 32) | (uint32_t)i;
+                }
+            }
+        });
+        __syncthreads();
+    }
+    const int C = s_cnt;
+    if (C > kSampleCand || C < 1) {   // ties beyond the candidate space (or NaN keys): no draw
+        if (tid == 0) a.tokens[row] = -1;
+        return;
+    }
+    // bitonic sort of ck ascending (empty slots hold the largest key)
+    auto bitonic = [&]() {
+        for (int size = 2; size <= kSampleCand; size <<= 1)
+            for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                __syncthreads();
+                for (int t = tid; t < kSampleCand / 2; t += kSampleThreads) {
+                    const int i = 2 * t - (t & (stride - 1));
+                    const int j = i + stride;
+                    const bool up = (i & size) == 0;
+                    const unsigned long long x = ck[i], y = ck[j];
+                    if ((x > y) == up) { ck[i] = y; ck[j] = x; }
+                }
+            }
+        __syncthreads();
+    };
+    bitonic();
+
+    // 3. e_j = exp(z_j - max z) over the ascending order; S by a tree sum; the
+    //    cumulative sum of e_j / S one term at a time; remove while it is <= 1 - p
+    auto zval = [&](unsigned long long key) {
+        const uint32_t ok = (uint32_t)(key >> 32);
+        return __uint_as_float(ok ^ ((ok & 0x80000000u) ? 0x80000000u : 0xffffffffu));
+    };
+    const float zmax = zval(ck[C - 1]);
+    float part = 0.f;
+    for (int j = tid; j < C; j += kSampleThreads) {
+        const float e = expf(zval(ck[j]) - zmax);
+        ce[j] = e;
+        part += e;
+    }
+    part = group_sum<kWave>(part);
+    if (lane == 0) s_red[wave] = part;
+    __syncthreads();
+    if (tid == 0) {
+        float S = 0.f;
+        for (int w = 0; w < kSampleThreads / kWave; ++w) S += s_red[w];
+        int j0 = C - 1;   // the largest always stays
+        if (a.top_p < 1.f) {
+            float cum = 0.f;
+            for (int j = 0; j < C - 1; ++j) {
+                cum += __fdiv_rn(ce[j], S);
+                if (!(cum <= a.one_minus_p)) { j0 = j; break; }
+            }
+        } else {
+            j0 = 0;
+        }
+        s_j0 = j0;
+    }
+    __syncthreads();
+    const int j0 = s_j0;
+
+    // 4. the kept tokens back in token order (removed ones sort to the end), their
+    //    e values carried along; S_kept by a tree sum; the draw
+    for (int j = tid; j < kSampleCand; j += kSampleThreads) {
+        if (j < C && j >= j0) {
+            const uint32_t tok = (uint32_t)(ck[j] & 0xffffffffu);
+            ck[j] = ((unsigned long long)tok << 32) | (uint32_t)__float_as_uint(ce[j]);
+        } else {
+            ck[j] = ~0ull;
+        }
+    }
+    bitonic();
+    const int nk = C - j0;
+    float kp = 0.f;
+    for (int j = tid; j < nk; j += kSampleThreads) kp += __uint_as_float((uint32_t)(ck[j] & 0xffffffffu));
+    kp = group_sum<kWave>(kp);
+    if (lane == 0) s_red[wave] = kp;
+    __syncthreads();
+    if (tid == 0) {
+        float Sk = 0.f;
+        for (int w = 0; w < kSampleThreads / kWave; ++w) Sk += s_red[w];
+        float cdf = 0.f;
+        for (int j = 0; j < nk; ++j) cdf += __fdiv_rn(__uint_as_float((uint32_t)(ck[j] & 0xffffffffu)), Sk);
+        const float target = a.uniforms[row] * cdf;
+        int tok = (int)(ck[nk - 1] >> 32);
+        float run = 0.f;
+        for (int j = 0; j < nk; ++j) {
+            run += __fdiv_rn(__uint_as_float((uint32_t)(ck[j] & 0xffffffffu)), Sk);
+            if (run > target) { tok = (int)(ck[j] >> 32); break; }
+        }
+        a.tokens[row] = tok;
+    }
+}
+
+hipError_t launch_sample(const SampleArgs& a, hipStream_t s) {
+    if (a.B < 1 || a.V < 1 || (a.temperature > 0.f && (a.top_k < 1 || a.top_k > kSampleMaxK)))
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(sample_kernel, dim3(a.B), dim3(kSampleThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace qd

@@ -51,6 +51,7 @@ class qd_kv(Structure):
 
 
 EXPORTS = ["qd_workspace_bytes", "qd_decode_step", "qd_prefill_block", "qd_kv_append", "qd_quantize_rows_int8",
+           "qd_sample",
            "qd_last_error", "qd_abi_version", "qd_profile_enable", "qd_profile_read",
            "qd_profile_reset"]
 
@@ -83,6 +84,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qd_kv_append.restype = c_int32
     lib.qd_quantize_rows_int8.argtypes = [P, c_int32, ctypes.c_int64, c_int32, P, P, P]
     lib.qd_quantize_rows_int8.restype = c_int32
+    lib.qd_sample.argtypes = [P, c_int32, c_int32, c_float, c_int32, c_float, P, P, P]
+    lib.qd_sample.restype = c_int32
     lib.qd_last_error.argtypes = []
     lib.qd_last_error.restype = c_char_p
     lib.qd_abi_version.argtypes = []
@@ -138,6 +141,11 @@ def qd_kv_append(cfg, kv, layer_index, batch, pos, pos_host, k, v, stream) -> in
 def qd_quantize_rows_int8(w, w_dtype, rows, cols, q, scale, stream) -> int:
     """Raw call; pointers are integers (device addresses)."""
     return int(lib().qd_quantize_rows_int8(w, w_dtype, rows, cols, q, scale, stream))
+
+
+def qd_sample(logits, batch, vocab, temperature, top_k, top_p, uniforms, tokens, stream) -> int:
+    """Raw call; pointers are integers (device addresses) or None."""
+    return int(lib().qd_sample(logits, batch, vocab, temperature, top_k, top_p, uniforms, tokens, stream))
 
 
 def qd_last_error() -> str:

@@ -75,6 +75,22 @@ def quantize_weights_int8(weights: dict, stream=None) -> dict:
     return out
 
 
+def sample(logits: torch.Tensor, temperature: float, top_k: int, top_p: float,
+           uniforms: Optional[torch.Tensor], tokens: Optional[torch.Tensor] = None, stream=None,
+           raise_on_error=True):
+    """qd_sample over the rows of a contiguous float32 [B][V] logits tensor; returns
+    the int32 token tensor (or the status when raise_on_error is False)."""
+    B, V = logits.shape
+    if tokens is None:
+        tokens = torch.empty(B, dtype=torch.int32, device=logits.device)
+    st = Q.qd_sample(_ptr(logits), B, V, float(temperature), int(top_k), float(top_p), _ptr(uniforms),
+                     _ptr(tokens), _stream_handle(stream))
+    if not raise_on_error:
+        return st
+    Q.check(st)
+    return tokens
+
+
 class DecodeRunner:
     """Holds the C views of one model's weights, KV pools and block table."""
 

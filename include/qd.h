@@ -168,6 +168,26 @@ qd_status qd_kv_append(const qd_config *cfg, const qd_kv *kv, int32_t layer_inde
 qd_status qd_quantize_rows_int8(const void *w, int32_t w_dtype, int64_t rows, int32_t cols,
                                 int8_t *q, float *scale, void *stream);
 
+/* One next token per row of logits [batch][vocab] (nanoinfer, phase 5), in the
+ * page's order: temperature -> top-k -> top-p -> softmax -> inverse-CDF draw.
+ *   temperature == 0: the argmax (lowest index on a tie); uniforms may be NULL.
+ *   temperature  > 0: z = logits / temperature (float32); top-k keeps every token
+ *     whose logit is >= the k-th largest (ties at the boundary stay), with
+ *     1 <= top_k <= 1024 (other values: QD_EUNSUPPORTED); top-p in (0, 1] sorts
+ *     the survivors ascending by (z, token id), takes the float32 cumulative sum
+ *     of their softmax probabilities in that order, one term at a time, and
+ *     removes every token whose sum is <= float32(1 - top_p), keeping at least
+ *     the largest (top_p = 1 removes none); the kept tokens, in token-id order,
+ *     are drawn by the first whose running probability exceeds u * total, with
+ *     u = uniforms[b] in [0, 1) supplied by the caller.
+ *   tokens [batch] int32 out; -1 for a row where more than 2048 logits tie at
+ *     the top-k boundary.
+ * One workgroup per row, enqueued on `stream`; no device memory is used beyond
+ * the arguments. */
+qd_status qd_sample(const float *logits, int32_t batch, int32_t vocab, float temperature,
+                    int32_t top_k, float top_p, const float *uniforms, int32_t *tokens,
+                    void *stream);
+
 /* Kernel kinds for the optional event timing below. */
 typedef enum {
     QD_K_EMBED = 0, QD_K_QKV = 1, QD_K_QKV_POST = 2, QD_K_ATTN = 3, QD_K_MERGE = 4,

@@ -235,3 +235,16 @@ def test_quantize_checks(lib):
     _expect(Q.qd_quantize_rows_int8(FAKE, Q.QD_BF16, 4, 20, FAKE, FAKE, None), Q.QD_ESHAPE)
     _expect(Q.qd_quantize_rows_int8(FAKE, Q.QD_BF16, 0, 32, FAKE, FAKE, None), Q.QD_ESHAPE)
     _expect(Q.qd_quantize_rows_int8(FAKE + 8, Q.QD_F32, 4, 32, FAKE, FAKE, None), Q.QD_EALIGN)
+
+
+def test_sample_checks(lib):
+    s = Q.qd_sample
+    _expect(s(None, 1, 100, 1.0, 10, 0.9, FAKE, FAKE, None), Q.QD_EINVAL)
+    _expect(s(FAKE, 0, 100, 1.0, 10, 0.9, FAKE, FAKE, None), Q.QD_ESHAPE)
+    _expect(s(FAKE, 1, 100, -1.0, 10, 0.9, FAKE, FAKE, None), Q.QD_EINVAL)
+    _expect(s(FAKE, 1, 100, 1.0, 10, 0.0, FAKE, FAKE, None), Q.QD_EINVAL)
+    _expect(s(FAKE, 1, 100, 1.0, 10, 1.5, FAKE, FAKE, None), Q.QD_EINVAL)
+    _expect(s(FAKE, 1, 100, 1.0, 10, 0.9, None, FAKE, None), Q.QD_EINVAL)
+    _expect(s(FAKE, 1, 100, 1.0, 0, 0.9, FAKE, FAKE, None), Q.QD_EUNSUPPORTED)
+    _expect(s(FAKE, 1, 100, 1.0, 1025, 0.9, FAKE, FAKE, None), Q.QD_EUNSUPPORTED)
+    _expect(s(FAKE + 2, 1, 100, 1.0, 10, 0.9, FAKE, FAKE, None), Q.QD_EALIGN)

@@ -118,9 +118,16 @@ QWEN_8B_BLOCK_PREFILL512 = Workload(
     shape=replace(QWEN_8B_QKNORM, n_layers=1), kind="prefill", batch=1, past=0,
     prefill_tokens=512, block_only=True)
 
+# Sampling the next token of 16 sequences from 0.5B-vocabulary logits ~ N(0, 3) with the
+# settings the nanoinfer page reads from the model (temperature 0.7, top-k 20, top-p 0.8).
+QWEN2_SAMPLER_B16 = Workload(
+    name="qwen2-sampler-b16-t0.7-k20-p0.8", shape=QWEN2_0P5B, kind="sample", batch=16,
+    extra={"temperature": 0.7, "top_k": 20, "top_p": 0.8, "logit_std": 3.0})
+
 WORKLOADS = {w.name: w for w in (QWEN2_BLOCK_F32_PAST16, QWEN2_0P5B_B1_PAST512,
                                  QWEN2_0P5B_B16_PAGED, QWEN_8B_B1_PAST4096,
-                                 QWEN_8B_BLOCK_PREFILL512, QWEN2_0P5B_INT8_B1_PAST512)}
+                                 QWEN_8B_BLOCK_PREFILL512, QWEN2_0P5B_INT8_B1_PAST512,
+                                 QWEN2_SAMPLER_B16)}
 
 
 def tiny_shape(**over) -> ModelShape:
