@@ -534,7 +534,7 @@ qd_status qd_prefill_block(const qd_config* cfg, const qd_layer* layer, int32_t 
     if (start_pos < 0) return fail(QD_EPOSITION, "start_pos %d < 0", start_pos);
     if (!x_in || !x_out) return fail(QD_EINVAL, "x_in or x_out is NULL");
     if (x_dtype != QD_BF16 && x_dtype != QD_F32) return fail(QD_EINVAL, "x_dtype %d", x_dtype);
-    if (!aligned4(x_in) || !aligned4(x_out)) return fail(QD_EALIGN, "x_in / x_out not 4-byte aligned");
+    if (!aligned16(x_in) || !aligned16(x_out)) return fail(QD_EALIGN, "x_in / x_out not 16-byte aligned");
     // every position start .. start + n - 1 must have a page in row 0 of the block table
     const int32_t last = start_pos + n_tokens - 1;
     int max_tokens = 0;

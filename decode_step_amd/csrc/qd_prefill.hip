@@ -230,19 +230,20 @@ constexpr int kDmaLds = 147456;    // bytes of LDS the ring may take
 template <int BM, int BN>
 constexpr int dma_stages() { return kDmaLds / ((BM + BN) * kDmaBK * 2); }
 
-// BM x BN tile, 2 x 2 waves of BM/2 x BN/2 (TI x TJ MFMA tiles of 32 x 32)
-template <int EPI, int BM, int BN>
-__global__ __launch_bounds__(256) void mfma_gemm_dma_kernel(GemmArgs a, int ntn, int ntm, int splits) {
+// BM x BN tile, 2 x (NWV/2) waves of BM/2 x BN/(NWV/2) (TI x TJ MFMA tiles of 32 x 32)
+template <int EPI, int BM, int BN, int NWV = 4>
+__global__ __launch_bounds__(64 * NWV) void mfma_gemm_dma_kernel(GemmArgs a, int ntn, int ntm, int splits) {
     constexpr int BK = kDmaBK, RB = BK * 2;       // row bytes
-    constexpr int TI = BM / 64, TJ = BN / 64;
-    constexpr int QA = BM / 64, QW = BN / 64;    // load instructions (16 rows each) per wave per step
+    constexpr int WGN = NWV / 2;                  // waves along N
+    constexpr int TI = BM / 64, TJ = BN / (32 * WGN);
+    constexpr int QA = BM / (16 * NWV), QW = BN / (16 * NWV);   // load instructions (16 rows each) per wave per step
     constexpr int NQ = QA + QW;
     constexpr int NS = dma_stages<BM, BN>();
     constexpr int SA = BM * RB, SB = (BM + BN) * RB;            // A part, whole stage
     static_assert(NS >= 3 && (NS - 2) * NQ <= 63, "ring depth");
     __shared__ __attribute__((aligned(16))) uint8_t ring[NS * SB];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WGN, wn = wave % WGN;
     const int M = a.M, K = a.K;
 
     // tile and K range of this workgroup; the M tiles of an N tile (and K range) are
@@ -311,8 +312,8 @@ __global__ __launch_bounds__(256) void mfma_gemm_dma_kernel(GemmArgs a, int ntn,
     const int lrow = lane & 31, lhalf = lane >> 5;
     auto wtile_row = [&](int j) {
         if (EPI == GEMM_SWIGLU)
-            return (j < TJ / 2 ? 0 : BN / 2) + wn * (BN / 4) + (j % (TJ / 2)) * 32 + lrow;
-        return wn * (BN / 2) + j * 32 + lrow;
+            return (j < TJ / 2 ? 0 : BN / 2) + wn * (BN / (2 * WGN)) + (j % (TJ / 2)) * 32 + lrow;
+        return wn * (BN / WGN) + j * 32 + lrow;
     };
     auto frag = [&](const uint8_t* base, int row, int ks) {
         const int c = 2 * ks + lhalf;
@@ -358,7 +359,7 @@ __global__ __launch_bounds__(256) void mfma_gemm_dma_kernel(GemmArgs a, int ntn,
             if (EPI == GEMM_SWIGLU) {
 #pragma unroll
                 for (int j = 0; j < TJ / 2; ++j) {
-                    const int hcol = tileN * (BN / 2) + wn * (BN / 4) + j * 32 + lrow;
+                    const int hcol = tileN * (BN / 2) + wn * (BN / (2 * WGN)) + j * 32 + lrow;
                     if (hcol < a.N) {
                         const float g = acc[i][j][e], u = acc[i][j + TJ / 2][e];
                         ((uint16_t*)a.C)[(long)m * a.ldc + hcol] = f32_to_bf16(silu(g) * u);
@@ -367,7 +368,7 @@ __global__ __launch_bounds__(256) void mfma_gemm_dma_kernel(GemmArgs a, int ntn,
             } else {
 #pragma unroll
                 for (int j = 0; j < TJ; ++j) {
-                    const int n = tileN * BN + wn * (BN / 2) + j * 32 + lrow;
+                    const int n = tileN * BN + wn * (BN / WGN) + j * 32 + lrow;
                     if (n >= a.N) continue;
                     float* cp = (float*)a.C + (long)m * a.ldc + n;
                     float v = acc[i][j][e];
@@ -387,6 +388,9 @@ __global__ __launch_bounds__(256) void mfma_gemm_dma_kernel(GemmArgs a, int ntn,
 }
 
 constexpr int kGemmTargetWgs = 256;
+#ifndef QD_GEMM256_WAVES
+#define QD_GEMM256_WAVES 8     // waves of a 256 x 256 tile (2 x 4, 128 x 64 each)
+#endif
 
 // K a multiple of 32: LDS DMA kernel. Tile choice (measured at M = 512 on 256
 // CUs): SwiGLU takes 256 x 256 tiles (two 128 x 128 operand blocks per wave
@@ -429,7 +433,7 @@ hipError_t launch_mfma_gemm(const GemmArgs& a, int epi, int splits, hipStream_t 
     const int cols = epi == GEMM_SWIGLU ? pl.bn / 2 : pl.bn, ntn = (a.N + cols - 1) / cols;
     const dim3 grid(ntn * ntm * splits);
 #define QD_GEMM_DMA(E)                                                                                                  \
-    if (pl.bm == 256) hipLaunchKernelGGL((mfma_gemm_dma_kernel<E, 256, 256>), grid, dim3(256), 0, s, a, ntn, ntm, splits); \
+    if (pl.bm == 256) hipLaunchKernelGGL((mfma_gemm_dma_kernel<E, 256, 256, QD_GEMM256_WAVES>), grid, dim3(64 * QD_GEMM256_WAVES), 0, s, a, ntn, ntm, splits); \
     else if (pl.bn == 256) hipLaunchKernelGGL((mfma_gemm_dma_kernel<E, 128, 256>), grid, dim3(256), 0, s, a, ntn, ntm, splits); \
     else hipLaunchKernelGGL((mfma_gemm_dma_kernel<E, 128, 128>), grid, dim3(256), 0, s, a, ntn, ntm, splits);
     switch (epi) {
@@ -448,29 +452,50 @@ hipError_t launch_mfma_gemm(const GemmArgs& a, int epi, int splits, hipStream_t 
 // residual stream.
 template <typename WT>
 __global__ __launch_bounds__(256) void prefill_norm_kernel(PrefillNormArgs a) {
+    // One row per workgroup; each thread holds chunks of 8 consecutive elements
+    // (16-byte loads and stores), the row read once.
+    constexpr int kMaxChunks = 8;           // D <= 8 * 8 * 256 = 16384
     __shared__ float wsum[4];
     const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int D = a.D;
+    const int D = a.D, nch = D / 8;
     if (a.zero) {   // this row's share of the buffer to clear
         const long per = (a.zero_n + gridDim.x - 1) / gridDim.x;
         const long z0 = (long)row * per, z1 = min(a.zero_n, z0 + per);
         for (long i = z0 + tid; i < z1; i += 256) a.zero[i] = 0.f;
     }
+    float v[kMaxChunks][8];
     float ss = 0.f;
-    for (int d = tid; d < D; d += 256) {
-        const float v = a.x_bf16 ? bf16_to_f32(((const uint16_t*)a.x_bf16)[(long)row * D + d])
-                                 : a.x_f32[(long)row * D + d];
-        ss += v * v;
-        if (a.x_res) a.x_res[(long)row * D + d] = v;
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) {
+        const int ch = tid + 256 * c;
+        if (ch >= nch) break;
+        const long off = (long)row * D + 8 * ch;
+        if (a.x_bf16) {
+            widen16(*(const uint4*)((const uint16_t*)a.x_bf16 + off), v[c]);
+        } else {
+            const float4 p0 = *(const float4*)(a.x_f32 + off), p1 = *(const float4*)(a.x_f32 + off + 4);
+            v[c][0] = p0.x; v[c][1] = p0.y; v[c][2] = p0.z; v[c][3] = p0.w;
+            v[c][4] = p1.x; v[c][5] = p1.y; v[c][6] = p1.z; v[c][7] = p1.w;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss += v[c][e] * v[c][e];
+        if (a.x_res) {
+            *(float4*)(a.x_res + off) = make_float4(v[c][0], v[c][1], v[c][2], v[c][3]);
+            *(float4*)(a.x_res + off + 4) = make_float4(v[c][4], v[c][5], v[c][6], v[c][7]);
+        }
     }
     ss = group_sum<kWave>(ss);
     if (lane == 0) wsum[wave] = ss;
     __syncthreads();
     const float r = 1.0f / sqrtf((wsum[0] + wsum[1] + wsum[2] + wsum[3]) / (float)D + a.eps);
-    for (int d = tid; d < D; d += 256) {
-        const float v = a.x_bf16 ? bf16_to_f32(((const uint16_t*)a.x_bf16)[(long)row * D + d])
-                                 : a.x_f32[(long)row * D + d];
-        a.out[(long)row * D + d] = f32_to_bf16(v * r * load_scalar<WT>(a.gain, d));
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) {
+        const int ch = tid + 256 * c;
+        if (ch >= nch) break;
+        float o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = v[c][e] * r * load_scalar<WT>(a.gain, 8 * ch + e);
+        *(uint4*)(a.out + (long)row * D + 8 * ch) = pack16<uint16_t>(o);
     }
 }
 
@@ -485,62 +510,74 @@ hipError_t launch_prefill_norm(const PrefillNormArgs& a, int w_is_bf16, hipStrea
 // (half-split, angle in double reduced mod 2*pi, sine/cosine in float), q to a
 // float32 buffer, k and v stored into the cache slot of that position in the
 // cache type (keys rotated once, on insert -- nanoinfer page, phase 4). One
-// wavefront per (row, head); lane i rotates the pair (i, i + hd/2).
+// workgroup per row (its angles formed once); lane i rotates the pair
+// (i, i + hd/2) of every 16th head.
+constexpr int kRopeWaves = 16;
 template <typename WT, typename KVT>
-__global__ __launch_bounds__(64) void prefill_rope_append_kernel(PrefillRopeArgs a) {
-    const int row = blockIdx.x, h = blockIdx.y, i = threadIdx.x;
+__global__ __launch_bounds__(64 * kRopeWaves) void prefill_rope_append_kernel(PrefillRopeArgs a) {
+    // One workgroup per row: the row's hd/2 angles once into LDS, then each wave
+    // takes every 16th head, lane i the pair (i, i + hd/2).
+    __shared__ float2 tab[64];
+    const int row = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, i = tid & 63;
     const int hd = a.hd, half = hd >> 1;
     const int p = a.start + row;
     if (p < 0 || p >= a.capacity) return;
-    const int qkvr = (a.Hq + 2 * a.Hkv) * hd;
-    const bool is_q = h < a.Hq;
-    const float* src = a.qkv + (long)row * qkvr + (is_q ? h * hd : a.Hq * hd + (h - a.Hq) * hd);
-    const bool act = i < half;
-    float lo = act ? src[i] : 0.f, hi = act ? src[i + half] : 0.f;
-    if (a.qk_norm) {
-        const float ss = group_sum<kWave>(lo * lo + hi * hi);
-        const float r = 1.0f / sqrtf(ss / (float)hd + a.eps);
-        const void* g = is_q ? a.q_norm : a.k_norm;
-        if (act) {
-            lo = lo * r * load_scalar<WT>(g, i);
-            hi = hi * r * load_scalar<WT>(g, i + half);
-        }
+    if (tid < half) {
+        const double inv = pow((double)a.theta, -2.0 * (double)tid / (double)hd);
+        double ang = (double)p * inv;
+        const double two_pi = 6.283185307179586476925286766559;
+        ang -= two_pi * rint(ang / two_pi);
+        float sn, cs;
+        sincosf((float)ang, &sn, &cs);
+        tab[tid] = make_float2(cs, sn);
     }
-    if (!act) return;
-    const double inv = pow((double)a.theta, -2.0 * (double)i / (double)hd);
-    double ang = (double)p * inv;
-    const double two_pi = 6.283185307179586476925286766559;
-    ang -= two_pi * rint(ang / two_pi);
-    float sn, cs;
-    sincosf((float)ang, &sn, &cs);
-    const float lo2 = lo * cs - hi * sn, hi2 = hi * cs + lo * sn;
-    if (is_q) {
-        float* q = a.q_out + ((long)row * a.Hq + h) * hd;
-        q[i] = lo2;
-        q[i + half] = hi2;
-    } else {
-        const int g = h - a.Hq;
-        const int page_id = a.block_table[p / a.page];
-        if (page_id < 0 || page_id >= a.num_pages) return;
-        const long off = (((long)page_id * a.Hkv + g) * a.page + (p % a.page)) * hd;
-        const float* vs = a.qkv + (long)row * qkvr + (a.Hq + a.Hkv) * hd + g * hd;
-        KVT* kc = (KVT*)a.k_cache + off;
-        KVT* vc = (KVT*)a.v_cache + off;
-        kc[i] = from_f32<KVT>(lo2);
-        kc[i + half] = from_f32<KVT>(hi2);
-        vc[i] = from_f32<KVT>(vs[i]);
-        vc[i + half] = from_f32<KVT>(vs[i + half]);
+    __syncthreads();
+    const int qkvr = (a.Hq + 2 * a.Hkv) * hd;
+    const bool act = i < half;
+    const float2 cs = tab[act ? i : 0];
+    const int page_id = a.block_table[p / a.page];
+    for (int h = wave; h < a.Hq + a.Hkv; h += kRopeWaves) {
+        const bool is_q = h < a.Hq;
+        const float* src = a.qkv + (long)row * qkvr + (is_q ? h * hd : a.Hq * hd + (h - a.Hq) * hd);
+        float lo = act ? src[i] : 0.f, hi = act ? src[i + half] : 0.f;
+        if (a.qk_norm) {
+            const float ss = group_sum<kWave>(lo * lo + hi * hi);
+            const float r = 1.0f / sqrtf(ss / (float)hd + a.eps);
+            const void* g = is_q ? a.q_norm : a.k_norm;
+            if (act) {
+                lo = lo * r * load_scalar<WT>(g, i);
+                hi = hi * r * load_scalar<WT>(g, i + half);
+            }
+        }
+        if (!act) continue;
+        const float lo2 = lo * cs.x - hi * cs.y, hi2 = hi * cs.x + lo * cs.y;
+        if (is_q) {
+            float* q = a.q_out + ((long)row * a.Hq + h) * hd;
+            q[i] = lo2;
+            q[i + half] = hi2;
+        } else {
+            const int g = h - a.Hq;
+            if (page_id < 0 || page_id >= a.num_pages) continue;
+            const long off = (((long)page_id * a.Hkv + g) * a.page + (p % a.page)) * hd;
+            const float* vs = a.qkv + (long)row * qkvr + (a.Hq + a.Hkv) * hd + g * hd;
+            KVT* kc = (KVT*)a.k_cache + off;
+            KVT* vc = (KVT*)a.v_cache + off;
+            kc[i] = from_f32<KVT>(lo2);
+            kc[i + half] = from_f32<KVT>(hi2);
+            vc[i] = from_f32<KVT>(vs[i]);
+            vc[i + half] = from_f32<KVT>(vs[i + half]);
+        }
     }
 }
 
 hipError_t launch_prefill_rope_append(const PrefillRopeArgs& a, int w_is_bf16, int kv_is_bf16, hipStream_t s) {
-    dim3 grid(a.rows, a.Hq + a.Hkv);
+    dim3 grid(a.rows);
     if (w_is_bf16) {
-        if (kv_is_bf16) hipLaunchKernelGGL((prefill_rope_append_kernel<uint16_t, uint16_t>), grid, dim3(64), 0, s, a);
-        else hipLaunchKernelGGL((prefill_rope_append_kernel<uint16_t, float>), grid, dim3(64), 0, s, a);
+        if (kv_is_bf16) hipLaunchKernelGGL((prefill_rope_append_kernel<uint16_t, uint16_t>), grid, dim3(64 * kRopeWaves), 0, s, a);
+        else hipLaunchKernelGGL((prefill_rope_append_kernel<uint16_t, float>), grid, dim3(64 * kRopeWaves), 0, s, a);
     } else {
-        if (kv_is_bf16) hipLaunchKernelGGL((prefill_rope_append_kernel<float, uint16_t>), grid, dim3(64), 0, s, a);
-        else hipLaunchKernelGGL((prefill_rope_append_kernel<float, float>), grid, dim3(64), 0, s, a);
+        if (kv_is_bf16) hipLaunchKernelGGL((prefill_rope_append_kernel<float, uint16_t>), grid, dim3(64 * kRopeWaves), 0, s, a);
+        else hipLaunchKernelGGL((prefill_rope_append_kernel<float, float>), grid, dim3(64 * kRopeWaves), 0, s, a);
     }
     return hipGetLastError();
 }

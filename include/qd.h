@@ -141,7 +141,8 @@ qd_status qd_decode_step(const qd_config *cfg, const qd_weights *w, const qd_kv 
  * table, at positions start_pos .. start_pos + n_tokens - 1, causal (row i
  * attends to positions 0..start_pos+i). bf16 weights only: the projections are
  * MFMA bf16 matrix products with float accumulation, their activation operands
- * rounded to bf16. x_in [N][D] in x_dtype (QD_BF16 or QD_F32); x_out [N][D] float.
+ * rounded to bf16. x_in [N][D] in x_dtype (QD_BF16 or QD_F32); x_out [N][D] float;
+ * both 16-byte aligned.
  * K/V of all N tokens are written into layer `layer`'s cache. */
 qd_status qd_prefill_block(const qd_config *cfg, const qd_layer *layer, int32_t layer_index,
                            const qd_kv *kv, int32_t n_tokens, int32_t start_pos,
