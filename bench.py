@@ -208,7 +208,7 @@ def bench_prefill(wl, args):
     ng, ms_g = Q.qd_profile_read(Q.QD_K_PREFILL_GEMM)
     na, ms_a = Q.qd_profile_read(Q.QD_K_PREFILL_ATTN)
     Q.qd_profile_enable(0)
-    gemm_s = ms_g * 1e-3 / np_          # all four GEMM launches of one block
+    gemm_s = ms_g * 1e-3 / np_          # every GEMM launch of one block (with the down slabs' sum)
     gemm_tfs = gemm_f / gemm_s / 1e12
     print(f"[bench] {wl.name}: {ms:.4f} ms/block, GEMMs {1e6 * gemm_s:.1f} us = {gemm_tfs:.1f} TFLOP/s "
           f"({100 * gemm_tfs / MFMA_BF16_PEAK_TFLOPS:.1f}% of bf16 MFMA peak), attention "
@@ -221,7 +221,9 @@ def bench_prefill(wl, args):
            "block_tflops": round((gemm_f + attn_f) / el * args.steps / 1e12, 1),
            "roofline": {"bound": "mfma", "achieved": round(gemm_tfs, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                         "unit": "TFLOP/s", "frac": round(gemm_tfs / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
-                        "kernel": "mfma_gemm (4 launches per block)", "flops_per_block": int(gemm_f),
+                        "kernel": f"mfma_gemm ({ng // np_} launches per block: q|k|v, o_proj, gate|up, down"
+                                  f"{', the sum of the down K ranges' if ng // np_ > 4 else ''})",
+                        "flops_per_block": int(gemm_f),
                         "avg_block_gemm_us": round(1e6 * gemm_s, 2)},
            "attention_us": round(1e3 * ms_a / np_, 2), "cpu_baseline": None}
     print(json.dumps(rec), flush=True)

@@ -1,6 +1,7 @@
 // C ABI of libqd (declared in include/qd.h): argument checks on the host, the
 // workspace plan, and the in-order launch sequence of one decode step on the
 // caller's stream. Nothing here allocates, synchronises or reads device memory.
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -167,7 +168,8 @@ DecodePlan plan_decode(const qd_config* c, int B, int S, int chunk) {
 }
 
 struct PrefillPlan {
-    size_t off_nrm, off_qkv, off_q, off_part, off_ctx, off_ctxb, off_h, total;
+    size_t off_nrm, off_qkv, off_q, off_part, off_ctx, off_ctxb, off_h, off_slab, total;
+    int slabs_qkv, slabs_o, slabs_down;   // K-range slabs of the wide-tile products (0: other kernels)
 };
 
 PrefillPlan plan_prefill(const qd_config* c, int N, int S) {
@@ -183,6 +185,12 @@ PrefillPlan plan_prefill(const qd_config* c, int N, int S) {
     p.off_ctx = take(4 * (size_t)N * qdim);
     p.off_ctxb = take(2 * (size_t)N * qdim);
     p.off_h = take(2 * (size_t)N * c->ffn);
+    p.slabs_qkv = qd::mfma_gemm_slabs(N, qkvr, c->hidden, qd::GEMM_STORE);
+    p.slabs_o = qd::mfma_gemm_slabs(N, c->hidden, (int)qdim, qd::GEMM_RESID);
+    p.slabs_down = qd::mfma_gemm_slabs(N, c->hidden, c->ffn, qd::GEMM_RESID);
+    const size_t slab_floats = std::max((size_t)p.slabs_qkv * qkvr,
+                                        (size_t)std::max(p.slabs_o, p.slabs_down) * c->hidden) * (size_t)N;
+    p.off_slab = take(4 * slab_floats);   // one region: each product's slabs are consumed before the next
     p.total = o;
     return p;
 }
@@ -562,6 +570,7 @@ qd_status qd_prefill_block(const qd_config* cfg, const qd_layer* layer, int32_t 
     float* ctx = (float*)(ws + P.off_ctx);
     uint16_t* ctxb = (uint16_t*)(ws + P.off_ctxb);
     uint16_t* h = (uint16_t*)(ws + P.off_h);
+    float* slab = (float*)(ws + P.off_slab);
     const qd_layer& L = *layer;
     const int N = n_tokens, D = c.hidden, Hq = c.n_q_heads, Hkv = c.n_kv_heads, hd = c.head_dim;
     const int qkvr = (Hq + 2 * Hkv) * hd;
@@ -576,13 +585,22 @@ qd_status qd_prefill_block(const qd_config* cfg, const qd_layer* layer, int32_t 
     g.A = nrm; g.w[0] = L.wq; g.w[1] = L.wk; g.w[2] = L.wv; g.bias[0] = L.bq; g.bias[1] = L.bk; g.bias[2] = L.bv;
     g.seg_end[0] = Hq * hd; g.seg_end[1] = (Hq + Hkv) * hd; g.seg_end[2] = qkvr;
     g.M = N; g.N = qkvr; g.K = D; g.C = qkv; g.ldc = qkvr;
-    const int qkv_splits = qd::mfma_gemm_splits(g, qd::GEMM_STORE);
-    if (qkv_splits > 1) { nr.zero = qkv; nr.zero_n = (long)N * qkvr; }
-    QD_LAUNCH(qd::launch_prefill_norm(nr, 1, s), "prefill norm");
-    QD_LAUNCH_K(QD_K_PREFILL_GEMM, qd::launch_mfma_gemm(g, qd::GEMM_STORE, qkv_splits, s), "qkv gemm");
-    // [q/k norm] + RoPE; K/V of every row into the cache
     qd::PrefillRopeArgs rp{};
-    rp.qkv = qkv; rp.q_out = qrot; rp.k_cache = kc; rp.v_cache = vc; rp.block_table = kv->block_table;
+    rp.qkv = qkv;
+    if (P.slabs_qkv > 0) {   // K-range slabs; the RoPE kernel adds them and the bias
+        g.C = slab;
+        QD_LAUNCH(qd::launch_prefill_norm(nr, 1, s), "prefill norm");
+        QD_LAUNCH_K(QD_K_PREFILL_GEMM, qd::launch_mfma_gemm_slabs(g, P.slabs_qkv, s), "qkv gemm");
+        rp.qkv = slab; rp.nslab = P.slabs_qkv; rp.slab_stride = (long)N * qkvr;
+        for (int i = 0; i < 3; ++i) { rp.bias[i] = g.bias[i]; rp.seg_end[i] = g.seg_end[i]; }
+    } else {
+        const int qkv_splits = qd::mfma_gemm_splits(g, qd::GEMM_STORE);
+        if (qkv_splits > 1) { nr.zero = qkv; nr.zero_n = (long)N * qkvr; }
+        QD_LAUNCH(qd::launch_prefill_norm(nr, 1, s), "prefill norm");
+        QD_LAUNCH_K(QD_K_PREFILL_GEMM, qd::launch_mfma_gemm(g, qd::GEMM_STORE, qkv_splits, s), "qkv gemm");
+    }
+    // [q/k norm] + RoPE; K/V of every row into the cache
+    rp.q_out = qrot; rp.k_cache = kc; rp.v_cache = vc; rp.block_table = kv->block_table;
     rp.num_pages = kv->num_pages; rp.capacity = kv->max_blocks * c.page_size; rp.start = start_pos; rp.rows = N;
     rp.q_norm = L.q_norm; rp.k_norm = L.k_norm; rp.qk_norm = c.qk_norm; rp.eps = c.rms_eps; rp.theta = c.rope_theta;
     rp.Hq = Hq; rp.Hkv = Hkv; rp.hd = hd; rp.page = c.page_size;
@@ -609,10 +627,16 @@ qd_status qd_prefill_block(const qd_config* cfg, const qd_layer* layer, int32_t 
     qd::GemmArgs go{};
     go.A = ctxb; go.w[0] = L.wo; go.seg_end[0] = go.seg_end[1] = go.seg_end[2] = D;
     go.M = N; go.N = D; go.K = Hq * hd; go.C = x_out; go.ldc = D;
-    QD_LAUNCH_K(QD_K_PREFILL_GEMM, qd::launch_mfma_gemm(go, qd::GEMM_RESID, 0, s), "o_proj gemm");
     // RMSNorm -> bf16; h = silu(n W_g^T) * (n W_u^T) in bf16
     qd::PrefillNormArgs n2{};
     n2.x_f32 = x_out; n2.gain = L.mlp_norm; n2.out = nrm; n2.rows = N; n2.D = D; n2.eps = c.rms_eps;
+    if (P.slabs_o > 0) {   // the MLP norm adds the slabs into the residual as it reads it
+        go.C = slab;
+        QD_LAUNCH_K(QD_K_PREFILL_GEMM, qd::launch_mfma_gemm_slabs(go, P.slabs_o, s), "o_proj gemm");
+        n2.part = slab; n2.nslab = P.slabs_o; n2.slab_stride = (long)N * D; n2.x_res = x_out;
+    } else {
+        QD_LAUNCH_K(QD_K_PREFILL_GEMM, qd::launch_mfma_gemm(go, qd::GEMM_RESID, 0, s), "o_proj gemm");
+    }
     QD_LAUNCH(qd::launch_prefill_norm(n2, 1, s), "prefill mlp norm");
     qd::GemmArgs gu{};
     gu.A = nrm; gu.w[0] = L.w_gate; gu.w[1] = L.w_up; gu.seg_end[0] = gu.seg_end[1] = gu.seg_end[2] = c.ffn;
@@ -622,7 +646,14 @@ qd_status qd_prefill_block(const qd_config* cfg, const qd_layer* layer, int32_t 
     qd::GemmArgs gd{};
     gd.A = h; gd.w[0] = L.w_down; gd.seg_end[0] = gd.seg_end[1] = gd.seg_end[2] = D;
     gd.M = N; gd.N = D; gd.K = c.ffn; gd.C = x_out; gd.ldc = D;
-    QD_LAUNCH_K(QD_K_PREFILL_GEMM, qd::launch_mfma_gemm(gd, qd::GEMM_RESID, 0, s), "down gemm");
+    if (P.slabs_down > 0) {
+        gd.C = slab;
+        QD_LAUNCH_K(QD_K_PREFILL_GEMM, qd::launch_mfma_gemm_slabs(gd, P.slabs_down, s), "down gemm");
+        QD_LAUNCH_K(QD_K_PREFILL_GEMM, qd::launch_add_slabs(x_out, slab, P.slabs_down, (long)N * D, (long)N * D, s),
+                    "down slabs");
+    } else {
+        QD_LAUNCH_K(QD_K_PREFILL_GEMM, qd::launch_mfma_gemm(gd, qd::GEMM_RESID, 0, s), "down gemm");
+    }
     return QD_OK;
 }
 

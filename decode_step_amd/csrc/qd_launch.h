@@ -142,6 +142,14 @@ struct GemmArgs {
 // beforehand, bias added by the first range); splits = 0 picks a value
 hipError_t launch_mfma_gemm(const GemmArgs& a, int epi, int splits, hipStream_t s);
 int mfma_gemm_splits(const GemmArgs& a, int epi);
+// Wide-tile products with float32 partial slabs: mfma_gemm_slabs gives the number
+// of K ranges (slabs) the plan takes for an M x N x K product (0: not this path);
+// launch_mfma_gemm_slabs writes slab s of C = A W^T over K range s to
+// a.C + s * M * ldc (no bias; the consumer adds the slabs and the bias).
+int mfma_gemm_slabs(int M, int N, int K, int epi);
+hipError_t launch_mfma_gemm_slabs(const GemmArgs& a, int slabs, hipStream_t s);
+// x[i] += sum of the nslab slabs part[s * stride + i], i < n
+hipError_t launch_add_slabs(float* x, const float* part, int nslab, long stride, long n, hipStream_t s);
 
 struct PrefillNormArgs {
     const void* x_bf16;     // input rows, bf16 ... or
@@ -153,6 +161,9 @@ struct PrefillNormArgs {
     float eps;
     float* zero;            // optional: zero_n floats cleared (the next split-K GEMM's output)
     long zero_n;
+    const float* part;      // optional (with x_f32): nslab float32 slabs [rows][D], slab_stride
+    int nslab;              // floats apart, added to the input row (x_res gets the sum)
+    long slab_stride;
 };
 hipError_t launch_prefill_norm(const PrefillNormArgs& a, int w_is_bf16, hipStream_t s);
 
@@ -168,6 +179,10 @@ struct PrefillRopeArgs {
     int qk_norm;
     float eps, theta;
     int Hq, Hkv, hd, page;
+    int nslab;              // qkv holds nslab partial slabs slab_stride floats apart (0 or 1: one)
+    long slab_stride;
+    const void* bias[3];    // with slabs: optional bf16 q/k/v biases, segments ending at seg_end
+    int seg_end[3];
 };
 hipError_t launch_prefill_rope_append(const PrefillRopeArgs& a, int w_is_bf16, int kv_is_bf16, hipStream_t s);
 hipError_t launch_to_bf16(const float* x, void* y, long n, hipStream_t s);

@@ -28,6 +28,12 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 
 constexpr int kGemmBM = 128, kGemmBK = 64;
+
+// silu(z) = z / (1 + e^-z) from the hardware exp2 and reciprocal (each within
+// about an ulp), for results rounded to bf16; z -> -inf gives e^-z = inf and 0.
+__device__ __forceinline__ float silu_fast(float z) {
+    return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * 1.4426950408889634f));
+}
 constexpr int kGemmLdsRow = kGemmBK + 8;   // bf16 elements per padded LDS row (144 bytes)
 constexpr int kXcds = 8;
 
@@ -387,6 +393,292 @@ __global__ __launch_bounds__(64 * NWV) void mfma_gemm_dma_kernel(GemmArgs a, int
     }
 }
 
+// ---------------------------------------------------------------------------
+// Wide-tile GEMM (M > 128, K a multiple of 64). What bounds a GEMM of 512 rows
+// here is the bytes each CU pulls from L2: about 50-60 GB/s per CU whatever the
+// number of CUs loading (measured), so the tile is the one that spends the
+// fewest bytes per MAC with one tile per CU: 256 x BN (BN = 192 or 128), four
+// waves of 128 x BN/2 with their accumulators in AGPRs. K steps of 64 make each
+// row's share of a step one whole 128-byte line (rows of 64 bytes measured 2.5x
+// slower to load); they go through an LDS ring (2 stages at BN = 192, 3 at 128)
+// by LDS DMA, rows XOR-swizzled in 16-byte chunks (chunk c of row r at
+// c ^ ((r / 2) % 8), which keeps 16 consecutive rows on distinct banks for the
+// fragment reads). Within a step the fragments of sub-step ks + 1 are read
+// while the MFMAs of sub-step ks run; the one barrier per step sits after the
+// first MFMAs of the last sub-step, so the next step's loads and first reads
+// overlap the rest.
+//
+// Products too small for one tile per CU cut K into `splits` ranges; each range
+// writes its float32 partial product to its own slab C + split * M * ldc (plain
+// stores) and the consumer adds the slabs (no atomics: about 2.4e11 float
+// atomics per second would cost more than the product). SwiGLU tiles hold BN/2
+// gate and the matching BN/2 up columns; the up waves pass their accumulators
+// to the gate waves through LDS, and all four waves form silu(g) * u for half of
+// the rows at a time and store bf16 rows 16 bytes per lane.
+constexpr int kV2BM = 256, kV2BK = 64, kV2RB = 128;
+constexpr int kV2Lds = 159744;
+constexpr int kV2MinWgs = 240;
+
+template <int BN>
+constexpr int v2_stages() { return kV2Lds / ((kV2BM + BN) * kV2RB); }
+__device__ __forceinline__ int v2_swz(int r) { return (r >> 1) & 7; }
+
+template <int EPI, int BN>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mfma_gemm_v2_kernel(GemmArgs a, int ntn, int ntm, int splits) {
+    constexpr int BM = kV2BM, BK = kV2BK, RB = kV2RB, NWV = 4;
+    constexpr int WM = BM / 2, WN = BN / 2, TI = WM / 32, TJ = WN / 32;
+    constexpr int RPI = 8;                                      // rows per DMA instruction
+    constexpr int QA = BM / (RPI * NWV), QW = BN / (RPI * NWV);
+    constexpr int NQ = QA + QW;
+    constexpr int SA = BM * RB, SB = (BM + BN) * RB;
+    constexpr int NS = v2_stages<BN>();
+    constexpr int KS = BK / 16;
+    constexpr int NR = TI + TJ;                                 // fragment reads per sub-step
+    constexpr int PRE = 2;                                      // last-sub-step MFMAs before the barrier
+    constexpr int TP = BN + 8;                                  // floats per row of the SwiGLU tile
+    static_assert(NS >= 2 && (NS - 1) * NQ <= 63, "ring depth");
+    static_assert(EPI != GEMM_SWIGLU || 128 * TP * 4 <= NS * SB, "SwiGLU tile");
+    __shared__ __attribute__((aligned(16))) uint8_t ring[NS * SB];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int M = a.M, K = a.K;
+
+    // tile and K range; the M tiles of one (N tile, K range) are consecutive on one XCD
+    int tileN, tileM, split;
+    {
+        const int id = blockIdx.x, combos = ntn * splits;
+        int c;
+        if (combos % kXcds == 0) {
+            const int slot = id / kXcds;
+            tileM = slot % ntm;
+            c = (slot / ntm) * kXcds + id % kXcds;
+        } else {
+            tileM = (id / combos) % ntm;
+            c = id % combos;
+        }
+        tileN = c / splits;
+        split = c % splits;
+    }
+    const int m0 = tileM * BM;
+
+    // lane's source in DMA instruction q: row RPI (wave Q + q) + lane / 8, logical
+    // chunk (lane % 8) ^ swz(row), landing at physical chunk lane % 8
+    const uint16_t* asrc[QA];
+    const uint16_t* wsrc[QW];
+#pragma unroll
+    for (int q = 0; q < QA; ++q) {
+        const int r = RPI * (wave * QA + q) + (lane >> 3);
+        const int m = m0 + r;
+        asrc[q] = (const uint16_t*)a.A + (long)(m < M ? m : 0) * K + (((lane & 7) ^ v2_swz(r)) * 8);
+    }
+#pragma unroll
+    for (int q = 0; q < QW; ++q) {
+        const int r = RPI * (wave * QW + q) + (lane >> 3);
+        const uint16_t* p;
+        if (EPI == GEMM_SWIGLU) {
+            const int f = tileN * (BN / 2) + (r % (BN / 2));
+            p = (const uint16_t*)a.w[r / (BN / 2)] + (long)(f < a.N ? f : 0) * K;
+        } else {
+            const int n = tileN * BN + r;
+            p = n < a.N ? gemm_wrow(a, n) : (const uint16_t*)a.w[0];
+        }
+        wsrc[q] = p + (((lane & 7) ^ v2_swz(r)) * 8);
+    }
+    const uint32_t ring_lds = lds_addr(ring);
+    const int nk_all = K / BK;
+    const int kt_begin = split * nk_all / splits;
+    const int nk = (split + 1) * nk_all / splits - kt_begin;   // >= 1: the plan keeps splits <= nk_all
+    if (nk < 1) return;
+    auto issue = [&](int buf, int kt) {
+        const int k0 = (kt_begin + kt) * BK;
+        const uint32_t base = ring_lds + buf * SB;
+#pragma unroll
+        for (int q = 0; q < QA; ++q)
+            lds_dma16(asrc[q] + k0, __builtin_amdgcn_readfirstlane(base + RPI * (wave * QA + q) * RB));
+#pragma unroll
+        for (int q = 0; q < QW; ++q)
+            lds_dma16(wsrc[q] + k0, __builtin_amdgcn_readfirstlane(base + SA + RPI * (wave * QW + q) * RB));
+    };
+
+    const int lrow = lane & 31, lhalf = lane >> 5;
+    f32x16_t acc[TI][TJ];
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    auto frag = [&](const uint8_t* base, int row, int ks) {
+        const int c = 2 * ks + lhalf;
+        return as_bf16x8(*(const uint4*)(base + row * RB + ((c ^ v2_swz(row)) << 4)));
+    };
+    bf16x8_t fa[2][TI], fb[2][TJ];
+    auto rd = [&](int buf, int ks, bf16x8_t (&av)[TI], bf16x8_t (&bv)[TJ]) {
+        const uint8_t* st = ring + buf * SB;
+#pragma unroll
+        for (int i = 0; i < TI; ++i) av[i] = frag(st, wm * WM + i * 32 + lrow, ks);
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) bv[j] = frag(st + SA, wn * WN + j * 32 + lrow, ks);
+    };
+    auto mm = [&](const bf16x8_t (&av)[TI], const bf16x8_t (&bv)[TJ], int lo, int hi) {
+#pragma unroll
+        for (int q = 0; q < TI * TJ; ++q)
+            if (q >= lo && q < hi)
+                acc[q / TJ][q % TJ] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[q / TJ], bv[q % TJ], acc[q / TJ][q % TJ], 0, 0, 0);
+    };
+
+    // Ring: steps 0 .. NS-1 issued up front; at step t's barrier every wave has read
+    // stage t (its fragments are in registers) and the DMA of step t + NS takes its
+    // buffer. Past the end the last step is reloaded (unused), so every step issues
+    // NQ loads per lane and one wait count serves all.
+#pragma unroll
+    for (int st = 0; st < NS; ++st) issue(st, st < nk ? st : nk - 1);
+    __builtin_amdgcn_s_waitcnt(wait_vm((NS - 1) * NQ));
+    __builtin_amdgcn_s_barrier();
+    rd(0, 0, fa[0], fb[0]);
+    for (int t = 0; t < nk; ++t) {
+        const int buf = t % NS;
+#pragma unroll
+        for (int ks = 0; ks < KS - 1; ++ks) {
+            rd(buf, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+            mm(fa[ks & 1], fb[ks & 1], 0, TI * TJ);
+#pragma unroll
+            for (int r = 0; r < NR; ++r) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, TI * TJ - NR, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        mm(fa[(KS - 1) & 1], fb[(KS - 1) & 1], 0, PRE);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(wait_vm((NS - 2) * NQ));     // step t + 1 landed (this lane's part)
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);                 // this lane's reads of step t done
+        __builtin_amdgcn_s_barrier();                           // ... and every lane's
+        issue(buf, t + NS < nk ? t + NS : nk - 1);
+        __builtin_amdgcn_sched_barrier(0);
+        rd((t + 1) % NS, 0, fa[0], fb[0]);                      // past the last step: unused
+        mm(fa[(KS - 1) & 1], fb[(KS - 1) & 1], PRE, TI * TJ);
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        if constexpr (TI * TJ - PRE - NR > 0) __builtin_amdgcn_sched_group_barrier(0x008, TI * TJ - PRE - NR, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_waitcnt(wait_vm(0));   // no DMA into LDS outlives the loop
+    __syncthreads();
+
+    if (EPI == GEMM_SWIGLU) {
+        // rows 64 r .. 64 r + 63 of each wave's 128 go through T[128][TP]: gate
+        // columns [0, WN), up columns [WN, 2 WN); then 8 h columns per item
+        float* T = (float*)ring;
+        constexpr int CPR = WN / 8;
+        const int f0 = tileN * WN;
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+#pragma unroll
+            for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+                for (int j = 0; j < TJ; ++j)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        T[(wm * 64 + ii * 32 + (e >> 2) * 8 + lhalf * 4 + (e & 3)) * TP + wn * WN + j * 32 + lrow] =
+                            acc[2 * r + ii][j][e];
+            lds_barrier();
+            for (int item = tid; item < 128 * CPR; item += 256) {
+                const int R = item / CPR, c = item - R * CPR;
+                const int m = m0 + (R >> 6) * WM + r * 64 + (R & 63);
+                const int f = f0 + c * 8;
+                const float4* gp = (const float4*)(T + R * TP + c * 8);
+                const float4* up = (const float4*)(T + R * TP + WN + c * 8);
+                const float4 g0 = gp[0], g1 = gp[1], u0 = up[0], u1 = up[1];
+                const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+                const float u[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+                float hv[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) hv[k] = silu_fast(g[k]) * u[k];
+                if (m < M && f < a.N) *(uint4*)((uint16_t*)a.C + (long)m * a.ldc + f) = pack16<uint16_t>(hv);
+            }
+            lds_barrier();
+        }
+    } else {
+        float* out = (float*)a.C + (long)split * M * a.ldc;
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int m = m0 + wm * WM + i * 32 + (e >> 2) * 8 + lhalf * 4 + (e & 3);
+                if (m >= M) continue;
+#pragma unroll
+                for (int j = 0; j < TJ; ++j) {
+                    const int n = tileN * BN + wn * WN + j * 32 + lrow;
+                    if (n < a.N) out[(long)m * a.ldc + n] = acc[i][j][e];
+                }
+            }
+    }
+}
+
+// Wide-tile plan: use it when M > 128 and K % 64 == 0 (SwiGLU also needs N and
+// ldc multiples of 8 for its 16-byte stores). BN = 192 unless the columns fit
+// 128-wide tiles better; K ranges double while the tiles fill fewer than about
+// one workgroup per CU and each range keeps at least 4 steps.
+struct V2Plan { bool use; int bn, splits; };
+static V2Plan v2_plan(int M, int N, int K, int ldc, int epi) {
+    if (M <= 128 || K % kV2BK != 0 || K < kV2BK) return {false, 0, 0};
+    const int ntm = (M + kV2BM - 1) / kV2BM;
+    if (epi == GEMM_SWIGLU) {
+        if (N % 8 || ldc % 8) return {false, 0, 0};
+        const int bn = (N % 96 != 0 && N % 64 == 0) ? 128 : 192;
+        return {true, bn, 1};
+    }
+    const int bn = (N % 192 != 0 && (N % 128 == 0 || N < 192)) ? 128 : 192;
+    const long tiles = (long)ntm * ((N + bn - 1) / bn);
+    const int nk = K / kV2BK;
+    int s = 1;
+    while (s < 8 && tiles * s < kV2MinWgs && nk / (2 * s) >= 4) s *= 2;
+    return {true, bn, s};
+}
+
+int mfma_gemm_slabs(int M, int N, int K, int epi) {
+    if (epi == GEMM_SWIGLU || N % 4) return 0;
+    const V2Plan p = v2_plan(M, N, K, N, epi);
+    return p.use ? p.splits : 0;
+}
+
+hipError_t launch_mfma_gemm_slabs(const GemmArgs& a, int slabs, hipStream_t s) {
+    const V2Plan p = v2_plan(a.M, a.N, a.K, a.ldc, GEMM_STORE);
+    if (!p.use || slabs != p.splits || a.ldc < a.N) return hipErrorInvalidValue;
+    const int ntm = (a.M + kV2BM - 1) / kV2BM, ntn = (a.N + p.bn - 1) / p.bn;
+    const dim3 grid(ntm * ntn * p.splits);
+    if (p.bn == 192) hipLaunchKernelGGL((mfma_gemm_v2_kernel<GEMM_STORE, 192>), grid, dim3(256), 0, s, a, ntn, ntm, p.splits);
+    else hipLaunchKernelGGL((mfma_gemm_v2_kernel<GEMM_STORE, 128>), grid, dim3(256), 0, s, a, ntn, ntm, p.splits);
+    return hipGetLastError();
+}
+
+// x[i] += sum over s < nslab of part[s * stride + i], n a multiple of 4: the K
+// ranges of a residual product added into the float32 residual stream.
+__global__ __launch_bounds__(256) void add_slabs_kernel(float* x, const float* part, int nslab, long stride, long n4) {
+    for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n4; i += (long)gridDim.x * 256) {
+        float4 v = ((const float4*)x)[i];
+        for (int sl = 0; sl < nslab; ++sl) {
+            const float4 p = ((const float4*)(part + sl * stride))[i];
+            v.x += p.x; v.y += p.y; v.z += p.z; v.w += p.w;
+        }
+        ((float4*)x)[i] = v;
+    }
+}
+
+hipError_t launch_add_slabs(float* x, const float* part, int nslab, long stride, long n, hipStream_t s) {
+    if (n % 4 || stride % 4 || nslab < 1) return hipErrorInvalidValue;
+    long blocks = (n / 4 + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(add_slabs_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, part, nslab, stride, n / 4);
+    return hipGetLastError();
+}
+
 constexpr int kGemmTargetWgs = 256;
 #ifndef QD_GEMM256_WAVES
 #define QD_GEMM256_WAVES 8     // waves of a 256 x 256 tile (2 x 4, 128 x 64 each)
@@ -416,6 +708,16 @@ int mfma_gemm_splits(const GemmArgs& a, int epi) { return gemm_plan(a, epi).spli
 
 hipError_t launch_mfma_gemm(const GemmArgs& a, int epi, int splits, hipStream_t s) {
     if (a.M < 1 || a.N < 1 || a.K < 8 || a.K % 8) return hipErrorInvalidValue;
+    if (epi == GEMM_SWIGLU) {
+        const V2Plan p = v2_plan(a.M, a.N, a.K, a.ldc, GEMM_SWIGLU);
+        if (p.use) {
+            if (splits > 1) return hipErrorInvalidValue;
+            const int ntm = (a.M + kV2BM - 1) / kV2BM, ntn = (a.N + p.bn / 2 - 1) / (p.bn / 2);
+            if (p.bn == 192) hipLaunchKernelGGL((mfma_gemm_v2_kernel<GEMM_SWIGLU, 192>), dim3(ntm * ntn), dim3(256), 0, s, a, ntn, ntm, 1);
+            else hipLaunchKernelGGL((mfma_gemm_v2_kernel<GEMM_SWIGLU, 128>), dim3(ntm * ntn), dim3(256), 0, s, a, ntn, ntm, 1);
+            return hipGetLastError();
+        }
+    }
     const GemmPlan pl = gemm_plan(a, epi);
     if (splits <= 0) splits = pl.splits;
     if (splits != pl.splits) return hipErrorInvalidValue;
@@ -476,6 +778,12 @@ __global__ __launch_bounds__(256) void prefill_norm_kernel(PrefillNormArgs a) {
             const float4 p0 = *(const float4*)(a.x_f32 + off), p1 = *(const float4*)(a.x_f32 + off + 4);
             v[c][0] = p0.x; v[c][1] = p0.y; v[c][2] = p0.z; v[c][3] = p0.w;
             v[c][4] = p1.x; v[c][5] = p1.y; v[c][6] = p1.z; v[c][7] = p1.w;
+            for (int sl = 0; sl < a.nslab; ++sl) {   // K ranges of the product feeding the residual
+                const float* q = a.part + sl * a.slab_stride + off;
+                const float4 q0 = *(const float4*)q, q1 = *(const float4*)(q + 4);
+                v[c][0] += q0.x; v[c][1] += q0.y; v[c][2] += q0.z; v[c][3] += q0.w;
+                v[c][4] += q1.x; v[c][5] += q1.y; v[c][6] += q1.z; v[c][7] += q1.w;
+            }
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) ss += v[c][e] * v[c][e];
@@ -536,10 +844,23 @@ __global__ __launch_bounds__(64 * kRopeWaves) void prefill_rope_append_kernel(Pr
     const bool act = i < half;
     const float2 cs = tab[act ? i : 0];
     const int page_id = a.block_table[p / a.page];
+    // element col of this row's q|k|v: one buffer, or the sum of the K-range slabs
+    // plus the segment's bias
+    const float* rowp = a.qkv + (long)row * qkvr;
+    auto qkv_at = [&](int col) -> float {
+        float v = rowp[col];
+        if (a.nslab > 0) {
+            for (int sl = 1; sl < a.nslab; ++sl) v += rowp[sl * a.slab_stride + col];
+            const bool s0 = col < a.seg_end[0], s1 = col < a.seg_end[1];
+            const void* b = s0 ? a.bias[0] : (s1 ? a.bias[1] : a.bias[2]);
+            if (b) v += load_scalar<WT>(b, col - (s0 ? 0 : (s1 ? a.seg_end[0] : a.seg_end[1])));
+        }
+        return v;
+    };
     for (int h = wave; h < a.Hq + a.Hkv; h += kRopeWaves) {
         const bool is_q = h < a.Hq;
-        const float* src = a.qkv + (long)row * qkvr + (is_q ? h * hd : a.Hq * hd + (h - a.Hq) * hd);
-        float lo = act ? src[i] : 0.f, hi = act ? src[i + half] : 0.f;
+        const int c0 = is_q ? h * hd : a.Hq * hd + (h - a.Hq) * hd;
+        float lo = act ? qkv_at(c0 + i) : 0.f, hi = act ? qkv_at(c0 + i + half) : 0.f;
         if (a.qk_norm) {
             const float ss = group_sum<kWave>(lo * lo + hi * hi);
             const float r = 1.0f / sqrtf(ss / (float)hd + a.eps);
@@ -559,13 +880,13 @@ __global__ __launch_bounds__(64 * kRopeWaves) void prefill_rope_append_kernel(Pr
             const int g = h - a.Hq;
             if (page_id < 0 || page_id >= a.num_pages) continue;
             const long off = (((long)page_id * a.Hkv + g) * a.page + (p % a.page)) * hd;
-            const float* vs = a.qkv + (long)row * qkvr + (a.Hq + a.Hkv) * hd + g * hd;
+            const int vcol = (a.Hq + a.Hkv) * hd + g * hd;
             KVT* kc = (KVT*)a.k_cache + off;
             KVT* vc = (KVT*)a.v_cache + off;
             kc[i] = from_f32<KVT>(lo2);
             kc[i + half] = from_f32<KVT>(hi2);
-            vc[i] = from_f32<KVT>(vs[i]);
-            vc[i + half] = from_f32<KVT>(vs[i + half]);
+            vc[i] = from_f32<KVT>(qkv_at(vcol + i));
+            vc[i + half] = from_f32<KVT>(qkv_at(vcol + i + half));
         }
     }
 }

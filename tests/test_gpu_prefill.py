@@ -58,9 +58,17 @@ def _prefill(case, n, start, x_in):
     return x_out
 
 
+# The last three take the wide-tile GEMMs (more than 128 rows, K a multiple of 64):
+# a ragged last row tile, K-range slabs (2 or 4, with uneven ranges: 17 steps of
+# 64 over 4), column tiles of 128 and 192 with a ragged last one, SwiGLU tiles of
+# 64 h columns, q/k/v biases added from the slabs, and the q/k-norm shape.
 @pytest.mark.parametrize("shape,n", [(SMALL, 37), (SMALL, 130),
                                      (replace(SMALL, qkv_bias=False, qk_norm=True, n_q_heads=8,
-                                              n_kv_heads=2, head_dim=128, hidden=256), 71)])
+                                              n_kv_heads=2, head_dim=128, hidden=256), 71),
+                                     (replace(SMALL, hidden=512, n_q_heads=8, n_kv_heads=2, ffn=1088), 300),
+                                     (replace(SMALL, hidden=320, n_q_heads=5, n_kv_heads=1, ffn=704), 260),
+                                     (replace(SMALL, qkv_bias=False, qk_norm=True, n_q_heads=4, n_kv_heads=2,
+                                              head_dim=128, hidden=512, ffn=1024), 384)])
 def test_small_prefill_block(shape, n):
     case = make_case(shape, np.array([0]), seed=13, extra=n + 1, prefill_tokens=n)
     x = synth.make_x(n, shape.hidden, seed=13, dtype="bf16", device="cuda")
