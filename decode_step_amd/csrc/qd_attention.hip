@@ -105,28 +105,23 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
     const int s = blockIdx.x, g = blockIdx.y / hgroups, hg = blockIdx.y % hgroups, b = blockIdx.z;
     const int h0 = hg * a.hpw, nh = min(a.hpw, G - h0);   // query heads g*G + h0 .. + nh - 1
     const bool prefill = a.prefill_start >= 0;
-    const int p = prefill ? a.prefill_start + b : a.pos[b];
-    if (p < 0 || p >= a.capacity || a.chunk > MAXT || a.hpw > kMaxGroup || nh <= 0) return;
-    const int T = p + 1;
-    const int ns = min(a.S, (T + a.chunk - 1) / a.chunk);
-    const int t_begin = s * a.chunk;
-    if (t_begin >= T) return;
-    const int t_end = min(T, t_begin + a.chunk);
-    const int n = t_end - t_begin;
-    const bool has_new = !prefill && p >= t_begin && p < t_end;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
     const int li = lane % LPT, slot = lane / LPT;
     const int* bt = a.block_table + (prefill ? 0L : (long)b * a.max_blocks);
+    const int t_begin = s * a.chunk;
+    const int pg0 = t_begin / PG;
 
-    // 1. loads of the q/k rotation (one head-chunk of CE elements per thread, LPT
-    //    threads per head; item nh is the new k), issued first so their latency
-    //    overlaps the page-table and K/V loads below
+    // 1. the loads that do not need the position go out together with it: the page
+    //    ids of the split's whole range and the q/k/v rows of the rotation (one
+    //    head-chunk of CE elements per thread, LPT threads per head; item nh is the
+    //    new k, loaded by every split and used by the one that holds p)
+    int pgv = -1;
+    if (tid < (a.chunk + PG - 1) / PG + 1 && pg0 + tid < a.max_blocks) pgv = bt[pg0 + tid];
     const int qkvr = (a.Hq + 2 * a.Hkv) * HD;
-    const int items = prefill ? 0 : (nh + (has_new ? 1 : 0)) * LPT;
-    const bool pro = tid < items;                       // whole LPT-lane groups
+    const bool pro_ld = !prefill && nh > 0 && tid < (nh + 1) * LPT;
     const int phl = tid / LPT, pl2 = tid % LPT, plp2 = pl2 ^ (LPT / 2);
     float u[CE], up[CE], cs[CE], sn[CE], vn[CE];
-    if (pro) {
+    if (pro_ld) {
         const float* src = a.qkv + (long)b * qkvr;
         const float* hsrc = phl < nh ? src + (g * G + h0 + phl) * HD : src + a.Hq * HD + g * HD;
         load_f32xN(hsrc + pl2 * CE, u, CE);
@@ -136,6 +131,15 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
         for (int e = 0; e < CE; ++e) { const float2 t = tab[e]; cs[e] = t.x; sn[e] = t.y; }
         if (phl == nh) load_f32xN(src + (a.Hq + a.Hkv) * HD + g * HD + pl2 * CE, vn, CE);
     }
+    const int p = prefill ? a.prefill_start + b : a.pos[b];
+    if (p < 0 || p >= a.capacity || a.chunk > MAXT || a.hpw > kMaxGroup || nh <= 0) return;
+    const int T = p + 1;
+    const int ns = min(a.S, (T + a.chunk - 1) / a.chunk);
+    if (t_begin >= T) return;
+    const int t_end = min(T, t_begin + a.chunk);
+    const int n = t_end - t_begin;
+    const bool has_new = !prefill && p >= t_begin && p < t_end;
+    const bool pro = pro_ld && tid < (nh + (has_new ? 1 : 0)) * LPT;   // whole LPT-lane groups
     if (prefill) {   // q already normed and rotated
         for (int idx = tid; idx < nh * HD; idx += NT) {
             const int hl = idx / HD, d = idx - hl * HD;
@@ -143,14 +147,10 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
         }
     }
 
-    // 2. page ids of this split's pages (an entry outside the pool reads as page 0
-    //    and is masked), then every K/V row load issued back to back
-    const int pg0 = t_begin / PG;
+    // 2. page ids of this split's pages to LDS (an entry outside the pool reads as
+    //    page 0 and is masked), then every K/V row load issued back to back
     const int npg = (t_end - 1) / PG - pg0 + 1;
-    if (tid < npg) {
-        const int pg = bt[pg0 + tid];
-        spage[tid] = (pg >= 0 && pg < a.num_pages) ? pg : -1;
-    }
+    if (tid < npg) spage[tid] = (pgv >= 0 && pgv < a.num_pages) ? pgv : -1;
     __syncthreads();
     uint4 kraw[NP], vraw[NP];
 #pragma unroll
@@ -433,27 +433,22 @@ __global__ __launch_bounds__(kAmWaves * kWave) void attn_mfma_kernel(AttnArgs a)
 
     const int G = a.Hq / a.Hkv;
     const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-    const int p = a.pos[b];
-    if (p < 0 || p >= a.capacity || a.chunk > kAmChunk || G > kAmHeads) return;
-    const int T = p + 1;
-    const int ns = min(a.S, (T + a.chunk - 1) / a.chunk);
-    const int t_begin = s * a.chunk;
-    if (t_begin >= T) return;
-    const int t_end = min(T, t_begin + a.chunk);
-    const int n = t_end - t_begin;
-    const bool has_new = p >= t_begin && p < t_end;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
     const int c16 = lane & 15, q4 = lane >> 4;
     const int* bt = a.block_table + (long)b * a.max_blocks;
+    const int t_begin = s * a.chunk;
+    const int pg0 = t_begin / PG;
 
-    // 1. loads of the q/k rotation: the G query heads of KV head g and, in the split
-    //    that holds position p, the new k (row G) and v
+    // 1. loads that do not need the position, issued with it: the page ids of the
+    //    split's whole range and the q/k rotation rows (the G query heads of KV
+    //    head g and the new k (row G) and v, used by the split that holds p)
+    int pgv = -1;
+    if (tid < (a.chunk + PG - 1) / PG + 1 && pg0 + tid < a.max_blocks) pgv = bt[pg0 + tid];
     const int qkvr = (a.Hq + 2 * a.Hkv) * HD;
-    const int items = (G + (has_new ? 1 : 0)) * LPT;
-    const bool pro = tid < items;
+    const bool pro_ld = G <= kAmHeads && tid < (G + 1) * LPT;
     const int phl = tid / LPT, pl2 = tid % LPT, plp2 = pl2 ^ (LPT / 2);
     float u[8], up[8], cs[8], sn[8], vn[8];
-    if (pro) {
+    if (pro_ld) {
         const float* src = a.qkv + (long)b * qkvr;
         const float* hsrc = phl < G ? src + (g * G + phl) * HD : src + a.Hq * HD + g * HD;
         load_f32xN(hsrc + pl2 * 8, u, 8);
@@ -463,14 +458,19 @@ __global__ __launch_bounds__(kAmWaves * kWave) void attn_mfma_kernel(AttnArgs a)
         for (int e = 0; e < 8; ++e) { const float2 t = tab[e]; cs[e] = t.x; sn[e] = t.y; }
         if (phl == G) load_f32xN(src + (a.Hq + a.Hkv) * HD + g * HD + pl2 * 8, vn, 8);
     }
+    const int p = a.pos[b];
+    if (p < 0 || p >= a.capacity || a.chunk > kAmChunk || G > kAmHeads) return;
+    const int T = p + 1;
+    const int ns = min(a.S, (T + a.chunk - 1) / a.chunk);
+    if (t_begin >= T) return;
+    const int t_end = min(T, t_begin + a.chunk);
+    const int n = t_end - t_begin;
+    const bool has_new = p >= t_begin && p < t_end;
+    const bool pro = pro_ld && tid < (G + (has_new ? 1 : 0)) * LPT;
 
-    // 2. page ids of the split (an entry outside the pool reads as page 0, masked)
-    const int pg0 = t_begin / PG;
+    // 2. page ids of the split to LDS (an entry outside the pool reads as page 0, masked)
     const int npg = (t_end - 1) / PG - pg0 + 1;
-    if (tid < npg) {
-        const int pg = bt[pg0 + tid];
-        spage[tid] = (pg >= 0 && pg < a.num_pages) ? pg : -1;
-    }
+    if (tid < npg) spage[tid] = (pgv >= 0 && pgv < a.num_pages) ? pgv : -1;
     __syncthreads();
 
     // 3. every K/V load of this wave's blocks (block wave + NWV j of the split): K as
