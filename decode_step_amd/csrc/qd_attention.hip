@@ -49,6 +49,12 @@ constexpr int kAmChunk = kAmWaves * kAmBlocksPerWave * kAmKeys;   // keys per sp
 constexpr int kAmHeads = 16;     // query heads per workgroup at most (the MFMA's columns)
 
 
+// What a masked K/V row load (a key past the split, or without a page in the
+// pool) reads instead of the cache: the load's address is chosen, not its
+// result, so no load waits on a select before the next one is issued. Static
+// device memory, zero from load time and never written (one row, any type).
+__device__ __align__(16) uint32_t kAttnZeros[128];
+
 // 2^x from the hardware exp2 (v_exp_f32); e^x = 2^(x log2 e)
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -120,7 +126,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
     const int qkvr = (a.Hq + 2 * a.Hkv) * HD;
     const bool pro_ld = !prefill && nh > 0 && tid < (nh + 1) * LPT;
     const int phl = tid / LPT, pl2 = tid % LPT, plp2 = pl2 ^ (LPT / 2);
-    float u[CE], up[CE], cs[CE], sn[CE], vn[CE];
+    float u[CE], up[CE], cs[CE], sn[CE], vn[CE], gn[CE], gnp[CE];
     if (pro_ld) {
         const float* src = a.qkv + (long)b * qkvr;
         const float* hsrc = phl < nh ? src + (g * G + h0 + phl) * HD : src + a.Hq * HD + g * HD;
@@ -130,6 +136,11 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
 #pragma unroll
         for (int e = 0; e < CE; ++e) { const float2 t = tab[e]; cs[e] = t.x; sn[e] = t.y; }
         if (phl == nh) load_f32xN(src + (a.Hq + a.Hkv) * HD + g * HD + pl2 * CE, vn, CE);
+        if (a.qk_norm) {   // the per-head norm gains of the lane's elements and partners
+            const void* gain = phl < nh ? a.q_norm : a.k_norm;
+#pragma unroll
+            for (int e = 0; e < CE; ++e) { gn[e] = load_scalar<WT>(gain, pl2 * CE + e); gnp[e] = load_scalar<WT>(gain, plp2 * CE + e); }
+        }
     }
     const int p = prefill ? a.prefill_start + b : a.pos[b];
     if (p < 0 || p >= a.capacity || a.chunk > MAXT || a.hpw > kMaxGroup || nh <= 0) return;
@@ -152,22 +163,19 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
     const int npg = (t_end - 1) / PG - pg0 + 1;
     if (tid < npg) spage[tid] = (pgv >= 0 && pgv < a.num_pages) ? pgv : -1;
     __syncthreads();
+    // (straight-line: a pass past the split reads the zero row, so no load result
+    // is moved or selected before the last load is issued)
     uint4 kraw[NP], vraw[NP];
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
-        if (i * TPB >= n) {   // past this split's tokens (uniform over the workgroup)
-            kraw[i] = vraw[i] = make_uint4(0, 0, 0, 0);
-            continue;
-        }
         const int t = t_begin + i * TPB + wave * TPW + slot;
         const int tt = t < t_end ? t : t_begin;
         const int pg = spage[tt / PG - pg0];
-        const bool ok = t < t_end && (t != p || prefill) && pg >= 0;
+        const bool ok = t < t_end && pg >= 0;   // the row at p is replaced below
         const long off = (((long)max(pg, 0) * a.Hkv + g) * PG + (tt % PG)) * HD + li * CE;
-        const uint4 kv = *(const uint4*)((const KVT*)a.k_cache + off);
-        const uint4 vv = *(const uint4*)((const KVT*)a.v_cache + off);
-        kraw[i] = ok ? kv : make_uint4(0, 0, 0, 0);
-        vraw[i] = ok ? vv : make_uint4(0, 0, 0, 0);
+        const KVT* zr = (const KVT*)kAttnZeros + li * CE;
+        kraw[i] = *(const uint4*)(ok ? (const KVT*)a.k_cache + off : zr);
+        vraw[i] = *(const uint4*)(ok ? (const KVT*)a.v_cache + off : zr);
     }
 
     // 3. [per-head q/k RMSNorm] and RoPE of the loaded rows; the new k and v go to
@@ -179,11 +187,10 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
             for (int e = 0; e < CE; ++e) ss += u[e] * u[e];
             ss = group_sum<LPT>(ss);
             const float r = 1.0f / sqrtf(ss / (float)HD + a.eps);
-            const void* gain = phl < nh ? a.q_norm : a.k_norm;
 #pragma unroll
             for (int e = 0; e < CE; ++e) {
-                u[e] = u[e] * r * load_scalar<WT>(gain, pl2 * CE + e);
-                up[e] = up[e] * r * load_scalar<WT>(gain, plp2 * CE + e);
+                u[e] = u[e] * r * gn[e];
+                up[e] = up[e] * r * gnp[e];
             }
         }
         rope_lane<CE>(u, up, cs, sn, pl2 < LPT / 2);
@@ -447,7 +454,7 @@ __global__ __launch_bounds__(kAmWaves * kWave) void attn_mfma_kernel(AttnArgs a)
     const int qkvr = (a.Hq + 2 * a.Hkv) * HD;
     const bool pro_ld = G <= kAmHeads && tid < (G + 1) * LPT;
     const int phl = tid / LPT, pl2 = tid % LPT, plp2 = pl2 ^ (LPT / 2);
-    float u[8], up[8], cs[8], sn[8], vn[8];
+    float u[8], up[8], cs[8], sn[8], vn[8], gn[8], gnp[8];
     if (pro_ld) {
         const float* src = a.qkv + (long)b * qkvr;
         const float* hsrc = phl < G ? src + (g * G + phl) * HD : src + a.Hq * HD + g * HD;
@@ -457,6 +464,11 @@ __global__ __launch_bounds__(kAmWaves * kWave) void attn_mfma_kernel(AttnArgs a)
 #pragma unroll
         for (int e = 0; e < 8; ++e) { const float2 t = tab[e]; cs[e] = t.x; sn[e] = t.y; }
         if (phl == G) load_f32xN(src + (a.Hq + a.Hkv) * HD + g * HD + pl2 * 8, vn, 8);
+        if (a.qk_norm) {   // the per-head norm gains of the lane's elements and partners
+            const void* gain = phl < G ? a.q_norm : a.k_norm;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) { gn[e] = load_scalar<WT>(gain, pl2 * 8 + e); gnp[e] = load_scalar<WT>(gain, plp2 * 8 + e); }
+        }
     }
     const int p = a.pos[b];
     if (p < 0 || p >= a.capacity || a.chunk > kAmChunk || G > kAmHeads) return;
@@ -482,30 +494,35 @@ __global__ __launch_bounds__(kAmWaves * kWave) void attn_mfma_kernel(AttnArgs a)
     for (int j = 0; j < NBW; ++j) {
         const int kb = wave + NWV * j;
         const int kbase = t_begin + kb * kAmKeys;
+        if (kb * kAmKeys >= n) {   // past the split (uniform over the wave): no loads
+#pragma unroll
+            for (int half = 0; half < 2; ++half)
+#pragma unroll
+                for (int kk = 0; kk < KS; ++kk) kf[j][half][kk] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int jj = 0; jj < VL; ++jj) vf[j][jj] = make_uint4(0, 0, 0, 0);
+            continue;
+        }
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
             const int t = kbase + half * 16 + c16;
             const int tt = t < t_end ? t : t_begin;
             const int pg = spage[tt / PG - pg0];
-            const bool ok = t < t_end && t != p && pg >= 0;
+            const bool ok = t < t_end && pg >= 0;   // the row at p is replaced below
             const long off = (((long)max(pg, 0) * a.Hkv + g) * PG + (tt % PG)) * HD + 8 * q4;
+            const uint16_t* src = ok ? (const uint16_t*)a.k_cache + off : (const uint16_t*)kAttnZeros + 8 * q4;
 #pragma unroll
-            for (int kk = 0; kk < KS; ++kk) {
-                const uint4 v = *(const uint4*)((const uint16_t*)a.k_cache + off + 32 * kk);
-                kf[j][half][kk] = ok ? v : make_uint4(0, 0, 0, 0);
-            }
+            for (int kk = 0; kk < KS; ++kk) kf[j][half][kk] = *(const uint4*)(src + 32 * kk);
         }
         {
             const int t = kbase + (lane & 31);
             const int tt = t < t_end ? t : t_begin;
             const int pg = spage[tt / PG - pg0];
-            const bool ok = t < t_end && t != p && pg >= 0;
+            const bool ok = t < t_end && pg >= 0;
             const long off = (((long)max(pg, 0) * a.Hkv + g) * PG + (tt % PG)) * HD + (lane >> 5) * (HD / 2);
+            const uint16_t* src = ok ? (const uint16_t*)a.v_cache + off : (const uint16_t*)kAttnZeros + (lane >> 5) * (HD / 2);
 #pragma unroll
-            for (int jj = 0; jj < VL; ++jj) {
-                const uint4 v = *(const uint4*)((const uint16_t*)a.v_cache + off + 8 * jj);
-                vf[j][jj] = ok ? v : make_uint4(0, 0, 0, 0);
-            }
+            for (int jj = 0; jj < VL; ++jj) vf[j][jj] = *(const uint4*)(src + 8 * jj);
         }
     }
 
@@ -519,11 +536,10 @@ __global__ __launch_bounds__(kAmWaves * kWave) void attn_mfma_kernel(AttnArgs a)
             for (int e = 0; e < 8; ++e) ss += u[e] * u[e];
             ss = group_sum<LPT>(ss);
             const float r = 1.0f / sqrtf(ss / (float)HD + a.eps);
-            const void* gain = phl < G ? a.q_norm : a.k_norm;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                u[e] = u[e] * r * load_scalar<WT>(gain, pl2 * 8 + e);
-                up[e] = up[e] * r * load_scalar<WT>(gain, plp2 * 8 + e);
+                u[e] = u[e] * r * gn[e];
+                up[e] = up[e] * r * gnp[e];
             }
         }
         rope_lane<8>(u, up, cs, sn, pl2 < LPT / 2);
