@@ -35,15 +35,15 @@ constexpr int kG16U = 4;          // k-steps (of 32) per pipeline stage
 
 __device__ __forceinline__ g16_bf16x8 g16_frag(uint4 v) { return __builtin_bit_cast(g16_bf16x8, v); }
 
-// Loads are issued unconditionally from an address that is always valid (the
-// caller clamps it) and masked afterwards: a load under a per-lane branch makes
-// the compiler wait for every outstanding load before the branch joins, which
-// would empty the prefetch pipeline.
-__device__ __forceinline__ uint4 masked(uint4 v, bool ok) {
-    return ok ? v : make_uint4(0, 0, 0, 0);
-}
-__device__ __forceinline__ float4 masked(float4 v, bool ok) {
-    return ok ? v : make_float4(0.f, 0.f, 0.f, 0.f);
+// Loads are issued unconditionally and masked by their address: a masked lane
+// reads a static zero block instead. (A load under a per-lane branch makes the
+// compiler wait for every outstanding load before the branch joins, and a select
+// on a load's result makes it wait for that load before issuing the next one;
+// either would empty the prefetch pipeline.)
+__device__ __align__(16) uint32_t kG16Zeros[8];   // zero from load time, never written
+template <typename T>
+__device__ __forceinline__ T load_or_zero(const void* p, bool ok) {
+    return *(const T*)(ok ? p : (const void*)kG16Zeros);
 }
 
 template <int EPI, int R, int WK>
@@ -162,7 +162,7 @@ __global__ __launch_bounds__(256) void gemm16_kernel(GemvArgs a) {
                     for (int rb = 0; rb < R; ++rb)
 #pragma unroll
                         for (int n = 0; n < NW; ++n)
-                            w[u][rb][n] = masked(*(const uint4*)(wrow[rb][n] + kc), kok && rok[rb]);
+                            w[u][rb][n] = load_or_zero<uint4>(wrow[rb][n] + kc, kok && rok[rb]);
                 }
             };
             auto mma = [&](const uint4 (&w)[U][R][NW], int sb) {
@@ -334,10 +334,10 @@ __global__ __launch_bounds__(64 * WK) void gemm16_direct_kernel(GemvArgs a) {
             const bool ok = s < s1 && k < K;
             const int kc = ok ? k : 0;
 #pragma unroll
-            for (int n = 0; n < NW; ++n) st.w[u][n] = masked(*(const uint4*)(wrow[n] + kc), ok && rok);
-            st.x0[u] = masked(*(const float4*)(xrow + kc), ok && tok);
-            st.x1[u] = masked(*(const float4*)(xrow + kc + 4), ok && tok);
-            if (GAIN) st.g[u] = masked(*(const uint4*)(gain + kc), ok);
+            for (int n = 0; n < NW; ++n) st.w[u][n] = load_or_zero<uint4>(wrow[n] + kc, ok && rok);
+            st.x0[u] = load_or_zero<float4>(xrow + kc, ok && tok);
+            st.x1[u] = load_or_zero<float4>(xrow + kc + 4, ok && tok);
+            if (GAIN) st.g[u] = load_or_zero<uint4>(gain + kc, ok);
         }
     };
     auto mma = [&](const Stage& st, int sbase) {
@@ -491,10 +491,10 @@ __global__ __launch_bounds__(256) void gemm16_split_kernel(GemvArgs a, int split
         const bool ok = st < s1 && k < K;
         const int kc = ok ? k : 0;
 #pragma unroll
-        for (int n = 0; n < NW; ++n) wv[u][n] = masked(*(const uint4*)(wrow[n] + kc), ok && rok);
-        x0[u] = masked(*(const float4*)(xrow + kc), ok && tok);
-        x1[u] = masked(*(const float4*)(xrow + kc + 4), ok && tok);
-        if (GAIN) gv[u] = masked(*(const uint4*)(gain + kc), ok);
+        for (int n = 0; n < NW; ++n) wv[u][n] = load_or_zero<uint4>(wrow[n] + kc, ok && rok);
+        x0[u] = load_or_zero<float4>(xrow + kc, ok && tok);
+        x1[u] = load_or_zero<float4>(xrow + kc + 4, ok && tok);
+        if (GAIN) gv[u] = load_or_zero<uint4>(gain + kc, ok);
     }
     const int rbase = tile * 16 + kq * 4;
     float yv[4] = {0.f, 0.f, 0.f, 0.f};       // single-range residual: y read with the loads

@@ -125,11 +125,15 @@ __global__ __launch_bounds__(256) void gemv1_kernel(GemvArgs a) {
         }
     };
     int tile = blockIdx.x;
-    issue(tile < ntiles ? tile : ntiles - 1, kc0, true);   // unconditional: no join for the loads to wait at
 
-    // MS > 0: this thread's four context elements from every split, and (threads
-    // below Hq) head tid's split maxima and sums, loaded behind the weights from
-    // clamped (always valid) indices; splits past the valid count are masked below
+    // The vector (or the attention partials) goes out first and the weights right
+    // behind it, so that waiting for it leaves the weights in flight and the RMSNorm
+    // pass (or the merge of the attention splits) runs under their latency; the
+    // wide-row shapes (LPR = 64, the K = 4096+ rows of the 8B-class shape) keep the
+    // weights first (measured: x first costs them about 1%). MS > 0: this thread's
+    // four context elements from every
+    // split, and (threads below Hq) head tid's split maxima and sums, from clamped
+    // (always valid) indices; splits past the valid count are masked below.
     float4 ov[MS > 0 ? MS : 1];
     float2 mlv[MS > 0 ? MS : 1];
     int ns = 0;
@@ -149,9 +153,10 @@ __global__ __launch_bounds__(256) void gemv1_kernel(GemvArgs a) {
         }
         const int p = a.part_pos[0];
         ns = p >= 0 ? min(S, (p + 1 + a.part_chunk - 1) / a.part_chunk) : 0;
-    } else {
-        // x and the gain into LDS by DMA, behind the weights (source indices clamped
-        // to the vectors; what lands past K is never read)
+    }
+    // x and the gain into LDS by DMA (source indices clamped to the vectors; what
+    // lands past K is never read)
+    auto stage_x = [&]() {
         const uint32_t xl = lds_addr(xs);
         for (int j = wave; j < xpad / 256; j += 4) {
             const int f = min(j * 256 + lane * 4, K - 4);
@@ -165,12 +170,27 @@ __global__ __launch_bounds__(256) void gemv1_kernel(GemvArgs a) {
                 lds_dma16((const GT*)a.gain + e, __builtin_amdgcn_readfirstlane(gl + j * 1024));
             }
         }
+    };
+    // the weight loads each lane issues in the first issue() (its bias/residual/scale
+    // loads, which the compiler may turn into scalar loads, are not counted): with
+    // the vector first, waiting until no more than that many vector-memory operations
+    // are outstanding means the vector's loads landed (they retire in issue order)
+    constexpr int kLoadsAfterX = UR * NW * CPL;
+    static_assert(kLoadsAfterX <= 63, "vmcnt range");
+    const int tile0 = tile < ntiles ? tile : ntiles - 1;
+    if constexpr (MS > 0 || LPR < 64) {
+        if constexpr (MS == 0) stage_x();
+        issue(tile0, kc0, true);   // unconditional: no join for the loads to wait at
+        __builtin_amdgcn_s_waitcnt(wait_vm(kLoadsAfterX));   // this wave's vector loads / DMA landed
+    } else {
+        issue(tile0, kc0, true);
+        stage_x();
+        __builtin_amdgcn_s_waitcnt(wait_vm(0));              // this wave's weights and DMA landed
     }
+    lds_barrier();                                           // ... and every wave's DMA
     // counters a later kernel of the step starts from zero
     if (a.zero_ptr && blockIdx.x == 0)
         for (int i = tid; i < a.zero_n; i += 256) a.zero_ptr[i] = 0u;
-    __builtin_amdgcn_s_waitcnt(wait_vm(0));   // this wave's weights and DMA landed
-    lds_barrier();                            // ... and every wave's DMA
 
     if constexpr (MS > 0) {
         // merge of the splits (Tang page, section 2.2: the online-softmax monoid):
