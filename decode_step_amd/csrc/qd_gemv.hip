@@ -411,9 +411,12 @@ static hipError_t gemv1_dispatch(const GemvArgs& a, int cfg, int* grid_out, int 
 // possible); a matrix too tall for that takes the largest such tile and a
 // capped, grid-strided grid; a K no shape covers in one pass keeps the old
 // rule (largest tile with at least 256 workgroups). The lm_head keeps its
-// grid-strided wide tile.
+// grid-strided wide tile. A bf16/float gate|up product counts a round as 1024
+// workgroups (four per CU fit): at the 0.5B shape its 608 eight-row tiles beat
+// 152 32-row ones by about 0.8 us (measured; other products and int8 gain nothing).
 static int gemv1_pick(int N, int K, int epi, int ce) {
     const bool small_k = K <= 2048, i8 = ce == 16;
+    const int round = (epi == EPI_SWIGLU && !i8) ? 4 * kCus : kCus;
     if (epi == EPI_LOGITS) return i8 ? (K <= gemv1_kpass(G_I8_WIDE, ce) ? G_I8_WIDE : G_I8_LONGK)
                                      : (small_k ? G_SMALLK_UR2 : G_BIGK_UR2);
     int best = -1, widest = -1;
@@ -421,7 +424,7 @@ static int gemv1_pick(int N, int K, int epi, int ce) {
         if (gemv1_kpass(c, ce) < K) continue;
         const int tiles = (N + gemv1_rpt(c) - 1) / gemv1_rpt(c);
         // ties on the row tile go to the shape with the least idle lanes (smallest pass)
-        if (tiles <= kCus && (best < 0 || gemv1_rpt(c) < gemv1_rpt(best) ||
+        if (tiles <= round && (best < 0 || gemv1_rpt(c) < gemv1_rpt(best) ||
                               (gemv1_rpt(c) == gemv1_rpt(best) && gemv1_kpass(c, ce) < gemv1_kpass(best, ce))))
             best = c;
         if (widest < 0 || gemv1_rpt(c) > gemv1_rpt(widest) ||
