@@ -9,18 +9,21 @@
 // section 2.5: the causal row sees keys up to its own position). Query tiles
 // with the most keys are dispatched first. Query head h reads KV head h / group.
 //
-// Products: S = Q K^T with Q as the A operand (rows = queries) and K straight
-// from the paged cache as the B operand (a lane's 16-byte fragment is 8
-// consecutive dims of one key row); O += P V with P as the A operand and V as
-// the B operand. Both contractions need operands whose k index runs along
-// memory: Q and K do (the head dim), P and V do not (the key index), so P goes
-// through LDS as a [row][key] tile and V is written into LDS transposed,
-// [dim][key], while it is loaded. The matrix cores take bf16; q and P are
-// float32 here, so each is split into bf16 hi + lo and multiplied twice (K and
-// V are bf16 in the cache and exact), which keeps the products at float32
-// accuracy. The next key block's K/V loads are issued as soon as the current
-// block's K and V have been used (after S = Q K^T and the V transpose), so they
-// land while its softmax and P V run.
+// Products, transposed so that a lane holds one query's scores: S^T = K Q^T with
+// K straight from the paged cache as the A operand (a lane's 16-byte fragment is
+// 8 consecutive dims of one key row) and Q^T as the B operand; the lane (query
+// r32, half hi) then holds its query's scores for 16 of the block's 32 keys, so
+// the block's row maximum is a max over registers and one swap with the other
+// half, and the exponentials are formed once each. Those 16 probabilities are
+// directly the lane's B fragments of P^T for O^T += V^T P^T (the contraction runs
+// over keys in the order the lane holds them: 4 keys of each 8), and the V^T
+// fragment (A operand) reads the same keys, two runs of 4, from the wave's LDS
+// tile, which V is written into transposed ([dim][key]) as it is loaded. The
+// matrix cores take bf16; q and P are float32 here, so each is split into bf16
+// hi + lo and multiplied twice (K and V are bf16 in the cache and exact), which
+// keeps the products at float32 accuracy. The next key block's K/V loads are
+// issued as soon as the current block's K and V have been used (after S^T and the
+// V transpose), so they land while its softmax and P V run.
 //
 // The output is the attention context rounded to bf16, the operand of the
 // o_proj matrix product.
@@ -39,6 +42,10 @@ __device__ __forceinline__ pa_bf16x8 pa_frag(uint4 v) { return __builtin_bit_cas
 
 constexpr int kPaWaves = 4;   // waves per workgroup, each over every 4th key block
 
+// The row a query past the block's rows reads instead of q (static device memory,
+// zero from load time, never written; one head of the widest head dim).
+__device__ __align__(16) float kPaZeros[128];
+
 template <int HD>
 __global__ __launch_bounds__(64 * kPaWaves) __attribute__((amdgpu_waves_per_eu(2))) void prefill_attn_mfma_kernel(PrefillAttnArgs a) {
     constexpr int NWV = kPaWaves;
@@ -46,17 +53,15 @@ __global__ __launch_bounds__(64 * kPaWaves) __attribute__((amdgpu_waves_per_eu(2
     constexpr int CB = HD / 32;          // 32-dim column blocks of the output
     constexpr int VL = HD / 16;          // 16-byte V loads per lane (half a key row)
     constexpr int VTS = kPaKeys + 8;     // bf16 per transposed V row (16-byte aligned, padded)
-    constexpr int PSS = kPaKeys + 4;     // floats per P row
-    constexpr int VT_B = HD * VTS * 2, PS_B = kPaRows * PSS * 4;   // one wave's tiles
-    constexpr int TILES = NWV * (VT_B + PS_B);
+    constexpr int VT_B = HD * VTS * 2;   // one wave's tile
+    constexpr int TILES = NWV * VT_B;
     constexpr int MERGE = (NWV - 1) * (kPaRows * HD + 2 * kPaRows) * 4;
     __shared__ __align__(16) char smem[TILES > MERGE ? TILES : MERGE];
     __shared__ uint4 qfr[2][KS][64];     // Q fragments (bf16 hi, lo) of every lane, shared by the waves
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r32 = lane & 31, hi = lane >> 5;
-    uint16_t (*vt)[VTS] = (uint16_t (*)[VTS])(smem + wave * (VT_B + PS_B));
-    float (*ps)[PSS] = (float (*)[PSS])(smem + wave * (VT_B + PS_B) + VT_B);
+    uint16_t (*vt)[VTS] = (uint16_t (*)[VTS])(smem + wave * VT_B);
     // the longest query tiles (most key blocks) are dispatched first
     const int q0 = (gridDim.x - 1 - blockIdx.x) * kPaRows, h = blockIdx.y;
     const int G = a.Hq / a.Hkv, g = h / G;
@@ -66,36 +71,50 @@ __global__ __launch_bounds__(64 * kPaWaves) __attribute__((amdgpu_waves_per_eu(2
     const int nkb = t_max / kPaKeys + 1;
     const int* bt = a.block_table;
 
+    // Page ids go out first, as the addresses of the first K/V loads: key 0's (the
+    // fallback row) and the page of this lane's key (kb*32 + r32, clamped to t_max)
+    // in the wave's first two blocks; each later block's id is loaded one block
+    // ahead of its K/V loads, so no block waits for a page-table round trip.
+    auto page_of = [&](int kb) -> int {
+        const int t = kb * kPaKeys + r32;
+        return bt[(t <= t_max ? t : t_max) / a.page];
+    };
+    const int pg_key0 = bt[0];
+    int pg_cur = page_of(wave < nkb ? wave : 0);
+    int pg_nxt = page_of(wave + NWV < nkb ? wave + NWV : 0);
+
     // Q fragments: row q0 + r32, dims 16 kk + 8 hi .. + 7, as bf16 hi + lo, formed
-    // once by wave 0 and read from LDS at each block (registers are the limit here)
-    if (wave == 0) {
-        uint4 qh[KS], ql[KS];
+    // once (wave w takes slices kk of its quarter) and read from LDS at each block
+    // (registers are the limit here); a row past N reads the zero row, so no load
+    // waits on a select before the next one goes out
+    {
+        constexpr int KW = (KS + NWV - 1) / NWV;
         const int row = q0 + r32;
-        const bool ok = row < N;
-        const float* qp = a.q + ((long)(ok ? row : 0) * a.Hq + h) * HD + 8 * hi;
+        const float* qp = row < N ? a.q + ((long)row * a.Hq + h) * HD + 8 * hi : kPaZeros + 8 * hi;
+        float4 u[KW], w[KW];
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-            const float4 u = *(const float4*)(qp + 16 * kk);
-            const float4 w = *(const float4*)(qp + 16 * kk + 4);
-            float v[8] = {u.x, u.y, u.z, u.w, w.x, w.y, w.z, w.w};
-            if (!ok)
+        for (int i = 0; i < KW; ++i) {
+            const int kk = wave * KW + i < KS ? wave * KW + i : KS - 1;
+            u[i] = *(const float4*)(qp + 16 * kk);
+            w[i] = *(const float4*)(qp + 16 * kk + 4);
+        }
 #pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] = 0.f;
-            split_hi_lo(v, qh[kk], ql[kk]);
-            qfr[0][kk][lane] = qh[kk];
-            qfr[1][kk][lane] = ql[kk];
+        for (int i = 0; i < KW; ++i) {
+            const int kk = wave * KW + i;
+            if (kk >= KS) break;
+            const float v[8] = {u[i].x, u[i].y, u[i].z, u[i].w, w[i].x, w[i].y, w[i].z, w[i].w};
+            uint4 qh, ql;
+            split_hi_lo(v, qh, ql);
+            qfr[0][kk][lane] = qh;
+            qfr[1][kk][lane] = ql;
         }
     }
-    __syncthreads();
 
-    // Lane's key of block kb: kb*32 + r32. Keys past t_max, or whose page is not in
-    // the pool, read the row of key 0 (a written row) and are masked out.
-    const int pg_key0 = bt[0];
+    // Lane's key of block kb: kb*32 + r32, in page pg. Keys past t_max, or whose page
+    // is not in the pool, read the row of key 0 (a written row) and are masked out.
     const int pg_fallback = (pg_key0 >= 0 && pg_key0 < a.num_pages) ? pg_key0 : 0;
-    auto key_row = [&](int kb, bool& ok) -> long {
+    auto key_row = [&](int kb, int pg, bool& ok) -> long {
         const int t = kb * kPaKeys + r32;
-        const int tc = t <= t_max ? t : t_max;
-        const int pg = bt[tc / a.page];
         ok = t <= t_max && pg >= 0 && pg < a.num_pages;
         const int pgu = ok ? pg : pg_fallback;
         const int tt = ok ? t : 0;
@@ -106,8 +125,8 @@ __global__ __launch_bounds__(64 * kPaWaves) __attribute__((amdgpu_waves_per_eu(2
         uint4 v[VL];
         bool ok;
     };
-    auto load = [&](Blk& b, int kb) {
-        const long off = key_row(kb, b.ok);
+    auto load = [&](Blk& b, int kb, int pg) {
+        const long off = key_row(kb, pg, b.ok);
         const uint16_t* kp = (const uint16_t*)a.k_cache + off + 8 * hi;
         const uint16_t* vp = (const uint16_t*)a.v_cache + off + hi * (HD / 2);
 #pragma unroll
@@ -122,17 +141,19 @@ __global__ __launch_bounds__(64 * kPaWaves) __attribute__((amdgpu_waves_per_eu(2
         asm volatile("" ::: "memory");
     };
 
-    float m[16], l[16];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) { m[e] = -INFINITY; l[e] = 0.f; }
-    pa_f32x16 o[CB];
+    // Lane (query r32, half hi) keeps the running softmax of its query: m in base-2
+    // units (the same in both halves), l its half's share of the sum.
+    float m = -INFINITY, l = 0.f;
+    pa_f32x16 o[CB];                  // O^T: dims cb*32 + (e/4)*8 + hi*4 + e%4 of query r32
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[cb][e] = 0.f;
+    const float scale2 = a.scale * 1.4426950408889634f;
+    const int lim = min(start + q0 + r32, t_max);     // the last key query r32 sees
 
-    // one block: V^T into LDS and S = Q K^T, then the next block's loads go into the
-    // same registers (they land while this block's softmax and P V run)
+    // one block: V^T into LDS and S^T = K Q^T, then the next block's loads go into the
+    // same registers (they land while this block's softmax and O^T += V^T P^T run)
     auto compute = [&](Blk& b, int kb, int next) {
         // V block into LDS, transposed: vt[dim][key]
 #pragma unroll
@@ -145,64 +166,91 @@ __global__ __launch_bounds__(64 * kPaWaves) __attribute__((amdgpu_waves_per_eu(2
                 vt[d0 + 2 * e + 1][r32] = (uint16_t)(w[e] >> 16);
             }
         }
-        // scores of the 32 x 32 tile; lane holds key r32 of rows (e/4)*8 + hi*4 + e%4
+        // S^T of the 32 x 32 tile: K as the A operand, Q^T as the B operand; the lane
+        // then holds query r32's scores of keys (e/4)*8 + hi*4 + e%4
         pa_f32x16 sacc;
 #pragma unroll
         for (int e = 0; e < 16; ++e) sacc[e] = 0.f;
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
-            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa_frag(qfr[0][kk][lane]), pa_frag(b.k[kk]), sacc, 0, 0, 0);
-            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa_frag(qfr[1][kk][lane]), pa_frag(b.k[kk]), sacc, 0, 0, 0);
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa_frag(b.k[kk]), pa_frag(qfr[0][kk][lane]), sacc, 0, 0, 0);
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa_frag(b.k[kk]), pa_frag(qfr[1][kk][lane]), sacc, 0, 0, 0);
         }
-        const bool bok = b.ok;
-        if (next >= 0) load(b, next);
-        const int key = kb * kPaKeys + r32;
+        // which of the block's keys were loaded from a real row: lane r32 loaded key
+        // r32 (bit r32), while the scores this lane holds are other keys'
+        const uint32_t okm = (uint32_t)__ballot(b.ok);
+        if (next >= 0) {
+            // the next block's K/V (its page id came a block ago), then the page id of
+            // the block after it: issued in that order, nothing waits for the fresh one
+            load(b, next, pg_nxt);
+            pg_nxt = page_of(next + NWV < nkb ? next + NWV : 0);
+        }
+        // online softmax of the query over the block (Tang page, section 2.2), scores
+        // in base-2 units so that e^(s - m) is the hardware exp2 of s' - m'
+        float sv[16];
+        float mx = -INFINITY;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-            const int row = (e >> 2) * 8 + hi * 4 + (e & 3);
-            const bool valid = bok && key <= start + q0 + row && key <= t_max;
-            const float sv = valid ? sacc[e] * a.scale : -INFINITY;
-            const float mb = group_max<32>(sv);
-            const float mn = fmaxf(m[e], mb);
-            const float alpha = mn == -INFINITY ? 1.f : expf(m[e] - mn);
-            const float p = valid ? expf(sv - mn) : 0.f;
-            l[e] = l[e] * alpha + group_sum<32>(p);
-            m[e] = mn;
-#pragma unroll
-            for (int cb = 0; cb < CB; ++cb) o[cb][e] *= alpha;
-            ps[row][r32] = p;
+            const int kk = (e >> 2) * 8 + hi * 4 + (e & 3);
+            const bool valid = ((okm >> kk) & 1u) && kb * kPaKeys + kk <= lim;
+            sv[e] = valid ? sacc[e] * scale2 : -INFINITY;
+            mx = fmaxf(mx, sv[e]);
         }
-        wave_sync();
-        // P as A fragments (row r32, keys 16 ks + 8 hi .. + 7), split hi + lo
+        mx = swap32_max(mx);                          // with the other half's 16 keys
+        const float mn = fmaxf(m, mx);
+        const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - mn);
+        float pv[16];
+        float psum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            pv[e] = sv[e] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[e] - mn);
+            psum += pv[e];
+        }
+        l = l * alpha + psum;
+        m = mn;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) o[cb][e] *= alpha;
+        // P^T as B fragments straight from the registers: k-step ks takes e = 8 ks .. + 7,
+        // i.e. keys 16 ks + {hi*4 .. +3, 8 + hi*4 .. +3}; split hi + lo
         uint4 ph[2], pl[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            const float4 u = *(const float4*)&ps[r32][16 * ks + 8 * hi];
-            const float4 w = *(const float4*)&ps[r32][16 * ks + 8 * hi + 4];
-            const float v[8] = {u.x, u.y, u.z, u.w, w.x, w.y, w.z, w.w};
+            float v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = pv[8 * ks + j];
             split_hi_lo(v, ph[ks], pl[ks]);
         }
-        // O += P V: V^T fragments are dim cb*32 + r32, keys 16 ks + 8 hi .. + 7
+        wave_sync();                                  // V^T written by every lane of the wave
+        // O^T += V^T P^T: the V^T fragment of dim cb*32 + r32 takes the same keys, two
+        // runs of 4 from the LDS tile
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                const uint4 vf = *(const uint4*)&vt[cb * 32 + r32][16 * ks + 8 * hi];
-                o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa_frag(ph[ks]), pa_frag(vf), o[cb], 0, 0, 0);
-                o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa_frag(pl[ks]), pa_frag(vf), o[cb], 0, 0, 0);
+                const uint16_t* row = &vt[cb * 32 + r32][16 * ks + 4 * hi];
+                const uint2 v0 = *(const uint2*)row;
+                const uint2 v1 = *(const uint2*)(row + 8);
+                const uint4 vf = make_uint4(v0.x, v0.y, v1.x, v1.y);
+                o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa_frag(vf), pa_frag(ph[ks]), o[cb], 0, 0, 0);
+                o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa_frag(vf), pa_frag(pl[ks]), o[cb], 0, 0, 0);
             }
-        wave_sync();   // the tiles are rewritten by this wave's next block
+        wave_sync();   // the tile is rewritten by this wave's next block
     };
 
-    // this wave's blocks: wave, wave + NWV, ...
+    // this wave's blocks: wave, wave + NWV, ...; the first one's loads go out before
+    // the wait for the Q fragments
     Blk b;
     int kb = wave;
-    if (kb < nkb) load(b, kb);
+    if (kb < nkb) load(b, kb, pg_cur);
+    __syncthreads();                                  // the Q fragments are in LDS
     while (kb < nkb) {
         const int next = kb + NWV;
         compute(b, kb, next < nkb ? next : -1);
         kb = next;
     }
+    l = swap32_sum(l);                                // the query's whole sum in both halves
 
     // the waves' (m, l, o) meet in LDS (the online-softmax merge); wave 0 (which
     // always holds key 0, valid for every row) forms context = O / L in bf16
@@ -211,42 +259,47 @@ __global__ __launch_bounds__(64 * kPaWaves) __attribute__((amdgpu_waves_per_eu(2
     float2* mlw = (float2*)(mo + (NWV - 1) * kPaRows * HD);
     if (wave > 0) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int row = (e >> 2) * 8 + hi * 4 + (e & 3);
+        for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-            for (int cb = 0; cb < CB; ++cb) mo[((wave - 1) * kPaRows + row) * HD + cb * 32 + r32] = o[cb][e];
-            if (r32 == 0) mlw[(wave - 1) * kPaRows + row] = make_float2(m[e], l[e]);
-        }
+            for (int e = 0; e < 16; ++e)
+                mo[((wave - 1) * kPaRows + r32) * HD + cb * 32 + (e >> 2) * 8 + hi * 4 + (e & 3)] = o[cb][e];
+        if (hi == 0) mlw[(wave - 1) * kPaRows + r32] = make_float2(m, l);
     }
     __syncthreads();
     if (wave != 0) return;
+    const int row = q0 + r32;
+    float M = m;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        const int rl = (e >> 2) * 8 + hi * 4 + (e & 3);
-        const int row = q0 + rl;
-        float M = m[e];
+    for (int w = 1; w < NWV; ++w) M = fmaxf(M, mlw[(w - 1) * kPaRows + r32].x);
+    float wt[NWV];
+    wt[0] = __builtin_amdgcn_exp2f(m - M);
+    float L = l * wt[0];
 #pragma unroll
-        for (int w = 1; w < NWV; ++w) M = fmaxf(M, mlw[(w - 1) * kPaRows + rl].x);
-        float wt[NWV];
-        wt[0] = expf(m[e] - M);
-        float L = l[e] * wt[0];
-#pragma unroll
-        for (int w = 1; w < NWV; ++w) {
-            const float2 ml = mlw[(w - 1) * kPaRows + rl];
-            wt[w] = ml.x == -INFINITY ? 0.f : expf(ml.x - M);
-            L = fmaf(ml.y, wt[w], L);
-        }
-        if (row >= N) continue;
-        const float inv = 1.0f / L;
-        uint16_t* dst = a.out + (long)row * a.Hq * HD + h * HD + r32;
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-            float v = o[cb][e] * wt[0];
-#pragma unroll
-            for (int w = 1; w < NWV; ++w) v = fmaf(mo[((w - 1) * kPaRows + rl) * HD + cb * 32 + r32], wt[w], v);
-            dst[cb * 32] = f32_to_bf16(v * inv);
-        }
+    for (int w = 1; w < NWV; ++w) {
+        const float2 ml = mlw[(w - 1) * kPaRows + r32];
+        wt[w] = ml.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml.x - M);
+        L = fmaf(ml.y, wt[w], L);
     }
+    if (row >= N) return;
+    const float inv = 1.0f / L;
+    uint16_t* dst = a.out + (long)row * a.Hq * HD + h * HD;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {             // dims cb*32 + e4*8 + hi*4 .. + 3
+            float v[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int e = 4 * e4 + i, d = cb * 32 + e4 * 8 + hi * 4 + i;
+                float t = o[cb][e] * wt[0];
+#pragma unroll
+                for (int w = 1; w < NWV; ++w) t = fmaf(mo[((w - 1) * kPaRows + r32) * HD + d], wt[w], t);
+                v[i] = t * inv;
+            }
+            const uint2 pk = make_uint2((uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
+                                        (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16));
+            *(uint2*)(dst + cb * 32 + e4 * 8 + hi * 4) = pk;
+        }
 }
 
 hipError_t launch_prefill_attn_mfma(const PrefillAttnArgs& a, hipStream_t s) {
