@@ -51,8 +51,10 @@ __global__ __launch_bounds__(64 * kPaWaves) __attribute__((amdgpu_waves_per_eu(2
     constexpr int NWV = kPaWaves;
     constexpr int KS = HD / 16;          // 16-dim slices of the score product
     constexpr int CB = HD / 32;          // 32-dim column blocks of the output
-    constexpr int VL = HD / 16;          // 16-byte V loads per lane (half a key row)
-    constexpr int VTS = kPaKeys + 8;     // bf16 per transposed V row (16-byte aligned, padded)
+    constexpr int VL = HD / 16;          // 16-byte V loads per lane: 4 keys x DPL dims
+    constexpr int DPL = HD / 8;          // dims of each of its 4 keys a lane loads
+    constexpr int VTS = kPaKeys + 4;     // bf16 per transposed V row (8-byte aligned; 36 spreads the
+                                         // 8 dim groups of a write over the banks)
     constexpr int VT_B = HD * VTS * 2;   // one wave's tile
     constexpr int TILES = NWV * VT_B;
     constexpr int MERGE = (NWV - 1) * (kPaRows * HD + 2 * kPaRows) * 4;
@@ -62,8 +64,18 @@ __global__ __launch_bounds__(64 * kPaWaves) __attribute__((amdgpu_waves_per_eu(2
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r32 = lane & 31, hi = lane >> 5;
     uint16_t (*vt)[VTS] = (uint16_t (*)[VTS])(smem + wave * VT_B);
-    // the longest query tiles (most key blocks) are dispatched first
-    const int q0 = (gridDim.x - 1 - blockIdx.x) * kPaRows, h = blockIdx.y;
+    // (query tile, head) by rank of work (rank k: tile ntile-1 - k/Hq, head k%Hq): the
+    // first half of the dispatch takes the heaviest ranks in order and the second
+    // half the lightest first, so the two workgroups that share a CU (one from each
+    // half, when the whole grid is resident) sum to about the mean work
+    int q0, h;
+    {
+        const int ntile = gridDim.x, total = ntile * a.Hq, half = (total + 1) / 2;
+        const int id = blockIdx.y * ntile + blockIdx.x;
+        const int rank = id < half ? id : total - 1 - (id - half);
+        q0 = (ntile - 1 - rank / a.Hq) * kPaRows;
+        h = rank % a.Hq;
+    }
     const int G = a.Hq / a.Hkv, g = h / G;
     const int N = a.rows, start = a.start;
     const int last_row = min(q0 + kPaRows, N) - 1;
@@ -125,14 +137,26 @@ __global__ __launch_bounds__(64 * kPaWaves) __attribute__((amdgpu_waves_per_eu(2
         uint4 v[VL];
         bool ok;
     };
+    // K: lane's key r32, dims 16 kk + 8 hi (its A fragments). V: lane's keys 4 vq .. + 3
+    // (one page: 4 | page), dims vdg*DPL .. + DPL - 1, so that the transposed tile takes
+    // 4 keys of a dim per 8-byte write; the page of key 4 vq is lane 4 vq's.
+    const int vq = lane & 7, vdg = lane >> 3;
+    const long vrow0 = (((long)pg_fallback * a.Hkv + g) * a.page) * HD;   // key 0's row
     auto load = [&](Blk& b, int kb, int pg) {
         const long off = key_row(kb, pg, b.ok);
         const uint16_t* kp = (const uint16_t*)a.k_cache + off + 8 * hi;
-        const uint16_t* vp = (const uint16_t*)a.v_cache + off + hi * (HD / 2);
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) b.k[kk] = *(const uint4*)(kp + 16 * kk);
+        const int pgv = __shfl(pg, 4 * vq);
+        const bool pgok = pgv >= 0 && pgv < a.num_pages;
 #pragma unroll
-        for (int j = 0; j < VL; ++j) b.v[j] = *(const uint4*)(vp + 8 * j);
+        for (int i = 0; i < 4; ++i) {
+            const int t = kb * kPaKeys + 4 * vq + i;
+            const long vo = (t <= t_max && pgok) ? (((long)pgv * a.Hkv + g) * a.page + (t % a.page)) * HD : vrow0;
+            const uint16_t* vp = (const uint16_t*)a.v_cache + vo + vdg * DPL;
+#pragma unroll
+            for (int c = 0; c < DPL / 8; ++c) b.v[i * (DPL / 8) + c] = *(const uint4*)(vp + 8 * c);
+        }
     };
     // this wave's LDS tiles are its own: ordering them needs only the wave itself
     auto wave_sync = [&]() {
@@ -155,15 +179,18 @@ __global__ __launch_bounds__(64 * kPaWaves) __attribute__((amdgpu_waves_per_eu(2
     // one block: V^T into LDS and S^T = K Q^T, then the next block's loads go into the
     // same registers (they land while this block's softmax and O^T += V^T P^T run)
     auto compute = [&](Blk& b, int kb, int next) {
-        // V block into LDS, transposed: vt[dim][key]
+        // V block into LDS, transposed: vt[dim][key], the lane's 4 keys of a dim packed
+        // into one 8-byte write
 #pragma unroll
-        for (int j = 0; j < VL; ++j) {
-            const uint32_t w[4] = {b.v[j].x, b.v[j].y, b.v[j].z, b.v[j].w};
-            const int d0 = hi * (HD / 2) + 8 * j;
+        for (int c = 0; c < DPL / 8; ++c) {
+            const uint4 k0 = b.v[c], k1 = b.v[DPL / 8 + c], k2 = b.v[2 * (DPL / 8) + c], k3 = b.v[3 * (DPL / 8) + c];
+            const uint32_t w0[4] = {k0.x, k0.y, k0.z, k0.w}, w1[4] = {k1.x, k1.y, k1.z, k1.w};
+            const uint32_t w2[4] = {k2.x, k2.y, k2.z, k2.w}, w3[4] = {k3.x, k3.y, k3.z, k3.w};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                vt[d0 + 2 * e][r32] = (uint16_t)(w[e] & 0xffffu);
-                vt[d0 + 2 * e + 1][r32] = (uint16_t)(w[e] >> 16);
+            for (int e = 0; e < 4; ++e) {   // word e holds dims 2e (low half) and 2e + 1
+                const int d = vdg * DPL + 8 * c + 2 * e;
+                *(uint2*)&vt[d][4 * vq] = make_uint2((w0[e] & 0xffffu) | (w1[e] << 16), (w2[e] & 0xffffu) | (w3[e] << 16));
+                *(uint2*)&vt[d + 1][4 * vq] = make_uint2((w0[e] >> 16) | (w1[e] & 0xffff0000u), (w2[e] >> 16) | (w3[e] & 0xffff0000u));
             }
         }
         // S^T of the 32 x 32 tile: K as the A operand, Q^T as the B operand; the lane
