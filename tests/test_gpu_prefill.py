@@ -81,9 +81,14 @@ def test_small_prefill_block(shape, n):
     _check_kv(case.kv.v[0], case.v_host[0])
 
 
-def test_chunked_prefill_over_a_cache_then_decode():
-    shape = replace(SMALL, vocab=300)
-    n1, n2 = 20, 29
+# The second case: four query heads per KV head at head_dim 128 (the 8B class), a
+# second chunk of 170 rows at an unaligned start (wide-tile GEMMs, several query
+# tiles whose key blocks straddle the chunk boundary).
+@pytest.mark.parametrize("shape,n1,n2", [
+    (replace(SMALL, vocab=300), 20, 29),
+    (replace(SMALL, vocab=300, qkv_bias=False, qk_norm=True, n_q_heads=8, n_kv_heads=2, head_dim=128,
+             hidden=256), 45, 170)])
+def test_chunked_prefill_over_a_cache_then_decode(shape, n1, n2):
     case = make_case(shape, np.array([0]), seed=17, extra=n1 + n2 + 2, prefill_tokens=n1 + n2)
     x = synth.make_x(n1 + n2, shape.hidden, seed=17, dtype="bf16", device="cuda")
     ow = OracleWeights(shape, case.host_w)
