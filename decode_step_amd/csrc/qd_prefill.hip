@@ -752,7 +752,7 @@ hipError_t launch_mfma_gemm(const GemmArgs& a, int epi, int splits, hipStream_t 
 // (nanocompile page, phase 1: sum then divide, eps inside the root). With
 // x_res set, the input row (bf16 or float) is also widened into the float32
 // residual stream.
-template <typename WT>
+template <typename WT, int NSL>
 __global__ __launch_bounds__(256) void prefill_norm_kernel(PrefillNormArgs a) {
     // One row per workgroup; each thread holds chunks of 8 consecutive elements
     // (16-byte loads and stores), the row read once.
@@ -778,7 +778,8 @@ __global__ __launch_bounds__(256) void prefill_norm_kernel(PrefillNormArgs a) {
             const float4 p0 = *(const float4*)(a.x_f32 + off), p1 = *(const float4*)(a.x_f32 + off + 4);
             v[c][0] = p0.x; v[c][1] = p0.y; v[c][2] = p0.z; v[c][3] = p0.w;
             v[c][4] = p1.x; v[c][5] = p1.y; v[c][6] = p1.z; v[c][7] = p1.w;
-            for (int sl = 0; sl < a.nslab; ++sl) {   // K ranges of the product feeding the residual
+#pragma unroll
+            for (int sl = 0; sl < NSL; ++sl) {   // K ranges of the product feeding the residual (all loads issued together)
                 const float* q = a.part + sl * a.slab_stride + off;
                 const float4 q0 = *(const float4*)q, q1 = *(const float4*)(q + 4);
                 v[c][0] += q0.x; v[c][1] += q0.y; v[c][2] += q0.z; v[c][3] += q0.w;
@@ -808,8 +809,18 @@ __global__ __launch_bounds__(256) void prefill_norm_kernel(PrefillNormArgs a) {
 }
 
 hipError_t launch_prefill_norm(const PrefillNormArgs& a, int w_is_bf16, hipStream_t s) {
-    if (w_is_bf16) hipLaunchKernelGGL((prefill_norm_kernel<uint16_t>), dim3(a.rows), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((prefill_norm_kernel<float>), dim3(a.rows), dim3(256), 0, s, a);
+    const int nsl = a.part ? a.nslab : 0;
+#define QD_PN(WT)                                                                                  \
+    switch (nsl) {                                                                                 \
+        case 0: hipLaunchKernelGGL((prefill_norm_kernel<WT, 0>), dim3(a.rows), dim3(256), 0, s, a); break; \
+        case 1: hipLaunchKernelGGL((prefill_norm_kernel<WT, 1>), dim3(a.rows), dim3(256), 0, s, a); break; \
+        case 2: hipLaunchKernelGGL((prefill_norm_kernel<WT, 2>), dim3(a.rows), dim3(256), 0, s, a); break; \
+        case 4: hipLaunchKernelGGL((prefill_norm_kernel<WT, 4>), dim3(a.rows), dim3(256), 0, s, a); break; \
+        case 8: hipLaunchKernelGGL((prefill_norm_kernel<WT, 8>), dim3(a.rows), dim3(256), 0, s, a); break; \
+        default: return hipErrorInvalidValue;                                                      \
+    }
+    if (w_is_bf16) { QD_PN(uint16_t) } else { QD_PN(float) }
+#undef QD_PN
     return hipGetLastError();
 }
 
@@ -821,15 +832,41 @@ hipError_t launch_prefill_norm(const PrefillNormArgs& a, int w_is_bf16, hipStrea
 // workgroup per row (its angles formed once); lane i rotates the pair
 // (i, i + hd/2) of every 16th head.
 constexpr int kRopeWaves = 16;
-template <typename WT, typename KVT>
+template <typename WT, typename KVT, int NSL>
 __global__ __launch_bounds__(64 * kRopeWaves) void prefill_rope_append_kernel(PrefillRopeArgs a) {
-    // One workgroup per row: the row's hd/2 angles once into LDS, then each wave
-    // takes every 16th head, lane i the pair (i, i + hd/2).
+    // One workgroup per row: the row's q|k|v into LDS (the sum of its NSL K-range
+    // slabs plus the bias, or the one buffer when NSL = 0; 16-byte loads, all of a
+    // thread's issued together) while the row's hd/2 angles are formed, then each
+    // wave takes every 16th head, lane i the pair (i, i + hd/2).
     __shared__ float2 tab[64];
+    extern __shared__ __align__(16) float rowv[];   // [(Hq + 2 Hkv) hd]
     const int row = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, i = tid & 63;
     const int hd = a.hd, half = hd >> 1;
     const int p = a.start + row;
     if (p < 0 || p >= a.capacity) return;
+    const int qkvr = (a.Hq + 2 * a.Hkv) * hd;
+    {
+        const float* rowp = a.qkv + (long)row * qkvr;
+        for (int i4 = tid; i4 < qkvr / 4; i4 += 64 * kRopeWaves) {
+            float4 v = *(const float4*)(rowp + 4 * i4);
+#pragma unroll
+            for (int sl = 1; sl < NSL; ++sl) {
+                const float4 t = *(const float4*)(rowp + sl * a.slab_stride + 4 * i4);
+                v.x += t.x; v.y += t.y; v.z += t.z; v.w += t.w;
+            }
+            if (NSL > 0) {   // the segment's bias (segments end on multiples of 4)
+                const int col = 4 * i4;
+                const bool s0 = col < a.seg_end[0], s1 = col < a.seg_end[1];
+                const void* b = s0 ? a.bias[0] : (s1 ? a.bias[1] : a.bias[2]);
+                if (b) {
+                    const int bc = col - (s0 ? 0 : (s1 ? a.seg_end[0] : a.seg_end[1]));
+                    v.x += load_scalar<WT>(b, bc); v.y += load_scalar<WT>(b, bc + 1);
+                    v.z += load_scalar<WT>(b, bc + 2); v.w += load_scalar<WT>(b, bc + 3);
+                }
+            }
+            *(float4*)(rowv + 4 * i4) = v;
+        }
+    }
     if (tid < half) {
         const double inv = pow((double)a.theta, -2.0 * (double)tid / (double)hd);
         double ang = (double)p * inv;
@@ -840,23 +877,10 @@ __global__ __launch_bounds__(64 * kRopeWaves) void prefill_rope_append_kernel(Pr
         tab[tid] = make_float2(cs, sn);
     }
     __syncthreads();
-    const int qkvr = (a.Hq + 2 * a.Hkv) * hd;
     const bool act = i < half;
     const float2 cs = tab[act ? i : 0];
     const int page_id = a.block_table[p / a.page];
-    // element col of this row's q|k|v: one buffer, or the sum of the K-range slabs
-    // plus the segment's bias
-    const float* rowp = a.qkv + (long)row * qkvr;
-    auto qkv_at = [&](int col) -> float {
-        float v = rowp[col];
-        if (a.nslab > 0) {
-            for (int sl = 1; sl < a.nslab; ++sl) v += rowp[sl * a.slab_stride + col];
-            const bool s0 = col < a.seg_end[0], s1 = col < a.seg_end[1];
-            const void* b = s0 ? a.bias[0] : (s1 ? a.bias[1] : a.bias[2]);
-            if (b) v += load_scalar<WT>(b, col - (s0 ? 0 : (s1 ? a.seg_end[0] : a.seg_end[1])));
-        }
-        return v;
-    };
+    auto qkv_at = [&](int col) -> float { return rowv[col]; };
     for (int h = wave; h < a.Hq + a.Hkv; h += kRopeWaves) {
         const bool is_q = h < a.Hq;
         const int c0 = is_q ? h * hd : a.Hq * hd + (h - a.Hq) * hd;
@@ -891,16 +915,26 @@ __global__ __launch_bounds__(64 * kRopeWaves) void prefill_rope_append_kernel(Pr
     }
 }
 
-hipError_t launch_prefill_rope_append(const PrefillRopeArgs& a, int w_is_bf16, int kv_is_bf16, hipStream_t s) {
-    dim3 grid(a.rows);
-    if (w_is_bf16) {
-        if (kv_is_bf16) hipLaunchKernelGGL((prefill_rope_append_kernel<uint16_t, uint16_t>), grid, dim3(64 * kRopeWaves), 0, s, a);
-        else hipLaunchKernelGGL((prefill_rope_append_kernel<uint16_t, float>), grid, dim3(64 * kRopeWaves), 0, s, a);
-    } else {
-        if (kv_is_bf16) hipLaunchKernelGGL((prefill_rope_append_kernel<float, uint16_t>), grid, dim3(64 * kRopeWaves), 0, s, a);
-        else hipLaunchKernelGGL((prefill_rope_append_kernel<float, float>), grid, dim3(64 * kRopeWaves), 0, s, a);
+template <typename WT, typename KVT>
+static hipError_t rope_append_nsl(const PrefillRopeArgs& a, size_t shm, hipStream_t s) {
+    const dim3 grid(a.rows), block(64 * kRopeWaves);
+    switch (a.nslab) {
+        case 0: hipLaunchKernelGGL((prefill_rope_append_kernel<WT, KVT, 0>), grid, block, shm, s, a); break;
+        case 1: hipLaunchKernelGGL((prefill_rope_append_kernel<WT, KVT, 1>), grid, block, shm, s, a); break;
+        case 2: hipLaunchKernelGGL((prefill_rope_append_kernel<WT, KVT, 2>), grid, block, shm, s, a); break;
+        case 4: hipLaunchKernelGGL((prefill_rope_append_kernel<WT, KVT, 4>), grid, block, shm, s, a); break;
+        case 8: hipLaunchKernelGGL((prefill_rope_append_kernel<WT, KVT, 8>), grid, block, shm, s, a); break;
+        default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+hipError_t launch_prefill_rope_append(const PrefillRopeArgs& a, int w_is_bf16, int kv_is_bf16, hipStream_t s) {
+    // the row's q|k|v stays in LDS: (Hq + 2 Hkv) hd floats, at most 64 KB
+    const size_t shm = (size_t)(a.Hq + 2 * a.Hkv) * a.hd * sizeof(float);
+    if (shm > 65536 || a.hd % 4) return hipErrorInvalidValue;
+    if (w_is_bf16) return kv_is_bf16 ? rope_append_nsl<uint16_t, uint16_t>(a, shm, s) : rope_append_nsl<uint16_t, float>(a, shm, s);
+    return kv_is_bf16 ? rope_append_nsl<float, uint16_t>(a, shm, s) : rope_append_nsl<float, float>(a, shm, s);
 }
 
 // Float32 -> bf16 (round half to even), n elements: the attention context as
