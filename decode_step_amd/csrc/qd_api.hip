@@ -67,7 +67,7 @@ qd_status check_config(const qd_config* c) {
 struct DecodePlan {
     int B, D, Hq, Hkv, hd, G, F, V, qkvr;
     int chunk, S;
-    size_t off_x, off_qkv, off_part, off_rope, off_ctx, off_h, off_logits, off_pv, off_pi, total;
+    size_t off_x, off_qkv, off_qss, off_part, off_rope, off_ctx, off_h, off_logits, off_pv, off_pi, total;
 };
 
 // Attention work split. Grouped: one workgroup holds all query heads of a KV
@@ -155,7 +155,9 @@ DecodePlan plan_decode(const qd_config* c, int B, int S, int chunk) {
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o = round_up(o + bytes, 256); return at; };
     p.off_x = take(sizeof(float) * B * p.D);
-    p.off_qkv = take(sizeof(float) * B * p.qkvr);
+    // q|k|v, or (batch 2..16) its K-range partial products and their sums of squares
+    p.off_qkv = take(sizeof(float) * qd::kGemm16MaxStoreSplits * B * p.qkvr);
+    p.off_qss = take(sizeof(float) * qd::kGemm16MaxStoreSplits * B);
     p.off_part = take(sizeof(float) * (size_t)B * p.Hq * S * (p.hd + 2));
     p.off_rope = take(sizeof(float) * 2 * B * (p.hd / 2));
     p.off_ctx = take(sizeof(float) * B * p.Hq * p.hd);
@@ -350,6 +352,8 @@ qd_status qd_decode_step(const qd_config* cfg, const qd_weights* w, const qd_kv*
     char* ws = (char*)workspace;
     float* x = (float*)(ws + P.off_x);
     float* qkv = (float*)(ws + P.off_qkv);
+    float* qss = (float*)(ws + P.off_qss);
+    const int qkv_splits = qd::gemm16_store_splits(P.D, P.qkvr);
     float* part = (float*)(ws + P.off_part);
     float2* part_ml = (float2*)(part + (size_t)batch * P.Hq * S * P.hd);
     float2* rope = (float2*)(ws + P.off_rope);
@@ -389,7 +393,6 @@ qd_status qd_decode_step(const qd_config* cfg, const qd_weights* w, const qd_kv*
         g.wscale[0] = L.s_q; g.wscale[1] = L.s_k; g.wscale[2] = L.s_v;
         g.nseg = 3; g.N = P.qkvr; g.K = D; g.B = B; g.x = x; g.gain = L.attn_norm; g.eps = c.rms_eps;
         g.y = qkv; g.kt = gemv_kt(B, D);
-        QD_LAUNCH_K(QD_K_QKV, gemv(g, qd::EPI_STORE, kGemvGridCap, nullptr), "qkv gemv");
         // [q/k norm] + RoPE + KV append + split-K attention + merge
         qd::AttnArgs at{};
         at.qkv = qkv; at.k_cache = kv->k_pages_host[l]; at.v_cache = kv->v_pages_host[l];
@@ -400,6 +403,14 @@ qd_status qd_decode_step(const qd_config* cfg, const qd_weights* w, const qd_kv*
         at.Hq = P.Hq; at.Hkv = P.Hkv; at.hd = P.hd; at.page = c.page_size; at.chunk = P.chunk; at.S = P.S;
         at.B = B; at.hpw = hpw; at.scale = 1.0f / sqrtf((float)P.hd);
         at.prefill_start = -1; at.q_rot = nullptr;
+        // batch 2..16 on the matrix cores: q|k|v as K-range partial products, which
+        // the attention kernel finishes (RMSNorm scale, bias) as it loads them
+        if (B > 1 && wbf && qkv_splits > 1 && qd::attn_uses_mfma(at, kvbf)) {
+            g.ss_out = qss;
+            at.qkv_slabs = qkv_splits; at.qkv_slab_stride = (long)B * P.qkvr; at.qkv_ss = qss;
+            at.qkv_bias[0] = L.bq; at.qkv_bias[1] = L.bk; at.qkv_bias[2] = L.bv; at.x_dim = D;
+        }
+        QD_LAUNCH_K(QD_K_QKV, gemv(g, qd::EPI_STORE, kGemvGridCap, nullptr), "qkv gemv");
         QD_LAUNCH_K(QD_K_ATTN, qd::launch_attention(at, wbf, kvbf, s), "attention");
         // o_proj + residual
         qd::GemvArgs go{};

@@ -418,7 +418,7 @@ typedef __attribute__((ext_vector_type(4))) float am_f32x4;
 __device__ __forceinline__ am_bf16x8 am_frag(uint4 v) { return __builtin_bit_cast(am_bf16x8, v); }
 
 
-template <typename WT, int HD>
+template <typename WT, int HD, int NSL>
 __global__ __launch_bounds__(kAmWaves * kWave) void attn_mfma_kernel(AttnArgs a) {
     constexpr int NWV = kAmWaves, NBW = kAmBlocksPerWave;
     constexpr int NT = NWV * kWave;
@@ -451,26 +451,61 @@ __global__ __launch_bounds__(kAmWaves * kWave) void attn_mfma_kernel(AttnArgs a)
     //    head g and the new k (row G) and v, used by the split that holds p)
     int pgv = -1;
     if (tid < (a.chunk + PG - 1) / PG + 1 && pg0 + tid < a.max_blocks) pgv = bt[pg0 + tid];
+    const int p = a.pos[b];
     const int qkvr = (a.Hq + 2 * a.Hkv) * HD;
     const bool pro_ld = G <= kAmHeads && tid < (G + 1) * LPT;
     const int phl = tid / LPT, pl2 = tid % LPT, plp2 = pl2 ^ (LPT / 2);
     float u[8], up[8], cs[8], sn[8], vn[8], gn[8], gnp[8];
+    // q|k|v rows: the finished projection (NSL = 1), or its K-range partial products
+    // (NSL slabs, the count given by the arguments, slabs past it read zeros), summed
+    // after the barrier below as r * sum + bias with r the RMSNorm scale of the step's
+    // input. Either way the loads go out here, with the position and the page ids,
+    // and nothing waits for them before that barrier.
+    constexpr bool PART = NSL > 1;
+    float t[NSL][3][8], ssv[NSL];
+    uint32_t bq[3][4];              // biases (PART), bf16 pairs (4-byte aligned: biases need no more)
     if (pro_ld) {
         const float* src = a.qkv + (long)b * qkvr;
-        const float* hsrc = phl < G ? src + (g * G + phl) * HD : src + a.Hq * HD + g * HD;
-        load_f32xN(hsrc + pl2 * 8, u, 8);
-        load_f32xN(hsrc + plp2 * 8, up, 8);
+        const int hoff = phl < G ? (g * G + phl) * HD : a.Hq * HD + g * HD;
+        const int voff = (a.Hq + a.Hkv) * HD + g * HD;
+        const float* z = (const float*)kAttnZeros;
+#pragma unroll
+        for (int sl = 0; sl < NSL; ++sl) {
+            const bool on = !PART || sl < a.qkv_slabs;
+            const float* ss = src + (long)sl * a.qkv_slab_stride;
+            load_f32xN(on ? ss + hoff + pl2 * 8 : z, t[sl][0], 8);
+            load_f32xN(on ? ss + hoff + plp2 * 8 : z, t[sl][1], 8);
+            load_f32xN(on && phl == G ? ss + voff + pl2 * 8 : z, t[sl][2], 8);
+            if (PART) ssv[sl] = *(on ? a.qkv_ss + sl * a.B + b : z);
+        }
+        if (PART) {
+            // bias rows of the lane's head (pointers chosen among scalar registers)
+            gbyte* const zb = (gbyte*)kAttnZeros;
+            gbyte* const pq = sgpr_gptr(a.qkv_bias[0]);
+            gbyte* const pk = sgpr_gptr(a.qkv_bias[1]);
+            gbyte* const pv = sgpr_gptr(a.qkv_bias[2]);
+            const bool hq = a.qkv_bias[0] != nullptr, hk = a.qkv_bias[1] != nullptr, hv = a.qkv_bias[2] != nullptr;
+            const bool oh = phl < G ? hq : hk, ov = hv && phl == G;
+            gbyte* const bh = phl < G ? pq + 2 * (g * G + phl) * HD : pk + 2 * g * HD;
+            gbyte* const b0 = oh ? bh + 2 * pl2 * 8 : zb;
+            gbyte* const b1 = oh ? bh + 2 * plp2 * 8 : zb;
+            gbyte* const b2 = ov ? pv + 2 * (g * HD + pl2 * 8) : zb;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                bq[0][e] = *(const __attribute__((address_space(1))) uint32_t*)(b0 + 4 * e);
+                bq[1][e] = *(const __attribute__((address_space(1))) uint32_t*)(b1 + 4 * e);
+                bq[2][e] = *(const __attribute__((address_space(1))) uint32_t*)(b2 + 4 * e);
+            }
+        }
         const float2* tab = a.rope + (long)b * (HD / 2) + (pl2 % (LPT / 2)) * 8;
 #pragma unroll
         for (int e = 0; e < 8; ++e) { const float2 t = tab[e]; cs[e] = t.x; sn[e] = t.y; }
-        if (phl == G) load_f32xN(src + (a.Hq + a.Hkv) * HD + g * HD + pl2 * 8, vn, 8);
         if (a.qk_norm) {   // the per-head norm gains of the lane's elements and partners
             const void* gain = phl < G ? a.q_norm : a.k_norm;
 #pragma unroll
             for (int e = 0; e < 8; ++e) { gn[e] = load_scalar<WT>(gain, pl2 * 8 + e); gnp[e] = load_scalar<WT>(gain, plp2 * 8 + e); }
         }
     }
-    const int p = a.pos[b];
     if (p < 0 || p >= a.capacity || a.chunk > kAmChunk || G > kAmHeads) return;
     const int T = p + 1;
     const int ns = min(a.S, (T + a.chunk - 1) / a.chunk);
@@ -484,6 +519,28 @@ __global__ __launch_bounds__(kAmWaves * kWave) void attn_mfma_kernel(AttnArgs a)
     const int npg = (t_end - 1) / PG - pg0 + 1;
     if (tid < npg) spage[tid] = (pgv >= 0 && pgv < a.num_pages) ? pgv : -1;
     __syncthreads();
+    if (pro_ld) {
+        float ssl = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { u[e] = t[0][0][e]; up[e] = t[0][1][e]; vn[e] = t[0][2][e]; }
+        if (PART) ssl = ssv[0];
+#pragma unroll
+        for (int sl = 1; sl < NSL; ++sl) {
+            ssl += ssv[sl];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) { u[e] += t[sl][0][e]; up[e] += t[sl][1][e]; vn[e] += t[sl][2][e]; }
+        }
+        if (PART) {
+            const float r = 1.0f / sqrtf(ssl / (float)a.x_dim + a.eps);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int sh = (e & 1) ? 16 : 0;
+                u[e] = u[e] * r + bf16_to_f32((bq[0][e >> 1] >> sh) & 0xffffu);
+                up[e] = up[e] * r + bf16_to_f32((bq[1][e >> 1] >> sh) & 0xffffu);
+                vn[e] = vn[e] * r + bf16_to_f32((bq[2][e >> 1] >> sh) & 0xffffu);
+            }
+        }
+    }
 
     // 3. every K/V load of this wave's blocks (block wave + NWV j of the split): K as
     //    A fragments (key half*16 + c16, dims 32 kk + 8 q4), V rows (key lane % 32,
@@ -753,19 +810,26 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a) {
     }
 }
 
+bool attn_uses_mfma(const AttnArgs& a, int kv_is_bf16) {
+    const int G = a.Hq / a.Hkv;
+    return kv_is_bf16 && a.prefill_start < 0 && a.hpw == G && G <= kAmHeads &&
+           (G + 1) * (a.hd / 8) <= kAmWaves * kWave && a.chunk <= kAmChunk && (a.hd == 64 || a.hd == 128);
+}
+
 hipError_t launch_attention(const AttnArgs& a, int w_is_bf16, int kv_is_bf16, hipStream_t s) {
     if (a.page != kAttnPage) return hipErrorInvalidValue;
     const int G = a.Hq / a.Hkv;
     const int hgroups = (G + a.hpw - 1) / a.hpw;
-    const bool mfma = kv_is_bf16 && a.prefill_start < 0 && a.hpw == G && G <= kAmHeads &&
-                      (G + 1) * (a.hd / 8) <= kAmWaves * kWave && a.chunk <= kAmChunk &&
-                      (a.hd == 64 || a.hd == 128);
+    const bool mfma = attn_uses_mfma(a, kv_is_bf16);
+    if (a.qkv_slabs > 0 && (!mfma || !w_is_bf16 || a.qkv_slabs > kGemm16MaxStoreSplits || !a.qkv_ss || a.x_dim < 1))
+        return hipErrorInvalidValue;
     if (mfma) {
         const dim3 grid(a.S, a.Hkv, a.B), block(kAmWaves * kWave);
-#define QD_AM(WT)                                                                             \
-        if (a.hd == 64) hipLaunchKernelGGL((attn_mfma_kernel<WT, 64>), grid, block, 0, s, a); \
-        else hipLaunchKernelGGL((attn_mfma_kernel<WT, 128>), grid, block, 0, s, a);
-        if (w_is_bf16) { QD_AM(uint16_t) } else { QD_AM(float) }
+#define QD_AM(WT, NSL)                                                                             \
+        if (a.hd == 64) hipLaunchKernelGGL((attn_mfma_kernel<WT, 64, NSL>), grid, block, 0, s, a); \
+        else hipLaunchKernelGGL((attn_mfma_kernel<WT, 128, NSL>), grid, block, 0, s, a);
+        if (a.qkv_slabs > 0) { QD_AM(uint16_t, kGemm16MaxStoreSplits) }
+        else if (w_is_bf16) { QD_AM(uint16_t, 1) } else { QD_AM(float, 1) }
 #undef QD_AM
         hipError_t e = hipGetLastError();
         if (e != hipSuccess || a.S == 1 || a.part_always) return e;

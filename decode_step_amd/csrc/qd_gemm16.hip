@@ -22,6 +22,8 @@
 // MFMA B-fragment layout, [k/8][token] of 16-byte groups, hi and lo apart, so
 // a fragment read is one conflict-free 16-byte LDS read per lane. Weight
 // fragments are loaded U k-steps ahead of their use.
+#include <algorithm>
+
 #include "qd_device.h"
 #include "qd_launch.h"
 
@@ -32,6 +34,7 @@ typedef __attribute__((ext_vector_type(4))) float g16_f32x4;
 
 constexpr int kG16Chunk = 1024;   // K elements staged per chunk: 64 KB of LDS for 16 tokens
 constexpr int kG16U = 4;          // k-steps (of 32) per pipeline stage
+constexpr int kG16Cus = 256;      // compute units of the chip (MI355X)
 
 __device__ __forceinline__ g16_bf16x8 g16_frag(uint4 v) { return __builtin_bit_cast(g16_bf16x8, v); }
 
@@ -437,21 +440,184 @@ __global__ __launch_bounds__(64 * WK) void gemm16_direct_kernel(GemvArgs a) {
     }
 }
 
+// Normed products with more 16-row blocks than the chip has CUs (gate|up at the
+// 0.5B shape: 304 blocks of gate and up rows). With one block per workgroup every
+// workgroup would load the whole activation (16 tokens x K float32, as many bytes
+// as its own weights) through its CU's load path, which is what bounds these
+// kernels, and some CUs would take two workgroups. Here the grid is one
+// workgroup per CU and workgroup w takes rows [N w / G, N (w + 1) / G) in RB
+// MFMA blocks of 16 starting at its first row (rows past its range read the zero
+// block), so every CU loads an equal share of the weights and the activation
+// once: the tokens' rows (zeros past B) and the gain go into LDS by DMA, ahead of
+// the weights, then every wave issues its weight loads for all of its k-steps
+// at once (RB blocks x NW matrices), waits only for the DMA, and runs each
+// step's MFMAs as its weights land. The four waves split K and meet in LDS in a
+// fixed order. LDS layout of the activation: 32-byte units (8 float32 of one
+// token), unit ((s * 4 + q) * 16 + t) = token t, k = 32 s + 8 q .. + 8, so a
+// fragment read is two conflict-free 16-byte reads per lane.
+template <int EPI, int RB, int SPW>
+__global__ __launch_bounds__(256) void gemm16_rows_kernel(GemvArgs a) {
+    constexpr int NW = (EPI == EPI_SWIGLU) ? 2 : 1;
+    constexpr int NLD = SPW * RB * NW;      // weight loads per lane
+    static_assert(NLD <= 63, "vmcnt range");
+    extern __shared__ __align__(16) char g16r_smem[];
+    __shared__ float ssum[4][16];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+    const int col = lane & 15, kq = lane >> 4;
+    const int B = a.B, K = a.K, N = a.N;
+    const int nsteps = K / 32;
+    const int r0 = (int)((long)N * blockIdx.x / gridDim.x), r1 = (int)((long)N * (blockIdx.x + 1) / gridDim.x);
+    float* xs = (float*)g16r_smem;
+    const uint16_t* gs = (const uint16_t*)(g16r_smem + nsteps * 2048);
+
+    // 1. activation and gain by DMA (each 1 KB instruction fills 32 units)
+    {
+        const uint32_t xl = lds_addr(xs), gl = lds_addr(gs);
+        for (int c = wave; c < nsteps * 2; c += 4) {
+            const int u = c * 32 + (lane >> 1);
+            const int t = u & 15, k = (u >> 4) * 8 + (lane & 1) * 4;
+            const void* src = t < B ? (const void*)(a.x + (long)t * K + k) : (const void*)kG16Zeros;
+            lds_dma16(src, __builtin_amdgcn_readfirstlane(xl + c * 1024));
+        }
+        for (int c = wave; c < (K * 2 + 1023) / 1024; c += 4) {
+            const int e = min(c * 512 + lane * 8, K - 8);       // what lands past K is never read
+            lds_dma16((const uint16_t*)a.gain + e, __builtin_amdgcn_readfirstlane(gl + c * 1024));
+        }
+    }
+    // 2. this wave's weights: steps s0 + u (past s1, and rows past r1, read the zero block)
+    const int s0 = wave * nsteps / 4, s1 = (wave + 1) * nsteps / 4;
+    const uint16_t* wrow[RB][NW];
+    bool rok[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        const int r = r0 + rb * 16 + col;
+        rok[rb] = r < r1;
+#pragma unroll
+        for (int n = 0; n < NW; ++n) {
+            const uint16_t* p = (const uint16_t*)a.w[n];
+            if (r < r1) {
+                if (EPI == EPI_SWIGLU) {
+                    p = (const uint16_t*)a.w[n] + (long)r * K;
+                } else {
+                    const bool q0 = r < a.seg_end[0], q1 = r < a.seg_end[1];
+                    const void* w = q0 ? a.w[0] : (q1 ? a.w[1] : a.w[2]);
+                    const int base = q0 ? 0 : (q1 ? a.seg_end[0] : a.seg_end[1]);
+                    p = (const uint16_t*)w + (long)(r - base) * K;
+                }
+            }
+            wrow[rb][n] = p;
+        }
+    }
+    uint4 wv[SPW][RB][NW];
+#pragma unroll
+    for (int u = 0; u < SPW; ++u) {
+        const int st = s0 + u;
+        const bool ok = st < s1;
+        const int k = ok ? st * 32 + kq * 8 : 0;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int n = 0; n < NW; ++n) wv[u][rb][n] = load_or_zero<uint4>(wrow[rb][n] + k, ok && rok[rb]);
+    }
+    __builtin_amdgcn_s_waitcnt(wait_vm(NLD));   // this wave's DMA landed (loads retire in issue order)
+    lds_barrier();                              // ... and every wave's
+    if (a.zero_ptr && blockIdx.x == 0)
+        for (int i = tid; i < a.zero_n; i += 256) a.zero_ptr[i] = 0u;
+
+    // 3. MFMAs, step by step
+    g16_f32x4 acc[RB][NW];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int n = 0; n < NW; ++n) acc[rb][n] = g16_f32x4{0.f, 0.f, 0.f, 0.f};
+    float ss = 0.f;
+#pragma unroll
+    for (int u = 0; u < SPW; ++u) {
+        const int st = s0 + u;
+        if (st >= s1) break;
+        const float* xp = xs + ((st * 4 + kq) * 16 + col) * 8;
+        const float4 p0 = *(const float4*)xp, p1 = *(const float4*)(xp + 4);
+        float gf[8];
+        widen16(*(const uint4*)(gs + st * 32 + kq * 8), gf);
+        float v[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            ss += v[e] * v[e];
+            v[e] *= gf[e];
+        }
+        uint4 hu, lu;
+        split_hi_lo(v, hu, lu);
+        const g16_bf16x8 bh = g16_frag(hu), bl = g16_frag(lu);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int n = 0; n < NW; ++n) {
+                const g16_bf16x8 af = g16_frag(wv[u][rb][n]);
+                acc[rb][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bh, acc[rb][n], 0, 0, 0);
+                acc[rb][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bl, acc[rb][n], 0, 0, 0);
+            }
+    }
+
+    // 4. the four waves' partial products and sums of squares meet in wave 0 (the
+    //    activation's LDS holds the partials once every wave is done reading it)
+    {
+        const float t = strided_sum<16>(ss);
+        if (lane < 16) ssum[wave][lane] = t;
+    }
+    g16_f32x4* red = (g16_f32x4*)g16r_smem;     // [3][RB][NW][64]
+    lds_barrier();
+    if (wave > 0)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int n = 0; n < NW; ++n) red[(((wave - 1) * RB + rb) * NW + n) * kWave + lane] = acc[rb][n];
+    lds_barrier();
+    if (wave != 0 || col >= B) return;
+#pragma unroll
+    for (int q = 0; q < 3; ++q)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int n = 0; n < NW; ++n) acc[rb][n] += red[((q * RB + rb) * NW + n) * kWave + lane];
+    const float rs = 1.0f / sqrtf((ssum[0][col] + ssum[1][col] + ssum[2][col] + ssum[3][col]) / (float)K + a.eps);
+    float* yrow = a.y + (long)col * N;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        const int rbase = r0 + rb * 16 + kq * 4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = rbase + e;
+            if (r >= r1) break;
+            const float v0 = acc[rb][0][e] * rs;
+            if (EPI == EPI_SWIGLU) {
+                yrow[r] = silu(v0) * (acc[rb][NW - 1][e] * rs);
+            } else {
+                const bool q0 = r < a.seg_end[0], q1 = r < a.seg_end[1];
+                const void* bsel = q0 ? a.bias[0] : (q1 ? a.bias[1] : a.bias[2]);
+                const int base = q0 ? 0 : (q1 ? a.seg_end[0] : a.seg_end[1]);
+                yrow[r] = bsel ? v0 + load_scalar<uint16_t>(bsel, r - base) : v0;
+            }
+        }
+    }
+}
+
 // Single-shot form for matrices whose K range fits the workgroup's registers:
 // every wave issues all of its k-steps' loads (weights, activation, gain) at
-// once, then runs its MFMAs. The grid is (16-row blocks, K splits); K is cut into
-// `splits` ranges of 32-wide steps and each range over the 4 waves, at most SPW
-// steps per wave. A residual product with several K ranges adds its partial
-// sums into y with float atomics (each range's sum is complete and fixed; only
-// the order of the final few additions varies from run to run); every other
-// epilogue takes one range (splits = 1), so its output is formed once.
-template <int EPI, int SPW>
+// once, then runs its MFMAs. The grid is (groups of R 16-row blocks, K splits);
+// K is cut into `splits` ranges of 32-wide steps and each range over the 4
+// waves, at most SPW steps per wave; the R blocks of a group share each
+// activation fragment. A residual product with several K ranges adds its
+// partial sums into y with float atomics (each range's sum is complete and
+// fixed; only the order of the final few additions varies from run to run);
+// every other epilogue takes one range (splits = 1), so its output is formed
+// once.
+template <int EPI, int SPW, int R>
 __global__ __launch_bounds__(256) void gemm16_split_kernel(GemvArgs a, int splits) {
     constexpr bool GAIN = EPI != EPI_RESID;
     constexpr int NW = (EPI == EPI_SWIGLU) ? 2 : 1;
     constexpr int WK = 4;
     __shared__ float ssum[WK][16];
-    __shared__ g16_f32x4 red[WK - 1][NW][kWave];
+    __shared__ g16_f32x4 red[WK - 1][R][NW][kWave];
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
     const int col = lane & 15, kq = lane >> 4;
     const int B = a.B, K = a.K, N = a.N;
@@ -463,25 +629,29 @@ __global__ __launch_bounds__(256) void gemm16_split_kernel(GemvArgs a, int split
     const int a0 = ks * nsteps / splits, a1 = (ks + 1) * nsteps / splits;
     const int s0 = a0 + wave * (a1 - a0) / WK, s1 = a0 + (wave + 1) * (a1 - a0) / WK;
 
-    const uint16_t* wrow[NW];        // a row past N reads row 0 (masked)
-    const int r_own = tile * 16 + col;
-    const bool rok = r_own < N;
+    const uint16_t* wrow[R][NW];     // a row past N reads row 0 (masked)
+    bool rok[R];
 #pragma unroll
-    for (int n = 0; n < NW; ++n) {
-        const uint16_t* p = (const uint16_t*)a.w[n];
-        if (rok) {
-            if (EPI == EPI_SWIGLU) {
-                p = (const uint16_t*)a.w[n] + (long)r_own * K;
-            } else {
-                const bool q0 = r_own < a.seg_end[0], q1 = r_own < a.seg_end[1];
-                const void* w = q0 ? a.w[0] : (q1 ? a.w[1] : a.w[2]);
-                const int base = q0 ? 0 : (q1 ? a.seg_end[0] : a.seg_end[1]);
-                p = (const uint16_t*)w + (long)(r_own - base) * K;
+    for (int rb = 0; rb < R; ++rb) {
+        const int r_own = (tile * R + rb) * 16 + col;
+        rok[rb] = r_own < N;
+#pragma unroll
+        for (int n = 0; n < NW; ++n) {
+            const uint16_t* p = (const uint16_t*)a.w[n];
+            if (rok[rb]) {
+                if (EPI == EPI_SWIGLU) {
+                    p = (const uint16_t*)a.w[n] + (long)r_own * K;
+                } else {
+                    const bool q0 = r_own < a.seg_end[0], q1 = r_own < a.seg_end[1];
+                    const void* w = q0 ? a.w[0] : (q1 ? a.w[1] : a.w[2]);
+                    const int base = q0 ? 0 : (q1 ? a.seg_end[0] : a.seg_end[1]);
+                    p = (const uint16_t*)w + (long)(r_own - base) * K;
+                }
             }
+            wrow[rb][n] = p;
         }
-        wrow[n] = p;
     }
-    uint4 wv[SPW][NW];
+    uint4 wv[SPW][R][NW];
     float4 x0[SPW], x1[SPW];
     uint4 gv[SPW];
 #pragma unroll
@@ -491,25 +661,30 @@ __global__ __launch_bounds__(256) void gemm16_split_kernel(GemvArgs a, int split
         const bool ok = st < s1 && k < K;
         const int kc = ok ? k : 0;
 #pragma unroll
-        for (int n = 0; n < NW; ++n) wv[u][n] = load_or_zero<uint4>(wrow[n] + kc, ok && rok);
+        for (int rb = 0; rb < R; ++rb)
+#pragma unroll
+            for (int n = 0; n < NW; ++n) wv[u][rb][n] = load_or_zero<uint4>(wrow[rb][n] + kc, ok && rok[rb]);
         x0[u] = load_or_zero<float4>(xrow + kc, ok && tok);
         x1[u] = load_or_zero<float4>(xrow + kc + 4, ok && tok);
         if (GAIN) gv[u] = load_or_zero<uint4>(gain + kc, ok);
     }
-    const int rbase = tile * 16 + kq * 4;
-    float yv[4] = {0.f, 0.f, 0.f, 0.f};       // single-range residual: y read with the loads
+    float yv[R][4] = {};                      // single-range residual: y read with the loads
     if (EPI == EPI_RESID && splits == 1) {
         const float* yrow = a.y + (long)(tok ? col : 0) * N;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = rbase + e;
-            const float t = yrow[r < N ? r : 0];
-            yv[e] = (tok && r < N) ? t : 0.f;
-        }
-    }
-    g16_f32x4 acc[NW];
+        for (int rb = 0; rb < R; ++rb)
 #pragma unroll
-    for (int n = 0; n < NW; ++n) acc[n] = g16_f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int e = 0; e < 4; ++e) {
+                const int r = (tile * R + rb) * 16 + kq * 4 + e;
+                const float t = yrow[r < N ? r : 0];
+                yv[rb][e] = (tok && r < N) ? t : 0.f;
+            }
+    }
+    g16_f32x4 acc[R][NW];
+#pragma unroll
+    for (int rb = 0; rb < R; ++rb)
+#pragma unroll
+        for (int n = 0; n < NW; ++n) acc[rb][n] = g16_f32x4{0.f, 0.f, 0.f, 0.f};
     float ss = 0.f;
 #pragma unroll
     for (int u = 0; u < SPW; ++u) {
@@ -528,11 +703,13 @@ __global__ __launch_bounds__(256) void gemm16_split_kernel(GemvArgs a, int split
         const g16_bf16x8 bh = g16_frag(hu);
         const g16_bf16x8 bl = g16_frag(lu);
 #pragma unroll
-        for (int n = 0; n < NW; ++n) {
-            const g16_bf16x8 af = g16_frag(wv[u][n]);
-            acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bh, acc[n], 0, 0, 0);
-            acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bl, acc[n], 0, 0, 0);
-        }
+        for (int rb = 0; rb < R; ++rb)
+#pragma unroll
+            for (int n = 0; n < NW; ++n) {
+                const g16_bf16x8 af = g16_frag(wv[u][rb][n]);
+                acc[rb][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bh, acc[rb][n], 0, 0, 0);
+                acc[rb][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bl, acc[rb][n], 0, 0, 0);
+            }
     }
     // the four waves' partial products and sums of squares meet in wave 0, in a fixed order
     if (GAIN) {
@@ -541,53 +718,108 @@ __global__ __launch_bounds__(256) void gemm16_split_kernel(GemvArgs a, int split
     }
     if (wave > 0)
 #pragma unroll
-        for (int n = 0; n < NW; ++n) red[wave - 1][n][lane] = acc[n];
+        for (int rb = 0; rb < R; ++rb)
+#pragma unroll
+            for (int n = 0; n < NW; ++n) red[wave - 1][rb][n][lane] = acc[rb][n];
     __syncthreads();
     if (wave != 0 || !tok) return;
 #pragma unroll
     for (int q = 0; q < WK - 1; ++q)
 #pragma unroll
-        for (int n = 0; n < NW; ++n) acc[n] += red[q][n][lane];
+        for (int rb = 0; rb < R; ++rb)
+#pragma unroll
+            for (int n = 0; n < NW; ++n) acc[rb][n] += red[q][rb][n][lane];
     float rs = 1.0f;
     if (GAIN) {
         float t = 0.f;
 #pragma unroll
         for (int q = 0; q < WK; ++q) t += ssum[q][col];
         rs = 1.0f / sqrtf(t / (float)K + a.eps);
+        if (EPI == EPI_STORE && a.ss_out) {   // partial form: this range's products and sum of squares
+            if (tile == 0 && kq == 0) a.ss_out[ks * B + col] = t;
+            float* prow = a.y + ((long)ks * B + col) * N;
+            const int rbase = tile * 16 + kq * 4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (rbase + e < N) prow[rbase + e] = acc[0][0][e];
+            return;
+        }
     }
     float* yrow = a.y + (long)col * N;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int r = rbase + e;
-        if (r >= N) break;
-        const float v0 = acc[0][e] * rs;
-        if (EPI == EPI_STORE) {
-            const bool q0 = r < a.seg_end[0], q1 = r < a.seg_end[1];
-            const void* bsel = q0 ? a.bias[0] : (q1 ? a.bias[1] : a.bias[2]);
-            const int base = q0 ? 0 : (q1 ? a.seg_end[0] : a.seg_end[1]);
-            yrow[r] = bsel ? v0 + load_scalar<uint16_t>(bsel, r - base) : v0;
-        } else if (EPI == EPI_RESID) {
-            if (splits == 1) yrow[r] = yv[e] + v0;
-            else unsafeAtomicAdd(yrow + r, v0);
-        } else {
-            yrow[r] = silu(v0) * (acc[NW - 1][e] * rs);
+    for (int rb = 0; rb < R; ++rb) {
+        const int rbase = (tile * R + rb) * 16 + kq * 4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = rbase + e;
+            if (r >= N) break;
+            const float v0 = acc[rb][0][e] * rs;
+            if (EPI == EPI_STORE) {
+                const bool q0 = r < a.seg_end[0], q1 = r < a.seg_end[1];
+                const void* bsel = q0 ? a.bias[0] : (q1 ? a.bias[1] : a.bias[2]);
+                const int base = q0 ? 0 : (q1 ? a.seg_end[0] : a.seg_end[1]);
+                yrow[r] = bsel ? v0 + load_scalar<uint16_t>(bsel, r - base) : v0;
+            } else if (EPI == EPI_RESID) {
+                if (splits == 1) yrow[r] = yv[rb][e] + v0;
+                else unsafeAtomicAdd(yrow + r, v0);
+            } else {
+                yrow[r] = silu(v0) * (acc[rb][NW - 1][e] * rs);
+            }
         }
     }
 }
 
-// Shape of the single-shot form for a matrix, or spw = 0 when it does not apply:
-// a residual product takes k-steps per wave by K (4 from 2048 up, else 2) and as
-// many K ranges as that needs; a normed product must fit one range of at most 8
-// steps per wave (K <= 1024).
-struct G16Split { int spw, splits; };
-static G16Split gemm16_split_shape(int K, int epi) {
+// Shape of the single-shot form for a matrix, or spw = 0 when it does not apply.
+// A long residual product (K >= 2048: down) takes groups of two row blocks and
+// as many K ranges as keep the grid within one workgroup per CU, so each CU
+// loads its share of the weights and the matching activation slice once (with
+// one block per workgroup and 4-step ranges the down product at batch 16 put
+// three workgroups, each loading twice its weight bytes of activation, on a CU).
+// Other residual products take k-steps per wave by K (2) and as many K ranges as
+// that needs; a normed product must fit one range of at most 8 steps per wave
+// (K <= 1024).
+struct G16Split { int spw, splits, r; };
+static G16Split gemm16_split_shape(int K, int N, int epi) {
     const int nsteps = (K + 31) / 32;
     if (epi == EPI_RESID) {
+        if (K >= 2048) {
+#ifndef QD_G16_DOWN_R
+#define QD_G16_DOWN_R 2
+#endif
+            const int groups = (N + 16 * QD_G16_DOWN_R - 1) / (16 * QD_G16_DOWN_R);
+            const int splits = std::max(1, std::min(kG16Cus / groups, nsteps / 8));
+            const int spw = ((nsteps + splits - 1) / splits + 3) / 4;
+            if (spw >= 2 && spw <= 6) return {spw, splits, QD_G16_DOWN_R};
+        }
         const int spw = K >= 2048 ? 4 : 2;
-        return {spw, (nsteps + 4 * spw - 1) / (4 * spw)};
+        return {spw, (nsteps + 4 * spw - 1) / (4 * spw), 1};
     }
-    if ((epi == EPI_STORE || epi == EPI_SWIGLU) && nsteps <= 32) return {8, 1};
-    return {0, 0};
+    if ((epi == EPI_STORE || epi == EPI_SWIGLU) && nsteps <= 32) return {8, 1, 1};
+    return {0, 0, 0};
+}
+
+// K ranges of a normed store product in the partial form (GemvArgs::ss_out): as
+// many as keep one workgroup per CU (at most 3, at least 4 k-steps each), for
+// the matrices the single-shot form takes; with one range per workgroup the
+// q|k|v product at the 0.5B shape ran on 72 of the 256 CUs, each loading the
+// whole activation.
+int gemm16_store_splits(int K, int N) {
+    const int nsteps = (K + 31) / 32, nb = (N + 15) / 16;
+    if (nsteps > 32) return 1;
+    const int s = std::min(kGemm16MaxStoreSplits, std::min(kG16Cus / nb, nsteps / 4));
+    if (s < 2 || (nsteps + s - 1) / s > 16) return 1;
+    return s;
+}
+
+// Blocks per workgroup of the multi-block normed kernel (gemm16_rows_kernel, one
+// workgroup per CU), or 0 when it does not apply: gate|up with more rows than
+// 16 per CU (up to 48), K a multiple of 32 up to 1024 with a per-wave step count
+// it is built for
+static int gemm16_rows_shape(int K, int N, int epi, int* spw) {
+    if (epi != EPI_SWIGLU || K % 32 || K > 1024 || N <= 16 * kG16Cus || N > 48 * kG16Cus) return 0;
+    *spw = (K / 32 + 3) / 4;
+    if (*spw != 2 && *spw != 4 && *spw != 7 && *spw != 8) return 0;
+    return ((N + kG16Cus - 1) / kG16Cus + 15) / 16;
 }
 
 // K split into the fewest chunks of at most kG16Chunk, evened out (multiples of 32)
@@ -608,23 +840,77 @@ hipError_t launch_gemm16(const GemvArgs& a, int epi, int grid_cap, int* grid_out
     const bool gain_ok = epi == EPI_RESID ? a.gain == nullptr
                                           : (a.gain != nullptr && ((uintptr_t)a.gain & 15u) == 0);
     if (!wide && gain_ok) {
-        const int grid = (a.N + 15) / 16;
-        const G16Split sp = gemm16_split_shape(a.K, epi);
+        int rspw = 0;
+        const int rb = gemm16_rows_shape(a.K, a.N, epi, &rspw);
+        if (rb) {
+            const int grid = kG16Cus;                // rows [N w / grid, N (w + 1) / grid) each
+            if (grid > grid_cap) return hipErrorInvalidValue;
+            if (grid_out) *grid_out = grid;
+            // activation and gain; the waves' partial products reuse it ([3][rb][2][64] x 16 bytes)
+            const size_t shm = std::max((size_t)(a.K / 32) * 2048 + (size_t)((a.K * 2 + 1023) / 1024) * 1024,
+                                        (size_t)rb * 6 * 1024);
+            auto go = [&](auto kern) {
+                if (shm > 65536 &&
+                    hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm) != hipSuccess)
+                    return hipErrorInvalidValue;
+                hipLaunchKernelGGL(kern, dim3(grid), dim3(256), shm, s, a);
+                return hipGetLastError();
+            };
+#define QD_G16R(RB)                                                      \
+            switch (rspw) {                                              \
+                case 2: return go(gemm16_rows_kernel<EPI_SWIGLU, RB, 2>); \
+                case 4: return go(gemm16_rows_kernel<EPI_SWIGLU, RB, 4>); \
+                case 7: return go(gemm16_rows_kernel<EPI_SWIGLU, RB, 7>); \
+                default: return go(gemm16_rows_kernel<EPI_SWIGLU, RB, 8>); \
+            }
+            if (rb == 2) { QD_G16R(2) } else { QD_G16R(3) }
+#undef QD_G16R
+        }
+        G16Split sp = gemm16_split_shape(a.K, a.N, epi);
+        if (a.ss_out) {                      // partial form: K ranges of at most 4 steps per wave
+            if (epi != EPI_STORE) return hipErrorInvalidValue;
+            const int sn = gemm16_store_splits(a.K, a.N);
+            if (sn < 2) return hipErrorInvalidValue;
+            sp = {((((a.K + 31) / 32) + sn - 1) / sn + 3) / 4, sn, 1};
+        }
         if (sp.spw) {
+            const int grid = ((a.N + 15) / 16 + sp.r - 1) / sp.r;
             if (grid > grid_cap) return hipErrorInvalidValue;
             if (grid_out) *grid_out = grid;
             const dim3 g2(grid, sp.splits);
-#define QD_G16S(E, S) hipLaunchKernelGGL((gemm16_split_kernel<E, S>), g2, dim3(256), 0, s, a, sp.splits)
+#define QD_G16S(E, S, R) hipLaunchKernelGGL((gemm16_split_kernel<E, S, R>), g2, dim3(256), 0, s, a, sp.splits)
             if (epi == EPI_RESID) {
-                if (sp.spw == 4) QD_G16S(EPI_RESID, 4); else QD_G16S(EPI_RESID, 2);
+                if (sp.r == 4) {
+                    switch (sp.spw) {
+                        case 2: QD_G16S(EPI_RESID, 2, 4); break;
+                        case 3: QD_G16S(EPI_RESID, 3, 4); break;
+                        default: QD_G16S(EPI_RESID, 4, 4); break;
+                    }
+                } else if (sp.r == 2) {
+                    switch (sp.spw) {
+                        case 2: QD_G16S(EPI_RESID, 2, 2); break;
+                        case 3: QD_G16S(EPI_RESID, 3, 2); break;
+                        case 4: QD_G16S(EPI_RESID, 4, 2); break;
+                        case 5: QD_G16S(EPI_RESID, 5, 2); break;
+                        default: QD_G16S(EPI_RESID, 6, 2); break;
+                    }
+                } else if (sp.spw == 4) {
+                    QD_G16S(EPI_RESID, 4, 1);
+                } else {
+                    QD_G16S(EPI_RESID, 2, 1);
+                }
             } else if (epi == EPI_STORE) {
-                QD_G16S(EPI_STORE, 8);
+                if (sp.spw <= 2) QD_G16S(EPI_STORE, 2, 1);
+                else if (sp.spw == 3) QD_G16S(EPI_STORE, 3, 1);
+                else if (sp.spw == 4) QD_G16S(EPI_STORE, 4, 1);
+                else QD_G16S(EPI_STORE, 8, 1);
             } else {
-                QD_G16S(EPI_SWIGLU, 8);
+                QD_G16S(EPI_SWIGLU, 8, 1);
             }
 #undef QD_G16S
             return hipGetLastError();
         }
+        const int grid = (a.N + 15) / 16;
         if (grid > grid_cap) return hipErrorInvalidValue;
         if (grid_out) *grid_out = grid;
         const bool deep = a.K >= 2048;       // long K: eight waves split it

@@ -37,6 +37,11 @@ struct GemvArgs {
     // int8 weights: float scale of each row, per segment (SWIGLU: [0] gate, [1] up);
     // the product of row r is scaled by it
     const float* wscale[3];
+    // optional, batch 2..16 normed store product (launch_gemm16, EPI_STORE) cut into
+    // gemm16_store_splits(K, N) K ranges: y receives [splits][B][N] partial products
+    // (neither the RMSNorm scale nor the bias applied) and ss_out [splits][B] the
+    // partial sums of squares of x over each range; the consumer finishes
+    float* ss_out;
 };
 hipError_t launch_gemv(const GemvArgs& a, int w_is_bf16, int epi, int grid_cap, int* grid_out,
                        hipStream_t s);
@@ -51,6 +56,9 @@ int gemv1_merge_max_splits();
 // gemm16_chunk(a.K); part_val/part_idx hold [B][grid] entries
 hipError_t launch_gemm16(const GemvArgs& a, int epi, int grid_cap, int* grid_out, hipStream_t s);
 int gemm16_chunk(int K);
+// K ranges of a normed store product given GemvArgs::ss_out (1: no partial form)
+int gemm16_store_splits(int K, int N);
+constexpr int kGemm16MaxStoreSplits = 3;
 
 // Decode attention with the q/k norm, RoPE, the new token's KV append and the
 // split merge fused in (one launch per layer); see qd_attention.hip.
@@ -80,9 +88,21 @@ struct AttnArgs {
     // [rows][Hq][hd], its K/V already in the cache (block table row 0)
     int prefill_start;
     const float* q_rot;
+    // qkv_slabs > 0 (matrix-core kernel, bf16 weights only): qkv holds that many K-range partial
+    // products of the q|k|v projection (slab stride qkv_slab_stride floats), without
+    // the RMSNorm scale or the bias; qkv_ss [slabs][B] holds the partial sums of
+    // squares of the normed input (x_dim elements) and qkv_bias the q, k and v biases
+    // (the weights' type, NULL: none). The kernel forms r * sum + bias itself.
+    int qkv_slabs;
+    long qkv_slab_stride;
+    const float* qkv_ss;
+    const void* qkv_bias[3];
+    int x_dim;
 };
 // attention kernel, plus the split merge kernel when S > 1
 hipError_t launch_attention(const AttnArgs& a, int w_is_bf16, int kv_is_bf16, hipStream_t s);
+// whether launch_attention takes the matrix-core grouped kernel for these arguments
+bool attn_uses_mfma(const AttnArgs& a, int kv_is_bf16);
 int attn_max_chunk(int hd, int kv_is_bf16, int grouped);
 int attn_max_splits();
 

@@ -97,6 +97,26 @@ def test_batched_projections_chunked_k_wide_vocab(batch):
     assert _cache_matches(case)
 
 
+@pytest.mark.parametrize("batch", [5, 16])
+def test_batched_multi_block_gate_up_and_grouped_down(batch):
+    """ffn 4200 gives 263 row blocks of gate|up, more than the chip has CUs: two
+    blocks per workgroup with the activation staged once (the last workgroup holds
+    one block, the last block 8 rows); down (K = 4200, a ragged last k-step) takes
+    groups of two row blocks over 16 K ranges."""
+    shape = replace(SMALL, n_layers=2, hidden=256, ffn=4200, vocab=3001, n_q_heads=4,
+                    n_kv_heads=2, head_dim=64)
+    ctx = np.array([(53 * b + 7) % 400 for b in range(batch)], np.int32)
+    case = make_case(shape, ctx, seed=71 + batch, random_order=True)
+    tok = synth.make_tokens(batch, shape.vocab, seed=71 + batch)
+    logits, nxt, x_out, layer_out = _run_step(case, ctx, tokens=tok)
+    ref = _oracle(case, ctx, tokens=tok)
+    assert rel_err(logits.cpu().numpy(), ref.logits) <= 2e-3
+    assert rel_err(layer_out.cpu().numpy(), ref.layer_out) <= 2e-3
+    assert rel_err(x_out.cpu().numpy(), ref.x_out) <= 2e-3
+    assert list(nxt.cpu().numpy()) == list(ref.next_tokens)
+    assert _cache_matches(case)
+
+
 def test_small_qk_norm_no_bias_untied():
     shape = replace(SMALL, qkv_bias=False, qk_norm=True, tied=False, n_q_heads=8, n_kv_heads=2,
                     head_dim=128)
