@@ -452,9 +452,12 @@ __global__ __launch_bounds__(64 * WK) void gemm16_direct_kernel(GemvArgs a) {
 // the weights, then every wave issues its weight loads for all of its k-steps
 // at once (RB blocks x NW matrices), waits only for the DMA, and runs each
 // step's MFMAs as its weights land. The four waves split K and meet in LDS in a
-// fixed order. LDS layout of the activation: 32-byte units (8 float32 of one
-// token), unit ((s * 4 + q) * 16 + t) = token t, k = 32 s + 8 q .. + 8, so a
-// fragment read is two conflict-free 16-byte reads per lane.
+// fixed order. LDS layout of the activation: one 128-byte line per (k-step s,
+// token t) at (16 s + t) * 128, holding x[t][32 s .. 32 s + 32) as 16-byte granules
+// with granule g at position g ^ sw(t), sw(t) = 2 ((t / 2) % 4): each DMA
+// instruction then fetches 8 whole lines (a layout with 32-byte pieces of 32
+// lines per instruction fetched every line twice), and the 8 lanes of a 16-byte
+// LDS read phase (tokens 0..7 or 8..15) land on distinct banks.
 template <int EPI, int RB, int SPW>
 __global__ __launch_bounds__(256) void gemm16_rows_kernel(GemvArgs a) {
     constexpr int NW = (EPI == EPI_SWIGLU) ? 2 : 1;
@@ -473,9 +476,9 @@ __global__ __launch_bounds__(256) void gemm16_rows_kernel(GemvArgs a) {
     // 1. activation and gain by DMA (each 1 KB instruction fills 32 units)
     {
         const uint32_t xl = lds_addr(xs), gl = lds_addr(gs);
-        for (int c = wave; c < nsteps * 2; c += 4) {
-            const int u = c * 32 + (lane >> 1);
-            const int t = u & 15, k = (u >> 4) * 8 + (lane & 1) * 4;
+        for (int c = wave; c < nsteps * 2; c += 4) {   // lines (c / 2, 8 (c % 2) + lane / 8)
+            const int t = (c & 1) * 8 + (lane >> 3);
+            const int k = (c >> 1) * 32 + ((lane & 7) ^ (((t >> 1) & 3) << 1)) * 4;
             const void* src = t < B ? (const void*)(a.x + (long)t * K + k) : (const void*)kG16Zeros;
             lds_dma16(src, __builtin_amdgcn_readfirstlane(xl + c * 1024));
         }
@@ -535,7 +538,7 @@ __global__ __launch_bounds__(256) void gemm16_rows_kernel(GemvArgs a) {
     for (int u = 0; u < SPW; ++u) {
         const int st = s0 + u;
         if (st >= s1) break;
-        const float* xp = xs + ((st * 4 + kq) * 16 + col) * 8;
+        const float* xp = xs + (st * 16 + col) * 32 + ((2 * kq) ^ (((col >> 1) & 3) << 1)) * 4;
         const float4 p0 = *(const float4*)xp, p1 = *(const float4*)(xp + 4);
         float gf[8];
         widen16(*(const uint4*)(gs + st * 32 + kq * 8), gf);
@@ -929,7 +932,11 @@ hipError_t launch_gemm16(const GemvArgs& a, int epi, int grid_cap, int* grid_out
     const size_t shm = (size_t)a.kt * 64;    // hi + lo, 16 tokens, 2 bytes each
     auto go = [&](auto kern, int tr) {
         const int tiles = (a.N + tr - 1) / tr;
-        const int grid = tiles < grid_cap ? tiles : grid_cap;
+        int grid = tiles < grid_cap ? tiles : grid_cap;
+        // wide tiles: as many workgroups as the LDS lets the CUs hold at once (two each),
+        // so each stages its activation once for several tiles (the lm_head at batch 16:
+        // 67 -> 62 us against one workgroup per tile)
+        if (tr == 128 && grid > 2 * kG16Cus) grid = 2 * kG16Cus;
         if (grid_out) *grid_out = grid;
         hipLaunchKernelGGL(kern, dim3(grid), dim3(256), shm, s, a);
         return hipGetLastError();
