@@ -130,6 +130,25 @@ def test_small_qk_norm_no_bias_untied():
     assert list(nxt.cpu().numpy()) == list(ref.next_tokens)
 
 
+@pytest.mark.parametrize("qkv_bias,qk_norm", [(False, True), (True, False)])
+def test_batched_partial_qkv_head_dim_128(qkv_bias, qk_norm):
+    """hidden 512 at batch 6: q|k|v runs as two K-range partial products that the
+    attention kernel (head_dim 128) sums, scales by the RMSNorm factor and biases
+    (or not) before the q/k norm and RoPE."""
+    shape = replace(SMALL, hidden=512, ffn=1024, qkv_bias=qkv_bias, qk_norm=qk_norm, tied=not qk_norm,
+                    n_q_heads=8, n_kv_heads=2, head_dim=128)
+    ctx = np.array([0, 3, 64, 130, 511, 17], np.int32)
+    case = make_case(shape, ctx, seed=13, random_order=True)
+    tok = synth.make_tokens(len(ctx), shape.vocab, seed=13)
+    logits, nxt, x_out, layer_out = _run_step(case, ctx, tokens=tok)
+    ref = _oracle(case, ctx, tokens=tok)
+    assert rel_err(logits.cpu().numpy(), ref.logits) <= 2e-3
+    assert rel_err(layer_out.cpu().numpy(), ref.layer_out) <= 2e-3
+    assert rel_err(x_out.cpu().numpy(), ref.x_out) <= 2e-3
+    assert list(nxt.cpu().numpy()) == list(ref.next_tokens)
+    assert _cache_matches(case)
+
+
 def test_position_zero_returns_v():
     """One cached token (the new one): attention output is the stored v exactly, so the
     block output equals the oracle's to fp32 rounding of the GEMVs."""
