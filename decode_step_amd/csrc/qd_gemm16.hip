@@ -786,13 +786,10 @@ static G16Split gemm16_split_shape(int K, int N, int epi) {
     const int nsteps = (K + 31) / 32;
     if (epi == EPI_RESID) {
         if (K >= 2048) {
-#ifndef QD_G16_DOWN_R
-#define QD_G16_DOWN_R 2
-#endif
-            const int groups = (N + 16 * QD_G16_DOWN_R - 1) / (16 * QD_G16_DOWN_R);
+            const int groups = (N + 31) / 32;
             const int splits = std::max(1, std::min(kG16Cus / groups, nsteps / 8));
             const int spw = ((nsteps + splits - 1) / splits + 3) / 4;
-            if (spw >= 2 && spw <= 6) return {spw, splits, QD_G16_DOWN_R};
+            if (spw >= 2 && spw <= 6) return {spw, splits, 2};
         }
         const int spw = K >= 2048 ? 4 : 2;
         return {spw, (nsteps + 4 * spw - 1) / (4 * spw), 1};
@@ -883,13 +880,7 @@ hipError_t launch_gemm16(const GemvArgs& a, int epi, int grid_cap, int* grid_out
             const dim3 g2(grid, sp.splits);
 #define QD_G16S(E, S, R) hipLaunchKernelGGL((gemm16_split_kernel<E, S, R>), g2, dim3(256), 0, s, a, sp.splits)
             if (epi == EPI_RESID) {
-                if (sp.r == 4) {
-                    switch (sp.spw) {
-                        case 2: QD_G16S(EPI_RESID, 2, 4); break;
-                        case 3: QD_G16S(EPI_RESID, 3, 4); break;
-                        default: QD_G16S(EPI_RESID, 4, 4); break;
-                    }
-                } else if (sp.r == 2) {
+                if (sp.r == 2) {
                     switch (sp.spw) {
                         case 2: QD_G16S(EPI_RESID, 2, 2); break;
                         case 3: QD_G16S(EPI_RESID, 3, 2); break;
