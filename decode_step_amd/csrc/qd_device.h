@@ -9,15 +9,18 @@ namespace qd {
 constexpr int kWave = 64;
 
 // bf16 is the top half of a float32: widening appends 16 zero bits (exact for
-// every pattern); narrowing rounds half to even (nanoinfer page, phase 1).
+// every pattern); narrowing rounds half to even (nanoinfer page, phase 1), here
+// by the hardware conversion v_cvt_pk_bf16_f32 (two values per instruction; a
+// NaN stays a NaN). The integer form of the rounding (add 0x7fff plus the kept
+// low bit, test for NaN) cost about 8 instructions per value.
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x0040u);  // quiet NaN
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi) {
+    typedef __attribute__((ext_vector_type(2))) float f2;
+    typedef __attribute__((ext_vector_type(2))) __bf16 b2;
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{lo, hi}, b2));
 }
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return (uint16_t)f32x2_to_bf16x2(f, 0.f); }
 
 // Elements per 16-byte vector for a storage type.
 template <typename T> struct VecN;
@@ -52,12 +55,8 @@ __device__ __forceinline__ void widen16(const uint4 v, float (&f)[4]) {
 // Round floats to the storage type and pack them into one 16-byte vector.
 template <typename T> __device__ __forceinline__ uint4 pack16(const float (&f)[VecN<T>::n]);
 template <> __device__ __forceinline__ uint4 pack16<uint16_t>(const float (&f)[8]) {
-    uint4 v;
-    v.x = (uint32_t)f32_to_bf16(f[0]) | ((uint32_t)f32_to_bf16(f[1]) << 16);
-    v.y = (uint32_t)f32_to_bf16(f[2]) | ((uint32_t)f32_to_bf16(f[3]) << 16);
-    v.z = (uint32_t)f32_to_bf16(f[4]) | ((uint32_t)f32_to_bf16(f[5]) << 16);
-    v.w = (uint32_t)f32_to_bf16(f[6]) | ((uint32_t)f32_to_bf16(f[7]) << 16);
-    return v;
+    return make_uint4(f32x2_to_bf16x2(f[0], f[1]), f32x2_to_bf16x2(f[2], f[3]),
+                      f32x2_to_bf16x2(f[4], f[5]), f32x2_to_bf16x2(f[6], f[7]));
 }
 template <> __device__ __forceinline__ uint4 pack16<float>(const float (&f)[4]) {
     return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3]));

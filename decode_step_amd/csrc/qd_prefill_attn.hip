@@ -323,8 +323,7 @@ __global__ __launch_bounds__(64 * kPaWaves) __attribute__((amdgpu_waves_per_eu(2
                 for (int w = 1; w < NWV; ++w) t = fmaf(mo[((w - 1) * kPaRows + r32) * HD + d], wt[w], t);
                 v[i] = t * inv;
             }
-            const uint2 pk = make_uint2((uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
-                                        (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16));
+            const uint2 pk = make_uint2(f32x2_to_bf16x2(v[0], v[1]), f32x2_to_bf16x2(v[2], v[3]));
             *(uint2*)(dst + cb * 32 + e4 * 8 + hi * 4) = pk;
         }
 }
