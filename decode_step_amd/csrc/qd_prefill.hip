@@ -588,7 +588,10 @@ void mfma_gemm_v2_kernel(GemmArgs a, int ntn, int ntm, int splits) {
                         T[(wm * 64 + ii * 32 + (e >> 2) * 8 + lhalf * 4 + (e & 3)) * TP + wn * WN + j * 32 + lrow] =
                             acc[2 * r + ii][j][e];
             lds_barrier();
-            for (int item = tid; item < 128 * CPR; item += 256) {
+            static_assert(128 * CPR % 256 == 0, "whole items per thread");
+#pragma unroll
+            for (int it = 0; it < 128 * CPR / 256; ++it) {   // unrolled: the LDS reads of all items go out together
+                const int item = tid + it * 256;
                 const int R = item / CPR, c = item - R * CPR;
                 const int m = m0 + (R >> 6) * WM + r * 64 + (R & 63);
                 const int f = f0 + c * 8;
@@ -606,18 +609,33 @@ void mfma_gemm_v2_kernel(GemmArgs a, int ntn, int ntm, int splits) {
         }
     } else {
         float* out = (float*)a.C + (long)split * M * a.ldc;
+        if (m0 + BM <= M && (tileN + 1) * BN <= a.N) {
+            // whole tile in range: one lane base, row offsets uniform over the wave
+            // (per-element bounds checks and 64-bit index arithmetic had made this
+            // epilogue instruction-bound: ~10 instructions per stored value)
+            float* base = out + (long)(m0 + wm * WM + lhalf * 4) * a.ldc + tileN * BN + wn * WN + lrow;
 #pragma unroll
-        for (int i = 0; i < TI; ++i)
+            for (int i = 0; i < TI; ++i)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int m = m0 + wm * WM + i * 32 + (e >> 2) * 8 + lhalf * 4 + (e & 3);
-                if (m >= M) continue;
+                for (int e = 0; e < 16; ++e) {
+                    float* row = base + (long)(i * 32 + (e >> 2) * 8 + (e & 3)) * a.ldc;
 #pragma unroll
-                for (int j = 0; j < TJ; ++j) {
-                    const int n = tileN * BN + wn * WN + j * 32 + lrow;
-                    if (n < a.N) out[(long)m * a.ldc + n] = acc[i][j][e];
+                    for (int j = 0; j < TJ; ++j) row[j * 32] = acc[i][j][e];
                 }
-            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < TI; ++i)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int m = m0 + wm * WM + i * 32 + (e >> 2) * 8 + lhalf * 4 + (e & 3);
+                    if (m >= M) continue;
+#pragma unroll
+                    for (int j = 0; j < TJ; ++j) {
+                        const int n = tileN * BN + wn * WN + j * 32 + lrow;
+                        if (n < a.N) out[(long)m * a.ldc + n] = acc[i][j][e];
+                    }
+                }
+        }
     }
 }
 
