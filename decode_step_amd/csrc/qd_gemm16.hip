@@ -839,6 +839,9 @@ hipError_t launch_gemm16(const GemvArgs& a, int epi, int grid_cap, int* grid_out
     const bool wide = a.N >= 16 * 2048;
     const bool gain_ok = epi == EPI_RESID ? a.gain == nullptr
                                           : (a.gain != nullptr && ((uintptr_t)a.gain & 15u) == 0);
+    // the partial form exists only as the single-shot store product below
+    if (a.ss_out && (epi != EPI_STORE || wide || !gain_ok || gemm16_store_splits(a.K, a.N) < 2))
+        return hipErrorInvalidValue;
     if (!wide && gain_ok) {
         int rspw = 0;
         const int rb = gemm16_rows_shape(a.K, a.N, epi, &rspw);
@@ -868,9 +871,7 @@ hipError_t launch_gemm16(const GemvArgs& a, int epi, int grid_cap, int* grid_out
         }
         G16Split sp = gemm16_split_shape(a.K, a.N, epi);
         if (a.ss_out) {                      // partial form: K ranges of at most 4 steps per wave
-            if (epi != EPI_STORE) return hipErrorInvalidValue;
             const int sn = gemm16_store_splits(a.K, a.N);
-            if (sn < 2) return hipErrorInvalidValue;
             sp = {((((a.K + 31) / 32) + sn - 1) / sn + 3) / 4, sn, 1};
         }
         if (sp.spw) {
