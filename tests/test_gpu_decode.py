@@ -130,6 +130,23 @@ def test_small_qk_norm_no_bias_untied():
     assert list(nxt.cpu().numpy()) == list(ref.next_tokens)
 
 
+def test_batched_three_block_gate_up_full_lds():
+    """hidden 1024 and ffn 8200 at batch 4: gate|up takes 32-33 rows per workgroup
+    (three MFMA blocks, the third mostly masked), eight k-steps per wave, and
+    66 KB of LDS for the staged activation (past the default 64 KB)."""
+    shape = replace(SMALL, hidden=1024, ffn=8200, vocab=2003, n_q_heads=8, n_kv_heads=2, head_dim=128)
+    ctx = np.array([5, 300, 77, 1000], np.int32)
+    case = make_case(shape, ctx, seed=91, random_order=True)
+    tok = synth.make_tokens(len(ctx), shape.vocab, seed=91)
+    logits, nxt, x_out, layer_out = _run_step(case, ctx, tokens=tok)
+    ref = _oracle(case, ctx, tokens=tok)
+    assert rel_err(logits.cpu().numpy(), ref.logits) <= 2e-3
+    assert rel_err(layer_out.cpu().numpy(), ref.layer_out) <= 2e-3
+    assert rel_err(x_out.cpu().numpy(), ref.x_out) <= 2e-3
+    assert list(nxt.cpu().numpy()) == list(ref.next_tokens)
+    assert _cache_matches(case)
+
+
 @pytest.mark.parametrize("qkv_bias,qk_norm", [(False, True), (True, False)])
 def test_batched_partial_qkv_head_dim_128(qkv_bias, qk_norm):
     """hidden 512 at batch 6: q|k|v runs as two K-range partial products that the
