@@ -439,7 +439,15 @@ __global__ __launch_bounds__(kAmWaves * kWave) void attn_mfma_kernel(AttnArgs a)
     __shared__ float2 wml[NWV][kAmHeads];
 
     const int G = a.Hq / a.Hkv;
-    const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    if (a.compact) {   // the grid holds only splits with keys: find the sequence (uniform scan)
+        const int id = blockIdx.x;
+        b = 0;
+        while (b + 1 < a.B && a.wg_base[b + 1] <= id) ++b;
+        const int local = id - a.wg_base[b];
+        s = local / a.Hkv;
+        g = local - s * a.Hkv;
+    }
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
     const int c16 = lane & 15, q4 = lane >> 4;
     const int* bt = a.block_table + (long)b * a.max_blocks;
@@ -823,8 +831,10 @@ hipError_t launch_attention(const AttnArgs& a, int w_is_bf16, int kv_is_bf16, hi
     const bool mfma = attn_uses_mfma(a, kv_is_bf16);
     if (a.qkv_slabs > 0 && (!mfma || !w_is_bf16 || a.qkv_slabs > kGemm16MaxStoreSplits || !a.qkv_ss || a.x_dim < 1))
         return hipErrorInvalidValue;
+    if (a.compact && (!mfma || a.B > kAttnMaxBatch || a.wg_base[0] != 0)) return hipErrorInvalidValue;
     if (mfma) {
-        const dim3 grid(a.S, a.Hkv, a.B), block(kAmWaves * kWave);
+        const dim3 grid = a.compact ? dim3(a.wg_base[a.B]) : dim3(a.S, a.Hkv, a.B), block(kAmWaves * kWave);
+        if (a.compact && a.wg_base[a.B] < 1) return hipSuccess;   // no keys anywhere (positions out of range)
 #define QD_AM(WT, NSL)                                                                             \
         if (a.hd == 64) hipLaunchKernelGGL((attn_mfma_kernel<WT, 64, NSL>), grid, block, 0, s, a); \
         else hipLaunchKernelGGL((attn_mfma_kernel<WT, 128, NSL>), grid, block, 0, s, a);

@@ -62,6 +62,7 @@ constexpr int kGemm16MaxStoreSplits = 3;
 
 // Decode attention with the q/k norm, RoPE, the new token's KV append and the
 // split merge fused in (one launch per layer); see qd_attention.hip.
+constexpr int kAttnMaxBatch = 16;   // sequences of one decode step at most
 struct AttnArgs {
     const float* qkv;       // [B][Hq*hd + 2*Hkv*hd] projections (bias added)
     void* k_cache;
@@ -98,6 +99,11 @@ struct AttnArgs {
     const float* qkv_ss;
     const void* qkv_bias[3];
     int x_dim;
+    // optional (matrix-core kernel): a one-dimensional grid of only the splits that
+    // hold keys, sequence b's at wg_base[b] .. wg_base[b + 1] - 1 (split-major, then
+    // KV head), from the host copy of the positions; wg_base[0] = 0, B + 1 entries
+    int compact;
+    int wg_base[kAttnMaxBatch + 1];
 };
 // attention kernel, plus the split merge kernel when S > 1
 hipError_t launch_attention(const AttnArgs& a, int w_is_bf16, int kv_is_bf16, hipStream_t s);
