@@ -35,6 +35,7 @@ typedef __attribute__((ext_vector_type(4))) float g16_f32x4;
 constexpr int kG16Chunk = 1024;   // K elements staged per chunk: 64 KB of LDS for 16 tokens
 constexpr int kG16U = 2;          // k-steps (of 32) per pipeline stage (lm_head at batch 16: 59.5 us at 2, 62.4 at 4, 63.8 at 8)
 constexpr int kG16Cus = 256;      // compute units of the chip (MI355X)
+constexpr int kG16RowsWgs = 2 * kG16Cus;   // grid of gemm16_rows_kernel
 
 __device__ __forceinline__ g16_bf16x8 g16_frag(uint4 v) { return __builtin_bit_cast(g16_bf16x8, v); }
 
@@ -441,15 +442,14 @@ __global__ __launch_bounds__(64 * WK) void gemm16_direct_kernel(GemvArgs a) {
 }
 
 // Normed products with more 16-row blocks than the chip has CUs (gate|up at the
-// 0.5B shape: 304 blocks of gate and up rows). With one block per workgroup every
-// workgroup would load the whole activation (16 tokens x K float32, as many bytes
-// as its own weights) through its CU's load path, which is what bounds these
-// kernels, and some CUs would take two workgroups. Here the grid is one
-// workgroup per CU and workgroup w takes rows [N w / G, N (w + 1) / G) in RB
-// MFMA blocks of 16 starting at its first row (rows past its range read the zero
-// block), so every CU loads an equal share of the weights and the activation
-// once: the tokens' rows (zeros past B) and the gain go into LDS by DMA, ahead of
-// the weights, then every wave issues its weight loads for all of its k-steps
+// 0.5B shape: 304 blocks of gate and up rows). With one block per workgroup some
+// CUs take two workgroups and others one, and every workgroup loads the whole
+// activation (16 tokens x K float32) as well. Here the grid is two workgroups per
+// CU and workgroup w takes rows [N w / G, N (w + 1) / G) in RB MFMA blocks of 16
+// starting at its first row (rows past its range read the zero block), so every
+// CU loads an equal share of the weights: the tokens' rows (zeros past B) and the
+// gain go into LDS by DMA, ahead of the weights, then every wave issues its
+// weight loads for all of its k-steps
 // at once (RB blocks x NW matrices), waits only for the DMA, and runs each
 // step's MFMAs as its weights land. The four waves split K and meet in LDS in a
 // fixed order. LDS layout of the activation: one 128-byte line per (k-step s,
@@ -811,15 +811,18 @@ int gemm16_store_splits(int K, int N) {
     return s;
 }
 
-// Blocks per workgroup of the multi-block normed kernel (gemm16_rows_kernel, one
-// workgroup per CU), or 0 when it does not apply: gate|up with more rows than
-// 16 per CU (up to 48), K a multiple of 32 up to 1024 with a per-wave step count
-// it is built for
+// Blocks per workgroup of the multi-block normed kernel (gemm16_rows_kernel, two
+// workgroups per CU: what the staged activation's LDS allows; against one per CU
+// with twice the rows, 9.7 -> 9.0 us for gate|up at batch 16 although each CU
+// then stages the activation twice: the load path wants the extra waves), or 0
+// when it does not apply: gate|up with more rows than 16 per CU (up to 48 per
+// workgroup), K a multiple of 32 up to 1024 with a per-wave step count it is
+// built for
 static int gemm16_rows_shape(int K, int N, int epi, int* spw) {
-    if (epi != EPI_SWIGLU || K % 32 || K > 1024 || N <= 16 * kG16Cus || N > 48 * kG16Cus) return 0;
+    if (epi != EPI_SWIGLU || K % 32 || K > 1024 || N <= 16 * kG16Cus || N > 48 * kG16RowsWgs) return 0;
     *spw = (K / 32 + 3) / 4;
     if (*spw != 2 && *spw != 4 && *spw != 7 && *spw != 8) return 0;
-    return ((N + kG16Cus - 1) / kG16Cus + 15) / 16;
+    return ((N + kG16RowsWgs - 1) / kG16RowsWgs + 15) / 16;
 }
 
 // K split into the fewest chunks of at most kG16Chunk, evened out (multiples of 32)
@@ -846,7 +849,7 @@ hipError_t launch_gemm16(const GemvArgs& a, int epi, int grid_cap, int* grid_out
         int rspw = 0;
         const int rb = gemm16_rows_shape(a.K, a.N, epi, &rspw);
         if (rb) {
-            const int grid = kG16Cus;                // rows [N w / grid, N (w + 1) / grid) each
+            const int grid = kG16RowsWgs;            // rows [N w / grid, N (w + 1) / grid) each
             if (grid > grid_cap) return hipErrorInvalidValue;
             if (grid_out) *grid_out = grid;
             // activation and gain; the waves' partial products reuse it ([3][rb][2][64] x 16 bytes)
@@ -866,7 +869,7 @@ hipError_t launch_gemm16(const GemvArgs& a, int epi, int grid_cap, int* grid_out
                 case 7: return go(gemm16_rows_kernel<EPI_SWIGLU, RB, 7>); \
                 default: return go(gemm16_rows_kernel<EPI_SWIGLU, RB, 8>); \
             }
-            if (rb == 2) { QD_G16R(2) } else { QD_G16R(3) }
+            if (rb == 1) { QD_G16R(1) } else if (rb == 2) { QD_G16R(2) } else { QD_G16R(3) }
 #undef QD_G16R
         }
         G16Split sp = gemm16_split_shape(a.K, a.N, epi);
