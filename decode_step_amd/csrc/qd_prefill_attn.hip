@@ -57,7 +57,7 @@ __global__ __launch_bounds__(64 * kPaWaves) __attribute__((amdgpu_waves_per_eu(2
                                          // 8 dim groups of a write over the banks)
     constexpr int VT_B = HD * VTS * 2;   // one wave's tile
     constexpr int TILES = NWV * VT_B;
-    constexpr int MERGE = (NWV - 1) * (kPaRows * HD + 2 * kPaRows) * 4;
+    constexpr int MERGE = (NWV - 1) * kPaRows * HD * 4 + NWV * kPaRows * 8;
     __shared__ __align__(16) char smem[TILES > MERGE ? TILES : MERGE];
     __shared__ uint4 qfr[2][KS][64];     // Q fragments (bf16 hi, lo) of every lane, shared by the waves
 
@@ -279,53 +279,57 @@ __global__ __launch_bounds__(64 * kPaWaves) __attribute__((amdgpu_waves_per_eu(2
     }
     l = swap32_sum(l);                                // the query's whole sum in both halves
 
-    // the waves' (m, l, o) meet in LDS (the online-softmax merge); wave 0 (which
-    // always holds key 0, valid for every row) forms context = O / L in bf16
+    // the waves' (m, l, o) meet in LDS (the online-softmax merge); wave c (c < CB)
+    // forms context = O / L in bf16 for the 32-dim column block c from its own o and
+    // the other waves' (one wave doing all four blocks was a serial tail of ~1 us)
     __syncthreads();                                  // every wave is done with its tiles
-    float* mo = (float*)smem;                         // [NWV-1][32][HD], then [NWV-1][32] (m, l)
-    float2* mlw = (float2*)(mo + (NWV - 1) * kPaRows * HD);
-    if (wave > 0) {
+    float* mo = (float*)smem;                         // [CB][NWV-1][32][32]: block c's partials of the other waves
+    float2* mlw = (float2*)(mo + CB * (NWV - 1) * kPaRows * 32);   // [NWV][32] (m, l)
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
+    for (int cb = 0; cb < CB; ++cb) {
+        if (cb == wave) continue;                     // uniform over the wave
+        const int slot = wave < cb ? wave : wave - 1;
+        float* dp = mo + ((cb * (NWV - 1) + slot) * kPaRows + r32) * 32 + hi * 4;
 #pragma unroll
-            for (int e = 0; e < 16; ++e)
-                mo[((wave - 1) * kPaRows + r32) * HD + cb * 32 + (e >> 2) * 8 + hi * 4 + (e & 3)] = o[cb][e];
-        if (hi == 0) mlw[(wave - 1) * kPaRows + r32] = make_float2(m, l);
+        for (int e = 0; e < 16; ++e) dp[(e >> 2) * 8 + (e & 3)] = o[cb][e];
     }
+    if (hi == 0) mlw[wave * kPaRows + r32] = make_float2(m, l);
     __syncthreads();
-    if (wave != 0) return;
+    if (wave >= CB) return;
     const int row = q0 + r32;
-    float M = m;
+    float M = -INFINITY;
 #pragma unroll
-    for (int w = 1; w < NWV; ++w) M = fmaxf(M, mlw[(w - 1) * kPaRows + r32].x);
+    for (int w = 0; w < NWV; ++w) M = fmaxf(M, mlw[w * kPaRows + r32].x);   // finite: wave 0 holds key 0
     float wt[NWV];
-    wt[0] = __builtin_amdgcn_exp2f(m - M);
-    float L = l * wt[0];
+    float L = 0.f;
 #pragma unroll
-    for (int w = 1; w < NWV; ++w) {
-        const float2 ml = mlw[(w - 1) * kPaRows + r32];
-        wt[w] = ml.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml.x - M);
+    for (int w = 0; w < NWV; ++w) {
+        const float2 ml = mlw[w * kPaRows + r32];
+        wt[w] = ml.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml.x - M);   // a wave without keys: 0
         L = fmaf(ml.y, wt[w], L);
     }
     if (row >= N) return;
     const float inv = 1.0f / L;
     uint16_t* dst = a.out + (long)row * a.Hq * HD + h * HD;
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
+    for (int c = 0; c < CB; ++c) {
+        if (c != wave) continue;                      // uniform; c is a constant below
 #pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {             // dims cb*32 + e4*8 + hi*4 .. + 3
+        for (int e4 = 0; e4 < 4; ++e4) {              // dims c*32 + e4*8 + hi*4 .. + 3
             float v[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int e = 4 * e4 + i, d = cb * 32 + e4 * 8 + hi * 4 + i;
-                float t = o[cb][e] * wt[0];
+                const int e = 4 * e4 + i, dl = e4 * 8 + hi * 4 + i;
+                float t = o[c][e] * wt[c];
 #pragma unroll
-                for (int w = 1; w < NWV; ++w) t = fmaf(mo[((w - 1) * kPaRows + r32) * HD + d], wt[w], t);
+                for (int sl = 0; sl < NWV - 1; ++sl)
+                    t = fmaf(mo[((c * (NWV - 1) + sl) * kPaRows + r32) * 32 + dl], wt[sl < c ? sl : sl + 1], t);
                 v[i] = t * inv;
             }
             const uint2 pk = make_uint2(f32x2_to_bf16x2(v[0], v[1]), f32x2_to_bf16x2(v[2], v[3]));
-            *(uint2*)(dst + cb * 32 + e4 * 8 + hi * 4) = pk;
+            *(uint2*)(dst + c * 32 + e4 * 8 + hi * 4) = pk;
         }
+    }
 }
 
 hipError_t launch_prefill_attn_mfma(const PrefillAttnArgs& a, hipStream_t s) {
