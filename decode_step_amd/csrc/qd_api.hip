@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/qd.h"
@@ -303,10 +304,18 @@ size_t qd_workspace_bytes(const qd_config* cfg, int32_t batch, int32_t max_ctx, 
     return plan_decode(cfg, batch, S, chunk).total;
 }
 
-qd_status qd_decode_step(const qd_config* cfg, const qd_weights* w, const qd_kv* kv, int32_t batch,
-                         const int32_t* tokens, const float* x_in, const int32_t* pos,
-                         const int32_t* pos_host, float* logits, int32_t* next_tokens, float* x_out,
-                         float* layer_out, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The decode step behind qd_decode_step and qd_decode_step_noalloc. `workspace`
+// NULL with scratch_bytes > 0 means: checks only up to the workspace size (the
+// caller resolves its scratch memory afterwards and calls again with it).
+qd_status decode_step_impl(const qd_config* cfg, const qd_weights* w, const qd_kv* kv, int32_t batch,
+                           const int32_t* tokens, const float* x_in, const int32_t* pos,
+                           const int32_t* pos_host, float* logits, int32_t* next_tokens, float* x_out,
+                           float* layer_out, void* workspace, size_t workspace_bytes, void* stream,
+                           bool checks_only = false) {
     g_err.clear();
     qd_status st = check_config(cfg);
     if (st != QD_OK) return st;
@@ -343,10 +352,11 @@ qd_status qd_decode_step(const qd_config* cfg, const qd_weights* w, const qd_kv*
         return fail(QD_ECAPACITY, "context of %d tokens needs %d attention splits > %d", max_tokens, S,
                     qd::attn_max_splits());
     const DecodePlan P = plan_decode(cfg, batch, S, chunk);
-    if (!workspace) return fail(QD_EWORKSPACE, "workspace is NULL");
-    if (((uintptr_t)workspace & 255u) != 0) return fail(QD_EALIGN, "workspace not 256-byte aligned");
     if (workspace_bytes < P.total)
         return fail(QD_EWORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, P.total);
+    if (checks_only) return QD_OK;
+    if (!workspace) return fail(QD_EWORKSPACE, "workspace is NULL");
+    if (((uintptr_t)workspace & 255u) != 0) return fail(QD_EALIGN, "workspace not 256-byte aligned");
 
     hipStream_t s = (hipStream_t)stream;
     char* ws = (char*)workspace;
@@ -463,6 +473,69 @@ qd_status qd_decode_step(const qd_config* cfg, const qd_weights* w, const qd_kv*
         if (next_tokens) QD_LAUNCH_K(QD_K_ARGMAX, qd::launch_argmax(pv, pi, grid, next_tokens, B, s), "argmax");
     }
     return QD_OK;
+}
+
+// Device scratch of qd_decode_step_noalloc: one copy per GPU, held until the
+// process ends. In host code `scratch` names a host-side stand-in, so its device
+// address on each GPU is taken once with hipGetSymbolAddress (that GPU current)
+// and only that address is ever handed to kernels.
+constexpr size_t kScratchBytes = QD_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+qd_status scratch_of_stream(hipStream_t s, void** out) {
+    int dev = -1, cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return fail(QD_EHIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    e = hipStreamGetDevice(s, &dev);
+    if (e != hipSuccess) return fail(QD_EHIP, "hipStreamGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(QD_EUNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess)
+            return fail(QD_EHIP, "hipSetDevice(%d) failed: %s", dev, hipGetErrorString(e));
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur) (void)hipSetDevice(cur);
+        if (e != hipSuccess || !p)
+            return fail(QD_EHIP, "hipGetSymbolAddress(scratch) on device %d failed: %s", dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return QD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+qd_status qd_decode_step(const qd_config* cfg, const qd_weights* w, const qd_kv* kv, int32_t batch,
+                         const int32_t* tokens, const float* x_in, const int32_t* pos,
+                         const int32_t* pos_host, float* logits, int32_t* next_tokens, float* x_out,
+                         float* layer_out, void* workspace, size_t workspace_bytes, void* stream) {
+    return decode_step_impl(cfg, w, kv, batch, tokens, x_in, pos, pos_host, logits, next_tokens, x_out,
+                            layer_out, workspace, workspace_bytes, stream);
+}
+
+qd_status qd_decode_step_noalloc(const qd_config* cfg, const qd_weights* w, const qd_kv* kv, int32_t batch,
+                                 const int32_t* tokens, const float* x_in, const int32_t* pos,
+                                 const int32_t* pos_host, float* logits, int32_t* next_tokens, float* x_out,
+                                 float* layer_out, void* stream) {
+    // every host check first, the size against the scratch maximum included
+    qd_status st = decode_step_impl(cfg, w, kv, batch, tokens, x_in, pos, pos_host, logits, next_tokens,
+                                    x_out, layer_out, nullptr, kScratchBytes, stream, /*checks_only=*/true);
+    if (st != QD_OK) {
+        if (st == QD_EWORKSPACE)
+            return fail(QD_EWORKSPACE, "qd_decode_step_noalloc: this step needs more than the %zu-byte static "
+                        "scratch (%s)", kScratchBytes, g_err.c_str());
+        return st;
+    }
+    void* ws = nullptr;
+    if ((st = scratch_of_stream((hipStream_t)stream, &ws)) != QD_OK) return st;
+    return decode_step_impl(cfg, w, kv, batch, tokens, x_in, pos, pos_host, logits, next_tokens, x_out,
+                            layer_out, ws, kScratchBytes, stream);
 }
 
 qd_status qd_quantize_rows_int8(const void* w, int32_t w_dtype, int64_t rows, int32_t cols, int8_t* q,

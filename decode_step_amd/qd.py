@@ -50,7 +50,7 @@ class qd_kv(Structure):
                 ("max_blocks", c_int32), ("num_pages", c_int32)]
 
 
-EXPORTS = ["qd_workspace_bytes", "qd_decode_step", "qd_prefill_block", "qd_kv_append", "qd_quantize_rows_int8",
+EXPORTS = ["qd_workspace_bytes", "qd_decode_step", "qd_decode_step_noalloc", "qd_prefill_block", "qd_kv_append", "qd_quantize_rows_int8",
            "qd_sample",
            "qd_last_error", "qd_abi_version", "qd_profile_enable", "qd_profile_read",
            "qd_profile_reset"]
@@ -76,6 +76,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qd_decode_step.argtypes = [POINTER(qd_config), POINTER(qd_weights), POINTER(qd_kv), c_int32,
                                    P, P, P, POINTER(c_int32), P, P, P, P, P, c_size_t, P]
     lib.qd_decode_step.restype = c_int32
+    lib.qd_decode_step_noalloc.argtypes = [POINTER(qd_config), POINTER(qd_weights), POINTER(qd_kv), c_int32,
+                                           P, P, P, POINTER(c_int32), P, P, P, P, P]
+    lib.qd_decode_step_noalloc.restype = c_int32
     lib.qd_prefill_block.argtypes = [POINTER(qd_config), POINTER(qd_layer), c_int32, POINTER(qd_kv),
                                      c_int32, c_int32, P, c_int32, P, P, c_size_t, P]
     lib.qd_prefill_block.restype = c_int32
@@ -124,6 +127,17 @@ def qd_decode_step(cfg, weights, kv, batch, tokens, x_in, pos, pos_host, logits,
     return int(lib().qd_decode_step(ctypes.byref(cfg), ctypes.byref(weights), ctypes.byref(kv),
                                     batch, tokens, x_in, pos, pos_host, logits, next_tokens, x_out,
                                     layer_out, workspace, workspace_bytes, stream))
+
+
+def qd_decode_step_noalloc(cfg, weights, kv, batch, tokens, x_in, pos, pos_host, logits, next_tokens,
+                           x_out, layer_out, stream) -> int:
+    """Raw call of the workspace-free step (the library's static device scratch)."""
+    return int(lib().qd_decode_step_noalloc(ctypes.byref(cfg), ctypes.byref(weights), ctypes.byref(kv),
+                                            batch, tokens, x_in, pos, pos_host, logits, next_tokens, x_out,
+                                            layer_out, stream))
+
+
+QD_NOALLOC_SCRATCH_BYTES = 16 << 20   # include/qd.h
 
 
 def qd_prefill_block(cfg, layer, layer_index, kv, n_tokens, start_pos, x_in, x_dtype, x_out,

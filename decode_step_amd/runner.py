@@ -143,6 +143,20 @@ class DecodeRunner:
             Q.check(st)
         return st
 
+    def step_noalloc(self, pos_host: np.ndarray, pos_dev: torch.Tensor, tokens: Optional[torch.Tensor] = None,
+                     x_in: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None,
+                     next_tokens: Optional[torch.Tensor] = None, x_out: Optional[torch.Tensor] = None,
+                     layer_out: Optional[torch.Tensor] = None, stream=None, raise_on_error=True) -> int:
+        """The same step through qd_decode_step_noalloc (no workspace argument)."""
+        ph = np.ascontiguousarray(pos_host, dtype=np.int32)
+        B = int(ph.shape[0])
+        st = Q.qd_decode_step_noalloc(self.cfg, self.weights, self.kv, B, _ptr(tokens), _ptr(x_in),
+                                      _ptr(pos_dev), ph.ctypes.data_as(POINTER(c_int32)), _ptr(logits),
+                                      _ptr(next_tokens), _ptr(x_out), _ptr(layer_out), _stream_handle(stream))
+        if raise_on_error:
+            Q.check(st)
+        return st
+
     def prefill(self, layer_index: int, n_tokens: int, start_pos: int, x_in: torch.Tensor,
                 x_out: torch.Tensor, stream=None, raise_on_error=True) -> int:
         xd = Q.QD_BF16 if x_in.dtype == torch.bfloat16 else Q.QD_F32

@@ -137,6 +137,24 @@ qd_status qd_decode_step(const qd_config *cfg, const qd_weights *w, const qd_kv 
                          float *logits, int32_t *next_tokens, float *x_out, float *layer_out,
                          void *workspace, size_t workspace_bytes, void *stream);
 
+/* qd_decode_step for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc. The
+ * same step with the same arguments, minus the workspace: its scratch memory is
+ * a static device array of QD_NOALLOC_SCRATCH_BYTES inside the library, one per
+ * GPU (taken by the first call on that GPU, held until the process ends). The
+ * call allocates nothing. A step whose workspace (qd_workspace_bytes) exceeds
+ * that size returns QD_EWORKSPACE before anything is enqueued. Every call on a
+ * GPU shares that GPU's scratch: calls that overlap on one GPU (different
+ * streams, or different threads) race and must be serialised by the caller;
+ * nothing of a call's scratch is read by the next (each step writes what it
+ * reads). The stream's device is the GPU used. */
+#define QD_NOALLOC_SCRATCH_BYTES (16u << 20)
+qd_status qd_decode_step_noalloc(const qd_config *cfg, const qd_weights *w, const qd_kv *kv,
+                                 int32_t batch, const int32_t *tokens, const float *x_in,
+                                 const int32_t *pos, const int32_t *pos_host,
+                                 float *logits, int32_t *next_tokens, float *x_out, float *layer_out,
+                                 void *stream);
+
 /* One decoder block over n_tokens consecutive tokens of sequence 0 of the block
  * table, at positions start_pos .. start_pos + n_tokens - 1, causal (row i
  * attends to positions 0..start_pos+i). bf16 weights only: the projections are

@@ -248,3 +248,17 @@ def test_sample_checks(lib):
     _expect(s(FAKE, 1, 100, 1.0, 0, 0.9, FAKE, FAKE, None), Q.QD_EUNSUPPORTED)
     _expect(s(FAKE, 1, 100, 1.0, 1025, 0.9, FAKE, FAKE, None), Q.QD_EUNSUPPORTED)
     _expect(s(FAKE + 2, 1, 100, 1.0, 10, 0.9, FAKE, FAKE, None), Q.QD_EALIGN)
+
+
+def test_noalloc_host_checks(lib):
+    # the workspace-free step runs every host check before it touches the GPU
+    f = Fixture(_cfg(vocab=300000), pos=[3] * 16, max_blocks=1)
+    ph = f.pos.ctypes.data_as(POINTER(c_int32))
+    need = Q.qd_workspace_bytes(f.cfg, 16, 4)
+    assert need > Q.QD_NOALLOC_SCRATCH_BYTES
+    _expect(Q.qd_decode_step_noalloc(f.cfg, f.w, f.kv, 16, FAKE, None, FAKE, ph, FAKE, None, None, None, None),
+            Q.QD_EWORKSPACE)
+    assert "static" in Q.qd_last_error()
+    g = Fixture(_cfg(head_dim=96))
+    _expect(Q.qd_decode_step_noalloc(g.cfg, g.w, g.kv, 1, FAKE, None, FAKE, g.pos.ctypes.data_as(POINTER(c_int32)),
+                                     FAKE, None, None, None, None), Q.QD_ESHAPE)
