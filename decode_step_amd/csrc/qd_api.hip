@@ -10,7 +10,9 @@
 
 #include "../../include/qd.h"
 #include "qd_launch.h"
+#include "qd_step_sched.h"
 #include <cmath>
+#include <cstdlib>
 
 namespace {
 
@@ -69,7 +71,13 @@ struct DecodePlan {
     int B, D, Hq, Hkv, hd, G, F, V, qkvr;
     int chunk, S;
     size_t off_x, off_qkv, off_qss, off_part, off_rope, off_ctx, off_h, off_logits, off_pv, off_pi, total;
+    // batch-1 one-launch step: tagged words (two layer parities each), argmax partials,
+    // RoPE table, error words
+    int step_S;   // attention splits the part region holds
+    size_t off_sxb, off_scnt, off_sqkv, off_spart, off_sy, off_sh, off_send, off_sam_v, off_sam_i, off_srope, off_serr;
 };
+
+
 
 // Attention work split. Grouped: one workgroup holds all query heads of a KV
 // head (each K/V row is read once) and a split of `chunk` tokens, the chunk
@@ -166,6 +174,25 @@ DecodePlan plan_decode(const qd_config* c, int B, int S, int chunk) {
     p.off_logits = take(sizeof(float) * (size_t)B * p.V);
     p.off_pv = take(sizeof(float) * B * kLogitsGridCap);
     p.off_pi = take(sizeof(int) * B * kLogitsGridCap);
+    p.step_S = 0;
+    if (B == 1 && qd::step::step_config_ok(c)) {
+        const int S1 = qd::step::step_split_cap(c);
+        p.step_S = S1;
+        const size_t w = sizeof(unsigned long long);
+        p.off_sxb = take(sizeof(float) * 2 * p.D);
+        p.off_sy = take(sizeof(float) * 2 * (size_t)p.Hkv * p.D);
+        p.off_sh = take(sizeof(float) * 2 * (size_t)p.F);
+        p.off_sqkv = o;   // the prologue clears from here to off_send: tagged words, then counters
+        o += w * 2 * p.qkvr;
+        p.off_spart = o; o += w * 2 * (size_t)p.Hkv * S1 * p.G * (p.hd + 2);
+        p.off_scnt = o; o += sizeof(uint32_t) * 3 * qd::kStepMaxLayers * 8 * 32;
+        p.off_send = o;
+        o = round_up(o, 256);
+        p.off_sam_v = take(sizeof(float) * qd::kStepWgs);
+        p.off_sam_i = take(sizeof(int) * qd::kStepWgs);
+        p.off_srope = take(sizeof(float) * 2 * (p.hd / 2));
+        p.off_serr = take(sizeof(uint32_t) * 4);
+    }
     p.total = o;
     return p;
 }
@@ -255,6 +282,45 @@ qd_status check_layer(const qd_config* c, const qd_layer* L, int l) {
     for (const void* p : opt)
         if (p && !aligned4(p)) return fail(QD_EALIGN, "layer %d: bias/gain not 4-byte aligned", l);
     return QD_OK;
+}
+
+// QD_STEP_KERNEL=1 in the environment sends eligible batch-1 steps to the one-launch
+// step kernel; otherwise they take the per-op launch path (read at every call, so a
+// process can compare the two).
+bool step_kernel_enabled() {
+    const char* e = getenv("QD_STEP_KERNEL");
+    return e && e[0] == '1';
+}
+
+// The one-launch step needs the 256 CUs in 8 XCDs of an MI355X (checked once per
+// device; the kernel also checks each workgroup's XCD).
+bool device_runs_step_grid(hipStream_t s) {
+    static std::mutex mu;
+    static signed char known[64] = {};
+    int dev = 0;
+    if (hipStreamGetDevice(s, &dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!known[dev]) {
+        int n = 0;
+        known[dev] = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+                      n == qd::kStepWgs) ? 1 : -1;
+    }
+    return known[dev] > 0;
+}
+
+// Pointers the step's loader copies by LDS DMA must be 16-byte aligned, and every
+// layer must have all of the q/k/v biases or none.
+bool step_pointers_ok(const qd_config* c, const qd_weights* w, bool head) {
+    if (head && !aligned16(w->final_norm)) return false;
+    const bool b0 = w->layers_host[0].bq != nullptr;
+    for (int l = 0; l < c->n_layers; ++l) {
+        const qd_layer& L = w->layers_host[l];
+        const bool b = L.bq != nullptr;
+        if (b != b0 || (L.bk != nullptr) != b || (L.bv != nullptr) != b) return false;
+        if (b && (!aligned16(L.bq) || !aligned16(L.bk) || !aligned16(L.bv))) return false;
+        if (c->qk_norm && (!aligned16(L.q_norm) || !aligned16(L.k_norm))) return false;
+    }
+    return true;
 }
 
 qd_status check_kv_positions(const qd_config* c, const qd_kv* kv, int B, const int32_t* pos_host,
@@ -386,6 +452,46 @@ qd_status decode_step_impl(const qd_config* cfg, const qd_weights* w, const qd_k
         }
         return qd::launch_gemv(g, wbf, epi, grid_cap, grid_out, s);
     };
+
+    // batch 1: the one-launch step, when the config, the device and the position allow
+    if (B == 1 && P.step_S > 0 && step_kernel_enabled() && device_runs_step_grid(s) &&
+        step_pointers_ok(cfg, w, want_head)) {
+        const qd::step::StepPlan sp = qd::step::plan_step(cfg, max_tokens);
+        if (sp.ok && sp.S <= P.step_S) {
+            qd::StepArgs sa{};
+            sa.L = c.n_layers; sa.D = D; sa.Hq = P.Hq; sa.Hkv = P.Hkv; sa.hd = P.hd; sa.G = P.G; sa.F = P.F;
+            sa.V = c.vocab; sa.qkvr = P.qkvr; sa.eps = c.rms_eps; sa.scale = 1.0f / sqrtf((float)P.hd);
+            sa.qk_norm = c.qk_norm; sa.has_bias = w->layers_host[0].bq != nullptr;
+            sa.S = sp.S; sa.C = sp.C;
+            sa.up_wa = sp.up_wa; sa.up_wb = sp.up_wb; sa.down_wa = sp.down_wa; sa.down_wb = sp.down_wb;
+            sa.pos = pos; sa.block_table = kv->block_table; sa.max_blocks = kv->max_blocks; sa.num_pages = kv->num_pages;
+            sa.final_norm = want_head ? w->final_norm : nullptr;
+            sa.lm_head = want_head ? w->lm_head : nullptr;
+            sa.logits = lg; sa.x_out = x_out; sa.layer_out = layer_out;
+            sa.argmax_val = (float*)(ws + P.off_sam_v); sa.argmax_idx = (int*)(ws + P.off_sam_i);
+            typedef unsigned long long u64;
+            sa.xb = (float*)(ws + P.off_sxb); sa.y = (float*)(ws + P.off_sy); sa.h = (float*)(ws + P.off_sh);
+            sa.qkv = (u64*)(ws + P.off_sqkv); sa.part = (u64*)(ws + P.off_spart);
+            sa.part_stride = (long)P.Hkv * sp.S * P.G * (P.hd + 2);
+            sa.cnt = (uint32_t*)(ws + P.off_scnt);
+            sa.rope = (float2*)(ws + P.off_srope); sa.err = (uint32_t*)(ws + P.off_serr);
+            sa.clear_from = sa.qkv; sa.clear_n = (long)((P.off_send - P.off_sqkv) / sizeof(u64));
+            for (int l = 0; l < c.n_layers; ++l) {
+                const qd_layer& L = w->layers_host[l];
+                qd::StepLayer& t = sa.layer[l];
+                t.attn_norm = L.attn_norm; t.wq = L.wq; t.wk = L.wk; t.wv = L.wv; t.bq = L.bq; t.bk = L.bk; t.bv = L.bv;
+                t.q_norm = L.q_norm; t.k_norm = L.k_norm; t.wo = L.wo; t.mlp_norm = L.mlp_norm; t.w_gate = L.w_gate;
+                t.w_up = L.w_up; t.w_down = L.w_down; t.kc = kv->k_pages_host[l]; t.vc = kv->v_pages_host[l];
+            }
+            QD_LAUNCH_K(QD_K_EMBED, qd::launch_step_prologue(sa, tokens, w->embed, x_in, c.rope_theta, s),
+                        "step prologue");
+            QD_LAUNCH_K(QD_K_STEP, qd::launch_step_kernel(sa, s), "step kernel");
+            if (next_tokens)
+                QD_LAUNCH_K(QD_K_ARGMAX, qd::launch_argmax(sa.argmax_val, sa.argmax_idx, qd::kStepWgs, next_tokens, 1, s),
+                            "argmax");
+            return QD_OK;
+        }
+    }
 
     qd::StepInputArgs si{};
     si.tokens = tokens; si.embed = w->embed; si.embed_scale = w->s_embed; si.x_in = x_in; si.x = x;

@@ -127,6 +127,49 @@ struct PrefillAttnArgs {
 };
 hipError_t launch_prefill_attn_mfma(const PrefillAttnArgs& a, hipStream_t s);
 
+// Batch-1 decode step as one persistent cooperative launch (qd_step.hip): bf16
+// weights and KV, one workgroup per CU, activations exchanged as tagged 64-bit
+// words. Pointers of every layer travel in the arguments.
+constexpr int kStepWgs = 256;
+constexpr int kStepMaxLayers = 64;
+struct StepLayer {
+    const void *attn_norm, *wq, *wk, *wv, *bq, *bk, *bv, *q_norm, *k_norm;
+    const void *wo, *mlp_norm, *w_gate, *w_up, *w_down;
+    void *kc, *vc;           // the layer's K and V page pools
+};
+struct StepArgs {
+    int L, D, Hq, Hkv, hd, G, F, V, qkvr;
+    float eps, scale;
+    int qk_norm, has_bias;
+    int S, C;                // attention splits of C keys (C a multiple of 64)
+    int up_wa, up_wb, down_wa, down_wb;   // gate|up and down row weights: XCDs < Hkv, the others
+    const int* pos;
+    const int* block_table;  // row 0
+    int max_blocks, num_pages;
+    const void* final_norm;
+    const void* lm_head;     // NULL: no head
+    float* logits;           // [V]
+    float* x_out;            // [D] or NULL
+    float* layer_out;        // [L][D] or NULL
+    float* argmax_val;       // [kStepWgs] per-workgroup partials
+    int* argmax_idx;
+    float *xb, *y, *h;       // vectors read across XCDs, two layer parities each: x [2][D],
+                             // y [2][Hkv][D], h [2][F]
+    unsigned long long *qkv, *part;   // tagged words read within an XCD, two parities each
+    long part_stride;        // words per parity of part
+    uint32_t* cnt;           // completion counters [3][kStepMaxLayers][8 XCDs][32]
+    float2* rope;            // [hd/2] (cos, sin) of the step's position
+    uint32_t* err;           // [4]: abort flag, code of the wait that gave up
+    unsigned long long* clear_from;   // words the prologue clears: tagged words and counters
+    long clear_n;
+    StepLayer layer[kStepMaxLayers];
+};
+// the prologue (embedding or x_in, RoPE table, cleared tags), then the step kernel
+hipError_t launch_step_prologue(const StepArgs& a, const int* tokens, const void* embed, const float* x_in,
+                                float theta, hipStream_t s);
+hipError_t launch_step_kernel(const StepArgs& a, hipStream_t s);
+int step_max_vin();   // floats of one input buffer: bounds (Hkv + 1) D, F and S G (hd + 2)
+
 // x = embedding rows of `tokens` (or a copy of x_in), plus the RoPE table of the
 // step's positions (qd_attention.hip).
 struct StepInputArgs {

@@ -56,7 +56,7 @@ EXPORTS = ["qd_workspace_bytes", "qd_decode_step", "qd_decode_step_noalloc", "qd
            "qd_profile_reset"]
 
 (QD_K_EMBED, QD_K_QKV, QD_K_QKV_POST, QD_K_ATTN, QD_K_MERGE, QD_K_O, QD_K_GATEUP, QD_K_DOWN,
- QD_K_LMHEAD, QD_K_ARGMAX, QD_K_PREFILL_GEMM, QD_K_PREFILL_ATTN, QD_K_OTHER) = range(13)
+ QD_K_LMHEAD, QD_K_ARGMAX, QD_K_PREFILL_GEMM, QD_K_PREFILL_ATTN, QD_K_OTHER, QD_K_STEP) = range(14)
 
 
 class QdError(RuntimeError):

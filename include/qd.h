@@ -211,7 +211,8 @@ qd_status qd_sample(const float *logits, int32_t batch, int32_t vocab, float tem
 typedef enum {
     QD_K_EMBED = 0, QD_K_QKV = 1, QD_K_QKV_POST = 2, QD_K_ATTN = 3, QD_K_MERGE = 4,
     QD_K_O = 5, QD_K_GATEUP = 6, QD_K_DOWN = 7, QD_K_LMHEAD = 8, QD_K_ARGMAX = 9,
-    QD_K_PREFILL_GEMM = 10, QD_K_PREFILL_ATTN = 11, QD_K_OTHER = 12
+    QD_K_PREFILL_GEMM = 10, QD_K_PREFILL_ATTN = 11, QD_K_OTHER = 12,
+    QD_K_STEP = 13   /* the batch-1 one-launch step kernel */
 } qd_kernel_kind;
 
 /* Measurement hook, off by default: while bit k of kind_mask is set, every launch
