@@ -168,7 +168,6 @@ struct StepArgs {
 hipError_t launch_step_prologue(const StepArgs& a, const int* tokens, const void* embed, const float* x_in,
                                 float theta, hipStream_t s);
 hipError_t launch_step_kernel(const StepArgs& a, hipStream_t s);
-int step_max_vin();   // floats of one input buffer: bounds (Hkv + 1) D, F and S G (hd + 2)
 
 // x = embedding rows of `tokens` (or a copy of x_in), plus the RoPE table of the
 // step's positions (qd_attention.hip).

@@ -93,13 +93,15 @@ __device__ __forceinline__ uint32_t hw_xcc_id() {
 // ---------------------------------------------------------------- shared state
 struct Smem {
     uint8_t ring[kRingSlots * 1024];
-    float vin[2][kVin];
-    float xa[1024];          // x_a (P3 -> P4); the merged context (P2); x (P0, head); new k, v (P1)
+    uint32_t xs_h[kXs], xs_l[kXs];  // a product's split input (bf16 hi / lo pairs)
+    float work[kWork];              // P1: q|k|v, scores, per-wave P.V; P2: the split partials
+    float xa[1024];                 // x_a (P3 -> P4)
     float2 rope[64];
+    float wts[8 * 32];              // P2: merge weight of head h, split s
     uint32_t filled;                // slots whose DMA has landed (loader)
     uint32_t consumed[kNcw];        // slots each compute wave is done with
     uint32_t bar, abort_;
-    float ssp[2][kNcw];             // sums of squares per compute wave (two parities)
+    float ssp[kNcw];                // sums of squares per compute wave
     float red_v[kNcw];
     int red_i[kNcw];
 };
@@ -125,7 +127,7 @@ __device__ __forceinline__ void raise_abort(Ctl& c, uint32_t code) {
 __device__ __forceinline__ bool spin_check(Ctl& c, uint32_t& it, uint32_t code) {
     ++it;
     if ((it & 15) == 0 && lds_ld(&g_sm.abort_)) return true;
-    if ((it & 255) == 0 && ld_far32(c.a->err)) {
+    if ((it & 4095) == 0 && ld_far32(c.a->err)) {   // rare: the load waits for this wave's stores
         lds_st(&g_sm.abort_, 1u);
         return true;
     }
@@ -255,66 +257,173 @@ __device__ __forceinline__ bool wait_counts(Ctl& c, int k0, int l0, int nx0, int
     }
 }
 
-// Read n floats (n a multiple of 4) that other XCDs wrote: dst[e] = src[e] (times
-// element e of the bf16 gain block at ring slot gain_slot when >= 0); *ss (when given) gains the lane's sum of
-// squares. Chunk q of 16 bytes goes to lane q % 256; every load of a lane is in
-// flight together (out-of-range chunks reread chunk 0 and are dropped).
-template <int PER>
-__device__ __forceinline__ void load_far(const float* src, int n, float* dst, int gain_slot, float* ss, int ct) {
-    const int nq = n >> 2;
-    float4 v[PER];
+// ---------------------------------------------------------------- products from the ring
+// A product's input vector (x after its norm gains, the merged context, h) is held
+// as two bf16 vectors, hi = bf16(v) and lo = bf16(v - hi), packed in pairs like
+// the weights, so each pair of weights takes two v_dot2_f32_bf16 (the products of
+// two bf16 are exact in float32; hi + lo carries v to about 2^-17 relative). A
+// float32 FMA per weight would take an extra instruction to widen each weight.
+typedef __bf16 qd_bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2(uint32_t w, uint32_t x, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(qd_bf16x2, w), __builtin_bit_cast(qd_bf16x2, x), acc,
+                                           false);
+}
+__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+    hi = f32x2_to_bf16x2(a, b);
+    lo = f32x2_to_bf16x2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
+}
+// elements 4 q .. 4 q + 3 of the split input
+__device__ __forceinline__ void xs_store4(int q, float4 v) {
+    uint32_t h0, l0, h1, l1;
+    split2(v.x, v.y, h0, l0);
+    split2(v.z, v.w, h1, l1);
+    *(uint2*)&g_sm.xs_h[2 * q] = make_uint2(h0, h1);
+    *(uint2*)&g_sm.xs_l[2 * q] = make_uint2(l0, l1);
+}
+// one 16-byte chunk (8 weights) times the matching split input chunk
+__device__ __forceinline__ float dot_chunk(const uint4 w, const uint4 h, const uint4 l, float acc) {
+    acc = dot2(w.x, h.x, acc);
+    acc = dot2(w.y, h.y, acc);
+    acc = dot2(w.z, h.z, acc);
+    acc = dot2(w.w, h.w, acc);
+    acc = dot2(w.x, l.x, acc);
+    acc = dot2(w.y, l.y, acc);
+    acc = dot2(w.z, l.z, acc);
+    acc = dot2(w.w, l.w, acc);
+    return acc;
+}
+
+// A product row is read by one wave at a time, lane i taking 16-byte chunks i,
+// i + 64, ...: each LDS read is then 1 KB of consecutive bytes. (Rows are 1792 or
+// 9728 bytes long, multiples of 256: with several rows per wave at once, the rows'
+// lanes met in the same LDS banks and every read cost several times over.) The
+// input's chunks of the lane stay in registers for the whole product; chunks at or
+// past the row's end are zero.
+template <int NJ>
+struct XW {
+    uint4 h[NJ], l[NJ];
+};
+template <int NJ>
+__device__ __forceinline__ void load_xw(XW<NJ>& x, int lane, int nch) {
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        const int q = ct + 256 * i;
-        v[i] = ld_far16(src, q < nq ? q : 0);
-    }
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        const int q = ct + 256 * i;
-        if (q < nq) {
-            float f[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-            if (ss) *ss += f[0] * f[0] + f[1] * f[1] + f[2] * f[2] + f[3] * f[3];
-            if (gain_slot >= 0) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) f[e] *= ring_bf16((uint32_t)gain_slot, 4 * q + e);
-            }
-            *(float4*)(dst + 4 * q) = make_float4(f[0], f[1], f[2], f[3]);
+    for (int j = 0; j < NJ; ++j) {
+        const int c = lane + 64 * j;
+        x.h[j] = make_uint4(0u, 0u, 0u, 0u);
+        x.l[j] = x.h[j];
+        if (c < nch) {
+            x.h[j] = *(const uint4*)&g_sm.xs_h[4 * c];
+            x.l[j] = *(const uint4*)&g_sm.xs_l[4 * c];
         }
     }
 }
 
-// Rows [0, nrows) of a packed bf16 block (row r at byte r * seg, in one lap of the
-// ring) times x (seg / 2 floats in LDS); LPR lanes per row. fn(row, sum) runs on the
-// first lane of each row's group.
-template <int LPR, typename Fn>
-__device__ __forceinline__ void block_dots(uint32_t s0, int nrows, int seg, const float* x, int ct,
+constexpr uint32_t kRingBytes = kRingSlots * 1024u;
+
+// ring byte offset of byte `off` of a block that starts at absolute slot s0
+__device__ __forceinline__ uint32_t ring_at(uint32_t s0, uint32_t off) {
+    const uint32_t o = (s0 % kRingSlots) * 1024u + off;
+    return o >= kRingBytes ? o - kRingBytes : o;
+}
+
+// R rows (ring byte offsets rb[r], wave-uniform; rows whose bit of `mask` is clear
+// are skipped) of nch chunks times the input: out[r] is the full sum in every lane.
+// Every chunk load of the R rows is issued before the first product.
+template <int NJ, int R>
+__device__ __forceinline__ void rows_dot(const uint32_t (&rb)[R], uint32_t mask, int lane, int nch, const XW<NJ>& x,
+                                         float (&out)[R]) {
+    uint4 w[R][NJ];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const uint32_t b = __builtin_amdgcn_readfirstlane(rb[r]);
+        const bool flat = b + (uint32_t)nch * 16u <= kRingBytes;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int c = lane + 64 * j;
+            w[r][j] = make_uint4(0u, 0u, 0u, 0u);
+            if (((mask >> r) & 1u) && c < nch) {
+                uint32_t o = b + (uint32_t)c * 16u;
+                if (!flat) o = o >= kRingBytes ? o - kRingBytes : o;
+                w[r][j] = *(const uint4*)(g_sm.ring + o);
+            }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        float acc = dot_chunk(w[r][0], x.h[0], x.l[0], 0.f);
+#pragma unroll
+        for (int j = 1; j < NJ; ++j) acc = dot_chunk(w[r][j], x.h[j], x.l[j], acc);
+        out[r] = group_sum<64>(acc);
+    }
+}
+
+// One row per wave with the input read from LDS beside each weight chunk, NG chunks
+// at a time: for a product whose rows are used once per wave (the down product),
+// holding the input in registers would not be repaid.
+template <int NG>
+__device__ __forceinline__ float row_dot_lds(uint32_t rb, int lane, int nch) {
+    const uint32_t b = __builtin_amdgcn_readfirstlane(rb);
+    const bool flat = b + (uint32_t)nch * 16u <= kRingBytes;
+    float acc = 0.f;
+    for (int c0 = 0; c0 < nch; c0 += 64 * NG) {
+        uint4 w[NG], xh[NG], xl[NG];
+#pragma unroll
+        for (int j = 0; j < NG; ++j) {
+            const int c = c0 + lane + 64 * j;
+            w[j] = make_uint4(0u, 0u, 0u, 0u);
+            xh[j] = w[j];
+            xl[j] = w[j];
+            if (c < nch) {
+                uint32_t o = b + (uint32_t)c * 16u;
+                if (!flat) o = o >= kRingBytes ? o - kRingBytes : o;
+                w[j] = *(const uint4*)(g_sm.ring + o);
+                xh[j] = *(const uint4*)&g_sm.xs_h[4 * c];
+                xl[j] = *(const uint4*)&g_sm.xs_l[4 * c];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NG; ++j) acc = dot_chunk(w[j], xh[j], xl[j], acc);
+    }
+    return group_sum<64>(acc);
+}
+
+// Rows [0, nrows) of a packed bf16 block at slot s0 (row i at byte i * seg): wave
+// w takes rows w R .. w R + R - 1, then the next 4 R, ...; fn(row, sum) runs on
+// lane 0 of the wave.
+template <int NJ, int R, typename Fn>
+__device__ __forceinline__ void block_rows(uint32_t s0, int nrows, int seg, const XW<NJ>& x, int wave, int lane,
                                            Fn fn) {
-    constexpr int RPP = 256 / LPR;
-    const int nch = seg >> 4, lr = ct % LPR;
-    for (int r0 = 0; r0 < nrows; r0 += RPP) {
-        const int row = r0 + ct / LPR;
-        float acc = 0.f;
-        if (row < nrows) {
-            for (int ch = lr; ch < nch; ch += LPR) {
-                const uint4 wv = *(const uint4*)(g_sm.ring + ring_off(s0, (uint32_t)(row * seg + ch * 16)));
-                const float4 x0 = *(const float4*)(x + ch * 8), x1 = *(const float4*)(x + ch * 8 + 4);
-                float f[8];
-                widen16(wv, f);
-                acc += f[0] * x0.x + f[1] * x0.y + f[2] * x0.z + f[3] * x0.w + f[4] * x1.x + f[5] * x1.y +
-                       f[6] * x1.z + f[7] * x1.w;
-            }
+    const int nch = seg >> 4;
+    for (int r0 = wave * R; r0 < nrows; r0 += kNcw * R) {
+        uint32_t rb[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) rb[r] = ring_at(s0, (uint32_t)((r0 + r) * seg));
+        float out[R];
+        const int nv = nrows - r0 < R ? nrows - r0 : R;
+        rows_dot<NJ, R>(rb, (1u << nv) - 1u, lane, nch, x, out);
+        if (lane == 0) {
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                if (r0 + r < nrows) fn(r0 + r, out[r]);
         }
-        acc = group_sum<LPR>(acc);
-        if (lr == 0 && row < nrows) fn(row, acc);
     }
 }
 
-__device__ __forceinline__ float rms_scale(const float* x, int D, float eps, int lane) {
+// Far vector loads (another XCD wrote them): n floats (n a multiple of 4) as
+// 16-byte chunks, chunk q to compute thread q % 256.
+// RMSNorm input: x (times the bf16 gains of the block at ring slot gs) goes to
+// the split input; the lane's sum of squares of x is returned.
+__device__ __forceinline__ float load_norm_input(const float* src, int n, uint32_t gs, int ct) {
     float ss = 0.f;
-    for (int d = lane; d < D; d += 64) ss += x[d] * x[d];
-    ss = group_sum<64>(ss);
-    return 1.0f / sqrtf(ss / (float)D + eps);
+    for (int q = ct; q < (n >> 2); q += 256) {
+        const float4 v = ld_far16(src, q);
+        ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+        const uint2 gw = *(const uint2*)(g_sm.ring + ring_off(gs, (uint32_t)(8 * q)));
+        xs_store4(q, make_float4(v.x * bf16_to_f32(gw.x & 0xffffu), v.y * bf16_to_f32(gw.x >> 16),
+                                 v.z * bf16_to_f32(gw.y & 0xffffu), v.w * bf16_to_f32(gw.y >> 16)));
+    }
+    return ss;
 }
+
 // 1/sqrt(mean of squares + eps) from the four compute waves' partial sums (each
 // wave publishes its lanes' sum before a barrier; every wave adds them in order)
 __device__ __forceinline__ void ss_publish(float* part, int wave, float ss) {
@@ -451,11 +560,25 @@ __device__ __forceinline__ void loader(const StepArgs& a, const Sched& S, Ctl& c
 }
 
 // ---------------------------------------------------------------- the compute waves
+// The thread index as a value the compiler cannot see through: each phase derives
+// its LDS addresses and lane masks from it, so they are recomputed in the phase
+// instead of being hoisted out of the layer loop, where the addresses and masks of
+// every phase at once spilled.
+__device__ __forceinline__ int opaque(int v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
 __device__ __forceinline__ uint32_t take(uint32_t& cur, const Blk& b) {
     const uint32_t s0 = cur;
     cur += blk_slots(b);
     return s0;
 }
+
+// P1's work buffer: q heads, k, v (G + 2 vectors of 64), then the scores of head h
+// at kScOff + 256 h (keys of the split), then the per-wave P.V sums.
+constexpr int kScOff = 640;
+constexpr int kPvOff = kScOff + 8 * 256;
+static_assert(kPvOff + kNcw * 512 <= kWork, "P1 work buffer");
 
 __device__ __forceinline__ void compute(const StepArgs& a, const Sched& S, Ctl& c) {
     const int ct = threadIdx.x - 64;          // 0..255
@@ -465,7 +588,11 @@ __device__ __forceinline__ void compute(const StepArgs& a, const Sched& S, Ctl& 
     const int g = S.xcd;
     const int p = S.p;
     uint32_t cur = 0;   // absolute ring slot of the next block
-    uint32_t vb = 0;    // input buffer parity
+    // The new token's k and v (lane d: dimension d) wait in registers from P1 to P3:
+    // stored in P1 they held up the next load of the wave (loads and stores share
+    // one in-order counter) until the cache had taken them.
+    uint32_t app = 0;
+    bool has_app = false;
     for (int i = ct; i < hd / 2; i += 256) g_sm.rope[i] = a.rope[i];
     float* const XB = a.xb;
     for (int l = 0; l < a.L; ++l) {
@@ -476,19 +603,20 @@ __device__ __forceinline__ void compute(const StepArgs& a, const Sched& S, Ctl& 
             const Blk gb = get_block(a, S, l, PH_QKV, 0);
             const uint32_t gs = take(cur, gb);
             if (!wait_filled(c, gs + blk_slots(gb), 0x1000u | l)) return;
-            float* xin = g_sm.vin[vb];
-            float ss = 0.f;
             if (l > 0) {   // layer 0 reads the prologue's x
                 if (wave == 0 && !wait_counts(c, CNT_X, l - 1, kXcd, kSlotsPerXcd, kSlotsPerXcd, -1, 0, 0, 0, 0,
                                               0x1050u | l)) return;
                 if (!cw_barrier(c, 0x1060u | l)) return;
             }
-            load_far<1>(XB + (size_t)ppar * D, D, xin, (int)gs, &ss, ct);
-            ss_publish(g_sm.ssp[vb], wave, ss);
+            ss_publish(g_sm.ssp, wave, load_norm_input(XB + (size_t)ppar * D, D, gs, ct));
             if (!cw_barrier(c, 0x1200u | l)) return;
-            const float r = ss_scale(g_sm.ssp[vb], D, a.eps);
+            const float r = ss_scale(g_sm.ssp, D, a.eps);
+            const int lno = opaque(lane);
+            XW<2> x;
+            load_xw<2>(x, lno, D >> 3);
             const int np = qkv_nparts(a, S.slot);
             u64* out = a.qkv + (size_t)par * a.qkvr;
+            const uint32_t tg = tag_of(l, PH_QKV);
             for (int k = 0; k < np; ++k) {
                 const QkvPart q = qkv_part(a, g, S.slot, k);
                 uint32_t bs = 0;
@@ -501,18 +629,15 @@ __device__ __forceinline__ void compute(const StepArgs& a, const Sched& S, Ctl& 
                 const uint32_t ws = take(cur, wb);
                 if (!wait_filled(c, ws + blk_slots(wb), 0x1300u | l)) return;
                 const bool hb = a.has_bias;
-                const uint32_t tg = tag_of(l, PH_QKV);
-                block_dots<16>(ws, q.n, D * 2, xin, ct, [&](int row, float s) {
+                block_rows<2, 4>(ws, q.n, D * 2, x, wave, lno, [&](int row, float s) {
                     float v = r * s;
                     if (hb) v += bf16_to_f32(*(const uint16_t*)(g_sm.ring + ring_off(bs, (uint32_t)(boff + 2 * row))));
                     st_near(out + q.out0 + row, pack(v, tg));
                 });
             }
             release(c, wave, cur);
-            vb ^= 1;
         }
         // ------------------------------------------------------------ P1: attention over split s
-        // (head_dim 64: lane d of a wave holds dimension d)
         if (grp && S.slot < a.S) {
             const int s = S.slot;
             uint32_t qns = 0, kns = 0;
@@ -520,12 +645,13 @@ __device__ __forceinline__ void compute(const StepArgs& a, const Sched& S, Ctl& 
                 qns = take(cur, get_block(a, S, l, PH_ATTN, 0));
                 kns = take(cur, get_block(a, S, l, PH_ATTN, 1));
             }
-            // the split's K pages, then its V pages: 2 slots (16 rows of 128 bytes) each
+            // the split's K pages, then its V pages: 2 slots (16 rows of 128 bytes) each,
+            // so 8 keys fill one slot
             const uint32_t kp0 = cur;
             cur += 2 * S.npg;
             const uint32_t vp0 = cur;
             cur += 2 * S.npg;
-            float* qv = g_sm.vin[vb];   // q heads of group g, then k, then v
+            float* qv = g_sm.work;   // q heads of group g, then k, then v
             const u64* qkvb = a.qkv + (size_t)par * a.qkvr;
             const int qn = G * 64;
             const uint32_t tg = tag_of(l, PH_QKV);
@@ -538,15 +664,17 @@ __device__ __forceinline__ void compute(const StepArgs& a, const Sched& S, Ctl& 
             if (!cw_barrier(c, 0x2200u | l)) return;
             // ring position of row t's bytes of page block `p0` (rows 0-7 in its first slot)
             auto row_off = [&](uint32_t p0, int t) {
-                const int pi = t / 16 - S.pg0, r = t % 16;
-                return ring_off(p0 + 2 * pi + (r >> 3), (uint32_t)((r & 7) * 128));
+                const int pi = t / 16 - S.pg0, rr = t % 16;
+                return ring_off(p0 + 2 * pi + (rr >> 3), (uint32_t)((rr & 7) * 128));
             };
             // vectors 0..G-1 (q heads) and G (k): per-head RMSNorm with the shared gains,
-            // then the half-split rotation (element i pairs with i + 32); the new k and v,
-            // rounded to bf16, go to the cache and into the ring rows of position p
+            // then the half-split rotation (element i pairs with i + 32). q, scaled by
+            // 1/sqrt(hd) log2(e) so scores come out in base 2, goes to the split input
+            // (head h at word 32 h); the new k and v, rounded to bf16, go to the cache and
+            // into the ring rows of position p.
+            const float qscale = a.scale * 1.4426950408889634f;
             for (int v = wave; v <= G; v += kNcw) {
-                float* vec = qv + v * 64;
-                float e0 = vec[lane];
+                float e0 = qv[v * 64 + lane];
                 if (a.qk_norm) {
                     const float ss = group_sum<64>(e0 * e0);
                     const float rr = 1.0f / sqrtf(ss / 64.0f + a.eps);
@@ -556,191 +684,212 @@ __device__ __forceinline__ void compute(const StepArgs& a, const Sched& S, Ctl& 
                 const float2 cs = g_sm.rope[lane & 31];
                 const float o0 = lane < 32 ? e0 * cs.x - partner * cs.y : e0 * cs.x + partner * cs.y;
                 if (v < G) {
-                    vec[lane] = o0;
+                    const float qs = o0 * qscale;
+                    const float nb = dpp_f<kDppQuadXor1>(qs);   // element lane ^ 1
+                    if ((lane & 1) == 0) {
+                        uint32_t hi, lo;
+                        split2(qs, nb, hi, lo);
+                        g_sm.xs_h[v * 32 + (lane >> 1)] = hi;
+                        g_sm.xs_l[v * 32 + (lane >> 1)] = lo;
+                    }
                 } else if (p / a.C == s) {   // the split holding p appends the new K/V
                     const uint16_t kb = f32_to_bf16(o0), vb16 = f32_to_bf16(qv[qn + 64 + lane]);
                     *(uint16_t*)(g_sm.ring + row_off(kp0, p) + 2 * lane) = kb;
                     *(uint16_t*)(g_sm.ring + row_off(vp0, p) + 2 * lane) = vb16;
-                    const int pid = a.block_table[p / 16];
-                    if (pid >= 0 && pid < a.num_pages) {
-                        const long off = (((long)pid * a.Hkv + g) * 16 + (p % 16)) * 64;
-                        ((uint16_t*)L.kc)[off + lane] = kb;
-                        ((uint16_t*)L.vc)[off + lane] = vb16;
-                    }
+                    app = (uint32_t)kb | ((uint32_t)vb16 << 16);   // stored to the cache in P3
+                    has_app = true;
                 }
             }
             if (!cw_barrier(c, 0x2400u | l)) return;
-            // scores (base 2), softmax and P.V; wave w takes heads w and w + 4 together
-            const int t0 = s * a.C, t1 = min(t0 + a.C, p + 1);
-            const float scl = a.scale * 1.4426950408889634f;
-            u64* part = a.part + (size_t)par * a.part_stride + ((size_t)g * a.S + s) * G * 66;
-            const uint32_t ta = tag_of(l, PH_ATTN);
-            const int hA = wave, hB = wave + kNcw;
-            const bool has_b = hB < G;
-            if (hA < G) {
-                constexpr int KPL = 4;   // keys per lane (C <= 256)
-                float sa[KPL], sb[KPL];
-                float ma = -INFINITY, mb = -INFINITY;
-                const float* qa = qv + hA * 64;
-                const float* qb = qv + (has_b ? hB : hA) * 64;
+            const int t0 = s * a.C, nk = min(a.C, p + 1 - t0), ngr = (nk + 7) >> 3;
+            float* sc = g_sm.work + kScOff;
+            // scores: key group i (8 keys, one ring slot) to wave i % 4; lane (key kk,
+            // chunk cc) takes 16 bytes of key kk's row and chunk cc of every q head
+            {
+                const int lno = opaque(lane);
+                const int kk = lno >> 3, cc = lno & 7;
+                for (int gi = wave; gi < ngr; gi += kNcw) {
+                    const uint4 kv = *(const uint4*)(g_sm.ring + ring_off(kp0 + gi, (uint32_t)lno * 16u));
+                    float mine = 0.f;
 #pragma unroll
-                for (int i = 0; i < KPL; ++i) {
-                    sa[i] = -INFINITY;
-                    sb[i] = -INFINITY;
-                    if (i * 64 < a.C) {
-                        const int t = t0 + lane + 64 * i;
-                        const bool ok = t < t1;
-                        const uint8_t* kr = g_sm.ring + row_off(kp0, ok ? t : t0);
-                        float acc_a = 0.f, acc_b = 0.f;
-#pragma unroll
-                        for (int d8 = 0; d8 < 64; d8 += 8) {
-                            float f[8];
-                            widen16(*(const uint4*)(kr + d8 * 2), f);
-                            const float4 a0 = *(const float4*)(qa + d8), a1 = *(const float4*)(qa + d8 + 4);
-                            const float4 b0 = *(const float4*)(qb + d8), b1 = *(const float4*)(qb + d8 + 4);
-                            acc_a += f[0] * a0.x + f[1] * a0.y + f[2] * a0.z + f[3] * a0.w + f[4] * a1.x + f[5] * a1.y +
-                                     f[6] * a1.z + f[7] * a1.w;
-                            acc_b += f[0] * b0.x + f[1] * b0.y + f[2] * b0.z + f[3] * b0.w + f[4] * b1.x + f[5] * b1.y +
-                                     f[6] * b1.z + f[7] * b1.w;
-                        }
-                        if (ok) {
-                            sa[i] = acc_a * scl;
-                            sb[i] = acc_b * scl;
-                            ma = fmaxf(ma, sa[i]);
-                            mb = fmaxf(mb, sb[i]);
+                    for (int h = 0; h < 8; ++h) {
+                        if (h < G) {
+                            const uint4 qh = *(const uint4*)&g_sm.xs_h[h * 32 + cc * 4];
+                            const uint4 ql = *(const uint4*)&g_sm.xs_l[h * 32 + cc * 4];
+                            const float sh = group_sum<8>(dot_chunk(kv, qh, ql, 0.f));
+                            mine = cc == h ? sh : mine;
                         }
                     }
-                }
-                ma = wave_max(ma);
-                mb = wave_max(mb);
-                float la = 0.f, lb = 0.f;
-#pragma unroll
-                for (int i = 0; i < KPL; ++i) {
-                    sa[i] = sa[i] == -INFINITY ? 0.f : exp2f(sa[i] - ma);
-                    sb[i] = sb[i] == -INFINITY ? 0.f : exp2f(sb[i] - mb);
-                    la += sa[i];
-                    lb += sb[i];
-                }
-                la = group_sum<64>(la);
-                lb = group_sum<64>(lb);
-                // o[d] = sum_t p_t V_t[d], a page (16 keys) at a time; the 16 keys of a page
-                // sit in lanes ln0 .. ln0 + 15 of key group i
-                float oa = 0.f, ob = 0.f;
-                for (int pi = 0; pi < S.npg; ++pi) {
-                    const int tp = (S.pg0 + pi) * 16, rel = tp - t0;
-                    const int i = rel >> 6, ln0 = rel & 63;
-                    const float pa = i == 0 ? sa[0] : i == 1 ? sa[1] : i == 2 ? sa[2] : sa[3];
-                    const float pb = i == 0 ? sb[0] : i == 1 ? sb[1] : i == 2 ? sb[2] : sb[3];
-                    const uint32_t v0 = ring_off(vp0 + 2 * pi, (uint32_t)(2 * lane));
-                    const uint32_t v1 = ring_off(vp0 + 2 * pi + 1, (uint32_t)(2 * lane));
-                    const int nk = min(16, t1 - tp);
-                    if (nk == 16) {
-                        float vv[16];
-#pragma unroll
-                        for (int k = 0; k < 16; ++k)
-                            vv[k] = bf16_to_f32(*(const uint16_t*)(g_sm.ring + (k < 8 ? v0 : v1) + (k & 7) * 128));
-#pragma unroll
-                        for (int k = 0; k < 16; ++k) {
-                            oa += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pa), ln0 + k)) * vv[k];
-                            ob += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pb), ln0 + k)) * vv[k];
-                        }
-                    } else {
-                        for (int k = 0; k < nk; ++k) {
-                            const float vk = bf16_to_f32(*(const uint16_t*)(g_sm.ring + (k < 8 ? v0 : v1) + (k & 7) * 128));
-                            oa += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pa), ln0 + k)) * vk;
-                            ob += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pb), ln0 + k)) * vk;
-                        }
-                    }
-                }
-                u64* pa_out = part + (size_t)hA * 66;
-                st_near(pa_out + lane, pack(oa, ta));
-                if (lane == 0) {
-                    st_near(pa_out + 64, pack(ma, ta));
-                    st_near(pa_out + 65, pack(la, ta));
-                }
-                if (has_b) {
-                    u64* pb_out = part + (size_t)hB * 66;
-                    st_near(pb_out + lane, pack(ob, ta));
-                    if (lane == 0) {
-                        st_near(pb_out + 64, pack(mb, ta));
-                        st_near(pb_out + 65, pack(lb, ta));
-                    }
+                    const int t = gi * 8 + kk;
+                    if (cc < G) sc[cc * 256 + t] = t < nk ? mine : -INFINITY;
                 }
             }
+            if (!cw_barrier(c, 0x2500u | l)) return;
+            // softmax of head h (wave h % 4): max, 2^(s - max) in place, sum
+            for (int h = wave; h < G; h += kNcw) {
+                float* sr = sc + h * 256;
+                float v4[4];
+                float m = -INFINITY;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = lane + 64 * i;
+                    v4[i] = t < nk ? sr[t] : -INFINITY;
+                    m = fmaxf(m, v4[i]);
+                }
+                m = wave_max(m);
+                float ls = 0.f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = lane + 64 * i;
+                    const float pe = t < nk ? exp2f(v4[i] - m) : 0.f;
+                    if (t < ngr * 8) sr[t] = pe;
+                    ls += pe;
+                }
+                ls = group_sum<64>(ls);
+                if (lane == 0) {
+                    g_sm.wts[2 * h] = m;
+                    g_sm.wts[2 * h + 1] = ls;
+                }
+            }
+            if (!cw_barrier(c, 0x2600u | l)) return;
+            // P.V: lane (head hh, chunk cc) sums its 8 output dimensions over the key
+            // groups of its wave
+            {
+                const int lno = opaque(lane);
+                const int hh = lno >> 3, cc = lno & 7;
+                float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+                if (hh < G) {
+                    for (int gi = wave; gi < ngr; gi += kNcw) {
+                        const float4 p0 = *(const float4*)&sc[hh * 256 + gi * 8];
+                        const float4 p1 = *(const float4*)&sc[hh * 256 + gi * 8 + 4];
+                        const float pk[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+                        const uint32_t vb = ring_off(vp0 + gi, (uint32_t)cc * 16u);
+                        uint4 vv[8];
+#pragma unroll
+                        for (int k = 0; k < 8; ++k) vv[k] = *(const uint4*)(g_sm.ring + vb + k * 128);
+#pragma unroll
+                        for (int k = 0; k < 8; ++k) {
+                            float f[8];
+                            widen16(vv[k], f);
+#pragma unroll
+                            for (int j = 0; j < 8; ++j) o[j] += pk[k] * f[j];
+                        }
+                    }
+                    float* pv = g_sm.work + kPvOff + wave * 512 + hh * 64 + cc * 8;
+                    *(float4*)pv = make_float4(o[0], o[1], o[2], o[3]);
+                    *(float4*)(pv + 4) = make_float4(o[4], o[5], o[6], o[7]);
+                }
+            }
+            if (!cw_barrier(c, 0x2700u | l)) return;
+            // the split's partial of head h: the sum over the waves (fixed order), then
+            // its max and sum of exponentials
+            u64* part = a.part + (size_t)par * a.part_stride + ((size_t)g * a.S + s) * G * 66;
+            const uint32_t ta = tag_of(l, PH_ATTN);
+            for (int e = ct; e < G * 64; e += 256) {
+                const float* pv = g_sm.work + kPvOff + e;
+                const float sum = ((pv[0] + pv[512]) + pv[1024]) + pv[1536];
+                st_near(part + (e >> 6) * 66 + (e & 63), pack(sum, ta));
+            }
+            if (ct < G) {
+                st_near(part + ct * 66 + 64, pack(g_sm.wts[2 * ct], ta));
+                st_near(part + ct * 66 + 65, pack(g_sm.wts[2 * ct + 1], ta));
+            }
             release(c, wave, cur);
-            vb ^= 1;
+            if (!cw_barrier(c, 0x2800u | l)) return;   // the work buffer is free again
         }
         // ------------------------------------------------------------ P2: split merge, o_proj (group columns)
         if (grp) {
             const Blk ob = get_block(a, S, l, PH_O, 0);
             const uint32_t os = take(cur, ob);
-            float* pin = g_sm.vin[vb];
+            float* pin = g_sm.work;
             const int stride_s = G * (hd + 2);
             const u64* part = a.part + (size_t)par * a.part_stride + (size_t)g * a.S * stride_s;
             if (!poll_vec<20, false>(c, part, a.S * stride_s, tag_of(l, PH_ATTN), pin, nullptr, nullptr, ct,
                                      0x3100u | l)) return;
             if (!cw_barrier(c, 0x3200u | l)) return;
-            // ctx[h][d] = sum_s 2^(m_s - M) o_s[d] / sum_s 2^(m_s - M) l_s
-            float* ctx = g_sm.xa;
-            for (int e = ct; e < G * hd; e += 256) {
-                const int h = e / hd, d = e % hd;
-                float M = -INFINITY;
-                for (int s = 0; s < a.S; ++s) M = fmaxf(M, pin[s * stride_s + h * (hd + 2) + hd]);
-                float lt = 0.f, ot = 0.f;
-                for (int s = 0; s < a.S; ++s) {
-                    const float* ps = pin + s * stride_s + h * (hd + 2);
-                    const float w = ps[hd] == -INFINITY ? 0.f : exp2f(ps[hd] - M);
-                    lt += w * ps[hd + 1];
-                    ot += w * ps[d];
-                }
-                ctx[e] = ot / lt;
+            // weight of split s for head h: 2^(m_s - M) / sum_s 2^(m_s - M) l_s
+            for (int h = wave; h < G; h += kNcw) {
+                const bool on = lane < a.S;
+                const float ms = on ? pin[lane * stride_s + h * (hd + 2) + hd] : -INFINITY;
+                const float M = wave_max(ms);
+                const float w = on ? exp2f(ms - M) : 0.f;
+                const float lt = group_sum<64>(on ? w * pin[lane * stride_s + h * (hd + 2) + hd + 1] : 0.f);
+                if (on) g_sm.wts[h * 32 + lane] = w / lt;
             }
-            if (!wait_filled(c, os + blk_slots(ob), 0x3300u | l)) return;
-            if (!cw_barrier(c, 0x3400u | l)) return;
+            if (!cw_barrier(c, 0x3300u | l)) return;
+            // ctx[h][d] = sum_s w[h][s] o_s[h][d], two elements per thread, into the split input
+            for (int e2 = ct; e2 < G * 32; e2 += 256) {
+                const int h = e2 >> 5, d = 2 * (e2 & 31);
+                float c0 = 0.f, c1 = 0.f;
+                const float* ps = pin + h * (hd + 2) + d;
+                for (int s = 0; s < a.S; ++s) {
+                    const float w = g_sm.wts[h * 32 + s];
+                    const float2 o2 = *(const float2*)(ps + s * stride_s);
+                    c0 += w * o2.x;
+                    c1 += w * o2.y;
+                }
+                uint32_t hi, lo;
+                split2(c0, c1, hi, lo);
+                g_sm.xs_h[e2] = hi;
+                g_sm.xs_l[e2] = lo;
+            }
+            if (!wait_filled(c, os + blk_slots(ob), 0x3400u | l)) return;
+            if (!cw_barrier(c, 0x3500u | l)) return;
+            const int lno = opaque(lane);
+            XW<1> x;
+            load_xw<1>(x, lno, G * 8);
             const int r0 = S.slot * D / kSlotsPerXcd;
             float* y = a.y + ((size_t)par * a.Hkv + g) * D + r0;
-            block_dots<16>(os, ob.rows, ob.seg, ctx, ct, [&](int row, float v) { st_farf(y + row, v); });
+            block_rows<1, 4>(os, ob.rows, ob.seg, x, wave, lno, [&](int row, float v) { st_farf(y + row, v); });
             release(c, wave, cur);
-            if (!publish(c, CNT_Y, l, S.xcd, wave, 0x3500u | l)) return;
-            vb ^= 1;
+            if (!publish(c, CNT_Y, l, S.xcd, wave, 0x3600u | l)) return;
         }
         // ------------------------------------------------------------ P3: x_a, RMSNorm, gate|up, SwiGLU
         {
             const Blk gb = get_block(a, S, l, PH_UP, 0);
             const uint32_t gs = take(cur, gb);
-            float* xin = g_sm.vin[vb];
             if (!wait_filled(c, gs + blk_slots(gb), 0x4120u | l)) return;
             // x of the previous layer (all XCDs) and y_g of this one (XCDs < Hkv)
             if (wave == 0 && !wait_counts(c, CNT_X, l - 1, kXcd, l > 0 ? kSlotsPerXcd : 0, l > 0 ? kSlotsPerXcd : 0,
                                           CNT_Y, l, a.Hkv, kSlotsPerXcd, 0, 0x4100u | l)) return;
             if (!cw_barrier(c, 0x4200u | l)) return;
-            // x_a = x + sum_g y_g (fixed order) into xa; x_a * g_mlp into xin; the sum of squares
+            // x_a = x + sum_g y_g (fixed order) into xa; x_a * g_mlp into the split input
             {
                 float ss = 0.f;
                 const float* xs = XB + (size_t)ppar * D;
                 const float* ys = a.y + (size_t)par * a.Hkv * D;
                 for (int q = ct; q < D / 4; q += 256) {
-                    const float4 xv = ld_far16(xs, q);
-                    float f[4] = {xv.x, xv.y, xv.z, xv.w};
+                    float4 v = ld_far16(xs, q);
                     for (int gg = 0; gg < a.Hkv; ++gg) {
                         const float4 yv = ld_far16(ys + (size_t)gg * D, q);
-                        f[0] += yv.x; f[1] += yv.y; f[2] += yv.z; f[3] += yv.w;
+                        v.x += yv.x; v.y += yv.y; v.z += yv.z; v.w += yv.w;
                     }
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        ss += f[e] * f[e];
-                        g_sm.xa[4 * q + e] = f[e];
-                        xin[4 * q + e] = f[e] * ring_bf16(gs, 4 * q + e);
-                    }
+                    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+                    *(float4*)&g_sm.xa[4 * q] = v;
+                    const uint2 gw = *(const uint2*)(g_sm.ring + ring_off(gs, (uint32_t)(8 * q)));
+                    xs_store4(q, make_float4(v.x * bf16_to_f32(gw.x & 0xffffu), v.y * bf16_to_f32(gw.x >> 16),
+                                             v.z * bf16_to_f32(gw.y & 0xffffu), v.w * bf16_to_f32(gw.y >> 16)));
                 }
-                ss_publish(g_sm.ssp[vb], wave, ss);
+                ss_publish(g_sm.ssp, wave, ss);
+            }
+            if (has_app) {
+                if (S.pid_p >= 0) {
+                    const long off = (((long)S.pid_p * a.Hkv + g) * 16 + (p % 16)) * 64;
+                    ((uint16_t*)L.kc)[off + lane] = (uint16_t)(app & 0xffffu);
+                    ((uint16_t*)L.vc)[off + lane] = (uint16_t)(app >> 16);
+                }
+                has_app = false;
             }
             if (!cw_barrier(c, 0x4300u | l)) return;
-            const float r = ss_scale(g_sm.ssp[vb], D, a.eps);
-            int f0, f1;
-            weighted_range(S.wg, F, a.Hkv, a.up_wa, a.up_wb, &f0, &f1);
-            const int nblk = (f1 - f0 + kP3Rows - 1) / kP3Rows;
+            const float r = ss_scale(g_sm.ssp, D, a.eps);
+            const int lno = opaque(lane);
+            XW<2> x;
+            load_xw<2>(x, lno, D >> 3);
+            const int nblk = (S.f1 - S.f0 + kP3Rows - 1) / kP3Rows;
             float* hout = a.h + (size_t)par * F;
+            // block pair k (8 gate rows, then the same 8 up rows): wave w takes rows 2 w
+            // and 2 w + 1 of both
+            const int row = 2 * wave;
             for (int k = 0; k < nblk; ++k) {
                 const Blk bg = get_block(a, S, l, PH_UP, 1 + 2 * k);
                 const uint32_t sg = take(cur, bg);
@@ -748,56 +897,58 @@ __device__ __forceinline__ void compute(const StepArgs& a, const Sched& S, Ctl& 
                 const uint32_t su = take(cur, bu);
                 if (!wait_filled(c, su + blk_slots(bu), 0x4500u | l)) return;
                 const int n = bg.seg / (D * 2);
-                // 16 lanes per row; wave w, lane group q: row 2w + (q & 1) of gate (q < 2) or up (q >= 2)
-                const int q = lane >> 4, row = 2 * wave + (q & 1), isup = q >> 1, lr = lane & 15;
-                float acc = 0.f;
-                if (row < n) {
-                    const uint32_t s0 = isup ? su : sg;
-                    for (int ch = lr; ch < D / 8; ch += 16) {
-                        const uint4 wv = *(const uint4*)(g_sm.ring + ring_off(s0, (uint32_t)(row * D * 2 + ch * 16)));
-                        const float4 x0 = *(const float4*)(xin + ch * 8), x1 = *(const float4*)(xin + ch * 8 + 4);
-                        float f[8];
-                        widen16(wv, f);
-                        acc += f[0] * x0.x + f[1] * x0.y + f[2] * x0.z + f[3] * x0.w + f[4] * x1.x + f[5] * x1.y +
-                               f[6] * x1.z + f[7] * x1.w;
-                    }
+                const uint32_t rb[4] = {ring_at(sg, (uint32_t)(row * D * 2)), ring_at(sg, (uint32_t)((row + 1) * D * 2)),
+                                        ring_at(su, (uint32_t)(row * D * 2)), ring_at(su, (uint32_t)((row + 1) * D * 2))};
+                const uint32_t m2 = row + 1 < n ? 3u : row < n ? 1u : 0u;
+                float o[4];
+                rows_dot<2, 4>(rb, m2 | (m2 << 2), lno, D >> 3, x, o);
+                if (lno == 0) {
+                    if (row < n) st_farf(hout + S.f0 + k * kP3Rows + row, silu(r * o[0]) * (r * o[2]));
+                    if (row + 1 < n) st_farf(hout + S.f0 + k * kP3Rows + row + 1, silu(r * o[1]) * (r * o[3]));
                 }
-                acc = group_sum<16>(acc);
-                // the up sum of a row sits 32 lanes above its gate sum
-                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(acc), __float_as_int(acc), false, false);
-                const float upv = __int_as_float(sw[1]);
-                if (lr == 0 && !isup && row < n)
-                    st_farf(hout + f0 + k * kP3Rows + row, silu(r * acc) * (r * upv));
                 release(c, wave, cur);
             }
             release(c, wave, cur);
             if (!publish(c, CNT_H, l, S.xcd, wave, 0x4600u | l)) return;
-            vb ^= 1;
         }
         // ------------------------------------------------------------ P4: down + residual
         {
             const Blk db = get_block(a, S, l, PH_DOWN, 0);
             const uint32_t ds = take(cur, db);
-            float* hin = g_sm.vin[vb];
             if (wave == 0 && !wait_counts(c, CNT_H, l, kXcd, kSlotsPerXcd, kSlotsPerXcd, -1, 0, 0, 0, 0, 0x5100u | l))
                 return;
             if (!cw_barrier(c, 0x5150u | l)) return;
-            load_far<5>(a.h + (size_t)par * F, F, hin, -1, nullptr, ct);
+            {
+                const float* hs = a.h + (size_t)par * F;
+                float4 v[5];
+#pragma unroll
+                for (int i = 0; i < 5; ++i) {
+                    const int q = ct + 256 * i;
+                    v[i] = ld_far16(hs, q < F / 4 ? q : 0);
+                }
+#pragma unroll
+                for (int i = 0; i < 5; ++i) {
+                    const int q = ct + 256 * i;
+                    if (q < F / 4) xs_store4(q, v[i]);
+                }
+            }
             if (!wait_filled(c, ds + blk_slots(db), 0x5200u | l)) return;
             if (!cw_barrier(c, 0x5300u | l)) return;
-            int d0, d1;
-            weighted_range(S.wg, D, a.Hkv, a.down_wa, a.down_wb, &d0, &d1);
-            float* xo = XB + (size_t)par * D + d0;
+            const int lno = opaque(lane);
+            float* xo = XB + (size_t)par * D + S.d0;
             const bool last = l == a.L - 1;
-            block_dots<64>(ds, d1 - d0, F * 2, hin, ct, [&](int row, float v) {
-                const float xn = g_sm.xa[d0 + row] + v;
-                st_farf(xo + row, xn);
-                if (a.layer_out) a.layer_out[(size_t)l * D + d0 + row] = xn;
-                if (last && a.x_out) a.x_out[d0 + row] = xn;
-            });
+            const int d0 = S.d0;
+            for (int row = wave; row < S.d1 - S.d0; row += kNcw) {
+                const float v = row_dot_lds<5>(ring_at(ds, (uint32_t)(row * F * 2)), lno, F >> 3);
+                if (lno == 0) {
+                    const float xn = g_sm.xa[d0 + row] + v;
+                    st_farf(xo + row, xn);
+                    if (a.layer_out) a.layer_out[(size_t)l * D + d0 + row] = xn;
+                    if (last && a.x_out) a.x_out[d0 + row] = xn;
+                }
+            }
             release(c, wave, cur);
             if (!publish(c, CNT_X, l, S.xcd, wave, 0x5500u | l)) return;
-            vb ^= 1;
         }
     }
     // ---------------------------------------------------------------- final norm, lm_head, argmax partials
@@ -805,26 +956,25 @@ __device__ __forceinline__ void compute(const StepArgs& a, const Sched& S, Ctl& 
         const int nb = n_blocks(a, S, PH_HEAD);
         const Blk gb = get_block(a, S, 0, PH_HEAD, 0);
         const uint32_t gs = take(cur, gb);
-        float* xin = g_sm.vin[vb];
         if (!wait_filled(c, gs + blk_slots(gb), 0x6000u)) return;
-        float ss = 0.f;
         const int lp = (a.L - 1) & 1;
         if (wave == 0 && !wait_counts(c, CNT_X, a.L - 1, kXcd, kSlotsPerXcd, kSlotsPerXcd, -1, 0, 0, 0, 0, 0x6050u))
             return;
         if (!cw_barrier(c, 0x6060u)) return;
-        load_far<1>(XB + (size_t)lp * D, D, xin, (int)gs, &ss, ct);
-        ss_publish(g_sm.ssp[vb], wave, ss);
+        ss_publish(g_sm.ssp, wave, load_norm_input(XB + (size_t)lp * D, D, gs, ct));
         if (!cw_barrier(c, 0x6200u)) return;
-        const float r = ss_scale(g_sm.ssp[vb], D, a.eps);
-        const int v0 = (int)((long)a.V * S.wg / kWgs);
+        const float r = ss_scale(g_sm.ssp, D, a.eps);
+        const int lno = opaque(lane);
+        XW<2> x;
+        load_xw<2>(x, lno, D >> 3);
         float bv = -INFINITY;
         int bi = 0x7fffffff;
         for (int k = 1; k < nb; ++k) {
             const Blk b = get_block(a, S, 0, PH_HEAD, k);
             const uint32_t s0 = take(cur, b);
             if (!wait_filled(c, s0 + blk_slots(b), 0x6300u)) return;
-            const int rbase = v0 + (k - 1) * kLmRows;
-            block_dots<16>(s0, b.seg / (D * 2), D * 2, xin, ct, [&](int row, float v) {
+            const int rbase = S.v0 + (k - 1) * kLmRows;
+            block_rows<2, 4>(s0, b.seg / (D * 2), D * 2, x, wave, lno, [&](int row, float v) {
                 const float lg = r * v;
                 a.logits[rbase + row] = lg;
                 if (better(lg, rbase + row, bv, bi)) { bv = lg; bi = rbase + row; }
@@ -852,6 +1002,7 @@ __global__ __launch_bounds__(kThreads) void step_kernel(StepArgs a) {
     S.wg = wg;
     S.xcd = wg % kXcd;
     S.slot = wg / kXcd;
+    init_rows(a, S);
     Ctl c{&a, 0};
     if (threadIdx.x == 0) {
         g_sm.filled = 0;
@@ -865,7 +1016,14 @@ __global__ __launch_bounds__(kThreads) void step_kernel(StepArgs a) {
     S.pg0 = 0;
     S.npg = 0;
     bool bad = p < 0 || p + 1 > a.S * a.C || p / 16 >= a.max_blocks;
-    if (!bad && S.xcd < a.Hkv && S.slot < a.S) split_pages(S.slot, a.C, p, &S.pg0, &S.npg);
+    S.pid_p = -1;
+    if (!bad && S.xcd < a.Hkv && S.slot < a.S) {
+        split_pages(S.slot, a.C, p, &S.pg0, &S.npg);
+        if (p / a.C == S.slot) {   // the page of the new token's K/V (read once per step)
+            const int pid = a.block_table[p / 16];
+            S.pid_p = pid >= 0 && pid < a.num_pages ? pid : -1;
+        }
+    }
     if (hw_xcc_id() != (uint32_t)S.xcd) bad = true;   // the XCD layout the schedule assumes
     if (bad) {
         if (threadIdx.x == 0) {
@@ -912,8 +1070,6 @@ __global__ __launch_bounds__(256) void step_prologue_kernel(StepArgs a, const in
 }
 
 }  // namespace
-
-int step_max_vin() { return kVin; }
 
 hipError_t launch_step_prologue(const StepArgs& a, const int* tokens, const void* embed, const float* x_in,
                                 float theta, hipStream_t s) {

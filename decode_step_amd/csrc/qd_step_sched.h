@@ -25,7 +25,8 @@ constexpr int kSlotsPerXcd = kWgs / kXcd;
 constexpr int kNcw = 4;                  // compute waves
 constexpr int kThreads = 64 * (1 + kNcw);
 constexpr int kRingSlots = 112;          // 1 KB LDS slots
-constexpr int kVin = 5120;               // floats per input buffer (two of them)
+constexpr int kWork = 5120;              // floats of the workgroup's work buffer
+constexpr int kXs = 2560;                // words of each half of the split product input (2 elements each)
 constexpr int kMaxOut = 56;              // DMA instructions the loader keeps in flight
 constexpr int kBatch = 8;                // DMAs the loader issues between two progress updates
 constexpr uint32_t kSpinMax = 1u << 21;  // polls before a wait gives up
@@ -64,7 +65,20 @@ struct Sched {
     int wg, xcd, slot;      // slot: rank among the XCD's workgroups
     int p;                  // position of the new token
     int pg0, npg;           // attention: first page index of the split and page count
+    int f0, f1;             // gate|up rows of the workgroup
+    int d0, d1;             // down rows
+    int v0, v1;             // lm_head rows
+    int pid_p;              // page of the new token (its attention split only; -1 elsewhere)
 };
+
+// The workgroup's row ranges, fixed for the whole step (computed once: the
+// 64-bit divisions of weighted_range are long instruction sequences).
+QD_HD inline void init_rows(const StepArgs& a, Sched& S) {
+    weighted_range(S.wg, a.F, a.Hkv, a.up_wa, a.up_wb, &S.f0, &S.f1);
+    weighted_range(S.wg, a.D, a.Hkv, a.down_wa, a.down_wb, &S.d0, &S.d1);
+    S.v0 = (int)((long)a.V * S.wg / kWgs);
+    S.v1 = (int)((long)a.V * (S.wg + 1) / kWgs);
+}
 
 // P0: group rows [gr0, gr1) of slot j out of group g's (G + 2) hd rows (q heads,
 // then k, then v), as up to three sub-ranges of wq, wk, wv
@@ -128,17 +142,9 @@ QD_HD inline int n_blocks(const StepArgs& a, const Sched& S, int ph) {
     }
     case PH_ATTN: return (grp && S.slot < a.S) ? (a.qk_norm ? 2 : 0) + 2 * S.npg : 0;
     case PH_O: return grp ? 1 : 0;
-    case PH_UP: {
-        int f0, f1;
-        weighted_range(S.wg, a.F, a.Hkv, a.up_wa, a.up_wb, &f0, &f1);
-        return 1 + 2 * ((f1 - f0 + kP3Rows - 1) / kP3Rows);
-    }
+    case PH_UP: return 1 + 2 * ((S.f1 - S.f0 + kP3Rows - 1) / kP3Rows);
     case PH_DOWN: return 1;
-    default: {
-        if (!a.lm_head) return 0;
-        const int v0 = (int)((long)a.V * S.wg / kWgs), v1 = (int)((long)a.V * (S.wg + 1) / kWgs);
-        return 1 + (v1 - v0 + kLmRows - 1) / kLmRows;
-    }
+    default: return a.lm_head ? 1 + (S.v1 - S.v0 + kLmRows - 1) / kLmRows : 0;
     }
 }
 
@@ -163,21 +169,14 @@ QD_HD inline Blk get_block(const StepArgs& a, const Sched& S, int l, int ph, int
     }
     case PH_UP: {
         if (k == 0) return Blk{(const char*)L.mlp_norm, 1, D * 2, 0};
-        int f0, f1;
-        weighted_range(S.wg, a.F, a.Hkv, a.up_wa, a.up_wb, &f0, &f1);
         const int blk = (k - 1) >> 1, up = (k - 1) & 1;
-        const int r0 = f0 + blk * kP3Rows, n = qd_min(kP3Rows, f1 - r0);
+        const int r0 = S.f0 + blk * kP3Rows, n = qd_min(kP3Rows, S.f1 - r0);
         return Blk{(const char*)(up ? L.w_up : L.w_gate) + (long)r0 * D * 2, 1, n * D * 2, 0};
     }
-    case PH_DOWN: {
-        int d0, d1;
-        weighted_range(S.wg, D, a.Hkv, a.down_wa, a.down_wb, &d0, &d1);
-        return Blk{(const char*)L.w_down + (long)d0 * a.F * 2, 1, (d1 - d0) * a.F * 2, 0};
-    }
+    case PH_DOWN: return Blk{(const char*)L.w_down + (long)S.d0 * a.F * 2, 1, (S.d1 - S.d0) * a.F * 2, 0};
     default: {
         if (k == 0) return Blk{(const char*)a.final_norm, 1, D * 2, 0};
-        const int v0 = (int)((long)a.V * S.wg / kWgs), v1 = (int)((long)a.V * (S.wg + 1) / kWgs);
-        const int r0 = v0 + (k - 1) * kLmRows, n = qd_min(kLmRows, v1 - r0);
+        const int r0 = S.v0 + (k - 1) * kLmRows, n = qd_min(kLmRows, S.v1 - r0);
         return Blk{(const char*)a.lm_head + (long)r0 * D * 2, 1, n * D * 2, 0};
     }
     }
@@ -219,13 +218,13 @@ struct StepPlan {
 };
 inline int step_split_cap(const qd_config* c) {
     const int G = c->n_q_heads / c->n_kv_heads;
-    return qd_min(32, kVin / (G * (c->head_dim + 2)));
+    return qd_min(32, kWork / (G * (c->head_dim + 2)));
 }
 inline bool step_config_ok(const qd_config* c) {
     const int G = c->n_q_heads / c->n_kv_heads, D = c->hidden, F = c->ffn;
     return c->w_dtype == QD_BF16 && c->kv_dtype == QD_BF16 && c->head_dim == 64 && c->n_kv_heads <= 8 &&
-           G <= 8 && c->n_kv_heads * D <= 2048 && c->n_layers <= kStepMaxLayers && D <= 1024 && (c->n_kv_heads + 1) * D <= kVin &&
-           F <= kVin && G * c->head_dim <= 1024 && step_split_cap(c) >= 1 &&
+           G <= 8 && c->n_kv_heads * D <= 2048 && c->n_layers <= kStepMaxLayers && D <= 1024 && D % 8 == 0 &&
+           F <= 2 * kXs && F % 8 == 0 && G * c->head_dim <= 512 && step_split_cap(c) >= 1 &&
            (long)((D + 255) / 256) * F * 2 <= 96 * 1024;   // a workgroup's down rows fit the ring
 }
 inline StepPlan plan_step(const qd_config* c, int tokens) {

@@ -147,6 +147,7 @@ void run_case(int L, int D, int Hq, int Hkv, int F, int V, int p, bool bias, boo
     for (int wg = 0; wg < kWgs; ++wg) {
         Sched S{};
         S.wg = wg; S.xcd = wg % kXcd; S.slot = wg / kXcd; S.p = p;
+        init_rows(a, S);
         if (S.xcd < a.Hkv && S.slot < a.S) split_pages(S.slot, a.C, p, &S.pg0, &S.npg);
         if (S.npg > kMaxPages) fail("a split holds more pages than the kernel keeps");
         uint32_t ldr = 0, cmp = 0;
