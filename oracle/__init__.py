@@ -13,8 +13,10 @@ at lower precision:
     float32 value, or float32) and read back as stored;
   * logits are float32 and the greedy argmax is taken over those float32 values
     (lowest index wins a tie);
-  * in the prefill block, the operands of the bf16 matrix products (normed
-    input, rotated q, attention context, SwiGLU output) are rounded to bf16.
+  * in the prefill block, the activation operands of the bf16 matrix products
+    (the two normed inputs, the attention context, the SwiGLU output) are
+    rounded to bf16; the rotated q, the attention probabilities and the
+    residual stream are not.
 Attention is the two-pass softmax over every key, not an online or split form;
 those appear only as alternate forms that the tests prove equal to it.
 

@@ -280,15 +280,18 @@ def decode_step(shape, weights: OracleWeights, k_pools: list, v_pools: list,
 
 
 def prefill_block(shape, W: dict, k_pool: np.ndarray, v_pool: np.ndarray, table_row: np.ndarray,
-                  start: int, x_in: np.ndarray) -> np.ndarray:
+                  start: int, x_in: np.ndarray, return_operands: bool = False):
     """One decoder block over N consecutive tokens of one sequence at positions
     start..start+N-1, causal (row i attends to positions 0..start+i).
 
     The projections are bf16 matrix products with float32 accumulation, so their
     activation operands are rounded to bf16: the normed input, the attention
-    context and the SwiGLU output. K/V are stored in the cache type and read back
-    as stored; q and the attention probabilities are not rounded. The residual
-    stream is float64 here (float32 on the device). Returns x_out [N, D]."""
+    context, the second normed input and the SwiGLU output. K/V are stored in the
+    cache type and read back as stored; q and the attention probabilities are not
+    rounded. The residual stream is float64 here (float32 on the device).
+    Returns x_out [N, D]; with return_operands, also a dict of the intermediate
+    values (n, q, ctx, x_mid, n2, h) for the tests that pin where the rounding
+    falls."""
     Hq, Hkv, hd, eps = shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.rms_eps
     # operand rounding of the matrix products: bf16 for bf16 weights, float32 otherwise
     op = round_bf16 if shape.w_dtype == "bf16" else round_f32
@@ -313,7 +316,11 @@ def prefill_block(shape, W: dict, k_pool: np.ndarray, v_pool: np.ndarray, table_
     for i in range(N):
         p = start + i
         ctx[i] = attention_heads(Q[i], Kc[:p + 1], Vc[:p + 1], shape.group).reshape(-1)
-    X = X + linear(W["wo"], op(ctx))
+    ctx_op = op(ctx)
+    X = X + linear(W["wo"], ctx_op)
     n2 = op(rms_norm(X, W["mlp_norm"], eps))
     H = op(silu(linear(W["w_gate"], n2)) * linear(W["w_up"], n2))
-    return X + linear(W["w_down"], H)
+    out = X + linear(W["w_down"], H)
+    if return_operands:
+        return out, {"n": n, "q": Q.reshape(N, -1), "ctx": ctx_op, "x_mid": X, "n2": n2, "h": H}
+    return out

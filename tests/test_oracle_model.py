@@ -315,3 +315,83 @@ def test_parameter_census_and_kv_bytes_match_the_pages():
     seq, past = 1, 17
     total = 5376 * past * seq + 5376 * seq * seq + 24576 * past + 2644488 * seq + gold["fused_bytes_const"]
     assert round(total / 1e9, 4) == gold["fused_bytes_seq1_past17_gb"]
+
+
+# ------------------------------------------------------------------ prefill bf16 operand rounding
+
+def _bf16_exact(a) -> bool:
+    """Every value is a bf16 number: float32-exact with the low 16 bits of its
+    float32 pattern zero (read off the bits, not through the oracle's rounding)."""
+    a = np.asarray(a, dtype=np.float64)
+    f = a.astype(np.float32)
+    return bool(np.all(f.astype(np.float64) == a) and np.all((f.view(np.uint32) & 0xFFFF) == 0))
+
+
+def _prefill_case(w_dtype, seed=4, N=9, start=3):
+    shape = replace(S.tiny_shape(w_dtype="bf16", kv_dtype="bf16"), n_layers=1)
+    host = synth.weights_to_host(synth.make_weights(shape, seed=seed, w_std=0.25, with_embed=False))
+    W = OracleWeights(shape, host).layer(0)
+    kv = synth.make_kv(shape, np.array([start]), extra=N, seed=seed)
+    X = synth.to_host_bits(synth.make_x(N, shape.hidden, seed=seed))
+    run_shape = replace(shape, w_dtype=w_dtype)
+    kp, vp = synth.to_host_bits(kv.k[0]).copy(), synth.to_host_bits(kv.v[0]).copy()
+    return prefill_block(run_shape, W, kp, vp, kv.block_table[0], start, X, return_operands=True)
+
+
+def test_prefill_bf16_operands_are_rounded_to_nearest():
+    """The bf16 prefill rounds exactly the four activation operands of its matrix
+    products (normed input, attention context, second normed input, SwiGLU output)
+    to bf16, each to the nearest bf16 of the value the float32 form computes."""
+    _, ob = _prefill_case("bf16")
+    _, of = _prefill_case("f32")
+    for name in ("n", "ctx", "n2", "h"):
+        assert _bf16_exact(ob[name]), name
+        assert not _bf16_exact(of[name]), name
+    # the first operand has no rounded input upstream: nearest bf16 of the float32 form
+    ulp_half = np.ldexp(1.0, np.frexp(np.abs(of["n"]))[1] - 9)
+    assert np.all(np.abs(ob["n"] - of["n"]) <= ulp_half * (1 + 1e-6))
+    # later operands inherit the first rounding: within a few bf16 steps of the float32 form
+    for name in ("ctx", "n2", "h"):
+        assert _rel(ob[name], of[name]) < 2e-2, name
+
+
+def test_prefill_q_and_residual_are_not_rounded():
+    """q after RoPE and the residual stream stay unrounded in the bf16 prefill."""
+    _, ob = _prefill_case("bf16")
+    assert not _bf16_exact(ob["q"])
+    assert not _bf16_exact(ob["x_mid"])
+
+
+def test_prefill_rounding_pin_catches_a_dropped_rounding(monkeypatch):
+    """Planted mistake: with the bf16 rounding replaced by the float32 one, the
+    operand check above fails."""
+    monkeypatch.setattr(oq, "round_bf16", oq.round_f32)
+    _, ob = _prefill_case("bf16")
+    assert not _bf16_exact(ob["n"])
+
+
+def test_prefill_bf16_branch_equals_f32_branch_on_bf16_exact_data():
+    """On a block whose operands are bf16 numbers before any rounding (x of
+    entries +-2^-3 with eps 0, so the normed input is +-g exactly; one token at
+    position 0, so the context is the stored v; o_proj and up rows zero, so the
+    second normed input is +-g_mlp and the SwiGLU output 0), the bf16 and float32
+    branches agree exactly."""
+    shape = replace(S.tiny_shape(w_dtype="bf16", kv_dtype="bf16"), n_layers=1, rms_eps=0.0)
+    host = synth.weights_to_host(synth.make_weights(shape, seed=6, w_std=0.25, with_embed=False))
+    W = dict(OracleWeights(shape, host).layer(0))
+    W["wo"] = np.zeros_like(W["wo"])
+    W["w_up"] = np.zeros_like(W["w_up"])
+    rng = np.random.default_rng(6)
+    X = np.where(rng.random((1, shape.hidden)) < 0.5, -0.125, 0.125)
+    outs = []
+    for wd in ("bf16", "f32"):
+        kv = synth.make_kv(shape, np.array([0]), extra=1, fill="zeros")
+        kp, vp = synth.to_host_bits(kv.k[0]).copy(), synth.to_host_bits(kv.v[0]).copy()
+        out, ops = prefill_block(replace(shape, w_dtype=wd), W, kp, vp, kv.block_table[0], 0, X,
+                                 return_operands=True)
+        for name in ("n", "ctx", "n2", "h"):
+            assert _bf16_exact(ops[name]), (wd, name)
+        outs.append((out, ops))
+    assert np.array_equal(outs[0][0], outs[1][0])
+    for name in ("n", "ctx", "n2", "h", "q"):
+        assert np.array_equal(outs[0][1][name], outs[1][1][name]), name
