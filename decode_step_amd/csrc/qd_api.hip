@@ -355,6 +355,36 @@ const char* qd_last_error(void) { return g_err.c_str(); }
 
 int32_t qd_abi_version(void) { return QD_ABI_VERSION; }
 
+qd_status qd_decode_plan(const qd_config* cfg, int32_t batch, int32_t max_tokens, qd_decode_plan_info* out) {
+    g_err.clear();
+    if (!out) return fail(QD_EINVAL, "out is NULL");
+    qd_status st = check_config(cfg);
+    if (st != QD_OK) return st;
+    if (batch < 1 || batch > kMaxBatch) return fail(QD_ESHAPE, "batch %d not in [1, %d]", batch, kMaxBatch);
+    if (max_tokens < 1) return fail(QD_ESHAPE, "max_tokens %d < 1", max_tokens);
+    int chunk, S, hpw;
+    bool merge_in_o = false;
+    if (!plan_split(cfg, batch, max_tokens, &chunk, &S, &hpw, &merge_in_o))
+        return fail(QD_ECAPACITY, "context of %d tokens needs more than %d attention splits", max_tokens,
+                    qd::attn_max_splits());
+    qd::AttnArgs at{};
+    at.Hq = cfg->n_q_heads; at.Hkv = cfg->n_kv_heads; at.hd = cfg->head_dim; at.page = cfg->page_size;
+    at.chunk = chunk; at.S = S; at.B = batch; at.hpw = hpw; at.prefill_start = -1;
+    const bool kvbf = cfg->kv_dtype == QD_BF16, wbf = cfg->w_dtype == QD_BF16;
+    const bool mfma = qd::attn_uses_mfma(at, kvbf);
+    const int qkvr = (cfg->n_q_heads + 2 * cfg->n_kv_heads) * cfg->head_dim;
+    const int qkv_splits = qd::gemm16_store_splits(cfg->hidden, qkvr);
+    *out = qd_decode_plan_info{};
+    out->chunk = chunk;
+    out->splits = S;
+    out->heads_per_wg = hpw;
+    out->matrix_core_attention = mfma ? 1 : 0;
+    out->qkv_partials = (batch > 1 && wbf && qkv_splits > 1 && mfma) ? qkv_splits : 0;
+    out->merge_in_o_proj = merge_in_o ? 1 : 0;
+    out->step_kernel = (batch == 1 && qd::step::step_config_ok(cfg) && qd::step::plan_step(cfg, max_tokens).ok) ? 1 : 0;
+    return QD_OK;
+}
+
 size_t qd_workspace_bytes(const qd_config* cfg, int32_t batch, int32_t max_ctx, int32_t prefill_tokens) {
     if (check_config(cfg) != QD_OK) return 0;
     if (prefill_tokens > 0) {
@@ -393,6 +423,13 @@ qd_status decode_step_impl(const qd_config* cfg, const qd_weights* w, const qd_k
     if (tokens && !aligned4(tokens)) return fail(QD_EALIGN, "tokens not 4-byte aligned");
     if (x_in && !aligned4(x_in)) return fail(QD_EALIGN, "x_in not 4-byte aligned");
     if (!pos) return fail(QD_EINVAL, "pos is NULL");
+    if (!aligned4(pos)) return fail(QD_EALIGN, "pos not 4-byte aligned");
+    {
+        const void* outs[] = {logits, next_tokens, x_out, layer_out};
+        const char* names[] = {"logits", "next_tokens", "x_out", "layer_out"};
+        for (int i = 0; i < 4; ++i)
+            if (outs[i] && !aligned4(outs[i])) return fail(QD_EALIGN, "%s not 4-byte aligned", names[i]);
+    }
     const bool want_head = logits || next_tokens;
     if (want_head && (!w->final_norm || !w->lm_head))
         return fail(QD_EINVAL, "logits/next_tokens requested but final_norm or lm_head is NULL");

@@ -50,7 +50,13 @@ class qd_kv(Structure):
                 ("max_blocks", c_int32), ("num_pages", c_int32)]
 
 
-EXPORTS = ["qd_workspace_bytes", "qd_decode_step", "qd_decode_step_noalloc", "qd_prefill_block", "qd_kv_append", "qd_quantize_rows_int8",
+class qd_decode_plan_info(Structure):
+    _fields_ = [("chunk", c_int32), ("splits", c_int32), ("heads_per_wg", c_int32),
+                ("matrix_core_attention", c_int32), ("qkv_partials", c_int32),
+                ("merge_in_o_proj", c_int32), ("step_kernel", c_int32)]
+
+
+EXPORTS = ["qd_workspace_bytes", "qd_decode_plan", "qd_decode_step", "qd_decode_step_noalloc", "qd_prefill_block", "qd_kv_append", "qd_quantize_rows_int8",
            "qd_sample",
            "qd_last_error", "qd_abi_version", "qd_profile_enable", "qd_profile_read",
            "qd_profile_reset"]
@@ -65,6 +71,9 @@ class QdError(RuntimeError):
         self.status = status
 
 
+ABI_VERSION = 3   # QD_ABI_VERSION of the header this binding follows
+
+
 def load(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise ImportError(f"{path} is not built; run decode_step_amd/build.py "
@@ -73,6 +82,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     P = c_void_p
     lib.qd_workspace_bytes.argtypes = [POINTER(qd_config), c_int32, c_int32, c_int32]
     lib.qd_workspace_bytes.restype = c_size_t
+    lib.qd_decode_plan.argtypes = [POINTER(qd_config), c_int32, c_int32, POINTER(qd_decode_plan_info)]
+    lib.qd_decode_plan.restype = c_int32
     lib.qd_decode_step.argtypes = [POINTER(qd_config), POINTER(qd_weights), POINTER(qd_kv), c_int32,
                                    P, P, P, POINTER(c_int32), P, P, P, P, P, c_size_t, P]
     lib.qd_decode_step.restype = c_int32
@@ -93,6 +104,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qd_last_error.restype = c_char_p
     lib.qd_abi_version.argtypes = []
     lib.qd_abi_version.restype = c_int32
+    if lib.qd_abi_version() != ABI_VERSION:
+        raise ImportError(f"{path} has ABI version {lib.qd_abi_version()}, this binding expects {ABI_VERSION}: "
+                          "rebuild the library")
     lib.qd_profile_enable.argtypes = [ctypes.c_uint32]
     lib.qd_profile_enable.restype = c_int32
     lib.qd_profile_read.argtypes = [c_int32, POINTER(c_int32), POINTER(ctypes.c_double)]
@@ -160,6 +174,13 @@ def qd_quantize_rows_int8(w, w_dtype, rows, cols, q, scale, stream) -> int:
 def qd_sample(logits, batch, vocab, temperature, top_k, top_p, uniforms, tokens, stream) -> int:
     """Raw call; pointers are integers (device addresses) or None."""
     return int(lib().qd_sample(logits, batch, vocab, temperature, top_k, top_p, uniforms, tokens, stream))
+
+
+def qd_decode_plan(cfg: qd_config, batch: int, max_tokens: int) -> qd_decode_plan_info:
+    """The attention plan and kernel path of a decode step (host-only query)."""
+    out = qd_decode_plan_info()
+    check(lib().qd_decode_plan(cfg, batch, max_tokens, ctypes.byref(out)))
+    return out
 
 
 def qd_last_error() -> str:

@@ -47,13 +47,15 @@
 extern "C" {
 #endif
 
-#define QD_ABI_VERSION 2
+#define QD_ABI_VERSION 3
 
 typedef enum {
     QD_OK = 0,
     QD_EINVAL = -1,        /* a required pointer is NULL, or an enum is out of range      */
     QD_ESHAPE = -2,        /* sizes inconsistent or outside the supported set             */
-    QD_EALIGN = -3,        /* a pointer is not 16-byte aligned (128-bit loads)            */
+    QD_EALIGN = -3,        /* a pointer lacks its required alignment: 16 bytes for        *
+                            * matrices, pools, x_in of a prefill and the workspace (128-  *
+                            * bit loads), 4 bytes for float / int32 vectors               */
     QD_ECAPACITY = -4,     /* a position lies beyond the block table or the page pool     */
     QD_EPOSITION = -5,     /* a position is negative                                       */
     QD_EWORKSPACE = -6,    /* workspace NULL or smaller than qd_workspace_bytes()         */
@@ -114,7 +116,10 @@ typedef struct {
 
 /* Workspace bytes a call needs: for a decode step over `batch` sequences whose
  * positions are all < max_ctx (prefill_tokens = 0), or a prefill of
- * prefill_tokens tokens (batch = 1). Returns 0 if the config is invalid. */
+ * prefill_tokens tokens (batch = 1). Returns 0 if the config is invalid.
+ * The caller sizes and owns this scratch once, so a step itself allocates
+ * nothing (Tang page, section 5 Lowering: the generated run function performs
+ * no allocation). */
 size_t qd_workspace_bytes(const qd_config *cfg, int32_t batch, int32_t max_ctx,
                           int32_t prefill_tokens);
 
@@ -128,9 +133,16 @@ size_t qd_workspace_bytes(const qd_config *cfg, int32_t batch, int32_t max_ctx,
  *   next_tokens [B] int32 out (greedy argmax of the logits), or NULL
  *   x_out       [B][D] float out: the last layer's output (before the final norm), or NULL
  *   layer_out   [n_layers][B][D] float out: residual stream after each layer, or NULL
+ * tokens, pos, x_in and every output must be 4-byte aligned (QD_EALIGN).
  * The new token's K/V are written into every layer's cache at pos[b] before it
  * attends over positions 0..pos[b]; re-running at the same pos is idempotent.
- * lm_head / final_norm may be NULL only when logits and next_tokens are NULL. */
+ * lm_head / final_norm may be NULL only when logits and next_tokens are NULL.
+ * HIP graphs: the launch configuration (attention splits, and at batch 2..16 the
+ * grid of splits that hold keys) is planned from pos_host. A captured step
+ * replays that plan, so a replay is valid only while every sequence's position
+ * stays inside the captured plan: the same qd_decode_plan for the new positions
+ * and no sequence reaching a split (chunk) it did not have at capture. Capture
+ * again when a sequence crosses a chunk boundary. */
 qd_status qd_decode_step(const qd_config *cfg, const qd_weights *w, const qd_kv *kv,
                          int32_t batch, const int32_t *tokens, const float *x_in,
                          const int32_t *pos, const int32_t *pos_host,
@@ -161,7 +173,12 @@ qd_status qd_decode_step_noalloc(const qd_config *cfg, const qd_weights *w, cons
  * MFMA bf16 matrix products with float accumulation, their activation operands
  * rounded to bf16. x_in [N][D] in x_dtype (QD_BF16 or QD_F32); x_out [N][D] float;
  * both 16-byte aligned.
- * K/V of all N tokens are written into layer `layer`'s cache. */
+ * K/V of all N tokens are rotated once and written into layer `layer`'s cache
+ * before any row attends (nanoinfer page, attention pitfalls: keys rotated once,
+ * on insert, and the causal boundary is j <= i, a token attending to itself;
+ * nanoserve day 49, lesson 1: this step's K/V are written before it attends).
+ * Rows attend through the cache, so a chunk at start_pos > 0 sees every earlier
+ * token already stored there. */
 qd_status qd_prefill_block(const qd_config *cfg, const qd_layer *layer, int32_t layer_index,
                            const qd_kv *kv, int32_t n_tokens, int32_t start_pos,
                            const void *x_in, int32_t x_dtype, float *x_out,
@@ -225,11 +242,35 @@ int32_t qd_profile_enable(uint32_t kind_mask);
 int32_t qd_profile_read(int32_t kind, int32_t *launches, double *total_ms);
 void qd_profile_reset(void);
 
-/* Message for the last non-OK status returned on this thread ("" if none). */
+/* Message for the last non-OK status returned on this thread ("" if none).
+ * Every unsupported or invalid request returns its own status with a message and
+ * enqueues nothing; nothing falls back to another implementation (ForgeML page,
+ * ONNX subset: what lies outside the supported set fails explicitly instead of
+ * falling back). */
 const char *qd_last_error(void);
 
-/* QD_ABI_VERSION of the loaded library. */
+/* QD_ABI_VERSION of the loaded library, for a binding to check that it was
+ * built against this header (no passage defines it: a build convention). */
 int32_t qd_abi_version(void);
+
+/* How qd_decode_step would run `batch` sequences whose longest context is
+ * max_tokens (largest position + 1): a host-only query, no device work. Lets a
+ * caller (or a test) see which kernels a step takes, and whether a captured
+ * graph stays valid for new positions (same plan). QD_ECAPACITY when the
+ * context needs more attention splits than one merge combines. */
+typedef struct {
+    int32_t chunk;                  /* keys per attention split                               */
+    int32_t splits;                 /* attention splits of the longest sequence               */
+    int32_t heads_per_wg;           /* query heads per attention workgroup                    */
+    int32_t matrix_core_attention;  /* 1: the MFMA grouped attention kernel                    */
+    int32_t qkv_partials;           /* > 0: q|k|v as that many K-range partial products,      *
+                                     * finished inside the attention kernel                   */
+    int32_t merge_in_o_proj;        /* 1: batch 1, o_proj merges the splits (no merge launch) */
+    int32_t step_kernel;            /* 1: batch 1 eligible for the one-launch step, taken      *
+                                     * when QD_STEP_KERNEL=1 is set in the environment        */
+} qd_decode_plan_info;
+qd_status qd_decode_plan(const qd_config *cfg, int32_t batch, int32_t max_tokens,
+                         qd_decode_plan_info *out);
 
 #ifdef __cplusplus
 }

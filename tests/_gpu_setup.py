@@ -7,6 +7,7 @@ from dataclasses import dataclass
 import numpy as np
 import torch
 
+from oracle.qwen2 import OracleWeights, decode_step
 from workloads import synth
 
 
@@ -90,3 +91,30 @@ def kv_mismatch(dev_pool, host_pool, abs_frac=1e-4) -> str:
 
 def kv_matches(dev_pool, host_pool, abs_frac=1e-4) -> bool:
     return kv_mismatch(dev_pool, host_pool, abs_frac) == ""
+
+
+def check_argmax_tie(case, pos, tok):
+    """Planted exact tie: the winning lm_head row copied to a higher and then to a
+    lower vocabulary index gives two bitwise-equal largest logits; the step (and
+    the oracle) must return the lower index both times."""
+    sh = case.shape
+    lm = case.w["lm_head"] if case.w.get("lm_head") is not None else case.w["embed"]
+    key = "lm_head" if case.w.get("lm_head") is not None else "embed"
+    logits = torch.empty(1, sh.vocab, device="cuda")
+    nxt = torch.empty(1, dtype=torch.int32, device="cuda")
+    case.runner.step(pos, dev_i32(pos), tokens=dev_i32(tok), logits=logits, next_tokens=nxt)
+    torch.cuda.synchronize()
+    i = int(nxt.cpu()[0])
+    for j in ((i + 1 + 37) % sh.vocab, (i + sh.vocab - 23) % sh.vocab):
+        assert j not in (i, int(tok[0]))
+        lm[j].copy_(lm[i])
+        case.host_w[key][j] = case.host_w[key][i]
+        case.runner.step(pos, dev_i32(pos), tokens=dev_i32(tok), logits=logits, next_tokens=nxt)
+        torch.cuda.synchronize()
+        lg = logits.cpu().numpy()[0]
+        assert lg[i] == lg[j] and lg[i] == lg.max()
+        assert int(nxt.cpu()[0]) == min(i, j)
+        ow = OracleWeights(sh, case.host_w, cache_layers=False)
+        ref = decode_step(sh, ow, case.k_host, case.v_host, case.kv.block_table, pos, tokens=tok)
+        assert int(ref.next_tokens[0]) == min(i, j)
+        i = min(i, j)

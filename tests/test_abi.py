@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol(lib):
     for n in declared_functions():
         assert n in exported, n
         assert hasattr(lib, n)
-    assert lib.qd_abi_version() == 2
+    assert lib.qd_abi_version() == Q.ABI_VERSION == 3
 
 
 def test_struct_layout_matches_the_header(tmp_path):
@@ -96,11 +96,11 @@ class Fixture:
         self.pos = np.ascontiguousarray(pos, np.int32)
 
     def decode(self, batch=None, tokens=FAKE, x_in=None, ws=FAKE, ws_bytes=1 << 40, logits=FAKE,
-               pos_host=True):
+               pos_host=True, pos=FAKE, next_tokens=None, x_out=None, layer_out=None):
         B = len(self.pos) if batch is None else batch
         ph = self.pos.ctypes.data_as(POINTER(c_int32)) if pos_host else None
-        return Q.qd_decode_step(self.cfg, self.w, self.kv, B, tokens, x_in, FAKE, ph, logits, None,
-                                None, None, ws, ws_bytes, None)
+        return Q.qd_decode_step(self.cfg, self.w, self.kv, B, tokens, x_in, pos, ph, logits, next_tokens,
+                                x_out, layer_out, ws, ws_bytes, None)
 
 
 def _expect(status, what):
@@ -262,3 +262,50 @@ def test_noalloc_host_checks(lib):
     g = Fixture(_cfg(head_dim=96))
     _expect(Q.qd_decode_step_noalloc(g.cfg, g.w, g.kv, 1, FAKE, None, FAKE, g.pos.ctypes.data_as(POINTER(c_int32)),
                                      FAKE, None, None, None, None), Q.QD_ESHAPE)
+
+
+def test_output_and_position_alignment(lib):
+    f = Fixture(_cfg())
+    _expect(f.decode(pos=FAKE + 2), Q.QD_EALIGN)
+    _expect(f.decode(logits=FAKE + 2), Q.QD_EALIGN)
+    _expect(f.decode(next_tokens=FAKE + 1), Q.QD_EALIGN)
+    _expect(f.decode(x_out=FAKE + 2), Q.QD_EALIGN)
+    _expect(f.decode(layer_out=FAKE + 3), Q.QD_EALIGN)
+    # 4-byte aligned outputs pass the host checks (the fake workspace then fails its own)
+    _expect(f.decode(logits=FAKE + 4, next_tokens=FAKE + 4, x_out=FAKE + 4, layer_out=FAKE + 4,
+                     ws_bytes=16), Q.QD_EWORKSPACE)
+
+
+def _cfg_05b(**over):
+    return _cfg(**{**dict(n_layers=24, hidden=896, n_q_heads=14, n_kv_heads=2, head_dim=64, ffn=4864,
+                          vocab=151936), **over})
+
+
+def test_decode_plan_paths(lib):
+    """The host plan names the kernel path a step takes."""
+    p = Q.qd_decode_plan(_cfg_05b(), 1, 513)
+    assert p.merge_in_o_proj == 1 and p.step_kernel == 1 and p.qkv_partials == 0
+    assert p.splits * p.chunk >= 513
+    # batch 16 over long contexts: the grouped matrix-core attention finishes q|k|v
+    p = Q.qd_decode_plan(_cfg_05b(), 16, 4096)
+    assert p.matrix_core_attention == 1 and p.qkv_partials > 1 and p.step_kernel == 0
+    hd128 = _cfg(hidden=512, ffn=1024, n_q_heads=8, n_kv_heads=2, head_dim=128, vocab=1000, n_layers=2)
+    # batch 6 at 512 keys leaves too few (sequence, head, split) items: one query head
+    # per workgroup on the wide kernel, no partial q|k|v
+    p = Q.qd_decode_plan(hd128, 6, 512)
+    assert p.heads_per_wg == 1 and p.matrix_core_attention == 0 and p.qkv_partials == 0
+    # batch 8 at 1000+ keys: the grouped matrix-core kernel with partial q|k|v
+    p = Q.qd_decode_plan(hd128, 8, 1001)
+    assert p.matrix_core_attention == 1 and p.qkv_partials > 1
+    # the step kernel takes head_dim 64, bf16 only
+    assert Q.qd_decode_plan(hd128, 1, 100).step_kernel == 0
+    assert Q.qd_decode_plan(_cfg_05b(kv_dtype=Q.QD_F32), 1, 100).step_kernel == 0
+
+
+def test_decode_plan_checks(lib):
+    out = Q.qd_decode_plan_info()
+    _expect(lib.qd_decode_plan(_cfg_05b(), 1, 10, None), Q.QD_EINVAL)
+    _expect(lib.qd_decode_plan(_cfg_05b(), 0, 10, ctypes.byref(out)), Q.QD_ESHAPE)
+    _expect(lib.qd_decode_plan(_cfg_05b(), 1, 0, ctypes.byref(out)), Q.QD_ESHAPE)
+    _expect(lib.qd_decode_plan(_cfg_05b(), 1, 1 << 24, ctypes.byref(out)), Q.QD_ECAPACITY)
+    _expect(lib.qd_decode_plan(_cfg(head_dim=96), 1, 10, ctypes.byref(out)), Q.QD_ESHAPE)

@@ -15,10 +15,11 @@ import numpy as np
 import pytest
 import torch
 
+from decode_step_amd import qd as Q
 from oracle.qwen2 import OracleWeights, decode_step
 from workloads import shapes as S
 from workloads import synth
-from tests._gpu_setup import make_case, dev_i32, rel_err, guarded, canaries_intact, kv_matches
+from tests._gpu_setup import make_case, dev_i32, rel_err, guarded, canaries_intact, kv_matches, check_argmax_tie
 
 pytestmark = pytest.mark.gpu
 
@@ -149,13 +150,17 @@ def test_batched_three_block_gate_up_full_lds():
 
 @pytest.mark.parametrize("qkv_bias,qk_norm", [(False, True), (True, False)])
 def test_batched_partial_qkv_head_dim_128(qkv_bias, qk_norm):
-    """hidden 512 at batch 6: q|k|v runs as two K-range partial products that the
-    attention kernel (head_dim 128) sums, scales by the RMSNorm factor and biases
-    (or not) before the q/k norm and RoPE."""
+    """hidden 512 at batch 8 with a context past 1000: q|k|v runs as K-range
+    partial products that the matrix-core attention kernel (head_dim 128) sums,
+    scales by the RMSNorm factor and biases (or not) before the q/k norm and RoPE.
+    The host plan confirms that path (at batch 6 and 512 keys the step takes one
+    query head per workgroup on the other kernel instead)."""
     shape = replace(SMALL, hidden=512, ffn=1024, qkv_bias=qkv_bias, qk_norm=qk_norm, tied=not qk_norm,
                     n_q_heads=8, n_kv_heads=2, head_dim=128)
-    ctx = np.array([0, 3, 64, 130, 511, 17], np.int32)
+    ctx = np.array([0, 3, 64, 130, 511, 17, 1001, 700], np.int32)
     case = make_case(shape, ctx, seed=13, random_order=True)
+    plan = Q.qd_decode_plan(case.runner.cfg, len(ctx), int(ctx.max()) + 1)
+    assert plan.matrix_core_attention == 1 and plan.qkv_partials > 1
     tok = synth.make_tokens(len(ctx), shape.vocab, seed=13)
     logits, nxt, x_out, layer_out = _run_step(case, ctx, tokens=tok)
     ref = _oracle(case, ctx, tokens=tok)
@@ -344,6 +349,8 @@ def test_qwen2_0p5b_b16_paged_random_ctx():
         torch.cuda.synchronize()
         assert list(nd.cpu().numpy()) == list(r.next_tokens)
         tok_d, ref_tok = nd, r.next_tokens
+    # every K/V the steps appended (4 per sequence, pages in random order)
+    assert _cache_matches(case)
 
 
 @pytest.mark.timeout(900)
@@ -358,3 +365,13 @@ def test_qwen_8b_qknorm_b1_past4096():
     assert rel_err(logits.cpu().numpy(), ref.logits) <= 2e-3
     assert rel_err(layer_out.cpu().numpy(), ref.layer_out) <= 2e-3
     assert int(nxt.cpu()[0]) == int(ref.next_tokens[0])
+    assert _cache_matches(case)
+
+
+# ---------------------------------------------------------------- argmax ties
+
+
+def test_argmax_tie_takes_the_lower_index():
+    ctx = np.array([33], np.int32)
+    case = make_case(SMALL, ctx, seed=21)
+    check_argmax_tie(case, ctx, synth.make_tokens(1, SMALL.vocab, seed=22, name="tie"))

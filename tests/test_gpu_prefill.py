@@ -3,8 +3,8 @@ against the oracle's prefill_block on the same seeded inputs.
 
 The projections are bf16 MFMA GEMMs with float32 accumulation; the oracle rounds
 the same operands to bf16 (normed input, attention context, SwiGLU output).
-Tolerance on the block output, max |gpu - ref| / max |ref|: 2e-3 on the small
-shapes, 4e-3 on the 8B-class block. The float32 values the device rounds to bf16
+Tolerance on the block output, max |gpu - ref| / max |ref|: 2e-3 on every shape,
+the 8B-class block included (measured there: 1.73e-3). The float32 values the device rounds to bf16
 differ from the oracle's float64 ones, so some rounded operands land one bf16 step
 (2^-8 relative) away, and each such step feeds the next rounding point: a plain
 float32 emulation of the 8B block at 512 tokens has 1.9% of the attention context,
@@ -12,7 +12,8 @@ float32 emulation of the 8B block at 512 tokens has 1.9% of the attention contex
 differs from the oracle by 1.8e-3. Taking every rounded operand as one step off,
 independently, gives a down-projection error of 2^-8/sqrt(3) * ||w_j * H_i||
 (about 5e-3 absolute at ffn 12288, std 0.02 weights), about 2.5e-3 of max |ref|
-at the six-sigma tail of 2M outputs; 4e-3 covers it with the o-projection's share.
+at the six-sigma tail of 2M outputs, so 2e-3 has little margin on that block:
+a change that moves more roundings shows here first.
 Every K/V the block stores is within one bf16 step of the oracle's plus 5e-4 of
 the pool's largest magnitude: one normed-input element one bf16 step off moves a
 K/V element of that token by up to 2^-8 * |x| * |w| (after the head norm's
@@ -84,10 +85,15 @@ def test_small_prefill_block(shape, n):
 # The second case: four query heads per KV head at head_dim 128 (the 8B class), a
 # second chunk of 170 rows at an unaligned start (wide-tile GEMMs, several query
 # tiles whose key blocks straddle the chunk boundary).
+# The last two keep the cache in float32 under bf16 weights (the attention reads a
+# float32 cache in prefill mode, the K/V append stores float32).
 @pytest.mark.parametrize("shape,n1,n2", [
     (replace(SMALL, vocab=300), 20, 29),
     (replace(SMALL, vocab=300, qkv_bias=False, qk_norm=True, n_q_heads=8, n_kv_heads=2, head_dim=128,
-             hidden=256), 45, 170)])
+             hidden=256), 45, 170),
+    (replace(SMALL, vocab=300, kv_dtype="f32"), 20, 29),
+    (replace(SMALL, vocab=300, kv_dtype="f32", qkv_bias=False, qk_norm=True, n_q_heads=8, n_kv_heads=2,
+             head_dim=128, hidden=256), 45, 170)])
 def test_chunked_prefill_over_a_cache_then_decode(shape, n1, n2):
     case = make_case(shape, np.array([0]), seed=17, extra=n1 + n2 + 2, prefill_tokens=n1 + n2)
     x = synth.make_x(n1 + n2, shape.hidden, seed=17, dtype="bf16", device="cuda")
@@ -135,6 +141,6 @@ def test_qwen_8b_block_prefill512():
     ref = prefill_block(sh, ow.layer(0), k_pool, v_pool, kv.block_table[0], 0, synth.to_host_bits(x))
     err = rel_err(x_out.cpu().numpy(), ref)
     print(f"8B block prefill 512: max rel err {err:.3e}")
-    assert err <= 4e-3
+    assert err <= 2e-3
     _check_kv(kv.k[0], k_pool)
     _check_kv(kv.v[0], v_pool)

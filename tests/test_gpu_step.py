@@ -25,7 +25,7 @@ from decode_step_amd import qd as Q
 from oracle.qwen2 import OracleWeights, decode_step
 from workloads import shapes as S
 from workloads import synth
-from tests._gpu_setup import make_case, dev_i32, rel_err, kv_matches
+from tests._gpu_setup import make_case, dev_i32, rel_err, kv_matches, check_argmax_tie
 
 pytestmark = pytest.mark.gpu
 
@@ -165,3 +165,13 @@ def test_step_kernel_qwen2_0p5b_past512_greedy():
     assert gpu_tokens == ref_tokens
     assert worst <= 2e-3
     assert _cache_matches(case)
+
+
+@pytest.mark.timeout(300)
+def test_step_kernel_argmax_tie_takes_the_lower_index():
+    sh = replace(S.QWEN2_0P5B, n_layers=2, vocab=5000)
+    ctx = np.array([40], np.int32)
+    case = make_case(sh, ctx, seed=23)
+    before = _step_launches()
+    check_argmax_tie(case, ctx, synth.make_tokens(1, sh.vocab, seed=24, name="tie"))
+    assert _step_launches() == before + 3
