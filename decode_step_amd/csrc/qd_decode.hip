@@ -231,27 +231,6 @@ hipError_t launch_gemv(const GemvArgs& a, int w_is_bf16, int epi, int grid_cap, 
                      : gemv_dispatch_bm<float, 64>(a, epi, grid, shm, s);
 }
 
-// ---------------------------------------------------------------------------
-// Embedding gather (exact widen of the row; tied embeddings, nanoinfer page,
-// model notes). An id outside [0, V) yields a zero row instead of a fault.
-template <typename WT>
-__global__ __launch_bounds__(256) void embed_kernel(const int* tokens, const void* embed, float* x,
-                                                    int D, int V) {
-    const int b = blockIdx.x;
-    const int tok = tokens[b];
-    const bool ok = tok >= 0 && tok < V;
-    const void* row = (const char*)embed + (ok ? (long)tok * D * (long)sizeof(WT) : 0L);
-    for (int d = threadIdx.x; d < D; d += blockDim.x)
-        x[(long)b * D + d] = ok ? load_scalar<WT>(row, d) : 0.f;
-}
-
-hipError_t launch_embed(const int* tokens, const void* embed, float* x, int B, int D, int V,
-                        int w_is_bf16, hipStream_t s) {
-    if (w_is_bf16) hipLaunchKernelGGL((embed_kernel<uint16_t>), dim3(B), dim3(256), 0, s, tokens, embed, x, D, V);
-    else hipLaunchKernelGGL((embed_kernel<float>), dim3(B), dim3(256), 0, s, tokens, embed, x, D, V);
-    return hipGetLastError();
-}
-
 __global__ __launch_bounds__(256) void copy_kernel(const float* src, float* dst, long n) {
     for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x)
         dst[i] = src[i];

@@ -184,8 +184,6 @@ struct StepInputArgs {
 };
 hipError_t launch_step_input(const StepInputArgs& a, int w_type, hipStream_t s);   // 0 f32, 1 bf16, 2 int8
 
-hipError_t launch_embed(const int* tokens, const void* embed, float* x, int B, int D, int V,
-                        int w_is_bf16, hipStream_t s);
 hipError_t launch_copy(const float* src, float* dst, long n, hipStream_t s);
 hipError_t launch_argmax(const float* part_val, const int* part_idx, int nparts, int* out, int B,
                          hipStream_t s);
