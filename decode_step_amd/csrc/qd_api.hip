@@ -293,7 +293,7 @@ bool step_kernel_enabled() {
 }
 
 // The one-launch step needs the 256 CUs in 8 XCDs of an MI355X (checked once per
-// device; the kernel also checks each workgroup's XCD).
+// device).
 bool device_runs_step_grid(hipStream_t s) {
     static std::mutex mu;
     static signed char known[64] = {};
@@ -397,7 +397,15 @@ size_t qd_workspace_bytes(const qd_config* cfg, int32_t batch, int32_t max_ctx, 
     int chunk, S, hpw;
     bool merge_in_o = false;
     if (!plan_split(cfg, batch, max_ctx, &chunk, &S, &hpw, &merge_in_o)) return 0;
-    return plan_decode(cfg, batch, S, chunk).total;
+    // a shorter context can take finer splits, so more of them: size for the most
+    // splits any context up to max_ctx takes (only the split count sizes the region)
+    int s_max = S;
+    for (int t = 1; t < max_ctx; ++t) {
+        int ch_t, s_t, h_t;
+        bool m_t = false;
+        if (plan_split(cfg, batch, t, &ch_t, &s_t, &h_t, &m_t) && s_t > s_max) s_max = s_t;
+    }
+    return plan_decode(cfg, batch, s_max, chunk).total;
 }
 
 }  // extern "C"

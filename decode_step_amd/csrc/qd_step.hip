@@ -25,9 +25,11 @@
 //      the 8 counters (one lane each) and then reads the vector once. Polling
 //      the data itself from every workgroup took most of the bandwidth the
 //      weights need.
-//  - the q|k|v rows, attention splits and o_proj columns of KV head g run on XCD
-//    g, so those two hand-offs stay in one L2; three hand-offs per layer cross
-//    XCDs.
+//  - the q|k|v rows, attention splits and o_proj columns of KV head g run on the
+//    workgroups b with b mod 8 = g, so those two hand-offs stay in one L2 (the
+//    dispatcher deals consecutive workgroups round robin over the 8 XCDs, from a
+//    starting XCD that varies between launches, so equal b mod 8 means one XCD);
+//    three hand-offs per layer cross XCDs.
 //
 // Per layer l (tag T(l, ph) = 8 (l + 1) + ph):
 //   P0 qkv   (XCD g < Hkv)          q|k|v rows of group g = r * (W (x * g_attn)) + b
@@ -86,9 +88,6 @@ typedef __attribute__((address_space(3))) uint32_t lds_u32;
 __device__ __forceinline__ uint32_t lds_ld(const uint32_t* p) { return *(volatile const lds_u32*)p; }
 __device__ __forceinline__ void lds_st(uint32_t* p, uint32_t v) { *(volatile lds_u32*)p = v; }
 
-__device__ __forceinline__ uint32_t hw_xcc_id() {
-    return __builtin_amdgcn_s_getreg((20) | (0 << 6) | ((4 - 1) << 11)) & 0xF;   // HW_REG_XCC_ID [3:0]
-}
 
 // ---------------------------------------------------------------- shared state
 struct Smem {
@@ -1024,7 +1023,6 @@ __global__ __launch_bounds__(kThreads) void step_kernel(StepArgs a) {
             S.pid_p = pid >= 0 && pid < a.num_pages ? pid : -1;
         }
     }
-    if (hw_xcc_id() != (uint32_t)S.xcd) bad = true;   // the XCD layout the schedule assumes
     if (bad) {
         if (threadIdx.x == 0) {
             st_far32(a.err + 1, 0x10u);

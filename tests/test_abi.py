@@ -179,6 +179,18 @@ def test_workspace_bytes(lib):
     assert Q.qd_workspace_bytes(cfg, 0, 512) == 0
 
 
+def test_workspace_bytes_cover_every_shorter_context(lib):
+    """A workspace sized for max_ctx serves every shorter context, although a shorter
+    context can take finer attention splits (more of them): the size never falls as
+    max_ctx grows (batch 4, 8 KV heads of 128 dims: 2048 keys take 32 splits of 64,
+    2052 take 26 of 80)."""
+    cfg = _cfg(hidden=512, ffn=1024, n_q_heads=32, n_kv_heads=8, head_dim=128, vocab=1000, n_layers=2)
+    for B in (1, 4, 16):
+        sizes = [Q.qd_workspace_bytes(cfg, B, t) for t in range(1, 2200, 7)]
+        assert all(x > 0 for x in sizes)
+        assert all(u <= v for u, v in zip(sizes, sizes[1:])), B
+
+
 def test_kv_append_checks(lib):
     f = Fixture(_cfg())
     ph = f.pos.ctypes.data_as(POINTER(c_int32))
