@@ -82,9 +82,11 @@ def _bytes_per_launch(shape, B, ctx):
     return out
 
 
-def step_bytes(shape, B, ctx):
+def step_bytes(shape, B, ctx, block_only=False):
     """Algorithmic bytes of one whole step (every weight once, every cached K/V once,
-    the new K/V written, the embedding rows and the logits)."""
+    the new K/V written, the embedding rows and the logits); block_only: the decoder
+    blocks alone (their matrices, gains and biases, the K/V, the float32 vector in
+    and out)."""
     wb, rb, gb = _dtype_bytes(shape)
     kvb = 2 if shape.kv_dtype == "bf16" else 4
     c = shape.param_counts()
@@ -98,6 +100,11 @@ def step_bytes(shape, B, ctx):
     weights = mat * wb + rows * rb + (c["norms"] + bias) * gb
     kv_read = int(np.sum(ctx)) * shape.n_layers * 2 * shape.kv_dim * kvb
     kv_write = B * shape.n_layers * 2 * shape.kv_dim * kvb
+    if block_only:
+        # mat holds one vocabulary table (the lm_head, or the tied table read as one),
+        # rows its row scales, norms the final norm
+        blocks = (mat - V * D) * wb + (rows - V) * rb + (c["norms"] - D + bias) * gb
+        return blocks + kv_read + kv_write + 2 * B * D * 4
     emb_rows = B * (D * wb + rb)
     logits = B * shape.vocab * 4
     return weights + kv_read + kv_write + emb_rows + logits
@@ -259,10 +266,10 @@ class OracleTimer:
     """The fp64 oracle's whole decode steps on the host, timed in rounds that
     alternate with the GPU's, plus a single-thread figure."""
 
-    def __init__(self, wl, case_host, ctx, tokens):
+    def __init__(self, wl, case_host, ctx, tokens, x_in=None):
         from oracle.qwen2 import OracleWeights, decode_step
         self.decode_step = decode_step
-        self.wl, self.ctx, self.tokens = wl, ctx, tokens
+        self.wl, self.ctx, self.tokens, self.x_in = wl, ctx, tokens, x_in
         self.host_w, self.kh, self.vh, self.table = case_host
         self.ow = OracleWeights(wl.shape, self.host_w, cache_layers=True)
         self.threads = blas_threads()
@@ -270,7 +277,11 @@ class OracleTimer:
         self.steps, self.secs, self.rounds = 0, 0.0, []
 
     def one(self):
-        self.decode_step(self.wl.shape, self.ow, self.kh, self.vh, self.table, self.ctx, tokens=self.tokens)
+        if self.x_in is not None:   # one decoder block from the float32 vector
+            self.decode_step(self.wl.shape, self.ow, self.kh, self.vh, self.table, self.ctx, x_in=self.x_in,
+                             with_logits=False)
+        else:
+            self.decode_step(self.wl.shape, self.ow, self.kh, self.vh, self.table, self.ctx, tokens=self.tokens)
 
     def round(self, budget_s):
         n, t0 = 0, time.perf_counter()
@@ -538,6 +549,9 @@ def main():
                          "(use when this command itself runs under rocprofv3)")
     ap.add_argument("--trace-child", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--rounds", type=int, default=3, help="GPU / CPU-oracle rounds that alternate")
+    ap.add_argument("--rotate", type=int, default=0,
+                    help="weight copies the steps rotate through, so that each step streams its weights from "
+                         "HBM rather than the last-level cache (default: 24 for a one-block workload, else 1)")
     ap.add_argument("--log", default=os.path.join(ROOT, "results", "bench_runs.jsonl"),
                     help="append-only JSON-lines log of every run ('' for none)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -584,16 +598,33 @@ def main():
         w = quantize_weights_int8(w)
         torch.cuda.synchronize()
     kv = synth.make_kv(shape, ctx, extra=2, seed=wl.seed, device=dev, random_order=wl.paged_random)
-    runner = DecodeRunner(shape, w, kv.k, kv.v, kv.block_table, max_batch=B, max_ctx=int(ctx.max()) + 2,
-                          device=dev)
+    # weight copies the steps rotate through (the blocks' tensors only; the vocabulary
+    # tables are shared): a one-block workload's weights (60 MB in fp32 for the 0.5B
+    # block) fit the last-level cache, so one copy would time cache hits, not HBM
+    rotate = args.rotate if args.rotate > 0 else (24 if wl.block_only else 1)
+    w_copies = [w] + [{**w, "layers": [{k: (v.clone() if torch.is_tensor(v) else v) for k, v in L.items()}
+                                       for L in w["layers"]]} for _ in range(rotate - 1)]
+    runners = [DecodeRunner(shape, wr, kv.k, kv.v, kv.block_table, max_batch=B, max_ctx=int(ctx.max()) + 2,
+                            device=dev) for wr in w_copies]
+    runner = runners[0]
     tokens = synth.make_tokens(B, shape.vocab, seed=wl.seed, name="tok0")
     tok_d = torch.from_numpy(tokens).to(dev)
     pos_d = torch.from_numpy(ctx).to(dev)
     logits = torch.empty(B, shape.vocab, device=dev)
     nxt = torch.empty(B, dtype=torch.int32, device=dev)
+    x_in = synth.make_x(B, shape.hidden, seed=wl.seed, device=dev) if wl.block_only else None
+    x_out = torch.empty(B, shape.hidden, device=dev) if wl.block_only else None
+    turn = [0]
+
+    def step_with(r):
+        if wl.block_only:   # one decoder block: the float32 vector in and out
+            r.step(ctx, pos_d, x_in=x_in, x_out=x_out, stream=torch.cuda.current_stream())
+        else:
+            r.step(ctx, pos_d, tokens=tok_d, logits=logits, next_tokens=nxt, stream=torch.cuda.current_stream())
+
     def step():
-        runner.step(ctx, pos_d, tokens=tok_d, logits=logits, next_tokens=nxt,
-                    stream=torch.cuda.current_stream())
+        step_with(runners[turn[0] % rotate])
+        turn[0] += 1
 
     def timed(fn, k):
         torch.cuda.synchronize()
@@ -604,26 +635,34 @@ def main():
         return time.perf_counter() - t0
 
     def capture():
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            step()
-        torch.cuda.current_stream().wait_stream(side)
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            step()
-        return g
+        """One graph per weight copy; the returned call replays them in turn."""
+        graphs = []
+        for r in runners:
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                step_with(r)
+            torch.cuda.current_stream().wait_stream(side)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step_with(r)
+            graphs.append(g)
+
+        def replay():
+            graphs[turn[0] % rotate].replay()
+            turn[0] += 1
+        return replay
 
     if args.trace_child:   # the replays a rocprofv3 parent traces, nothing else
         for _ in range(args.warmup):
             step()
-        g = capture()
+        replay = capture()
         for _ in range(args.warmup):
-            g.replay()
-        timed(g.replay, args.steps)
+            replay()
+        timed(replay, args.steps)
         return
 
-    sb = step_bytes(shape, B, ctx)
+    sb = step_bytes(shape, B, ctx, block_only=wl.block_only)
     # eager launches (one qd_decode_step call per step)
     for _ in range(args.warmup):
         step()
@@ -632,7 +671,7 @@ def main():
           f"{B * args.steps / el_eager:.1f} tokens/s", file=sys.stderr, flush=True)
     # the same call captured once in a HIP graph and replayed
     graph = None if args.no_graph else capture()
-    run = graph.replay if graph else step
+    run = graph if graph else step
     for _ in range(args.warmup):
         run()
 
@@ -646,7 +685,8 @@ def main():
             hw = synth.weights_to_host(w)
         case_host = (hw, [synth.to_host_bits(t).copy() for t in kv.k],
                      [synth.to_host_bits(t).copy() for t in kv.v], kv.block_table)
-        oracle = OracleTimer(wl, case_host, ctx, tokens)
+        oracle = OracleTimer(wl, case_host, ctx, tokens,
+                             x_in=synth.to_host_bits(x_in).astype(np.float64) if wl.block_only else None)
 
     # timed rounds: K steps split over R rounds, each after 3 untimed replays, with
     # an oracle round after each GPU round
@@ -760,7 +800,7 @@ def main():
            "data": "synthetic",
            "config": {"workload": wl.name, "batch": B, "past": int(ctx.max()) if wl.past else None,
                       "ctx_range": list(wl.ctx_range) if wl.ctx_range else None},
-           "launch": "hip_graph" if graph else "eager",
+           "launch": "hip_graph" if graph else "eager", "weight_copies": rotate,
            "step_ms": step_stats, "gpu_rounds_tokens_per_s": gpu_rounds,
            "eager_tokens_per_s": round(B * args.steps / el_eager, 2),
            "hbm_gbs_end_to_end": round(sb * args.steps / elapsed / 1e9, 1),

@@ -211,6 +211,62 @@ def test_outputs_guarded_and_deterministic(ctx_list):
         assert rel_err(outs[0][0].numpy(), outs[1][0].numpy().astype(np.float64)) <= 1e-5
 
 
+def _guard(t, pad, sentinel):
+    """t's values inside a larger buffer whose first and last pad elements hold the
+    sentinel; returns (full, view shaped like t)."""
+    n = t.numel()
+    full = torch.full((n + 2 * pad,), sentinel, dtype=t.dtype, device=t.device)
+    full[pad:pad + n].copy_(t.reshape(-1))
+    return full, full[pad:pad + n].view(t.shape)
+
+
+def _guard_intact(full, n, pad, sentinel):
+    f = full.cpu()
+    return bool(torch.all(f[:pad] == sentinel)) and bool(torch.all(f[pad + n:] == sentinel))
+
+
+@pytest.mark.parametrize("kv_dtype,ctx_list", [("bf16", [40]), ("bf16", [40, 7, 300]), ("f32", [33, 16])])
+def test_writes_stay_inside_outputs_and_pools(kv_dtype, ctx_list):
+    """Canaries on both sides of logits, next_tokens, x_out, layer_out and of every
+    layer's K and V page pool: a step writes none of them, every output element is
+    written, and the pools then equal the oracle's (which holds the new rows only)."""
+    from decode_step_amd.runner import DecodeRunner
+    shape = replace(SMALL, kv_dtype=kv_dtype)
+    ctx = np.array(ctx_list, np.int32)
+    B, pad = len(ctx), 2048
+    w = synth.make_weights(shape, seed=29, device="cuda")
+    kv = synth.make_kv(shape, ctx, extra=4, seed=29, device="cuda", random_order=True)
+    sent = 1024.0
+    kg = [_guard(t, pad, sent) for t in kv.k]
+    vg = [_guard(t, pad, sent) for t in kv.v]
+    runner = DecodeRunner(shape, w, [v for _, v in kg], [v for _, v in vg], kv.block_table, max_batch=B,
+                          max_ctx=int(ctx.max()) + 5)
+    k_host = [synth.to_host_bits(v).copy() for _, v in kg]
+    v_host = [synth.to_host_bits(v).copy() for _, v in vg]
+    tok = synth.make_tokens(B, shape.vocab, seed=29)
+    lg_full, lg = guarded(B * shape.vocab)
+    xo_full, xo = guarded(B * shape.hidden)
+    lo_full, lo = guarded(shape.n_layers * B * shape.hidden)
+    nx_full = torch.full((B + 2 * pad,), 777, dtype=torch.int32, device="cuda")
+    nx = nx_full[pad:pad + B]
+    nx.fill_(-1)
+    runner.step(ctx, dev_i32(ctx), tokens=dev_i32(tok), logits=lg.view(B, shape.vocab), next_tokens=nx,
+                x_out=xo.view(B, shape.hidden), layer_out=lo.view(shape.n_layers, B, shape.hidden))
+    torch.cuda.synchronize()
+    assert canaries_intact(lg_full, B * shape.vocab) and canaries_intact(xo_full, B * shape.hidden)
+    assert canaries_intact(lo_full, shape.n_layers * B * shape.hidden)
+    nf = nx_full.cpu()
+    assert bool(torch.all(nf[:pad] == 777)) and bool(torch.all(nf[pad + B:] == 777))
+    for full, view in kg + vg:
+        assert _guard_intact(full, view.numel(), pad, sent)
+    assert not torch.isnan(lg).any() and not torch.isnan(xo).any() and not torch.isnan(lo).any()
+    ow = OracleWeights(shape, synth.weights_to_host(w), cache_layers=True)
+    ref = decode_step(shape, ow, k_host, v_host, kv.block_table, ctx, tokens=tok)
+    assert rel_err(lg.cpu().numpy().reshape(B, -1), ref.logits) <= 2e-3
+    assert list(nx.cpu().numpy()) == list(ref.next_tokens)
+    assert all(kv_matches(view, host) for (_, view), host in zip(kg + vg, k_host + v_host))
+
+
 @pytest.mark.parametrize("ctx_list", [[70], [70, 3, 129]])
 def test_graph_replay_matches_eager(ctx_list):
     """One decode step captured in a HIP graph and replayed several times, with eager
