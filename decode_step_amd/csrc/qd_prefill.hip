@@ -500,6 +500,13 @@ void mfma_gemm_v2_kernel(GemmArgs a, int ntn, int ntm, int splits) {
         for (int q = 0; q < QW; ++q)
             lds_dma16(wsrc[q] + k0, __builtin_amdgcn_readfirstlane(base + SA + RPI * (wave * QW + q) * RB));
     };
+    // one DMA instruction of step kt: d < QA an A row group, else a W row group
+    auto issue_one = [&](int buf, int kt, int d) {
+        const int k0 = (kt_begin + kt) * BK;
+        const uint32_t base = ring_lds + buf * SB;
+        if (d < QA) lds_dma16(asrc[d] + k0, __builtin_amdgcn_readfirstlane(base + RPI * (wave * QA + d) * RB));
+        else lds_dma16(wsrc[d - QA] + k0, __builtin_amdgcn_readfirstlane(base + SA + RPI * (wave * QW + d - QA) * RB));
+    };
 
     const int lrow = lane & 31, lhalf = lane >> 5;
     f32x16_t acc[TI][TJ];
@@ -530,33 +537,63 @@ void mfma_gemm_v2_kernel(GemmArgs a, int ntn, int ntm, int splits) {
 
     // Ring: steps 0 .. NS-1 issued up front; at step t's barrier every wave has read
     // stage t (its fragments are in registers) and the DMA of step t + NS takes its
-    // buffer. Past the end the last step is reloaded (unused), so every step issues
-    // NQ loads per lane and one wait count serves all.
+    // buffer (right after the barrier, or spread over step t + 1, below). Past the
+    // end the last step is reloaded (unused), so every step issues NQ loads per lane
+    // and one wait count serves all.
 #pragma unroll
     for (int st = 0; st < NS; ++st) issue(st, st < nk ? st : nk - 1);
     __builtin_amdgcn_s_waitcnt(wait_vm((NS - 1) * NQ));
     __builtin_amdgcn_s_barrier();
     rd(0, 0, fa[0], fb[0]);
+    // SPREAD (three or more stages): the stage freed at step t - 1's barrier is
+    // refilled during step t, one DMA instruction after every second MFMA of the
+    // first KS - 1 sub-steps. Issued back to back after the barrier, a step's DMA
+    // held each wave's issue for about 0.3 us (the texture unit takes the CU's 1 KB
+    // instructions one after another) with the matrix core idle; spread, that work
+    // overlaps the MFMAs, and the data is needed only NS - 1 steps later. The wait
+    // at the end of step t still leaves exactly one slot's loads outstanding (the
+    // ones issued during step t).
+    constexpr bool SPREAD = NS >= 3 && (KS - 1) * (TI * TJ / 2) >= NQ;
     for (int t = 0; t < nk; ++t) {
         const int buf = t % NS;
+        if constexpr (SPREAD) {
+            const bool pend = t >= 1;                                   // a stage to refill
+            const int pbuf = (t + NS - 1) % NS;
+            const int pkt = t - 1 + NS < nk ? t - 1 + NS : nk - 1;    // past the end: the last step again (unused)
 #pragma unroll
-        for (int ks = 0; ks < KS - 1; ++ks) {
-            rd(buf, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
-            mm(fa[ks & 1], fb[ks & 1], 0, TI * TJ);
+            for (int ks = 0; ks < KS - 1; ++ks) {
+                rd(buf, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int r = 0; r < NR; ++r) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+                for (int q = 0; q < TI * TJ; ++q) {
+                    mm(fa[ks & 1], fb[ks & 1], q, q + 1);
+                    if (q & 1) {
+                        const int dd = ks * (TI * TJ / 2) + (q >> 1);
+                        if (dd < NQ && pend) issue_one(pbuf, pkt, dd);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, TI * TJ - NR, 0);
-            __builtin_amdgcn_sched_barrier(0);
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < KS - 1; ++ks) {
+                rd(buf, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+                mm(fa[ks & 1], fb[ks & 1], 0, TI * TJ);
+#pragma unroll
+                for (int r = 0; r < NR; ++r) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, TI * TJ - NR, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
         mm(fa[(KS - 1) & 1], fb[(KS - 1) & 1], 0, PRE);
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(wait_vm((NS - 2) * NQ));     // step t + 1 landed (this lane's part)
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);                 // this lane's reads of step t done
         __builtin_amdgcn_s_barrier();                           // ... and every lane's
-        issue(buf, t + NS < nk ? t + NS : nk - 1);
+        if constexpr (!SPREAD) issue(buf, t + NS < nk ? t + NS : nk - 1);
         __builtin_amdgcn_sched_barrier(0);
         rd((t + 1) % NS, 0, fa[0], fb[0]);                      // past the last step: unused
         mm(fa[(KS - 1) & 1], fb[(KS - 1) & 1], PRE, TI * TJ);
