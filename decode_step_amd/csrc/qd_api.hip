@@ -397,15 +397,21 @@ size_t qd_workspace_bytes(const qd_config* cfg, int32_t batch, int32_t max_ctx, 
     int chunk, S, hpw;
     bool merge_in_o = false;
     if (!plan_split(cfg, batch, max_ctx, &chunk, &S, &hpw, &merge_in_o)) return 0;
-    // a shorter context can take finer splits, so more of them: size for the most
-    // splits any context up to max_ctx takes (only the split count sizes the region)
-    int s_max = S;
-    for (int t = 1; t < max_ctx; ++t) {
-        int ch_t, s_t, h_t;
-        bool m_t = false;
-        if (plan_split(cfg, batch, t, &ch_t, &s_t, &h_t, &m_t) && s_t > s_max) s_max = s_t;
+    // any batch up to `batch` (batch 1 adds the one-launch step's buffers), and a
+    // shorter context can take finer splits, so more of them: size for the most
+    // splits any context up to max_ctx takes at each batch (only the split count
+    // sizes the partials region)
+    size_t need = 0;
+    for (int b = 1; b <= batch; ++b) {
+        int s_max = 0, ch_b = chunk;
+        for (int t = 1; t <= max_ctx; ++t) {
+            int ch_t, s_t, h_t;
+            bool m_t = false;
+            if (plan_split(cfg, b, t, &ch_t, &s_t, &h_t, &m_t) && s_t > s_max) { s_max = s_t; ch_b = ch_t; }
+        }
+        if (s_max > 0) need = std::max(need, plan_decode(cfg, b, s_max, ch_b).total);
     }
-    return plan_decode(cfg, batch, s_max, chunk).total;
+    return need;
 }
 
 }  // extern "C"

@@ -14,10 +14,13 @@
 //    kept (the transformers warper removes only scores below the k-th).
 //    Dividing by T > 0 keeps the order, so the threshold is taken on the logits
 //    themselves.
-// 2. The candidates (at most kSampleCand; more, from ties, give token -1) are
-//    compacted into LDS with z = logit / T (float32, IEEE division), and sorted
-//    ascending by (z, token id): a stable ascending sort, the order the page
-//    settles on (a tied pair keeps its index order).
+// 2. The candidates are compacted into LDS with z = logit / T (float32, IEEE
+//    division), and sorted ascending by (z, token id): a stable ascending sort,
+//    the order the page settles on (a tied pair keeps its index order). When more
+//    than kSampleCand candidates tie at the k-th largest value, only the fewer
+//    than k above it are stored and sorted; the tied ones share one z and one
+//    probability and come first in that order (by id), so they are counted, and
+//    when some of them stay, wave 0 draws over the row in token order itself.
 // 3. top-p as the page's reference defines it: with probabilities
 //    e_j / S (e_j = exp(z_j - max z), S their sum), the cumulative sum over the
 //    ascending order is taken in float32, one term at a time, and every token
@@ -155,6 +158,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleArgs a) {
     //    are compacted into LDS once and the last two digits run there; otherwise
     //    they read the row again.
     const int k = a.top_k < V ? a.top_k : V;
+    uint32_t thr_key = 0;                          // order key of the k-th largest logit
     uint32_t prefix = 0;
     int need = k;
     digit(21, 11, prefix, need, global_keys);
@@ -179,6 +183,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleArgs a) {
         digit(10, 11, prefix, need, lds_keys);
         digit(0, 10, prefix, need, lds_keys);
         const uint32_t thresh = prefix;
+        thr_key = thresh;
         // 2. the candidates, in place: keys at or above the threshold become (key of
         //    z = logit / T, token); the rest sort to the end
         if (tid == 0) s_cnt = 0;
@@ -199,6 +204,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleArgs a) {
         digit(10, 11, prefix, need, global_keys);
         digit(0, 10, prefix, need, global_keys);
         const uint32_t thresh = prefix;
+        thr_key = thresh;
         // 2. candidates: every logit whose key reaches the threshold, with z = logit / T
         scan([&](int i, float v) {
             if (order_key(v) >= thresh) {
@@ -211,8 +217,9 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleArgs a) {
         });
         __syncthreads();
     }
-    const int C = s_cnt;
-    if (C > kSampleCand || C < 1) {   // ties beyond the candidate space (or NaN keys): no draw
+    int C = s_cnt;
+    __syncthreads();   // every thread has read the count before the tie path below reuses s_cnt
+    if (C < 1) {   // no candidate: NaN keys
         if (tid == 0) a.tokens[row] = -1;
         return;
     }
@@ -231,41 +238,151 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleArgs a) {
             }
         __syncthreads();
     };
-    bitonic();
-
-    // 3. e_j = exp(z_j - max z) over the ascending order; S by a tree sum; the
-    //    cumulative sum of e_j / S one term at a time; remove while it is <= 1 - p
     auto zval = [&](unsigned long long key) {
         const uint32_t ok = (uint32_t)(key >> 32);
         return __uint_as_float(ok ^ ((ok & 0x80000000u) ? 0x80000000u : 0xffffffffu));
     };
-    const float zmax = zval(ck[C - 1]);
-    float part = 0.f;
-    for (int j = tid; j < C; j += kSampleThreads) {
-        const float e = expf(zval(ck[j]) - zmax);
-        ce[j] = e;
-        part += e;
-    }
-    part = group_sum<kWave>(part);
-    if (lane == 0) s_red[wave] = part;
-    __syncthreads();
-    if (tid == 0) {
-        float S = 0.f;
-        for (int w = 0; w < kSampleThreads / kWave; ++w) S += s_red[w];
-        int j0 = C - 1;   // the largest always stays
-        if (a.top_p < 1.f) {
-            float cum = 0.f;
-            for (int j = 0; j < C - 1; ++j) {
-                cum += __fdiv_rn(ce[j], S);
-                if (!(cum <= a.one_minus_p)) { j0 = j; break; }
-            }
-        } else {
-            j0 = 0;
+    auto block_sum = [&](float v) {   // tree sum over the workgroup (every thread returns it)
+        v = group_sum<kWave>(v);
+        __syncthreads();
+        if (lane == 0) s_red[wave] = v;
+        __syncthreads();
+        float t = 0.f;
+        for (int w = 0; w < kSampleThreads / kWave; ++w) t += s_red[w];
+        return t;
+    };
+
+    int j0;
+    if (C <= kSampleCand) {
+        bitonic();
+        // 3. e_j = exp(z_j - max z) over the ascending order; S by a tree sum; the
+        //    cumulative sum of e_j / S one term at a time; remove while it is <= 1 - p
+        const float zmax = zval(ck[C - 1]);
+        float part = 0.f;
+        for (int j = tid; j < C; j += kSampleThreads) {
+            const float e = expf(zval(ck[j]) - zmax);
+            ce[j] = e;
+            part += e;
         }
-        s_j0 = j0;
+        const float S = block_sum(part);
+        if (tid == 0) {
+            int jj = C - 1;   // the largest always stays
+            if (a.top_p < 1.f) {
+                float cum = 0.f;
+                for (int j = 0; j < C - 1; ++j) {
+                    cum += __fdiv_rn(ce[j], S);
+                    if (!(cum <= a.one_minus_p)) { jj = j; break; }
+                }
+            } else {
+                jj = 0;
+            }
+            s_j0 = jj;
+        }
+        __syncthreads();
+        j0 = s_j0;
+    } else {
+        // More candidates than LDS holds: fewer than k lie above the threshold and the
+        // rest tie at the threshold value itself, so they share one z and one e. In
+        // the ascending (z, id) order the tied ones come first, in id order. The
+        // above ones are sorted in LDS; the tied ones are counted, not stored.
+        if (tid == 0) s_cnt = 0;
+        for (int j = tid; j < kSampleCand; j += kSampleThreads) ck[j] = ~0ull;
+        __syncthreads();
+        const uint32_t thresh = thr_key;
+        scan([&](int i, float v) {
+            const uint32_t key = order_key(v);
+            if (key > thresh) {
+                const int slot = atomicAdd(&s_cnt, 1);
+                if (slot < kSampleCand) ck[slot] = ((unsigned long long)order_key(__fdiv_rn(v, a.temperature)) << 32) | (uint32_t)i;
+            }
+        });
+        __syncthreads();
+        const int ng = s_cnt, ne = C - ng;   // above (ng < k <= kSampleMaxK), tied
+        bitonic();
+        const float vt = __uint_as_float(thresh ^ ((thresh & 0x80000000u) ? 0x80000000u : 0xffffffffu));
+        const float zt = __fdiv_rn(vt, a.temperature);
+        const float zmax = ng > 0 ? zval(ck[ng - 1]) : zt;
+        const float et = expf(zt - zmax);
+        float part = 0.f;
+        for (int j = tid; j < ng; j += kSampleThreads) {
+            const float e = expf(zval(ck[j]) - zmax);
+            ce[j] = e;
+            part += e;
+        }
+        const float S = block_sum(part) + (float)ne * et;
+        if (tid == 0) {
+            int jj = C - 1;
+            if (a.top_p < 1.f) {
+                float cum = 0.f;
+                const float pt = __fdiv_rn(et, S);
+                for (int j = 0; j < C - 1; ++j) {
+                    cum += j < ne ? pt : __fdiv_rn(ce[j - ne], S);
+                    if (!(cum <= a.one_minus_p)) { jj = j; break; }
+                }
+            } else {
+                jj = 0;
+            }
+            s_j0 = jj;
+        }
+        __syncthreads();
+        j0 = s_j0;
+        if (j0 >= ne) {   // only above candidates stay: the LDS path below, over them
+            C = ng;
+            j0 -= ne;
+        } else {
+            // tied tokens of tie rank >= j0 and every above one stay; the draw runs over
+            // them in token order, one term at a time, by wave 0 reading the row in
+            // chunks of 64 ids (lane order = id order): once for the total, once for
+            // the search
+            const float Sk = block_sum(tid < ng ? ce[tid] : 0.f) + (float)(ne - j0) * et;
+            if (wave != 0) return;
+            const float pt = __fdiv_rn(et, Sk);
+            // the row's logit for lane l of the chunk at c0 (0 past the row)
+            auto load = [&](int c0) { return c0 + lane < V ? lg[c0 + lane] : 0.f; };
+            auto chunk = [&](int c0, float v, int& rank_base, float& p, bool& kept) {
+                const int i = c0 + lane;
+                const uint32_t key = order_key(v);
+                const bool tied = i < V && key == thresh, above = i < V && key > thresh;
+                const unsigned long long m = __ballot(tied);
+                const int rank = rank_base + __popcll(m & ((1ull << lane) - 1ull));
+                kept = above || (tied && rank >= j0);
+                p = !kept ? 0.f : (tied ? pt : __fdiv_rn(expf(__fdiv_rn(v, a.temperature) - zmax), Sk));
+                rank_base += __popcll(m);
+            };
+            float cdf = 0.f;
+            int rb = 0;
+            float vn = load(0);
+            for (int c0 = 0; c0 < V; c0 += kWave) {
+                const float v = vn;
+                vn = load(c0 + kWave);   // the next chunk's load goes out before this one's sum
+                float p;
+                bool kept;
+                chunk(c0, v, rb, p, kept);
+                for (int l = 0; l < kWave; ++l) cdf += __shfl(p, l);   // adding 0 leaves the sum as it is
+            }
+            const float target = a.uniforms[row] * cdf;
+            float run = 0.f;
+            int tok = -1, last = -1;
+            rb = 0;
+            vn = load(0);
+            for (int c0 = 0; c0 < V && tok < 0; c0 += kWave) {
+                const float v = vn;
+                vn = load(c0 + kWave);
+                float p;
+                bool kept;
+                chunk(c0, v, rb, p, kept);
+                const unsigned long long km = __ballot(kept);
+                for (int l = 0; l < kWave; ++l) {
+                    if (!((km >> l) & 1ull)) continue;
+                    run += __shfl(p, l);
+                    last = c0 + l;
+                    if (run > target) { tok = c0 + l; break; }
+                }
+            }
+            if (lane == 0) a.tokens[row] = tok >= 0 ? tok : last;
+            return;
+        }
     }
-    __syncthreads();
-    const int j0 = s_j0;
 
     // 4. the kept tokens back in token order (removed ones sort to the end), their
     //    e values carried along; S_kept by a tree sum; the draw

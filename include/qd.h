@@ -114,8 +114,8 @@ typedef struct {
     int32_t max_blocks, num_pages;
 } qd_kv;
 
-/* Workspace bytes a call needs: for a decode step over `batch` sequences whose
- * positions are all < max_ctx (prefill_tokens = 0), or a prefill of
+/* Workspace bytes a call needs: for a decode step over at most `batch` sequences
+ * whose positions are all < max_ctx (prefill_tokens = 0), or a prefill of
  * prefill_tokens tokens (batch = 1). Returns 0 if the config is invalid.
  * The caller sizes and owns this scratch once, so a step itself allocates
  * nothing (Tang page, section 5 Lowering: the generated run function performs
@@ -216,8 +216,9 @@ qd_status qd_quantize_rows_int8(const void *w, int32_t w_dtype, int64_t rows, in
  *     the largest (top_p = 1 removes none); the kept tokens, in token-id order,
  *     are drawn by the first whose running probability exceeds u * total, with
  *     u = uniforms[b] in [0, 1) supplied by the caller.
- *   tokens [batch] int32 out; -1 for a row where more than 2048 logits tie at
- *     the top-k boundary.
+ *   tokens [batch] int32 out (-1 only for a row of NaN logits, which yields no
+ *     candidate). Any number of logits may tie at the top-k boundary; past 2048
+ *     candidates the row's draw reads it in token order (slower, same rule).
  * One workgroup per row, enqueued on `stream`; no device memory is used beyond
  * the arguments. */
 qd_status qd_sample(const float *logits, int32_t batch, int32_t vocab, float temperature,

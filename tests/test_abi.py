@@ -189,6 +189,12 @@ def test_workspace_bytes_cover_every_shorter_context(lib):
         sizes = [Q.qd_workspace_bytes(cfg, B, t) for t in range(1, 2200, 7)]
         assert all(x > 0 for x in sizes)
         assert all(u <= v for u, v in zip(sizes, sizes[1:])), B
+    # and a workspace sized for a batch serves every smaller one (batch 1 adds the
+    # one-launch step's buffers at the 0.5B shape)
+    c05 = _cfg_05b(n_layers=2, vocab=4096)
+    for t in (22, 301, 4097):
+        by_batch = [Q.qd_workspace_bytes(c05, b, t) for b in range(1, 17)]
+        assert all(u <= v for u, v in zip(by_batch, by_batch[1:])), t
 
 
 def test_kv_append_checks(lib):

@@ -76,5 +76,35 @@ def test_top_k_boundary_ties():
     got = _gpu(lg, 1.0, 2, 1.0, u)
     assert got.tolist() == [sample_row(lg[0], 1.0, 2, 1.0, float(x)).token for x in u]
     assert set(got.tolist()) <= {0, 1, 2, 3}
-    flat = np.zeros((1, 4096), np.float32)         # 4096 logits tie at the boundary: no draw
-    assert _gpu(flat, 1.0, 10, 0.9, np.array([0.5], np.float32)).tolist() == [-1]
+    flat = np.zeros((3, 4096), np.float32)         # 4096 logits tie at the boundary: every one a candidate
+    u = np.array([0.5, 0.0, 0.999], np.float32)
+    got = _gpu(flat, 1.0, 10, 0.9, u)
+    assert got.tolist() == [sample_row(flat[0], 1.0, 10, 0.9, float(x)).token for x in u]
+
+
+@pytest.mark.parametrize("T,k,p", [(1.0, 10, 0.9), (0.7, 5, 0.5), (1.0, 64, 1.0), (1.5, 3, 0.3)])
+def test_more_boundary_ties_than_candidate_slots(T, k, p):
+    """Thousands of logits tie at the k-th largest value (more than the 2048
+    candidate slots in LDS), a few lie above it: the top-p cut may fall inside the
+    tied group (then the draw reads the row in token order) or among the ones above
+    (then the usual path runs over those); tokens as the oracle's."""
+    rng = np.random.default_rng(int(T * 10) + k)
+    B, V = 8, 151936
+    logits = np.full((B, V), -4.0, np.float32)
+    exact = 0
+    for b in range(B):
+        tied = rng.choice(V, size=3000 + 500 * b, replace=False)
+        logits[b, tied] = 1.0
+        above = rng.choice(np.setdiff1d(np.arange(V), tied), size=k - 1, replace=False)
+        logits[b, above] = (1.5 + 2.0 * rng.random(k - 1) * (b % 3)).astype(np.float32)
+    u = rng.random(B).astype(np.float32)
+    got = _gpu(logits, T, k, p, u)
+    for b in range(B):
+        d = sample_row(logits[b], T, k, p, float(u[b]))
+        if got[b] == d.token:
+            exact += 1
+            continue
+        assert min(d.cut_margin, d.draw_margin) < 1e-5, (b, got[b], d.token)
+        assert logits[b][got[b]] >= 1.0
+    print(f"T={T} k={k} p={p}: {exact}/{B} rows identical")
+    assert exact >= B - 1
