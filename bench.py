@@ -64,6 +64,7 @@ def _bytes_per_launch(shape, B, ctx):
     """Algorithmic bytes per launch of each kernel kind: weights read once, KV read
     once, activations counted at their float32 size."""
     from decode_step_amd import qd as Q
+    from decode_step_amd.runner import make_config
     wb, rb, gb = _dtype_bytes(shape)
     kvb = 2 if shape.kv_dtype == "bf16" else 4
     D, F, V = shape.hidden, shape.ffn, shape.vocab
@@ -79,6 +80,10 @@ def _bytes_per_launch(shape, B, ctx):
         Q.QD_K_DOWN: D * (F * wb + rb) + B * (F + 2 * D) * act,
         Q.QD_K_LMHEAD: V * (D * wb + rb) + D * gb + B * (D + V) * act,
     }
+    # batch 1 with the projection inside the attention launch: that launch also moves
+    # the projection's bytes (q|k|v rows, biases, gain, x, the projected vectors)
+    if B == 1 and Q.qd_decode_plan(make_config(shape), 1, int(np.max(ctx)) + 1).fused_qkv:
+        out[Q.QD_K_ATTN] += out.pop(Q.QD_K_QKV)
     return out
 
 
@@ -211,7 +216,7 @@ KIND_KERNELS = {
     "gate_up_gemv": [r"gemv1_kernel<[^>]*, 2, \d+>\(", r"gemm16_rows_kernel<"],
     "lm_head_gemv": [r"gemv1_kernel<[^>]*, 3, \d+>\(", r"gemm16_kernel<3,"],
     "down_gemv": [r"gemv1_kernel<[^>]*, 10, 1, 0>\(", r"gemm16_split_kernel<1, 5,"],
-    "attention": [r"attn_kernel<", r"attn_mfma_kernel<"],
+    "attention": [r"attn_kernel<", r"attn_mfma_kernel<", r"attn_fq_kernel<"],
     "step_kernel": [r"step_kernel\("],
 }
 

@@ -284,6 +284,24 @@ qd_status check_layer(const qd_config* c, const qd_layer* L, int l) {
     return QD_OK;
 }
 
+// Batch-1 steps form the q|k|v projection inside the attention launch when the
+// shape allows it (qd::attn_fq_ok); QD_FUSED_QKV=0 in the environment keeps the
+// separate projection launch (read at every call, so a process can compare the two).
+bool fused_qkv_enabled() {
+    const char* e = getenv("QD_FUSED_QKV");
+    return !(e && e[0] == '0');
+}
+
+// The attention arguments that decide the batch-1 fused projection.
+bool b1_fused_qkv(const qd_config* c, int B, bool merge_in_o, int chunk, int S, int hpw) {
+    if (B != 1 || !merge_in_o || !fused_qkv_enabled()) return false;
+    qd::AttnArgs at{};
+    at.Hq = c->n_q_heads; at.Hkv = c->n_kv_heads; at.hd = c->head_dim; at.page = c->page_size;
+    at.chunk = chunk; at.S = S; at.B = B; at.hpw = hpw; at.prefill_start = -1; at.qk_norm = c->qk_norm;
+    at.part_always = 1; at.x_dim = c->hidden;
+    return qd::attn_fq_ok(at, c->w_dtype == QD_BF16, c->kv_dtype == QD_BF16);
+}
+
 // QD_STEP_KERNEL=1 in the environment sends eligible batch-1 steps to the one-launch
 // step kernel; otherwise they take the per-op launch path (read at every call, so a
 // process can compare the two).
@@ -381,6 +399,7 @@ qd_status qd_decode_plan(const qd_config* cfg, int32_t batch, int32_t max_tokens
     out->matrix_core_attention = mfma ? 1 : 0;
     out->qkv_partials = (batch > 1 && wbf && qkv_splits > 1 && mfma) ? qkv_splits : 0;
     out->merge_in_o_proj = merge_in_o ? 1 : 0;
+    out->fused_qkv = b1_fused_qkv(cfg, batch, merge_in_o, chunk, S, hpw) ? 1 : 0;
     out->step_kernel = (batch == 1 && qd::step::step_config_ok(cfg) && qd::step::plan_step(cfg, max_tokens).ok) ? 1 : 0;
     return QD_OK;
 }
@@ -550,6 +569,7 @@ qd_status decode_step_impl(const qd_config* cfg, const qd_weights* w, const qd_k
     si.B = B; si.D = D; si.V = c.vocab; si.hd = P.hd; si.theta = c.rope_theta;
     QD_LAUNCH_K(QD_K_EMBED, qd::launch_step_input(si, wty, s), "step input");
 
+    const bool fq = b1_fused_qkv(cfg, B, merge_in_o, chunk, S, hpw);
     for (int l = 0; l < c.n_layers; ++l) {
         const qd_layer& L = w->layers_host[l];
         // RMSNorm -> q|k|v GEMV + bias
@@ -592,7 +612,13 @@ qd_status decode_step_impl(const qd_config* cfg, const qd_weights* w, const qd_k
             at.qkv_slabs = qkv_splits; at.qkv_slab_stride = (long)B * P.qkvr; at.qkv_ss = qss;
             at.qkv_bias[0] = L.bq; at.qkv_bias[1] = L.bk; at.qkv_bias[2] = L.bv; at.x_dim = D;
         }
-        QD_LAUNCH_K(QD_K_QKV, gemv(g, qd::EPI_STORE, kGemvGridCap, nullptr), "qkv gemv");
+        if (fq) {   // batch 1: the projection inside the attention launch
+            at.fq = 1; at.fq_x = x; at.fq_gain = L.attn_norm; at.fq_out = qkv; at.x_dim = D;
+            at.fq_w[0] = L.wq; at.fq_w[1] = L.wk; at.fq_w[2] = L.wv;
+            at.qkv_bias[0] = L.bq; at.qkv_bias[1] = L.bk; at.qkv_bias[2] = L.bv;
+        } else {
+            QD_LAUNCH_K(QD_K_QKV, gemv(g, qd::EPI_STORE, kGemvGridCap, nullptr), "qkv gemv");
+        }
         QD_LAUNCH_K(QD_K_ATTN, qd::launch_attention(at, wbf, kvbf, s), "attention");
         // o_proj + residual
         qd::GemvArgs go{};
@@ -602,6 +628,9 @@ qd_status decode_step_impl(const qd_config* cfg, const qd_weights* w, const qd_k
         if (merge_in_o) {   // the context is merged from the attention's splits here
             go.part = part; go.part_ml = part_ml; go.part_pos = pos;
             go.part_S = S; go.part_chunk = chunk; go.part_hd = P.hd;
+            if (fq) {   // ... and the new token's split from the projections
+                go.part_new = qkv; go.part_kv_heads = P.Hkv; go.part_scale2 = at.scale * 1.4426950408889634f;
+            }
         }
         QD_LAUNCH_K(QD_K_O, gemv(go, qd::EPI_RESID, kGemvGridCap, nullptr), "o_proj gemv");
         // RMSNorm -> gate|up GEMV -> SwiGLU

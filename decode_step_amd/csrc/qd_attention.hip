@@ -89,8 +89,121 @@ __device__ __forceinline__ void rope_lane(float (&u)[CE], const float (&pr)[CE],
     for (int e = 0; e < CE; ++e) u[e] = lower ? u[e] * c[e] - pr[e] * sn[e] : u[e] * c[e] + pr[e] * sn[e];
 }
 
-template <typename WT, typename KVT, int HD, int NP>
-__device__ __forceinline__ void attn_body(const AttnArgs& a) {
+// Batch 1 with the projection in the attention launch (AttnArgs::fq): each
+// workgroup forms 64 projection rows (one head) from x itself. 512 threads in 16
+// groups of 32 lanes; group q takes rows 4q .. 4q + 3, and lane li of a group the
+// 16-byte chunks li, li + 32, ... of those rows, at most kFqChunks of them
+// (x_dim <= kFqMaxD), so each chunk of x read from LDS serves four rows and a
+// group's load of one row covers 512 contiguous bytes. All of a lane's row loads
+// are issued before x is used; a chunk index past the row reads chunk 0 and meets
+// a block of zeros in LDS (no load under a per-lane condition).
+constexpr int kFqLanes = 32;
+constexpr int kFqRows = 4;
+constexpr int kFqChunks = kFqMaxD / (8 * kFqLanes);
+
+struct FqLoads {
+    uint4 w[kFqRows][kFqChunks];
+    float4 x;
+    uint2 gain;
+    float bias;   // of row 4q + (li & 3)
+};
+
+// Issue the loads of rows row0 .. row0 + 63 of the bf16 matrix w ([rows][x_dim]),
+// their bias (bf16, may be NULL), x and its RMSNorm gain. The small loads go first
+// and none sits under a condition (without a bias a weight is loaded and scaled by
+// 0), so that waiting for them, or for anything issued before, leaves the rows in
+// flight (loads complete in issue order). Compiler-only memory fences keep that
+// order and keep the row loads ahead of any branch that follows (left alone, the
+// compiler moves them below an early exit, behind a wait for the position).
+__device__ __forceinline__ void fq_issue(const AttnArgs& a, const void* w, const void* bias, int row0, FqLoads& f) {
+    const int tid = threadIdx.x, D = a.x_dim, KC = D / 8;
+    const int e4 = tid < D / 4 ? tid : 0;
+    const int r0 = row0 + (tid / kFqLanes) * kFqRows, li = tid % kFqLanes;
+    gbyte* wr = sgpr_gptr(w) + (long)r0 * D * 2;
+    f.x = ((const float4*)a.fq_x)[e4];
+    f.gain = ((const uint2*)a.fq_gain)[e4];
+    gbyte* bp = sgpr_gptr(bias ? bias : w);
+    f.bias = gld_scalar<uint16_t>(bp, bias ? r0 + (li & 3) : 0) * (bias ? 1.f : 0.f);
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int u = 0; u < kFqRows; ++u)
+#pragma unroll
+        for (int j = 0; j < kFqChunks; ++j) {
+            const int c = li + j * kFqLanes;
+            f.w[u][j] = gld16(wr + ((long)u * D * 2 + (c < KC ? c : 0) * 16));
+        }
+    asm volatile("" ::: "memory");
+}
+
+// The 64 rows' values r * (W (x * g)) + bias into out[64] (LDS), r = 1/sqrt(mean(x^2) + eps)
+// (the RMSNorm folded into the product, as in the GEMV kernels). Barriers inside
+// (every thread of the workgroup calls it); they are LDS-only, so loads issued
+// after the rows (the K/V rows of the attention) stay in flight across them.
+__device__ __forceinline__ void fq_finish(const AttnArgs& a, const FqLoads& f, float* out) {
+    constexpr int NWV = kAttnWaves;
+    static_assert(kFqRows == 4, "a row's bias sits in lane li & 3");
+    __shared__ __align__(16) float xg[kFqMaxD + 8];   // x * g, then one zero chunk
+    __shared__ float wsq[NWV];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+    const int D = a.x_dim, KC = D / 8;
+    float ss = 0.f;
+    if (tid < D / 4) {   // (waits for x only: the row loads stay in flight)
+        const float4 v = f.x;
+        ss = v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+        ((float4*)xg)[tid] = make_float4(v.x * bf16_to_f32(f.gain.x & 0xffffu), v.y * bf16_to_f32(f.gain.x >> 16),
+                                         v.z * bf16_to_f32(f.gain.y & 0xffffu), v.w * bf16_to_f32(f.gain.y >> 16));
+    }
+    if (tid < 8) xg[KC * 8 + tid] = 0.f;
+    ss = group_sum<kWave>(ss);
+    if (lane == 0) wsq[wave] = ss;
+    lds_barrier();
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) tot += wsq[w];
+    const float r = 1.0f / sqrtf(tot / (float)D + a.eps);
+    const int li = tid % kFqLanes;
+    float acc[kFqRows] = {};
+#pragma unroll
+    for (int j = 0; j < kFqChunks; ++j) {
+        const int c = li + j * kFqLanes;
+        const float4* xp = (const float4*)(xg + (c < KC ? c : KC) * 8);
+        const float4 x0 = xp[0], x1 = xp[1];
+#pragma unroll
+        for (int u = 0; u < kFqRows; ++u) {
+            float wf[8];
+            widen16(f.w[u][j], wf);
+            float t = acc[u];
+            t = fmaf(wf[0], x0.x, t); t = fmaf(wf[1], x0.y, t);
+            t = fmaf(wf[2], x0.z, t); t = fmaf(wf[3], x0.w, t);
+            t = fmaf(wf[4], x1.x, t); t = fmaf(wf[5], x1.y, t);
+            t = fmaf(wf[6], x1.z, t); t = fmaf(wf[7], x1.w, t);
+            acc[u] = t;
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kFqRows; ++u) acc[u] = group_sum<kFqLanes>(acc[u]);
+    const int u = li & 3;
+    const float mine = u == 0 ? acc[0] : u == 1 ? acc[1] : u == 2 ? acc[2] : acc[3];
+    if (li < kFqRows) out[(tid / kFqLanes) * kFqRows + li] = fmaf(mine, r, f.bias);
+    lds_barrier();
+}
+
+// The step's position of sequence 0 as a scalar load (the constant address space):
+// waiting for it leaves the vector loads in flight.
+__device__ __forceinline__ int fq_pos(const AttnArgs& a) {
+    return *(const __attribute__((address_space(4))) int*)a.pos;
+}
+
+// Element d of a 64-element head rotated by the step's table (pairs d and d ^ 32).
+__device__ __forceinline__ float fq_rope(const float* v, const float2* tab, int d) {
+    const float2 cs = tab[d & 31];
+    const float u = v[d], pr = v[d ^ 32];
+    return d < 32 ? u * cs.x - pr * cs.y : u * cs.x + pr * cs.y;
+}
+
+template <typename WT, typename KVT, int HD, int NP, bool FQ = false>
+__device__ __forceinline__ void attn_body(const AttnArgs& a, const int s, const int by, const int bz) {
+    static_assert(!FQ || (HD == 64 && NP <= kAttnPassesGrouped), "projection in the launch: hd 64, grouped");
     constexpr int CE = VecN<KVT>::n;
     constexpr int LPT = HD / CE;
     constexpr int TPW = kWave / LPT;
@@ -108,7 +221,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
 
     const int G = a.Hq / a.Hkv;
     const int hgroups = (G + a.hpw - 1) / a.hpw;
-    const int s = blockIdx.x, g = blockIdx.y / hgroups, hg = blockIdx.y % hgroups, b = blockIdx.z;
+    const int g = by / hgroups, hg = by % hgroups, b = bz;
     const int h0 = hg * a.hpw, nh = min(a.hpw, G - h0);   // query heads g*G + h0 .. + nh - 1
     const bool prefill = a.prefill_start >= 0;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
@@ -123,8 +236,16 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
     //    new k, loaded by every split and used by the one that holds p)
     int pgv = -1;
     if (tid < (a.chunk + PG - 1) / PG + 1 && pg0 + tid < a.max_blocks) pgv = bt[pg0 + tid];
+    // (projection in this launch: the position, then the query head's rows and x
+    // behind the page ids)
+    FqLoads fql;
+    int p_fq = 0;
+    if constexpr (FQ) {
+        p_fq = fq_pos(a);
+        fq_issue(a, a.fq_w[0], a.qkv_bias[0], (g * G + h0) * HD, fql);
+    }
     const int qkvr = (a.Hq + 2 * a.Hkv) * HD;
-    const bool pro_ld = !prefill && nh > 0 && tid < (nh + 1) * LPT;
+    const bool pro_ld = !FQ && !prefill && nh > 0 && tid < (nh + 1) * LPT;
     const int phl = tid / LPT, pl2 = tid % LPT, plp2 = pl2 ^ (LPT / 2);
     float u[CE], up[CE], cs[CE], sn[CE], vn[CE], gn[CE], gnp[CE];
     if (pro_ld) {
@@ -142,14 +263,16 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
             for (int e = 0; e < CE; ++e) { gn[e] = load_scalar<WT>(gain, pl2 * CE + e); gnp[e] = load_scalar<WT>(gain, plp2 * CE + e); }
         }
     }
-    const int p = prefill ? a.prefill_start + b : a.pos[b];
+    const int p = FQ ? p_fq : (prefill ? a.prefill_start + b : a.pos[b]);
     if (p < 0 || p >= a.capacity || a.chunk > MAXT || a.hpw > kMaxGroup || nh <= 0) return;
-    const int T = p + 1;
+    // keys 0 .. p (0 .. p - 1 when the new token is the residual product's split);
+    // split 0 always forms and publishes the rotated query head
+    const int T = FQ ? p : p + 1;
     const int ns = min(a.S, (T + a.chunk - 1) / a.chunk);
-    if (t_begin >= T) return;
+    if (t_begin >= T && !(FQ && s == 0)) return;
     const int t_end = min(T, t_begin + a.chunk);
     const int n = t_end - t_begin;
-    const bool has_new = !prefill && p >= t_begin && p < t_end;
+    const bool has_new = !FQ && !prefill && p >= t_begin && p < t_end;
     const bool pro = pro_ld && tid < (nh + (has_new ? 1 : 0)) * LPT;   // whole LPT-lane groups
     if (prefill) {   // q already normed and rotated
         for (int idx = tid; idx < nh * HD; idx += NT) {
@@ -162,7 +285,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
     //    page 0 and is masked), then every K/V row load issued back to back
     const int npg = (t_end - 1) / PG - pg0 + 1;
     if (tid < npg) spage[tid] = (pgv >= 0 && pgv < a.num_pages) ? pgv : -1;
-    __syncthreads();
+    if constexpr (FQ) lds_barrier();   // the projection rows stay in flight
+    else __syncthreads();
     // (straight-line: a pass past the split reads the zero row, so no load result
     // is moved or selected before the last load is issued)
     uint4 kraw[NP], vraw[NP];
@@ -176,6 +300,16 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
         const KVT* zr = (const KVT*)kAttnZeros + li * CE;
         kraw[i] = *(const uint4*)(ok ? (const KVT*)a.k_cache + off : zr);
         vraw[i] = *(const uint4*)(ok ? (const KVT*)a.v_cache + off : zr);
+    }
+    if constexpr (FQ) {   // the query head: project, rotate, publish (split 0)
+        __shared__ float qraw[HD];
+        fq_finish(a, fql, qraw);
+        if (tid < HD) {
+            const float q = fq_rope(qraw, a.rope, tid);
+            qs[0][tid] = q;
+            if (s == 0) a.fq_out[(g * G + h0) * HD + tid] = q;
+        }
+        if (n <= 0) return;
     }
 
     // 3. [per-head q/k RMSNorm] and RoPE of the loaded rows; the new k and v go to
@@ -227,9 +361,11 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
     const float scale2 = a.scale * kLog2e;
     const int hq0 = g * G + h0;   // first query head of this workgroup
 
-    if constexpr (NP <= kAttnPassesGrouped) {
+    if (NP <= kAttnPassesGrouped && nh > 1) {
         // Grouped heads: scores to LDS, one wave per head takes the split's max, exp
-        // and sum (each exponential once), then o = sum p v per head.
+        // and sum (each exponential once), then o = sum p v per head. (One head per
+        // workgroup takes the per-wave form below: no score round trip through LDS
+        // and no single-wave softmax.)
         __shared__ float sc[kMaxGroup][MAXT];
         __shared__ float mls[kMaxGroup][2];
         for (int hl = 0; hl < nh; ++hl) {
@@ -305,7 +441,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
         return;
     }
 
-    // 4. (one head per workgroup, many passes) per head, each wave over its own
+    // 4. (one head per workgroup: many passes, or a split that fits the grouped
+    //    form) per head, each wave over its own
     //    tokens: scores s = q.k/sqrt(hd) kept in
     //    registers, m = max s, p = exp(s - m), l = sum p, o = sum p v (the online
     //    softmax of Tang page, section 2.2, with the waves as its blocks)
@@ -384,12 +521,66 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
 // spill.
 template <typename WT, typename KVT, int HD, int NP>
 __global__ __launch_bounds__(kAttnWaves * kWave) void attn_kernel(AttnArgs a) {
-    attn_body<WT, KVT, HD, NP>(a);
+    attn_body<WT, KVT, HD, NP>(a, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 template <typename WT, typename KVT, int HD, int NP>
 __global__ __launch_bounds__(kAttnWaves * kWave) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void attn_wide_kernel(AttnArgs a) {
-    attn_body<WT, KVT, HD, NP>(a);
+    attn_body<WT, KVT, HD, NP>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
+// The new token's k or v row of one KV head (workgroup j: KV head j / 2, k when j
+// is even), projected like the query heads, k rotated, rounded to the cache type
+// and stored at the position (nanoinfer page, phase 4: keys are rotated once, on
+// insert); the stored values, widened, go to fq_out for the residual product.
+template <typename KVT>
+__device__ __forceinline__ void fq_kv_body(const AttnArgs& a, int j) {
+    constexpr int HD = 64, CE = VecN<KVT>::n, PG = kAttnPage;
+    __shared__ float row[HD], st[HD];
+    const int g = j >> 1, is_v = j & 1, tid = threadIdx.x;
+    const int p = fq_pos(a);
+    FqLoads f;
+    fq_issue(a, is_v ? a.fq_w[2] : a.fq_w[1], is_v ? a.qkv_bias[2] : a.qkv_bias[1], g * HD, f);
+    if (p < 0 || p >= a.capacity) return;
+    fq_finish(a, f, row);
+    if (tid < HD) st[tid] = is_v ? row[tid] : fq_rope(row, a.rope, tid);
+    lds_barrier();
+    if (tid < HD / CE) {
+        float v[CE];
+#pragma unroll
+        for (int e = 0; e < CE; ++e) v[e] = st[tid * CE + e];
+        const uint4 packed = pack16<KVT>(v);
+        float w[CE];
+        widen16(packed, w);
+        float* out = a.fq_out + (long)(a.Hq + is_v * a.Hkv + g) * HD + tid * CE;
+#pragma unroll
+        for (int e = 0; e < CE; ++e) out[e] = w[e];
+        const int page_id = a.block_table[p / PG];
+        if (page_id >= 0 && page_id < a.num_pages) {
+            const long off = (((long)page_id * a.Hkv + g) * PG + (p % PG)) * HD + tid * CE;
+            *(uint4*)((KVT*)(is_v ? a.v_cache : a.k_cache) + off) = packed;
+        }
+    }
+}
+
+// Batch 1, projection in the launch: fq_attn_wgs(S, Hq) attention workgroups, then
+// 2 * Hkv new-k/v workgroups. Workgroups whose ids agree mod 8 run on one XCD (one
+// L2), so the S splits of a query head, which all read its projection rows, take
+// ids 8 apart: id = 8 (S (h / 8) + s) + h % 8 (ids of heads past Hq exit at once).
+__host__ __device__ constexpr int fq_attn_wgs(int S, int Hq) { return 8 * S * ((Hq + 7) / 8); }
+
+template <typename KVT>
+__global__ __launch_bounds__(kAttnWaves * kWave) void attn_fq_kernel(AttnArgs a) {
+    static_assert(kAttnWaves * kWave == 64 / kFqRows * kFqLanes, "one 64-row block per workgroup");
+    const int n_att = fq_attn_wgs(a.S, a.Hq);
+    const int id = blockIdx.x;
+    if (id >= n_att) {
+        fq_kv_body<KVT>(a, id - n_att);
+        return;
+    }
+    const int slot = id >> 3, h = (slot / a.S) * 8 + (id & 7), s = slot % a.S;
+    if (h >= a.Hq) return;
+    attn_body<uint16_t, KVT, 64, kAttnPassesGrouped, true>(a, s, h, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -824,8 +1015,25 @@ bool attn_uses_mfma(const AttnArgs& a, int kv_is_bf16) {
            (G + 1) * (a.hd / 8) <= kAmWaves * kWave && a.chunk <= kAmChunk && (a.hd == 64 || a.hd == 128);
 }
 
+bool attn_fq_ok(const AttnArgs& a, int w_is_bf16, int kv_is_bf16) {
+    const int chunk_max = kv_is_bf16 ? attn_chunk<64, uint16_t, kAttnPassesGrouped>()
+                                     : attn_chunk<64, float, kAttnPassesGrouped>();
+    return w_is_bf16 && a.B == 1 && a.hd == 64 && a.hpw == 1 && !a.qk_norm && a.prefill_start < 0 &&
+           a.part_always && !a.compact && a.qkv_slabs == 0 && a.x_dim >= 8 && a.x_dim <= kFqMaxD &&
+           a.x_dim % 8 == 0 && a.chunk <= chunk_max && a.Hq % a.Hkv == 0;
+}
+
 hipError_t launch_attention(const AttnArgs& a, int w_is_bf16, int kv_is_bf16, hipStream_t s) {
     if (a.page != kAttnPage) return hipErrorInvalidValue;
+    if (a.fq) {
+        if (!attn_fq_ok(a, w_is_bf16, kv_is_bf16) || !a.fq_x || !a.fq_gain || !a.fq_w[0] || !a.fq_w[1] ||
+            !a.fq_w[2] || !a.fq_out)
+            return hipErrorInvalidValue;
+        const dim3 grid(fq_attn_wgs(a.S, a.Hq) + 2 * a.Hkv), block(kAttnWaves * kWave);
+        if (kv_is_bf16) hipLaunchKernelGGL(attn_fq_kernel<uint16_t>, grid, block, 0, s, a);
+        else hipLaunchKernelGGL(attn_fq_kernel<float>, grid, block, 0, s, a);
+        return hipGetLastError();
+    }
     const int G = a.Hq / a.Hkv;
     const int hgroups = (G + a.hpw - 1) / a.hpw;
     const bool mfma = attn_uses_mfma(a, kv_is_bf16);

@@ -136,6 +136,7 @@ __global__ __launch_bounds__(256) void gemv1_kernel(GemvArgs a) {
     // (always valid) indices; splits past the valid count are masked below.
     float4 ov[MS > 0 ? MS : 1];
     float2 mlv[MS > 0 ? MS : 1];
+    float4 qn, kn, vn;   // with part_new: this thread's elements of q, k_new and v_new
     int ns = 0;
     if constexpr (MS > 0) {
         const int hd = a.part_hd, S = a.part_S;
@@ -147,12 +148,22 @@ __global__ __launch_bounds__(256) void gemv1_kernel(GemvArgs a) {
             const int sc = sp < S ? sp : S - 1;
             ov[sp] = *(const float4*)(a.part + ((long)hh * S + sc) * hd + d);
         }
-        if (wave == 0) {   // wave-uniform: the (m, l) pairs are wave 0's (Hq <= 32)
-#pragma unroll
-            for (int sp = 0; sp < MS; ++sp) mlv[sp] = a.part_ml[(long)hm * S + (sp < S ? sp : S - 1)];
-        }
         const int p = a.part_pos[0];
-        ns = p >= 0 ? min(S, (p + 1 + a.part_chunk - 1) / a.part_chunk) : 0;
+        if (a.part_new) {   // every thread: its head's (m, l) pairs and its new-token elements
+#pragma unroll
+            for (int sp = 0; sp < MS; ++sp) mlv[sp] = a.part_ml[(long)hh * S + (sp < S ? sp : S - 1)];
+            const int Hq = K / hd, gk = hh / (Hq / a.part_kv_heads);
+            qn = *(const float4*)(a.part_new + e0);
+            kn = *(const float4*)(a.part_new + (long)(Hq + gk) * hd + d);
+            vn = *(const float4*)(a.part_new + (long)(Hq + a.part_kv_heads + gk) * hd + d);
+            ns = p >= 0 ? min(S, (p + a.part_chunk - 1) / a.part_chunk) : 0;
+        } else {
+            if (wave == 0) {   // wave-uniform: the (m, l) pairs are wave 0's (Hq <= 32)
+#pragma unroll
+                for (int sp = 0; sp < MS; ++sp) mlv[sp] = a.part_ml[(long)hm * S + (sp < S ? sp : S - 1)];
+            }
+            ns = p >= 0 ? min(S, (p + 1 + a.part_chunk - 1) / a.part_chunk) : 0;
+        }
     }
     // x and the gain into LDS by DMA (source indices clamped to the vectors; what
     // lands past K is never read)
@@ -192,7 +203,29 @@ __global__ __launch_bounds__(256) void gemv1_kernel(GemvArgs a) {
     if (a.zero_ptr && blockIdx.x == 0)
         for (int i = tid; i < a.zero_n; i += 256) a.zero_ptr[i] = 0u;
 
-    if constexpr (MS > 0) {
+    if (MS > 0 && a.part_new) {
+        // the same merge with the new token as one more split: score q . k_new
+        // (summed over the hd/4 threads of the head, aligned groups within a wave),
+        // weight sum 1, output v_new; every thread forms its own head's weights
+        float dq = qn.x * kn.x + qn.y * kn.y + qn.z * kn.z + qn.w * kn.w;
+        dq = a.part_hd == 64 ? group_sum<16>(dq) : group_sum<32>(dq);
+        const float sn = dq * a.part_scale2;
+        float M = sn;
+#pragma unroll
+        for (int sp = 0; sp < MS; ++sp) M = sp < ns ? fmaxf(M, mlv[sp].x) : M;
+        const float wn = __builtin_amdgcn_exp2f(sn - M);
+        float L = wn;
+        float4 o = make_float4(vn.x * wn, vn.y * wn, vn.z * wn, vn.w * wn);
+#pragma unroll
+        for (int sp = 0; sp < MS; ++sp) {
+            const float w = sp < ns ? __builtin_amdgcn_exp2f(mlv[sp].x - M) : 0.f;
+            L = fmaf(mlv[sp].y, w, L);
+            o.x = fmaf(ov[sp].x, w, o.x); o.y = fmaf(ov[sp].y, w, o.y);
+            o.z = fmaf(ov[sp].z, w, o.z); o.w = fmaf(ov[sp].w, w, o.w);
+        }
+        const float rl = 1.0f / L;
+        if (4 * tid < K) ((float4*)xs)[tid] = make_float4(o.x * rl, o.y * rl, o.z * rl, o.w * rl);
+    } else if constexpr (MS > 0) {
         // merge of the splits (Tang page, section 2.2: the online-softmax monoid):
         // with M = max m_s over the valid splits (base-2 units), head h's context is
         // sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M)
@@ -449,6 +482,9 @@ hipError_t launch_gemv1(const GemvArgs& a, int w_type, int epi, int grid_cap, in
     if (a.part) {   // residual product over the merged attention context
         if (epi != EPI_RESID || a.gain || a.part_hd % 4 || a.K % a.part_hd || a.K > 1024 ||
             a.K / a.part_hd > kG1MergeHeads || a.part_S < 1 || a.part_S > 16 || a.part_chunk < 1)
+            return hipErrorInvalidValue;
+        if (a.part_new && ((a.part_hd != 64 && a.part_hd != 128) || a.part_kv_heads < 1 ||
+                           (a.K / a.part_hd) % a.part_kv_heads))
             return hipErrorInvalidValue;
         // one shape (it covers K <= 1024 in one pass); MS = the smallest of 2, 4, 8, 16 >= S
         const int mc = w_type == 2 ? (int)G_I8_NARROW : QD_B1_OCFG;

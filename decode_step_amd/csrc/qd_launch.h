@@ -34,6 +34,14 @@ struct GemvArgs {
     const float2* part_ml;
     const int* part_pos;
     int part_S, part_chunk, part_hd;
+    // optional, with part: the new token comes as one more split, from the
+    // attention's projection output (AttnArgs::fq_out: rotated q [Hq][hd], then the
+    // stored k and v of the Hkv = part_kv_heads KV heads): its score is q . k_new
+    // times part_scale2 (1/sqrt(hd) * log2 e), its weight sum 1 and its output
+    // v_new; the other splits cover positions 0 .. pos[0] - 1
+    const float* part_new;
+    int part_kv_heads;
+    float part_scale2;
     // int8 weights: float scale of each row, per segment (SWIGLU: [0] gate, [1] up);
     // the product of row r is scaled by it
     const float* wscale[3];
@@ -104,11 +112,32 @@ struct AttnArgs {
     // KV head), from the host copy of the positions; wg_base[0] = 0, B + 1 entries
     int compact;
     int wg_base[kAttnMaxBatch + 1];
+    // optional, batch 1 (fq = 1): the q|k|v projection is formed inside the
+    // attention launch instead of read from qkv. One query head per workgroup, bf16
+    // weights, hd 64, no per-head norm, x_dim <= kFqMaxD and a multiple of 8. The
+    // grid is one-dimensional: the attention workgroups (one per split and query
+    // head, the splits of a head on one XCD), each projecting its query head from
+    // x (RMSNorm with fq_gain and eps, rows of fq_w[0], bias qkv_bias[0]) and
+    // rotating it, then 2 * Hkv workgroups that
+    // project the new token's k (rotated) and v of one KV head (fq_w[1], fq_w[2],
+    // biases qkv_bias[1], qkv_bias[2]) and store them in the cache at the position.
+    // The attention then covers the cached positions 0 .. p - 1 only, and fq_out
+    // ([Hq + 2 Hkv][hd]) receives the rotated query heads followed by the new k and
+    // v rows as stored (widened to float), from which the residual product adds
+    // the new token as one more split (needs part_always).
+    int fq;
+    const float* fq_x;
+    const void* fq_gain;
+    const void* fq_w[3];
+    float* fq_out;
 };
+constexpr int kFqMaxD = 1024;
 // attention kernel, plus the split merge kernel when S > 1
 hipError_t launch_attention(const AttnArgs& a, int w_is_bf16, int kv_is_bf16, hipStream_t s);
 // whether launch_attention takes the matrix-core grouped kernel for these arguments
 bool attn_uses_mfma(const AttnArgs& a, int kv_is_bf16);
+// whether these arguments allow the projection in the attention launch (fq)
+bool attn_fq_ok(const AttnArgs& a, int w_is_bf16, int kv_is_bf16);
 int attn_max_chunk(int hd, int kv_is_bf16, int grouped);
 int attn_max_splits();
 

@@ -53,7 +53,8 @@ class qd_kv(Structure):
 class qd_decode_plan_info(Structure):
     _fields_ = [("chunk", c_int32), ("splits", c_int32), ("heads_per_wg", c_int32),
                 ("matrix_core_attention", c_int32), ("qkv_partials", c_int32),
-                ("merge_in_o_proj", c_int32), ("step_kernel", c_int32)]
+                ("merge_in_o_proj", c_int32), ("step_kernel", c_int32),
+                ("fused_qkv", c_int32)]
 
 
 EXPORTS = ["qd_workspace_bytes", "qd_decode_plan", "qd_decode_step", "qd_decode_step_noalloc", "qd_prefill_block", "qd_kv_append", "qd_quantize_rows_int8",
@@ -71,7 +72,7 @@ class QdError(RuntimeError):
         self.status = status
 
 
-ABI_VERSION = 3   # QD_ABI_VERSION of the header this binding follows
+ABI_VERSION = 4   # QD_ABI_VERSION of the header this binding follows
 
 
 def load(path: str = LIB_PATH) -> ctypes.CDLL:

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define QD_ABI_VERSION 3
+#define QD_ABI_VERSION 4
 
 typedef enum {
     QD_OK = 0,
@@ -269,6 +269,9 @@ typedef struct {
     int32_t merge_in_o_proj;        /* 1: batch 1, o_proj merges the splits (no merge launch) */
     int32_t step_kernel;            /* 1: batch 1 eligible for the one-launch step, taken      *
                                      * when QD_STEP_KERNEL=1 is set in the environment        */
+    int32_t fused_qkv;              /* 1: batch 1, the q|k|v projection runs inside the        *
+                                     * attention launch (no projection launch); off when      *
+                                     * QD_FUSED_QKV=0 is set in the environment               */
 } qd_decode_plan_info;
 qd_status qd_decode_plan(const qd_config *cfg, int32_t batch, int32_t max_tokens,
                          qd_decode_plan_info *out);

@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol(lib):
     for n in declared_functions():
         assert n in exported, n
         assert hasattr(lib, n)
-    assert lib.qd_abi_version() == Q.ABI_VERSION == 3
+    assert lib.qd_abi_version() == Q.ABI_VERSION == 4
 
 
 def test_struct_layout_matches_the_header(tmp_path):
@@ -318,6 +318,24 @@ def test_decode_plan_paths(lib):
     # the step kernel takes head_dim 64, bf16 only
     assert Q.qd_decode_plan(hd128, 1, 100).step_kernel == 0
     assert Q.qd_decode_plan(_cfg_05b(kv_dtype=Q.QD_F32), 1, 100).step_kernel == 0
+
+
+def test_decode_plan_fused_projection(lib, monkeypatch):
+    """Batch 1 at the 0.5B shape (bf16, head_dim 64, hidden <= 1024, no per-head
+    norm) projects q|k|v inside the attention launch; every other case, and
+    QD_FUSED_QKV=0, keeps the projection launch."""
+    monkeypatch.delenv("QD_FUSED_QKV", raising=False)
+    for t in (1, 144, 145, 513, 2304):
+        assert Q.qd_decode_plan(_cfg_05b(), 1, t).fused_qkv == 1, t
+    assert Q.qd_decode_plan(_cfg_05b(), 2, 513).fused_qkv == 0                      # batch > 1
+    assert Q.qd_decode_plan(_cfg_05b(w_dtype=Q.QD_I8), 1, 513).fused_qkv == 0       # int8 rows
+    assert Q.qd_decode_plan(_cfg_05b(w_dtype=Q.QD_F32, kv_dtype=Q.QD_F32), 1, 100).fused_qkv == 0
+    assert Q.qd_decode_plan(_cfg_05b(qk_norm=1), 1, 513).fused_qkv == 0             # per-head norm
+    assert Q.qd_decode_plan(_cfg_05b(hidden=1536, ffn=8960, n_q_heads=12), 1, 513).fused_qkv == 0
+    assert Q.qd_decode_plan(_cfg(hidden=512, ffn=1024, n_q_heads=8, n_kv_heads=2, head_dim=128,
+                                 vocab=1000, n_layers=2), 1, 100).fused_qkv == 0    # head_dim 128
+    monkeypatch.setenv("QD_FUSED_QKV", "0")
+    assert Q.qd_decode_plan(_cfg_05b(), 1, 513).fused_qkv == 0
 
 
 def test_decode_plan_checks(lib):
