@@ -470,7 +470,6 @@ qd_status decode_step_impl(const qd_config* cfg, const qd_weights* w, const qd_k
     for (int l = 0; l < c.n_layers; ++l)
         if ((st = check_layer(cfg, &w->layers_host[l], l)) != QD_OK) return st;
     if (c.w_dtype == QD_I8) {
-        if (batch != 1) return fail(QD_EUNSUPPORTED, "int8 weights: batch-1 decode steps only (batch %d)", batch);
         if (tokens && !w->s_embed) return fail(QD_EINVAL, "int8 weights: s_embed is NULL");
         if (want_head && !w->s_lm_head) return fail(QD_EINVAL, "int8 weights: s_lm_head is NULL");
     }
@@ -515,12 +514,12 @@ qd_status decode_step_impl(const qd_config* cfg, const qd_weights* w, const qd_k
     auto gemv = [&](const qd::GemvArgs& g, int epi, int grid_cap, int* grid_out) {
         if (B == 1) return qd::launch_gemv1(g, wty, epi, epi == qd::EPI_LOGITS ? grid_cap : kGemv1GridCap,
                                             grid_out, s);
-        if (wbf) {
+        if (wty == QD_BF16) {
             qd::GemvArgs m = g;
             m.kt = qd::gemm16_chunk(g.K);
             return qd::launch_gemm16(m, epi, grid_cap, grid_out, s);
         }
-        return qd::launch_gemv(g, wbf, epi, grid_cap, grid_out, s);
+        return qd::launch_gemv(g, wty, epi, grid_cap, grid_out, s);   // float or int8 rows
     };
 
     // batch 1: the one-launch step, when the config, the device and the position allow
@@ -607,7 +606,7 @@ qd_status decode_step_impl(const qd_config* cfg, const qd_weights* w, const qd_k
         }
         // batch 2..16 on the matrix cores: q|k|v as K-range partial products, which
         // the attention kernel finishes (RMSNorm scale, bias) as it loads them
-        if (B > 1 && wbf && qkv_splits > 1 && qd::attn_uses_mfma(at, kvbf)) {
+        if (B > 1 && wty == QD_BF16 && qkv_splits > 1 && qd::attn_uses_mfma(at, kvbf)) {
             g.ss_out = qss;
             at.qkv_slabs = qkv_splits; at.qkv_slab_stride = (long)B * P.qkvr; at.qkv_ss = qss;
             at.qkv_bias[0] = L.bq; at.qkv_bias[1] = L.bk; at.qkv_bias[2] = L.bv; at.x_dim = D;

@@ -8,7 +8,9 @@
 // cross-lane shuffles, and the bias / residual / SwiGLU / argmax epilogue runs
 // on the lane holding the total (Tang page, section 2.3: epilogues on the
 // reducing thread; gate|up as one sibling reduction reading the normed input
-// once).
+// once). Rows are float, bf16 or int8 codes with one float scale per row
+// (nanoinfer page, phase 6: per-row symmetric weight-only int8), the scale
+// applied to the finished dot product; gains and biases of int8 models are bf16.
 #include "qd_device.h"
 #include "qd_launch.h"
 
@@ -26,6 +28,8 @@ int gemv_rows_per_tile(int K) { return K <= 2048 ? rows_per_tile<16>() : rows_pe
 template <typename WT, int LPR, int BM, int EPI>
 __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
     constexpr int CE = VecN<WT>::n;
+    using GT = typename GainT<WT>::type;      // gains and biases
+    constexpr bool I8 = sizeof(WT) == 1;
     constexpr int RPW = kWave / LPR;
     constexpr int UR = kGemvUR;
     constexpr int RPT = 4 * RPW * UR;
@@ -54,7 +58,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
         for (int idx = tid; idx < B * kt; idx += kGemvThreads) {
             int b = idx / kt, k = idx - b * kt;
             float v = a.x[(long)b * K + k0 + k];
-            if (a.gain) v = v * rscale[b] * load_scalar<WT>(a.gain, k0 + k);
+            if (a.gain) v = v * rscale[b] * load_scalar<GT>(a.gain, k0 + k);
             xs[b * kt + k] = v;
         }
     };
@@ -153,24 +157,31 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
             for (int u = 0; u < UR; ++u) {
                 const int r = rows[u];
                 if (r >= N) continue;
-                float bias = 0.f;
-                if (EPI == EPI_STORE) {
+                float bias = 0.f, sc0 = 1.f, sc1 = 1.f;   // int8: the rows' scales
+                {
                     const bool s0 = r < a.seg_end[0], s1 = r < a.seg_end[1];
-                    const void* bsel = s0 ? a.bias[0] : (s1 ? a.bias[1] : a.bias[2]);
                     const int base = s0 ? 0 : (s1 ? a.seg_end[0] : a.seg_end[1]);
-                    if (bsel) bias = load_scalar<WT>(bsel, r - base);
+                    if (EPI == EPI_STORE) {
+                        const void* bsel = s0 ? a.bias[0] : (s1 ? a.bias[1] : a.bias[2]);
+                        if (bsel) bias = load_scalar<GT>(bsel, r - base);
+                    }
+                    if (I8) {
+                        if (EPI == EPI_SWIGLU) { sc0 = a.wscale[0][r]; sc1 = a.wscale[1][r]; }
+                        else sc0 = (s0 ? a.wscale[0] : (s1 ? a.wscale[1] : a.wscale[2]))[r - base];
+                    }
                 }
 #pragma unroll
                 for (int b = 0; b < BM; ++b) {
                     if (b >= B) break;
                     float* yp = a.y + (long)b * N + r;
-                    if (EPI == EPI_STORE) *yp = acc[u][0][b] + bias;
-                    else if (EPI == EPI_RESID) *yp = *yp + acc[u][0][b];
-                    else if (EPI == EPI_SWIGLU) *yp = silu(acc[u][0][b]) * acc[u][NW - 1][b];
+                    const float v0 = I8 ? acc[u][0][b] * sc0 : acc[u][0][b];
+                    if (EPI == EPI_STORE) *yp = v0 + bias;
+                    else if (EPI == EPI_RESID) *yp = *yp + v0;
+                    else if (EPI == EPI_SWIGLU) *yp = silu(v0) * (I8 ? acc[u][NW - 1][b] * sc1 : acc[u][NW - 1][b]);
                     else {
-                        *yp = acc[u][0][b];
-                        if (better(acc[u][0][b], r, best_v[b], best_i[b])) {
-                            best_v[b] = acc[u][0][b];
+                        *yp = v0;
+                        if (better(v0, r, best_v[b], best_i[b])) {
+                            best_v[b] = v0;
                             best_i[b] = r;
                         }
                     }
@@ -217,18 +228,24 @@ static hipError_t gemv_dispatch_bm(const GemvArgs& a, int epi, int grid, size_t 
     return gemv_dispatch_epi<WT, LPR, 16>(a, epi, grid, shm, s);
 }
 
-hipError_t launch_gemv(const GemvArgs& a, int w_is_bf16, int epi, int grid_cap, int* grid_out,
+hipError_t launch_gemv(const GemvArgs& a, int w_type, int epi, int grid_cap, int* grid_out,
                        hipStream_t s) {
+    if (w_type == 2 && (a.K % 16 || (a.kt < a.K && a.kt % 16) || !a.wscale[0] ||
+                        (epi == EPI_SWIGLU && !a.wscale[1])))
+        return hipErrorInvalidValue;
     const int rpt = gemv_rows_per_tile(a.K);
     const int tiles = (a.N + rpt - 1) / rpt;
     const int grid = tiles < grid_cap ? tiles : grid_cap;
     if (grid_out) *grid_out = grid;
     const size_t shm = (size_t)a.B * (size_t)(a.kt < a.K ? a.kt : a.K) * sizeof(float);
-    if (a.K <= 2048)
-        return w_is_bf16 ? gemv_dispatch_bm<uint16_t, 16>(a, epi, grid, shm, s)
-                         : gemv_dispatch_bm<float, 16>(a, epi, grid, shm, s);
-    return w_is_bf16 ? gemv_dispatch_bm<uint16_t, 64>(a, epi, grid, shm, s)
-                     : gemv_dispatch_bm<float, 64>(a, epi, grid, shm, s);
+    if (a.K <= 2048) {
+        if (w_type == 2) return gemv_dispatch_bm<int8_t, 16>(a, epi, grid, shm, s);
+        return w_type == 1 ? gemv_dispatch_bm<uint16_t, 16>(a, epi, grid, shm, s)
+                           : gemv_dispatch_bm<float, 16>(a, epi, grid, shm, s);
+    }
+    if (w_type == 2) return gemv_dispatch_bm<int8_t, 64>(a, epi, grid, shm, s);
+    return w_type == 1 ? gemv_dispatch_bm<uint16_t, 64>(a, epi, grid, shm, s)
+                       : gemv_dispatch_bm<float, 64>(a, epi, grid, shm, s);
 }
 
 __global__ __launch_bounds__(256) void copy_kernel(const float* src, float* dst, long n) {

@@ -51,7 +51,9 @@ struct GemvArgs {
     // partial sums of squares of x over each range; the consumer finishes
     float* ss_out;
 };
-hipError_t launch_gemv(const GemvArgs& a, int w_is_bf16, int epi, int grid_cap, int* grid_out,
+// batch 1..16 on the vector ALUs (qd_decode.hip); w_type 0 float, 1 bf16, 2 int8 rows
+// with a.wscale (K and a.kt multiples of 16)
+hipError_t launch_gemv(const GemvArgs& a, int w_type, int epi, int grid_cap, int* grid_out,
                        hipStream_t s);
 // batch-1 fast path (qd_gemv.hip); part_val/part_idx hold one entry per workgroup;
 // w_type 0 float, 1 bf16, 2 int8 rows with a.wscale (K a multiple of 16)

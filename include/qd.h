@@ -75,7 +75,8 @@ typedef struct {
     int32_t w_dtype;   /* qd_dtype of matrices, biases, gains and the embedding; QD_I8:
                         * int8 matrices and embedding (per-row scales), bf16 biases
                         * and gains (nanoinfer, phase 6: norms and biases are never
-                        * quantized); batch-1 decode steps only                     */
+                        * quantized); decode steps only (batch 1..16; prefill blocks
+                        * need QD_BF16)                                             */
     int32_t kv_dtype;  /* qd_dtype of the KV cache                                      */
 } qd_config;
 

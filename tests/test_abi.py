@@ -243,7 +243,9 @@ def test_int8_checks(lib):
     f.layers[0].s_up = None
     _expect(f.decode(), Q.QD_EINVAL)                       # missing row scales
     f2 = Fixture(_cfg(w_dtype=Q.QD_I8), pos=(3, 4))
-    _expect(f2.decode(), Q.QD_EUNSUPPORTED)                # batch-1 steps only
+    _expect(f2.decode(), Q.QD_EINVAL)                      # batch 2 takes int8 rows too: s_embed NULL
+    f2.w.s_embed = f2.w.s_lm_head = FAKE
+    _expect(f2.decode(ws_bytes=16), Q.QD_EWORKSPACE)       # ... and passes every int8 check
     _expect(_prefill(Fixture(_cfg(w_dtype=Q.QD_I8))), Q.QD_EUNSUPPORTED)
 
 

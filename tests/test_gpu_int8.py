@@ -4,11 +4,12 @@ oracle.
 
 * qd_quantize_rows_int8: codes and scales bit-exact against oracle.quant on
   random bf16 and float32 matrices, including planted ties.
-* qd_decode_step with w_dtype = QD_I8 at batch 1: the GPU runs the int8 codes
-  with their row scales; the oracle runs the same codes dequantized (the page's
-  "simulated INT8", the same function). Tolerance 2e-3 max rel err per tensor,
-  as for bf16 weights (the KV cache is bf16 on both sides; what differs is
-  float32 accumulation against float64); greedy tokens identical.
+* qd_decode_step with w_dtype = QD_I8 at batch 1 and at batches of 2..16 (the
+  batched projections on the vector ALUs): the GPU runs the int8 codes with their
+  row scales; the oracle runs the same codes dequantized (the page's "simulated
+  INT8", the same function). Tolerance 2e-3 max rel err per tensor, as for bf16
+  weights (the KV cache is bf16 on both sides; what differs is float32
+  accumulation against float64); greedy tokens identical.
 """
 from dataclasses import replace
 
@@ -68,9 +69,10 @@ def test_quantizer_bit_exact(dtype):
 
 def _run(case, pos, tok):
     sh = case.shape
-    logits = torch.full((1, sh.vocab), float("nan"), device="cuda")
-    nxt = torch.full((1,), -1, dtype=torch.int32, device="cuda")
-    layer_out = torch.full((sh.n_layers, 1, sh.hidden), float("nan"), device="cuda")
+    B = len(pos)
+    logits = torch.full((B, sh.vocab), float("nan"), device="cuda")
+    nxt = torch.full((B,), -1, dtype=torch.int32, device="cuda")
+    layer_out = torch.full((sh.n_layers, B, sh.hidden), float("nan"), device="cuda")
     case.runner.step(np.asarray(pos, np.int32), dev_i32(pos), tokens=dev_i32(tok), logits=logits,
                      next_tokens=nxt, layer_out=layer_out)
     torch.cuda.synchronize()
@@ -82,7 +84,7 @@ def _int8_case(shape, ctx, seed, extra=4):
     case = make_case(shape, ctx, seed=seed, extra=extra, random_order=True)
     wq = quantize_weights_int8(case.w)
     torch.cuda.synchronize()
-    case.runner = DecodeRunner(shape, wq, case.kv.k, case.kv.v, case.kv.block_table, max_batch=1,
+    case.runner = DecodeRunner(shape, wq, case.kv.k, case.kv.v, case.kv.block_table, max_batch=len(ctx),
                                max_ctx=int(np.max(ctx)) + extra + 1)
     deq, codes = quantized_model(case.host_w)
     # the codes the GPU runs are the oracle's codes
@@ -108,14 +110,38 @@ def test_small_int8_decode_step(ctx0):
     assert int(nxt.cpu()[0]) == int(ref.next_tokens[0])
 
 
-def test_int8_rejects_batches_and_missing_scales():
+def _cache_matches(case):
+    from tests._gpu_setup import kv_matches
+    return all(kv_matches(dev, host) for l in range(case.shape.n_layers)
+               for dev, host in ((case.kv.k[l], case.k_host[l]), (case.kv.v[l], case.v_host[l])))
+
+
+@pytest.mark.parametrize("ctx_list", [[5, 9], [0, 17, 64, 130, 33], [3 * b + 1 for b in range(16)]])
+def test_small_int8_batched_decode_step(ctx_list):
+    """Batches of 2..16 with ragged positions (0, on and around page edges): every
+    layer's output and the logits within 2e-3, tokens identical, the new K/V stored
+    within one bf16 step of the oracle's."""
+    ctx = np.array(ctx_list, np.int32)
+    B = len(ctx)
+    case, deq = _int8_case(SMALL_I8, ctx, seed=60 + B)
+    tok = synth.make_tokens(B, SMALL_I8.vocab, seed=60 + B)
+    print(f"int8 batch {B} ctx {ctx_list}", flush=True)
+    logits, nxt, layer_out = _run(case, ctx, tok)
+    ow = OracleWeights(SMALL_I8, deq, cache_layers=True)
+    ref = decode_step(SMALL_I8, ow, case.k_host, case.v_host, case.kv.block_table, ctx, tokens=tok)
+    assert rel_err(logits.cpu().numpy(), ref.logits) <= 2e-3
+    for l in range(SMALL_I8.n_layers):
+        assert rel_err(layer_out[l].cpu().numpy(), ref.layer_out[l]) <= 2e-3, l
+    assert list(nxt.cpu().numpy()) == list(ref.next_tokens)
+    assert _cache_matches(case)
+
+
+def test_int8_rejects_missing_scales():
     from decode_step_amd import qd as Q
     ctx = np.array([5, 9], np.int32)
-    case, _ = _int8_case(SMALL_I8, ctx[:1], seed=3)
-    st = case.runner.step(ctx, dev_i32(ctx), tokens=dev_i32([1, 2]), raise_on_error=False)
-    assert st == Q.QD_EUNSUPPORTED
+    case, _ = _int8_case(SMALL_I8, ctx, seed=3)
     case.runner.layers[1].s_up = None
-    st = case.runner.step(ctx[:1], dev_i32(ctx[:1]), tokens=dev_i32([1]), raise_on_error=False)
+    st = case.runner.step(ctx, dev_i32(ctx), tokens=dev_i32([1, 2]), raise_on_error=False)
     assert st == Q.QD_EINVAL
 
 
@@ -142,3 +168,30 @@ def test_qwen2_0p5b_int8_b1_past512_greedy():
         pos = pos + 1
     print(f"int8 greedy: worst logits rel err {worst:.3e}")
     assert worst <= 2e-3
+
+
+@pytest.mark.timeout(600)
+def test_qwen2_0p5b_int8_batch4_paged():
+    """The 0.5B shape with int8 rows at batch 4 over a random paged block table
+    (contexts 100..700): logits and every layer's output within 2e-3, tokens
+    identical, over 3 greedy steps."""
+    sh = S.QWEN2_0P5B_INT8_B1_PAST512.shape
+    ctx = np.array([100, 371, 700, 512], np.int32)
+    case, deq = _int8_case(sh, ctx, seed=77, extra=4)
+    del case.w
+    tok = synth.make_tokens(4, sh.vocab, seed=77)
+    ow = OracleWeights(sh, deq, cache_layers=True)
+    pos = ctx.copy()
+    for step in range(3):
+        print(f"int8 0.5B batch 4 step {step}", flush=True)
+        logits, nxt, layer_out = _run(case, pos, tok)
+        ref = decode_step(sh, ow, case.k_host, case.v_host, case.kv.block_table, pos, tokens=tok)
+        err = rel_err(logits.cpu().numpy(), ref.logits)
+        print(f"  logits rel err {err:.3e}", flush=True)
+        assert err <= 2e-3
+        if step == 0:
+            for l in range(sh.n_layers):
+                assert rel_err(layer_out[l].cpu().numpy(), ref.layer_out[l]) <= 2e-3, l
+        assert list(nxt.cpu().numpy()) == list(ref.next_tokens), step
+        tok = ref.next_tokens.astype(np.int32)
+        pos = pos + 1
