@@ -107,6 +107,12 @@ QWEN2_0P5B_INT8_B1_PAST512 = Workload(
     name="qwen2-0.5b-int8-b1-past512",
     shape=replace(QWEN2_0P5B, w_dtype="i8"), kind="decode", batch=1, past=512, greedy_steps=8)
 
+# The batch-16 paged step with per-row int8 weights.
+QWEN2_0P5B_INT8_B16_PAGED = Workload(
+    name="qwen2-0.5b-int8-b16-ctx128to4096-paged",
+    shape=replace(QWEN2_0P5B, w_dtype="i8"), kind="decode", batch=16, ctx_range=(128, 4096),
+    paged_random=True, greedy_steps=4)
+
 # 8B-class shape with per-head q/k RMSNorm, batch 1, 4096 cached tokens.
 QWEN_8B_B1_PAST4096 = Workload(
     name="qwen-8b-qknorm-bf16-b1-past4096",
@@ -127,7 +133,7 @@ QWEN2_SAMPLER_B16 = Workload(
 WORKLOADS = {w.name: w for w in (QWEN2_BLOCK_F32_PAST16, QWEN2_0P5B_B1_PAST512,
                                  QWEN2_0P5B_B16_PAGED, QWEN_8B_B1_PAST4096,
                                  QWEN_8B_BLOCK_PREFILL512, QWEN2_0P5B_INT8_B1_PAST512,
-                                 QWEN2_SAMPLER_B16)}
+                                 QWEN2_0P5B_INT8_B16_PAGED, QWEN2_SAMPLER_B16)}
 
 
 def tiny_shape(**over) -> ModelShape:
