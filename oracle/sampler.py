@@ -12,6 +12,8 @@ nanoinfer page, phase 5 (sampling.py: temperature, top-k, top-p, seeded draw):
     tied pair the higher index counts as the more likely;
   * the draw is an inverse-CDF search, which does not need the probabilities to
     sum to exactly 1.0.
+  * "top-p alone" (the page's per-token cost table) is the same pipeline without
+    the top-k step: top_k <= 0 (or >= the vocabulary) keeps every token.
 Readings where the page is silent: the arithmetic is float32, as the page's
 tensors are, with every running sum taken one term at a time (the printed
 0.4999997913837433 is exactly that sum); top-k keeps every token whose logit is
@@ -53,7 +55,7 @@ def sample_row(logits: np.ndarray, temperature: float, top_k: int, top_p: float,
         t = int(argmax_first(lg[None, :])[0])
         return Draw(t, np.array([t]), np.inf, np.inf)
     V = lg.size
-    k = min(int(top_k), V)
+    k = V if int(top_k) <= 0 else min(int(top_k), V)             # top_k <= 0: no top-k ("top-p alone")
     kth = np.sort(lg)[::-1][k - 1]
     cand = np.nonzero(lg >= kth)[0]                              # top-k, ties kept; ids ascending
     z = (lg[cand] / np.float32(temperature)).astype(np.float32)  # temperature

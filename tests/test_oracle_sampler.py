@@ -67,3 +67,22 @@ def test_temperature_acts_before_top_p():
     # a nucleus cut on the raw logits and then rescaled would not change with T
     raw = len(sample_row(lg, 1.0, 1000, 0.8, 0.5).kept)
     assert sizes[0] != raw or sizes[-1] != raw
+
+
+def test_top_p_alone_is_the_whole_vocabulary():
+    # "top-p alone": no top-k step, so every token is a candidate; the page's
+    # 100-equiprobable example keeps the same 50 without a top-k
+    lg = np.zeros(100, np.float32)
+    for k in (0, -1, 100, 1000):
+        assert sample_row(lg, 1.0, k, 0.5, 0.0).kept.tolist() == list(range(50, 100))
+    # top-p alone at p = 1 keeps every token, and the draw is the inverse CDF of the
+    # full softmax: u just below the first token's probability picks token 0
+    lg = np.array([0.0, np.log(3.0), np.log(6.0)], np.float32)    # probabilities 0.1, 0.3, 0.6
+    assert sample_row(lg, 1.0, 0, 1.0, 0.0).kept.tolist() == [0, 1, 2]
+    assert sample_row(lg, 1.0, 0, 1.0, 0.09).token == 0
+    assert sample_row(lg, 1.0, 0, 1.0, 0.11).token == 1
+    assert sample_row(lg, 1.0, 0, 1.0, 0.41).token == 2
+    # p = 0.65, 1 - p = 0.35: of the ascending sums 0.1, 0.4, 1.0 only 0.1 is <= 0.35,
+    # so token 0 alone goes
+    d = sample_row(lg, 1.0, 0, 0.65, 0.0)
+    assert d.kept.tolist() == [1, 2]
