@@ -744,8 +744,9 @@ qd_status qd_sample(const float* logits, int32_t batch, int32_t vocab, float tem
     if (!(top_p > 0.f && top_p <= 1.f)) return fail(QD_EINVAL, "top_p %g not in (0, 1]", (double)top_p);
     if (temperature > 0.f) {
         if (!uniforms) return fail(QD_EINVAL, "uniforms is NULL");
-        if (top_k < 1 || top_k > qd::kSampleMaxK)
-            return fail(QD_EUNSUPPORTED, "top_k %d: sampling takes 1 <= top_k <= %d", top_k, qd::kSampleMaxK);
+        if (top_k > qd::kSampleMaxK && top_k < vocab)
+            return fail(QD_EUNSUPPORTED, "top_k %d: sampling takes 1 <= top_k <= %d, or top_k <= 0 / >= vocab %d "
+                        "(no top-k)", top_k, qd::kSampleMaxK, vocab);
     }
     if (!aligned4(logits) || !aligned4(tokens) || (uniforms && !aligned4(uniforms)))
         return fail(QD_EALIGN, "logits, uniforms or tokens not 4-byte aligned");

@@ -290,7 +290,7 @@ struct SampleArgs {
     const float* logits;    // [B][V]
     int B, V;
     float temperature;      // 0: argmax
-    int top_k;              // 1 .. kSampleMaxK when temperature > 0
+    int top_k;              // 1 .. kSampleMaxK when temperature > 0, or <= 0 / >= V: no top-k
     float top_p;            // (0, 1]; 1 keeps every top-k candidate
     float one_minus_p;      // the top-p threshold, float32(1 - p) formed in double
     const float* uniforms;  // [B] in [0, 1)

@@ -75,6 +75,257 @@ __device__ __forceinline__ void top_bin(const int* hist, int nb, int need, int l
     above = __shfl(a, src);
 }
 
+// Top-p over the whole vocabulary (top_k <= 0 or >= V), one workgroup per row,
+// every step a pass over the row (no candidate list):
+// A. max logit; z = logit / T keeps the order, so max z = (max logit) / T.
+// B. S = sum_j e_j, e_j = exp(z_j - max z) (tree sum).
+// C. the top-p cut, as a radix select by probability mass over the logits'
+//    order keys (11, 11, 10 bits): each digit's bins hold the mass m_j = e_j / S
+//    of their logits (LDS float adds), scanned from the lowest key up for the
+//    first bin where the running mass passes 1 - p. This gives the boundary key,
+//    the mass below it and the number of logits tied at it; the tied ones (equal
+//    z, equal m) are removed one at a time, in token-id order (the stable
+//    ascending order), while the running sum stays <= 1 - p, and the largest
+//    always stays.
+// D. S_kept over the kept tokens; the draw in token-id order: each wave runs over
+//    its own contiguous range of ids in chunks of 64 (lane order = id order, a
+//    wave prefix sum per chunk) for its range's total, then the wave whose range
+//    holds the first running value > u * total finds the token in it.
+// The masses are summed in a different order than one at a time, so a row whose
+// cut or draw lies within that rounding of a boundary may fall on its other side.
+template <typename Scan>
+__device__ __forceinline__ void sample_whole_vocab(const SampleArgs& a, int row, const float* lg, Scan&& scan, int* hist,
+                                                float* mass, unsigned long long* ids, float* s_red) {
+    __shared__ uint32_t s_key;
+    __shared__ float s_base;
+    __shared__ int s_idcut, s_cnt2;
+    __shared__ float s_wtot[kSampleThreads / kWave];
+    __shared__ int s_tok;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+    constexpr int NWV = kSampleThreads / kWave;
+    const int V = a.V;
+    const float T = a.temperature;
+    auto block_red = [&](float v, bool is_max) {   // every thread returns the workgroup's sum or max
+        v = is_max ? group_max<kWave>(v) : group_sum<kWave>(v);
+        __syncthreads();
+        if (lane == 0) s_red[wave] = v;
+        __syncthreads();
+        float t = is_max ? -INFINITY : 0.f;
+        for (int w = 0; w < NWV; ++w) t = is_max ? fmaxf(t, s_red[w]) : t + s_red[w];
+        return t;
+    };
+    // A, B
+    float m = -INFINITY;
+    scan([&](int, float v) { m = fmaxf(m, v); });
+    const float lmax = block_red(m, true);
+    if (!(lmax > -INFINITY)) {   // every logit NaN or -inf: no candidate
+        if (tid == 0) a.tokens[row] = -1;
+        return;
+    }
+    const float zmax = __fdiv_rn(lmax, T);
+    auto e_of = [&](float v) { return expf(__fdiv_rn(v, T) - zmax); };
+    float part = 0.f;
+    scan([&](int, float v) { part += e_of(v); });
+    const float S = block_red(part, false);
+    // C
+    const uint32_t kmax = order_key(lmax);
+    if (tid == 0) { s_key = 0u; s_base = 0.f; s_idcut = 0; }
+    if (a.top_p < 1.f) {
+        const float thr = a.one_minus_p;
+        uint32_t prefix = 0;
+        float base = 0.f;
+        int n_t = 0;
+        for (int d = 0; d < 3; ++d) {
+            const int width = d < 2 ? 11 : 10, sh = d == 0 ? 21 : (d == 1 ? 10 : 0), nb = 1 << width, hs = sh + width;
+            for (int j = tid; j < nb; j += kSampleThreads) { mass[j] = 0.f; hist[j] = 0; }
+            __syncthreads();
+            scan([&](int, float v) {
+                const uint32_t key = order_key(v);
+                if (hs >= 32 || (key >> hs) == prefix) {
+                    const int bin = (int)((key >> sh) & (uint32_t)(nb - 1));
+                    atomicAdd(&mass[bin], __fdiv_rn(e_of(v), S));
+                    atomicAdd(&hist[bin], 1);
+                }
+            });
+            __syncthreads();
+            if (wave == 0) {
+                // lane l holds bins [l * per, (l + 1) * per); the first lane whose running
+                // mass passes thr, then the first such bin in it (a nonempty one)
+                const int per = nb / kWave, lo = lane * per;
+                float mine = 0.f;
+                int last_ne = -1;
+                for (int j = lo; j < lo + per; ++j) { mine += mass[j]; if (hist[j]) last_ne = j; }
+                float incl = mine;
+#pragma unroll
+                for (int o = 1; o < kWave; o <<= 1) {
+                    const float t = __shfl_up(incl, o);
+                    if (lane >= o) incl += t;
+                }
+                const float excl = incl - mine;
+                const unsigned long long pass = __ballot(base + incl > thr);
+                const unsigned long long ne = __ballot(last_ne >= 0);
+                // no lane passes (rounding): the highest nonempty bin
+                const int src = pass ? __ffsll((long long)pass) - 1 : 63 - __clzll((long long)ne);
+                int bin = -1;
+                float below = 0.f;
+                if (lane == src) {
+                    float c = base + excl;
+                    for (int j = lo; j < lo + per; ++j) {
+                        if (hist[j] && c + mass[j] > thr) { bin = j; below = c; break; }
+                        c += mass[j];
+                    }
+                    if (bin < 0) {   // rounding: the last nonempty bin of the range
+                        c = base + excl;
+                        for (int j = lo; j < lo + per; ++j) { if (hist[j]) { bin = j; below = c; } c += mass[j]; }
+                    }
+                }
+                bin = max(__shfl(bin, src), 0);
+                below = __shfl(below, src);
+                if (lane == 0) { s_key = (prefix << width) | (uint32_t)bin; s_base = below; s_cnt2 = hist[bin]; }
+            }
+            __syncthreads();
+            prefix = s_key;
+            base = s_base;
+            n_t = s_cnt2;
+            __syncthreads();
+        }
+        // the tied logits at the boundary key, removed one at a time while the running
+        // sum stays <= thr; the largest always stays
+        if (tid == 0) {
+            const float vk = __uint_as_float(prefix ^ ((prefix & 0x80000000u) ? 0x80000000u : 0xffffffffu));
+            const float mk = __fdiv_rn(e_of(vk), S);
+            float c = base;
+            int r = 0;
+            while (r < n_t) {
+                const float c2 = c + mk;
+                if (!(c2 <= thr)) break;
+                c = c2;
+                ++r;
+            }
+            if (r == n_t && prefix == kmax) r = n_t - 1;
+            s_cnt2 = r;        // tied tokens removed (the lowest ids)
+            s_key = prefix;
+        }
+        __syncthreads();
+        const int r = s_cnt2;
+        const uint32_t kap = s_key;
+        // the id from which tied tokens stay: the r-th smallest tied id (V: none stays)
+        if (r == 0) {
+            if (tid == 0) s_idcut = 0;
+        } else if (r >= n_t) {
+            if (tid == 0) s_idcut = V;
+        } else if (n_t <= kSampleCand) {
+            if (tid == 0) s_cnt2 = 0;
+            __syncthreads();
+            scan([&](int i, float v) {
+                if (order_key(v) == kap) ids[atomicAdd(&s_cnt2, 1)] = (unsigned long long)i;
+            });
+            __syncthreads();
+            for (int j = tid; j < n_t; j += kSampleThreads) {
+                const unsigned long long me = ids[j];
+                int smaller = 0;
+                for (int q = 0; q < n_t; ++q) smaller += ids[q] < me ? 1 : 0;
+                if (smaller == r) s_idcut = (int)me;
+            }
+        } else if (wave == 0) {   // more tied logits than LDS holds: count them in id order
+            int seen = 0, cut = V;
+            for (int c0 = 0; c0 < V && cut == V; c0 += kWave) {
+                const int i = c0 + lane;
+                const bool tied = i < V && order_key(lg[i]) == kap;
+                const unsigned long long mk = __ballot(tied);
+                const int cnt = __popcll(mk);
+                if (seen + cnt > r) {   // the (r - seen)-th set lane of this chunk
+                    unsigned long long mm = mk;
+                    for (int q = 0; q < r - seen; ++q) mm &= mm - 1ull;
+                    cut = c0 + __ffsll((long long)mm) - 1;
+                }
+                seen += cnt;
+            }
+            if (lane == 0) s_idcut = cut;
+        }
+    }
+    __syncthreads();
+    const uint32_t kap = s_key;
+    const int idcut = s_idcut;
+    auto kept = [&](int i, float v) {
+        const uint32_t key = order_key(v);
+        return key > kap || (key == kap && i >= idcut);
+    };
+    // D
+    float kp = 0.f;
+    scan([&](int i, float v) { if (kept(i, v)) kp += e_of(v); });
+    const float Sk = block_red(kp, false);
+    const int seg = (((V + NWV - 1) / NWV) + kWave - 1) / kWave * kWave;   // ids per wave, whole chunks
+    const int i0 = wave * seg, i1 = min(V, i0 + seg);
+    // one pass over this wave's range in chunks of 64 (8 chunks of loads in flight);
+    // fn(chunk start, lane's p, wave-inclusive prefix of p) per chunk; stops when fn
+    // returns true
+    auto walk = [&](auto&& fn) {
+        for (int c0 = i0; c0 < i1; c0 += 8 * kWave) {
+            float v[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int i = c0 + q * kWave + lane;
+                v[q] = i < i1 ? lg[i] : 0.f;
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int cs = c0 + q * kWave, i = cs + lane;
+                if (cs >= i1) break;
+                const float p = (i < i1 && kept(i, v[q])) ? __fdiv_rn(e_of(v[q]), Sk) : 0.f;
+                float incl = p;
+#pragma unroll
+                for (int o = 1; o < kWave; o <<= 1) {
+                    const float t = __shfl_up(incl, o);
+                    if (lane >= o) incl += t;
+                }
+                if (fn(cs, p, incl)) return;
+            }
+        }
+    };
+    float wt = 0.f;
+    walk([&](int, float, float incl) { wt += __shfl(incl, kWave - 1); return false; });
+    if (lane == 0) s_wtot[wave] = wt;
+    if (tid == 0) s_tok = -1;
+    __syncthreads();
+    float tot = 0.f, before = 0.f;
+    for (int w = 0; w < NWV; ++w) { if (w < wave) before += s_wtot[w]; tot += s_wtot[w]; }
+    const float target = a.uniforms[row] * tot;
+    // the wave whose range holds the first running value > target (none: rounding, the last)
+    int wsel = NWV - 1;
+    {
+        float c = 0.f;
+        for (int w = 0; w < NWV; ++w) {
+            if (s_wtot[w] > 0.f && c + s_wtot[w] > target) { wsel = w; break; }
+            c += s_wtot[w];
+        }
+    }
+    if (wave == wsel) {
+        float run = before;
+        int last = -1;
+        walk([&](int cs, float p, float incl) {
+            const unsigned long long hit = __ballot(p > 0.f && run + incl > target);
+            const unsigned long long km = __ballot(p > 0.f);
+            if (km) last = cs + 63 - __clzll((long long)km);
+            if (hit) {
+                if (lane == 0) s_tok = cs + __ffsll((long long)hit) - 1;
+                return true;
+            }
+            run += __shfl(incl, kWave - 1);
+            return false;
+        });
+        if (lane == 0 && s_tok < 0) s_tok = last;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int t = s_tok;
+        if (t < 0) {   // the selected range kept nothing (rounding): the last kept token of the row
+            for (int i = V - 1; i >= 0; --i) if (kept(i, lg[i])) { t = i; break; }
+        }
+        a.tokens[row] = t;
+    }
+}
+
 __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleArgs a) {
     __shared__ int hist[2048];
     __shared__ unsigned long long ck[kSampleCand];   // (order key of z) << 32 | token
@@ -152,6 +403,11 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleArgs a) {
         __syncthreads();
     };
     auto global_keys = [&](auto&& f) { scan([&](int, float v) { f(order_key(v)); }); };
+
+    if (a.top_k <= 0 || a.top_k >= V) {   // no top-k: top-p over the whole vocabulary
+        sample_whole_vocab(a, row, lg, scan, hist, ce, ck, s_red);
+        return;
+    }
 
     // 1. the k-th largest key, 11 + 11 + 10 bits. After the first digit, when the
     //    boundary bin and everything above it fit the candidate space, those logits
@@ -418,7 +674,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleArgs a) {
 }
 
 hipError_t launch_sample(const SampleArgs& a, hipStream_t s) {
-    if (a.B < 1 || a.V < 1 || (a.temperature > 0.f && (a.top_k < 1 || a.top_k > kSampleMaxK)))
+    if (a.B < 1 || a.V < 1 || (a.temperature > 0.f && a.top_k > kSampleMaxK && a.top_k < a.V))
         return hipErrorInvalidValue;
     hipLaunchKernelGGL(sample_kernel, dim3(a.B), dim3(kSampleThreads), 0, s, a);
     return hipGetLastError();

@@ -210,7 +210,9 @@ qd_status qd_quantize_rows_int8(const void *w, int32_t w_dtype, int64_t rows, in
  *   temperature == 0: the argmax (lowest index on a tie); uniforms may be NULL.
  *   temperature  > 0: z = logits / temperature (float32); top-k keeps every token
  *     whose logit is >= the k-th largest (ties at the boundary stay), with
- *     1 <= top_k <= 1024 (other values: QD_EUNSUPPORTED); top-p in (0, 1] sorts
+ *     1 <= top_k <= 1024; top_k <= 0 or >= vocab applies no top-k (top-p over
+ *     the whole vocabulary, the page's "top-p alone"; other values:
+ *     QD_EUNSUPPORTED); top-p in (0, 1] sorts
  *     the survivors ascending by (z, token id), takes the float32 cumulative sum
  *     of their softmax probabilities in that order, one term at a time, and
  *     removes every token whose sum is <= float32(1 - top_p), keeping at least
@@ -220,6 +222,9 @@ qd_status qd_quantize_rows_int8(const void *w, int32_t w_dtype, int64_t rows, in
  *   tokens [batch] int32 out (-1 only for a row of NaN logits, which yields no
  *     candidate). Any number of logits may tie at the top-k boundary; past 2048
  *     candidates the row's draw reads it in token order (slower, same rule).
+ *     Without top-k the cut and the draw sum the probabilities in another order
+ *     than one at a time (the rule is the same; a row whose decision lies within
+ *     that rounding of a boundary may land on its other side).
  * One workgroup per row, enqueued on `stream`; no device memory is used beyond
  * the arguments. */
 qd_status qd_sample(const float *logits, int32_t batch, int32_t vocab, float temperature,

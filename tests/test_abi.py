@@ -265,8 +265,10 @@ def test_sample_checks(lib):
     _expect(s(FAKE, 1, 100, 1.0, 10, 0.0, FAKE, FAKE, None), Q.QD_EINVAL)
     _expect(s(FAKE, 1, 100, 1.0, 10, 1.5, FAKE, FAKE, None), Q.QD_EINVAL)
     _expect(s(FAKE, 1, 100, 1.0, 10, 0.9, None, FAKE, None), Q.QD_EINVAL)
-    _expect(s(FAKE, 1, 100, 1.0, 0, 0.9, FAKE, FAKE, None), Q.QD_EUNSUPPORTED)
-    _expect(s(FAKE, 1, 100, 1.0, 1025, 0.9, FAKE, FAKE, None), Q.QD_EUNSUPPORTED)
+    # top_k <= 0 or >= vocab: no top-k (top-p over the whole vocabulary), accepted;
+    # 1024 < top_k < vocab: not implemented
+    _expect(s(FAKE, 1, 5000, 1.0, 1025, 0.9, FAKE, FAKE, None), Q.QD_EUNSUPPORTED)
+    _expect(s(FAKE, 1, 5000, 1.0, 4999, 0.9, FAKE, FAKE, None), Q.QD_EUNSUPPORTED)
     _expect(s(FAKE + 2, 1, 100, 1.0, 10, 0.9, FAKE, FAKE, None), Q.QD_EALIGN)
 
 

@@ -130,10 +130,16 @@ QWEN2_SAMPLER_B16 = Workload(
     name="qwen2-sampler-b16-t0.7-k20-p0.8", shape=QWEN2_0P5B, kind="sample", batch=16,
     extra={"temperature": 0.7, "top_k": 20, "top_p": 0.8, "logit_std": 3.0})
 
+# The same rows with top-p alone (no top-k: the cut over the whole vocabulary), the
+# page's most expensive sampler configuration.
+QWEN2_SAMPLER_TOPP_B16 = Workload(
+    name="qwen2-sampler-b16-t0.7-topp0.8", shape=QWEN2_0P5B, kind="sample", batch=16,
+    extra={"temperature": 0.7, "top_k": 0, "top_p": 0.8, "logit_std": 3.0})
+
 WORKLOADS = {w.name: w for w in (QWEN2_BLOCK_F32_PAST16, QWEN2_0P5B_B1_PAST512,
                                  QWEN2_0P5B_B16_PAGED, QWEN_8B_B1_PAST4096,
                                  QWEN_8B_BLOCK_PREFILL512, QWEN2_0P5B_INT8_B1_PAST512,
-                                 QWEN2_0P5B_INT8_B16_PAGED, QWEN2_SAMPLER_B16)}
+                                 QWEN2_0P5B_INT8_B16_PAGED, QWEN2_SAMPLER_B16, QWEN2_SAMPLER_TOPP_B16)}
 
 
 def tiny_shape(**over) -> ModelShape:
