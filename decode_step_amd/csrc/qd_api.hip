@@ -292,6 +292,14 @@ bool fused_qkv_enabled() {
     return !(e && e[0] == '0');
 }
 
+// QD_DETERMINISTIC=1 in the environment: batch 2..16 residual products take one K
+// range per output block instead of adding K ranges with float atomics (read at
+// every call).
+bool deterministic_enabled() {
+    const char* e = getenv("QD_DETERMINISTIC");
+    return e && e[0] == '1';
+}
+
 // The attention arguments that decide the batch-1 fused projection.
 bool b1_fused_qkv(const qd_config* c, int B, bool merge_in_o, int chunk, int S, int hpw) {
     if (B != 1 || !merge_in_o || !fused_qkv_enabled()) return false;
@@ -569,6 +577,7 @@ qd_status decode_step_impl(const qd_config* cfg, const qd_weights* w, const qd_k
     QD_LAUNCH_K(QD_K_EMBED, qd::launch_step_input(si, wty, s), "step input");
 
     const bool fq = b1_fused_qkv(cfg, B, merge_in_o, chunk, S, hpw);
+    const int det = deterministic_enabled() ? 1 : 0;
     for (int l = 0; l < c.n_layers; ++l) {
         const qd_layer& L = w->layers_host[l];
         // RMSNorm -> q|k|v GEMV + bias
@@ -622,7 +631,7 @@ qd_status decode_step_impl(const qd_config* cfg, const qd_weights* w, const qd_k
         // o_proj + residual
         qd::GemvArgs go{};
         go.w[0] = L.wo; go.wscale[0] = L.s_o; go.seg_end[0] = go.seg_end[1] = go.seg_end[2] = D; go.nseg = 1;
-        go.N = D; go.K = P.Hq * P.hd; go.B = B; go.x = ctx; go.gain = nullptr; go.y = x;
+        go.N = D; go.K = P.Hq * P.hd; go.B = B; go.x = ctx; go.gain = nullptr; go.y = x; go.deterministic = det;
         go.kt = gemv_kt(B, go.K);
         if (merge_in_o) {   // the context is merged from the attention's splits here
             go.part = part; go.part_ml = part_ml; go.part_pos = pos;
@@ -643,6 +652,7 @@ qd_status decode_step_impl(const qd_config* cfg, const qd_weights* w, const qd_k
         qd::GemvArgs gd{};
         gd.w[0] = L.w_down; gd.wscale[0] = L.s_down; gd.seg_end[0] = gd.seg_end[1] = gd.seg_end[2] = D; gd.nseg = 1;
         gd.N = D; gd.K = P.F; gd.B = B; gd.x = h; gd.gain = nullptr; gd.y = x; gd.kt = gemv_kt(B, P.F);
+        gd.deterministic = det;
         QD_LAUNCH_K(QD_K_DOWN, gemv(gd, qd::EPI_RESID, kGemvGridCap, nullptr), "down gemv");
         if (layer_out) QD_LAUNCH(qd::launch_copy(x, layer_out + (size_t)l * B * D, (long)B * D, s), "layer_out copy");
     }

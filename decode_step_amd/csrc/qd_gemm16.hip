@@ -873,6 +873,7 @@ hipError_t launch_gemm16(const GemvArgs& a, int epi, int grid_cap, int* grid_out
 #undef QD_G16R
         }
         G16Split sp = gemm16_split_shape(a.K, a.N, epi);
+        if (epi == EPI_RESID && a.deterministic) sp = {0, 0, 0};   // one K range: the direct form
         if (a.ss_out) {                      // partial form: K ranges of at most 4 steps per wave
             const int sn = gemm16_store_splits(a.K, a.N);
             sp = {((((a.K + 31) / 32) + sn - 1) / sn + 3) / 4, sn, 1};

@@ -45,6 +45,9 @@ struct GemvArgs {
     // int8 weights: float scale of each row, per segment (SWIGLU: [0] gate, [1] up);
     // the product of row r is scaled by it
     const float* wscale[3];
+    // batch 2..16 residual products (launch_gemm16, EPI_RESID): nonzero takes one K
+    // range per output block (no float atomics, bitwise repeatable)
+    int deterministic;
     // optional, batch 2..16 normed store product (launch_gemm16, EPI_STORE) cut into
     // gemm16_store_splits(K, N) K ranges: y receives [splits][B][N] partial products
     // (neither the RMSNorm scale nor the bias applied) and ss_out [splits][B] the
