@@ -420,6 +420,8 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleArgs a) {
     digit(21, 11, prefix, need, global_keys);
     const int n0 = (k - need) + hist[prefix];      // logits in the boundary bin or above
     const bool in_lds = n0 <= kSampleCand;
+    // slots holding candidates (compacted in place: in LDS they stay among the n0)
+    const int nsort = in_lds ? n0 : kSampleCand;
     if (tid == 0) s_cnt = 0;
     for (int j = tid; j < kSampleCand; j += kSampleThreads) ck[j] = ~0ull;
     __syncthreads();
@@ -480,11 +482,15 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleArgs a) {
         return;
     }
     // bitonic sort of ck ascending (empty slots hold the largest key)
-    auto bitonic = [&]() {
-        for (int size = 2; size <= kSampleCand; size <<= 1)
+    // (the first n entries; every slot from n up holds the largest key, so the
+    // network runs over the next power of two only)
+    auto bitonic = [&](int n) {
+        int n2 = 2;
+        while (n2 < n) n2 <<= 1;
+        for (int size = 2; size <= n2; size <<= 1)
             for (int stride = size >> 1; stride > 0; stride >>= 1) {
                 __syncthreads();
-                for (int t = tid; t < kSampleCand / 2; t += kSampleThreads) {
+                for (int t = tid; t < n2 / 2; t += kSampleThreads) {
                     const int i = 2 * t - (t & (stride - 1));
                     const int j = i + stride;
                     const bool up = (i & size) == 0;
@@ -510,7 +516,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleArgs a) {
 
     int j0;
     if (C <= kSampleCand) {
-        bitonic();
+        bitonic(in_lds ? nsort : C);
         // 3. e_j = exp(z_j - max z) over the ascending order; S by a tree sum; the
         //    cumulative sum of e_j / S one term at a time; remove while it is <= 1 - p
         const float zmax = zval(ck[C - 1]);
@@ -554,7 +560,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleArgs a) {
         });
         __syncthreads();
         const int ng = s_cnt, ne = C - ng;   // above (ng < k <= kSampleMaxK), tied
-        bitonic();
+        bitonic(ng);
         const float vt = __uint_as_float(thresh ^ ((thresh & 0x80000000u) ? 0x80000000u : 0xffffffffu));
         const float zt = __fdiv_rn(vt, a.temperature);
         const float zmax = ng > 0 ? zval(ck[ng - 1]) : zt;
@@ -650,7 +656,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(SampleArgs a) {
             ck[j] = ~0ull;
         }
     }
-    bitonic();
+    bitonic(C);
     const int nk = C - j0;
     float kp = 0.f;
     for (int j = tid; j < nk; j += kSampleThreads) kp += __uint_as_float((uint32_t)(ck[j] & 0xffffffffu));
