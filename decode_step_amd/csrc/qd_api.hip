@@ -300,6 +300,13 @@ bool deterministic_enabled() {
     return e && e[0] == '1';
 }
 
+// QD_INT8_VALU=1 in the environment: batch 2..16 int8 projections on the vector
+// ALUs instead of the matrix cores (read at every call, so a process can compare).
+bool int8_valu_enabled() {
+    const char* e = getenv("QD_INT8_VALU");
+    return e && e[0] == '1';
+}
+
 // The attention arguments that decide the batch-1 fused projection.
 bool b1_fused_qkv(const qd_config* c, int B, bool merge_in_o, int chunk, int S, int hpw) {
     if (B != 1 || !merge_in_o || !fused_qkv_enabled()) return false;
@@ -522,12 +529,12 @@ qd_status decode_step_impl(const qd_config* cfg, const qd_weights* w, const qd_k
     auto gemv = [&](const qd::GemvArgs& g, int epi, int grid_cap, int* grid_out) {
         if (B == 1) return qd::launch_gemv1(g, wty, epi, epi == qd::EPI_LOGITS ? grid_cap : kGemv1GridCap,
                                             grid_out, s);
-        if (wty == QD_BF16) {
+        if (wty == QD_BF16 || (wty == QD_I8 && !int8_valu_enabled())) {   // the matrix cores
             qd::GemvArgs m = g;
             m.kt = qd::gemm16_chunk(g.K);
-            return qd::launch_gemm16(m, epi, grid_cap, grid_out, s);
+            return qd::launch_gemm16(m, wty, epi, grid_cap, grid_out, s);
         }
-        return qd::launch_gemv(g, wty, epi, grid_cap, grid_out, s);   // float or int8 rows
+        return qd::launch_gemv(g, wty, epi, grid_cap, grid_out, s);   // float rows (or int8, see above)
     };
 
     // batch 1: the one-launch step, when the config, the device and the position allow

@@ -50,8 +50,49 @@ __device__ __forceinline__ T load_or_zero(const void* p, bool ok) {
     return *(const T*)(ok ? p : (const void*)kG16Zeros);
 }
 
-template <int EPI, int R, int WK>
+// Weight rows: bf16 (a lane's 8 weights of a k-step in one 16-byte load), or int8
+// codes with one float scale per row (nanoinfer page, phase 6), whose 8 codes come
+// in one 8-byte load and are widened to bf16 exactly (|code| <= 127 fits the 8-bit
+// significand), so the same MFMAs run; the row's scale multiplies the finished
+// product. Gains and biases stay bf16.
+template <typename WT> struct G16W;
+template <> struct G16W<uint16_t> {
+    using L = uint4;
+    static __device__ __forceinline__ uint4 frag(uint4 v) { return v; }
+};
+template <> struct G16W<int8_t> {
+    using L = uint2;
+    static __device__ __forceinline__ uint4 frag(uint2 v) {
+        typedef __attribute__((ext_vector_type(2))) float f2;
+        typedef __attribute__((ext_vector_type(2))) __bf16 b2;
+        uint32_t o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {   // codes 2i, 2i + 1 (memory order) -> one bf16 pair
+            const uint32_t w = i < 2 ? v.x : v.y;
+            const int sh = (i & 1) * 16;
+            const float lo = (float)(int8_t)(w >> sh), hi = (float)(int8_t)(w >> (sh + 8));
+            o[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{lo, hi}, b2));
+        }
+        return make_uint4(o[0], o[1], o[2], o[3]);
+    }
+};
+// the scale of output row r (1 for bf16 rows): matrix n of a SwiGLU pair, else the
+// segment that holds r
+template <typename WT, int EPI>
+__device__ __forceinline__ float g16_scale(const GemvArgs& a, int r, int n) {
+    if constexpr (sizeof(WT) == 2) {
+        return 1.f;
+    } else {
+        if (EPI == EPI_SWIGLU) return a.wscale[n][r];
+        const bool q0 = r < a.seg_end[0], q1 = r < a.seg_end[1];
+        const int base = q0 ? 0 : (q1 ? a.seg_end[0] : a.seg_end[1]);
+        return (q0 ? a.wscale[0] : (q1 ? a.wscale[1] : a.wscale[2]))[r - base];
+    }
+}
+
+template <typename WT, int EPI, int R, int WK>
 __global__ __launch_bounds__(256) void gemm16_kernel(GemvArgs a) {
+    using WL = typename G16W<WT>::L;
     constexpr int NW = (EPI == EPI_SWIGLU) ? 2 : 1;
     constexpr int WR = 4 / WK;
     constexpr int TR = WR * R * 16;          // output rows per tile
@@ -115,7 +156,7 @@ __global__ __launch_bounds__(256) void gemm16_kernel(GemvArgs a) {
 
     for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
         // weight row pointers of this lane's A fragments (row = block base + col)
-        const uint16_t* wrow[R][NW];      // rows past N read row 0 (masked)
+        const WT* wrow[R][NW];      // rows past N read row 0 (masked)
         bool rok[R];
 #pragma unroll
         for (int rb = 0; rb < R; ++rb) {
@@ -123,15 +164,15 @@ __global__ __launch_bounds__(256) void gemm16_kernel(GemvArgs a) {
             rok[rb] = r < N;
 #pragma unroll
             for (int n = 0; n < NW; ++n) {
-                const uint16_t* p = (const uint16_t*)a.w[n];
+                const WT* p = (const WT*)a.w[n];
                 if (r < N) {
                     if (EPI == EPI_SWIGLU) {
-                        p = (const uint16_t*)a.w[n] + (long)r * K;
+                        p = (const WT*)a.w[n] + (long)r * K;
                     } else {
                         const bool s0 = r < a.seg_end[0], s1 = r < a.seg_end[1];
                         const void* w = s0 ? a.w[0] : (s1 ? a.w[1] : a.w[2]);
                         const int base = s0 ? 0 : (s1 ? a.seg_end[0] : a.seg_end[1]);
-                        p = (const uint16_t*)w + (long)(r - base) * K;
+                        p = (const WT*)w + (long)(r - base) * K;
                     }
                 }
                 wrow[rb][n] = p;
@@ -154,8 +195,8 @@ __global__ __launch_bounds__(256) void gemm16_kernel(GemvArgs a) {
             }
             const int nsteps = kcp / 32;
             const int s0 = wk * nsteps / WK, s1 = (wk + 1) * nsteps / WK;
-            uint4 wa[U][R][NW], wb[U][R][NW];
-            auto load = [&](uint4 (&w)[U][R][NW], int sb) {
+            WL wa[U][R][NW], wb[U][R][NW];
+            auto load = [&](WL (&w)[U][R][NW], int sb) {
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     const int s = sb + u;
@@ -166,10 +207,10 @@ __global__ __launch_bounds__(256) void gemm16_kernel(GemvArgs a) {
                     for (int rb = 0; rb < R; ++rb)
 #pragma unroll
                         for (int n = 0; n < NW; ++n)
-                            w[u][rb][n] = load_or_zero<uint4>(wrow[rb][n] + kc, kok && rok[rb]);
+                            w[u][rb][n] = load_or_zero<WL>(wrow[rb][n] + kc, kok && rok[rb]);
                 }
             };
-            auto mma = [&](const uint4 (&w)[U][R][NW], int sb) {
+            auto mma = [&](const WL (&w)[U][R][NW], int sb) {
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     const int s = sb + u;
@@ -180,7 +221,7 @@ __global__ __launch_bounds__(256) void gemm16_kernel(GemvArgs a) {
                     for (int rb = 0; rb < R; ++rb)
 #pragma unroll
                         for (int n = 0; n < NW; ++n) {
-                            const g16_bf16x8 af = g16_frag(w[u][rb][n]);
+                            const g16_bf16x8 af = g16_frag(G16W<WT>::frag(w[u][rb][n]));
                             acc[rb][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bh, acc[rb][n], 0, 0, 0);
                             acc[rb][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bl, acc[rb][n], 0, 0, 0);
                         }
@@ -235,7 +276,7 @@ __global__ __launch_bounds__(256) void gemm16_kernel(GemvArgs a) {
                 for (int e = 0; e < 4; ++e) {
                     const int r = rbase + e;
                     if (r >= N) break;
-                    const float v0 = acc[rb][0][e] * rs;
+                    const float v0 = acc[rb][0][e] * rs * g16_scale<WT, EPI>(a, r, 0);
                     if (EPI == EPI_STORE) {
                         const bool s0 = r < a.seg_end[0], s1 = r < a.seg_end[1];
                         const void* bsel = s0 ? a.bias[0] : (s1 ? a.bias[1] : a.bias[2]);
@@ -244,7 +285,7 @@ __global__ __launch_bounds__(256) void gemm16_kernel(GemvArgs a) {
                     } else if (EPI == EPI_RESID) {
                         yrow[r] = yrow[r] + v0;
                     } else if (EPI == EPI_SWIGLU) {
-                        yrow[r] = silu(v0) * (acc[rb][NW - 1][e] * rs);
+                        yrow[r] = silu(v0) * (acc[rb][NW - 1][e] * rs * g16_scale<WT, EPI>(a, r, NW - 1));
                     } else {
                         yrow[r] = v0;
                         if (better(v0, r, best_v, best_i)) { best_v = v0; best_i = r; }
@@ -275,8 +316,9 @@ __global__ __launch_bounds__(256) void gemm16_kernel(GemvArgs a) {
 // L2 in the same pipeline as the weights and splits it into hi/lo in
 // registers. No LDS staging, no barrier before the first MFMA. The gain, when
 // present, must be 16-byte aligned.
-template <int EPI, int WK>
+template <typename WT, int EPI, int WK>
 __global__ __launch_bounds__(64 * WK) void gemm16_direct_kernel(GemvArgs a) {
+    using WL = typename G16W<WT>::L;
     constexpr bool GAIN = EPI != EPI_RESID;       // every normed projection; residual ones have none
     constexpr int NW = (EPI == EPI_SWIGLU) ? 2 : 1;
     constexpr int TR = 16;
@@ -296,22 +338,22 @@ __global__ __launch_bounds__(64 * WK) void gemm16_direct_kernel(GemvArgs a) {
     if (a.zero_ptr && blockIdx.x == 0)
         for (int i = tid; i < a.zero_n; i += 64 * WK) a.zero_ptr[i] = 0u;
 
-    const uint16_t* wrow[NW];         // a row past N reads row 0 (masked)
+    const WT* wrow[NW];         // a row past N reads row 0 (masked)
     const int r_own = tile * TR + col;
     const bool rok = r_own < N;
     {
         const int r = r_own;
 #pragma unroll
         for (int n = 0; n < NW; ++n) {
-            const uint16_t* p = (const uint16_t*)a.w[n];
+            const WT* p = (const WT*)a.w[n];
             if (r < N) {
                 if (EPI == EPI_SWIGLU) {
-                    p = (const uint16_t*)a.w[n] + (long)r * K;
+                    p = (const WT*)a.w[n] + (long)r * K;
                 } else {
                     const bool s0 = r < a.seg_end[0], s1 = r < a.seg_end[1];
                     const void* w = s0 ? a.w[0] : (s1 ? a.w[1] : a.w[2]);
                     const int base = s0 ? 0 : (s1 ? a.seg_end[0] : a.seg_end[1]);
-                    p = (const uint16_t*)w + (long)(r - base) * K;
+                    p = (const WT*)w + (long)(r - base) * K;
                 }
             }
             wrow[n] = p;
@@ -325,7 +367,7 @@ __global__ __launch_bounds__(64 * WK) void gemm16_direct_kernel(GemvArgs a) {
     const int nsteps = (K + 31) / 32;
     const int s0 = wk * nsteps / WK, s1 = (wk + 1) * nsteps / WK;
     struct Stage {
-        uint4 w[U][NW];
+        WL w[U][NW];
         float4 x0[U], x1[U];
         uint4 g[U];
     };
@@ -338,7 +380,7 @@ __global__ __launch_bounds__(64 * WK) void gemm16_direct_kernel(GemvArgs a) {
             const bool ok = s < s1 && k < K;
             const int kc = ok ? k : 0;
 #pragma unroll
-            for (int n = 0; n < NW; ++n) st.w[u][n] = load_or_zero<uint4>(wrow[n] + kc, ok && rok);
+            for (int n = 0; n < NW; ++n) st.w[u][n] = load_or_zero<WL>(wrow[n] + kc, ok && rok);
             st.x0[u] = load_or_zero<float4>(xrow + kc, ok && tok);
             st.x1[u] = load_or_zero<float4>(xrow + kc + 4, ok && tok);
             if (GAIN) st.g[u] = load_or_zero<uint4>(gain + kc, ok);
@@ -365,7 +407,7 @@ __global__ __launch_bounds__(64 * WK) void gemm16_direct_kernel(GemvArgs a) {
             const g16_bf16x8 bl = g16_frag(lu);
 #pragma unroll
             for (int n = 0; n < NW; ++n) {
-                const g16_bf16x8 af = g16_frag(st.w[u][n]);
+                const g16_bf16x8 af = g16_frag(G16W<WT>::frag(st.w[u][n]));
                 acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bh, acc[n], 0, 0, 0);
                 acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bl, acc[n], 0, 0, 0);
             }
@@ -416,7 +458,7 @@ __global__ __launch_bounds__(64 * WK) void gemm16_direct_kernel(GemvArgs a) {
         for (int e = 0; e < 4; ++e) {
             const int r = rbase + e;
             if (r >= N) break;
-            const float v0 = acc[0][e] * rs;
+            const float v0 = acc[0][e] * rs * g16_scale<WT, EPI>(a, r, 0);
             if (EPI == EPI_STORE) {
                 const bool q0 = r < a.seg_end[0], q1 = r < a.seg_end[1];
                 const void* bsel = q0 ? a.bias[0] : (q1 ? a.bias[1] : a.bias[2]);
@@ -425,7 +467,7 @@ __global__ __launch_bounds__(64 * WK) void gemm16_direct_kernel(GemvArgs a) {
             } else if (EPI == EPI_RESID) {
                 yrow[r] = yrow[r] + v0;
             } else if (EPI == EPI_SWIGLU) {
-                yrow[r] = silu(v0) * (acc[NW - 1][e] * rs);
+                yrow[r] = silu(v0) * (acc[NW - 1][e] * rs * g16_scale<WT, EPI>(a, r, NW - 1));
             } else {
                 yrow[r] = v0;
                 if (better(v0, r, best_v, best_i)) { best_v = v0; best_i = r; }
@@ -458,8 +500,9 @@ __global__ __launch_bounds__(64 * WK) void gemm16_direct_kernel(GemvArgs a) {
 // instruction then fetches 8 whole lines (a layout with 32-byte pieces of 32
 // lines per instruction fetched every line twice), and the 8 lanes of a 16-byte
 // LDS read phase (tokens 0..7 or 8..15) land on distinct banks.
-template <int EPI, int RB, int SPW>
+template <typename WT, int EPI, int RB, int SPW>
 __global__ __launch_bounds__(256) void gemm16_rows_kernel(GemvArgs a) {
+    using WL = typename G16W<WT>::L;
     constexpr int NW = (EPI == EPI_SWIGLU) ? 2 : 1;
     constexpr int NLD = SPW * RB * NW;      // weight loads per lane
     static_assert(NLD <= 63, "vmcnt range");
@@ -489,7 +532,7 @@ __global__ __launch_bounds__(256) void gemm16_rows_kernel(GemvArgs a) {
     }
     // 2. this wave's weights: steps s0 + u (past s1, and rows past r1, read the zero block)
     const int s0 = wave * nsteps / 4, s1 = (wave + 1) * nsteps / 4;
-    const uint16_t* wrow[RB][NW];
+    const WT* wrow[RB][NW];
     bool rok[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -497,21 +540,21 @@ __global__ __launch_bounds__(256) void gemm16_rows_kernel(GemvArgs a) {
         rok[rb] = r < r1;
 #pragma unroll
         for (int n = 0; n < NW; ++n) {
-            const uint16_t* p = (const uint16_t*)a.w[n];
+            const WT* p = (const WT*)a.w[n];
             if (r < r1) {
                 if (EPI == EPI_SWIGLU) {
-                    p = (const uint16_t*)a.w[n] + (long)r * K;
+                    p = (const WT*)a.w[n] + (long)r * K;
                 } else {
                     const bool q0 = r < a.seg_end[0], q1 = r < a.seg_end[1];
                     const void* w = q0 ? a.w[0] : (q1 ? a.w[1] : a.w[2]);
                     const int base = q0 ? 0 : (q1 ? a.seg_end[0] : a.seg_end[1]);
-                    p = (const uint16_t*)w + (long)(r - base) * K;
+                    p = (const WT*)w + (long)(r - base) * K;
                 }
             }
             wrow[rb][n] = p;
         }
     }
-    uint4 wv[SPW][RB][NW];
+    WL wv[SPW][RB][NW];
 #pragma unroll
     for (int u = 0; u < SPW; ++u) {
         const int st = s0 + u;
@@ -520,7 +563,7 @@ __global__ __launch_bounds__(256) void gemm16_rows_kernel(GemvArgs a) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-            for (int n = 0; n < NW; ++n) wv[u][rb][n] = load_or_zero<uint4>(wrow[rb][n] + k, ok && rok[rb]);
+            for (int n = 0; n < NW; ++n) wv[u][rb][n] = load_or_zero<WL>(wrow[rb][n] + k, ok && rok[rb]);
     }
     __builtin_amdgcn_s_waitcnt(wait_vm(NLD));   // this wave's DMA landed (loads retire in issue order)
     lds_barrier();                              // ... and every wave's
@@ -555,7 +598,7 @@ __global__ __launch_bounds__(256) void gemm16_rows_kernel(GemvArgs a) {
         for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
             for (int n = 0; n < NW; ++n) {
-                const g16_bf16x8 af = g16_frag(wv[u][rb][n]);
+                const g16_bf16x8 af = g16_frag(G16W<WT>::frag(wv[u][rb][n]));
                 acc[rb][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bh, acc[rb][n], 0, 0, 0);
                 acc[rb][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bl, acc[rb][n], 0, 0, 0);
             }
@@ -591,9 +634,9 @@ __global__ __launch_bounds__(256) void gemm16_rows_kernel(GemvArgs a) {
         for (int e = 0; e < 4; ++e) {
             const int r = rbase + e;
             if (r >= r1) break;
-            const float v0 = acc[rb][0][e] * rs;
+            const float v0 = acc[rb][0][e] * rs * g16_scale<WT, EPI>(a, r, 0);
             if (EPI == EPI_SWIGLU) {
-                yrow[r] = silu(v0) * (acc[rb][NW - 1][e] * rs);
+                yrow[r] = silu(v0) * (acc[rb][NW - 1][e] * rs * g16_scale<WT, EPI>(a, r, NW - 1));
             } else {
                 const bool q0 = r < a.seg_end[0], q1 = r < a.seg_end[1];
                 const void* bsel = q0 ? a.bias[0] : (q1 ? a.bias[1] : a.bias[2]);
@@ -614,8 +657,9 @@ __global__ __launch_bounds__(256) void gemm16_rows_kernel(GemvArgs a) {
 // fixed; only the order of the final few additions varies from run to run);
 // every other epilogue takes one range (splits = 1), so its output is formed
 // once.
-template <int EPI, int SPW, int R>
+template <typename WT, int EPI, int SPW, int R>
 __global__ __launch_bounds__(256) void gemm16_split_kernel(GemvArgs a, int splits) {
+    using WL = typename G16W<WT>::L;
     constexpr bool GAIN = EPI != EPI_RESID;
     constexpr int NW = (EPI == EPI_SWIGLU) ? 2 : 1;
     constexpr int WK = 4;
@@ -632,7 +676,7 @@ __global__ __launch_bounds__(256) void gemm16_split_kernel(GemvArgs a, int split
     const int a0 = ks * nsteps / splits, a1 = (ks + 1) * nsteps / splits;
     const int s0 = a0 + wave * (a1 - a0) / WK, s1 = a0 + (wave + 1) * (a1 - a0) / WK;
 
-    const uint16_t* wrow[R][NW];     // a row past N reads row 0 (masked)
+    const WT* wrow[R][NW];     // a row past N reads row 0 (masked)
     bool rok[R];
 #pragma unroll
     for (int rb = 0; rb < R; ++rb) {
@@ -640,21 +684,21 @@ __global__ __launch_bounds__(256) void gemm16_split_kernel(GemvArgs a, int split
         rok[rb] = r_own < N;
 #pragma unroll
         for (int n = 0; n < NW; ++n) {
-            const uint16_t* p = (const uint16_t*)a.w[n];
+            const WT* p = (const WT*)a.w[n];
             if (rok[rb]) {
                 if (EPI == EPI_SWIGLU) {
-                    p = (const uint16_t*)a.w[n] + (long)r_own * K;
+                    p = (const WT*)a.w[n] + (long)r_own * K;
                 } else {
                     const bool q0 = r_own < a.seg_end[0], q1 = r_own < a.seg_end[1];
                     const void* w = q0 ? a.w[0] : (q1 ? a.w[1] : a.w[2]);
                     const int base = q0 ? 0 : (q1 ? a.seg_end[0] : a.seg_end[1]);
-                    p = (const uint16_t*)w + (long)(r_own - base) * K;
+                    p = (const WT*)w + (long)(r_own - base) * K;
                 }
             }
             wrow[rb][n] = p;
         }
     }
-    uint4 wv[SPW][R][NW];
+    WL wv[SPW][R][NW];
     float4 x0[SPW], x1[SPW];
     uint4 gv[SPW];
 #pragma unroll
@@ -666,7 +710,7 @@ __global__ __launch_bounds__(256) void gemm16_split_kernel(GemvArgs a, int split
 #pragma unroll
         for (int rb = 0; rb < R; ++rb)
 #pragma unroll
-            for (int n = 0; n < NW; ++n) wv[u][rb][n] = load_or_zero<uint4>(wrow[rb][n] + kc, ok && rok[rb]);
+            for (int n = 0; n < NW; ++n) wv[u][rb][n] = load_or_zero<WL>(wrow[rb][n] + kc, ok && rok[rb]);
         x0[u] = load_or_zero<float4>(xrow + kc, ok && tok);
         x1[u] = load_or_zero<float4>(xrow + kc + 4, ok && tok);
         if (GAIN) gv[u] = load_or_zero<uint4>(gain + kc, ok);
@@ -709,7 +753,7 @@ __global__ __launch_bounds__(256) void gemm16_split_kernel(GemvArgs a, int split
         for (int rb = 0; rb < R; ++rb)
 #pragma unroll
             for (int n = 0; n < NW; ++n) {
-                const g16_bf16x8 af = g16_frag(wv[u][rb][n]);
+                const g16_bf16x8 af = g16_frag(G16W<WT>::frag(wv[u][rb][n]));
                 acc[rb][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bh, acc[rb][n], 0, 0, 0);
                 acc[rb][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bl, acc[rb][n], 0, 0, 0);
             }
@@ -756,7 +800,7 @@ __global__ __launch_bounds__(256) void gemm16_split_kernel(GemvArgs a, int split
         for (int e = 0; e < 4; ++e) {
             const int r = rbase + e;
             if (r >= N) break;
-            const float v0 = acc[rb][0][e] * rs;
+            const float v0 = acc[rb][0][e] * rs * g16_scale<WT, EPI>(a, r, 0);
             if (EPI == EPI_STORE) {
                 const bool q0 = r < a.seg_end[0], q1 = r < a.seg_end[1];
                 const void* bsel = q0 ? a.bias[0] : (q1 ? a.bias[1] : a.bias[2]);
@@ -766,7 +810,7 @@ __global__ __launch_bounds__(256) void gemm16_split_kernel(GemvArgs a, int split
                 if (splits == 1) yrow[r] = yv[rb][e] + v0;
                 else unsafeAtomicAdd(yrow + r, v0);
             } else {
-                yrow[r] = silu(v0) * (acc[rb][NW - 1][e] * rs);
+                yrow[r] = silu(v0) * (acc[rb][NW - 1][e] * rs * g16_scale<WT, EPI>(a, r, NW - 1));
             }
         }
     }
@@ -837,8 +881,8 @@ int gemm16_chunk(int K) {
 // block per workgroup with the four waves splitting K and the activation read
 // directly, which spreads even the smallest decode matrix (896 rows) over 56
 // workgroups.
-hipError_t launch_gemm16(const GemvArgs& a, int epi, int grid_cap, int* grid_out, hipStream_t s) {
-    if (a.B < 1 || a.B > 16 || a.K % 8 || a.kt != gemm16_chunk(a.K)) return hipErrorInvalidValue;
+template <typename WT>
+static hipError_t gemm16_dispatch(const GemvArgs& a, int epi, int grid_cap, int* grid_out, hipStream_t s) {
     const bool wide = a.N >= 16 * 2048;
     const bool gain_ok = epi == EPI_RESID ? a.gain == nullptr
                                           : (a.gain != nullptr && ((uintptr_t)a.gain & 15u) == 0);
@@ -864,10 +908,10 @@ hipError_t launch_gemm16(const GemvArgs& a, int epi, int grid_cap, int* grid_out
             };
 #define QD_G16R(RB)                                                      \
             switch (rspw) {                                              \
-                case 2: return go(gemm16_rows_kernel<EPI_SWIGLU, RB, 2>); \
-                case 4: return go(gemm16_rows_kernel<EPI_SWIGLU, RB, 4>); \
-                case 7: return go(gemm16_rows_kernel<EPI_SWIGLU, RB, 7>); \
-                default: return go(gemm16_rows_kernel<EPI_SWIGLU, RB, 8>); \
+                case 2: return go(gemm16_rows_kernel<WT, EPI_SWIGLU, RB, 2>); \
+                case 4: return go(gemm16_rows_kernel<WT, EPI_SWIGLU, RB, 4>); \
+                case 7: return go(gemm16_rows_kernel<WT, EPI_SWIGLU, RB, 7>); \
+                default: return go(gemm16_rows_kernel<WT, EPI_SWIGLU, RB, 8>); \
             }
             if (rb == 1) { QD_G16R(1) } else if (rb == 2) { QD_G16R(2) } else { QD_G16R(3) }
 #undef QD_G16R
@@ -883,7 +927,7 @@ hipError_t launch_gemm16(const GemvArgs& a, int epi, int grid_cap, int* grid_out
             if (grid > grid_cap) return hipErrorInvalidValue;
             if (grid_out) *grid_out = grid;
             const dim3 g2(grid, sp.splits);
-#define QD_G16S(E, S, R) hipLaunchKernelGGL((gemm16_split_kernel<E, S, R>), g2, dim3(256), 0, s, a, sp.splits)
+#define QD_G16S(E, S, R) hipLaunchKernelGGL((gemm16_split_kernel<WT, E, S, R>), g2, dim3(256), 0, s, a, sp.splits)
             if (epi == EPI_RESID) {
                 if (sp.r == 2) {
                     switch (sp.spw) {
@@ -914,8 +958,8 @@ hipError_t launch_gemm16(const GemvArgs& a, int epi, int grid_cap, int* grid_out
         if (grid_out) *grid_out = grid;
         const bool deep = a.K >= 2048;       // long K: eight waves split it
 #define QD_G16D(E)                                                                                       \
-    if (deep) hipLaunchKernelGGL((gemm16_direct_kernel<E, 8>), dim3(grid), dim3(512), 0, s, a);          \
-    else hipLaunchKernelGGL((gemm16_direct_kernel<E, 4>), dim3(grid), dim3(256), 0, s, a);
+    if (deep) hipLaunchKernelGGL((gemm16_direct_kernel<WT, E, 8>), dim3(grid), dim3(512), 0, s, a);          \
+    else hipLaunchKernelGGL((gemm16_direct_kernel<WT, E, 4>), dim3(grid), dim3(256), 0, s, a);
         switch (epi) {
             case EPI_STORE: QD_G16D(EPI_STORE) break;
             case EPI_RESID: QD_G16D(EPI_RESID) break;
@@ -938,11 +982,21 @@ hipError_t launch_gemm16(const GemvArgs& a, int epi, int grid_cap, int* grid_out
         return hipGetLastError();
     };
     switch (epi) {
-        case EPI_STORE: return wide ? go(gemm16_kernel<EPI_STORE, 2, 1>, 128) : go(gemm16_kernel<EPI_STORE, 1, 4>, 16);
-        case EPI_RESID: return wide ? go(gemm16_kernel<EPI_RESID, 2, 1>, 128) : go(gemm16_kernel<EPI_RESID, 1, 4>, 16);
-        case EPI_SWIGLU: return go(gemm16_kernel<EPI_SWIGLU, 1, 4>, 16);
-        default: return wide ? go(gemm16_kernel<EPI_LOGITS, 2, 1>, 128) : go(gemm16_kernel<EPI_LOGITS, 1, 4>, 16);
+        case EPI_STORE: return wide ? go(gemm16_kernel<WT, EPI_STORE, 2, 1>, 128) : go(gemm16_kernel<WT, EPI_STORE, 1, 4>, 16);
+        case EPI_RESID: return wide ? go(gemm16_kernel<WT, EPI_RESID, 2, 1>, 128) : go(gemm16_kernel<WT, EPI_RESID, 1, 4>, 16);
+        case EPI_SWIGLU: return go(gemm16_kernel<WT, EPI_SWIGLU, 1, 4>, 16);
+        default: return wide ? go(gemm16_kernel<WT, EPI_LOGITS, 2, 1>, 128) : go(gemm16_kernel<WT, EPI_LOGITS, 1, 4>, 16);
     }
+}
+
+hipError_t launch_gemm16(const GemvArgs& a, int w_type, int epi, int grid_cap, int* grid_out, hipStream_t s) {
+    if (a.B < 1 || a.B > 16 || a.K % 8 || a.kt != gemm16_chunk(a.K)) return hipErrorInvalidValue;
+    if (w_type == 2) {   // int8 rows: row scales, no partial form (its consumer adds no scale)
+        if (a.ss_out || a.K % 16 || !a.wscale[0] || (epi == EPI_SWIGLU && !a.wscale[1])) return hipErrorInvalidValue;
+        return gemm16_dispatch<int8_t>(a, epi, grid_cap, grid_out, s);
+    }
+    if (w_type != 1) return hipErrorInvalidValue;
+    return gemm16_dispatch<uint16_t>(a, epi, grid_cap, grid_out, s);
 }
 
 }  // namespace qd

@@ -65,9 +65,10 @@ hipError_t launch_gemv1(const GemvArgs& a, int w_type, int epi, int grid_cap, in
 int gemv_rows_per_tile(int K);
 // most attention splits launch_gemv1 merges itself (GemvArgs::part)
 int gemv1_merge_max_splits();
-// batch 2..16 with bf16 weights on the matrix cores (qd_gemm16.hip); a.kt must be
+// batch 2..16 on the matrix cores (qd_gemm16.hip): w_type 1 bf16 rows, 2 int8 rows
+// with a.wscale (K a multiple of 16, widened to bf16 exactly); a.kt must be
 // gemm16_chunk(a.K); part_val/part_idx hold [B][grid] entries
-hipError_t launch_gemm16(const GemvArgs& a, int epi, int grid_cap, int* grid_out, hipStream_t s);
+hipError_t launch_gemm16(const GemvArgs& a, int w_type, int epi, int grid_cap, int* grid_out, hipStream_t s);
 int gemm16_chunk(int K);
 // K ranges of a normed store product given GemvArgs::ss_out (1: no partial form)
 int gemm16_store_splits(int K, int N);
