@@ -412,7 +412,8 @@ qd_status qd_decode_plan(const qd_config* cfg, int32_t batch, int32_t max_tokens
     out->splits = S;
     out->heads_per_wg = hpw;
     out->matrix_core_attention = mfma ? 1 : 0;
-    out->qkv_partials = (batch > 1 && wbf && qkv_splits > 1 && mfma) ? qkv_splits : 0;
+    out->qkv_partials = (batch > 1 && (wbf || (cfg->w_dtype == QD_I8 && !int8_valu_enabled())) && qkv_splits > 1 &&
+                         mfma) ? qkv_splits : 0;
     out->merge_in_o_proj = merge_in_o ? 1 : 0;
     out->fused_qkv = b1_fused_qkv(cfg, batch, merge_in_o, chunk, S, hpw) ? 1 : 0;
     out->step_kernel = (batch == 1 && qd::step::step_config_ok(cfg) && qd::step::plan_step(cfg, max_tokens).ok) ? 1 : 0;
@@ -622,10 +623,12 @@ qd_status decode_step_impl(const qd_config* cfg, const qd_weights* w, const qd_k
         }
         // batch 2..16 on the matrix cores: q|k|v as K-range partial products, which
         // the attention kernel finishes (RMSNorm scale, bias) as it loads them
-        if (B > 1 && wty == QD_BF16 && qkv_splits > 1 && qd::attn_uses_mfma(at, kvbf)) {
+        if (B > 1 && (wty == QD_BF16 || (wty == QD_I8 && !int8_valu_enabled())) && qkv_splits > 1 &&
+            qd::attn_uses_mfma(at, kvbf)) {
             g.ss_out = qss;
             at.qkv_slabs = qkv_splits; at.qkv_slab_stride = (long)B * P.qkvr; at.qkv_ss = qss;
             at.qkv_bias[0] = L.bq; at.qkv_bias[1] = L.bk; at.qkv_bias[2] = L.bv; at.x_dim = D;
+            if (wty == QD_I8) { at.qkv_scale[0] = L.s_q; at.qkv_scale[1] = L.s_k; at.qkv_scale[2] = L.s_v; }
         }
         if (fq) {   // batch 1: the projection inside the attention launch
             at.fq = 1; at.fq_x = x; at.fq_gain = L.attn_norm; at.fq_out = qkv; at.x_dim = D;

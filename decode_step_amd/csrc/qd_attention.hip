@@ -663,6 +663,7 @@ __global__ __launch_bounds__(kAmWaves * kWave) void attn_mfma_kernel(AttnArgs a)
     constexpr bool PART = NSL > 1;
     float t[NSL][3][8], ssv[NSL];
     uint32_t bq[3][4];              // biases (PART), bf16 pairs (4-byte aligned: biases need no more)
+    float sc[3][8];                 // int8 rows (PART): the rows' scales
     if (pro_ld) {
         const float* src = a.qkv + (long)b * qkvr;
         const int hoff = phl < G ? (g * G + phl) * HD : a.Hq * HD + g * HD;
@@ -695,6 +696,12 @@ __global__ __launch_bounds__(kAmWaves * kWave) void attn_mfma_kernel(AttnArgs a)
                 bq[1][e] = *(const __attribute__((address_space(1))) uint32_t*)(b1 + 4 * e);
                 bq[2][e] = *(const __attribute__((address_space(1))) uint32_t*)(b2 + 4 * e);
             }
+            // int8 rows: the scales of the same rows (bf16 rows read zeros, unused)
+            const bool i8 = a.qkv_scale[0] != nullptr;
+            const float* const sh = phl < G ? a.qkv_scale[0] + (g * G + phl) * HD : a.qkv_scale[1] + g * HD;
+            load_f32xN(i8 ? sh + pl2 * 8 : z, sc[0], 8);
+            load_f32xN(i8 ? sh + plp2 * 8 : z, sc[1], 8);
+            load_f32xN(i8 && phl == G ? a.qkv_scale[2] + g * HD + pl2 * 8 : z, sc[2], 8);
         }
         const float2* tab = a.rope + (long)b * (HD / 2) + (pl2 % (LPT / 2)) * 8;
 #pragma unroll
@@ -731,12 +738,13 @@ __global__ __launch_bounds__(kAmWaves * kWave) void attn_mfma_kernel(AttnArgs a)
         }
         if (PART) {
             const float r = 1.0f / sqrtf(ssl / (float)a.x_dim + a.eps);
+            const bool i8 = a.qkv_scale[0] != nullptr;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int sh = (e & 1) ? 16 : 0;
-                u[e] = u[e] * r + bf16_to_f32((bq[0][e >> 1] >> sh) & 0xffffu);
-                up[e] = up[e] * r + bf16_to_f32((bq[1][e >> 1] >> sh) & 0xffffu);
-                vn[e] = vn[e] * r + bf16_to_f32((bq[2][e >> 1] >> sh) & 0xffffu);
+                u[e] = u[e] * (i8 ? r * sc[0][e] : r) + bf16_to_f32((bq[0][e >> 1] >> sh) & 0xffffu);
+                up[e] = up[e] * (i8 ? r * sc[1][e] : r) + bf16_to_f32((bq[1][e >> 1] >> sh) & 0xffffu);
+                vn[e] = vn[e] * (i8 ? r * sc[2][e] : r) + bf16_to_f32((bq[2][e >> 1] >> sh) & 0xffffu);
             }
         }
     }

@@ -991,8 +991,8 @@ static hipError_t gemm16_dispatch(const GemvArgs& a, int epi, int grid_cap, int*
 
 hipError_t launch_gemm16(const GemvArgs& a, int w_type, int epi, int grid_cap, int* grid_out, hipStream_t s) {
     if (a.B < 1 || a.B > 16 || a.K % 8 || a.kt != gemm16_chunk(a.K)) return hipErrorInvalidValue;
-    if (w_type == 2) {   // int8 rows: row scales, no partial form (its consumer adds no scale)
-        if (a.ss_out || a.K % 16 || !a.wscale[0] || (epi == EPI_SWIGLU && !a.wscale[1])) return hipErrorInvalidValue;
+    if (w_type == 2) {   // int8 rows: row scales (the partial form leaves them to its consumer)
+        if (a.K % 16 || !a.wscale[0] || (epi == EPI_SWIGLU && !a.wscale[1])) return hipErrorInvalidValue;
         return gemm16_dispatch<int8_t>(a, epi, grid_cap, grid_out, s);
     }
     if (w_type != 1) return hipErrorInvalidValue;

@@ -112,6 +112,7 @@ struct AttnArgs {
     long qkv_slab_stride;
     const float* qkv_ss;
     const void* qkv_bias[3];
+    const float* qkv_scale[3];   // int8 rows: the q, k and v row scales (NULL: bf16 rows)
     int x_dim;
     // optional (matrix-core kernel): a one-dimensional grid of only the splits that
     // hold keys, sequence b's at wg_base[b] .. wg_base[b + 1] - 1 (split-major, then
