@@ -93,10 +93,15 @@ __device__ __forceinline__ float g16_scale(const GemvArgs& a, int r, int n) {
 template <typename WT, int EPI, int R, int WK>
 __global__ __launch_bounds__(256) void gemm16_kernel(GemvArgs a) {
     using WL = typename G16W<WT>::L;
+    // int8 rows: one 16-byte load per lane covers a pair of k-steps (s, s + 1): lane
+    // kq holds the 16 codes at 32 s + 16 kq, codes 8u .. 8u + 7 feeding the pair's
+    // MFMA u with the activation group (32 s + 16 kq + 8 u) / 8, the same products
+    // in another k order, and half the load instructions of 8-byte loads
+    constexpr bool PAIR = sizeof(WT) == 1;
     constexpr int NW = (EPI == EPI_SWIGLU) ? 2 : 1;
     constexpr int WR = 4 / WK;
     constexpr int TR = WR * R * 16;          // output rows per tile
-    constexpr int U = kG16U;
+    constexpr int U = sizeof(WT) == 1 ? 2 * kG16U : kG16U;   // int8: as many load instructions per stage as bf16
     extern __shared__ uint4 xs[];            // hi: [chunk/8][16], then lo: [chunk/8][16]
     __shared__ float ssum[4][16];
     __shared__ g16_f32x4 red[WK > 1 ? WK - 1 : 1][WR][R][NW][kWave];
@@ -197,26 +202,47 @@ __global__ __launch_bounds__(256) void gemm16_kernel(GemvArgs a) {
             const int s0 = wk * nsteps / WK, s1 = (wk + 1) * nsteps / WK;
             WL wa[U][R][NW], wb[U][R][NW];
             auto load = [&](WL (&w)[U][R][NW], int sb) {
+                if constexpr (PAIR) {
+                    static_assert(U % 2 == 0, "whole pairs of k-steps per stage");
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int s = sb + u;
-                    const int k = k0 + s * 32 + kq * 8;
-                    const bool kok = s < s1 && k < K;
-                    const int kc = kok ? k : 0;
+                    for (int q = 0; q < U / 2; ++q) {
+                        const int sp = sb + 2 * q;
+                        const int k = k0 + sp * 32 + kq * 16;
+                        const bool kok = sp + (kq >> 1) < s1 && k < K;   // the step these codes belong to
+                        const int kc = kok ? k : 0;
 #pragma unroll
-                    for (int rb = 0; rb < R; ++rb)
+                        for (int rb = 0; rb < R; ++rb)
 #pragma unroll
-                        for (int n = 0; n < NW; ++n)
-                            w[u][rb][n] = load_or_zero<WL>(wrow[rb][n] + kc, kok && rok[rb]);
+                            for (int n = 0; n < NW; ++n) {
+                                const uint4 v = load_or_zero<uint4>(wrow[rb][n] + kc, kok && rok[rb]);
+                                w[2 * q][rb][n] = WL{v.x, v.y};
+                                w[2 * q + 1][rb][n] = WL{v.z, v.w};
+                            }
+                    }
+                } else {
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const int s = sb + u;
+                        const int k = k0 + s * 32 + kq * 8;
+                        const bool kok = s < s1 && k < K;
+                        const int kc = kok ? k : 0;
+#pragma unroll
+                        for (int rb = 0; rb < R; ++rb)
+#pragma unroll
+                            for (int n = 0; n < NW; ++n)
+                                w[u][rb][n] = load_or_zero<WL>(wrow[rb][n] + kc, kok && rok[rb]);
+                    }
                 }
             };
             auto mma = [&](const WL (&w)[U][R][NW], int sb) {
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    const int s = sb + u;
-                    if (s >= s1) break;
-                    const g16_bf16x8 bh = g16_frag(xhi[(s * 4 + kq) * 16 + col]);
-                    const g16_bf16x8 bl = g16_frag(xlo[(s * 4 + kq) * 16 + col]);
+                    const int s = sb + u, sp = sb + (u & ~1);   // (PAIR: the pair's first step)
+                    if (PAIR ? sp >= s1 : s >= s1) break;
+                    // (PAIR: a lane whose codes lie past the range holds zeros; it reads group 0)
+                    const int grp = PAIR ? (sp + (kq >> 1) < s1 ? 4 * sp + 2 * kq + (u & 1) : 0) : s * 4 + kq;
+                    const g16_bf16x8 bh = g16_frag(xhi[grp * 16 + col]);
+                    const g16_bf16x8 bl = g16_frag(xlo[grp * 16 + col]);
 #pragma unroll
                     for (int rb = 0; rb < R; ++rb)
 #pragma unroll
