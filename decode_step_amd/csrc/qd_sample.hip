@@ -209,6 +209,7 @@ __device__ __forceinline__ void sample_whole_vocab(const SampleArgs& a, int row,
         __syncthreads();
         const int r = s_cnt2;
         const uint32_t kap = s_key;
+        __syncthreads();   // every thread has read r before s_cnt2 counts the tied ids below
         // the id from which tied tokens stay: the r-th smallest tied id (V: none stays)
         if (r == 0) {
             if (tid == 0) s_idcut = 0;
