@@ -314,7 +314,7 @@ bool b1_fused_qkv(const qd_config* c, int B, bool merge_in_o, int chunk, int S, 
     at.Hq = c->n_q_heads; at.Hkv = c->n_kv_heads; at.hd = c->head_dim; at.page = c->page_size;
     at.chunk = chunk; at.S = S; at.B = B; at.hpw = hpw; at.prefill_start = -1; at.qk_norm = c->qk_norm;
     at.part_always = 1; at.x_dim = c->hidden;
-    return qd::attn_fq_ok(at, c->w_dtype == QD_BF16, c->kv_dtype == QD_BF16);
+    return qd::attn_fq_ok(at, c->w_dtype == QD_BF16 ? 1 : (c->w_dtype == QD_I8 ? 2 : 0), c->kv_dtype == QD_BF16);
 }
 
 // QD_STEP_KERNEL=1 in the environment sends eligible batch-1 steps to the one-launch
@@ -633,6 +633,7 @@ qd_status decode_step_impl(const qd_config* cfg, const qd_weights* w, const qd_k
         if (fq) {   // batch 1: the projection inside the attention launch
             at.fq = 1; at.fq_x = x; at.fq_gain = L.attn_norm; at.fq_out = qkv; at.x_dim = D;
             at.fq_w[0] = L.wq; at.fq_w[1] = L.wk; at.fq_w[2] = L.wv;
+            if (wty == QD_I8) { at.fq_scale[0] = L.s_q; at.fq_scale[1] = L.s_k; at.fq_scale[2] = L.s_v; }
             at.qkv_bias[0] = L.bq; at.qkv_bias[1] = L.bk; at.qkv_bias[2] = L.bv;
         } else {
             QD_LAUNCH_K(QD_K_QKV, gemv(g, qd::EPI_STORE, kGemvGridCap, nullptr), "qkv gemv");

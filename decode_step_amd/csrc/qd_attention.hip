@@ -92,45 +92,58 @@ __device__ __forceinline__ void rope_lane(float (&u)[CE], const float (&pr)[CE],
 // Batch 1 with the projection in the attention launch (AttnArgs::fq): each
 // workgroup forms 64 projection rows (one head) from x itself. 512 threads in 16
 // groups of 32 lanes; group q takes rows 4q .. 4q + 3, and lane li of a group the
-// 16-byte chunks li, li + 32, ... of those rows, at most kFqChunks of them
-// (x_dim <= kFqMaxD), so each chunk of x read from LDS serves four rows and a
-// group's load of one row covers 512 contiguous bytes. All of a lane's row loads
-// are issued before x is used; a chunk index past the row reads chunk 0 and meets
-// a block of zeros in LDS (no load under a per-lane condition).
+// 16-byte chunks li, li + 32, ... of those rows (8 bf16 or 16 int8 columns each),
+// at most FqT<RT>::NC of them (x_dim <= kFqMaxD), so each chunk of x read from LDS
+// serves four rows and a group's load of one row covers 512 contiguous bytes. All
+// of a lane's row loads are issued before x is used; a chunk index past the row
+// reads chunk 0 and meets a block of zeros in LDS (no load under a per-lane
+// condition). int8 rows (nanoinfer page, phase 6) carry a float scale per row,
+// applied to the finished dot product.
 constexpr int kFqLanes = 32;
 constexpr int kFqRows = 4;
-constexpr int kFqChunks = kFqMaxD / (8 * kFqLanes);
-
-struct FqLoads {
-    uint4 w[kFqRows][kFqChunks];
-    float4 x;
-    uint2 gain;
-    float bias;   // of row 4q + (li & 3)
+template <typename RT> struct FqT {
+    static constexpr int CE = VecN<RT>::n;                      // columns per 16-byte chunk
+    static constexpr int NC = kFqMaxD / (CE * kFqLanes);        // chunks per lane per row
 };
 
-// Issue the loads of rows row0 .. row0 + 63 of the bf16 matrix w ([rows][x_dim]),
-// their bias (bf16, may be NULL), x and its RMSNorm gain. The small loads go first
-// and none sits under a condition (without a bias a weight is loaded and scaled by
-// 0), so that waiting for them, or for anything issued before, leaves the rows in
-// flight (loads complete in issue order). Compiler-only memory fences keep that
-// order and keep the row loads ahead of any branch that follows (left alone, the
-// compiler moves them below an early exit, behind a wait for the position).
-__device__ __forceinline__ void fq_issue(const AttnArgs& a, const void* w, const void* bias, int row0, FqLoads& f) {
-    const int tid = threadIdx.x, D = a.x_dim, KC = D / 8;
+template <typename RT>
+struct FqLoads {
+    uint4 w[kFqRows][FqT<RT>::NC];
+    float4 x;
+    uint2 gain;
+    float bias;    // of row 4q + (li & 3)
+    float scale;   // int8: that row's scale (1 for bf16 rows)
+};
+
+// Issue the loads of rows row0 .. row0 + 63 of the matrix w ([rows][x_dim]), their
+// bias (bf16, may be NULL), int8 row scale, x and its RMSNorm gain. The small loads
+// go first and none sits under a condition (without a bias a weight is loaded and
+// scaled by 0), so that waiting for them, or for anything issued before, leaves the
+// rows in flight (loads complete in issue order). Compiler-only memory fences keep
+// that order and keep the row loads ahead of any branch that follows (left alone,
+// the compiler moves them below an early exit, behind a wait for the position).
+template <typename RT>
+__device__ __forceinline__ void fq_issue(const AttnArgs& a, const void* w, const void* bias, const float* scale,
+                                         int row0, FqLoads<RT>& f) {
+    constexpr int CE = FqT<RT>::CE, NC = FqT<RT>::NC;
+    const int tid = threadIdx.x, D = a.x_dim, KC = D / CE;
     const int e4 = tid < D / 4 ? tid : 0;
     const int r0 = row0 + (tid / kFqLanes) * kFqRows, li = tid % kFqLanes;
-    gbyte* wr = sgpr_gptr(w) + (long)r0 * D * 2;
+    const long rbytes = (long)D * sizeof(RT);
+    gbyte* wr = sgpr_gptr(w) + r0 * rbytes;
     f.x = ((const float4*)a.fq_x)[e4];
     f.gain = ((const uint2*)a.fq_gain)[e4];
     gbyte* bp = sgpr_gptr(bias ? bias : w);
     f.bias = gld_scalar<uint16_t>(bp, bias ? r0 + (li & 3) : 0) * (bias ? 1.f : 0.f);
+    if constexpr (sizeof(RT) == 1) f.scale = gld_scalar<float>(sgpr_gptr(scale), r0 + (li & 3));
+    else f.scale = 1.f;
     asm volatile("" ::: "memory");
 #pragma unroll
     for (int u = 0; u < kFqRows; ++u)
 #pragma unroll
-        for (int j = 0; j < kFqChunks; ++j) {
+        for (int j = 0; j < NC; ++j) {
             const int c = li + j * kFqLanes;
-            f.w[u][j] = gld16(wr + ((long)u * D * 2 + (c < KC ? c : 0) * 16));
+            f.w[u][j] = gld16(wr + (u * rbytes + (c < KC ? c : 0) * 16));
         }
     asm volatile("" ::: "memory");
 }
@@ -139,13 +152,14 @@ __device__ __forceinline__ void fq_issue(const AttnArgs& a, const void* w, const
 // (the RMSNorm folded into the product, as in the GEMV kernels). Barriers inside
 // (every thread of the workgroup calls it); they are LDS-only, so loads issued
 // after the rows (the K/V rows of the attention) stay in flight across them.
-__device__ __forceinline__ void fq_finish(const AttnArgs& a, const FqLoads& f, float* out) {
-    constexpr int NWV = kAttnWaves;
-    static_assert(kFqRows == 4, "a row's bias sits in lane li & 3");
-    __shared__ __align__(16) float xg[kFqMaxD + 8];   // x * g, then one zero chunk
+template <typename RT>
+__device__ __forceinline__ void fq_finish(const AttnArgs& a, const FqLoads<RT>& f, float* out) {
+    constexpr int NWV = kAttnWaves, CE = FqT<RT>::CE, NC = FqT<RT>::NC;
+    static_assert(kFqRows == 4, "a row's bias and scale sit in lane li & 3");
+    __shared__ __align__(16) float xg[kFqMaxD + 16];   // x * g, then one zero chunk
     __shared__ float wsq[NWV];
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
-    const int D = a.x_dim, KC = D / 8;
+    const int D = a.x_dim, KC = D / CE;
     float ss = 0.f;
     if (tid < D / 4) {   // (waits for x only: the row loads stay in flight)
         const float4 v = f.x;
@@ -153,7 +167,7 @@ __device__ __forceinline__ void fq_finish(const AttnArgs& a, const FqLoads& f, f
         ((float4*)xg)[tid] = make_float4(v.x * bf16_to_f32(f.gain.x & 0xffffu), v.y * bf16_to_f32(f.gain.x >> 16),
                                          v.z * bf16_to_f32(f.gain.y & 0xffffu), v.w * bf16_to_f32(f.gain.y >> 16));
     }
-    if (tid < 8) xg[KC * 8 + tid] = 0.f;
+    if (tid < CE) xg[KC * CE + tid] = 0.f;
     ss = group_sum<kWave>(ss);
     if (lane == 0) wsq[wave] = ss;
     lds_barrier();
@@ -164,19 +178,22 @@ __device__ __forceinline__ void fq_finish(const AttnArgs& a, const FqLoads& f, f
     const int li = tid % kFqLanes;
     float acc[kFqRows] = {};
 #pragma unroll
-    for (int j = 0; j < kFqChunks; ++j) {
+    for (int j = 0; j < NC; ++j) {
         const int c = li + j * kFqLanes;
-        const float4* xp = (const float4*)(xg + (c < KC ? c : KC) * 8);
-        const float4 x0 = xp[0], x1 = xp[1];
+        const float4* xp = (const float4*)(xg + (c < KC ? c : KC) * CE);
+        float xv[CE];
+#pragma unroll
+        for (int q = 0; q < CE / 4; ++q) {
+            const float4 t = xp[q];
+            xv[4 * q] = t.x; xv[4 * q + 1] = t.y; xv[4 * q + 2] = t.z; xv[4 * q + 3] = t.w;
+        }
 #pragma unroll
         for (int u = 0; u < kFqRows; ++u) {
-            float wf[8];
+            float wf[CE];
             widen16(f.w[u][j], wf);
             float t = acc[u];
-            t = fmaf(wf[0], x0.x, t); t = fmaf(wf[1], x0.y, t);
-            t = fmaf(wf[2], x0.z, t); t = fmaf(wf[3], x0.w, t);
-            t = fmaf(wf[4], x1.x, t); t = fmaf(wf[5], x1.y, t);
-            t = fmaf(wf[6], x1.z, t); t = fmaf(wf[7], x1.w, t);
+#pragma unroll
+            for (int e = 0; e < CE; ++e) t = fmaf(wf[e], xv[e], t);
             acc[u] = t;
         }
     }
@@ -184,7 +201,7 @@ __device__ __forceinline__ void fq_finish(const AttnArgs& a, const FqLoads& f, f
     for (int u = 0; u < kFqRows; ++u) acc[u] = group_sum<kFqLanes>(acc[u]);
     const int u = li & 3;
     const float mine = u == 0 ? acc[0] : u == 1 ? acc[1] : u == 2 ? acc[2] : acc[3];
-    if (li < kFqRows) out[(tid / kFqLanes) * kFqRows + li] = fmaf(mine, r, f.bias);
+    if (li < kFqRows) out[(tid / kFqLanes) * kFqRows + li] = fmaf(mine * f.scale, r, f.bias);
     lds_barrier();
 }
 
@@ -201,7 +218,7 @@ __device__ __forceinline__ float fq_rope(const float* v, const float2* tab, int 
     return d < 32 ? u * cs.x - pr * cs.y : u * cs.x + pr * cs.y;
 }
 
-template <typename WT, typename KVT, int HD, int NP, bool FQ = false>
+template <typename WT, typename KVT, int HD, int NP, bool FQ = false, typename RT = uint16_t>
 __device__ __forceinline__ void attn_body(const AttnArgs& a, const int s, const int by, const int bz) {
     static_assert(!FQ || (HD == 64 && NP <= kAttnPassesGrouped), "projection in the launch: hd 64, grouped");
     constexpr int CE = VecN<KVT>::n;
@@ -238,11 +255,11 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int s, const 
     if (tid < (a.chunk + PG - 1) / PG + 1 && pg0 + tid < a.max_blocks) pgv = bt[pg0 + tid];
     // (projection in this launch: the position, then the query head's rows and x
     // behind the page ids)
-    FqLoads fql;
+    FqLoads<RT> fql;
     int p_fq = 0;
     if constexpr (FQ) {
         p_fq = fq_pos(a);
-        fq_issue(a, a.fq_w[0], a.qkv_bias[0], (g * G + h0) * HD, fql);
+        fq_issue<RT>(a, a.fq_w[0], a.qkv_bias[0], a.fq_scale[0], (g * G + h0) * HD, fql);
     }
     const int qkvr = (a.Hq + 2 * a.Hkv) * HD;
     const bool pro_ld = !FQ && !prefill && nh > 0 && tid < (nh + 1) * LPT;
@@ -303,7 +320,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int s, const 
     }
     if constexpr (FQ) {   // the query head: project, rotate, publish (split 0)
         __shared__ float qraw[HD];
-        fq_finish(a, fql, qraw);
+        fq_finish<RT>(a, fql, qraw);
         if (tid < HD) {
             const float q = fq_rope(qraw, a.rope, tid);
             qs[0][tid] = q;
@@ -533,16 +550,17 @@ void attn_wide_kernel(AttnArgs a) {
 // is even), projected like the query heads, k rotated, rounded to the cache type
 // and stored at the position (nanoinfer page, phase 4: keys are rotated once, on
 // insert); the stored values, widened, go to fq_out for the residual product.
-template <typename KVT>
+template <typename RT, typename KVT>
 __device__ __forceinline__ void fq_kv_body(const AttnArgs& a, int j) {
     constexpr int HD = 64, CE = VecN<KVT>::n, PG = kAttnPage;
     __shared__ float row[HD], st[HD];
     const int g = j >> 1, is_v = j & 1, tid = threadIdx.x;
     const int p = fq_pos(a);
-    FqLoads f;
-    fq_issue(a, is_v ? a.fq_w[2] : a.fq_w[1], is_v ? a.qkv_bias[2] : a.qkv_bias[1], g * HD, f);
+    FqLoads<RT> f;
+    fq_issue<RT>(a, is_v ? a.fq_w[2] : a.fq_w[1], is_v ? a.qkv_bias[2] : a.qkv_bias[1],
+                 is_v ? a.fq_scale[2] : a.fq_scale[1], g * HD, f);
     if (p < 0 || p >= a.capacity) return;
-    fq_finish(a, f, row);
+    fq_finish<RT>(a, f, row);
     if (tid < HD) st[tid] = is_v ? row[tid] : fq_rope(row, a.rope, tid);
     lds_barrier();
     if (tid < HD / CE) {
@@ -569,18 +587,18 @@ __device__ __forceinline__ void fq_kv_body(const AttnArgs& a, int j) {
 // ids 8 apart: id = 8 (S (h / 8) + s) + h % 8 (ids of heads past Hq exit at once).
 __host__ __device__ constexpr int fq_attn_wgs(int S, int Hq) { return 8 * S * ((Hq + 7) / 8); }
 
-template <typename KVT>
+template <typename RT, typename KVT>
 __global__ __launch_bounds__(kAttnWaves * kWave) void attn_fq_kernel(AttnArgs a) {
     static_assert(kAttnWaves * kWave == 64 / kFqRows * kFqLanes, "one 64-row block per workgroup");
     const int n_att = fq_attn_wgs(a.S, a.Hq);
     const int id = blockIdx.x;
     if (id >= n_att) {
-        fq_kv_body<KVT>(a, id - n_att);
+        fq_kv_body<RT, KVT>(a, id - n_att);
         return;
     }
     const int slot = id >> 3, h = (slot / a.S) * 8 + (id & 7), s = slot % a.S;
     if (h >= a.Hq) return;
-    attn_body<uint16_t, KVT, 64, kAttnPassesGrouped, true>(a, s, h, 0);
+    attn_body<uint16_t, KVT, 64, kAttnPassesGrouped, true, RT>(a, s, h, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -1023,23 +1041,30 @@ bool attn_uses_mfma(const AttnArgs& a, int kv_is_bf16) {
            (G + 1) * (a.hd / 8) <= kAmWaves * kWave && a.chunk <= kAmChunk && (a.hd == 64 || a.hd == 128);
 }
 
-bool attn_fq_ok(const AttnArgs& a, int w_is_bf16, int kv_is_bf16) {
+bool attn_fq_ok(const AttnArgs& a, int w_type, int kv_is_bf16) {
     const int chunk_max = kv_is_bf16 ? attn_chunk<64, uint16_t, kAttnPassesGrouped>()
                                      : attn_chunk<64, float, kAttnPassesGrouped>();
-    return w_is_bf16 && a.B == 1 && a.hd == 64 && a.hpw == 1 && !a.qk_norm && a.prefill_start < 0 &&
-           a.part_always && !a.compact && a.qkv_slabs == 0 && a.x_dim >= 8 && a.x_dim <= kFqMaxD &&
-           a.x_dim % 8 == 0 && a.chunk <= chunk_max && a.Hq % a.Hkv == 0;
+    const int ce = w_type == 2 ? 16 : 8;   // columns per 16-byte chunk (int8 or bf16 rows)
+    return (w_type == 1 || w_type == 2) && a.B == 1 && a.hd == 64 && a.hpw == 1 && !a.qk_norm &&
+           a.prefill_start < 0 && a.part_always && !a.compact && a.qkv_slabs == 0 && a.x_dim >= ce &&
+           a.x_dim <= kFqMaxD && a.x_dim % ce == 0 && a.chunk <= chunk_max && a.Hq % a.Hkv == 0;
 }
 
 hipError_t launch_attention(const AttnArgs& a, int w_is_bf16, int kv_is_bf16, hipStream_t s) {
     if (a.page != kAttnPage) return hipErrorInvalidValue;
-    if (a.fq) {
-        if (!attn_fq_ok(a, w_is_bf16, kv_is_bf16) || !a.fq_x || !a.fq_gain || !a.fq_w[0] || !a.fq_w[1] ||
-            !a.fq_w[2] || !a.fq_out)
+    if (a.fq) {   // int8 rows when the row scales are given
+        const bool i8 = a.fq_scale[0] != nullptr;
+        if (!w_is_bf16 || !attn_fq_ok(a, i8 ? 2 : 1, kv_is_bf16) || !a.fq_x || !a.fq_gain || !a.fq_w[0] ||
+            !a.fq_w[1] || !a.fq_w[2] || !a.fq_out || (i8 && (!a.fq_scale[1] || !a.fq_scale[2])))
             return hipErrorInvalidValue;
         const dim3 grid(fq_attn_wgs(a.S, a.Hq) + 2 * a.Hkv), block(kAttnWaves * kWave);
-        if (kv_is_bf16) hipLaunchKernelGGL(attn_fq_kernel<uint16_t>, grid, block, 0, s, a);
-        else hipLaunchKernelGGL(attn_fq_kernel<float>, grid, block, 0, s, a);
+        if (i8) {
+            if (kv_is_bf16) hipLaunchKernelGGL((attn_fq_kernel<int8_t, uint16_t>), grid, block, 0, s, a);
+            else hipLaunchKernelGGL((attn_fq_kernel<int8_t, float>), grid, block, 0, s, a);
+        } else {
+            if (kv_is_bf16) hipLaunchKernelGGL((attn_fq_kernel<uint16_t, uint16_t>), grid, block, 0, s, a);
+            else hipLaunchKernelGGL((attn_fq_kernel<uint16_t, float>), grid, block, 0, s, a);
+        }
         return hipGetLastError();
     }
     const int G = a.Hq / a.Hkv;

@@ -121,7 +121,8 @@ struct AttnArgs {
     int wg_base[kAttnMaxBatch + 1];
     // optional, batch 1 (fq = 1): the q|k|v projection is formed inside the
     // attention launch instead of read from qkv. One query head per workgroup, bf16
-    // weights, hd 64, no per-head norm, x_dim <= kFqMaxD and a multiple of 8. The
+    // or int8 rows (fq_scale), hd 64, no per-head norm, x_dim <= kFqMaxD and a
+    // multiple of 8 (bf16) or 16 (int8). The
     // grid is one-dimensional: the attention workgroups (one per split and query
     // head, the splits of a head on one XCD), each projecting its query head from
     // x (RMSNorm with fq_gain and eps, rows of fq_w[0], bias qkv_bias[0]) and
@@ -136,6 +137,7 @@ struct AttnArgs {
     const float* fq_x;
     const void* fq_gain;
     const void* fq_w[3];
+    const float* fq_scale[3];   // int8 rows: the q, k and v row scales (NULL: bf16 rows)
     float* fq_out;
 };
 constexpr int kFqMaxD = 1024;
@@ -143,8 +145,9 @@ constexpr int kFqMaxD = 1024;
 hipError_t launch_attention(const AttnArgs& a, int w_is_bf16, int kv_is_bf16, hipStream_t s);
 // whether launch_attention takes the matrix-core grouped kernel for these arguments
 bool attn_uses_mfma(const AttnArgs& a, int kv_is_bf16);
-// whether these arguments allow the projection in the attention launch (fq)
-bool attn_fq_ok(const AttnArgs& a, int w_is_bf16, int kv_is_bf16);
+// whether these arguments allow the projection in the attention launch (fq);
+// w_type 1 bf16 rows, 2 int8 rows
+bool attn_fq_ok(const AttnArgs& a, int w_type, int kv_is_bf16);
 int attn_max_chunk(int hd, int kv_is_bf16, int grouped);
 int attn_max_splits();
 

@@ -325,14 +325,15 @@ def test_decode_plan_paths(lib):
 
 
 def test_decode_plan_fused_projection(lib, monkeypatch):
-    """Batch 1 at the 0.5B shape (bf16, head_dim 64, hidden <= 1024, no per-head
-    norm) projects q|k|v inside the attention launch; every other case, and
-    QD_FUSED_QKV=0, keeps the projection launch."""
+    """Batch 1 at the 0.5B shape (bf16 or int8 rows, head_dim 64, hidden <= 1024,
+    no per-head norm) projects q|k|v inside the attention launch; every other
+    case, and QD_FUSED_QKV=0, keeps the projection launch."""
     monkeypatch.delenv("QD_FUSED_QKV", raising=False)
     for t in (1, 144, 145, 513, 2304):
         assert Q.qd_decode_plan(_cfg_05b(), 1, t).fused_qkv == 1, t
     assert Q.qd_decode_plan(_cfg_05b(), 2, 513).fused_qkv == 0                      # batch > 1
-    assert Q.qd_decode_plan(_cfg_05b(w_dtype=Q.QD_I8), 1, 513).fused_qkv == 0       # int8 rows
+    assert Q.qd_decode_plan(_cfg_05b(w_dtype=Q.QD_I8), 1, 513).fused_qkv == 1       # int8 rows too
+    assert Q.qd_decode_plan(_cfg_05b(w_dtype=Q.QD_I8, hidden=1040), 1, 513).fused_qkv == 0  # hidden > 1024
     assert Q.qd_decode_plan(_cfg_05b(w_dtype=Q.QD_F32, kv_dtype=Q.QD_F32), 1, 100).fused_qkv == 0
     assert Q.qd_decode_plan(_cfg_05b(qk_norm=1), 1, 513).fused_qkv == 0             # per-head norm
     assert Q.qd_decode_plan(_cfg_05b(hidden=1536, ffn=8960, n_q_heads=12), 1, 513).fused_qkv == 0
