@@ -97,6 +97,9 @@ constexpr int kAttnMinChunk = 64;
 #ifndef QD_B1_CHUNK
 #define QD_B1_CHUNK 144     // tokens per split at batch 1 (o_proj merges the splits)
 #endif
+#ifndef QD_B1_WIDE_SPLITS
+#define QD_B1_WIDE_SPLITS 32   // most splits of a batch-1 step whose o_proj cannot merge them itself
+#endif
 #ifndef QD_B1_HPW
 #define QD_B1_HPW 1         // query heads per workgroup at batch 1 (0: the whole group)
 #endif
@@ -140,6 +143,10 @@ bool plan_split(const qd_config* c, int B, int max_tokens, int* chunk, int* S, i
     if (ch < kAttnMinChunk) ch = kAttnMinChunk;
     const long need = (tokens + qd::attn_max_splits() - 1) / qd::attn_max_splits();   // merge capacity
     if (ch < need) ch = (need + pg - 1) / pg * pg;
+    // a batch-1 decode step: at most QD_B1_WIDE_SPLITS splits where the chunk allows
+    // (fewer partials for the residual product to merge)
+    const long need1 = (tokens + QD_B1_WIDE_SPLITS - 1) / QD_B1_WIDE_SPLITS;
+    if (merge_in_o && B == 1 && ch < need1) ch = (need1 + pg - 1) / pg * pg;
     if (ch > ch_max) ch = ch_max;
     *chunk = (int)ch;
     *S = (tokens + *chunk - 1) / *chunk;
@@ -317,6 +324,21 @@ bool b1_fused_qkv(const qd_config* c, int B, bool merge_in_o, int chunk, int S, 
     return qd::attn_fq_ok(at, c->w_dtype == QD_BF16 ? 1 : (c->w_dtype == QD_I8 ? 2 : 0), c->kv_dtype == QD_BF16);
 }
 
+// Batch-1 steps whose context is too wide for the o_proj GEMV to merge the
+// attention splits itself (more than 1024 values, or more splits than it takes)
+// run o_proj by head slices over the split partials instead of a merge launch
+// and a GEMV; the head slices meet through float atomics, so this form is off
+// with QD_DETERMINISTIC=1, and QD_O_HEADS=0 in the environment keeps the merge
+// launch (both read at every call).
+bool o_heads_enabled() {
+    const char* e = getenv("QD_O_HEADS");
+    return !(e && e[0] == '0');
+}
+bool b1_o_heads(const qd_config* c, int B, bool merge_in_o, int S) {
+    return B == 1 && !merge_in_o && S > 1 && S <= 64 && c->w_dtype == QD_BF16 &&
+           (c->head_dim == 64 || c->head_dim == 128) && o_heads_enabled() && !deterministic_enabled();
+}
+
 // QD_STEP_KERNEL=1 in the environment sends eligible batch-1 steps to the one-launch
 // step kernel; otherwise they take the per-op launch path (read at every call, so a
 // process can compare the two).
@@ -414,7 +436,7 @@ qd_status qd_decode_plan(const qd_config* cfg, int32_t batch, int32_t max_tokens
     out->matrix_core_attention = mfma ? 1 : 0;
     out->qkv_partials = (batch > 1 && (wbf || (cfg->w_dtype == QD_I8 && !int8_valu_enabled())) && qkv_splits > 1 &&
                          mfma) ? qkv_splits : 0;
-    out->merge_in_o_proj = merge_in_o ? 1 : 0;
+    out->merge_in_o_proj = merge_in_o ? 1 : (b1_o_heads(cfg, batch, merge_in_o, S) ? 2 : 0);
     out->fused_qkv = b1_fused_qkv(cfg, batch, merge_in_o, chunk, S, hpw) ? 1 : 0;
     out->step_kernel = (batch == 1 && qd::step::step_config_ok(cfg) && qd::step::plan_step(cfg, max_tokens).ok) ? 1 : 0;
     return QD_OK;
@@ -586,6 +608,7 @@ qd_status decode_step_impl(const qd_config* cfg, const qd_weights* w, const qd_k
 
     const bool fq = b1_fused_qkv(cfg, B, merge_in_o, chunk, S, hpw);
     const int det = deterministic_enabled() ? 1 : 0;
+    const bool o_heads = b1_o_heads(cfg, B, merge_in_o, S);
     for (int l = 0; l < c.n_layers; ++l) {
         const qd_layer& L = w->layers_host[l];
         // RMSNorm -> q|k|v GEMV + bias
@@ -602,7 +625,7 @@ qd_status decode_step_impl(const qd_config* cfg, const qd_weights* w, const qd_k
         at.block_table = kv->block_table; at.max_blocks = kv->max_blocks; at.num_pages = kv->num_pages;
         at.pos = pos; at.capacity = cap; at.q_norm = L.q_norm; at.k_norm = L.k_norm; at.qk_norm = c.qk_norm;
         at.eps = c.rms_eps; at.theta = c.rope_theta; at.part = part; at.part_ml = part_ml;
-        at.part_always = merge_in_o ? 1 : 0; at.rope = rope; at.ctx = ctx;
+        at.part_always = (merge_in_o || o_heads) ? 1 : 0; at.rope = rope; at.ctx = ctx;
         at.Hq = P.Hq; at.Hkv = P.Hkv; at.hd = P.hd; at.page = c.page_size; at.chunk = P.chunk; at.S = P.S;
         at.B = B; at.hpw = hpw; at.scale = 1.0f / sqrtf((float)P.hd);
         at.prefill_start = -1; at.q_rot = nullptr;
@@ -651,7 +674,13 @@ qd_status decode_step_impl(const qd_config* cfg, const qd_weights* w, const qd_k
                 go.part_new = qkv; go.part_kv_heads = P.Hkv; go.part_scale2 = at.scale * 1.4426950408889634f;
             }
         }
-        QD_LAUNCH_K(QD_K_O, gemv(go, qd::EPI_RESID, kGemvGridCap, nullptr), "o_proj gemv");
+        if (o_heads) {   // ... or by head slices, each merging its head's splits
+            go.part = part; go.part_ml = part_ml; go.part_pos = pos;
+            go.part_S = S; go.part_chunk = chunk; go.part_hd = P.hd;
+            QD_LAUNCH_K(QD_K_O, qd::launch_oproj_heads(go, s), "o_proj by head slices");
+        } else {
+            QD_LAUNCH_K(QD_K_O, gemv(go, qd::EPI_RESID, kGemvGridCap, nullptr), "o_proj gemv");
+        }
         // RMSNorm -> gate|up GEMV -> SwiGLU
         qd::GemvArgs gu{};
         gu.w[0] = L.w_gate; gu.w[1] = L.w_up; gu.wscale[0] = L.s_gate; gu.wscale[1] = L.s_up;

@@ -507,4 +507,134 @@ hipError_t launch_gemv1(const GemvArgs& a, int w_type, int epi, int grid_cap, in
 #undef QD_G1
 }
 
+
+// ---------------------------------------------------------------------------
+// Batch-1 residual product by head slices, for contexts too wide for one
+// workgroup to merge (Hq * hd > 1024) and split over several attention
+// workgroups. Workgroup (query head h, block of R output rows):
+//   1. loads head h's split partials (o_s, and the (m_s, l_s) pairs in base-2
+//      units), then its R rows' slice of W (columns h*hd .. h*hd+hd-1), so the
+//      merge below runs under the weights' latency;
+//   2. merges the valid splits (Tang page, section 2.2: the online-softmax
+//      monoid): ctx_h = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M), with M the
+//      largest m_s, in a fixed order;
+//   3. adds W[r, h-slice] . ctx_h into y[r] with a float atomic: y holds the
+//      residual, and the Hq head slices of each row meet there (their order of
+//      addition varies from run to run).
+// One 16-byte chunk per lane per row (hd/8 lanes per row slice), kOhLoads rows
+// per lane: R = 4 * (64 / (hd/8)) * kOhLoads rows per workgroup. Workgroups of
+// one head are 8 ids apart when Hq is a multiple of 8, so they share an XCD and
+// read the head's partials through one L2.
+#ifndef QD_OH_LOADS
+#define QD_OH_LOADS 8
+#endif
+constexpr int kOhLoads = QD_OH_LOADS;
+constexpr int kOhMaxSplits = 64;
+__host__ __device__ constexpr int oproj_heads_rows(int hd) { return 4 * (64 / (hd / 8)) * kOhLoads; }
+
+template <int HD, int MS>
+__global__ __launch_bounds__(256) void oproj_heads_kernel(GemvArgs a) {
+    constexpr int LPR = HD / 8;                    // lanes per row slice
+    constexpr int RPI = 4 * (kWave / LPR);         // rows per workgroup load
+    constexpr int R = RPI * kOhLoads;
+    constexpr int Q4 = HD / 4;                     // float4s per split's context row
+    constexpr int NG = 256 / Q4;                   // split groups of threads
+    constexpr int MSL = (MS + NG - 1) / NG;        // partial loads per thread (MS >= part_S)
+    __shared__ float wgt[kOhMaxSplits];
+    __shared__ float4 red[NG][Q4];
+    __shared__ float4 ctx4[Q4];
+
+    const int N = a.N, K = a.K, Hq = K / HD, NB = (N + R - 1) / R, S = a.part_S;
+    const int id = blockIdx.x;
+    int h, rb;
+    if ((Hq & 7) == 0) { const int k = id >> 3; h = (k / NB) * 8 + (id & 7); rb = k - (k / NB) * NB; }
+    else { h = id / NB; rb = id - h * NB; }
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+    // the position as a scalar load (a vector load issued here would return after
+    // the weights, and the merge would wait for them)
+    const int p = *(const __attribute__((address_space(4))) int*)a.part_pos;
+
+    // partials first (indices clamped to valid splits; the invalid are weighted 0)
+    const int q4 = tid % Q4, grp = tid / Q4;
+    const float* pb = a.part + (long)h * S * HD + 4 * q4;
+    float4 ov[MSL];
+#pragma unroll
+    for (int u = 0; u < MSL; ++u) {
+        const int j = grp + u * NG;
+        ov[u] = *(const float4*)(pb + (long)(j < S ? j : S - 1) * HD);
+    }
+    const float2 ml = a.part_ml[(long)h * S + (lane < S ? lane : S - 1)];
+    asm volatile("" ::: "memory");
+    gbyte* wb = sgpr_gptr(a.w[0]) + (long)h * HD * 2 + (lane % LPR) * 16;
+    const int row0 = rb * R + wave * (kWave / LPR) + lane / LPR;
+    uint4 wv[kOhLoads];
+#pragma unroll
+    for (int i = 0; i < kOhLoads; ++i) {
+        const int r = row0 + i * RPI;
+        wv[i] = gld16(wb + (long)(r < N ? r : N - 1) * K * 2);
+    }
+    asm volatile("" ::: "memory");
+
+    const int ns = p >= 0 ? min(S, (p + a.part_chunk) / a.part_chunk) : 0;
+    if (wave == 0) {   // the splits' weights, 1/L folded in
+        const float mj = lane < ns ? ml.x : -INFINITY;
+        const float m = group_max<kWave>(mj);
+        const float w = lane < ns ? __builtin_amdgcn_exp2f(mj - m) : 0.f;
+        const float l = group_sum<kWave>((lane < ns ? ml.y : 0.f) * w);
+        wgt[lane] = ns > 0 ? w / l : 0.f;
+    }
+    lds_barrier();
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int u = 0; u < MSL; ++u) {
+        const int j = grp + u * NG;
+        const float wj = j < ns ? wgt[j < kOhMaxSplits ? j : 0] : 0.f;
+        o.x = fmaf(ov[u].x, wj, o.x); o.y = fmaf(ov[u].y, wj, o.y);
+        o.z = fmaf(ov[u].z, wj, o.z); o.w = fmaf(ov[u].w, wj, o.w);
+    }
+    red[grp][q4] = o;
+    lds_barrier();
+    if (tid < Q4) {
+        float4 t = red[0][tid];
+#pragma unroll
+        for (int g = 1; g < NG; ++g) {
+            const float4 v = red[g][tid];
+            t.x += v.x; t.y += v.y; t.z += v.z; t.w += v.w;
+        }
+        ctx4[tid] = t;
+    }
+    lds_barrier();
+    const int li = lane % LPR;
+    const float4 c0 = ctx4[2 * li], c1 = ctx4[2 * li + 1];
+    const float cx[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+    for (int i = 0; i < kOhLoads; ++i) {
+        float wf[8];
+        widen16(wv[i], wf);
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc = fmaf(wf[e], cx[e], acc);
+        acc = group_sum<LPR>(acc);
+        const int r = row0 + i * RPI;
+        if (li == 0 && r < N && ns > 0) unsafeAtomicAdd(a.y + r, acc);
+    }
+}
+
+hipError_t launch_oproj_heads(const GemvArgs& a, hipStream_t s) {
+    const int hd = a.part_hd;
+    if ((hd != 64 && hd != 128) || !a.part || !a.part_ml || !a.part_pos || !a.w[0] || !a.y || a.gain ||
+        a.part_S < 1 || a.part_S > kOhMaxSplits || a.part_chunk < 1 || a.N < 1 || a.K < hd || a.K % hd ||
+        a.B != 1)
+        return hipErrorInvalidValue;
+    const int R = oproj_heads_rows(hd), nb = (a.N + R - 1) / R;
+    const dim3 grid((a.K / hd) * nb), block(256);
+#define QD_OH(HD)                                                                                              \
+    if (a.part_S <= 16) hipLaunchKernelGGL((oproj_heads_kernel<HD, 16>), grid, block, 0, s, a);                \
+    else if (a.part_S <= 32) hipLaunchKernelGGL((oproj_heads_kernel<HD, 32>), grid, block, 0, s, a);           \
+    else hipLaunchKernelGGL((oproj_heads_kernel<HD, 64>), grid, block, 0, s, a);
+    if (hd == 64) { QD_OH(64) } else { QD_OH(128) }
+#undef QD_OH
+    return hipGetLastError();
+}
+
 }  // namespace qd

@@ -65,6 +65,10 @@ hipError_t launch_gemv1(const GemvArgs& a, int w_type, int epi, int grid_cap, in
 int gemv_rows_per_tile(int K);
 // most attention splits launch_gemv1 merges itself (GemvArgs::part)
 int gemv1_merge_max_splits();
+// batch 1, bf16 rows: the residual product by head slices over the attention's
+// split partials (GemvArgs::part, part_ml, part_pos, part_S <= 64, part_chunk,
+// part_hd 64 or 128), adding into y with float atomics
+hipError_t launch_oproj_heads(const GemvArgs& a, hipStream_t s);
 // batch 2..16 on the matrix cores (qd_gemm16.hip): w_type 1 bf16 rows, 2 int8 rows
 // with a.wscale (K a multiple of 16, widened to bf16 exactly); a.kt must be
 // gemm16_chunk(a.K); part_val/part_idx hold [B][grid] entries

@@ -72,7 +72,7 @@ class QdError(RuntimeError):
         self.status = status
 
 
-ABI_VERSION = 4   # QD_ABI_VERSION of the header this binding follows
+ABI_VERSION = 5   # QD_ABI_VERSION of the header this binding follows
 
 
 def load(path: str = LIB_PATH) -> ctypes.CDLL:

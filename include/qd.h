@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define QD_ABI_VERSION 4
+#define QD_ABI_VERSION 5
 
 typedef enum {
     QD_OK = 0,
@@ -272,7 +272,11 @@ typedef struct {
     int32_t matrix_core_attention;  /* 1: the MFMA grouped attention kernel                    */
     int32_t qkv_partials;           /* > 0: q|k|v as that many K-range partial products,      *
                                      * finished inside the attention kernel                   */
-    int32_t merge_in_o_proj;        /* 1: batch 1, o_proj merges the splits (no merge launch) */
+    int32_t merge_in_o_proj;        /* 1: batch 1, o_proj merges the splits (no merge launch); *
+                                     * 2: batch 1, o_proj by head slices, each merging its    *
+                                     * head's splits, the slices added into the residual with *
+                                     * float atomics (no merge launch; off when               *
+                                     * QD_DETERMINISTIC=1 or QD_O_HEADS=0 is set)             */
     int32_t step_kernel;            /* 1: batch 1 eligible for the one-launch step, taken      *
                                      * when QD_STEP_KERNEL=1 is set in the environment        */
     int32_t fused_qkv;              /* 1: batch 1, the q|k|v projection runs inside the        *

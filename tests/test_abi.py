@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol(lib):
     for n in declared_functions():
         assert n in exported, n
         assert hasattr(lib, n)
-    assert lib.qd_abi_version() == Q.ABI_VERSION == 4
+    assert lib.qd_abi_version() == Q.ABI_VERSION == 5
 
 
 def test_struct_layout_matches_the_header(tmp_path):
@@ -341,6 +341,27 @@ def test_decode_plan_fused_projection(lib, monkeypatch):
                                  vocab=1000, n_layers=2), 1, 100).fused_qkv == 0    # head_dim 128
     monkeypatch.setenv("QD_FUSED_QKV", "0")
     assert Q.qd_decode_plan(_cfg_05b(), 1, 513).fused_qkv == 0
+
+
+def test_decode_plan_o_proj_by_head_slices(lib, monkeypatch):
+    """Batch 1 with a context wider than 1024 values (8B class: 32 heads of 128)
+    over several splits: o_proj by head slices, no merge launch (plan value 2).
+    One split, batch > 1, non-bf16 rows, QD_O_HEADS=0 and QD_DETERMINISTIC=1 keep
+    the merge launch; the 0.5B shape merges inside its o_proj GEMV (value 1)."""
+    monkeypatch.delenv("QD_O_HEADS", raising=False)
+    monkeypatch.delenv("QD_DETERMINISTIC", raising=False)
+    c8b = _cfg(hidden=4096, ffn=12288, n_q_heads=32, n_kv_heads=8, head_dim=128, vocab=151936, n_layers=36,
+               qk_norm=1)
+    p = Q.qd_decode_plan(c8b, 1, 4097)
+    assert p.merge_in_o_proj == 2 and 1 < p.splits <= 64
+    assert Q.qd_decode_plan(c8b, 1, 64).merge_in_o_proj == 0          # one split: no merge at all
+    assert Q.qd_decode_plan(c8b, 2, 4097).merge_in_o_proj == 0        # batch 2
+    assert Q.qd_decode_plan(_cfg_05b(), 1, 513).merge_in_o_proj == 1
+    for name, val in (("QD_O_HEADS", "0"), ("QD_DETERMINISTIC", "1")):
+        monkeypatch.setenv(name, val)
+        assert Q.qd_decode_plan(c8b, 1, 4097).merge_in_o_proj == 0, name
+        monkeypatch.delenv(name)
+    assert Q.qd_decode_plan(c8b, 1, 4097).merge_in_o_proj == 2
 
 
 def test_decode_plan_checks(lib):
