@@ -35,7 +35,12 @@ typedef __attribute__((ext_vector_type(4))) float g16_f32x4;
 constexpr int kG16Chunk = 1024;   // K elements staged per chunk: 64 KB of LDS for 16 tokens
 constexpr int kG16U = 2;          // k-steps (of 32) per pipeline stage (lm_head at batch 16: 59.5 us at 2, 62.4 at 4, 63.8 at 8)
 constexpr int kG16Cus = 256;      // compute units of the chip (MI355X)
-constexpr int kG16RowsWgs = 2 * kG16Cus;   // grid of gemm16_rows_kernel
+// Waves of a gemm16_rows_kernel workgroup and its grid (8 waves per CU): at batch 16
+// the 0.5B gate|up takes 8.55 us with two 4-wave workgroups per CU against 8.67
+// with one of 8 (one staged activation per CU) for bf16 rows, and 9.94 against
+// 9.52 us for int8 rows, so int8 rows take the 8-wave form.
+template <typename WT> constexpr int g16_rows_waves() { return sizeof(WT) == 1 ? 8 : 4; }
+template <typename WT> constexpr int g16_rows_wgs() { return 8 * kG16Cus / g16_rows_waves<WT>(); }
 
 __device__ __forceinline__ g16_bf16x8 g16_frag(uint4 v) { return __builtin_bit_cast(g16_bf16x8, v); }
 
@@ -526,14 +531,14 @@ __global__ __launch_bounds__(64 * WK) void gemm16_direct_kernel(GemvArgs a) {
 // instruction then fetches 8 whole lines (a layout with 32-byte pieces of 32
 // lines per instruction fetched every line twice), and the 8 lanes of a 16-byte
 // LDS read phase (tokens 0..7 or 8..15) land on distinct banks.
-template <typename WT, int EPI, int RB, int SPW>
-__global__ __launch_bounds__(256) void gemm16_rows_kernel(GemvArgs a) {
+template <typename WT, int EPI, int RB, int SPW, int NWV>
+__global__ __launch_bounds__(NWV * 64) void gemm16_rows_kernel(GemvArgs a) {
     using WL = typename G16W<WT>::L;
     constexpr int NW = (EPI == EPI_SWIGLU) ? 2 : 1;
     constexpr int NLD = SPW * RB * NW;      // weight loads per lane
     static_assert(NLD <= 63, "vmcnt range");
     extern __shared__ __align__(16) char g16r_smem[];
-    __shared__ float ssum[4][16];
+    __shared__ float ssum[NWV][16];
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
     const int col = lane & 15, kq = lane >> 4;
     const int B = a.B, K = a.K, N = a.N;
@@ -545,19 +550,19 @@ __global__ __launch_bounds__(256) void gemm16_rows_kernel(GemvArgs a) {
     // 1. activation and gain by DMA (each 1 KB instruction fills 32 units)
     {
         const uint32_t xl = lds_addr(xs), gl = lds_addr(gs);
-        for (int c = wave; c < nsteps * 2; c += 4) {   // lines (c / 2, 8 (c % 2) + lane / 8)
+        for (int c = wave; c < nsteps * 2; c += NWV) {   // lines (c / 2, 8 (c % 2) + lane / 8)
             const int t = (c & 1) * 8 + (lane >> 3);
             const int k = (c >> 1) * 32 + ((lane & 7) ^ (((t >> 1) & 3) << 1)) * 4;
             const void* src = t < B ? (const void*)(a.x + (long)t * K + k) : (const void*)kG16Zeros;
             lds_dma16(src, __builtin_amdgcn_readfirstlane(xl + c * 1024));
         }
-        for (int c = wave; c < (K * 2 + 1023) / 1024; c += 4) {
+        for (int c = wave; c < (K * 2 + 1023) / 1024; c += NWV) {
             const int e = min(c * 512 + lane * 8, K - 8);       // what lands past K is never read
             lds_dma16((const uint16_t*)a.gain + e, __builtin_amdgcn_readfirstlane(gl + c * 1024));
         }
     }
     // 2. this wave's weights: steps s0 + u (past s1, and rows past r1, read the zero block)
-    const int s0 = wave * nsteps / 4, s1 = (wave + 1) * nsteps / 4;
+    const int s0 = wave * nsteps / NWV, s1 = (wave + 1) * nsteps / NWV;
     const WT* wrow[RB][NW];
     bool rok[RB];
 #pragma unroll
@@ -594,7 +599,7 @@ __global__ __launch_bounds__(256) void gemm16_rows_kernel(GemvArgs a) {
     __builtin_amdgcn_s_waitcnt(wait_vm(NLD));   // this wave's DMA landed (loads retire in issue order)
     lds_barrier();                              // ... and every wave's
     if (a.zero_ptr && blockIdx.x == 0)
-        for (int i = tid; i < a.zero_n; i += 256) a.zero_ptr[i] = 0u;
+        for (int i = tid; i < a.zero_n; i += NWV * 64) a.zero_ptr[i] = 0u;
 
     // 3. MFMAs, step by step
     g16_f32x4 acc[RB][NW];
@@ -630,13 +635,13 @@ __global__ __launch_bounds__(256) void gemm16_rows_kernel(GemvArgs a) {
             }
     }
 
-    // 4. the four waves' partial products and sums of squares meet in wave 0 (the
+    // 4. the waves' partial products and sums of squares meet in wave 0 (the
     //    activation's LDS holds the partials once every wave is done reading it)
     {
         const float t = strided_sum<16>(ss);
         if (lane < 16) ssum[wave][lane] = t;
     }
-    g16_f32x4* red = (g16_f32x4*)g16r_smem;     // [3][RB][NW][64]
+    g16_f32x4* red = (g16_f32x4*)g16r_smem;     // [NWV - 1][RB][NW][64]
     lds_barrier();
     if (wave > 0)
 #pragma unroll
@@ -646,12 +651,15 @@ __global__ __launch_bounds__(256) void gemm16_rows_kernel(GemvArgs a) {
     lds_barrier();
     if (wave != 0 || col >= B) return;
 #pragma unroll
-    for (int q = 0; q < 3; ++q)
+    for (int q = 0; q < NWV - 1; ++q)
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
             for (int n = 0; n < NW; ++n) acc[rb][n] += red[((q * RB + rb) * NW + n) * kWave + lane];
-    const float rs = 1.0f / sqrtf((ssum[0][col] + ssum[1][col] + ssum[2][col] + ssum[3][col]) / (float)K + a.eps);
+    float sst = 0.f;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) sst += ssum[w][col];
+    const float rs = 1.0f / sqrtf(sst / (float)K + a.eps);
     float* yrow = a.y + (long)col * N;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -881,18 +889,21 @@ int gemm16_store_splits(int K, int N) {
     return s;
 }
 
-// Blocks per workgroup of the multi-block normed kernel (gemm16_rows_kernel, two
-// workgroups per CU: what the staged activation's LDS allows; against one per CU
-// with twice the rows, 9.7 -> 9.0 us for gate|up at batch 16 although each CU
-// then stages the activation twice: the load path wants the extra waves), or 0
+// Blocks per workgroup of the multi-block normed kernel (gemm16_rows_kernel: two
+// 4-wave workgroups per CU for bf16 rows, what the staged activation's LDS allows;
+// against one 4-wave workgroup per CU with twice the rows, 9.7 -> 9.0 us for
+// gate|up at batch 16 although each CU then stages the activation twice: the load
+// path wants the extra waves; int8 rows one 8-wave workgroup per CU), or 0
 // when it does not apply: gate|up with more rows than 16 per CU (up to 48 per
 // workgroup), K a multiple of 32 up to 1024 with a per-wave step count it is
 // built for
+template <typename WT>
 static int gemm16_rows_shape(int K, int N, int epi, int* spw) {
-    if (epi != EPI_SWIGLU || K % 32 || K > 1024 || N <= 16 * kG16Cus || N > 48 * kG16RowsWgs) return 0;
-    *spw = (K / 32 + 3) / 4;
+    constexpr int nwv = g16_rows_waves<WT>(), wgs = g16_rows_wgs<WT>();
+    if (epi != EPI_SWIGLU || K % 32 || K > 1024 || N <= 16 * kG16Cus || N > 48 * wgs) return 0;
+    *spw = (K / 32 + nwv - 1) / nwv;
     if (*spw != 2 && *spw != 4 && *spw != 7 && *spw != 8) return 0;
-    return ((N + kG16RowsWgs - 1) / kG16RowsWgs + 15) / 16;
+    return ((N + wgs - 1) / wgs + 15) / 16;
 }
 
 // K split into the fewest chunks of at most kG16Chunk, evened out (multiples of 32)
@@ -917,27 +928,28 @@ static hipError_t gemm16_dispatch(const GemvArgs& a, int epi, int grid_cap, int*
         return hipErrorInvalidValue;
     if (!wide && gain_ok) {
         int rspw = 0;
-        const int rb = gemm16_rows_shape(a.K, a.N, epi, &rspw);
+        const int rb = gemm16_rows_shape<WT>(a.K, a.N, epi, &rspw);
+        constexpr int nwv = g16_rows_waves<WT>();
         if (rb) {
-            const int grid = kG16RowsWgs;            // rows [N w / grid, N (w + 1) / grid) each
+            const int grid = g16_rows_wgs<WT>();     // rows [N w / grid, N (w + 1) / grid) each
             if (grid > grid_cap) return hipErrorInvalidValue;
             if (grid_out) *grid_out = grid;
-            // activation and gain; the waves' partial products reuse it ([3][rb][2][64] x 16 bytes)
+            // activation and gain; the waves' partial products reuse it ([waves - 1][rb][2][64] x 16 bytes)
             const size_t shm = std::max((size_t)(a.K / 32) * 2048 + (size_t)((a.K * 2 + 1023) / 1024) * 1024,
-                                        (size_t)rb * 6 * 1024);
+                                        (size_t)rb * (nwv - 1) * 2 * 1024);
             auto go = [&](auto kern) {
                 if (shm > 65536 &&
                     hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm) != hipSuccess)
                     return hipErrorInvalidValue;
-                hipLaunchKernelGGL(kern, dim3(grid), dim3(256), shm, s, a);
+                hipLaunchKernelGGL(kern, dim3(grid), dim3(nwv * 64), shm, s, a);
                 return hipGetLastError();
             };
-#define QD_G16R(RB)                                                      \
-            switch (rspw) {                                              \
-                case 2: return go(gemm16_rows_kernel<WT, EPI_SWIGLU, RB, 2>); \
-                case 4: return go(gemm16_rows_kernel<WT, EPI_SWIGLU, RB, 4>); \
-                case 7: return go(gemm16_rows_kernel<WT, EPI_SWIGLU, RB, 7>); \
-                default: return go(gemm16_rows_kernel<WT, EPI_SWIGLU, RB, 8>); \
+#define QD_G16R(RB)                                                                         \
+            switch (rspw) {                                                                 \
+                case 2: return go(gemm16_rows_kernel<WT, EPI_SWIGLU, RB, 2, nwv>);  \
+                case 4: return go(gemm16_rows_kernel<WT, EPI_SWIGLU, RB, 4, nwv>);  \
+                case 7: return go(gemm16_rows_kernel<WT, EPI_SWIGLU, RB, 7, nwv>);  \
+                default: return go(gemm16_rows_kernel<WT, EPI_SWIGLU, RB, 8, nwv>); \
             }
             if (rb == 1) { QD_G16R(1) } else if (rb == 2) { QD_G16R(2) } else { QD_G16R(3) }
 #undef QD_G16R
