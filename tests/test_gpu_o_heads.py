@@ -99,3 +99,49 @@ def test_o_proj_by_head_slices(shape_name, p, monkeypatch):
     b = _step(case, p, tok)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[2], b[2]) and a[1] == b[1]
     assert np.array_equal(a[0], logits2) and np.array_equal(a[2], layer_out2)
+
+
+@pytest.mark.timeout(300)
+def test_o_proj_by_head_slices_graph_replay(monkeypatch):
+    """The head-sliced step captured in a HIP graph and replayed several times, with
+    eager work and synchronisations in between: every replay matches the eager
+    result to float32 rounding (the slices' atomic additions may come in another
+    order) with the same token."""
+    monkeypatch.delenv("QD_O_HEADS", raising=False)
+    monkeypatch.delenv("QD_DETERMINISTIC", raising=False)
+    sh = SHAPES["hd128_qknorm"]
+    p = 1999
+    case = make_case(sh, np.array([p], np.int32), seed=77, extra=2)
+    assert Q.qd_decode_plan(case.runner.cfg, 1, p + 1).merge_in_o_proj == 2
+    ctx = np.array([p], np.int32)
+    pos = dev_i32(ctx)
+    tok = dev_i32(synth.make_tokens(1, sh.vocab, seed=77))
+    logits = torch.empty(1, sh.vocab, device="cuda")
+    nxt = torch.empty(1, dtype=torch.int32, device="cuda")
+
+    def step():
+        case.runner.step(ctx, pos, tokens=tok, logits=logits, next_tokens=nxt, stream=torch.cuda.current_stream())
+
+    step()
+    torch.cuda.synchronize()
+    ref_logits, ref_next = logits.clone(), nxt.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for i in range(4):
+        logits.fill_(float("nan"))
+        nxt.fill_(-1)
+        junk = torch.randn(1000, device="cuda").sum()   # eager work between replays
+        torch.cuda.synchronize()
+        print(f"replay {i}", flush=True)
+        g.replay()
+        torch.cuda.synchronize()
+        assert not torch.isnan(logits).any(), i
+        assert rel_err(logits.cpu().numpy(), ref_logits.cpu().numpy().astype(np.float64)) <= 1e-5, i
+        assert torch.equal(nxt, ref_next), i
+    del junk
