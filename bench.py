@@ -564,8 +564,8 @@ def main():
                          "that scales the FETCH_SIZE / WRITE_SIZE counters to bytes")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the multi-GPU layout is described in DESIGN.md and not run.", file=sys.stderr)
+        print(f"bench.py: the decode step runs on one GPU only (asked for --gpus {args.gpus}); "
+              "sharding over several GPUs is a design, not an implemented path.", file=sys.stderr)
         sys.exit(2)
 
     from workloads import shapes as S
