@@ -600,13 +600,18 @@ qd_status decode_step_impl(const qd_config* cfg, const qd_weights* w, const qd_k
         }
     }
 
-    qd::StepInputArgs si{};
-    si.tokens = tokens; si.embed = w->embed; si.embed_scale = w->s_embed; si.x_in = x_in; si.x = x;
-    si.pos = pos; si.rope = rope;
-    si.B = B; si.D = D; si.V = c.vocab; si.hd = P.hd; si.theta = c.rope_theta;
-    QD_LAUNCH_K(QD_K_EMBED, qd::launch_step_input(si, wty, s), "step input");
-
     const bool fq = b1_fused_qkv(cfg, B, merge_in_o, chunk, S, hpw);
+    // with the projection in the attention launch and a token to embed, the first
+    // layer's launch gathers the embedding row and forms the RoPE table itself
+    const bool emb_in_fq = fq && tokens;
+    if (!emb_in_fq) {
+        qd::StepInputArgs si{};
+        si.tokens = tokens; si.embed = w->embed; si.embed_scale = w->s_embed; si.x_in = x_in; si.x = x;
+        si.pos = pos; si.rope = rope;
+        si.B = B; si.D = D; si.V = c.vocab; si.hd = P.hd; si.theta = c.rope_theta;
+        QD_LAUNCH_K(QD_K_EMBED, qd::launch_step_input(si, wty, s), "step input");
+    }
+
     const int det = deterministic_enabled() ? 1 : 0;
     const bool o_heads = b1_o_heads(cfg, B, merge_in_o, S);
     for (int l = 0; l < c.n_layers; ++l) {
@@ -655,6 +660,9 @@ qd_status decode_step_impl(const qd_config* cfg, const qd_weights* w, const qd_k
         }
         if (fq) {   // batch 1: the projection inside the attention launch
             at.fq = 1; at.fq_x = x; at.fq_gain = L.attn_norm; at.fq_out = qkv; at.x_dim = D;
+            if (emb_in_fq && l == 0) {
+                at.fq_tok = tokens; at.fq_embed = w->embed; at.fq_embed_scale = w->s_embed; at.fq_vocab = c.vocab;
+            }
             at.fq_w[0] = L.wq; at.fq_w[1] = L.wk; at.fq_w[2] = L.wv;
             if (wty == QD_I8) { at.fq_scale[0] = L.s_q; at.fq_scale[1] = L.s_k; at.fq_scale[2] = L.s_v; }
             at.qkv_bias[0] = L.bq; at.qkv_bias[1] = L.bk; at.qkv_bias[2] = L.bv;

@@ -113,7 +113,37 @@ struct FqLoads {
     uint2 gain;
     float bias;    // of row 4q + (li & 3)
     float scale;   // int8: that row's scale (1 for bf16 rows)
+    uint2 xe;      // x from the embedding: 4 bf16 values, or 4 int8 codes in xe.x
+    float xs;      // ... their factor (int8: the row scale; 0 for an id outside the table)
 };
+
+// (cos, sin) of pair i of the RoPE table at position p: the angle p * theta^(-2i/hd)
+// is formed and reduced modulo 2*pi in double, then its cosine and sine are taken in
+// float (the step-input kernel and the first layer's fused launch share it).
+__device__ __forceinline__ float2 rope_cs(float theta, int hd, int i, int p) {
+    const double inv = pow((double)theta, -2.0 * (double)i / (double)hd);
+    double ang = (double)p * inv;
+    const double two_pi = 6.283185307179586476925286766559;
+    ang -= two_pi * rint(ang / two_pi);
+    float sv, cv;
+    sincosf((float)ang, &sv, &cv);
+    return make_float2(cv, sv);
+}
+
+// x as 4 floats: loaded, or widened from the embedding row
+template <typename RT, bool EMB>
+__device__ __forceinline__ float4 fq_xval(const FqLoads<RT>& f) {
+    if constexpr (!EMB) {
+        return f.x;
+    } else if constexpr (sizeof(RT) == 1) {
+        const uint32_t c = f.xe.x;
+        return make_float4((float)(int8_t)(c & 0xffu) * f.xs, (float)(int8_t)((c >> 8) & 0xffu) * f.xs,
+                           (float)(int8_t)((c >> 16) & 0xffu) * f.xs, (float)(int8_t)(c >> 24) * f.xs);
+    } else {
+        return make_float4(bf16_to_f32(f.xe.x & 0xffffu) * f.xs, bf16_to_f32(f.xe.x >> 16) * f.xs,
+                           bf16_to_f32(f.xe.y & 0xffffu) * f.xs, bf16_to_f32(f.xe.y >> 16) * f.xs);
+    }
+}
 
 // Issue the loads of rows row0 .. row0 + 63 of the matrix w ([rows][x_dim]), their
 // bias (bf16, may be NULL), int8 row scale, x and its RMSNorm gain. The small loads
@@ -122,7 +152,7 @@ struct FqLoads {
 // rows in flight (loads complete in issue order). Compiler-only memory fences keep
 // that order and keep the row loads ahead of any branch that follows (left alone,
 // the compiler moves them below an early exit, behind a wait for the position).
-template <typename RT>
+template <typename RT, bool EMB>
 __device__ __forceinline__ void fq_issue(const AttnArgs& a, const void* w, const void* bias, const float* scale,
                                          int row0, FqLoads<RT>& f) {
     constexpr int CE = FqT<RT>::CE, NC = FqT<RT>::NC;
@@ -131,7 +161,7 @@ __device__ __forceinline__ void fq_issue(const AttnArgs& a, const void* w, const
     const int r0 = row0 + (tid / kFqLanes) * kFqRows, li = tid % kFqLanes;
     const long rbytes = (long)D * sizeof(RT);
     gbyte* wr = sgpr_gptr(w) + r0 * rbytes;
-    f.x = ((const float4*)a.fq_x)[e4];
+    if constexpr (!EMB) f.x = ((const float4*)a.fq_x)[e4];
     f.gain = ((const uint2*)a.fq_gain)[e4];
     gbyte* bp = sgpr_gptr(bias ? bias : w);
     f.bias = gld_scalar<uint16_t>(bp, bias ? r0 + (li & 3) : 0) * (bias ? 1.f : 0.f);
@@ -146,13 +176,25 @@ __device__ __forceinline__ void fq_issue(const AttnArgs& a, const void* w, const
             f.w[u][j] = gld16(wr + (u * rbytes + (c < KC ? c : 0) * 16));
         }
     asm volatile("" ::: "memory");
+    if constexpr (EMB) {   // behind the rows: its address waits for the token id
+        const int tok = *(const __attribute__((address_space(4))) int*)a.fq_tok;
+        const bool ok = tok >= 0 && tok < a.fq_vocab;
+        const long e0 = (ok ? (long)tok * D : 0L) + 4L * e4;
+        if constexpr (sizeof(RT) == 1) {
+            f.xe = make_uint2(*(const uint32_t*)((const int8_t*)a.fq_embed + e0), 0u);
+            f.xs = ok ? a.fq_embed_scale[tok] : 0.f;
+        } else {
+            f.xe = *(const uint2*)((const uint16_t*)a.fq_embed + e0);
+            f.xs = ok ? 1.f : 0.f;
+        }
+    }
 }
 
 // The 64 rows' values r * (W (x * g)) + bias into out[64] (LDS), r = 1/sqrt(mean(x^2) + eps)
 // (the RMSNorm folded into the product, as in the GEMV kernels). Barriers inside
 // (every thread of the workgroup calls it); they are LDS-only, so loads issued
 // after the rows (the K/V rows of the attention) stay in flight across them.
-template <typename RT>
+template <typename RT, bool EMB>
 __device__ __forceinline__ void fq_finish(const AttnArgs& a, const FqLoads<RT>& f, float* out) {
     constexpr int NWV = kAttnWaves, CE = FqT<RT>::CE, NC = FqT<RT>::NC;
     static_assert(kFqRows == 4, "a row's bias and scale sit in lane li & 3");
@@ -162,8 +204,9 @@ __device__ __forceinline__ void fq_finish(const AttnArgs& a, const FqLoads<RT>& 
     const int D = a.x_dim, KC = D / CE;
     float ss = 0.f;
     if (tid < D / 4) {   // (waits for x only: the row loads stay in flight)
-        const float4 v = f.x;
+        const float4 v = fq_xval<RT, EMB>(f);
         ss = v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+        if (EMB && blockIdx.x == 0) ((float4*)const_cast<float*>(a.fq_x))[tid] = v;   // x for the launches that follow
         ((float4*)xg)[tid] = make_float4(v.x * bf16_to_f32(f.gain.x & 0xffffu), v.y * bf16_to_f32(f.gain.x >> 16),
                                          v.z * bf16_to_f32(f.gain.y & 0xffffu), v.w * bf16_to_f32(f.gain.y >> 16));
     }
@@ -218,7 +261,7 @@ __device__ __forceinline__ float fq_rope(const float* v, const float2* tab, int 
     return d < 32 ? u * cs.x - pr * cs.y : u * cs.x + pr * cs.y;
 }
 
-template <typename WT, typename KVT, int HD, int NP, bool FQ = false, typename RT = uint16_t>
+template <typename WT, typename KVT, int HD, int NP, bool FQ = false, typename RT = uint16_t, bool EMB = false>
 __device__ __forceinline__ void attn_body(const AttnArgs& a, const int s, const int by, const int bz) {
     static_assert(!FQ || (HD == 64 && NP <= kAttnPassesGrouped), "projection in the launch: hd 64, grouped");
     constexpr int CE = VecN<KVT>::n;
@@ -259,7 +302,17 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int s, const 
     int p_fq = 0;
     if constexpr (FQ) {
         p_fq = fq_pos(a);
-        fq_issue<RT>(a, a.fq_w[0], a.qkv_bias[0], a.fq_scale[0], (g * G + h0) * HD, fql);
+        fq_issue<RT, EMB>(a, a.fq_w[0], a.qkv_bias[0], a.fq_scale[0], (g * G + h0) * HD, fql);
+    }
+    // first layer: the table row of this position, formed while the loads are out
+    // (workgroup 0 stores it for the launches that follow)
+    __shared__ float2 rtab[FQ && EMB ? 32 : 1];
+    if constexpr (FQ && EMB) {
+        if (tid < 32) {
+            const float2 cs = rope_cs(a.theta, HD, tid, p_fq);
+            rtab[tid] = cs;
+            if (blockIdx.x == 0) const_cast<float2*>(a.rope)[tid] = cs;
+        }
     }
     const int qkvr = (a.Hq + 2 * a.Hkv) * HD;
     const bool pro_ld = !FQ && !prefill && nh > 0 && tid < (nh + 1) * LPT;
@@ -320,9 +373,9 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, const int s, const 
     }
     if constexpr (FQ) {   // the query head: project, rotate, publish (split 0)
         __shared__ float qraw[HD];
-        fq_finish<RT>(a, fql, qraw);
+        fq_finish<RT, EMB>(a, fql, qraw);
         if (tid < HD) {
-            const float q = fq_rope(qraw, a.rope, tid);
+            const float q = fq_rope(qraw, EMB ? rtab : a.rope, tid);
             qs[0][tid] = q;
             if (s == 0) a.fq_out[(g * G + h0) * HD + tid] = q;
         }
@@ -550,18 +603,22 @@ void attn_wide_kernel(AttnArgs a) {
 // is even), projected like the query heads, k rotated, rounded to the cache type
 // and stored at the position (nanoinfer page, phase 4: keys are rotated once, on
 // insert); the stored values, widened, go to fq_out for the residual product.
-template <typename RT, typename KVT>
+template <typename RT, typename KVT, bool EMB>
 __device__ __forceinline__ void fq_kv_body(const AttnArgs& a, int j) {
     constexpr int HD = 64, CE = VecN<KVT>::n, PG = kAttnPage;
     __shared__ float row[HD], st[HD];
+    __shared__ float2 rtab[EMB ? 32 : 1];
     const int g = j >> 1, is_v = j & 1, tid = threadIdx.x;
     const int p = fq_pos(a);
     FqLoads<RT> f;
-    fq_issue<RT>(a, is_v ? a.fq_w[2] : a.fq_w[1], is_v ? a.qkv_bias[2] : a.qkv_bias[1],
-                 is_v ? a.fq_scale[2] : a.fq_scale[1], g * HD, f);
+    fq_issue<RT, EMB>(a, is_v ? a.fq_w[2] : a.fq_w[1], is_v ? a.qkv_bias[2] : a.qkv_bias[1],
+                      is_v ? a.fq_scale[2] : a.fq_scale[1], g * HD, f);
     if (p < 0 || p >= a.capacity) return;
-    fq_finish<RT>(a, f, row);
-    if (tid < HD) st[tid] = is_v ? row[tid] : fq_rope(row, a.rope, tid);
+    if constexpr (EMB) {   // first layer: the table row of this position
+        if (tid < 32) rtab[tid] = rope_cs(a.theta, HD, tid, p);
+    }
+    fq_finish<RT, EMB>(a, f, row);   // (its barriers order the table's writes too)
+    if (tid < HD) st[tid] = is_v ? row[tid] : fq_rope(row, EMB ? rtab : a.rope, tid);
     lds_barrier();
     if (tid < HD / CE) {
         float v[CE];
@@ -587,18 +644,18 @@ __device__ __forceinline__ void fq_kv_body(const AttnArgs& a, int j) {
 // ids 8 apart: id = 8 (S (h / 8) + s) + h % 8 (ids of heads past Hq exit at once).
 __host__ __device__ constexpr int fq_attn_wgs(int S, int Hq) { return 8 * S * ((Hq + 7) / 8); }
 
-template <typename RT, typename KVT>
+template <typename RT, typename KVT, bool EMB>
 __global__ __launch_bounds__(kAttnWaves * kWave) void attn_fq_kernel(AttnArgs a) {
     static_assert(kAttnWaves * kWave == 64 / kFqRows * kFqLanes, "one 64-row block per workgroup");
     const int n_att = fq_attn_wgs(a.S, a.Hq);
     const int id = blockIdx.x;
     if (id >= n_att) {
-        fq_kv_body<RT, KVT>(a, id - n_att);
+        fq_kv_body<RT, KVT, EMB>(a, id - n_att);
         return;
     }
     const int slot = id >> 3, h = (slot / a.S) * 8 + (id & 7), s = slot % a.S;
     if (h >= a.Hq) return;
-    attn_body<uint16_t, KVT, 64, kAttnPassesGrouped, true, RT>(a, s, h, 0);
+    attn_body<uint16_t, KVT, 64, kAttnPassesGrouped, true, RT, EMB>(a, s, h, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -1057,14 +1114,18 @@ hipError_t launch_attention(const AttnArgs& a, int w_is_bf16, int kv_is_bf16, hi
         if (!w_is_bf16 || !attn_fq_ok(a, i8 ? 2 : 1, kv_is_bf16) || !a.fq_x || !a.fq_gain || !a.fq_w[0] ||
             !a.fq_w[1] || !a.fq_w[2] || !a.fq_out || (i8 && (!a.fq_scale[1] || !a.fq_scale[2])))
             return hipErrorInvalidValue;
+        if (a.fq_tok && (!a.fq_embed || a.fq_vocab < 1 || !a.rope || (i8 && !a.fq_embed_scale)))
+            return hipErrorInvalidValue;
         const dim3 grid(fq_attn_wgs(a.S, a.Hq) + 2 * a.Hkv), block(kAttnWaves * kWave);
+#define QD_FQ(RT, KVT)                                                                            \
+        if (a.fq_tok) hipLaunchKernelGGL((attn_fq_kernel<RT, KVT, true>), grid, block, 0, s, a); \
+        else hipLaunchKernelGGL((attn_fq_kernel<RT, KVT, false>), grid, block, 0, s, a);
         if (i8) {
-            if (kv_is_bf16) hipLaunchKernelGGL((attn_fq_kernel<int8_t, uint16_t>), grid, block, 0, s, a);
-            else hipLaunchKernelGGL((attn_fq_kernel<int8_t, float>), grid, block, 0, s, a);
+            if (kv_is_bf16) { QD_FQ(int8_t, uint16_t) } else { QD_FQ(int8_t, float) }
         } else {
-            if (kv_is_bf16) hipLaunchKernelGGL((attn_fq_kernel<uint16_t, uint16_t>), grid, block, 0, s, a);
-            else hipLaunchKernelGGL((attn_fq_kernel<uint16_t, float>), grid, block, 0, s, a);
+            if (kv_is_bf16) { QD_FQ(uint16_t, uint16_t) } else { QD_FQ(uint16_t, float) }
         }
+#undef QD_FQ
         return hipGetLastError();
     }
     const int G = a.Hq / a.Hkv;
@@ -1134,16 +1195,7 @@ __global__ __launch_bounds__(256) void step_input_kernel(StepInputArgs a) {
         for (int d = tid; d < a.D; d += blockDim.x) x[d] = a.x_in[(long)b * a.D + d];
     }
     const int half = a.hd / 2;
-    if (tid < half) {
-        const int p = a.pos[b];
-        const double inv = pow((double)a.theta, -2.0 * (double)tid / (double)a.hd);
-        double ang = (double)p * inv;
-        const double two_pi = 6.283185307179586476925286766559;
-        ang -= two_pi * rint(ang / two_pi);
-        float sv, cv;
-        sincosf((float)ang, &sv, &cv);
-        a.rope[(long)b * half + tid] = make_float2(cv, sv);
-    }
+    if (tid < half) a.rope[(long)b * half + tid] = rope_cs(a.theta, a.hd, tid, a.pos[b]);
 }
 
 hipError_t launch_step_input(const StepInputArgs& a, int w_type, hipStream_t s) {

@@ -143,6 +143,15 @@ struct AttnArgs {
     const void* fq_w[3];
     const float* fq_scale[3];   // int8 rows: the q, k and v row scales (NULL: bf16 rows)
     float* fq_out;
+    // batch 1 with the projection in the launch, first layer (fq_tok != NULL): x is
+    // the embedding row of token fq_tok[0] (int8 rows: times fq_embed_scale of the
+    // token; an id outside [0, fq_vocab) gives a zero row) and the RoPE table is
+    // formed in the launch; workgroup 0 stores both (x to fq_x, the table to rope)
+    // for the launches that follow, in place of the step-input launch
+    const int* fq_tok;
+    const void* fq_embed;
+    const float* fq_embed_scale;
+    int fq_vocab;
 };
 constexpr int kFqMaxD = 1024;
 // attention kernel, plus the split merge kernel when S > 1
